@@ -1,0 +1,383 @@
+"""Python marshalling for the plain CPU oracle in ``oracle.c``.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by ``__graft_entry__.smoke``
+and by the CPU-baseline leg of ``bench.py``.  The product package
+(``realtime_transformer_amd``) never imports this module, and this module never
+imports the product package; the only code both sides share is the seeded input
+generator (``realtime_transformer_amd.datagen``), which holds none of the
+method's arithmetic.
+
+All arithmetic lives in ``oracle.c``.  This file only moves numpy arrays in and
+out and strings the per-layer steps together in the pages' order:
+quantise weights at load, calibrate (measurement pass, then static scales),
+then run the block layer after layer (FlashRT architecture doc, "predict()
+flow": weights -> calibration -> capture -> replay).
+
+Array conventions: bf16 tensors are ``numpy.uint16`` holding the bf16 bit
+pattern; E4M3 tensors are ``numpy.uint8`` codes; weights use the nn.Linear
+layout ``[out, in]``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+from typing import Callable, Iterable, List, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+ACT_GEGLU_TANH = 0
+ACT_SWIGLU = 1
+ACT_GELU_TANH = 2
+
+_c_u8p = ctypes.POINTER(ctypes.c_uint8)
+_c_u16p = ctypes.POINTER(ctypes.c_uint16)
+_c_f32p = ctypes.POINTER(ctypes.c_float)
+_c_f64p = ctypes.POINTER(ctypes.c_double)
+
+
+def build(force: bool = False) -> str:
+    """Compile liboracle.so with gcc (ISO C11, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-ffp-contract=off",
+               "-fno-fast-math", "-pthread", "-o", tmp, _SRC, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        L.orc_bf16_round.restype = ctypes.c_uint16
+        L.orc_bf16_round.argtypes = [ctypes.c_float]
+        L.orc_bf16_to_f32.restype = ctypes.c_float
+        L.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.orc_e4m3_decode.restype = ctypes.c_double
+        L.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.orc_e4m3_encode.restype = ctypes.c_uint8
+        L.orc_e4m3_encode.argtypes = [ctypes.c_float]
+        L.orc_e4m3_encode_array.argtypes = [_c_f32p, _c_u8p, ctypes.c_int64]
+        L.orc_e4m3_decode_array.argtypes = [_c_u8p, _c_f64p, ctypes.c_int64]
+        L.orc_bf16_round_array.argtypes = [_c_f32p, _c_u16p, ctypes.c_int64]
+        L.orc_gelu_tanh.restype = ctypes.c_double
+        L.orc_gelu_tanh.argtypes = [ctypes.c_double]
+        L.orc_silu.restype = ctypes.c_double
+        L.orc_silu.argtypes = [ctypes.c_double]
+        L.orc_act_f32.restype = ctypes.c_float
+        L.orc_act_f32.argtypes = [ctypes.c_int, ctypes.c_float]
+        L.orc_gemm_e4m3.restype = ctypes.c_int
+        L.orc_gemm_e4m3.argtypes = [ctypes.c_int] * 3 + [_c_u8p, _c_u8p, _c_f32p, ctypes.c_int]
+        L.orc_scale_from_amax.restype = ctypes.c_float
+        L.orc_scale_from_amax.argtypes = [ctypes.c_float]
+        L.orc_quant_tensor.restype = ctypes.c_float
+        L.orc_quant_tensor.argtypes = [_c_u16p, ctypes.c_int64, _c_u8p]
+        L.orc_add_rmsnorm_quant.restype = None
+        L.orc_add_rmsnorm_quant.argtypes = [ctypes.c_int, ctypes.c_int, _c_u16p, _c_u16p, _c_u16p,
+                                            ctypes.c_float, ctypes.c_float, _c_u16p, _c_f32p,
+                                            _c_u8p, ctypes.c_int]
+        L.orc_gateup.restype = ctypes.c_int
+        L.orc_gateup.argtypes = [ctypes.c_int] * 4 + [_c_u8p, _c_u8p, _c_u8p, ctypes.c_float,
+                                                      ctypes.c_float, ctypes.c_float, _c_f32p,
+                                                      _c_u8p, ctypes.c_int]
+        L.orc_down.restype = ctypes.c_int
+        L.orc_down.argtypes = [ctypes.c_int] * 3 + [_c_u8p, _c_u8p, ctypes.c_float, _c_u16p,
+                                                    ctypes.c_int]
+        L.orc_block.restype = ctypes.c_int
+        L.orc_block.argtypes = ([ctypes.c_int] * 4 + [ctypes.c_float, _c_u16p, _c_u16p, _c_u16p,
+                                                     _c_u8p, _c_u8p, _c_u8p] + [ctypes.c_float] * 5
+                                + [_c_u16p, _c_u8p, _c_u8p, _c_u16p, ctypes.c_int])
+        L.orc_block_measure.restype = ctypes.c_int
+        L.orc_block_measure.argtypes = ([ctypes.c_int] * 4 + [ctypes.c_float, _c_u16p, _c_u16p,
+                                                             _c_u16p, _c_u8p, _c_u8p, _c_u8p]
+                                        + [ctypes.c_float] * 3
+                                        + [_c_u16p, _c_u16p, _c_f32p, _c_f32p, ctypes.c_int])
+        _lib = L
+    return _lib
+
+
+def default_threads() -> int:
+    """Host threads the oracle uses: the CPUs this process may run on, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _p(a: Optional[np.ndarray], ptype):
+    if a is None:
+        return ctypes.cast(None, ptype)
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ptype)
+
+
+def _u16(a):
+    a = np.ascontiguousarray(a)
+    assert a.dtype == np.uint16, a.dtype
+    return a
+
+
+def _u8(a):
+    a = np.ascontiguousarray(a)
+    assert a.dtype == np.uint8, a.dtype
+    return a
+
+
+# --------------------------------------------------------------------------
+# scalar codecs (bulk forms for tests)
+# --------------------------------------------------------------------------
+
+def e4m3_encode(x) -> np.ndarray:
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    out = np.empty(x.shape, dtype=np.uint8)
+    lib().orc_e4m3_encode_array(_p(x, _c_f32p), _p(out, _c_u8p), x.size)
+    return out
+
+
+def e4m3_decode(c) -> np.ndarray:
+    c = _u8(np.asarray(c, dtype=np.uint8))
+    out = np.empty(c.shape, dtype=np.float64)
+    lib().orc_e4m3_decode_array(_p(c, _c_u8p), _p(out, _c_f64p), c.size)
+    return out
+
+
+def bf16_round(x) -> np.ndarray:
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().orc_bf16_round_array(_p(x, _c_f32p), _p(out, _c_u16p), x.size)
+    return out
+
+
+def bf16_to_f32(b) -> np.ndarray:
+    """Widen bf16 bit patterns to fp32 (exact: the bits become the top half)."""
+    b = np.ascontiguousarray(np.asarray(b, dtype=np.uint16))
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def gelu_tanh(z: float) -> float:
+    return lib().orc_gelu_tanh(float(z))
+
+
+def silu(z: float) -> float:
+    return lib().orc_silu(float(z))
+
+
+def act_f32(kind_is_silu: bool, z: float) -> float:
+    return lib().orc_act_f32(1 if kind_is_silu else 0, float(z))
+
+
+def scale_from_amax(amax: float) -> float:
+    return lib().orc_scale_from_amax(float(amax))
+
+
+# --------------------------------------------------------------------------
+# GEMM, weight quantisation, block steps
+# --------------------------------------------------------------------------
+
+def gemm_e4m3(a_codes, b_codes, nthreads: Optional[int] = None) -> np.ndarray:
+    """f32(exact sum_k dec(a[m,k]) * dec(b[n,k])) for a [M,K], b [N,K]."""
+    a = _u8(a_codes)
+    b = _u8(b_codes)
+    M, K = a.shape
+    N, K2 = b.shape
+    assert K == K2
+    out = np.empty((M, N), dtype=np.float32)
+    rc = lib().orc_gemm_e4m3(M, N, K, _p(a, _c_u8p), _p(b, _c_u8p), _p(out, _c_f32p),
+                             nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("K too large for the exact int64 sum")
+    return out
+
+
+def quant_tensor(w_bf16) -> tuple:
+    """Per-tensor E4M3 quantisation of a bf16 tensor -> (codes, scale)."""
+    w = _u16(w_bf16)
+    codes = np.empty(w.shape, dtype=np.uint8)
+    s = lib().orc_quant_tensor(_p(w, _c_u16p), w.size, _p(codes, _c_u8p))
+    return codes, float(np.float32(s))
+
+
+def add_rmsnorm_quant(r_prev, y_prev, w_norm, eps: float, inv_x: float,
+                      nthreads: Optional[int] = None):
+    """-> (r_out bf16 [M,H], x fp32 [M,H], xq codes [M,H])."""
+    r = _u16(r_prev)
+    M, H = r.shape
+    y = None if y_prev is None else _u16(y_prev)
+    w = _u16(w_norm)
+    r_out = np.empty((M, H), np.uint16)
+    x = np.empty((M, H), np.float32)
+    xq = np.empty((M, H), np.uint8)
+    lib().orc_add_rmsnorm_quant(M, H, _p(r, _c_u16p), _p(y, _c_u16p), _p(w, _c_u16p),
+                                float(eps), float(inv_x), _p(r_out, _c_u16p), _p(x, _c_f32p),
+                                _p(xq, _c_u8p), nthreads or default_threads())
+    return r_out, x, xq
+
+
+def gateup(xq, qg, qu, act: int, alpha_g: float, alpha_u: float, inv_h: float,
+           nthreads: Optional[int] = None):
+    """-> (h fp32 [M,I], hq codes [M,I])."""
+    xq = _u8(xq)
+    qu = _u8(qu)
+    M, H = xq.shape
+    I = qu.shape[0]
+    qg = None if act == ACT_GELU_TANH else _u8(qg)
+    h = np.empty((M, I), np.float32)
+    hq = np.empty((M, I), np.uint8)
+    rc = lib().orc_gateup(M, H, I, act, _p(xq, _c_u8p), _p(qg, _c_u8p), _p(qu, _c_u8p),
+                          float(alpha_g), float(alpha_u), float(inv_h), _p(h, _c_f32p),
+                          _p(hq, _c_u8p), nthreads or default_threads())
+    if rc:
+        raise RuntimeError("orc_gateup failed (%d)" % rc)
+    return h, hq
+
+
+def down(hq, qd, alpha_d: float, nthreads: Optional[int] = None) -> np.ndarray:
+    hq = _u8(hq)
+    qd = _u8(qd)
+    M, I = hq.shape
+    H = qd.shape[0]
+    y = np.empty((M, H), np.uint16)
+    rc = lib().orc_down(M, H, I, _p(hq, _c_u8p), _p(qd, _c_u8p), float(alpha_d),
+                        _p(y, _c_u16p), nthreads or default_threads())
+    if rc:
+        raise RuntimeError("orc_down failed (%d)" % rc)
+    return y
+
+
+@dataclass
+class LayerWeights:
+    """One layer's quantised weights as the oracle holds them."""
+    qg: Optional[np.ndarray]  # [I,H] codes (None when non-gated)
+    qu: np.ndarray            # [I,H] codes
+    qd: np.ndarray            # [H,I] codes
+    w_norm: np.ndarray        # [H] bf16 bits
+    s_g: float
+    s_u: float
+    s_d: float
+
+    @staticmethod
+    def quantize(w_gate, w_up, w_down, w_norm) -> "LayerWeights":
+        if w_gate is not None:
+            qg, s_g = quant_tensor(w_gate)
+        else:
+            qg, s_g = None, 1.0
+        qu, s_u = quant_tensor(w_up)
+        qd, s_d = quant_tensor(w_down)
+        return LayerWeights(qg, qu, qd, _u16(w_norm), s_g, s_u, s_d)
+
+
+def block(r_prev, y_prev, lw: LayerWeights, act: int, eps: float, s_x: float, s_h: float,
+          nthreads: Optional[int] = None):
+    """One FFN block -> (r_out, xq, hq, y_out)."""
+    r = _u16(r_prev)
+    M, H = r.shape
+    I = lw.qu.shape[0]
+    y = None if y_prev is None else _u16(y_prev)
+    r_out = np.empty((M, H), np.uint16)
+    xq = np.empty((M, H), np.uint8)
+    hq = np.empty((M, I), np.uint8)
+    y_out = np.empty((M, H), np.uint16)
+    rc = lib().orc_block(M, H, I, act, float(eps), _p(r, _c_u16p), _p(y, _c_u16p),
+                         _p(lw.w_norm, _c_u16p), _p(lw.qg, _c_u8p), _p(lw.qu, _c_u8p),
+                         _p(lw.qd, _c_u8p), lw.s_g, lw.s_u, lw.s_d, float(s_x), float(s_h),
+                         _p(r_out, _c_u16p), _p(xq, _c_u8p), _p(hq, _c_u8p), _p(y_out, _c_u16p),
+                         nthreads or default_threads())
+    if rc:
+        raise RuntimeError("orc_block failed (%d)" % rc)
+    return r_out, xq, hq, y_out
+
+
+def block_measure(r_prev, y_prev, lw: LayerWeights, act: int, eps: float,
+                  nthreads: Optional[int] = None):
+    """Calibration measurement pass of one block -> (r_out, y_out, amax_x, amax_h)."""
+    r = _u16(r_prev)
+    M, H = r.shape
+    I = lw.qu.shape[0]
+    y = None if y_prev is None else _u16(y_prev)
+    r_out = np.empty((M, H), np.uint16)
+    y_out = np.empty((M, H), np.uint16)
+    ax = ctypes.c_float(0.0)
+    ah = ctypes.c_float(0.0)
+    rc = lib().orc_block_measure(M, H, I, act, float(eps), _p(r, _c_u16p), _p(y, _c_u16p),
+                                 _p(lw.w_norm, _c_u16p), _p(lw.qg, _c_u8p), _p(lw.qu, _c_u8p),
+                                 _p(lw.qd, _c_u8p), lw.s_g, lw.s_u, lw.s_d, _p(r_out, _c_u16p),
+                                 _p(y_out, _c_u16p), ctypes.byref(ax), ctypes.byref(ah),
+                                 nthreads or default_threads())
+    if rc:
+        raise RuntimeError("orc_block_measure failed (%d)" % rc)
+    return r_out, y_out, float(ax.value), float(ah.value)
+
+
+def final_hidden(r_last, y_last) -> np.ndarray:
+    """Z = bf16(f32(R[L] + Y[L])) (the residual add after the last block)."""
+    s = bf16_to_f32(r_last) + bf16_to_f32(y_last)
+    return bf16_round(s)
+
+
+@dataclass
+class ChainResult:
+    s_x: List[float]
+    s_h: List[float]
+    amax_x: List[float]
+    amax_h: List[float]
+    r: List[np.ndarray]   # R[0..L]
+    y: List[np.ndarray]   # Y[0..L]
+    xq: List[np.ndarray]  # XQ[0..L-1]
+    hq: List[np.ndarray]  # HQ[0..L-1]
+    weights: List[Optional[LayerWeights]]
+
+
+def calibrate_and_run(layers: Iterable[Callable[[], LayerWeights]], act: int, eps: float,
+                      r0, y0, calib_batches: Sequence[tuple], keep_weights: bool = False,
+                      act_scales: Optional[Sequence[tuple]] = None,
+                      nthreads: Optional[int] = None) -> ChainResult:
+    """Layer-major chain: for each layer, measure the calibration batches
+    (amax of the gate/up input and of the down input over all batches, rows
+    and elements), derive the static scales s = f32(amax/448), then run the
+    quantised block on the evaluation state.  ``layers`` yields one callable
+    per layer that returns its quantised weights, so huge chains can stream
+    their weights.  ``act_scales`` (per layer (s_x, s_h)) skips the
+    measurement and uses the given scales (the calibration cache-hit path).
+    """
+    cal_states = [(_u16(r), None if y is None else _u16(y)) for r, y in calib_batches]
+    res = ChainResult([], [], [], [], [_u16(r0)], [None if y0 is None else _u16(y0)], [], [], [])
+    for li, get_w in enumerate(layers):
+        lw = get_w()
+        if act_scales is None:
+            ax = 0.0
+            ah = 0.0
+            nxt = []
+            for (r, y) in cal_states:
+                r2, y2, bx, bh = block_measure(r, y, lw, act, eps, nthreads)
+                ax = max(ax, bx)
+                ah = max(ah, bh)
+                nxt.append((r2, y2))
+            cal_states = nxt
+            s_x = scale_from_amax(ax)
+            s_h = scale_from_amax(ah)
+        else:
+            ax = ah = float("nan")
+            s_x, s_h = act_scales[li]
+        r_out, xq, hq, y_out = block(res.r[-1], res.y[-1], lw, act, eps, s_x, s_h, nthreads)
+        res.s_x.append(s_x)
+        res.s_h.append(s_h)
+        res.amax_x.append(ax)
+        res.amax_h.append(ah)
+        res.r.append(r_out)
+        res.y.append(y_out)
+        res.xq.append(xq)
+        res.hq.append(hq)
+        res.weights.append(lw if keep_weights else None)
+    return res

@@ -1,0 +1,466 @@
+/*
+ * oracle.c -- plain, slow CPU definition of the fused FP8 FFN block.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The product path
+ * (libfrt) never links, loads or calls it, and the two share no source,
+ * header, table or helper.
+ *
+ * What is computed follows the FlashRT pages:
+ *   - FlashRT project page (agentlenshq), "main ideas": weights and
+ *     activations in FP8 with per-tensor calibrated scales;
+ *   - itsolotime article, section 7.1 (FP8 path, E4M3) and 7.2 (the encoder
+ *     FFN loop: fp16/bf16 residual stream, RMSNorm, gate and up GEMMs,
+ *     gated activation fused with re-quantisation, down GEMM, residual add);
+ *   - FlashRT architecture doc, component "Calibration": amax per FP8 GEMM
+ *     input in a measurement pass, then alpha = act_scale * weight_scale
+ *     baked as host scalars;
+ *   - FlashRT architecture doc, component "Kernel library": the fused
+ *     residual + norm + quant kernel.
+ * Every rounding point the pages leave open is fixed here: OCP E4M3FN with
+ * saturation at +-448, round-to-nearest-even everywhere, the RMSNorm mean
+ * square summed in fp64 with 1/rms rounded once to fp32, FP8 products summed
+ * exactly and rounded once to fp32, activations evaluated in fp64 and rounded
+ * once to fp32, bf16 outputs by round-to-nearest-even.
+ *
+ * Style: scalar loops, no SIMD intrinsics, no blocking.  The only
+ * parallelism is pthreads over independent output elements.
+ *
+ * Parity status: every function here is pinned by the CPU tests
+ * (codec vs the OCP table and torch, bf16 vs torch, GEMM vs fp64 matmul,
+ * RMSNorm closed form, activations vs torch fp64, block vs an independent
+ * transcription, calibration brute force).  Nothing is "parity unpinned".
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_ACT_GEGLU_TANH 0 /* gelu_tanh(gate) * up              */
+#define ORC_ACT_SWIGLU 1     /* silu(gate) * up                   */
+#define ORC_ACT_GELU_TANH 2  /* gelu_tanh(up), no gate projection */
+
+/* ------------------------------------------------------------------------ */
+/* bf16: the top 16 bits of an fp32 after round-to-nearest-even.            */
+/* ------------------------------------------------------------------------ */
+
+static float bits_to_f32(uint32_t u) {
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+static uint32_t f32_to_bits(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return u;
+}
+
+float orc_bf16_to_f32(uint16_t b) { return bits_to_f32((uint32_t)b << 16); }
+
+uint16_t orc_bf16_round(float v) {
+  uint32_t u = f32_to_bits(v);
+  if ((u & 0x7fffffffu) > 0x7f800000u) /* NaN stays a quiet NaN */
+    return (uint16_t)((u >> 16) | 0x0040u);
+  uint32_t lower = u & 0xffffu;
+  uint32_t upper = u >> 16;
+  /* round half to even on the dropped 16 bits */
+  if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1u;
+  return (uint16_t)upper;
+}
+
+/* ------------------------------------------------------------------------ */
+/* OCP FP8 E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits.           */
+/* Exponent field 0 is subnormal (m * 2^-9).  S.1111.111 is NaN; there is   */
+/* no infinity; the largest finite value is S.1111.110 = 448.              */
+/* ------------------------------------------------------------------------ */
+
+double orc_e4m3_decode(uint8_t c) {
+  int sign = (c >> 7) & 1;
+  int e = (c >> 3) & 0xf;
+  int m = c & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9); /* m/8 * 2^(1-7) */
+  else
+    v = ldexp(1.0 + m / 8.0, e - 7);
+  return sign ? -v : v;
+}
+
+/* Round to nearest integer, ties to even.  x >= 0 and small. */
+static long rne_nonneg(double x) {
+  double f = floor(x);
+  double r = x - f;
+  long n = (long)f;
+  if (r > 0.5) return n + 1;
+  if (r < 0.5) return n;
+  return (n & 1) ? n + 1 : n;
+}
+
+uint8_t orc_e4m3_encode(float v) {
+  uint8_t sign = signbit(v) ? 0x80 : 0x00;
+  if (isnan(v)) return (uint8_t)(sign | 0x7f);
+  double a = fabs((double)v);
+  if (a >= 448.0) return (uint8_t)(sign | 0x7e); /* saturate, incl. inf */
+  if (a < ldexp(1.0, -6)) {
+    /* subnormal range: value = m * 2^-9, m in 0..8 (8 is the min normal) */
+    long m = rne_nonneg(a * 512.0);
+    return (uint8_t)(sign | (uint8_t)m); /* m == 8 encodes 0x08 = 2^-6 */
+  }
+  int e2;
+  double fr = frexp(a, &e2); /* a = fr * 2^e2, fr in [0.5, 1) */
+  int e = e2 - 1;            /* a = (2*fr) * 2^e, 2*fr in [1, 2) */
+  long mant = rne_nonneg((2.0 * fr - 1.0) * 8.0);
+  if (mant == 8) { /* carry into the next binade */
+    mant = 0;
+    e += 1;
+  }
+  /* a < 448 and RNE at step 32 in [256,512) keeps e+7 <= 15 and the code
+     at most 0x7e: 448 <= a < 464 was excluded above only for a >= 448,
+     and 432 < a < 448 rounds to 448 (mant 6) at most. */
+  return (uint8_t)(sign | (uint8_t)(((e + 7) << 3) | (int)mant));
+}
+
+/* e4m3 codes as integers in units of 2^-9 (exact): the value of code c is
+   k(c) * 2^-9 with |k| <= 448 * 512.  NaN codes never reach a GEMM. */
+static int32_t code_units(uint8_t c) {
+  double v = orc_e4m3_decode(c);
+  return (int32_t)(v * 512.0);
+}
+
+void orc_e4m3_encode_array(const float *in, uint8_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_encode(in[i]);
+}
+void orc_e4m3_decode_array(const uint8_t *in, double *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_decode(in[i]);
+}
+void orc_bf16_round_array(const float *in, uint16_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_round(in[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Activations, evaluated in fp64 with host libm and rounded once to fp32.  */
+/* gelu_tanh is Hendrycks & Gimpel's tanh approximation of GELU.            */
+/* ------------------------------------------------------------------------ */
+
+double orc_gelu_tanh(double z) {
+  const double pi = 3.14159265358979323846;
+  const double c = sqrt(2.0 / pi);
+  return 0.5 * z * (1.0 + tanh(c * (z + 0.044715 * z * z * z)));
+}
+double orc_silu(double z) { return z / (1.0 + exp(-z)); }
+
+float orc_act_f32(int act_kind_is_silu, float z) {
+  return act_kind_is_silu ? (float)orc_silu((double)z) : (float)orc_gelu_tanh((double)z);
+}
+
+/* ------------------------------------------------------------------------ */
+/* A tiny parallel-for over [0, n).                                         */
+/* ------------------------------------------------------------------------ */
+
+typedef void (*range_fn)(void *ctx, int64_t begin, int64_t end);
+typedef struct {
+  range_fn fn;
+  void *ctx;
+  int64_t begin, end;
+} range_job;
+
+static void *run_range(void *p) {
+  range_job *j = (range_job *)p;
+  j->fn(j->ctx, j->begin, j->end);
+  return NULL;
+}
+
+static void parallel_for(int64_t n, int nthreads, range_fn fn, void *ctx) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  if ((int64_t)nthreads > n) nthreads = (int)(n > 0 ? n : 1);
+  if (nthreads == 1) {
+    fn(ctx, 0, n);
+    return;
+  }
+  pthread_t th[256];
+  int started[256];
+  range_job jobs[256];
+  for (int t = 0; t < nthreads; ++t) {
+    jobs[t].fn = fn;
+    jobs[t].ctx = ctx;
+    jobs[t].begin = n * t / nthreads;
+    jobs[t].end = n * (t + 1) / nthreads;
+    started[t] = pthread_create(&th[t], NULL, run_range, &jobs[t]) == 0;
+    if (!started[t]) run_range(&jobs[t]); /* no thread: do it inline */
+  }
+  for (int t = 0; t < nthreads; ++t)
+    if (started[t]) pthread_join(th[t], NULL);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Exact FP8 GEMM: out[m][n] = f32( sum_k dec(a[m][k]) * dec(b[n][k]) ).    */
+/* a is [M,K] row-major codes, b is [N,K] (nn.Linear [out,in]) codes.       */
+/* Each product is an integer in units of 2^-18 below 2^36; for K < 2^15   */
+/* the int64 sum is exact, so the only rounding is the final one to fp32.   */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int M, N, K;
+  const uint8_t *a, *b;
+  float *out;
+  int32_t units[256];
+} gemm_ctx;
+
+static void gemm_range(void *p, int64_t begin, int64_t end) {
+  gemm_ctx *g = (gemm_ctx *)p;
+  for (int64_t idx = begin; idx < end; ++idx) {
+    int m = (int)(idx / g->N);
+    int n = (int)(idx % g->N);
+    const uint8_t *ar = g->a + (int64_t)m * g->K;
+    const uint8_t *br = g->b + (int64_t)n * g->K;
+    int64_t acc = 0;
+    for (int k = 0; k < g->K; ++k)
+      acc += (int64_t)g->units[ar[k]] * (int64_t)g->units[br[k]];
+    g->out[idx] = (float)ldexp((double)acc, -18);
+  }
+}
+
+int orc_gemm_e4m3(int M, int N, int K, const uint8_t *a, const uint8_t *b, float *out,
+                  int nthreads) {
+  if (K >= (1 << 15)) return -1; /* exactness bound of the int64 sum */
+  gemm_ctx g;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.a = a;
+  g.b = b;
+  g.out = out;
+  for (int c = 0; c < 256; ++c) g.units[c] = ((c & 0x7f) == 0x7f) ? 0 : code_units((uint8_t)c);
+  parallel_for((int64_t)M * N, nthreads, gemm_range, &g);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Per-tensor weight quantisation (architecture doc, "Weights": transpose + */
+/* Quant() transforms with a per-tensor scale collected into a table).      */
+/*   s = amax > 0 ? f32(amax / 448) : 1;  inv = f32(1/s);                   */
+/*   code = e4m3( f32(w * inv) )                                            */
+/* ------------------------------------------------------------------------ */
+
+float orc_scale_from_amax(float amax) { return amax > 0.0f ? amax / 448.0f : 1.0f; }
+
+float orc_quant_tensor(const uint16_t *w, int64_t n, uint8_t *codes) {
+  float amax = 0.0f;
+  for (int64_t i = 0; i < n; ++i) {
+    float a = fabsf(orc_bf16_to_f32(w[i]));
+    if (a > amax) amax = a;
+  }
+  float s = orc_scale_from_amax(amax);
+  float inv = 1.0f / s;
+  for (int64_t i = 0; i < n; ++i) codes[i] = orc_e4m3_encode(orc_bf16_to_f32(w[i]) * inv);
+  return s;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step 1: fused residual add + RMSNorm + E4M3 quantise, one row at a time. */
+/*   r'  = bf16( r + y )                          (new residual, stored)     */
+/*   S   = sum r'^2 in fp64;  inv_rms = f32( 1/sqrt(S/H + eps) ), fp64 math */
+/*   x   = f32( f32(r' * inv_rms) * w )                                     */
+/*   xq  = e4m3( f32(x * inv_x) )                                           */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int H;
+  const uint16_t *r_prev, *y_prev, *w_norm;
+  float eps, inv_x;
+  uint16_t *r_out;
+  float *x_out; /* optional: the unquantised normalised row */
+  uint8_t *xq_out;
+} norm_ctx;
+
+static void norm_range(void *p, int64_t begin, int64_t end) {
+  norm_ctx *c = (norm_ctx *)p;
+  int H = c->H;
+  for (int64_t m = begin; m < end; ++m) {
+    const uint16_t *r = c->r_prev + m * H;
+    const uint16_t *y = c->y_prev ? c->y_prev + m * H : NULL;
+    uint16_t *ro = c->r_out + m * H;
+    double S = 0.0;
+    for (int j = 0; j < H; ++j) {
+      float sum = orc_bf16_to_f32(r[j]) + (y ? orc_bf16_to_f32(y[j]) : 0.0f);
+      ro[j] = orc_bf16_round(sum);
+      double rv = (double)orc_bf16_to_f32(ro[j]);
+      S += rv * rv;
+    }
+    float inv_rms = (float)(1.0 / sqrt(S / (double)H + (double)c->eps));
+    for (int j = 0; j < H; ++j) {
+      float t = orc_bf16_to_f32(ro[j]) * inv_rms;
+      float x = t * orc_bf16_to_f32(c->w_norm[j]);
+      if (c->x_out) c->x_out[m * H + j] = x;
+      if (c->xq_out) c->xq_out[m * H + j] = orc_e4m3_encode(x * c->inv_x);
+    }
+  }
+}
+
+void orc_add_rmsnorm_quant(int M, int H, const uint16_t *r_prev, const uint16_t *y_prev,
+                           const uint16_t *w_norm, float eps, float inv_x, uint16_t *r_out,
+                           float *x_out, uint8_t *xq_out, int nthreads) {
+  norm_ctx c = {H, r_prev, y_prev, w_norm, eps, inv_x, r_out, x_out, xq_out};
+  parallel_for(M, nthreads, norm_range, &c);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step 2: gate/up GEMM, dequant, gated activation, re-quantise.            */
+/*   g = f32( f32(Ag) * alpha_g ),  u = f32( f32(Au) * alpha_u )            */
+/*   GeGLU: h = f32( f32(gelu_tanh(g)) * u );  SwiGLU: silu instead;         */
+/*   non-gated: h = f32( gelu_tanh(u) )                                      */
+/*   hq = e4m3( f32(h * inv_h) )                                            */
+/* ------------------------------------------------------------------------ */
+
+static float gated_value(int act, float g, float u) {
+  if (act == ORC_ACT_GELU_TANH) return (float)orc_gelu_tanh((double)u);
+  float a = (act == ORC_ACT_SWIGLU) ? (float)orc_silu((double)g) : (float)orc_gelu_tanh((double)g);
+  return a * u;
+}
+
+int orc_gateup(int M, int H, int I, int act, const uint8_t *xq, const uint8_t *qg,
+               const uint8_t *qu, float alpha_g, float alpha_u, float inv_h, float *h_out,
+               uint8_t *hq_out, int nthreads) {
+  float *Ag = NULL, *Au = (float *)malloc(sizeof(float) * (size_t)M * I);
+  if (!Au) return -2;
+  if (orc_gemm_e4m3(M, I, H, xq, qu, Au, nthreads)) return free(Au), -1;
+  if (act != ORC_ACT_GELU_TANH) {
+    Ag = (float *)malloc(sizeof(float) * (size_t)M * I);
+    if (!Ag) return free(Au), -2;
+    if (orc_gemm_e4m3(M, I, H, xq, qg, Ag, nthreads)) return free(Au), free(Ag), -1;
+  }
+  for (int64_t idx = 0; idx < (int64_t)M * I; ++idx) {
+    float u = Au[idx] * alpha_u;
+    float g = Ag ? Ag[idx] * alpha_g : 0.0f;
+    float h = gated_value(act, g, u);
+    if (h_out) h_out[idx] = h;
+    if (hq_out) hq_out[idx] = orc_e4m3_encode(h * inv_h);
+  }
+  free(Au);
+  free(Ag);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step 3: down GEMM, dequant, bf16 output.                                 */
+/*   y = bf16( f32( f32(Ad) * alpha_d ) )                                   */
+/* ------------------------------------------------------------------------ */
+
+int orc_down(int M, int H, int I, const uint8_t *hq, const uint8_t *qd, float alpha_d,
+             uint16_t *y_out, int nthreads) {
+  float *Ad = (float *)malloc(sizeof(float) * (size_t)M * H);
+  if (!Ad) return -2;
+  if (orc_gemm_e4m3(M, H, I, hq, qd, Ad, nthreads)) return free(Ad), -1;
+  for (int64_t idx = 0; idx < (int64_t)M * H; ++idx) y_out[idx] = orc_bf16_round(Ad[idx] * alpha_d);
+  free(Ad);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* One whole block (layer): (r_prev, y_prev) -> (r_out, y_out).              */
+/* Host scalars are derived exactly as the architecture doc's calibration   */
+/* component describes: alpha = act_scale * weight_scale, plus the two      */
+/* reciprocal activation scales used by the quantisers.                     */
+/* ------------------------------------------------------------------------ */
+
+int orc_block(int M, int H, int I, int act, float eps, const uint16_t *r_prev,
+              const uint16_t *y_prev, const uint16_t *w_norm, const uint8_t *qg,
+              const uint8_t *qu, const uint8_t *qd, float s_g, float s_u, float s_d, float s_x,
+              float s_h, uint16_t *r_out, uint8_t *xq_out, uint8_t *hq_out, uint16_t *y_out,
+              int nthreads) {
+  float inv_x = 1.0f / s_x, inv_h = 1.0f / s_h;
+  float alpha_g = s_x * s_g, alpha_u = s_x * s_u, alpha_d = s_h * s_d;
+  uint8_t *xq = xq_out ? xq_out : (uint8_t *)malloc((size_t)M * H);
+  uint8_t *hq = hq_out ? hq_out : (uint8_t *)malloc((size_t)M * I);
+  int rc = 0;
+  if (!xq || !hq) rc = -2;
+  if (!rc) orc_add_rmsnorm_quant(M, H, r_prev, y_prev, w_norm, eps, inv_x, r_out, NULL, xq, nthreads);
+  if (!rc) rc = orc_gateup(M, H, I, act, xq, qg, qu, alpha_g, alpha_u, inv_h, NULL, hq, nthreads);
+  if (!rc) rc = orc_down(M, H, I, hq, qd, alpha_d, y_out, nthreads);
+  if (!xq_out) free(xq);
+  if (!hq_out) free(hq);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Calibration measurement pass for one block (architecture doc,            */
+/* "Calibration" (a); the predict() flow's "run 1 fwd, record amax").        */
+/* Activations stay unquantised (fp32 as produced), weights are the already */
+/* quantised FP8 codes times their per-tensor scale; dot products in fp64.  */
+/* Returns the running maxima of |x| (gate/up GEMM input) and |h| (down     */
+/* GEMM input) through amax_x / amax_h (max-accumulated, not reset).        */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int M, N, K;
+  const float *a;   /* [M,K] fp32 activations */
+  const uint8_t *b; /* [N,K] codes */
+  float scale;
+  double *out; /* [M,N] fp64 sums (unscaled) */
+  double dec[256];
+} mgemm_ctx;
+
+static void mgemm_range(void *p, int64_t begin, int64_t end) {
+  mgemm_ctx *g = (mgemm_ctx *)p;
+  for (int64_t idx = begin; idx < end; ++idx) {
+    int m = (int)(idx / g->N);
+    int n = (int)(idx % g->N);
+    const float *ar = g->a + (int64_t)m * g->K;
+    const uint8_t *br = g->b + (int64_t)n * g->K;
+    double acc = 0.0;
+    for (int k = 0; k < g->K; ++k) acc += (double)ar[k] * g->dec[br[k]];
+    g->out[idx] = acc;
+  }
+}
+
+static void measure_gemm(int M, int N, int K, const float *a, const uint8_t *b, double *out,
+                         int nthreads) {
+  mgemm_ctx g;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.a = a;
+  g.b = b;
+  g.out = out;
+  for (int c = 0; c < 256; ++c) g.dec[c] = ((c & 0x7f) == 0x7f) ? 0.0 : orc_e4m3_decode((uint8_t)c);
+  parallel_for((int64_t)M * N, nthreads, mgemm_range, &g);
+}
+
+int orc_block_measure(int M, int H, int I, int act, float eps, const uint16_t *r_prev,
+                      const uint16_t *y_prev, const uint16_t *w_norm, const uint8_t *qg,
+                      const uint8_t *qu, const uint8_t *qd, float s_g, float s_u, float s_d,
+                      uint16_t *r_out, uint16_t *y_out, float *amax_x, float *amax_h,
+                      int nthreads) {
+  float *x = (float *)malloc(sizeof(float) * (size_t)M * H);
+  float *h = (float *)malloc(sizeof(float) * (size_t)M * I);
+  double *su = (double *)malloc(sizeof(double) * (size_t)M * I);
+  double *sg = (act != ORC_ACT_GELU_TANH) ? (double *)malloc(sizeof(double) * (size_t)M * I) : NULL;
+  double *sd = (double *)malloc(sizeof(double) * (size_t)M * H);
+  int rc = 0;
+  if (!x || !h || !su || !sd || (act != ORC_ACT_GELU_TANH && !sg)) rc = -2;
+  if (!rc) {
+    orc_add_rmsnorm_quant(M, H, r_prev, y_prev, w_norm, eps, 1.0f, r_out, x, NULL, nthreads);
+    for (int64_t i = 0; i < (int64_t)M * H; ++i)
+      if (fabsf(x[i]) > *amax_x) *amax_x = fabsf(x[i]);
+    measure_gemm(M, I, H, x, qu, su, nthreads);
+    if (sg) measure_gemm(M, I, H, x, qg, sg, nthreads);
+    for (int64_t i = 0; i < (int64_t)M * I; ++i) {
+      float u = (float)((double)s_u * su[i]);
+      float g = sg ? (float)((double)s_g * sg[i]) : 0.0f;
+      h[i] = gated_value(act, g, u);
+      if (fabsf(h[i]) > *amax_h) *amax_h = fabsf(h[i]);
+    }
+    measure_gemm(M, H, I, h, qd, sd, nthreads);
+    for (int64_t i = 0; i < (int64_t)M * H; ++i)
+      y_out[i] = orc_bf16_round((float)((double)s_d * sd[i]));
+  }
+  free(x);
+  free(h);
+  free(su);
+  free(sg);
+  free(sd);
+  return rc;
+}
