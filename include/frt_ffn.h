@@ -1,0 +1,197 @@
+/*
+ * frt_ffn.h -- C ABI of the fused FP8 transformer-FFN chain for AMD MI355X
+ * (gfx950).
+ *
+ * The operation (FlashRT pages):
+ *   - itsolotime article, section 7.2 (the encoder FFN loop): a high
+ *     precision residual stream, RMSNorm, gate and up projections, a fused
+ *     gated activation (GEGLU / SiLU family) that re-quantises its output,
+ *     the down projection, and the residual add;
+ *   - itsolotime article, section 7.1 and the FlashRT project page ("main
+ *     ideas"): FP8 E4M3 weights and activations with per-tensor scales;
+ *   - FlashRT architecture doc, component "Kernel library": residual + norm
+ *     + quant fusions as hand-written kernels;
+ *   - FlashRT architecture doc, component "Calibration": a measurement pass
+ *     records amax per FP8 GEMM input, then alpha = act_scale * weight_scale
+ *     is baked into the captured graph as host scalars;
+ *   - FlashRT architecture doc, component "CUDA Graph" and the layer
+ *     diagram's "C ABI execution contract: Buffer / Graph / Plan": the
+ *     captured forward takes only device pointers, allocates nothing,
+ *     lives for the process lifetime, and replay before capture is an error
+ *     (itsolotime article, section 4.1: relaxed capture of one stream).
+ *
+ * Per layer i (0-based) the chain maps slots (R[i], Y[i]) -> (R[i+1], Y[i+1]):
+ *   R[i+1] = bf16(R[i] + Y[i])                         new residual
+ *   XQ[i]  = e4m3(RMSNorm(R[i+1]) * w_norm[i] / s_x[i])  kernel 1
+ *   HQ[i]  = e4m3(act(XQ Wg^T a_g, XQ Wu^T a_u) / s_h[i]) kernel 2 (gate/up)
+ *   Y[i+1] = bf16(HQ Wd^T a_d)                          kernel 3 (down)
+ * and after the last layer Z = bf16(R[L] + Y[L]).  a_g = s_x s_g,
+ * a_u = s_x s_u, a_d = s_h s_d.  GeGLU: gelu_tanh(g) * u; SwiGLU: silu(g) * u;
+ * non-gated GELU: gelu_tanh(u) (no gate projection).
+ *
+ * Conventions:
+ *   - bf16 tensors are row-major uint16 bit patterns, E4M3 tensors are
+ *     row-major bytes (OCP E4M3FN: bias 7, max 448, saturating quantisers).
+ *   - Weights are passed in nn.Linear layout [out, in], bf16.
+ *   - Every pointer argument marked "device" must point to device memory of
+ *     the plan's device; "host" pointers are ordinary host memory.
+ *   - The caller owns all device memory, including the workspace the plan is
+ *     carved from.  The library never calls hipMalloc / hipFree.
+ *   - No function throws; each returns a frt_status.  On failure
+ *     frt_last_error() (thread-local) names the failing check or HIP call.
+ *   - Calls on one plan must not overlap (a plan holds no lock).
+ */
+#ifndef FRT_FFN_H
+#define FRT_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FRT_OK = 0,
+  FRT_ERR_INVALID_ARG = 1, /* bad pointer / dimension / index              */
+  FRT_ERR_HIP = 2,         /* a HIP runtime call failed (named in last_error) */
+  FRT_ERR_STATE = 3,       /* call out of order (e.g. replay before capture) */
+  FRT_ERR_UNSUPPORTED = 4, /* valid but unsupported (e.g. wrong device arch) */
+  FRT_ERR_WORKSPACE = 5    /* workspace too small or misaligned              */
+} frt_status;
+
+typedef enum {
+  FRT_ACT_GEGLU_TANH = 0, /* gelu_tanh(gate) * up            */
+  FRT_ACT_SWIGLU = 1,     /* silu(gate) * up                 */
+  FRT_ACT_GELU_TANH = 2   /* gelu_tanh(up), no gate weights  */
+} frt_act;
+
+/* Problem description.  Requirements: M >= 1, L >= 1, H and I multiples of
+ * 128, H <= 16384, I <= 32768, act in frt_act, eps > 0.  `device` is the HIP
+ * device ordinal the plan and its workspace live on.  `flags` must be 0. */
+typedef struct {
+  int32_t M, H, I, L;
+  int32_t act;
+  float eps;
+  int32_t device;
+  uint32_t flags;
+} frt_ffn_desc;
+
+typedef struct frt_plan frt_plan; /* opaque */
+
+/* Fixed device addresses inside the plan's workspace, valid until
+ * frt_ffn_plan_destroy (the architecture doc's slot pointers that stay stable
+ * across capture and replay).  Slot i of a per-layer array starts at
+ * base + i * stride bytes. */
+typedef struct {
+  void *r_slots;  /* bf16 [L+1][M][H]: R[0] (input) .. R[L]       */
+  void *y_slots;  /* bf16 [L+1][M][H]: Y[0] (input) .. Y[L]       */
+  void *xq_slots; /* e4m3 [L][M][H]:   XQ[0] .. XQ[L-1]           */
+  void *hq_slots; /* e4m3 [L][M][I]:   HQ[0] .. HQ[L-1]           */
+  void *z_out;    /* bf16 [M][H]:      Z = bf16(R[L] + Y[L])      */
+  size_t stride_rh;  /* bytes between R (and Y) slots = M*H*2      */
+  size_t stride_xq;  /* bytes between XQ slots = M*H              */
+  size_t stride_hq;  /* bytes between HQ slots = M*I              */
+} frt_ffn_io;
+
+/* Workspace bytes a plan for `desc` needs (weights, slots, split-K partials,
+ * counters, calibration scratch).  Fails with FRT_ERR_INVALID_ARG on a bad
+ * desc.  Pure host computation. */
+frt_status frt_ffn_workspace_size(const frt_ffn_desc *desc, size_t *bytes);
+
+/* Create a plan over a caller-owned device workspace of at least
+ * frt_ffn_workspace_size bytes, 256-byte aligned, on desc->device.  Zeroes
+ * the plan's counters and slot Y[0] on the null stream and synchronises.
+ * Checks that the device is gfx950 (FRT_ERR_UNSUPPORTED otherwise).
+ * *out receives the plan (host memory owned by the library). */
+frt_status frt_ffn_plan_create(const frt_ffn_desc *desc, void *d_workspace, size_t bytes,
+                               frt_plan **out);
+
+/* Destroy a plan (and its captured graph).  The workspace stays the
+ * caller's.  NULL is accepted. */
+frt_status frt_ffn_plan_destroy(frt_plan *plan);
+
+/* Quantise one layer's weights into the plan (architecture doc, component
+ * "Weights": transpose/Quant transforms with per-tensor scales collected in a
+ * table; itsolotime article section 5.2: FusedGateUp).  Per tensor T:
+ * s = amax(|T|) > 0 ? f32(amax/448) : 1, code = e4m3(f32(T * f32(1/s))).
+ *   d_w_gate  device bf16 [I,H] (must be NULL for FRT_ACT_GELU_TANH)
+ *   d_w_up    device bf16 [I,H]
+ *   d_w_down  device bf16 [H,I]
+ *   d_norm_w  device bf16 [H] RMSNorm weight (copied into the plan)
+ * Runs on `stream` and synchronises it (the scales are host scalars).  The
+ * caller may free the bf16 inputs after return.  Marks a captured graph
+ * stale. */
+frt_status frt_quant_weights(frt_plan *plan, int32_t layer, const void *d_w_gate,
+                             const void *d_w_up, const void *d_w_down, const void *d_norm_w,
+                             void *stream);
+
+/* Copy one layer's quantised weight codes out in canonical nn.Linear layout
+ * (which: 0 gate [I,H], 1 up [I,H], 2 down [H,I]) into host memory of
+ * I*H bytes.  Synchronous. */
+frt_status frt_export_weight_codes(const frt_plan *plan, int32_t layer, int32_t which,
+                                   void *host_dst);
+
+/* Calibration measurement pass (architecture doc, component "Calibration",
+ * phase (a); the predict() flow's cache-miss path "run 1 fwd, record amax").
+ * Runs the chain with unquantised fp32 activations and the quantised weights
+ * (codes times their scale) over `nbatch` batches of `rows` (1..M) rows and
+ * records per layer amax(|x|) (gate/up input) and amax(|h|) (down input)
+ * over all batches; sets s_x = f32(amax_x/448), s_h = f32(amax_h/448)
+ * (1 when amax is 0).
+ *   d_r_batches  host array of nbatch device pointers, bf16 [rows][H]
+ *   d_y_batches  host array of nbatch device pointers (bf16 [rows][H]) or
+ *                NULL for zero previous outputs
+ * All weights must be set.  Synchronises `stream`.  Marks a captured graph
+ * stale. */
+frt_status frt_calibrate(frt_plan *plan, const void *const *d_r_batches,
+                         const void *const *d_y_batches, int32_t nbatch, int32_t rows,
+                         void *stream);
+
+/* Read all per-layer scales into host memory as float[L][5] =
+ * {s_x, s_g, s_u, s_h, s_d} (s_g = 1 for the non-gated activation; s_x, s_h
+ * are 0 until calibrated or set). */
+frt_status frt_get_scales(const frt_plan *plan, float *host_out);
+
+/* Install static activation scales float[L][2] = {s_x, s_h} from host memory
+ * (the calibration cache-hit path: "load JSON, bake alpha").  Every value
+ * must be finite and > 0.  Marks a captured graph stale. */
+frt_status frt_set_act_scales(frt_plan *plan, const float *host_in);
+
+/* Fixed device addresses of the plan's activation slots. */
+frt_status frt_ffn_io_get(const frt_plan *plan, frt_ffn_io *out);
+
+/* Eager forward of layers [layer_begin, layer_end) on `stream`: reads slots
+ * R[layer_begin], Y[layer_begin], writes the later slots; when layer_end == L
+ * also writes Z.  Asynchronous: no allocation, no host synchronisation.
+ * Requires all weights and activation scales (FRT_ERR_STATE otherwise). */
+frt_status frt_ffn_forward_range(frt_plan *plan, int32_t layer_begin, int32_t layer_end,
+                                 void *stream);
+
+/* Eager forward of the whole chain: frt_ffn_forward_range(plan, 0, L). */
+frt_status frt_ffn_forward(frt_plan *plan, void *stream);
+
+/* Capture the whole-chain forward on `stream` (not the null stream) in
+ * relaxed stream-capture mode and instantiate it; replaces an earlier graph.
+ * The scales and pointers in force are baked into the graph. */
+frt_status frt_graph_capture(frt_plan *plan, void *stream);
+
+/* Launch the captured graph on `stream`.  FRT_ERR_STATE if nothing was
+ * captured ("No graph captured") or the graph is stale (weights or scales
+ * changed after capture).  Asynchronous; the caller synchronises. */
+frt_status frt_graph_replay(frt_plan *plan, void *stream);
+
+/* Device E4M3 quantiser as used by every kernel: out[i] = e4m3(in[i]) with
+ * saturation to +-448 and round-to-nearest-even.  d_in device float[n],
+ * d_out device uint8[n].  Asynchronous on `stream`.  For tests of the
+ * conversion. */
+frt_status frt_e4m3_encode_f32(const void *d_in, void *d_out, int64_t n, void *stream);
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char *frt_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FRT_FFN_H */

@@ -1,0 +1,136 @@
+// frt_device.h -- device-side helpers shared by the gfx950 kernels of libfrt.
+//
+// Number formats (FlashRT pages: itsolotime article, section 7.1, FP8 E4M3;
+// section 7.2, high-precision residual stream):
+//   bf16  : uint16 bit pattern, widened exactly to fp32, narrowed by
+//           round-to-nearest-even (inputs are never NaN on this path).
+//   E4M3  : OCP E4M3FN byte.  The quantiser clamps to +-448 first and then
+//           uses the hardware converter, which rounds to nearest even; on
+//           gfx950 the converter alone turns |v| > 464 into NaN, so the clamp
+//           is what makes it saturate.
+//
+// Packed weight layout (written by the weight quantiser, read by the GEMV,
+// GEMM and calibration kernels).  A weight matrix W[N][K] (nn.Linear
+// [out, in]) is cut into blocks of 16 rows x 128 columns; block (g, kb) is
+// 2048 contiguous bytes at ((g * K/128) + kb) * 2048.  Inside a block, lane
+// l (0..63) of a wave owns row g*16 + l%16 and columns kb*128 + (l/16)*32 +
+// [0, 32); its 32 bytes sit as two 16-byte halves at offsets l*16 (columns
+// +0..15) and 1024 + l*16 (columns +16..31).  This is the operand fragment
+// of a 16-row MFMA tile, so one 16-byte load per lane reads 1 KiB
+// contiguously.  For the gated activations the packed matrix is [2I][K] with
+// 16-row groups alternating gate (even group) and up (odd group):
+// packed row 32*(i/16) + i%16 is gate row i, 32*(i/16) + 16 + i%16 is up
+// row i.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace frt {
+
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+constexpr float kE4M3Max = 448.0f;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ float clamp_e4m3(float v) {
+  return __builtin_fminf(__builtin_fmaxf(v, -kE4M3Max), kE4M3Max);
+}
+
+// four fp32 -> four E4M3 bytes (byte i = value i), saturating, RNE
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  int p = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_e4m3(a), clamp_e4m3(b), 0, false);
+  p = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_e4m3(c), clamp_e4m3(d), p, true);
+  return (uint32_t)p;
+}
+__device__ __forceinline__ uint32_t e4m3x1(float a) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp_e4m3(a), 0.0f, 0, false) & 0xffu;
+}
+
+// E4M3 bytes -> fp32 (exact)
+template <bool HI>
+__device__ __forceinline__ v2f e4m3x2_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+}
+__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8((int)byte, false)[0];
+}
+
+// E4M3 bytes -> f16 (exact: every E4M3 value is an f16 value)
+template <bool HI>
+__device__ __forceinline__ v2h e4m3x2_to_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, HI);
+}
+// 8 E4M3 bytes (two dwords) -> 8 f16
+__device__ __forceinline__ v8h e4m3x8_to_f16(uint32_t w0, uint32_t w1) {
+  v2h a = e4m3x2_to_f16<false>(w0), b = e4m3x2_to_f16<true>(w0);
+  v2h c = e4m3x2_to_f16<false>(w1), d = e4m3x2_to_f16<true>(w1);
+  v8h r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// Byte offset of element (n, k) of a packed [N][K] weight (K % 128 == 0).
+__host__ __device__ __forceinline__ size_t packed_offset(uint32_t n, uint32_t k, uint32_t K) {
+  uint32_t g = n >> 4, kb = k >> 7, lane = (n & 15u) + 16u * ((k & 127u) >> 5);
+  uint32_t half = (k & 31u) >> 4;
+  return ((size_t)g * (K >> 7) + kb) * 2048u + half * 1024u + lane * 16u + (k & 15u);
+}
+
+// Packed row of gate row i / up row i in the gated [2I][K] matrix.
+__host__ __device__ __forceinline__ uint32_t gate_row(uint32_t i) { return 32u * (i >> 4) + (i & 15u); }
+__host__ __device__ __forceinline__ uint32_t up_row_gated(uint32_t i) {
+  return 32u * (i >> 4) + 16u + (i & 15u);
+}
+
+// Activations in fp32, written from their definitions:
+//   tanh-GELU(z) = 0.5 z (1 + tanh(c (z + 0.044715 z^3))), c = sqrt(2/pi),
+//                = z * sigmoid(2 c (z + 0.044715 z^3))
+//   SiLU(z)      = z * sigmoid(z)
+// sigmoid(t) = 1 / (1 + exp(-t)) with the device library's expf; for
+// t < -88 exp overflows to +inf and the quotient is 0, the correct limit.
+__device__ __forceinline__ float sigmoid_f32(float t) { return 1.0f / (1.0f + expf(-t)); }
+__device__ __forceinline__ float gelu_tanh_f32(float z) {
+  const float c2 = 1.5957691216057308f;  // 2 * sqrt(2/pi)
+  float inner = z * (1.0f + 0.044715f * z * z);
+  return z * sigmoid_f32(c2 * inner);
+}
+__device__ __forceinline__ float silu_f32(float z) { return z * sigmoid_f32(z); }
+
+// wave64 reductions
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// max of non-negative floats through their bit patterns (monotone for >= 0)
+__device__ __forceinline__ void atomic_max_nonneg(float* addr, float v) {
+  atomicMax(reinterpret_cast<unsigned int*>(addr), __float_as_uint(v));
+}
+
+}  // namespace frt

@@ -1,0 +1,570 @@
+// frt_ffn.hip -- host side of the C ABI declared in include/frt_ffn.h.
+//
+// FlashRT architecture doc: the layer diagram's "C ABI execution contract:
+// Buffer / Graph / Plan, replay-time mechanism for native hosts";
+// component "CUDA Graph": the captured forward takes only device pointers,
+// allocates nothing during replay and lives for the process lifetime;
+// itsolotime article, section 4.1: capture in relaxed mode (only this
+// stream), every runtime call checked by name, replay without a captured
+// graph is an error; section 4.2: all intermediates preallocated, the
+// forward passes raw pointers, shapes are stable.
+//
+// The plan never allocates device memory: every buffer is carved out of the
+// caller's workspace at plan creation.  The only host allocations are the
+// plan object and the temporary host buffer of frt_export_weight_codes.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/frt_ffn.h"
+#include "frt_device.h"
+
+namespace frt {
+hipError_t launch_add_rmsnorm_quant(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*,
+                                    uint8_t*, int, int, float, float, hipStream_t);
+hipError_t launch_add_rmsnorm_measure(const uint16_t*, const uint16_t*, const uint16_t*,
+                                      uint16_t*, float*, float*, int, int, float, hipStream_t);
+hipError_t launch_residual_add(const uint16_t*, const uint16_t*, uint16_t*, size_t, hipStream_t);
+hipError_t launch_e4m3_encode(const float*, uint8_t*, int64_t, hipStream_t);
+hipError_t launch_amax_bf16(const uint16_t*, size_t, float*, hipStream_t);
+hipError_t launch_quant_pack(const uint16_t*, uint8_t*, int, int, float, int, hipStream_t);
+hipError_t launch_gemv_gateup(int, const uint8_t*, const uint8_t*, uint8_t*, float*, uint32_t*,
+                              int, int, int, int, float, float, float, hipStream_t);
+hipError_t launch_gemv_down(const uint8_t*, const uint8_t*, uint16_t*, float*, uint32_t*, int,
+                            int, int, int, float, hipStream_t);
+hipError_t launch_gemm_gateup(int, const uint8_t*, const uint8_t*, uint8_t*, int, int, int, float,
+                              float, float, hipStream_t);
+hipError_t launch_gemm_down(const uint8_t*, const uint8_t*, uint16_t*, float*, uint32_t*, int,
+                            int, int, int, float, hipStream_t);
+hipError_t launch_calib_gateup(int, const float*, const uint8_t*, float*, float*, int, int, int,
+                               float, float, hipStream_t);
+hipError_t launch_calib_down(const float*, const uint8_t*, uint16_t*, int, int, int, float,
+                             hipStream_t);
+}  // namespace frt
+
+using namespace frt;
+
+// ---------------------------------------------------------------------------
+// errors
+// ---------------------------------------------------------------------------
+
+static thread_local std::string g_last_error;
+
+static frt_status fail(frt_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+#define HIP_CHECK(call)                                                                    \
+  do {                                                                                     \
+    hipError_t e_ = (call);                                                                \
+    if (e_ != hipSuccess) return fail(FRT_ERR_HIP, "%s failed: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+#define KERNEL_CHECK(call, name)                                                           \
+  do {                                                                                     \
+    hipError_t e_ = (call);                                                                \
+    if (e_ != hipSuccess) return fail(FRT_ERR_HIP, "launch of %s failed: %s", name, hipGetErrorString(e_)); \
+  } while (0)
+
+// Keep the plan's device current for the duration of a call, then restore.
+struct DeviceGuard {
+  int prev = -1;
+  hipError_t err = hipSuccess;
+  explicit DeviceGuard(int dev) {
+    err = hipGetDevice(&prev);
+    if (err == hipSuccess && prev != dev) err = hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// plan and workspace layout
+// ---------------------------------------------------------------------------
+
+namespace {
+
+constexpr int kGemvMaxM = 16;
+constexpr int kTargetWaves = 4096;  // split-K target for the GEMV path: ~4 waves per SIMD
+
+struct Layout {
+  size_t wgu, wgu_layer;  // packed gate/up (or up) weights, per-layer stride
+  size_t wd, wd_layer;    // packed down weights
+  size_t wn;              // norm weights [L][H] bf16
+  size_t r, y, xq, hq, z; // activation slots
+  size_t part, part_bytes;
+  size_t cnt, cnt_words;  // 2 regions of cnt_words uint32
+  size_t amax;            // [2 + 2L] floats
+  size_t cal_x, cal_h, cal_r, cal_y;
+  size_t total;
+  int s_gu, s_dn;  // split counts (GEMV: per wave; GEMM: down only)
+};
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+bool desc_ok(const frt_ffn_desc* d) {
+  if (!d) return false;
+  if (d->M < 1 || d->L < 1 || d->H < 128 || d->I < 128) return false;
+  if (d->H % 128 || d->I % 128) return false;
+  if (d->H > 16384 || d->I > 32768) return false;
+  if (d->act < FRT_ACT_GEGLU_TANH || d->act > FRT_ACT_GELU_TANH) return false;
+  if (!(d->eps > 0.0f) || !std::isfinite(d->eps)) return false;
+  if (d->flags != 0u || d->device < 0) return false;
+  if ((int64_t)d->M * d->I > (int64_t)1 << 31) return false;
+  return true;
+}
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+Layout make_layout(const frt_ffn_desc& d) {
+  Layout lo{};
+  const size_t M = d.M, H = d.H, I = d.I, L = d.L;
+  const bool gated = d.act != FRT_ACT_GELU_TANH;
+  const size_t npk = gated ? 2 * I : I;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  lo.wgu_layer = align256(npk * H);
+  lo.wgu = take(lo.wgu_layer * L);
+  lo.wd_layer = align256(H * I);
+  lo.wd = take(lo.wd_layer * L);
+  lo.wn = take(L * H * 2);
+  lo.r = take((L + 1) * M * H * 2);
+  lo.y = take((L + 1) * M * H * 2);
+  lo.xq = take(L * M * H);
+  lo.hq = take(L * M * I);
+  lo.z = take(M * H * 2);
+
+  size_t part = 0, words = 1;
+  if (d.M <= kGemvMaxM) {
+    const int pg = (int)(I / 16), pd = (int)(H / 16);
+    const int kb_g = (int)(H / 128), kb_d = (int)(I / 128);
+    lo.s_gu = std::min(std::max(1, ceil_div(kTargetWaves, pg)), kb_g);
+    lo.s_dn = std::min(std::max(1, ceil_div(kTargetWaves, pd)), kb_d);
+    part = std::max((size_t)pg * lo.s_gu * 2 * 16 * M, (size_t)pd * lo.s_dn * 16 * M) * 4;
+    words = (size_t)std::max(pg, pd);
+  } else {
+    const int tiles = (int)(H / 128) * ceil_div(d.M, 128);
+    const int kb_d = (int)(I / 128);
+    int s = std::max(1, ceil_div(512, tiles));
+    s = std::min(s, 16);
+    s = std::min(s, std::max(1, kb_d / 2));
+    lo.s_gu = 1;
+    lo.s_dn = s;
+    part = s > 1 ? (size_t)s * M * H * 4 : 4;
+    words = (size_t)tiles;
+  }
+  lo.part = take(part);
+  lo.part_bytes = part;
+  lo.cnt_words = words;
+  lo.cnt = take(2 * words * 4);
+  lo.amax = take((2 + 2 * L) * 4);
+  lo.cal_x = take(M * H * 4);
+  lo.cal_h = take(M * I * 4);
+  lo.cal_r = take(2 * M * H * 2);
+  lo.cal_y = take(2 * M * H * 2);
+  lo.total = off;
+  return lo;
+}
+
+}  // namespace
+
+struct frt_plan {
+  frt_ffn_desc d{};
+  Layout lo{};
+  uint8_t* ws = nullptr;
+  bool gated = true;
+  std::vector<uint8_t> w_set;
+  std::vector<float> s_x, s_g, s_u, s_h, s_d;
+  bool act_scales_set = false;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  bool captured = false, stale = false;
+
+  uint8_t* wgu(int l) const { return ws + lo.wgu + (size_t)l * lo.wgu_layer; }
+  uint8_t* wd(int l) const { return ws + lo.wd + (size_t)l * lo.wd_layer; }
+  uint16_t* wn(int l) const { return reinterpret_cast<uint16_t*>(ws + lo.wn) + (size_t)l * d.H; }
+  size_t mh() const { return (size_t)d.M * d.H; }
+  uint16_t* r(int l) const { return reinterpret_cast<uint16_t*>(ws + lo.r) + (size_t)l * mh(); }
+  uint16_t* y(int l) const { return reinterpret_cast<uint16_t*>(ws + lo.y) + (size_t)l * mh(); }
+  uint8_t* xq(int l) const { return ws + lo.xq + (size_t)l * mh(); }
+  uint8_t* hq(int l) const { return ws + lo.hq + (size_t)l * d.M * d.I; }
+  uint16_t* z() const { return reinterpret_cast<uint16_t*>(ws + lo.z); }
+  float* part() const { return reinterpret_cast<float*>(ws + lo.part); }
+  uint32_t* cnt(int region) const {
+    return reinterpret_cast<uint32_t*>(ws + lo.cnt) + (size_t)region * lo.cnt_words;
+  }
+  float* amax() const { return reinterpret_cast<float*>(ws + lo.amax); }
+  bool all_weights() const {
+    for (auto v : w_set)
+      if (!v) return false;
+    return true;
+  }
+  void drop_graph() {
+    if (exec) (void)hipGraphExecDestroy(exec);
+    if (graph) (void)hipGraphDestroy(graph);
+    exec = nullptr;
+    graph = nullptr;
+    captured = false;
+    stale = false;
+  }
+  void mark_stale() {
+    if (captured) stale = true;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// exported entry points
+// ---------------------------------------------------------------------------
+
+extern "C" {
+
+const char* frt_last_error(void) { return g_last_error.c_str(); }
+
+frt_status frt_ffn_workspace_size(const frt_ffn_desc* desc, size_t* bytes) {
+  if (!bytes) return fail(FRT_ERR_INVALID_ARG, "frt_ffn_workspace_size: bytes is NULL");
+  if (!desc_ok(desc)) return fail(FRT_ERR_INVALID_ARG, "frt_ffn_workspace_size: invalid descriptor");
+  *bytes = make_layout(*desc).total;
+  return FRT_OK;
+}
+
+frt_status frt_ffn_plan_create(const frt_ffn_desc* desc, void* d_workspace, size_t bytes,
+                               frt_plan** out) {
+  if (!out) return fail(FRT_ERR_INVALID_ARG, "frt_ffn_plan_create: out is NULL");
+  *out = nullptr;
+  if (!desc_ok(desc)) return fail(FRT_ERR_INVALID_ARG, "frt_ffn_plan_create: invalid descriptor");
+  if (!d_workspace) return fail(FRT_ERR_INVALID_ARG, "frt_ffn_plan_create: workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(d_workspace) % 256)
+    return fail(FRT_ERR_WORKSPACE, "frt_ffn_plan_create: workspace not 256-byte aligned");
+  Layout lo = make_layout(*desc);
+  if (bytes < lo.total)
+    return fail(FRT_ERR_WORKSPACE, "frt_ffn_plan_create: workspace %zu bytes < %zu needed", bytes,
+                lo.total);
+  int ndev = 0;
+  HIP_CHECK(hipGetDeviceCount(&ndev));
+  if (desc->device >= ndev)
+    return fail(FRT_ERR_INVALID_ARG, "frt_ffn_plan_create: device %d of %d", desc->device, ndev);
+  DeviceGuard g(desc->device);
+  HIP_CHECK(g.err);
+  hipDeviceProp_t prop;
+  HIP_CHECK(hipGetDeviceProperties(&prop, desc->device));
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(FRT_ERR_UNSUPPORTED, "frt_ffn_plan_create: device is %s, need gfx950",
+                prop.gcnArchName);
+  hipPointerAttribute_t attr;
+  HIP_CHECK(hipPointerGetAttributes(&attr, d_workspace));
+  if (attr.type != hipMemoryTypeDevice || attr.device != desc->device)
+    return fail(FRT_ERR_INVALID_ARG, "frt_ffn_plan_create: workspace is not device memory of device %d",
+                desc->device);
+
+  frt_plan* p = new (std::nothrow) frt_plan();
+  if (!p) return fail(FRT_ERR_INVALID_ARG, "frt_ffn_plan_create: out of host memory");
+  p->d = *desc;
+  p->lo = lo;
+  p->ws = static_cast<uint8_t*>(d_workspace);
+  p->gated = desc->act != FRT_ACT_GELU_TANH;
+  p->w_set.assign(desc->L, 0);
+  p->s_x.assign(desc->L, 0.0f);
+  p->s_h.assign(desc->L, 0.0f);
+  p->s_g.assign(desc->L, 1.0f);
+  p->s_u.assign(desc->L, 1.0f);
+  p->s_d.assign(desc->L, 1.0f);
+  hipError_t e = hipMemset(p->ws + lo.cnt, 0, 2 * lo.cnt_words * 4);
+  if (e == hipSuccess) e = hipMemset(p->y(0), 0, p->mh() * 2);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    delete p;
+    return fail(FRT_ERR_HIP, "frt_ffn_plan_create: clearing counters failed: %s", hipGetErrorString(e));
+  }
+  *out = p;
+  return FRT_OK;
+}
+
+frt_status frt_ffn_plan_destroy(frt_plan* plan) {
+  if (!plan) return FRT_OK;
+  {
+    DeviceGuard g(plan->d.device);
+    plan->drop_graph();
+  }
+  delete plan;
+  return FRT_OK;
+}
+
+static frt_status quant_one(frt_plan* p, const void* src, int N, int K, uint8_t* dst, int mode,
+                            float* scale_out, hipStream_t s) {
+  float* am = p->amax();
+  float amax_h = 0.0f;
+  HIP_CHECK(hipMemsetAsync(am, 0, sizeof(float), s));
+  KERNEL_CHECK(launch_amax_bf16(static_cast<const uint16_t*>(src), (size_t)N * K, am, s), "amax_bf16");
+  HIP_CHECK(hipMemcpyAsync(&amax_h, am, sizeof(float), hipMemcpyDeviceToHost, s));
+  HIP_CHECK(hipStreamSynchronize(s));
+  if (!std::isfinite(amax_h))
+    return fail(FRT_ERR_INVALID_ARG, "frt_quant_weights: weight tensor holds a non-finite value");
+  const float sc = amax_h > 0.0f ? amax_h / 448.0f : 1.0f;
+  const float inv = 1.0f / sc;
+  KERNEL_CHECK(launch_quant_pack(static_cast<const uint16_t*>(src), dst, N, K, inv, mode, s),
+               "quant_pack");
+  *scale_out = sc;
+  return FRT_OK;
+}
+
+frt_status frt_quant_weights(frt_plan* p, int32_t layer, const void* d_w_gate, const void* d_w_up,
+                             const void* d_w_down, const void* d_norm_w, void* stream) {
+  if (!p) return fail(FRT_ERR_INVALID_ARG, "frt_quant_weights: plan is NULL");
+  if (layer < 0 || layer >= p->d.L) return fail(FRT_ERR_INVALID_ARG, "frt_quant_weights: layer %d out of range", layer);
+  if (!d_w_up || !d_w_down || !d_norm_w)
+    return fail(FRT_ERR_INVALID_ARG, "frt_quant_weights: NULL weight pointer");
+  if (p->gated != (d_w_gate != nullptr))
+    return fail(FRT_ERR_INVALID_ARG, "frt_quant_weights: gate weight must be %s for this activation",
+                p->gated ? "given" : "NULL");
+  DeviceGuard g(p->d.device);
+  HIP_CHECK(g.err);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int H = p->d.H, I = p->d.I;
+  float sg = 1.0f, su = 1.0f, sd = 1.0f;
+  frt_status st;
+  if (p->gated) {
+    if ((st = quant_one(p, d_w_gate, I, H, p->wgu(layer), 1, &sg, s)) != FRT_OK) return st;
+    if ((st = quant_one(p, d_w_up, I, H, p->wgu(layer), 2, &su, s)) != FRT_OK) return st;
+  } else {
+    if ((st = quant_one(p, d_w_up, I, H, p->wgu(layer), 0, &su, s)) != FRT_OK) return st;
+  }
+  if ((st = quant_one(p, d_w_down, H, I, p->wd(layer), 0, &sd, s)) != FRT_OK) return st;
+  HIP_CHECK(hipMemcpyAsync(p->wn(layer), d_norm_w, (size_t)H * 2, hipMemcpyDeviceToDevice, s));
+  HIP_CHECK(hipStreamSynchronize(s));
+  p->s_g[layer] = sg;
+  p->s_u[layer] = su;
+  p->s_d[layer] = sd;
+  p->w_set[layer] = 1;
+  p->mark_stale();
+  return FRT_OK;
+}
+
+frt_status frt_export_weight_codes(const frt_plan* p, int32_t layer, int32_t which, void* host_dst) {
+  if (!p || !host_dst) return fail(FRT_ERR_INVALID_ARG, "frt_export_weight_codes: NULL argument");
+  if (layer < 0 || layer >= p->d.L) return fail(FRT_ERR_INVALID_ARG, "frt_export_weight_codes: layer out of range");
+  if (which < 0 || which > 2 || (which == 0 && !p->gated))
+    return fail(FRT_ERR_INVALID_ARG, "frt_export_weight_codes: bad tensor index %d", which);
+  if (!p->w_set[layer]) return fail(FRT_ERR_STATE, "frt_export_weight_codes: layer %d not quantised", layer);
+  DeviceGuard g(p->d.device);
+  HIP_CHECK(g.err);
+  const uint32_t H = p->d.H, I = p->d.I;
+  const bool down = which == 2;
+  const uint32_t N = down ? H : I, K = down ? I : H;
+  const uint32_t rows_packed = down ? H : (p->gated ? 2 * I : I);
+  const size_t bytes = (size_t)rows_packed * K;
+  std::vector<uint8_t> tmp;
+  try {
+    tmp.resize(bytes);
+  } catch (...) {
+    return fail(FRT_ERR_INVALID_ARG, "frt_export_weight_codes: out of host memory");
+  }
+  HIP_CHECK(hipMemcpy(tmp.data(), down ? p->wd(layer) : p->wgu(layer), bytes, hipMemcpyDeviceToHost));
+  uint8_t* dst = static_cast<uint8_t*>(host_dst);
+  for (uint32_t n = 0; n < N; ++n) {
+    uint32_t prow = n;
+    if (!down && p->gated) prow = which == 0 ? gate_row(n) : up_row_gated(n);
+    for (uint32_t k = 0; k < K; k += 16)
+      memcpy(dst + (size_t)n * K + k, tmp.data() + packed_offset(prow, k, K), 16);
+  }
+  return FRT_OK;
+}
+
+frt_status frt_calibrate(frt_plan* p, const void* const* d_r_batches, const void* const* d_y_batches,
+                         int32_t nbatch, int32_t rows, void* stream) {
+  if (!p || !d_r_batches) return fail(FRT_ERR_INVALID_ARG, "frt_calibrate: NULL argument");
+  if (nbatch < 1 || rows < 1 || rows > p->d.M)
+    return fail(FRT_ERR_INVALID_ARG, "frt_calibrate: nbatch %d rows %d (1..%d)", nbatch, rows, p->d.M);
+  for (int b = 0; b < nbatch; ++b)
+    if (!d_r_batches[b]) return fail(FRT_ERR_INVALID_ARG, "frt_calibrate: batch %d residual is NULL", b);
+  if (!p->all_weights()) return fail(FRT_ERR_STATE, "frt_calibrate: weights not set for every layer");
+  DeviceGuard g(p->d.device);
+  HIP_CHECK(g.err);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int L = p->d.L, H = p->d.H, I = p->d.I;
+  float* am = p->amax() + 2;  // [L] x, then [L] h
+  HIP_CHECK(hipMemsetAsync(am, 0, sizeof(float) * 2 * L, s));
+  float* x = reinterpret_cast<float*>(p->ws + p->lo.cal_x);
+  float* h = reinterpret_cast<float*>(p->ws + p->lo.cal_h);
+  uint16_t* cr = reinterpret_cast<uint16_t*>(p->ws + p->lo.cal_r);
+  uint16_t* cy = reinterpret_cast<uint16_t*>(p->ws + p->lo.cal_y);
+  const size_t rh = (size_t)rows * H;
+  for (int b = 0; b < nbatch; ++b) {
+    const uint16_t* r_cur = static_cast<const uint16_t*>(d_r_batches[b]);
+    const uint16_t* y_cur = d_y_batches ? static_cast<const uint16_t*>(d_y_batches[b]) : nullptr;
+    for (int l = 0; l < L; ++l) {
+      uint16_t* r_next = cr + (size_t)(l & 1) * rh;
+      uint16_t* y_next = cy + (size_t)(l & 1) * rh;
+      KERNEL_CHECK(launch_add_rmsnorm_measure(r_cur, y_cur, p->wn(l), r_next, x, am + l, rows, H,
+                                              p->d.eps, s), "add_rmsnorm_measure");
+      KERNEL_CHECK(launch_calib_gateup(p->d.act, x, p->wgu(l), h, am + L + l, rows, H, I,
+                                       p->gated ? p->s_g[l] : p->s_u[l], p->s_u[l], s), "calib_gateup");
+      KERNEL_CHECK(launch_calib_down(h, p->wd(l), y_next, rows, I, H, p->s_d[l], s), "calib_down");
+      r_cur = r_next;
+      y_cur = y_next;
+    }
+  }
+  std::vector<float> hm(2 * L);
+  HIP_CHECK(hipMemcpyAsync(hm.data(), am, sizeof(float) * 2 * L, hipMemcpyDeviceToHost, s));
+  HIP_CHECK(hipStreamSynchronize(s));
+  for (int l = 0; l < L; ++l) {
+    if (!std::isfinite(hm[l]) || !std::isfinite(hm[L + l]))
+      return fail(FRT_ERR_INVALID_ARG, "frt_calibrate: non-finite activation at layer %d", l);
+    p->s_x[l] = hm[l] > 0.0f ? hm[l] / 448.0f : 1.0f;
+    p->s_h[l] = hm[L + l] > 0.0f ? hm[L + l] / 448.0f : 1.0f;
+  }
+  p->act_scales_set = true;
+  p->mark_stale();
+  return FRT_OK;
+}
+
+frt_status frt_get_scales(const frt_plan* p, float* host_out) {
+  if (!p || !host_out) return fail(FRT_ERR_INVALID_ARG, "frt_get_scales: NULL argument");
+  for (int l = 0; l < p->d.L; ++l) {
+    host_out[5 * l + 0] = p->s_x[l];
+    host_out[5 * l + 1] = p->s_g[l];
+    host_out[5 * l + 2] = p->s_u[l];
+    host_out[5 * l + 3] = p->s_h[l];
+    host_out[5 * l + 4] = p->s_d[l];
+  }
+  return FRT_OK;
+}
+
+frt_status frt_set_act_scales(frt_plan* p, const float* host_in) {
+  if (!p || !host_in) return fail(FRT_ERR_INVALID_ARG, "frt_set_act_scales: NULL argument");
+  for (int l = 0; l < 2 * p->d.L; ++l)
+    if (!std::isfinite(host_in[l]) || !(host_in[l] > 0.0f))
+      return fail(FRT_ERR_INVALID_ARG, "frt_set_act_scales: scale %d is not finite and positive", l);
+  for (int l = 0; l < p->d.L; ++l) {
+    p->s_x[l] = host_in[2 * l];
+    p->s_h[l] = host_in[2 * l + 1];
+  }
+  p->act_scales_set = true;
+  p->mark_stale();
+  return FRT_OK;
+}
+
+frt_status frt_ffn_io_get(const frt_plan* p, frt_ffn_io* out) {
+  if (!p || !out) return fail(FRT_ERR_INVALID_ARG, "frt_ffn_io_get: NULL argument");
+  out->r_slots = p->r(0);
+  out->y_slots = p->y(0);
+  out->xq_slots = p->xq(0);
+  out->hq_slots = p->hq(0);
+  out->z_out = p->z();
+  out->stride_rh = p->mh() * 2;
+  out->stride_xq = p->mh();
+  out->stride_hq = (size_t)p->d.M * p->d.I;
+  return FRT_OK;
+}
+
+static frt_status forward_range(frt_plan* p, int lb, int le, hipStream_t s) {
+  const int M = p->d.M, H = p->d.H, I = p->d.I, L = p->d.L;
+  const int npk = p->gated ? 2 * I : I;
+  for (int l = lb; l < le; ++l) {
+    const float s_x = p->s_x[l], s_h = p->s_h[l];
+    const float inv_x = 1.0f / s_x, inv_h = 1.0f / s_h;
+    const float a_g = s_x * p->s_g[l], a_u = s_x * p->s_u[l], a_d = s_h * p->s_d[l];
+    KERNEL_CHECK(launch_add_rmsnorm_quant(p->r(l), p->y(l), p->wn(l), p->r(l + 1), p->xq(l), M, H,
+                                          p->d.eps, inv_x, s), "add_rmsnorm_quant");
+    if (M <= kGemvMaxM) {
+      KERNEL_CHECK(launch_gemv_gateup(p->d.act, p->xq(l), p->wgu(l), p->hq(l), p->part(), p->cnt(0),
+                                      M, H, I, p->lo.s_gu, a_g, a_u, inv_h, s), "gemv_gateup");
+      KERNEL_CHECK(launch_gemv_down(p->hq(l), p->wd(l), p->y(l + 1), p->part(), p->cnt(1), M, I, H,
+                                    p->lo.s_dn, a_d, s), "gemv_down");
+    } else {
+      KERNEL_CHECK(launch_gemm_gateup(p->d.act, p->xq(l), p->wgu(l), p->hq(l), M, H, npk, a_g, a_u,
+                                      inv_h, s), "gemm_gateup");
+      KERNEL_CHECK(launch_gemm_down(p->hq(l), p->wd(l), p->y(l + 1), p->part(), p->cnt(1), M, I, H,
+                                    p->lo.s_dn, a_d, s), "gemm_down");
+    }
+  }
+  if (le == L) KERNEL_CHECK(launch_residual_add(p->r(L), p->y(L), p->z(), p->mh(), s), "residual_add");
+  return FRT_OK;
+}
+
+frt_status frt_ffn_forward_range(frt_plan* p, int32_t layer_begin, int32_t layer_end, void* stream) {
+  if (!p) return fail(FRT_ERR_INVALID_ARG, "frt_ffn_forward_range: plan is NULL");
+  if (layer_begin < 0 || layer_end > p->d.L || layer_begin >= layer_end)
+    return fail(FRT_ERR_INVALID_ARG, "frt_ffn_forward_range: bad range [%d, %d)", layer_begin, layer_end);
+  for (int l = layer_begin; l < layer_end; ++l)
+    if (!p->w_set[l]) return fail(FRT_ERR_STATE, "frt_ffn_forward_range: weights of layer %d not set", l);
+  if (!p->act_scales_set) return fail(FRT_ERR_STATE, "frt_ffn_forward_range: activation scales not set");
+  DeviceGuard g(p->d.device);
+  HIP_CHECK(g.err);
+  return forward_range(p, layer_begin, layer_end, static_cast<hipStream_t>(stream));
+}
+
+frt_status frt_ffn_forward(frt_plan* p, void* stream) {
+  if (!p) return fail(FRT_ERR_INVALID_ARG, "frt_ffn_forward: plan is NULL");
+  return frt_ffn_forward_range(p, 0, p->d.L, stream);
+}
+
+frt_status frt_graph_capture(frt_plan* p, void* stream) {
+  if (!p) return fail(FRT_ERR_INVALID_ARG, "frt_graph_capture: plan is NULL");
+  if (!stream) return fail(FRT_ERR_INVALID_ARG, "frt_graph_capture: the null stream cannot be captured");
+  if (!p->all_weights() || !p->act_scales_set)
+    return fail(FRT_ERR_STATE, "frt_graph_capture: weights and activation scales must be set first");
+  DeviceGuard g(p->d.device);
+  HIP_CHECK(g.err);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  p->drop_graph();
+  HIP_CHECK(hipStreamBeginCapture(s, hipStreamCaptureModeRelaxed));
+  frt_status st = forward_range(p, 0, p->d.L, s);
+  hipGraph_t graph = nullptr;
+  hipError_t e = hipStreamEndCapture(s, &graph);
+  if (st != FRT_OK) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return st;
+  }
+  if (e != hipSuccess) return fail(FRT_ERR_HIP, "hipStreamEndCapture failed: %s", hipGetErrorString(e));
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(graph);
+    return fail(FRT_ERR_HIP, "hipGraphInstantiate failed: %s", hipGetErrorString(e));
+  }
+  p->graph = graph;
+  p->exec = exec;
+  p->captured = true;
+  p->stale = false;
+  return FRT_OK;
+}
+
+frt_status frt_graph_replay(frt_plan* p, void* stream) {
+  if (!p) return fail(FRT_ERR_INVALID_ARG, "frt_graph_replay: plan is NULL");
+  if (!p->captured) return fail(FRT_ERR_STATE, "frt_graph_replay: No graph captured");
+  if (p->stale)
+    return fail(FRT_ERR_STATE, "frt_graph_replay: graph is stale (weights or scales changed); capture again");
+  DeviceGuard g(p->d.device);
+  HIP_CHECK(g.err);
+  HIP_CHECK(hipGraphLaunch(p->exec, static_cast<hipStream_t>(stream)));
+  return FRT_OK;
+}
+
+frt_status frt_e4m3_encode_f32(const void* d_in, void* d_out, int64_t n, void* stream) {
+  if ((!d_in || !d_out) && n > 0) return fail(FRT_ERR_INVALID_ARG, "frt_e4m3_encode_f32: NULL pointer");
+  if (n < 0) return fail(FRT_ERR_INVALID_ARG, "frt_e4m3_encode_f32: negative length");
+  KERNEL_CHECK(launch_e4m3_encode(static_cast<const float*>(d_in), static_cast<uint8_t*>(d_out), n,
+                                  static_cast<hipStream_t>(stream)), "e4m3_encode");
+  return FRT_OK;
+}
+
+}  // extern "C"

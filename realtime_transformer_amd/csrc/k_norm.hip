@@ -1,0 +1,219 @@
+// k_norm.hip -- fused residual add + RMSNorm + per-tensor E4M3 quantise.
+//
+// FlashRT architecture doc, component "Kernel library": hand-written kernels
+// for the memory-bound ops, including residual + norm + quant fusions;
+// itsolotime article, section 3.3: rms_norm(x, w, out, S, D, eps, stream)
+// calling convention; section 7.2: the residual stream stays high precision
+// and the norm output feeds the low-precision GEMMs.
+//
+// Per row (rows are independent):
+//   r'  = bf16(r + y)                       stored as the new residual
+//   S   = sum r'^2 in fp64 (each square is exact in fp64)
+//   inv = f32(1 / sqrt(S / H + eps)) in fp64, rounded once
+//   x   = f32(f32(r' * inv) * w)
+//   xq  = e4m3(f32(x * inv_x))              (measure mode: store x, amax|x|)
+//
+// Bound: HBM.  Algorithmic bytes per row: 2H (r) + 2H (y) + 2H (r') + H (xq),
+// plus 2H once for w.  Layout: TPR threads own one row; each thread holds
+// NC chunks of 8 bf16 (16-byte loads) in registers between the two passes,
+// so r' is read from HBM once.  The fp64 sum of squares is reduced across
+// the wave with shuffles and across the row's waves through LDS.
+#include "frt_device.h"
+
+namespace frt {
+
+template <int TPR, int NC, bool MEASURE>
+__global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
+    const uint16_t* __restrict__ r_prev, const uint16_t* __restrict__ y_prev,
+    const uint16_t* __restrict__ w_norm, uint16_t* __restrict__ r_out,
+    uint8_t* __restrict__ xq_out, float* __restrict__ x_out, float* __restrict__ amax_out,
+    int M, int H, float eps, float inv_x) {
+  constexpr int RPW = 256 / TPR;  // rows per workgroup
+  constexpr int WPR = TPR / 64;   // waves per row
+  __shared__ double red[256 / 64];
+  const int tid = threadIdx.x;
+  const int row_in_wg = tid / TPR;
+  const int t = tid % TPR;
+  const int row = blockIdx.x * RPW + row_in_wg;
+  const bool active = row < M;
+  const int nchunk = H >> 3;
+  const size_t base = (size_t)(active ? row : 0) * (size_t)H;
+
+  uint4 rn[NC];
+  double sq = 0.0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int ch = t + c * TPR;
+    rn[c] = make_uint4(0, 0, 0, 0);
+    if (active && ch < nchunk) {
+      const uint4 rv = *reinterpret_cast<const uint4*>(r_prev + base + (size_t)ch * 8);
+      uint4 yv = make_uint4(0, 0, 0, 0);
+      if (y_prev) yv = *reinterpret_cast<const uint4*>(y_prev + base + (size_t)ch * 8);
+      uint32_t rr[4] = {rv.x, rv.y, rv.z, rv.w};
+      uint32_t yy[4] = {yv.x, yv.y, yv.z, yv.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float lo = bf16_lo(rr[j]) + bf16_lo(yy[j]);
+        float hi = bf16_hi(rr[j]) + bf16_hi(yy[j]);
+        o[j] = pack_bf16x2(lo, hi);
+        double dlo = (double)bf16_lo(o[j]), dhi = (double)bf16_hi(o[j]);
+        sq += dlo * dlo;
+        sq += dhi * dhi;
+      }
+      rn[c] = make_uint4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<uint4*>(r_out + base + (size_t)ch * 8) = rn[c];
+    }
+  }
+  sq = wave_sum_f64(sq);
+  if (WPR > 1) {
+    const int wave = tid >> 6;
+    if ((tid & 63) == 0) red[wave] = sq;
+    __syncthreads();
+    sq = 0.0;
+    const int w0 = row_in_wg * WPR;
+    for (int w = 0; w < WPR; ++w) sq += red[w0 + w];
+  }
+  const float inv_rms = (float)(1.0 / sqrt(sq / (double)H + (double)eps));
+
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int ch = t + c * TPR;
+    if (active && ch < nchunk) {
+      const uint4 wv = *reinterpret_cast<const uint4*>(w_norm + (size_t)ch * 8);
+      uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+      uint32_t rr[4] = {rn[c].x, rn[c].y, rn[c].z, rn[c].w};
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[2 * j] = (bf16_lo(rr[j]) * inv_rms) * bf16_lo(ww[j]);
+        x[2 * j + 1] = (bf16_hi(rr[j]) * inv_rms) * bf16_hi(ww[j]);
+      }
+      if (MEASURE) {
+        float4* dst = reinterpret_cast<float4*>(x_out + base + (size_t)ch * 8);
+        dst[0] = make_float4(x[0], x[1], x[2], x[3]);
+        dst[1] = make_float4(x[4], x[5], x[6], x[7]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[j]));
+      } else {
+        uint2 q;
+        q.x = e4m3x4(x[0] * inv_x, x[1] * inv_x, x[2] * inv_x, x[3] * inv_x);
+        q.y = e4m3x4(x[4] * inv_x, x[5] * inv_x, x[6] * inv_x, x[7] * inv_x);
+        *reinterpret_cast<uint2*>(xq_out + base + (size_t)ch * 8) = q;
+      }
+    }
+  }
+  if (MEASURE) {
+    amax = wave_max_f32(amax);
+    if ((tid & 63) == 0) atomic_max_nonneg(amax_out, amax);
+  }
+}
+
+// Z = bf16(R + Y), the residual add after the last block.
+__global__ __launch_bounds__(256) void k_residual_add(const uint16_t* __restrict__ r,
+                                                      const uint16_t* __restrict__ y,
+                                                      uint16_t* __restrict__ z, size_t n8) {
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  uint4 a = reinterpret_cast<const uint4*>(r)[i];
+  uint4 b = reinterpret_cast<const uint4*>(y)[i];
+  uint32_t aa[4] = {a.x, a.y, a.z, a.w}, bb[4] = {b.x, b.y, b.z, b.w}, o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    o[j] = pack_bf16x2(bf16_lo(aa[j]) + bf16_lo(bb[j]), bf16_hi(aa[j]) + bf16_hi(bb[j]));
+  reinterpret_cast<uint4*>(z)[i] = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Device E4M3 quantiser over an fp32 array (the same conversion every kernel uses).
+__global__ __launch_bounds__(256) void k_e4m3_encode(const float* __restrict__ in,
+                                                     uint8_t* __restrict__ out, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) out[i] = (uint8_t)e4m3x1(in[i]);
+}
+
+// ---------------------------------------------------------------------------
+// host-side launchers
+// ---------------------------------------------------------------------------
+
+template <bool MEASURE>
+static hipError_t launch_norm_t(const uint16_t* r_prev, const uint16_t* y_prev,
+                                const uint16_t* w, uint16_t* r_out, uint8_t* xq, float* x_out,
+                                float* amax, int M, int H, float eps, float inv_x,
+                                hipStream_t s) {
+  const int nchunk = H / 8;
+  // one wave per row when the row fits 8 chunks per lane, else a whole
+  // workgroup per row
+  if (nchunk <= 64 * 8) {
+    const int nc = (nchunk + 63) / 64;
+    dim3 grid((M + 3) / 4);
+    if (nc <= 2)
+      hipLaunchKernelGGL((k_add_rmsnorm_quant<64, 2, MEASURE>), grid, dim3(256), 0, s, r_prev,
+                         y_prev, w, r_out, xq, x_out, amax, M, H, eps, inv_x);
+    else if (nc <= 4)
+      hipLaunchKernelGGL((k_add_rmsnorm_quant<64, 4, MEASURE>), grid, dim3(256), 0, s, r_prev,
+                         y_prev, w, r_out, xq, x_out, amax, M, H, eps, inv_x);
+    else
+      hipLaunchKernelGGL((k_add_rmsnorm_quant<64, 8, MEASURE>), grid, dim3(256), 0, s, r_prev,
+                         y_prev, w, r_out, xq, x_out, amax, M, H, eps, inv_x);
+  } else {
+    const int nc = (nchunk + 255) / 256;
+    dim3 grid(M);
+    if (nc <= 4)
+      hipLaunchKernelGGL((k_add_rmsnorm_quant<256, 4, MEASURE>), grid, dim3(256), 0, s, r_prev,
+                         y_prev, w, r_out, xq, x_out, amax, M, H, eps, inv_x);
+    else
+      hipLaunchKernelGGL((k_add_rmsnorm_quant<256, 8, MEASURE>), grid, dim3(256), 0, s, r_prev,
+                         y_prev, w, r_out, xq, x_out, amax, M, H, eps, inv_x);
+  }
+  return hipGetLastError();
+}
+
+// Small M: spread one row over a whole workgroup so the row's loads are
+// issued by many waves at once (latency, not bandwidth, bounds M <= 64).
+hipError_t launch_add_rmsnorm_quant(const uint16_t* r_prev, const uint16_t* y_prev,
+                                    const uint16_t* w, uint16_t* r_out, uint8_t* xq, int M,
+                                    int H, float eps, float inv_x, hipStream_t s) {
+  const int nchunk = H / 8;
+  if (M <= 64 && nchunk > 64 && nchunk <= 256 * 8) {
+    const int nc = (nchunk + 255) / 256;
+    dim3 grid(M);
+    if (nc <= 1)
+      hipLaunchKernelGGL((k_add_rmsnorm_quant<256, 1, false>), grid, dim3(256), 0, s, r_prev,
+                         y_prev, w, r_out, xq, nullptr, nullptr, M, H, eps, inv_x);
+    else if (nc <= 2)
+      hipLaunchKernelGGL((k_add_rmsnorm_quant<256, 2, false>), grid, dim3(256), 0, s, r_prev,
+                         y_prev, w, r_out, xq, nullptr, nullptr, M, H, eps, inv_x);
+    else if (nc <= 4)
+      hipLaunchKernelGGL((k_add_rmsnorm_quant<256, 4, false>), grid, dim3(256), 0, s, r_prev,
+                         y_prev, w, r_out, xq, nullptr, nullptr, M, H, eps, inv_x);
+    else
+      hipLaunchKernelGGL((k_add_rmsnorm_quant<256, 8, false>), grid, dim3(256), 0, s, r_prev,
+                         y_prev, w, r_out, xq, nullptr, nullptr, M, H, eps, inv_x);
+    return hipGetLastError();
+  }
+  return launch_norm_t<false>(r_prev, y_prev, w, r_out, xq, nullptr, nullptr, M, H, eps, inv_x,
+                              s);
+}
+
+hipError_t launch_add_rmsnorm_measure(const uint16_t* r_prev, const uint16_t* y_prev,
+                                      const uint16_t* w, uint16_t* r_out, float* x_out,
+                                      float* amax, int M, int H, float eps, hipStream_t s) {
+  return launch_norm_t<true>(r_prev, y_prev, w, r_out, nullptr, x_out, amax, M, H, eps, 1.0f, s);
+}
+
+hipError_t launch_residual_add(const uint16_t* r, const uint16_t* y, uint16_t* z, size_t n,
+                               hipStream_t s) {
+  size_t n8 = n / 8;
+  hipLaunchKernelGGL(k_residual_add, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, r, y, z,
+                     n8);
+  return hipGetLastError();
+}
+
+hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_e4m3_encode, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, in, out, n);
+  return hipGetLastError();
+}
+
+}  // namespace frt

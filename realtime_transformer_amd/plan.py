@@ -1,0 +1,153 @@
+"""FFNPlan: a plan over a torch-allocated workspace (memory and streams only).
+
+PyTorch provides the device memory (one uint8 workspace tensor, staging
+tensors for uploads) and the stream; every step of the FFN chain runs in
+libfrt.  Slot accessors return torch views into the workspace at the fixed
+addresses frt_ffn_io_get reports, so reading or writing a slot is a plain
+device copy.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _abi
+
+
+def _require_gpu():
+    if not torch.cuda.is_available():
+        raise _abi.FrtError(_abi.FRT_ERR_UNSUPPORTED, "no HIP device visible")
+
+
+def _to_dev_u16(a: np.ndarray, device) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
+    return t.to(device, non_blocking=False)
+
+
+class FFNPlan:
+    def __init__(self, M: int, H: int, I: int, L: int, act: int, eps: float = 1e-6,
+                 device: int = 0, stream: Optional[torch.cuda.Stream] = None):
+        _require_gpu()
+        _abi.load()
+        self.M, self.H, self.I, self.L, self.act = M, H, I, L, act
+        self.gated = act != _abi.FRT_ACT_GELU_TANH
+        self.device = torch.device("cuda", device)
+        self.desc = _abi.make_desc(M, H, I, L, act, eps, device)
+        self.nbytes = _abi.frt_ffn_workspace_size(self.desc)
+        self.ws = torch.empty(self.nbytes + 256, dtype=torch.uint8, device=self.device)
+        base = self.ws.data_ptr()
+        self._off0 = (-base) % 256
+        self.ws_ptr = base + self._off0
+        self.plan = _abi.frt_ffn_plan_create(self.desc, self.ws_ptr, self.nbytes)
+        self.io = _abi.frt_ffn_io_get(self.plan)
+        self.stream = stream if stream is not None else torch.cuda.Stream(self.device)
+
+    # ---- lifetime ---------------------------------------------------------
+    def close(self):
+        if getattr(self, "plan", None):
+            torch.cuda.synchronize(self.device)
+            _abi.frt_ffn_plan_destroy(self.plan)
+            self.plan = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def s(self) -> int:
+        return self.stream.cuda_stream
+
+    def sync(self):
+        self.stream.synchronize()
+
+    # ---- workspace views --------------------------------------------------
+    def _view(self, ptr: int, nbytes: int) -> torch.Tensor:
+        off = ptr - self.ws.data_ptr()
+        assert 0 <= off and off + nbytes <= self.ws.numel()
+        return self.ws[off:off + nbytes]
+
+    def r_slot(self, l: int) -> torch.Tensor:
+        n = self.M * self.H * 2
+        return self._view(self.io.r_slots + l * self.io.stride_rh, n).view(torch.int16).view(self.M, self.H)
+
+    def y_slot(self, l: int) -> torch.Tensor:
+        n = self.M * self.H * 2
+        return self._view(self.io.y_slots + l * self.io.stride_rh, n).view(torch.int16).view(self.M, self.H)
+
+    def xq_slot(self, l: int) -> torch.Tensor:
+        return self._view(self.io.xq_slots + l * self.io.stride_xq, self.M * self.H).view(self.M, self.H)
+
+    def hq_slot(self, l: int) -> torch.Tensor:
+        return self._view(self.io.hq_slots + l * self.io.stride_hq, self.M * self.I).view(self.M, self.I)
+
+    def z(self) -> torch.Tensor:
+        return self._view(self.io.z_out, self.M * self.H * 2).view(torch.int16).view(self.M, self.H)
+
+    # ---- setup --------------------------------------------------------------
+    def load_layer(self, layer: int, w_gate, w_up, w_down, w_norm):
+        """Upload one layer's bf16 weights (numpy uint16 bit patterns) and quantise them."""
+        tg = _to_dev_u16(w_gate, self.device) if w_gate is not None else None
+        tu = _to_dev_u16(w_up, self.device)
+        td = _to_dev_u16(w_down, self.device)
+        tn = _to_dev_u16(w_norm, self.device)
+        torch.cuda.synchronize(self.device)
+        _abi.frt_quant_weights(self.plan, layer, tg.data_ptr() if tg is not None else None,
+                               tu.data_ptr(), td.data_ptr(), tn.data_ptr(), self.s)
+        del tg, tu, td, tn
+
+    def export_codes(self, layer: int, which: int) -> np.ndarray:
+        rows, cols = (self.H, self.I) if which == 2 else (self.I, self.H)
+        return _abi.frt_export_weight_codes(self.plan, layer, which, rows, cols)
+
+    def scales(self) -> np.ndarray:
+        return _abi.frt_get_scales(self.plan, self.L)
+
+    def set_act_scales(self, s_x: Sequence[float], s_h: Sequence[float]):
+        a = np.stack([np.asarray(s_x, np.float32), np.asarray(s_h, np.float32)], axis=1)
+        _abi.frt_set_act_scales(self.plan, a)
+
+    def calibrate(self, batches, rows: Optional[int] = None):
+        """batches: list of (r, y-or-None) numpy uint16 arrays [rows][H]."""
+        rows = rows if rows is not None else batches[0][0].shape[0]
+        rs = [_to_dev_u16(r, self.device) for r, _ in batches]
+        ys = None
+        if batches[0][1] is not None:
+            ys = [_to_dev_u16(y, self.device) for _, y in batches]
+        torch.cuda.synchronize(self.device)
+        _abi.frt_calibrate(self.plan, [t.data_ptr() for t in rs],
+                           None if ys is None else [t.data_ptr() for t in ys], rows, self.s)
+        del rs, ys
+
+    def set_inputs(self, r0: np.ndarray, y0: Optional[np.ndarray]):
+        with torch.cuda.stream(self.stream):
+            self.r_slot(0).copy_(_to_dev_u16(r0, self.device))
+            if y0 is None:
+                self.y_slot(0).zero_()
+            else:
+                self.y_slot(0).copy_(_to_dev_u16(y0, self.device))
+        self.sync()
+
+    # ---- run ----------------------------------------------------------------
+    def forward(self):
+        _abi.frt_ffn_forward(self.plan, self.s)
+
+    def forward_range(self, lb: int, le: int):
+        _abi.frt_ffn_forward_range(self.plan, lb, le, self.s)
+
+    def capture(self):
+        _abi.frt_graph_capture(self.plan, self.s)
+
+    def replay(self):
+        _abi.frt_graph_replay(self.plan, self.s)
+
+
+def to_np_u16(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
+def to_np_u8(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy()

@@ -1,0 +1,260 @@
+"""Shared GPU-vs-oracle parity procedure for one FFN-chain workload.
+
+Direction of data: seeded inputs (datagen) feed both sides; the oracle runs
+its own chain from them; its per-layer states are written INTO the GPU's
+slots for the teacher-forced per-block checks.  Nothing read back from the
+GPU is ever given to the oracle.
+
+Checks (tolerances from the workload statement; C-19 reading for HQ):
+  weights   GPU codes and scales equal the oracle's bit for bit
+  calib     GPU activation scales within CAL_RTOL of the oracle's (the GPU
+            sums fp32 in its own order, the oracle in fp64)
+  per block (teacher-forced, every checked layer):
+            R  bit-exact
+            XQ adjacent-code mismatches only, rate <= 1e-4
+            HQ adjacent-code mismatches only, rate <= 1e-4
+            Y  max|d|/max|ref| <= 2e-2 and cosine >= 0.999
+  chain     free-running Z cosine >= 0.999 against the oracle's chain
+  graph     replay == eager forward, bit for bit; two replays agree
+  saturation every XQ/HQ code finite (no 0x7f/0xff)
+"""
+from __future__ import annotations
+
+import math
+import time
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+import oracle
+from realtime_transformer_amd import datagen
+from realtime_transformer_amd.configs import FFNConfig
+from realtime_transformer_amd.plan import FFNPlan, to_np_u16, to_np_u8
+
+CODE_RATE = 1e-4
+Y_MAX_REL = 2e-2
+MIN_COS = 0.999
+# Calibration scales: |s_gpu/s_oracle - 1|.  In the first layer both sides
+# see identical inputs and differ only by the GPU's fp32 K-sequential sums
+# against the oracle's fp64 sums (~sqrt(K) * 2^-24 relative, 1e-3 worst
+# case at K = 16384): CAL_RTOL_FIRST.  Deeper layers measure a chain whose
+# bf16 residual and previous output may round the other way in single
+# elements (2^-8 = 0.4% of that element) and propagate; amax over the layer
+# then moves by up to a few of those steps: CAL_RTOL.
+CAL_RTOL_FIRST = 1e-4
+CAL_RTOL = 1e-2
+
+
+def log(msg: str):
+    print(msg, flush=True)
+
+
+def e4m3_rank(codes: np.ndarray) -> np.ndarray:
+    c = codes.astype(np.int32)
+    mag = c & 0x7F
+    return np.where(c & 0x80, -mag, mag)
+
+
+@dataclass
+class CodeStats:
+    n: int
+    mismatches: int
+    max_rank_diff: int
+    near_boundary: int = -1
+
+    @property
+    def rate(self) -> float:
+        return self.mismatches / max(1, self.n)
+
+
+def code_stats(gpu: np.ndarray, ref: np.ndarray, pre: Optional[np.ndarray] = None) -> CodeStats:
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    d = np.abs(e4m3_rank(gpu) - e4m3_rank(ref))
+    bad = d > 0
+    st = CodeStats(int(gpu.size), int(bad.sum()), int(d.max()) if d.size else 0)
+    if pre is not None and st.mismatches:
+        # mismatches whose oracle pre-rounding value lies within 1 fp32 ulp
+        # of the rounding boundary between the two codes
+        v = pre[bad].astype(np.float32)
+        a = oracle.e4m3_decode(gpu[bad])
+        b = oracle.e4m3_decode(ref[bad])
+        mid = (a + b) / 2
+        ulp = np.spacing(np.abs(v)).astype(np.float64)
+        st.near_boundary = int(np.sum(np.abs(v.astype(np.float64) - mid) <= ulp))
+    return st
+
+
+def check_codes(name: str, st: CodeStats):
+    assert st.max_rank_diff <= 1, "%s: non-adjacent code mismatch (%d steps)" % (name, st.max_rank_diff)
+    assert st.rate <= CODE_RATE, "%s: code mismatch rate %.3g > %g (%d/%d)" % (
+        name, st.rate, CODE_RATE, st.mismatches, st.n)
+
+
+def bf16_f64(bits: np.ndarray) -> np.ndarray:
+    return oracle.bf16_to_f32(bits).astype(np.float64)
+
+
+def y_metrics(gpu_bits: np.ndarray, ref_bits: np.ndarray):
+    g = bf16_f64(gpu_bits).ravel()
+    r = bf16_f64(ref_bits).ravel()
+    denom = np.max(np.abs(r))
+    max_rel = float(np.max(np.abs(g - r)) / denom) if denom > 0 else float(np.max(np.abs(g)))
+    ng, nr = np.linalg.norm(g), np.linalg.norm(r)
+    cos = float(g @ r / (ng * nr)) if ng > 0 and nr > 0 else (1.0 if ng == nr else 0.0)
+    return max_rel, cos
+
+
+def check_y(name: str, gpu_bits, ref_bits):
+    max_rel, cos = y_metrics(gpu_bits, ref_bits)
+    assert max_rel <= Y_MAX_REL, "%s: max rel %.4g > %g" % (name, max_rel, Y_MAX_REL)
+    assert cos >= MIN_COS, "%s: cosine %.6f < %g" % (name, cos, MIN_COS)
+    return max_rel, cos
+
+
+@dataclass
+class CaseReport:
+    name: str
+    layers_checked: List[int] = field(default_factory=list)
+    xq_mismatch: int = 0
+    xq_n: int = 0
+    xq_near_boundary: int = 0
+    hq_mismatch: int = 0
+    hq_n: int = 0
+    y_max_rel: float = 0.0
+    y_min_cos: float = 1.0
+    z_cos: float = 1.0
+    z_max_rel: float = 0.0
+    cal_max_rel: float = 0.0
+    saturated_codes: int = 0
+    seconds: float = 0.0
+
+
+def run_case(cfg: FFNConfig, rows: Optional[Sequence[int]] = None, cal_rows: Optional[Sequence[int]] = None,
+             check_layers: Optional[Sequence[int]] = None, nbatch: int = 4) -> CaseReport:
+    """Full parity procedure; rows / cal_rows select the evaluated / calibration
+    rows (None = all); check_layers selects the teacher-forced layers (None = all)."""
+    t0 = time.time()
+    rep = CaseReport(cfg.name)
+    M, H, I, L, act = cfg.M, cfg.H, cfg.I, cfg.L, cfg.act
+    rows = np.arange(M) if rows is None else np.asarray(sorted(rows))
+    r0, y0 = datagen.eval_inputs(cfg)
+    cal = datagen.calib_batches(cfg, nbatch)
+    if cal_rows is not None:
+        cr = np.asarray(sorted(cal_rows))
+        cal = [(r[cr], None if y is None else y[cr]) for r, y in cal]
+    log("[case %s] M=%d H=%d I=%d L=%d act=%d rows=%d cal_rows=%d" % (
+        cfg.name, M, H, I, L, act, len(rows), cal[0][0].shape[0]))
+
+    plan = FFNPlan(M, H, I, L, act, cfg.eps)
+    try:
+        weight_scales = []
+        norm_w = {}
+
+        def provider(l):
+            def get():
+                wg, wu, wd, wn = datagen.layer_weights(cfg, l)
+                plan.load_layer(l, wg, wu, wd, wn)
+                lw = oracle.LayerWeights.quantize(wg, wu, wd, wn)
+                names = ["up", "down"] if wg is None else ["gate", "up", "down"]
+                refs = [lw.qu, lw.qd] if wg is None else [lw.qg, lw.qu, lw.qd]
+                idx = [1, 2] if wg is None else [0, 1, 2]
+                for nm, which, ref in zip(names, idx, refs):
+                    got = plan.export_codes(l, which)
+                    nbad = int(np.count_nonzero(got != ref))
+                    assert nbad == 0, "layer %d %s weight codes: %d mismatches" % (l, nm, nbad)
+                weight_scales.append((lw.s_g, lw.s_u, lw.s_d))
+                norm_w[l] = wn
+                return lw
+            return get
+
+        orc = oracle.calibrate_and_run((provider(l) for l in range(L)), act, cfg.eps,
+                                       r0[rows], None if y0 is None else y0[rows], cal)
+        log("[case %s] weights bit-exact; oracle chain done (%.1fs)" % (cfg.name, time.time() - t0))
+
+        sc = plan.scales()
+        for l in range(L):
+            sg, su, sd = weight_scales[l]
+            assert (sc[l, 1], sc[l, 2], sc[l, 4]) == (np.float32(sg), np.float32(su), np.float32(sd)), \
+                "layer %d weight scales differ: gpu %s oracle %s" % (l, sc[l], weight_scales[l])
+
+        # calibration on the GPU over the same batches, compared with the oracle
+        plan.calibrate(cal)
+        sc = plan.scales()
+        rel_x = np.abs(sc[:, 0] / np.asarray(orc.s_x, np.float64) - 1)
+        rel_h = np.abs(sc[:, 3] / np.asarray(orc.s_h, np.float64) - 1)
+        rep.cal_max_rel = float(max(rel_x.max(), rel_h.max()))
+        assert max(rel_x[0], rel_h[0]) <= CAL_RTOL_FIRST, "first-layer calibration scales differ by %.3g" % max(
+            rel_x[0], rel_h[0])
+        assert rep.cal_max_rel <= CAL_RTOL, "calibration scales differ by %.3g" % rep.cal_max_rel
+        log("[case %s] calibration scales within %.2e" % (cfg.name, rep.cal_max_rel))
+
+        # the forward uses the oracle's scales (cache-hit path)
+        plan.set_act_scales(orc.s_x, orc.s_h)
+        plan.set_inputs(r0, y0)
+        plan.capture()
+        plan.replay()
+        plan.sync()
+        z_graph = to_np_u16(plan.z())
+        yl_graph = to_np_u16(plan.y_slot(L))
+        plan.replay()
+        plan.sync()
+        assert np.array_equal(to_np_u16(plan.z()), z_graph), "two graph replays differ"
+        plan.forward()
+        plan.sync()
+        assert np.array_equal(to_np_u16(plan.z()), z_graph), "eager forward differs from graph replay"
+        assert np.array_equal(to_np_u16(plan.y_slot(L)), yl_graph), "eager Y[L] differs from replay"
+        # saturation invariant over every quantised slot
+        for l in range(L):
+            for t in (plan.xq_slot(l), plan.hq_slot(l)):
+                codes = to_np_u8(t)
+                assert not np.any((codes & 0x7F) == 0x7F), "NaN code in layer %d" % l
+                rep.saturated_codes += int(np.count_nonzero((codes & 0x7F) == 0x7E))
+        z_ref = oracle.final_hidden(orc.r[L], orc.y[L])
+        rep.z_max_rel, rep.z_cos = y_metrics(z_graph[rows], z_ref)
+        assert rep.z_cos >= MIN_COS, "free-running Z cosine %.6f" % rep.z_cos
+        log("[case %s] graph == eager; Z cos %.6f max rel %.3g" % (cfg.name, rep.z_cos, rep.z_max_rel))
+
+        # teacher-forced per-block checks
+        idx = torch.as_tensor(rows, device=plan.device)
+        layers = range(L) if check_layers is None else check_layers
+        for l in layers:
+            with torch.cuda.stream(plan.stream):
+                plan.r_slot(l).index_copy_(0, idx, torch.from_numpy(orc.r[l].view(np.int16)).to(plan.device))
+                if orc.y[l] is None:
+                    plan.y_slot(l).index_fill_(0, idx, 0)
+                else:
+                    plan.y_slot(l).index_copy_(0, idx, torch.from_numpy(orc.y[l].view(np.int16)).to(plan.device))
+            plan.sync()
+            plan.forward_range(l, l + 1)
+            plan.sync()
+            r_g = to_np_u16(plan.r_slot(l + 1)[idx])
+            xq_g = to_np_u8(plan.xq_slot(l)[idx])
+            hq_g = to_np_u8(plan.hq_slot(l)[idx])
+            y_g = to_np_u16(plan.y_slot(l + 1)[idx])
+            nb = int(np.count_nonzero(r_g != orc.r[l + 1]))
+            assert nb == 0, "layer %d residual: %d bf16 mismatches" % (l, nb)
+            # oracle pre-rounding value of XQ for the boundary report
+            _, x_pre, _ = oracle.add_rmsnorm_quant(orc.r[l], orc.y[l], norm_w[l], cfg.eps, 1.0)
+            inv_x = np.float32(np.float32(1.0) / np.float32(orc.s_x[l]))
+            xs = code_stats(xq_g, orc.xq[l], (x_pre * inv_x).astype(np.float32))
+            check_codes("layer %d XQ" % l, xs)
+            hs = code_stats(hq_g, orc.hq[l])
+            check_codes("layer %d HQ" % l, hs)
+            mr, cs = check_y("layer %d Y" % l, y_g, orc.y[l + 1])
+            rep.layers_checked.append(l)
+            rep.xq_mismatch += xs.mismatches
+            rep.xq_n += xs.n
+            rep.xq_near_boundary += max(0, xs.near_boundary)
+            rep.hq_mismatch += hs.mismatches
+            rep.hq_n += hs.n
+            rep.y_max_rel = max(rep.y_max_rel, mr)
+            rep.y_min_cos = min(rep.y_min_cos, cs)
+        log("[case %s] per-block: XQ %d/%d (near boundary %d), HQ %d/%d, Y max rel %.3g min cos %.6f"
+            % (cfg.name, rep.xq_mismatch, rep.xq_n, rep.xq_near_boundary, rep.hq_mismatch, rep.hq_n,
+               rep.y_max_rel, rep.y_min_cos))
+    finally:
+        plan.close()
+    rep.seconds = time.time() - t0
+    return rep

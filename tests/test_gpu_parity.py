@@ -1,0 +1,71 @@
+"""GPU parity of the whole hot path against the CPU oracle, through the C ABI.
+
+Small workloads span several tiles and ragged tails of every kernel (GEMV
+M <= 16, GEMM M > 16 with partial 128-row tiles, split-K reductions, all three
+activations); the five named workloads run at their full sizes in the launch
+configuration the benchmark times, with the oracle on sampled rows where M is
+large (rows are independent under static per-tensor scales).
+"""
+import numpy as np
+import pytest
+
+from realtime_transformer_amd.configs import CONFIGS, FFNConfig, ACT_GEGLU_TANH, ACT_SWIGLU, ACT_GELU_TANH
+
+from _ffn_case import run_case, log
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    # (index for seeds, M, H, I, L, act)
+    (101, 1, 256, 512, 2, ACT_SWIGLU),
+    (102, 3, 384, 640, 2, ACT_GEGLU_TANH),
+    (103, 16, 256, 384, 2, ACT_GELU_TANH),
+    (104, 17, 256, 512, 2, ACT_GEGLU_TANH),
+    (105, 130, 384, 640, 2, ACT_SWIGLU),
+    (106, 300, 256, 512, 3, ACT_GELU_TANH),
+    (5, 40, 256, 512, 2, ACT_GELU_TANH),  # index 5: +-20 outliers exercise saturation
+]
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
+def test_small_shapes(spec):
+    idx, M, H, I, L, act = spec
+    cfg = FFNConfig(idx, "small_%d" % idx, M, H, I, L, act)
+    rep = run_case(cfg)
+    log(str(rep))
+
+
+def test_ffn_block_m16():
+    rep = run_case(CONFIGS[1])
+    log(str(rep))
+
+
+def test_action_expert_m50_chain():
+    rep = run_case(CONFIGS[2])
+    log(str(rep))
+
+
+@pytest.mark.timeout(900)
+def test_vlm_prefix_m788_full_size():
+    cfg = CONFIGS[3]
+    rng = np.random.default_rng(31)
+    rows = sorted(set(range(768, 788)) | set(rng.choice(768, 44, replace=False).tolist()))
+    cal_rows = sorted(set(range(772, 780)) | set(rng.choice(768, 8, replace=False).tolist()))
+    rep = run_case(cfg, rows=rows, cal_rows=cal_rows)
+    log(str(rep))
+
+
+@pytest.mark.timeout(900)
+def test_llm_decode_m1_full_size():
+    rep = run_case(CONFIGS[4], check_layers=[0, 1, 31, 62, 63])
+    log(str(rep))
+
+
+@pytest.mark.timeout(900)
+def test_dit_video_m4096_full_size():
+    cfg = CONFIGS[5]
+    rng = np.random.default_rng(53)
+    rows = sorted(rng.choice(cfg.M, 48, replace=False).tolist())
+    cal_rows = sorted(rng.choice(cfg.M, 12, replace=False).tolist())
+    rep = run_case(cfg, rows=rows, cal_rows=cal_rows, check_layers=[0, 1, 14, 29])
+    log(str(rep))
