@@ -181,6 +181,13 @@ frt_status frt_graph_capture(frt_plan *plan, void *stream);
  * changed after capture).  Asynchronous; the caller synchronises. */
 frt_status frt_graph_replay(frt_plan *plan, void *stream);
 
+/* Eager forward of the whole chain with a HIP event recorded on `stream`
+ * before and after every kernel; writes each kernel's duration in
+ * milliseconds to host_ms[L][3] = {norm+quantise, gate/up GEMM, down GEMM}.
+ * Same kernels and launch configuration as frt_ffn_forward.  Synchronises
+ * `stream`.  For measuring per-kernel time inside a running program. */
+frt_status frt_ffn_forward_profiled(frt_plan *plan, void *stream, float *host_ms);
+
 /* Device E4M3 quantiser as used by every kernel: out[i] = e4m3(in[i]) with
  * saturation to +-448 and round-to-nearest-even.  d_in device float[n],
  * d_out device uint8[n].  Asynchronous on `stream`.  For tests of the

@@ -198,6 +198,7 @@ struct frt_plan {
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
   bool captured = false, stale = false;
+  std::vector<hipEvent_t> prof_events;  // created on the first profiled forward
 
   uint8_t* wgu(int l) const { return ws + lo.wgu + (size_t)l * lo.wgu_layer; }
   uint8_t* wd(int l) const { return ws + lo.wd + (size_t)l * lo.wd_layer; }
@@ -217,6 +218,10 @@ struct frt_plan {
     for (auto v : w_set)
       if (!v) return false;
     return true;
+  }
+  void drop_events() {
+    for (auto e : prof_events) (void)hipEventDestroy(e);
+    prof_events.clear();
   }
   void drop_graph() {
     if (exec) (void)hipGraphExecDestroy(exec);
@@ -303,6 +308,7 @@ frt_status frt_ffn_plan_destroy(frt_plan* plan) {
   {
     DeviceGuard g(plan->d.device);
     plan->drop_graph();
+    plan->drop_events();
   }
   delete plan;
   return FRT_OK;
@@ -475,26 +481,33 @@ frt_status frt_ffn_io_get(const frt_plan* p, frt_ffn_io* out) {
   return FRT_OK;
 }
 
-static frt_status forward_range(frt_plan* p, int lb, int le, hipStream_t s) {
+static frt_status forward_range(frt_plan* p, int lb, int le, hipStream_t s,
+                                const hipEvent_t* ev = nullptr) {
   const int M = p->d.M, H = p->d.H, I = p->d.I, L = p->d.L;
   const int npk = p->gated ? 2 * I : I;
   for (int l = lb; l < le; ++l) {
+    const hipEvent_t* e = ev ? ev + 4 * (l - lb) : nullptr;
+    if (e) HIP_CHECK(hipEventRecord(e[0], s));
     const float s_x = p->s_x[l], s_h = p->s_h[l];
     const float inv_x = 1.0f / s_x, inv_h = 1.0f / s_h;
     const float a_g = s_x * p->s_g[l], a_u = s_x * p->s_u[l], a_d = s_h * p->s_d[l];
     KERNEL_CHECK(launch_add_rmsnorm_quant(p->r(l), p->y(l), p->wn(l), p->r(l + 1), p->xq(l), M, H,
                                           p->d.eps, inv_x, s), "add_rmsnorm_quant");
-    if (M <= kGemvMaxM) {
+    if (e) HIP_CHECK(hipEventRecord(e[1], s));
+    if (M <= kGemvMaxM)
       KERNEL_CHECK(launch_gemv_gateup(p->d.act, p->xq(l), p->wgu(l), p->hq(l), p->part(), p->cnt(0),
                                       M, H, I, p->lo.s_gu, a_g, a_u, inv_h, s), "gemv_gateup");
-      KERNEL_CHECK(launch_gemv_down(p->hq(l), p->wd(l), p->y(l + 1), p->part(), p->cnt(1), M, I, H,
-                                    p->lo.s_dn, a_d, s), "gemv_down");
-    } else {
+    else
       KERNEL_CHECK(launch_gemm_gateup(p->d.act, p->xq(l), p->wgu(l), p->hq(l), M, H, npk, a_g, a_u,
                                       inv_h, s), "gemm_gateup");
+    if (e) HIP_CHECK(hipEventRecord(e[2], s));
+    if (M <= kGemvMaxM)
+      KERNEL_CHECK(launch_gemv_down(p->hq(l), p->wd(l), p->y(l + 1), p->part(), p->cnt(1), M, I, H,
+                                    p->lo.s_dn, a_d, s), "gemv_down");
+    else
       KERNEL_CHECK(launch_gemm_down(p->hq(l), p->wd(l), p->y(l + 1), p->part(), p->cnt(1), M, I, H,
                                     p->lo.s_dn, a_d, s), "gemm_down");
-    }
+    if (e) HIP_CHECK(hipEventRecord(e[3], s));
   }
   if (le == L) KERNEL_CHECK(launch_residual_add(p->r(L), p->y(L), p->z(), p->mh(), s), "residual_add");
   return FRT_OK;
@@ -515,6 +528,33 @@ frt_status frt_ffn_forward_range(frt_plan* p, int32_t layer_begin, int32_t layer
 frt_status frt_ffn_forward(frt_plan* p, void* stream) {
   if (!p) return fail(FRT_ERR_INVALID_ARG, "frt_ffn_forward: plan is NULL");
   return frt_ffn_forward_range(p, 0, p->d.L, stream);
+}
+
+frt_status frt_ffn_forward_profiled(frt_plan* p, void* stream, float* host_ms) {
+  if (!p || !host_ms) return fail(FRT_ERR_INVALID_ARG, "frt_ffn_forward_profiled: NULL argument");
+  if (!p->all_weights() || !p->act_scales_set)
+    return fail(FRT_ERR_STATE, "frt_ffn_forward_profiled: weights and activation scales must be set first");
+  DeviceGuard g(p->d.device);
+  HIP_CHECK(g.err);
+  const int L = p->d.L;
+  if (p->prof_events.empty()) {
+    p->prof_events.resize((size_t)4 * L, nullptr);
+    for (auto& e : p->prof_events) {
+      hipError_t err = hipEventCreate(&e);
+      if (err != hipSuccess) {
+        p->drop_events();
+        return fail(FRT_ERR_HIP, "hipEventCreate failed: %s", hipGetErrorString(err));
+      }
+    }
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  frt_status st = forward_range(p, 0, L, s, p->prof_events.data());
+  if (st != FRT_OK) return st;
+  HIP_CHECK(hipStreamSynchronize(s));
+  for (int l = 0; l < L; ++l)
+    for (int k = 0; k < 3; ++k)
+      HIP_CHECK(hipEventElapsedTime(&host_ms[3 * l + k], p->prof_events[4 * l + k], p->prof_events[4 * l + k + 1]));
+  return FRT_OK;
 }
 
 frt_status frt_graph_capture(frt_plan* p, void* stream) {

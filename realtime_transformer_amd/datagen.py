@@ -3,7 +3,9 @@
 This module only draws numbers and lays them out; it holds none of the FFN
 block's arithmetic.  Draws use numpy's PCG64 through SeedSequence([seed,
 chunk]) in fixed 4 Mi-element chunks (so the bytes do not depend on the thread
-count); fp32 -> bf16 conversion is torch's (round to nearest even).
+count).  A bf16 input is the top 16 bits of its fp32 draw (truncation toward
+zero): a plain bit extraction, no rounding logic, which shifts each value by
+less than 2^-8 of itself.
 
 Distributions (one reading per workload, stated in the design doc of the repo):
   weights        W_gate, W_up [I,H], W_down [H,I] ~ N(0, 0.02) (std), bf16
@@ -25,8 +27,6 @@ from concurrent.futures import ThreadPoolExecutor
 from typing import List, Optional, Tuple
 
 import numpy as np
-import torch
-
 from .configs import FFNConfig
 
 _CHUNK = 1 << 22
@@ -61,9 +61,10 @@ def normal_f32(seed: int, n: int) -> np.ndarray:
 
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """fp32 -> bf16 bit patterns (uint16) using torch's round-to-nearest-even."""
-    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
-    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    """fp32 draws -> bf16 bit patterns (uint16): the top half of each fp32."""
+    assert np.little_endian
+    h = np.ascontiguousarray(x, dtype=np.float32).view(np.uint16)
+    return h[1::2].copy()  # little-endian: odd halves are the high 16 bits
 
 
 def normal_bf16(seed: int, shape, std: float = 1.0, mean: float = 0.0) -> np.ndarray:

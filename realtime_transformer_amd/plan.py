@@ -138,6 +138,10 @@ class FFNPlan:
     def forward_range(self, lb: int, le: int):
         _abi.frt_ffn_forward_range(self.plan, lb, le, self.s)
 
+    def forward_profiled(self) -> np.ndarray:
+        """Per-kernel milliseconds [L][3] (norm+quantise, gate/up, down) of one eager forward."""
+        return _abi.frt_ffn_forward_profiled(self.plan, self.s, self.L)
+
     def capture(self):
         _abi.frt_graph_capture(self.plan, self.s)
 
