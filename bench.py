@@ -107,7 +107,7 @@ def cpu_baseline(cfg, kept, inputs, budget_s):
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
-    return {"value": el / done * 1e6, "unit": "us/layer", "cores": nthreads, "kind": "oracle",
+    return {"value": round(el / done * 1e6, 1), "unit": "us/layer", "cores": nthreads, "kind": "oracle",
             "sample": "%d block forwards of the %s workload (M=%d, H=%d, I=%d), exact int64 "
                       "FP8 GEMMs and fp64 norm/activations, weights quantised beforehand"
                       % (done, cfg.name, cfg.M, cfg.H, cfg.I)}
@@ -144,7 +144,8 @@ def main():
         plan.set_act_scales([0.01] * cfg.L, [0.01] * cfg.L)
         plan.capture()
     ms, wall = time_replays(plan, args.steps, args.warmup)
-    kms = per_kernel_ms(plan)
+    kms = [float(v) for v in per_kernel_ms(plan)]
+    ms = float(ms)
     plan.close()
     log("[bench %s] %.3f ms/step, kernels (norm, gate/up, down) %s ms" % (cfg.name, ms, np.round(kms, 4)))
 
@@ -187,7 +188,8 @@ def main():
             p2.set_act_scales([0.01] * c2.L, [0.01] * c2.L)
             p2.capture()
         ms2, _ = time_replays(p2, args.steps, args.warmup)
-        k2 = per_kernel_ms(p2)
+        k2 = [float(v) for v in per_kernel_ms(p2)]
+        ms2 = float(ms2)
         p2.close()
         us2 = ms2 * 1000.0 / c2.L
         chain_tf = c2.layer_flops() * c2.L / (ms2 * 1e-3) / 1e12

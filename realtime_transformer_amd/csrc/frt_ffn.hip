@@ -35,14 +35,14 @@ hipError_t launch_residual_add(const uint16_t*, const uint16_t*, uint16_t*, size
 hipError_t launch_e4m3_encode(const float*, uint8_t*, int64_t, hipStream_t);
 hipError_t launch_amax_bf16(const uint16_t*, size_t, float*, hipStream_t);
 hipError_t launch_quant_pack(const uint16_t*, uint8_t*, int, int, float, int, hipStream_t);
-hipError_t launch_gemv_gateup(int, const uint8_t*, const uint8_t*, uint8_t*, float*, uint32_t*,
-                              int, int, int, int, float, float, float, hipStream_t);
-hipError_t launch_gemv_down(const uint8_t*, const uint8_t*, uint16_t*, float*, uint32_t*, int,
-                            int, int, int, float, hipStream_t);
+hipError_t launch_gemv_gateup(int, const uint8_t*, const uint8_t*, uint8_t*, int, int, int, int,
+                              float, float, float, hipStream_t);
+hipError_t launch_gemv_down(const uint8_t*, const uint8_t*, uint16_t*, int, int, int, int, bool,
+                            float, hipStream_t);
 hipError_t launch_gemm_gateup(int, const uint8_t*, const uint8_t*, uint8_t*, int, int, int, float,
                               float, float, hipStream_t);
 hipError_t launch_gemm_down(const uint8_t*, const uint8_t*, uint16_t*, float*, uint32_t*, int,
-                            int, int, int, float, hipStream_t);
+                            int, int, int, bool, float, hipStream_t);
 hipError_t launch_calib_gateup(int, const float*, const uint8_t*, float*, float*, int, int, int,
                                float, float, hipStream_t);
 hipError_t launch_calib_down(const float*, const uint8_t*, uint16_t*, int, int, int, float,
@@ -100,7 +100,23 @@ struct DeviceGuard {
 namespace {
 
 constexpr int kGemvMaxM = 16;
-constexpr int kTargetWaves = 4096;  // split-K target for the GEMV path: ~4 waves per SIMD
+constexpr int kTargetWaves = 6144;  // GEMV: ~6 waves per SIMD across the chip
+
+// Waves per GEMV workgroup: the smallest power of two (<= 16, <= K blocks)
+// that brings groups * W to kTargetWaves.  FRT_GEMV_WAVES_GATEUP /
+// FRT_GEMV_WAVES_DOWN override it (tuning sweeps).
+int gemv_waves(int groups, int kblocks, const char* env) {
+  const char* e = getenv(env);
+  int w = 1;
+  if (e && *e) {
+    w = atoi(e);
+  } else {
+    while (w < 16 && groups * w < kTargetWaves) w *= 2;
+  }
+  if (w != 1 && w != 2 && w != 4 && w != 8 && w != 16) w = 4;
+  while (w > 1 && w > kblocks) w /= 2;
+  return w;
+}
 
 struct Layout {
   size_t wgu, wgu_layer;  // packed gate/up (or up) weights, per-layer stride
@@ -112,7 +128,7 @@ struct Layout {
   size_t amax;            // [2 + 2L] floats
   size_t cal_x, cal_h, cal_r, cal_y;
   size_t total;
-  int s_gu, s_dn;  // split counts (GEMV: per wave; GEMM: down only)
+  int s_gu, s_dn;  // GEMV: waves per workgroup; GEMM: K splits of the down GEMM
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -124,7 +140,7 @@ bool desc_ok(const frt_ffn_desc* d) {
   if (d->H > 16384 || d->I > 32768) return false;
   if (d->act < FRT_ACT_GEGLU_TANH || d->act > FRT_ACT_GELU_TANH) return false;
   if (!(d->eps > 0.0f) || !std::isfinite(d->eps)) return false;
-  if (d->flags != 0u || d->device < 0) return false;
+  if ((d->flags & ~(uint32_t)FRT_FLAG_FP8_MFMA_DOWN) != 0u || d->device < 0) return false;
   if ((int64_t)d->M * d->I > (int64_t)1 << 31) return false;
   return true;
 }
@@ -155,18 +171,18 @@ Layout make_layout(const frt_ffn_desc& d) {
 
   size_t part = 0, words = 1;
   if (d.M <= kGemvMaxM) {
-    const int pg = (int)(I / 16), pd = (int)(H / 16);
-    const int kb_g = (int)(H / 128), kb_d = (int)(I / 128);
-    lo.s_gu = std::min(std::max(1, ceil_div(kTargetWaves, pg)), kb_g);
-    lo.s_dn = std::min(std::max(1, ceil_div(kTargetWaves, pd)), kb_d);
-    part = std::max((size_t)pg * lo.s_gu * 2 * 16 * M, (size_t)pd * lo.s_dn * 16 * M) * 4;
-    words = (size_t)std::max(pg, pd);
+    lo.s_gu = gemv_waves((int)(I / 16), (int)(H / 128), "FRT_GEMV_WAVES_GATEUP");
+    lo.s_dn = gemv_waves((int)(H / 16), (int)(I / 128), "FRT_GEMV_WAVES_DOWN");
+    part = 4;
+    words = 1;
   } else {
     const int tiles = (int)(H / 128) * ceil_div(d.M, 128);
     const int kb_d = (int)(I / 128);
     int s = std::max(1, ceil_div(512, tiles));
     s = std::min(s, 16);
     s = std::min(s, std::max(1, kb_d / 2));
+    if (const char* e = getenv("FRT_GEMM_DOWN_SPLIT"))
+      if (*e) s = std::max(1, std::min(atoi(e), std::max(1, kb_d)));
     lo.s_gu = 1;
     lo.s_dn = s;
     part = s > 1 ? (size_t)s * M * H * 4 : 4;
@@ -214,6 +230,7 @@ struct frt_plan {
     return reinterpret_cast<uint32_t*>(ws + lo.cnt) + (size_t)region * lo.cnt_words;
   }
   float* amax() const { return reinterpret_cast<float*>(ws + lo.amax); }
+  bool fp8_down() const { return (d.flags & FRT_FLAG_FP8_MFMA_DOWN) != 0u; }
   bool all_weights() const {
     for (auto v : w_set)
       if (!v) return false;
@@ -495,18 +512,18 @@ static frt_status forward_range(frt_plan* p, int lb, int le, hipStream_t s,
                                           p->d.eps, inv_x, s), "add_rmsnorm_quant");
     if (e) HIP_CHECK(hipEventRecord(e[1], s));
     if (M <= kGemvMaxM)
-      KERNEL_CHECK(launch_gemv_gateup(p->d.act, p->xq(l), p->wgu(l), p->hq(l), p->part(), p->cnt(0),
-                                      M, H, I, p->lo.s_gu, a_g, a_u, inv_h, s), "gemv_gateup");
+      KERNEL_CHECK(launch_gemv_gateup(p->d.act, p->xq(l), p->wgu(l), p->hq(l), M, H, I, p->lo.s_gu,
+                                      a_g, a_u, inv_h, s), "gemv_gateup");
     else
       KERNEL_CHECK(launch_gemm_gateup(p->d.act, p->xq(l), p->wgu(l), p->hq(l), M, H, npk, a_g, a_u,
                                       inv_h, s), "gemm_gateup");
     if (e) HIP_CHECK(hipEventRecord(e[2], s));
     if (M <= kGemvMaxM)
-      KERNEL_CHECK(launch_gemv_down(p->hq(l), p->wd(l), p->y(l + 1), p->part(), p->cnt(1), M, I, H,
-                                    p->lo.s_dn, a_d, s), "gemv_down");
+      KERNEL_CHECK(launch_gemv_down(p->hq(l), p->wd(l), p->y(l + 1), M, I, H, p->lo.s_dn, p->fp8_down(),
+                                    a_d, s), "gemv_down");
     else
       KERNEL_CHECK(launch_gemm_down(p->hq(l), p->wd(l), p->y(l + 1), p->part(), p->cnt(1), M, I, H,
-                                    p->lo.s_dn, a_d, s), "gemm_down");
+                                    p->lo.s_dn, p->fp8_down(), a_d, s), "gemm_down");
     if (e) HIP_CHECK(hipEventRecord(e[3], s));
   }
   if (le == L) KERNEL_CHECK(launch_residual_add(p->r(L), p->y(L), p->z(), p->mh(), s), "residual_add");

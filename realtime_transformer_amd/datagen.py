@@ -63,8 +63,9 @@ def normal_f32(seed: int, n: int) -> np.ndarray:
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """fp32 draws -> bf16 bit patterns (uint16): the top half of each fp32."""
     assert np.little_endian
-    h = np.ascontiguousarray(x, dtype=np.float32).view(np.uint16)
-    return h[1::2].copy()  # little-endian: odd halves are the high 16 bits
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    h = x.reshape(-1).view(np.uint16)
+    return h[1::2].copy().reshape(x.shape)  # little-endian: odd halves are the high bits
 
 
 def normal_bf16(seed: int, shape, std: float = 1.0, mean: float = 0.0) -> np.ndarray:

@@ -28,13 +28,13 @@ def _to_dev_u16(a: np.ndarray, device) -> torch.Tensor:
 
 class FFNPlan:
     def __init__(self, M: int, H: int, I: int, L: int, act: int, eps: float = 1e-6,
-                 device: int = 0, stream: Optional[torch.cuda.Stream] = None):
+                 device: int = 0, stream: Optional[torch.cuda.Stream] = None, flags: int = 0):
         _require_gpu()
         _abi.load()
         self.M, self.H, self.I, self.L, self.act = M, H, I, L, act
         self.gated = act != _abi.FRT_ACT_GELU_TANH
         self.device = torch.device("cuda", device)
-        self.desc = _abi.make_desc(M, H, I, L, act, eps, device)
+        self.desc = _abi.make_desc(M, H, I, L, act, eps, device, flags)
         self.nbytes = _abi.frt_ffn_workspace_size(self.desc)
         self.ws = torch.empty(self.nbytes + 256, dtype=torch.uint8, device=self.device)
         base = self.ws.data_ptr()

@@ -132,9 +132,11 @@ class CaseReport:
 
 
 def run_case(cfg: FFNConfig, rows: Optional[Sequence[int]] = None, cal_rows: Optional[Sequence[int]] = None,
-             check_layers: Optional[Sequence[int]] = None, nbatch: int = 4) -> CaseReport:
+             check_layers: Optional[Sequence[int]] = None, nbatch: int = 4, flags: int = 0,
+             z_min_cos: Optional[float] = MIN_COS) -> CaseReport:
     """Full parity procedure; rows / cal_rows select the evaluated / calibration
-    rows (None = all); check_layers selects the teacher-forced layers (None = all)."""
+    rows (None = all); check_layers selects the teacher-forced layers (None = all);
+    flags are plan flags; z_min_cos gates the free-running chain (None: report only)."""
     t0 = time.time()
     rep = CaseReport(cfg.name)
     M, H, I, L, act = cfg.M, cfg.H, cfg.I, cfg.L, cfg.act
@@ -147,7 +149,7 @@ def run_case(cfg: FFNConfig, rows: Optional[Sequence[int]] = None, cal_rows: Opt
     log("[case %s] M=%d H=%d I=%d L=%d act=%d rows=%d cal_rows=%d" % (
         cfg.name, M, H, I, L, act, len(rows), cal[0][0].shape[0]))
 
-    plan = FFNPlan(M, H, I, L, act, cfg.eps)
+    plan = FFNPlan(M, H, I, L, act, cfg.eps, flags=flags)
     try:
         weight_scales = []
         norm_w = {}
@@ -213,7 +215,8 @@ def run_case(cfg: FFNConfig, rows: Optional[Sequence[int]] = None, cal_rows: Opt
                 rep.saturated_codes += int(np.count_nonzero((codes & 0x7F) == 0x7E))
         z_ref = oracle.final_hidden(orc.r[L], orc.y[L])
         rep.z_max_rel, rep.z_cos = y_metrics(z_graph[rows], z_ref)
-        assert rep.z_cos >= MIN_COS, "free-running Z cosine %.6f" % rep.z_cos
+        if z_min_cos is not None:
+            assert rep.z_cos >= z_min_cos, "free-running Z cosine %.6f" % rep.z_cos
         log("[case %s] graph == eager; Z cos %.6f max rel %.3g" % (cfg.name, rep.z_cos, rep.z_max_rel))
 
         # teacher-forced per-block checks

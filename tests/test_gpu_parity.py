@@ -35,6 +35,17 @@ def test_small_shapes(spec):
     log(str(rep))
 
 
+@pytest.mark.parametrize("spec", [SMALL[0], SMALL[3], SMALL[5]],
+                         ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
+def test_small_shapes_fp8_down(spec):
+    # opt-in FP8 matrix cores for the down projection: the per-block
+    # tolerance still holds; the free-running drift is reported, not gated
+    idx, M, H, I, L, act = spec
+    cfg = FFNConfig(idx, "small_fp8dn_%d" % idx, M, H, I, L, act)
+    rep = run_case(cfg, flags=1, z_min_cos=None)
+    log(str(rep))
+
+
 def test_ffn_block_m16():
     rep = run_case(CONFIGS[1])
     log(str(rep))
