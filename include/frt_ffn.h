@@ -145,23 +145,26 @@ frt_status frt_export_weight_codes(const frt_plan *plan, int32_t layer, int32_t 
 
 /* Calibration measurement pass (architecture doc, component "Calibration",
  * phase (a); the predict() flow's cache-miss path "run 1 fwd, record amax").
- * Runs the chain with unquantised fp32 activations and the quantised weights
- * (codes times their scale) over `nbatch` batches of `rows` (1..M) rows and
- * records per layer amax(|x|) (gate/up input) and amax(|h|) (down input)
- * over all batches; sets s_x = f32(amax_x/448), s_h = f32(amax_h/448)
- * (1 when amax is 0).
- *   d_r_batches  host array of nbatch device pointers, bf16 [rows][H]
- *   d_y_batches  host array of nbatch device pointers (bf16 [rows][H]) or
- *                NULL for zero previous outputs
- * All weights must be set.  Synchronises `stream`.  Marks a captured graph
- * stale. */
+ * Runs layers [layer_begin, layer_end) with unquantised fp32 activations and
+ * the quantised weights (codes times their scale) over `nbatch` batches of
+ * `rows` (1..M) rows and records per layer amax(|x|) (gate/up input) and
+ * amax(|h|) (down input) over all batches; sets s_x = f32(amax_x/448) and
+ * s_h = f32(amax_h/448) (1 when amax is 0) for those layers only.  The
+ * whole-chain calibration is layer_begin = 0, layer_end = L.
+ *   d_r_batches  host array of nbatch device pointers, bf16 [rows][H]: the
+ *                residual entering layer_begin
+ *   d_y_batches  host array of nbatch device pointers (bf16 [rows][H]): the
+ *                previous block output entering layer_begin, or NULL (zeros)
+ * The weights of those layers must be set.  Synchronises `stream`.  Marks a
+ * captured graph stale. */
 frt_status frt_calibrate(frt_plan *plan, const void *const *d_r_batches,
                          const void *const *d_y_batches, int32_t nbatch, int32_t rows,
-                         void *stream);
+                         int32_t layer_begin, int32_t layer_end, void *stream);
 
 /* Read all per-layer scales into host memory as float[L][5] =
  * {s_x, s_g, s_u, s_h, s_d} (s_g = 1 for the non-gated activation; s_x, s_h
- * are 0 until calibrated or set). */
+ * are 0 until calibrated or set).  The forward needs every layer's s_x and
+ * s_h set (FRT_ERR_STATE otherwise). */
 frt_status frt_get_scales(const frt_plan *plan, float *host_out);
 
 /* Install static activation scales float[L][2] = {s_x, s_h} from host memory

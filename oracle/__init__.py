@@ -83,6 +83,8 @@ def lib():
         L.orc_scale_from_amax.argtypes = [ctypes.c_float]
         L.orc_quant_tensor.restype = ctypes.c_float
         L.orc_quant_tensor.argtypes = [_c_u16p, ctypes.c_int64, _c_u8p]
+        L.orc_quant_tensor_mt.restype = ctypes.c_float
+        L.orc_quant_tensor_mt.argtypes = [_c_u16p, ctypes.c_int64, _c_u8p, ctypes.c_int]
         L.orc_add_rmsnorm_quant.restype = None
         L.orc_add_rmsnorm_quant.argtypes = [ctypes.c_int, ctypes.c_int, _c_u16p, _c_u16p, _c_u16p,
                                             ctypes.c_float, ctypes.c_float, _c_u16p, _c_f32p,
@@ -91,6 +93,11 @@ def lib():
         L.orc_gateup.argtypes = [ctypes.c_int] * 4 + [_c_u8p, _c_u8p, _c_u8p, ctypes.c_float,
                                                       ctypes.c_float, ctypes.c_float, _c_f32p,
                                                       _c_u8p, ctypes.c_int]
+        L.orc_gateup_epilogue.restype = None
+        L.orc_gateup_epilogue.argtypes = [ctypes.c_int64, ctypes.c_int, _c_f32p, _c_f32p, ctypes.c_float,
+                                          ctypes.c_float, ctypes.c_float, _c_f32p, _c_u8p]
+        L.orc_down_epilogue.restype = None
+        L.orc_down_epilogue.argtypes = [ctypes.c_int64, _c_f32p, ctypes.c_float, _c_u16p]
         L.orc_down.restype = ctypes.c_int
         L.orc_down.argtypes = [ctypes.c_int] * 3 + [_c_u8p, _c_u8p, ctypes.c_float, _c_u16p,
                                                     ctypes.c_int]
@@ -163,7 +170,10 @@ def bf16_round(x) -> np.ndarray:
 def bf16_to_f32(b) -> np.ndarray:
     """Widen bf16 bit patterns to fp32 (exact: the bits become the top half)."""
     b = np.ascontiguousarray(np.asarray(b, dtype=np.uint16))
-    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    assert np.little_endian
+    out = np.zeros(b.shape + (2,), dtype=np.uint16)
+    out[..., 1] = b  # little-endian: the second half-word is the high half
+    return out.view(np.float32).reshape(b.shape)
 
 
 def gelu_tanh(z: float) -> float:
@@ -201,11 +211,12 @@ def gemm_e4m3(a_codes, b_codes, nthreads: Optional[int] = None) -> np.ndarray:
     return out
 
 
-def quant_tensor(w_bf16) -> tuple:
+def quant_tensor(w_bf16, nthreads: Optional[int] = None) -> tuple:
     """Per-tensor E4M3 quantisation of a bf16 tensor -> (codes, scale)."""
     w = _u16(w_bf16)
     codes = np.empty(w.shape, dtype=np.uint8)
-    s = lib().orc_quant_tensor(_p(w, _c_u16p), w.size, _p(codes, _c_u8p))
+    s = lib().orc_quant_tensor_mt(_p(w, _c_u16p), w.size, _p(codes, _c_u8p),
+                                  nthreads or default_threads())
     return codes, float(np.float32(s))
 
 
@@ -241,6 +252,25 @@ def gateup(xq, qg, qu, act: int, alpha_g: float, alpha_u: float, inv_h: float,
     if rc:
         raise RuntimeError("orc_gateup failed (%d)" % rc)
     return h, hq
+
+
+def gateup_epilogue(Ag, Au, act: int, alpha_g: float, alpha_u: float, inv_h: float):
+    """Step-2 epilogue on given fp32 accumulators -> (h fp32, hq codes)."""
+    Au = np.ascontiguousarray(Au, dtype=np.float32)
+    Ag = None if act == ACT_GELU_TANH else np.ascontiguousarray(Ag, dtype=np.float32)
+    h = np.empty(Au.shape, np.float32)
+    hq = np.empty(Au.shape, np.uint8)
+    lib().orc_gateup_epilogue(Au.size, act, _p(Ag, _c_f32p), _p(Au, _c_f32p), float(alpha_g),
+                              float(alpha_u), float(inv_h), _p(h, _c_f32p), _p(hq, _c_u8p))
+    return h, hq
+
+
+def down_epilogue(Ad, alpha_d: float) -> np.ndarray:
+    """Step-3 epilogue on given fp32 accumulators -> bf16 bits."""
+    Ad = np.ascontiguousarray(Ad, dtype=np.float32)
+    y = np.empty(Ad.shape, np.uint16)
+    lib().orc_down_epilogue(Ad.size, _p(Ad, _c_f32p), float(alpha_d), _p(y, _c_u16p))
+    return y
 
 
 def down(hq, qd, alpha_d: float, nthreads: Optional[int] = None) -> np.ndarray:
@@ -337,12 +367,14 @@ class ChainResult:
     xq: List[np.ndarray]  # XQ[0..L-1]
     hq: List[np.ndarray]  # HQ[0..L-1]
     weights: List[Optional[LayerWeights]]
+    cal_states: List[list] = None  # per layer: the (r, y) batches entering it (measure mode)
 
 
 def calibrate_and_run(layers: Iterable[Callable[[], LayerWeights]], act: int, eps: float,
                       r0, y0, calib_batches: Sequence[tuple], keep_weights: bool = False,
                       act_scales: Optional[Sequence[tuple]] = None,
-                      nthreads: Optional[int] = None) -> ChainResult:
+                      nthreads: Optional[int] = None, keep_cal_states: bool = False,
+                      post_layer: Optional[Callable] = None) -> ChainResult:
     """Layer-major chain: for each layer, measure the calibration batches
     (amax of the gate/up input and of the down input over all batches, rows
     and elements), derive the static scales s = f32(amax/448), then run the
@@ -350,11 +382,14 @@ def calibrate_and_run(layers: Iterable[Callable[[], LayerWeights]], act: int, ep
     per layer that returns its quantised weights, so huge chains can stream
     their weights.  ``act_scales`` (per layer (s_x, s_h)) skips the
     measurement and uses the given scales (the calibration cache-hit path).
+    ``post_layer(li, lw, s_x, s_h)`` is called after each layer.
     """
     cal_states = [(_u16(r), None if y is None else _u16(y)) for r, y in calib_batches]
-    res = ChainResult([], [], [], [], [_u16(r0)], [None if y0 is None else _u16(y0)], [], [], [])
+    res = ChainResult([], [], [], [], [_u16(r0)], [None if y0 is None else _u16(y0)], [], [], [], [])
     for li, get_w in enumerate(layers):
         lw = get_w()
+        if keep_cal_states:
+            res.cal_states.append(list(cal_states))
         if act_scales is None:
             ax = 0.0
             ah = 0.0
@@ -380,4 +415,6 @@ def calibrate_and_run(layers: Iterable[Callable[[], LayerWeights]], act: int, ep
         res.xq.append(xq)
         res.hq.append(hq)
         res.weights.append(lw if keep_weights else None)
+        if post_layer is not None:
+            post_layer(li, lw, s_x, s_h)
     return res

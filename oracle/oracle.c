@@ -247,16 +247,57 @@ int orc_gemm_e4m3(int M, int N, int K, const uint8_t *a, const uint8_t *b, float
 
 float orc_scale_from_amax(float amax) { return amax > 0.0f ? amax / 448.0f : 1.0f; }
 
-float orc_quant_tensor(const uint16_t *w, int64_t n, uint8_t *codes) {
-  float amax = 0.0f;
-  for (int64_t i = 0; i < n; ++i) {
-    float a = fabsf(orc_bf16_to_f32(w[i]));
-    if (a > amax) amax = a;
+typedef struct {
+  const uint16_t *w;
+  uint8_t *codes;
+  float inv;
+  float part_max[256];
+  int64_t n;
+  int nthreads;
+} quant_ctx;
+
+static void amax_range(void *p, int64_t begin, int64_t end) {
+  /* one range per thread: begin..end covers thread t's slice */
+  quant_ctx *q = (quant_ctx *)p;
+  int64_t t = begin; /* ranges are thread indices here */
+  for (; t < end; ++t) {
+    int64_t lo = q->n * t / q->nthreads, hi = q->n * (t + 1) / q->nthreads;
+    float m = 0.0f;
+    for (int64_t i = lo; i < hi; ++i) {
+      float a = fabsf(orc_bf16_to_f32(q->w[i]));
+      if (a > m) m = a;
+    }
+    q->part_max[t] = m;
   }
+}
+
+static void encode_range(void *p, int64_t begin, int64_t end) {
+  quant_ctx *q = (quant_ctx *)p;
+  for (int64_t i = begin; i < end; ++i) q->codes[i] = orc_e4m3_encode(orc_bf16_to_f32(q->w[i]) * q->inv);
+}
+
+/* amax is an exact max (order does not matter); the threads only split the
+   elements. */
+float orc_quant_tensor_mt(const uint16_t *w, int64_t n, uint8_t *codes, int nthreads) {
+  quant_ctx q;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  q.w = w;
+  q.codes = codes;
+  q.n = n;
+  q.nthreads = nthreads;
+  parallel_for(nthreads, nthreads, amax_range, &q);
+  float amax = 0.0f;
+  for (int t = 0; t < nthreads; ++t)
+    if (q.part_max[t] > amax) amax = q.part_max[t];
   float s = orc_scale_from_amax(amax);
-  float inv = 1.0f / s;
-  for (int64_t i = 0; i < n; ++i) codes[i] = orc_e4m3_encode(orc_bf16_to_f32(w[i]) * inv);
+  q.inv = 1.0f / s;
+  parallel_for(n, nthreads, encode_range, &q);
   return s;
+}
+
+float orc_quant_tensor(const uint16_t *w, int64_t n, uint8_t *codes) {
+  return orc_quant_tensor_mt(w, n, codes, 1);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -321,6 +362,19 @@ static float gated_value(int act, float g, float u) {
   return a * u;
 }
 
+/* Epilogue of step 2 on given fp32 accumulators Ag, Au [M*I] (Ag unused for
+   the non-gated form). */
+void orc_gateup_epilogue(int64_t n, int act, const float *Ag, const float *Au, float alpha_g,
+                         float alpha_u, float inv_h, float *h_out, uint8_t *hq_out) {
+  for (int64_t idx = 0; idx < n; ++idx) {
+    float u = Au[idx] * alpha_u;
+    float g = (act != ORC_ACT_GELU_TANH) ? Ag[idx] * alpha_g : 0.0f;
+    float h = gated_value(act, g, u);
+    if (h_out) h_out[idx] = h;
+    if (hq_out) hq_out[idx] = orc_e4m3_encode(h * inv_h);
+  }
+}
+
 int orc_gateup(int M, int H, int I, int act, const uint8_t *xq, const uint8_t *qg,
                const uint8_t *qu, float alpha_g, float alpha_u, float inv_h, float *h_out,
                uint8_t *hq_out, int nthreads) {
@@ -332,13 +386,7 @@ int orc_gateup(int M, int H, int I, int act, const uint8_t *xq, const uint8_t *q
     if (!Ag) return free(Au), -2;
     if (orc_gemm_e4m3(M, I, H, xq, qg, Ag, nthreads)) return free(Au), free(Ag), -1;
   }
-  for (int64_t idx = 0; idx < (int64_t)M * I; ++idx) {
-    float u = Au[idx] * alpha_u;
-    float g = Ag ? Ag[idx] * alpha_g : 0.0f;
-    float h = gated_value(act, g, u);
-    if (h_out) h_out[idx] = h;
-    if (hq_out) hq_out[idx] = orc_e4m3_encode(h * inv_h);
-  }
+  orc_gateup_epilogue((int64_t)M * I, act, Ag, Au, alpha_g, alpha_u, inv_h, h_out, hq_out);
   free(Au);
   free(Ag);
   return 0;
@@ -349,12 +397,16 @@ int orc_gateup(int M, int H, int I, int act, const uint8_t *xq, const uint8_t *q
 /*   y = bf16( f32( f32(Ad) * alpha_d ) )                                   */
 /* ------------------------------------------------------------------------ */
 
+void orc_down_epilogue(int64_t n, const float *Ad, float alpha_d, uint16_t *y_out) {
+  for (int64_t idx = 0; idx < n; ++idx) y_out[idx] = orc_bf16_round(Ad[idx] * alpha_d);
+}
+
 int orc_down(int M, int H, int I, const uint8_t *hq, const uint8_t *qd, float alpha_d,
              uint16_t *y_out, int nthreads) {
   float *Ad = (float *)malloc(sizeof(float) * (size_t)M * H);
   if (!Ad) return -2;
   if (orc_gemm_e4m3(M, H, I, hq, qd, Ad, nthreads)) return free(Ad), -1;
-  for (int64_t idx = 0; idx < (int64_t)M * H; ++idx) y_out[idx] = orc_bf16_round(Ad[idx] * alpha_d);
+  orc_down_epilogue((int64_t)M * H, Ad, alpha_d, y_out);
   free(Ad);
   return 0;
 }

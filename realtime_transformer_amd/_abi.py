@@ -82,7 +82,7 @@ def load(build_if_missing: bool = True):
         "frt_ffn_plan_destroy": [vp],
         "frt_quant_weights": [vp, i32, vp, vp, vp, vp, vp],
         "frt_export_weight_codes": [vp, i32, i32, vp],
-        "frt_calibrate": [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i32, vp],
+        "frt_calibrate": [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i32, i32, i32, vp],
         "frt_get_scales": [vp, ctypes.POINTER(ctypes.c_float)],
         "frt_set_act_scales": [vp, ctypes.POINTER(ctypes.c_float)],
         "frt_ffn_io_get": [vp, ctypes.POINTER(frt_ffn_io)],
@@ -142,11 +142,11 @@ def frt_export_weight_codes(plan: int, layer: int, which: int, rows: int, cols: 
 
 
 def frt_calibrate(plan: int, d_r_batches: Sequence[int], d_y_batches: Optional[Sequence[int]],
-                  rows: int, stream: int) -> None:
+                  rows: int, layer_begin: int, layer_end: int, stream: int) -> None:
     n = len(d_r_batches)
     rb = (ctypes.c_void_p * n)(*d_r_batches)
     yb = None if d_y_batches is None else (ctypes.c_void_p * n)(*d_y_batches)
-    _check(load().frt_calibrate(plan, rb, yb, n, rows, stream))
+    _check(load().frt_calibrate(plan, rb, yb, n, rows, layer_begin, layer_end, stream))
 
 
 def frt_get_scales(plan: int, L: int) -> np.ndarray:

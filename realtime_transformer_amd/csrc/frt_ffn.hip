@@ -210,7 +210,6 @@ struct frt_plan {
   bool gated = true;
   std::vector<uint8_t> w_set;
   std::vector<float> s_x, s_g, s_u, s_h, s_d;
-  bool act_scales_set = false;
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
   bool captured = false, stale = false;
@@ -231,6 +230,11 @@ struct frt_plan {
   }
   float* amax() const { return reinterpret_cast<float*>(ws + lo.amax); }
   bool fp8_down() const { return (d.flags & FRT_FLAG_FP8_MFMA_DOWN) != 0u; }
+  bool act_scales_set() const {
+    for (int l = 0; l < d.L; ++l)
+      if (!(s_x[l] > 0.0f) || !(s_h[l] > 0.0f)) return false;
+    return true;
+  }
   bool all_weights() const {
     for (auto v : w_set)
       if (!v) return false;
@@ -412,13 +416,17 @@ frt_status frt_export_weight_codes(const frt_plan* p, int32_t layer, int32_t whi
 }
 
 frt_status frt_calibrate(frt_plan* p, const void* const* d_r_batches, const void* const* d_y_batches,
-                         int32_t nbatch, int32_t rows, void* stream) {
+                         int32_t nbatch, int32_t rows, int32_t layer_begin, int32_t layer_end,
+                         void* stream) {
   if (!p || !d_r_batches) return fail(FRT_ERR_INVALID_ARG, "frt_calibrate: NULL argument");
   if (nbatch < 1 || rows < 1 || rows > p->d.M)
     return fail(FRT_ERR_INVALID_ARG, "frt_calibrate: nbatch %d rows %d (1..%d)", nbatch, rows, p->d.M);
+  if (layer_begin < 0 || layer_end > p->d.L || layer_begin >= layer_end)
+    return fail(FRT_ERR_INVALID_ARG, "frt_calibrate: bad layer range [%d, %d)", layer_begin, layer_end);
   for (int b = 0; b < nbatch; ++b)
     if (!d_r_batches[b]) return fail(FRT_ERR_INVALID_ARG, "frt_calibrate: batch %d residual is NULL", b);
-  if (!p->all_weights()) return fail(FRT_ERR_STATE, "frt_calibrate: weights not set for every layer");
+  for (int l = layer_begin; l < layer_end; ++l)
+    if (!p->w_set[l]) return fail(FRT_ERR_STATE, "frt_calibrate: weights of layer %d not set", l);
   DeviceGuard g(p->d.device);
   HIP_CHECK(g.err);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -433,7 +441,7 @@ frt_status frt_calibrate(frt_plan* p, const void* const* d_r_batches, const void
   for (int b = 0; b < nbatch; ++b) {
     const uint16_t* r_cur = static_cast<const uint16_t*>(d_r_batches[b]);
     const uint16_t* y_cur = d_y_batches ? static_cast<const uint16_t*>(d_y_batches[b]) : nullptr;
-    for (int l = 0; l < L; ++l) {
+    for (int l = layer_begin; l < layer_end; ++l) {
       uint16_t* r_next = cr + (size_t)(l & 1) * rh;
       uint16_t* y_next = cy + (size_t)(l & 1) * rh;
       KERNEL_CHECK(launch_add_rmsnorm_measure(r_cur, y_cur, p->wn(l), r_next, x, am + l, rows, H,
@@ -448,13 +456,14 @@ frt_status frt_calibrate(frt_plan* p, const void* const* d_r_batches, const void
   std::vector<float> hm(2 * L);
   HIP_CHECK(hipMemcpyAsync(hm.data(), am, sizeof(float) * 2 * L, hipMemcpyDeviceToHost, s));
   HIP_CHECK(hipStreamSynchronize(s));
-  for (int l = 0; l < L; ++l) {
+  for (int l = layer_begin; l < layer_end; ++l) {
     if (!std::isfinite(hm[l]) || !std::isfinite(hm[L + l]))
       return fail(FRT_ERR_INVALID_ARG, "frt_calibrate: non-finite activation at layer %d", l);
+  }
+  for (int l = layer_begin; l < layer_end; ++l) {
     p->s_x[l] = hm[l] > 0.0f ? hm[l] / 448.0f : 1.0f;
     p->s_h[l] = hm[L + l] > 0.0f ? hm[L + l] / 448.0f : 1.0f;
   }
-  p->act_scales_set = true;
   p->mark_stale();
   return FRT_OK;
 }
@@ -480,7 +489,6 @@ frt_status frt_set_act_scales(frt_plan* p, const float* host_in) {
     p->s_x[l] = host_in[2 * l];
     p->s_h[l] = host_in[2 * l + 1];
   }
-  p->act_scales_set = true;
   p->mark_stale();
   return FRT_OK;
 }
@@ -536,7 +544,7 @@ frt_status frt_ffn_forward_range(frt_plan* p, int32_t layer_begin, int32_t layer
     return fail(FRT_ERR_INVALID_ARG, "frt_ffn_forward_range: bad range [%d, %d)", layer_begin, layer_end);
   for (int l = layer_begin; l < layer_end; ++l)
     if (!p->w_set[l]) return fail(FRT_ERR_STATE, "frt_ffn_forward_range: weights of layer %d not set", l);
-  if (!p->act_scales_set) return fail(FRT_ERR_STATE, "frt_ffn_forward_range: activation scales not set");
+  if (!p->act_scales_set()) return fail(FRT_ERR_STATE, "frt_ffn_forward_range: activation scales not set");
   DeviceGuard g(p->d.device);
   HIP_CHECK(g.err);
   return forward_range(p, layer_begin, layer_end, static_cast<hipStream_t>(stream));
@@ -549,7 +557,7 @@ frt_status frt_ffn_forward(frt_plan* p, void* stream) {
 
 frt_status frt_ffn_forward_profiled(frt_plan* p, void* stream, float* host_ms) {
   if (!p || !host_ms) return fail(FRT_ERR_INVALID_ARG, "frt_ffn_forward_profiled: NULL argument");
-  if (!p->all_weights() || !p->act_scales_set)
+  if (!p->all_weights() || !p->act_scales_set())
     return fail(FRT_ERR_STATE, "frt_ffn_forward_profiled: weights and activation scales must be set first");
   DeviceGuard g(p->d.device);
   HIP_CHECK(g.err);
@@ -577,7 +585,7 @@ frt_status frt_ffn_forward_profiled(frt_plan* p, void* stream, float* host_ms) {
 frt_status frt_graph_capture(frt_plan* p, void* stream) {
   if (!p) return fail(FRT_ERR_INVALID_ARG, "frt_graph_capture: plan is NULL");
   if (!stream) return fail(FRT_ERR_INVALID_ARG, "frt_graph_capture: the null stream cannot be captured");
-  if (!p->all_weights() || !p->act_scales_set)
+  if (!p->all_weights() || !p->act_scales_set())
     return fail(FRT_ERR_STATE, "frt_graph_capture: weights and activation scales must be set first");
   DeviceGuard g(p->d.device);
   HIP_CHECK(g.err);

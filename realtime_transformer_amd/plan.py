@@ -110,8 +110,10 @@ class FFNPlan:
         a = np.stack([np.asarray(s_x, np.float32), np.asarray(s_h, np.float32)], axis=1)
         _abi.frt_set_act_scales(self.plan, a)
 
-    def calibrate(self, batches, rows: Optional[int] = None):
-        """batches: list of (r, y-or-None) numpy uint16 arrays [rows][H]."""
+    def calibrate(self, batches, rows: Optional[int] = None, layer_begin: int = 0,
+                  layer_end: Optional[int] = None):
+        """batches: list of (r, y-or-None) numpy uint16 arrays [rows][H] entering layer_begin."""
+        layer_end = self.L if layer_end is None else layer_end
         rows = rows if rows is not None else batches[0][0].shape[0]
         rs = [_to_dev_u16(r, self.device) for r, _ in batches]
         ys = None
@@ -119,7 +121,8 @@ class FFNPlan:
             ys = [_to_dev_u16(y, self.device) for _, y in batches]
         torch.cuda.synchronize(self.device)
         _abi.frt_calibrate(self.plan, [t.data_ptr() for t in rs],
-                           None if ys is None else [t.data_ptr() for t in ys], rows, self.s)
+                           None if ys is None else [t.data_ptr() for t in ys], rows, layer_begin,
+                           layer_end, self.s)
         del rs, ys
 
     def set_inputs(self, r0: np.ndarray, y0: Optional[np.ndarray]):

@@ -33,6 +33,8 @@ from realtime_transformer_amd import datagen
 from realtime_transformer_amd.configs import FFNConfig
 from realtime_transformer_amd.plan import FFNPlan, to_np_u16, to_np_u8
 
+import _natural
+
 CODE_RATE = 1e-4
 Y_MAX_REL = 2e-2
 MIN_COS = 0.999
@@ -45,6 +47,17 @@ MIN_COS = 0.999
 # then moves by up to a few of those steps: CAL_RTOL.
 CAL_RTOL_FIRST = 1e-4
 CAL_RTOL = 1e-2
+# Free-running chain: the GPU's distance from the oracle (1 - cosine of Z)
+# may be at most DRIFT_FACTOR times the distance between the oracle and a
+# second valid implementation (fp32 GEMM sums in BLAS order), plus a floor
+# for chains too short to drift at all.
+DRIFT_FACTOR = 4.0
+DRIFT_FLOOR = 1e-6
+# Free-running whole-chain calibration: after tens of layers the measurement
+# chains of two valid implementations (fp32 vs fp64 sums) drift apart by a
+# few percent in amax; gated only as a sanity bound.  The per-layer check
+# below feeds both sides the same states and is gated at CAL_RTOL_FIRST.
+CAL_DRIFT_MAX = 0.1
 
 
 def log(msg: str):
@@ -125,18 +138,21 @@ class CaseReport:
     y_max_rel: float = 0.0
     y_min_cos: float = 1.0
     z_cos: float = 1.0
+    z_dist: float = 0.0
+    z_dist_natural: float = 0.0
     z_max_rel: float = 0.0
     cal_max_rel: float = 0.0
+    cal_tf_max_rel: float = 0.0
     saturated_codes: int = 0
     seconds: float = 0.0
 
 
 def run_case(cfg: FFNConfig, rows: Optional[Sequence[int]] = None, cal_rows: Optional[Sequence[int]] = None,
              check_layers: Optional[Sequence[int]] = None, nbatch: int = 4, flags: int = 0,
-             z_min_cos: Optional[float] = MIN_COS) -> CaseReport:
+             gate_drift: bool = True) -> CaseReport:
     """Full parity procedure; rows / cal_rows select the evaluated / calibration
     rows (None = all); check_layers selects the teacher-forced layers (None = all);
-    flags are plan flags; z_min_cos gates the free-running chain (None: report only)."""
+    flags are plan flags; gate_drift gates the free-running chain (else report only)."""
     t0 = time.time()
     rep = CaseReport(cfg.name)
     M, H, I, L, act = cfg.M, cfg.H, cfg.I, cfg.L, cfg.act
@@ -168,11 +184,19 @@ def run_case(cfg: FFNConfig, rows: Optional[Sequence[int]] = None, cal_rows: Opt
                     assert nbad == 0, "layer %d %s weight codes: %d mismatches" % (l, nm, nbad)
                 weight_scales.append((lw.s_g, lw.s_u, lw.s_d))
                 norm_w[l] = wn
+                if L > 4 and (l % 4 == 3 or l == L - 1):
+                    log("[case %s] layers 0..%d quantised and compared (%.1fs)" % (cfg.name, l, time.time() - t0))
                 return lw
             return get
 
+        nat = {"r": r0[rows], "y": None if y0 is None else y0[rows]}
+
+        def natural_step(li, lw, s_x, s_h):
+            nat["r"], nat["y"] = _natural.block_fp32_sums(nat["r"], nat["y"], lw, act, cfg.eps, s_x, s_h)
+
         orc = oracle.calibrate_and_run((provider(l) for l in range(L)), act, cfg.eps,
-                                       r0[rows], None if y0 is None else y0[rows], cal)
+                                       r0[rows], None if y0 is None else y0[rows], cal,
+                                       keep_cal_states=True, post_layer=natural_step)
         log("[case %s] weights bit-exact; oracle chain done (%.1fs)" % (cfg.name, time.time() - t0))
 
         sc = plan.scales()
@@ -189,8 +213,17 @@ def run_case(cfg: FFNConfig, rows: Optional[Sequence[int]] = None, cal_rows: Opt
         rep.cal_max_rel = float(max(rel_x.max(), rel_h.max()))
         assert max(rel_x[0], rel_h[0]) <= CAL_RTOL_FIRST, "first-layer calibration scales differ by %.3g" % max(
             rel_x[0], rel_h[0])
-        assert rep.cal_max_rel <= CAL_RTOL, "calibration scales differ by %.3g" % rep.cal_max_rel
-        log("[case %s] calibration scales within %.2e" % (cfg.name, rep.cal_max_rel))
+        assert rep.cal_max_rel <= CAL_DRIFT_MAX, "calibration scales drift by %.3g" % rep.cal_max_rel
+        # teacher-forced calibration: each checked layer measured from the
+        # oracle's own measurement states entering it
+        tf_layers = range(L) if check_layers is None else check_layers
+        for l in tf_layers:
+            plan.calibrate(orc.cal_states[l], layer_begin=l, layer_end=l + 1)
+        sc = plan.scales()
+        tf = [max(abs(sc[l, 0] / orc.s_x[l] - 1), abs(sc[l, 3] / orc.s_h[l] - 1)) for l in tf_layers]
+        rep.cal_tf_max_rel = float(max(tf))
+        assert rep.cal_tf_max_rel <= CAL_RTOL_FIRST, "per-layer calibration scales differ by %.3g" % rep.cal_tf_max_rel
+        log("[case %s] calibration: chain drift %.2e, per-layer %.2e" % (cfg.name, rep.cal_max_rel, rep.cal_tf_max_rel))
 
         # the forward uses the oracle's scales (cache-hit path)
         plan.set_act_scales(orc.s_x, orc.s_h)
@@ -214,10 +247,15 @@ def run_case(cfg: FFNConfig, rows: Optional[Sequence[int]] = None, cal_rows: Opt
                 assert not np.any((codes & 0x7F) == 0x7F), "NaN code in layer %d" % l
                 rep.saturated_codes += int(np.count_nonzero((codes & 0x7F) == 0x7E))
         z_ref = oracle.final_hidden(orc.r[L], orc.y[L])
+        z_nat = oracle.final_hidden(nat["r"], nat["y"])
         rep.z_max_rel, rep.z_cos = y_metrics(z_graph[rows], z_ref)
-        if z_min_cos is not None:
-            assert rep.z_cos >= z_min_cos, "free-running Z cosine %.6f" % rep.z_cos
-        log("[case %s] graph == eager; Z cos %.6f max rel %.3g" % (cfg.name, rep.z_cos, rep.z_max_rel))
+        rep.z_dist = _natural.cos_distance(z_graph[rows], z_ref)
+        rep.z_dist_natural = _natural.cos_distance(z_nat, z_ref)
+        log("[case %s] graph == eager; Z cos %.6f max rel %.3g; drift %.3g vs natural %.3g" % (
+            cfg.name, rep.z_cos, rep.z_max_rel, rep.z_dist, rep.z_dist_natural))
+        if gate_drift:
+            assert rep.z_dist <= DRIFT_FACTOR * rep.z_dist_natural + DRIFT_FLOOR, \
+                "free-running drift %.3g > %g x natural %.3g" % (rep.z_dist, DRIFT_FACTOR, rep.z_dist_natural)
 
         # teacher-forced per-block checks
         idx = torch.as_tensor(rows, device=plan.device)

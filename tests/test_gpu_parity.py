@@ -42,7 +42,7 @@ def test_small_shapes_fp8_down(spec):
     # tolerance still holds; the free-running drift is reported, not gated
     idx, M, H, I, L, act = spec
     cfg = FFNConfig(idx, "small_fp8dn_%d" % idx, M, H, I, L, act)
-    rep = run_case(cfg, flags=1, z_min_cos=None)
+    rep = run_case(cfg, flags=1, gate_drift=False)
     log(str(rep))
 
 
@@ -68,7 +68,7 @@ def test_vlm_prefix_m788_full_size():
 
 @pytest.mark.timeout(900)
 def test_llm_decode_m1_full_size():
-    rep = run_case(CONFIGS[4], check_layers=[0, 1, 31, 62, 63])
+    rep = run_case(CONFIGS[4])
     log(str(rep))
 
 
@@ -78,5 +78,5 @@ def test_dit_video_m4096_full_size():
     rng = np.random.default_rng(53)
     rows = sorted(rng.choice(cfg.M, 48, replace=False).tolist())
     cal_rows = sorted(rng.choice(cfg.M, 12, replace=False).tolist())
-    rep = run_case(cfg, rows=rows, cal_rows=cal_rows, check_layers=[0, 1, 14, 29])
+    rep = run_case(cfg, rows=rows, cal_rows=cal_rows)
     log(str(rep))
