@@ -37,6 +37,21 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def recorded_traffic(kernel_file_record):
+    """HBM bytes per launch from the committed rocprofv3 counter record, or None
+    if the kernel sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", kernel_file_record)
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    for rel, digest in rec.get("sources_sha256", {}).items():
+        f = os.path.join(ROOT, rel)
+        if not os.path.exists(f) or hashlib.sha256(open(f, "rb").read()).hexdigest() != digest:
+            return None
+    return rec.get("bytes_per_launch")
+
+
 def setup(cfg, calibrate=True, keep_layers=()):
     """Plan with every layer quantised, calibrated, inputs set, graph captured."""
     from realtime_transformer_amd import datagen
@@ -80,9 +95,10 @@ def time_replays(plan, steps, warmup):
 
 
 def per_kernel_ms(plan, reps=3):
-    """Median over reps of each kernel's duration, averaged over layers: [norm, gate/up, down]."""
-    runs = np.stack([plan.forward_profiled() for _ in range(reps)])  # reps x L x 3
-    return np.median(runs, axis=0).mean(axis=0)
+    """Average duration (ms) of each kernel kind [norm, gate/up, down]: every
+    layer's launch of that kind back to back between two HIP events on the
+    plan's stream, reps times."""
+    return [plan.time_kernel(k, reps) / 1000.0 for k in range(3)]
 
 
 def cpu_baseline(cfg, kept, inputs, budget_s):
@@ -122,6 +138,9 @@ def main():
     ap.add_argument("--secondary", default="vlm_prefix_m788", help="second workload or 'none'")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="first copy this many MiB device-to-device once (a plain copy kernel of known "
+                         "size against which HBM byte counters are scaled)")
     ap.add_argument("--no-calibrate", action="store_true",
                     help="skip the calibration pass (scales fixed to 1/448-ish); for profiling runs")
     args = ap.parse_args()
@@ -137,6 +156,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     _abi.load(build_if_missing=False)
+
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy probe: %d bytes read, %d bytes written" % (n, n))
+        del src, dst
 
     cfg = BY_NAME[args.workload]
     plan, kept, inputs = setup(cfg, calibrate=not args.no_calibrate, keep_layers=(0, 1))
@@ -174,7 +203,9 @@ def main():
                    "wall_s_timed": round(wall, 4)},
         "roofline": {"bound": "hbm", "kernel": "gemv_gateup", "achieved": round(gu_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": gu_bytes,
+                     "traffic": recorded_traffic("traffic_gemv_gateup_llm_decode_m1.json")
+                     if cfg.name == "llm_decode_m1" else None,
+                     "bytes_per_launch": gu_bytes,
                      "avg_launch_us": round(float(kms[1]) * 1000, 3),
                      "kernel_us": {"norm_quant": round(float(kms[0]) * 1000, 3),
                                    "gateup": round(float(kms[1]) * 1000, 3),
@@ -205,7 +236,8 @@ def main():
                                    "mfma": "f16 (FP8 operands converted exactly)",
                                    "frac_of_f16_peak": round(gu_tf / F16_PEAK_TFLOPS, 4)},
                         "down": {"us": round(float(k2[2]) * 1000, 3), "tflops": round(dn_tf, 1),
-                                 "mfma": "fp8", "frac_of_fp8_peak": round(dn_tf / FP8_PEAK_TFLOPS, 4)},
+                                 "mfma": "f16 (FP8 operands converted exactly)",
+                                 "frac_of_f16_peak": round(dn_tf / F16_PEAK_TFLOPS, 4)},
                         "norm_quant": {"us": round(float(k2[0]) * 1000, 3)}},
         }
         log("[bench %s] %.3f ms/step (%.2f us/layer), %.1f TFLOP/s chain" % (c2.name, ms2, us2, chain_tf))

@@ -202,6 +202,15 @@ frt_status frt_graph_replay(frt_plan *plan, void *stream);
  * `stream`.  For measuring per-kernel time inside a running program. */
 frt_status frt_ffn_forward_profiled(frt_plan *plan, void *stream, float *host_ms);
 
+/* Average duration in microseconds of one kernel kind (which: 0 norm +
+ * quantise, 1 gate/up GEMM, 2 down GEMM): launches it for every layer, `reps`
+ * times, back to back on `stream` between two HIP events (same kernels and
+ * launch configuration as the forward; each launch recomputes the same slot
+ * from the same inputs, so the plan's state is unchanged).  Synchronises
+ * `stream`. */
+frt_status frt_ffn_time_kernel(frt_plan *plan, int32_t which, int32_t reps, void *stream,
+                               float *avg_us);
+
 /* Device E4M3 quantiser as used by every kernel: out[i] = e4m3(in[i]) with
  * saturation to +-448 and round-to-nearest-even.  d_in device float[n],
  * d_out device uint8[n].  Asynchronous on `stream`.  For tests of the

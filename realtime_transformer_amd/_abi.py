@@ -35,7 +35,8 @@ EXPORTED = [
     "frt_ffn_workspace_size", "frt_ffn_plan_create", "frt_ffn_plan_destroy", "frt_quant_weights",
     "frt_export_weight_codes", "frt_calibrate", "frt_get_scales", "frt_set_act_scales",
     "frt_ffn_io_get", "frt_ffn_forward_range", "frt_ffn_forward", "frt_graph_capture",
-    "frt_graph_replay", "frt_ffn_forward_profiled", "frt_e4m3_encode_f32", "frt_last_error",
+    "frt_graph_replay", "frt_ffn_forward_profiled", "frt_ffn_time_kernel", "frt_e4m3_encode_f32",
+    "frt_last_error",
 ]
 
 
@@ -91,6 +92,7 @@ def load(build_if_missing: bool = True):
         "frt_graph_capture": [vp, vp],
         "frt_graph_replay": [vp, vp],
         "frt_ffn_forward_profiled": [vp, vp, ctypes.POINTER(ctypes.c_float)],
+        "frt_ffn_time_kernel": [vp, i32, i32, vp, ctypes.POINTER(ctypes.c_float)],
         "frt_e4m3_encode_f32": [vp, vp, ctypes.c_int64, vp],
     }
     for name, args in sig.items():
@@ -186,6 +188,12 @@ def frt_ffn_forward_profiled(plan: int, stream: int, L: int) -> np.ndarray:
     out = np.zeros((L, 3), dtype=np.float32)
     _check(load().frt_ffn_forward_profiled(plan, stream, out.ctypes.data_as(ctypes.POINTER(ctypes.c_float))))
     return out
+
+
+def frt_ffn_time_kernel(plan: int, which: int, reps: int, stream: int) -> float:
+    out = ctypes.c_float(0.0)
+    _check(load().frt_ffn_time_kernel(plan, which, reps, stream, ctypes.byref(out)))
+    return float(out.value)
 
 
 def frt_e4m3_encode_f32(d_in: int, d_out: int, n: int, stream: int) -> None:

@@ -506,32 +506,45 @@ frt_status frt_ffn_io_get(const frt_plan* p, frt_ffn_io* out) {
   return FRT_OK;
 }
 
-static frt_status forward_range(frt_plan* p, int lb, int le, hipStream_t s,
-                                const hipEvent_t* ev = nullptr) {
-  const int M = p->d.M, H = p->d.H, I = p->d.I, L = p->d.L;
+// Launch kernel `which` (0: add+RMSNorm+quantise, 1: gate/up GEMM, 2: down
+// GEMM) of layer l on stream s.
+static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t s) {
+  const int M = p->d.M, H = p->d.H, I = p->d.I;
   const int npk = p->gated ? 2 * I : I;
-  for (int l = lb; l < le; ++l) {
-    const hipEvent_t* e = ev ? ev + 4 * (l - lb) : nullptr;
-    if (e) HIP_CHECK(hipEventRecord(e[0], s));
-    const float s_x = p->s_x[l], s_h = p->s_h[l];
-    const float inv_x = 1.0f / s_x, inv_h = 1.0f / s_h;
-    const float a_g = s_x * p->s_g[l], a_u = s_x * p->s_u[l], a_d = s_h * p->s_d[l];
+  const float s_x = p->s_x[l], s_h = p->s_h[l];
+  const float inv_x = 1.0f / s_x, inv_h = 1.0f / s_h;
+  const float a_g = s_x * p->s_g[l], a_u = s_x * p->s_u[l], a_d = s_h * p->s_d[l];
+  if (which == 0) {
     KERNEL_CHECK(launch_add_rmsnorm_quant(p->r(l), p->y(l), p->wn(l), p->r(l + 1), p->xq(l), M, H,
                                           p->d.eps, inv_x, s), "add_rmsnorm_quant");
-    if (e) HIP_CHECK(hipEventRecord(e[1], s));
+  } else if (which == 1) {
     if (M <= kGemvMaxM)
       KERNEL_CHECK(launch_gemv_gateup(p->d.act, p->xq(l), p->wgu(l), p->hq(l), M, H, I, p->lo.s_gu,
                                       a_g, a_u, inv_h, s), "gemv_gateup");
     else
       KERNEL_CHECK(launch_gemm_gateup(p->d.act, p->xq(l), p->wgu(l), p->hq(l), M, H, npk, a_g, a_u,
                                       inv_h, s), "gemm_gateup");
-    if (e) HIP_CHECK(hipEventRecord(e[2], s));
+  } else {
     if (M <= kGemvMaxM)
       KERNEL_CHECK(launch_gemv_down(p->hq(l), p->wd(l), p->y(l + 1), M, I, H, p->lo.s_dn, p->fp8_down(),
                                     a_d, s), "gemv_down");
     else
       KERNEL_CHECK(launch_gemm_down(p->hq(l), p->wd(l), p->y(l + 1), p->part(), p->cnt(1), M, I, H,
                                     p->lo.s_dn, p->fp8_down(), a_d, s), "gemm_down");
+  }
+  return FRT_OK;
+}
+
+static frt_status forward_range(frt_plan* p, int lb, int le, hipStream_t s,
+                                const hipEvent_t* ev = nullptr) {
+  const int L = p->d.L;
+  for (int l = lb; l < le; ++l) {
+    const hipEvent_t* e = ev ? ev + 4 * (l - lb) : nullptr;
+    for (int k = 0; k < 3; ++k) {
+      if (e) HIP_CHECK(hipEventRecord(e[k], s));
+      frt_status st = launch_layer_kernel(p, l, k, s);
+      if (st != FRT_OK) return st;
+    }
     if (e) HIP_CHECK(hipEventRecord(e[3], s));
   }
   if (le == L) KERNEL_CHECK(launch_residual_add(p->r(L), p->y(L), p->z(), p->mh(), s), "residual_add");
@@ -579,6 +592,38 @@ frt_status frt_ffn_forward_profiled(frt_plan* p, void* stream, float* host_ms) {
   for (int l = 0; l < L; ++l)
     for (int k = 0; k < 3; ++k)
       HIP_CHECK(hipEventElapsedTime(&host_ms[3 * l + k], p->prof_events[4 * l + k], p->prof_events[4 * l + k + 1]));
+  return FRT_OK;
+}
+
+frt_status frt_ffn_time_kernel(frt_plan* p, int32_t which, int32_t reps, void* stream, float* avg_us) {
+  if (!p || !avg_us) return fail(FRT_ERR_INVALID_ARG, "frt_ffn_time_kernel: NULL argument");
+  if (which < 0 || which > 2 || reps < 1)
+    return fail(FRT_ERR_INVALID_ARG, "frt_ffn_time_kernel: which %d reps %d", which, reps);
+  if (!p->all_weights() || !p->act_scales_set())
+    return fail(FRT_ERR_STATE, "frt_ffn_time_kernel: weights and activation scales must be set first");
+  DeviceGuard g(p->d.device);
+  HIP_CHECK(g.err);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  HIP_CHECK(hipEventCreate(&e0));
+  hipError_t err = hipEventCreate(&e1);
+  if (err != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return fail(FRT_ERR_HIP, "hipEventCreate failed: %s", hipGetErrorString(err));
+  }
+  frt_status st = FRT_OK;
+  float ms = 0.0f;
+  err = hipEventRecord(e0, s);
+  for (int r = 0; r < reps && st == FRT_OK && err == hipSuccess; ++r)
+    for (int l = 0; l < p->d.L && st == FRT_OK; ++l) st = launch_layer_kernel(p, l, which, s);
+  if (err == hipSuccess && st == FRT_OK) err = hipEventRecord(e1, s);
+  if (err == hipSuccess && st == FRT_OK) err = hipEventSynchronize(e1);
+  if (err == hipSuccess && st == FRT_OK) err = hipEventElapsedTime(&ms, e0, e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (st != FRT_OK) return st;
+  if (err != hipSuccess) return fail(FRT_ERR_HIP, "frt_ffn_time_kernel: event timing failed: %s", hipGetErrorString(err));
+  *avg_us = ms * 1000.0f / (float)((int64_t)reps * p->d.L);
   return FRT_OK;
 }
 

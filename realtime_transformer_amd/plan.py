@@ -145,6 +145,10 @@ class FFNPlan:
         """Per-kernel milliseconds [L][3] (norm+quantise, gate/up, down) of one eager forward."""
         return _abi.frt_ffn_forward_profiled(self.plan, self.s, self.L)
 
+    def time_kernel(self, which: int, reps: int = 3) -> float:
+        """Average microseconds of kernel kind `which` (0 norm, 1 gate/up, 2 down)."""
+        return _abi.frt_ffn_time_kernel(self.plan, which, reps, self.s)
+
     def capture(self):
         _abi.frt_graph_capture(self.plan, self.s)
 
