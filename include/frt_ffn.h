@@ -75,11 +75,20 @@ typedef enum {
  *   Without the flag every GEMM runs on the f16 matrix cores with exactly
  *   converted E4M3 operands (fp32-accurate accumulation). */
 #define FRT_FLAG_FP8_MFMA_DOWN 1u
+/* FRT_FLAG_FUSED_NORM: for M <= 16 (when M*H <= 32768) run the add +
+ *   RMSNorm + quantise step inside the gate/up GEMV kernel (two kernels per
+ *   layer); every workgroup recomputes the rows' norm from the L2-resident
+ *   inputs.  Results are identical to the separate kernel, which is the
+ *   default because it measures faster.  Ignored for other shapes. */
+#define FRT_FLAG_FUSED_NORM 2u
+/* FRT_FLAG_FP8_MFMA_GATEUP: the gate/up GEMM for M > 16 runs on the FP8
+ *   matrix cores (same accumulation behaviour as FRT_FLAG_FP8_MFMA_DOWN). */
+#define FRT_FLAG_FP8_MFMA_GATEUP 4u
 
 /* Problem description.  Requirements: M >= 1, L >= 1, H and I multiples of
  * 128, H <= 16384, I <= 32768, act in frt_act, eps > 0.  `device` is the HIP
- * device ordinal the plan and its workspace live on.  `flags` is 0 or
- * FRT_FLAG_FP8_MFMA_DOWN. */
+ * device ordinal the plan and its workspace live on.  `flags` is a bitwise OR
+ * of FRT_FLAG_* values (0 for the defaults). */
 typedef struct {
   int32_t M, H, I, L;
   int32_t act;
@@ -197,17 +206,18 @@ frt_status frt_graph_replay(frt_plan *plan, void *stream);
 
 /* Eager forward of the whole chain with a HIP event recorded on `stream`
  * before and after every kernel; writes each kernel's duration in
- * milliseconds to host_ms[L][3] = {norm+quantise, gate/up GEMM, down GEMM}.
+ * milliseconds to host_ms[L][3] = {norm+quantise, gate/up GEMM, down GEMM}
+ * (with the norm fused into gate/up, the first entry times an empty slot).
  * Same kernels and launch configuration as frt_ffn_forward.  Synchronises
  * `stream`.  For measuring per-kernel time inside a running program. */
 frt_status frt_ffn_forward_profiled(frt_plan *plan, void *stream, float *host_ms);
 
 /* Average duration in microseconds of one kernel kind (which: 0 norm +
- * quantise, 1 gate/up GEMM, 2 down GEMM): launches it for every layer, `reps`
- * times, back to back on `stream` between two HIP events (same kernels and
- * launch configuration as the forward; each launch recomputes the same slot
- * from the same inputs, so the plan's state is unchanged).  Synchronises
- * `stream`. */
+ * quantise, 1 gate/up GEMM (including the norm when fused), 2 down GEMM):
+ * launches it for every layer, `reps` times, back to back on `stream`
+ * between two HIP events (same kernels and launch configuration as the
+ * forward).  The activation slots are left undefined (run the forward or
+ * replay again before reading them).  Synchronises `stream`. */
 frt_status frt_ffn_time_kernel(frt_plan *plan, int32_t which, int32_t reps, void *stream,
                                float *avg_us);
 

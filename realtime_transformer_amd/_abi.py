@@ -27,6 +27,8 @@ FRT_ACT_SWIGLU = 1
 FRT_ACT_GELU_TANH = 2
 
 FRT_FLAG_FP8_MFMA_DOWN = 1
+FRT_FLAG_FUSED_NORM = 2
+FRT_FLAG_FP8_MFMA_GATEUP = 4
 
 _STATUS_NAMES = {0: "FRT_OK", 1: "FRT_ERR_INVALID_ARG", 2: "FRT_ERR_HIP", 3: "FRT_ERR_STATE",
                  4: "FRT_ERR_UNSUPPORTED", 5: "FRT_ERR_WORKSPACE"}

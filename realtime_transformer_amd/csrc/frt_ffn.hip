@@ -28,10 +28,12 @@
 
 namespace frt {
 hipError_t launch_add_rmsnorm_quant(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*,
-                                    uint8_t*, int, int, float, float, hipStream_t);
+                                    uint8_t*, int, int, float, float, hipStream_t, const float*, int,
+                                    float, uint16_t*);
 hipError_t launch_add_rmsnorm_measure(const uint16_t*, const uint16_t*, const uint16_t*,
                                       uint16_t*, float*, float*, int, int, float, hipStream_t);
-hipError_t launch_residual_add(const uint16_t*, const uint16_t*, uint16_t*, size_t, hipStream_t);
+hipError_t launch_residual_add(const uint16_t*, uint16_t*, uint16_t*, size_t, hipStream_t, const float*,
+                               int, float);
 hipError_t launch_e4m3_encode(const float*, uint8_t*, int64_t, hipStream_t);
 hipError_t launch_amax_bf16(const uint16_t*, size_t, float*, hipStream_t);
 hipError_t launch_quant_pack(const uint16_t*, uint8_t*, int, int, float, int, hipStream_t);
@@ -39,10 +41,17 @@ hipError_t launch_gemv_gateup(int, const uint8_t*, const uint8_t*, uint8_t*, int
                               float, float, float, hipStream_t);
 hipError_t launch_gemv_down(const uint8_t*, const uint8_t*, uint16_t*, int, int, int, int, bool,
                             float, hipStream_t);
-hipError_t launch_gemm_gateup(int, const uint8_t*, const uint8_t*, uint8_t*, int, int, int, float,
-                              float, float, hipStream_t);
-hipError_t launch_gemm_down(const uint8_t*, const uint8_t*, uint16_t*, float*, uint32_t*, int,
-                            int, int, int, bool, float, hipStream_t);
+bool gemv_fused_supported(int, int, int);
+hipError_t launch_gemv_gateup_fused(int, const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*,
+                                    uint8_t*, const uint8_t*, uint8_t*, int, int, int, int, float,
+                                    float, float, float, float, hipStream_t);
+hipError_t launch_gemm_gateup(int, int, bool, const uint8_t*, const uint8_t*, uint8_t*, int, int, int,
+                              float, float, float, hipStream_t);
+hipError_t launch_gemm_down(int, const uint8_t*, const uint8_t*, uint16_t*, float*, int, int, int, int,
+                            bool, float, hipStream_t);
+bool gemm_config_ok(int, bool);
+int gemm_config_bm(int);
+int gemm_config_bn(int);
 hipError_t launch_calib_gateup(int, const float*, const uint8_t*, float*, float*, int, int, int,
                                float, float, hipStream_t);
 hipError_t launch_calib_down(const float*, const uint8_t*, uint16_t*, int, int, int, float,
@@ -129,6 +138,7 @@ struct Layout {
   size_t cal_x, cal_h, cal_r, cal_y;
   size_t total;
   int s_gu, s_dn;  // GEMV: waves per workgroup; GEMM: K splits of the down GEMM
+  int cfg_gu, cfg_dn;  // GEMM tile configurations
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -140,12 +150,45 @@ bool desc_ok(const frt_ffn_desc* d) {
   if (d->H > 16384 || d->I > 32768) return false;
   if (d->act < FRT_ACT_GEGLU_TANH || d->act > FRT_ACT_GELU_TANH) return false;
   if (!(d->eps > 0.0f) || !std::isfinite(d->eps)) return false;
-  if ((d->flags & ~(uint32_t)FRT_FLAG_FP8_MFMA_DOWN) != 0u || d->device < 0) return false;
+  if ((d->flags & ~(uint32_t)(FRT_FLAG_FP8_MFMA_DOWN | FRT_FLAG_FUSED_NORM | FRT_FLAG_FP8_MFMA_GATEUP)) != 0u || d->device < 0)
+    return false;
   if ((int64_t)d->M * d->I > (int64_t)1 << 31) return false;
   return true;
 }
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+int env_int(const char* name, int dflt) {
+  const char* e = getenv(name);
+  return (e && *e) ? atoi(e) : dflt;
+}
+
+constexpr int kCUs = 256;  // MI355X compute units (workgroup rounds are counted against them)
+
+// GEMM tile configurations for M > 16 (see k_gemm.hip): the gate/up GEMM
+// takes the largest tile whose workgroups fill the chip; the down GEMM (few
+// output columns) takes 128 x 256 tiles and splits K until about two
+// workgroups per CU, its splits summed by the consumer.
+// FRT_GEMM_GATEUP_CFG / FRT_GEMM_DOWN_CFG / FRT_GEMM_DOWN_SPLIT override.
+void choose_gemm(const frt_ffn_desc& d, Layout& lo) {
+  const int npk = d.act != FRT_ACT_GELU_TANH ? 2 * d.I : d.I;
+  const bool fp8_gu = (d.flags & FRT_FLAG_FP8_MFMA_GATEUP) != 0u;
+  const bool fp8_dn = (d.flags & FRT_FLAG_FP8_MFMA_DOWN) != 0u;
+  int gu = env_int("FRT_GEMM_GATEUP_CFG", 1);
+  if (!gemm_config_ok(gu, fp8_gu) || npk % gemm_config_bn(gu)) gu = 0;
+  int dn = env_int("FRT_GEMM_DOWN_CFG", 1);
+  if (!gemm_config_ok(dn, fp8_dn) || d.H % gemm_config_bn(dn)) dn = 0;
+  const int tiles = (d.H / gemm_config_bn(dn)) * ceil_div(d.M, gemm_config_bm(dn));
+  const int kb = d.I / 128;
+  int split = std::max(1, std::min(16, ceil_div(2 * kCUs, tiles)));
+  split = std::min(split, std::max(1, kb / 4));
+  split = env_int("FRT_GEMM_DOWN_SPLIT", split);
+  split = std::max(1, std::min(split, kb));
+  lo.cfg_gu = gu;
+  lo.cfg_dn = dn;
+  lo.s_gu = 1;
+  lo.s_dn = split;
+}
 
 Layout make_layout(const frt_ffn_desc& d) {
   Layout lo{};
@@ -176,17 +219,9 @@ Layout make_layout(const frt_ffn_desc& d) {
     part = 4;
     words = 1;
   } else {
-    const int tiles = (int)(H / 128) * ceil_div(d.M, 128);
-    const int kb_d = (int)(I / 128);
-    int s = std::max(1, ceil_div(512, tiles));
-    s = std::min(s, 16);
-    s = std::min(s, std::max(1, kb_d / 2));
-    if (const char* e = getenv("FRT_GEMM_DOWN_SPLIT"))
-      if (*e) s = std::max(1, std::min(atoi(e), std::max(1, kb_d)));
-    lo.s_gu = 1;
-    lo.s_dn = s;
-    part = s > 1 ? (size_t)s * M * H * 4 : 4;
-    words = (size_t)tiles;
+    choose_gemm(d, lo);
+    part = lo.s_dn > 1 ? (size_t)lo.s_dn * M * H * 4 : 4;
+    words = 1;
   }
   lo.part = take(part);
   lo.part_bytes = part;
@@ -230,6 +265,12 @@ struct frt_plan {
   }
   float* amax() const { return reinterpret_cast<float*>(ws + lo.amax); }
   bool fp8_down() const { return (d.flags & FRT_FLAG_FP8_MFMA_DOWN) != 0u; }
+  bool fp8_gateup() const { return (d.flags & FRT_FLAG_FP8_MFMA_GATEUP) != 0u; }
+  // optionally, decode shapes run the norm inside the gate/up GEMV
+  bool fused_norm() const {
+    return d.M <= kGemvMaxM && (d.flags & FRT_FLAG_FUSED_NORM) != 0u &&
+           gemv_fused_supported(d.M, d.H, lo.s_gu);
+  }
   bool act_scales_set() const {
     for (int l = 0; l < d.L; ++l)
       if (!(s_x[l] > 0.0f) || !(s_h[l] > 0.0f)) return false;
@@ -307,7 +348,7 @@ frt_status frt_ffn_plan_create(const frt_ffn_desc* desc, void* d_workspace, size
   p->lo = lo;
   p->ws = static_cast<uint8_t*>(d_workspace);
   p->gated = desc->act != FRT_ACT_GELU_TANH;
-  p->w_set.assign(desc->L, 0);
+  p->w_set.assign(desc->L, 0);  // (GEMM tiles chosen in make_layout)
   p->s_x.assign(desc->L, 0.0f);
   p->s_h.assign(desc->L, 0.0f);
   p->s_g.assign(desc->L, 1.0f);
@@ -507,47 +548,76 @@ frt_status frt_ffn_io_get(const frt_plan* p, frt_ffn_io* out) {
 }
 
 // Launch kernel `which` (0: add+RMSNorm+quantise, 1: gate/up GEMM, 2: down
-// GEMM) of layer l on stream s.
-static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t s) {
+// GEMM) of layer l on stream s.  When the norm is fused into the gate/up
+// kernel, `which` 0 launches nothing and 1 runs both steps.
+// Down output of layer l-1 still in split-K partials (GEMM path, split > 1)?
+static bool down_split(const frt_plan* p) { return p->d.M > kGemvMaxM && p->lo.s_dn > 1; }
+
+static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t s,
+                                      bool y_from_partials = false) {
   const int M = p->d.M, H = p->d.H, I = p->d.I;
   const int npk = p->gated ? 2 * I : I;
   const float s_x = p->s_x[l], s_h = p->s_h[l];
   const float inv_x = 1.0f / s_x, inv_h = 1.0f / s_h;
   const float a_g = s_x * p->s_g[l], a_u = s_x * p->s_u[l], a_d = s_h * p->s_d[l];
+  const bool fused = p->fused_norm();
   if (which == 0) {
-    KERNEL_CHECK(launch_add_rmsnorm_quant(p->r(l), p->y(l), p->wn(l), p->r(l + 1), p->xq(l), M, H,
-                                          p->d.eps, inv_x, s), "add_rmsnorm_quant");
+    if (!fused) {
+      const float* yp = nullptr;
+      float a_prev = 0.0f;
+      if (y_from_partials && l > 0) {
+        yp = p->part();
+        a_prev = p->s_h[l - 1] * p->s_d[l - 1];
+      }
+      KERNEL_CHECK(launch_add_rmsnorm_quant(p->r(l), p->y(l), p->wn(l), p->r(l + 1), p->xq(l), M, H,
+                                            p->d.eps, inv_x, s, yp, p->lo.s_dn, a_prev, p->y(l)),
+                   "add_rmsnorm_quant");
+    }
   } else if (which == 1) {
-    if (M <= kGemvMaxM)
+    if (fused)
+      KERNEL_CHECK(launch_gemv_gateup_fused(p->d.act, p->r(l), p->y(l), p->wn(l), p->r(l + 1), p->xq(l),
+                                            p->wgu(l), p->hq(l), M, H, I, p->lo.s_gu, p->d.eps, inv_x,
+                                            a_g, a_u, inv_h, s), "gemv_gateup_fused");
+    else if (M <= kGemvMaxM)
       KERNEL_CHECK(launch_gemv_gateup(p->d.act, p->xq(l), p->wgu(l), p->hq(l), M, H, I, p->lo.s_gu,
                                       a_g, a_u, inv_h, s), "gemv_gateup");
     else
-      KERNEL_CHECK(launch_gemm_gateup(p->d.act, p->xq(l), p->wgu(l), p->hq(l), M, H, npk, a_g, a_u,
-                                      inv_h, s), "gemm_gateup");
+      KERNEL_CHECK(launch_gemm_gateup(p->d.act, p->lo.cfg_gu, p->fp8_gateup(), p->xq(l), p->wgu(l),
+                                      p->hq(l), M, H, npk, a_g, a_u, inv_h, s), "gemm_gateup");
   } else {
     if (M <= kGemvMaxM)
       KERNEL_CHECK(launch_gemv_down(p->hq(l), p->wd(l), p->y(l + 1), M, I, H, p->lo.s_dn, p->fp8_down(),
                                     a_d, s), "gemv_down");
     else
-      KERNEL_CHECK(launch_gemm_down(p->hq(l), p->wd(l), p->y(l + 1), p->part(), p->cnt(1), M, I, H,
+      KERNEL_CHECK(launch_gemm_down(p->lo.cfg_dn, p->hq(l), p->wd(l), p->y(l + 1), p->part(), M, I, H,
                                     p->lo.s_dn, p->fp8_down(), a_d, s), "gemm_down");
   }
   return FRT_OK;
 }
 
+// Layers [lb, le): layer lb reads its Y slot; later layers take Y from the
+// previous down GEMM's split-K partials when it split.  After the last layer
+// of the range the Y slot is materialised (and Z formed after layer L-1).
 static frt_status forward_range(frt_plan* p, int lb, int le, hipStream_t s,
                                 const hipEvent_t* ev = nullptr) {
   const int L = p->d.L;
+  const bool split = down_split(p);
   for (int l = lb; l < le; ++l) {
     const hipEvent_t* e = ev ? ev + 4 * (l - lb) : nullptr;
     for (int k = 0; k < 3; ++k) {
       if (e) HIP_CHECK(hipEventRecord(e[k], s));
-      frt_status st = launch_layer_kernel(p, l, k, s);
+      frt_status st = launch_layer_kernel(p, l, k, s, split && l > lb);
       if (st != FRT_OK) return st;
     }
     if (e) HIP_CHECK(hipEventRecord(e[3], s));
   }
-  if (le == L) KERNEL_CHECK(launch_residual_add(p->r(L), p->y(L), p->z(), p->mh(), s), "residual_add");
+  const float a_last = p->s_h[le - 1] * p->s_d[le - 1];
+  if (le == L)
+    KERNEL_CHECK(launch_residual_add(p->r(L), p->y(L), p->z(), p->mh(), s, split ? p->part() : nullptr,
+                                     p->lo.s_dn, a_last), "residual_add");
+  else if (split)
+    KERNEL_CHECK(launch_residual_add(p->r(le), p->y(le), nullptr, p->mh(), s, p->part(), p->lo.s_dn, a_last),
+                 "finalize_y");
   return FRT_OK;
 }
 
@@ -615,7 +685,8 @@ frt_status frt_ffn_time_kernel(frt_plan* p, int32_t which, int32_t reps, void* s
   float ms = 0.0f;
   err = hipEventRecord(e0, s);
   for (int r = 0; r < reps && st == FRT_OK && err == hipSuccess; ++r)
-    for (int l = 0; l < p->d.L && st == FRT_OK; ++l) st = launch_layer_kernel(p, l, which, s);
+    for (int l = 0; l < p->d.L && st == FRT_OK; ++l)
+      st = launch_layer_kernel(p, l, which, s, down_split(p) && l > 0);
   if (err == hipSuccess && st == FRT_OK) err = hipEventRecord(e1, s);
   if (err == hipSuccess && st == FRT_OK) err = hipEventSynchronize(e1);
   if (err == hipSuccess && st == FRT_OK) err = hipEventElapsedTime(&ms, e0, e1);

@@ -33,7 +33,7 @@
 
 namespace frt {
 
-enum { GU_GEGLU = 0, GU_SWIGLU = 1, GU_GELU = 2 };
+enum { GU_GEGLU = 0, GU_SWIGLU = 1, GU_GELU = 2, EPI_DOWN = 3 };
 
 template <int ACT>
 __device__ __forceinline__ float gated_h(float g, float u) {
@@ -182,35 +182,248 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup(const uint8_t* __restric
   }
 }
 
-template <int W, bool FP8>
+// Decode form of gate/up with the norm fused in front (one kernel instead of
+// two per layer; batch-1 time goes to kernel boundaries).  Every workgroup
+// recomputes R' = bf16(R + Y), the fp64 mean square and the E4M3 row XQ of
+// its M <= 16 rows into LDS (the inputs are a few KiB, L2-resident after the
+// first workgroup), then streams its 16 columns of gate/up weights exactly as
+// k_gemv_gateup does with the activation fragments read from LDS.  Workgroup
+// 0 also stores R' and XQ to their slots.  The first two K blocks of weights
+// are requested before the prologue so the HBM stream starts at once.
+// Row layout of the prologue: for M == 1 the whole workgroup shares the row
+// (chunks of 8 elements, at most NCH per thread kept in registers); for
+// M > 1 each wave takes rows wave, wave + W, ...
+constexpr int kFusedXqBytes = 32768;  // LDS for the quantised rows: M * H <= this
+
+template <int ACT, int W, int NCH, int G>
+__global__ __launch_bounds__(W * 64) void k_gemv_gateup_fused(
+    const uint16_t* __restrict__ r_prev, const uint16_t* __restrict__ y_prev,
+    const uint16_t* __restrict__ w_norm, uint16_t* __restrict__ r_out, uint8_t* __restrict__ xq_out,
+    const uint8_t* __restrict__ w, uint8_t* __restrict__ hq, int M, int K, int I, float eps,
+    float inv_x, float alpha_g, float alpha_u, float inv_h) {
+  constexpr bool GATED = ACT != GU_GELU;
+  constexpr int NACC = GATED ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) uint8_t xs[kFusedXqBytes];
+  __shared__ v4f red[W * NACC * 64];
+  __shared__ double dred[W];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool writer = blockIdx.x == 0;
+  const int KB = K >> 7;
+  const int kb0 = wave * KB / W, kb1 = (wave + 1) * KB / W;
+  const int P = I >> 4;
+  // this workgroup's column groups: blockIdx.x + g * gridDim.x, g < G
+  const int p0 = blockIdx.x;
+  const uint8_t* wg0 = w + (size_t)(GATED ? 2 * p0 : 0) * KB * 2048 + lane * 16;
+  const uint8_t* wu0 = w + (size_t)(GATED ? 2 * p0 + 1 : p0) * KB * 2048 + lane * 16;
+
+  // request the first two weight blocks of the first group before the prologue
+  uint32_t u0[8] = {}, u1[8] = {}, g0[8] = {}, g1[8] = {};
+  if (kb0 < kb1) {
+    load_w32(wu0, kb0, u0);
+    if (GATED) load_w32(wg0, kb0, g0);
+  }
+  if (kb0 + 1 < kb1) {
+    load_w32(wu0, kb0 + 1, u1);
+    if (GATED) load_w32(wg0, kb0 + 1, g1);
+  }
+
+  // ---- prologue: R' = bf16(R + Y), RMSNorm, E4M3 -> xs (once per workgroup) ----
+  const int nchunk = K >> 3;
+  const int group_threads = (M == 1) ? W * 64 : 64;
+  const int t_in = (M == 1) ? tid : lane;
+  for (int m = (M == 1) ? 0 : wave; m < M; m += (M == 1) ? 1 : W) {
+    const size_t base = (size_t)m * K;
+    uint4 rn[NCH], wn[NCH];
+    double sq = 0.0;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = t_in + c * group_threads;
+      rn[c] = make_uint4(0, 0, 0, 0);
+      wn[c] = rn[c];
+      if (ch < nchunk) {
+        const uint4 rv = *reinterpret_cast<const uint4*>(r_prev + base + (size_t)ch * 8);
+        const uint4 yv = *reinterpret_cast<const uint4*>(y_prev + base + (size_t)ch * 8);
+        wn[c] = *reinterpret_cast<const uint4*>(w_norm + (size_t)ch * 8);
+        const uint32_t rr[4] = {rv.x, rv.y, rv.z, rv.w}, yy[4] = {yv.x, yv.y, yv.z, yv.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          o[j] = pack_bf16x2(bf16_lo(rr[j]) + bf16_lo(yy[j]), bf16_hi(rr[j]) + bf16_hi(yy[j]));
+          const double dlo = (double)bf16_lo(o[j]), dhi = (double)bf16_hi(o[j]);
+          sq += dlo * dlo;
+          sq += dhi * dhi;
+        }
+        rn[c] = make_uint4(o[0], o[1], o[2], o[3]);
+        if (writer) *reinterpret_cast<uint4*>(r_out + base + (size_t)ch * 8) = rn[c];
+      }
+    }
+    sq = wave_sum_f64(sq);
+    if (M == 1) {
+      if (lane == 0) dred[wave] = sq;
+      __syncthreads();
+      sq = 0.0;
+#pragma unroll
+      for (int v = 0; v < W; ++v) sq += dred[v];
+    }
+    const float inv_rms = (float)(1.0 / sqrt(sq / (double)K + (double)eps));
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = t_in + c * group_threads;
+      if (ch < nchunk) {
+        const uint32_t ww[4] = {wn[c].x, wn[c].y, wn[c].z, wn[c].w};
+        const uint32_t rr[4] = {rn[c].x, rn[c].y, rn[c].z, rn[c].w};
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[2 * j] = (bf16_lo(rr[j]) * inv_rms) * bf16_lo(ww[j]);
+          x[2 * j + 1] = (bf16_hi(rr[j]) * inv_rms) * bf16_hi(ww[j]);
+        }
+        uint2 q;
+        q.x = e4m3x4(x[0] * inv_x, x[1] * inv_x, x[2] * inv_x, x[3] * inv_x);
+        q.y = e4m3x4(x[4] * inv_x, x[5] * inv_x, x[6] * inv_x, x[7] * inv_x);
+        *reinterpret_cast<uint2*>(xs + base + (size_t)ch * 8) = q;
+        if (writer) *reinterpret_cast<uint2*>(xq_out + base + (size_t)ch * 8) = q;
+      }
+    }
+  }
+  __syncthreads();
+
+  const int row = lane & 15, q = lane >> 4;
+  const bool has_row = row < M;
+  const uint8_t* xr = xs + (has_row ? row : 0) * K + q * 32;
+#pragma unroll 1
+  for (int gi = 0; gi < G; ++gi) {
+    const int p = p0 + gi * (int)gridDim.x;
+    if (p >= P) break;  // uniform across the workgroup
+    const uint8_t* wg = w + (size_t)(GATED ? 2 * p : 0) * KB * 2048 + lane * 16;
+    const uint8_t* wu = w + (size_t)(GATED ? 2 * p + 1 : p) * KB * 2048 + lane * 16;
+    v4f accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
+    int kb = kb0;
+    if (gi > 0) {
+      if (kb0 < kb1) {
+        load_w32(wu, kb0, u0);
+        if (GATED) load_w32(wg, kb0, g0);
+      }
+      if (kb0 + 1 < kb1) {
+        load_w32(wu, kb0 + 1, u1);
+        if (GATED) load_w32(wg, kb0 + 1, g1);
+      }
+    }
+    if (kb + 1 < kb1) {
+      uint32_t x0[8], x1[8];
+      load_x32(xr, has_row, kb, x0);
+      load_x32(xr, has_row, kb + 1, x1);
+      accu = mfma_f16_x4(x0, u0, accu);
+      if (GATED) accg = mfma_f16_x4(x0, g0, accg);
+      accu = mfma_f16_x4(x1, u1, accu);
+      if (GATED) accg = mfma_f16_x4(x1, g1, accg);
+      kb += 2;
+    } else if (kb < kb1) {
+      uint32_t x0[8];
+      load_x32(xr, has_row, kb, x0);
+      accu = mfma_f16_x4(x0, u0, accu);
+      if (GATED) accg = mfma_f16_x4(x0, g0, accg);
+      kb += 1;
+    }
+    for (; kb + 1 < kb1; kb += 2) {
+      uint32_t x0[8], x1[8], a0[8], a1[8], b0[8], b1[8];
+      load_w32(wu, kb, a0);
+      load_w32(wu, kb + 1, a1);
+      if (GATED) {
+        load_w32(wg, kb, b0);
+        load_w32(wg, kb + 1, b1);
+      }
+      load_x32(xr, has_row, kb, x0);
+      load_x32(xr, has_row, kb + 1, x1);
+      accu = mfma_f16_x4(x0, a0, accu);
+      if (GATED) accg = mfma_f16_x4(x0, b0, accg);
+      accu = mfma_f16_x4(x1, a1, accu);
+      if (GATED) accg = mfma_f16_x4(x1, b1, accg);
+    }
+    if (kb < kb1) {
+      uint32_t x0[8], a0[8], b0[8];
+      load_w32(wu, kb, a0);
+      if (GATED) load_w32(wg, kb, b0);
+      load_x32(xr, has_row, kb, x0);
+      accu = mfma_f16_x4(x0, a0, accu);
+      if (GATED) accg = mfma_f16_x4(x0, b0, accg);
+    }
+    red[(wave * NACC + 0) * 64 + lane] = accu;
+    if (GATED) red[(wave * NACC + NACC - 1) * 64 + lane] = accg;
+    __syncthreads();
+    if (wave == 0) {
+      accu = red[0 * 64 + lane];
+      if (GATED) accg = red[(NACC - 1) * 64 + lane];
+#pragma unroll
+      for (int v = 1; v < W; ++v) {
+        accu += red[(v * NACC + 0) * 64 + lane];
+        if (GATED) accg += red[(v * NACC + NACC - 1) * 64 + lane];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * q + r;
+        if (m < M) {
+          const float h = gated_h<ACT>(accg[r] * alpha_g, accu[r] * alpha_u);
+          hq[(size_t)m * I + p * 16 + row] = (uint8_t)e4m3x1(h * inv_h);
+        }
+      }
+    }
+    __syncthreads();  // red is reused by the next group
+  }
+}
+
+// Down GEMV.  COLS = 16: a workgroup owns one 16-row group of Wd; COLS = 8:
+// it owns half a group (lanes of the other half load nothing and their
+// accumulator columns are discarded), doubling the workgroups so that every
+// CU gets the same share when the group count is small (H/16 = 320 for
+// H = 5120 on 256 CUs).  Half-group loads still read whole 128-byte lines.
+template <int W, bool FP8, int COLS>
 __global__ __launch_bounds__(W * 64) void k_gemv_down(const uint8_t* __restrict__ hq,
                                                       const uint8_t* __restrict__ w,
                                                       uint16_t* __restrict__ y, int M, int K, int N,
                                                       float alpha_d) {
   __shared__ v4f red[W][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int p = blockIdx.x;
+  const int p = (COLS == 16) ? blockIdx.x : (blockIdx.x >> 1);
+  const int half = (COLS == 16) ? 0 : (blockIdx.x & 1);
   const int KB = K >> 7;
   const int kb0 = wave * KB / W, kb1 = (wave + 1) * KB / W;
   const int row = lane & 15, q = lane >> 4;
   const bool has_row = row < M;
+  const bool my_col = (COLS == 16) || ((row >> 3) == half);
   const uint8_t* wp = w + (size_t)p * KB * 2048 + lane * 16;
   const uint8_t* xr = hq + (size_t)(has_row ? row : 0) * K + q * 32;
+  const uint32_t zero8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 
   v4f acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
   int kb = kb0;
-  for (; kb + 1 < kb1; kb += 2) {
-    uint32_t x0[8], x1[8], w0[8], w1[8];
-    load_w32(wp, kb, w0);
-    load_w32(wp, kb + 1, w1);
+  for (; kb + 3 < kb1; kb += 4) {
+    uint32_t x0[8], x1[8], w0[8], w1[8], x2[8], x3[8], w2[8], w3[8];
+    if (my_col) {
+      load_w32(wp, kb, w0);
+      load_w32(wp, kb + 1, w1);
+      load_w32(wp, kb + 2, w2);
+      load_w32(wp, kb + 3, w3);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w0[i] = w1[i] = w2[i] = w3[i] = zero8[i];
+    }
     load_x32(xr, has_row, kb, x0);
     load_x32(xr, has_row, kb + 1, x1);
+    load_x32(xr, has_row, kb + 2, x2);
+    load_x32(xr, has_row, kb + 3, x3);
     acc0 = mfma_step<FP8>(x0, w0, acc0);
     acc1 = mfma_step<FP8>(x1, w1, acc1);
+    acc0 = mfma_step<FP8>(x2, w2, acc0);
+    acc1 = mfma_step<FP8>(x3, w3, acc1);
   }
-  if (kb < kb1) {
+  for (; kb < kb1; ++kb) {
     uint32_t x0[8], w0[8];
-    load_w32(wp, kb, w0);
+    if (my_col) load_w32(wp, kb, w0);
+    else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w0[i] = 0;
+    }
     load_x32(xr, has_row, kb, x0);
     acc0 = mfma_step<FP8>(x0, w0, acc0);
   }
@@ -223,6 +436,7 @@ __global__ __launch_bounds__(W * 64) void k_gemv_down(const uint8_t* __restrict_
 #pragma unroll
     for (int v = 1; v < W; ++v) acc += red[v][lane];
   }
+  if (!my_col) return;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = 4 * q + r;
@@ -233,200 +447,205 @@ __global__ __launch_bounds__(W * 64) void k_gemv_down(const uint8_t* __restrict_
 // ===========================================================================
 // GEMM path (M > 16)
 // ===========================================================================
+//
+// Workgroup tile BM rows x BN packed columns, K step 128, WGM x WGN waves of
+// (BM/WGM) x (BN/WGN).  Both operand tiles are staged through LDS in
+// fragment order (16-row blocks of 2 KiB, lane l's 16-byte halves at l*16 and
+// 1024 + l*16: every ds_read_b128 reads 1 KiB contiguously), double
+// buffered: the next step's global loads are in flight while the current
+// step computes.  The down GEMM may split K over gridDim.z; each split then
+// writes its fp32 partial tile and the consumer (the next layer's norm
+// kernel, or the final residual add) sums the splits in split order, so no
+// workgroup waits for another and no device-scope fence is needed.
 
-constexpr int BM = 128, BN = 128, BKB = 128;  // tile rows, packed tile columns, K step (bytes)
-constexpr int TILE_BYTES = 8 * 2048;            // 8 fragment blocks of 16 x 128
-
-// Stage one K step: A (activations, row-major [M][K]) into fragment order,
-// B (packed weights) verbatim.  Thread t moves 4 + 4 16-byte pieces.
-struct StageRegs {
-  uint4 a[4], b[4];
+template <int BM, int BN, int NT>
+struct Stage {
+  static constexpr int AP = BM * 8 / NT;  // 16-byte pieces per thread
+  static constexpr int BP = BN * 8 / NT;
+  uint4 a[AP], b[BP];
 };
 
-__device__ __forceinline__ void stage_load(StageRegs& st, const uint8_t* __restrict__ act, int M,
-                                           int K, int m0, const uint8_t* __restrict__ wt,
+template <int BM, int BN, int NT>
+__device__ __forceinline__ void stage_load(Stage<BM, BN, NT>& st, const uint8_t* __restrict__ act,
+                                           int M, int K, int m0, const uint8_t* __restrict__ wt,
                                            int g0, int KB, int kb) {
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = tid + 256 * j;  // 0..1023
-    const int r = c >> 3, kc = c & 7;
-    const int m = m0 + r;
+  for (int j = 0; j < Stage<BM, BN, NT>::AP; ++j) {
+    const int c = tid + NT * j;  // piece: row c / 8, 16-byte column c % 8
+    const int m = m0 + (c >> 3);
     st.a[j] = make_uint4(0, 0, 0, 0);
-    if (m < M) st.a[j] = ld16(act + (size_t)m * K + kb * 128 + kc * 16);
-    const int grp = c >> 7, off = (c & 127) * 16;
-    st.b[j] = ld16(wt + ((size_t)(g0 + grp) * KB + kb) * 2048 + off);
+    if (m < M) st.a[j] = ld16(act + (size_t)m * K + kb * 128 + (c & 7) * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < Stage<BM, BN, NT>::BP; ++j) {
+    const int c = tid + NT * j;  // piece: group c / 128, byte (c % 128) * 16
+    st.b[j] = ld16(wt + ((size_t)(g0 + (c >> 7)) * KB + kb) * 2048 + (c & 127) * 16);
   }
 }
-__device__ __forceinline__ void stage_store(const StageRegs& st, uint8_t* lds_a, uint8_t* lds_b) {
+
+// Both operands go to LDS as E4M3 bytes in the 2 KiB fragment order of the
+// packed weights (16-row block mg: half h of lane ln at mg*2048 + h*1024 +
+// ln*16, lane ln = row + 16 * (k-chunk / 2)), so one 1 KiB contiguous
+// ds_read_b128 per wave serves each half fragment.
+template <int BM, int BN, int NT>
+__device__ __forceinline__ void stage_store(const Stage<BM, BN, NT>& st, uint8_t* lds_a, uint8_t* lds_b) {
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = tid + 256 * j;
+  for (int j = 0; j < Stage<BM, BN, NT>::AP; ++j) {
+    const int c = tid + NT * j;
     const int r = c >> 3, kc = c & 7;
-    const int mg = r >> 4, ln = (r & 15) + 16 * (kc >> 1), half = kc & 1;
-    *reinterpret_cast<uint4*>(lds_a + mg * 2048 + half * 1024 + ln * 16) = st.a[j];
+    *reinterpret_cast<uint4*>(lds_a + (r >> 4) * 2048 + (kc & 1) * 1024 + ((r & 15) + 16 * (kc >> 1)) * 16) =
+        st.a[j];
+  }
+#pragma unroll
+  for (int j = 0; j < Stage<BM, BN, NT>::BP; ++j) {
+    const int c = tid + NT * j;
     *reinterpret_cast<uint4*>(lds_b + c * 16) = st.b[j];
   }
 }
 
-// MODE: GU_GEGLU / GU_SWIGLU / GU_GELU for gate/up, 3 for down (f16 matrix
-// cores), 4 for down on the FP8 matrix cores.
-template <int MODE>
-__global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ act,
-                                              const uint8_t* __restrict__ wt,
-                                              void* __restrict__ out, float* __restrict__ part,
-                                              uint32_t* __restrict__ cnt, int M, int K,
-                                              int Npk, int S, float alpha_a, float alpha_b,
-                                              float inv_out) {
-  constexpr bool DOWN = MODE >= 3;
-  constexpr bool FP8 = MODE == 4;
-  constexpr bool GATED = MODE == GU_GEGLU || MODE == GU_SWIGLU;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][TILE_BYTES];  // [buf][A/B]
-  int* s_last = reinterpret_cast<int*>(&lds[0][0][0]);  // reused after the main loop
+// EPI: GU_GEGLU / GU_SWIGLU / GU_GELU for gate/up (E4M3 output), EPI_DOWN for
+// down (bf16 output or fp32 split partials).  FP8: the products run on the
+// FP8 matrix cores (one 16x16x128 instruction per tile and K step), else on
+// the f16 matrix cores from exactly converted operands (four 16x16x32 steps).
+template <int EPI, bool FP8, int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const uint8_t* __restrict__ act,
+                                                         const uint8_t* __restrict__ wt,
+                                                         void* __restrict__ out, float* __restrict__ part,
+                                                         int M, int K, int Npk, int S, float alpha_a,
+                                                         float alpha_b, float inv_out) {
+  constexpr int NT = WGM * WGN * 64;
+  constexpr int MTM = BM / WGM / 16, MTN = BN / WGN / 16;  // 16x16 tiles per wave
+  constexpr bool DOWN = EPI == EPI_DOWN;
+  constexpr bool GATED = EPI == GU_GEGLU || EPI == GU_SWIGLU;
+  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+  static_assert(!GATED || (MTN % 2) == 0, "gated tiles hold whole gate/up pairs");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][A_BYTES + B_BYTES];
 
   const int tn = blockIdx.x, tm = blockIdx.y, s = blockIdx.z;
   const int m0 = tm * BM, g0 = tn * (BN / 16);
   const int KB = K >> 7;
   const int kb0 = s * KB / S, kb1 = (s + 1) * KB / S;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
 
-  v4f acc[4][4];
+  v4f acc[MTM][MTN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MTM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0, 0, 0, 0};
+    for (int j = 0; j < MTN; ++j) acc[i][j] = v4f{0, 0, 0, 0};
 
-  StageRegs st;
-  stage_load(st, act, M, K, m0, wt, g0, KB, kb0);
-  stage_store(st, lds[0][0], lds[0][1]);
+  Stage<BM, BN, NT> st;
+  stage_load<BM, BN, NT>(st, act, M, K, m0, wt, g0, KB, kb0);
+  stage_store<BM, BN, NT>(st, lds[0], lds[0] + A_BYTES);
   __syncthreads();
   int cur = 0;
   for (int kb = kb0; kb < kb1; ++kb) {
     const bool more = kb + 1 < kb1;
-    if (more) stage_load(st, act, M, K, m0, wt, g0, KB, kb + 1);
-    const uint8_t* la = lds[cur][0] + (wm * 4) * 2048 + lane * 16;
-    const uint8_t* lb = lds[cur][1] + (wn * 4) * 2048 + lane * 16;
-    uint32_t af[4][8], bf[4][8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      unpack8(*reinterpret_cast<const uint4*>(la + i * 2048),
-              *reinterpret_cast<const uint4*>(la + i * 2048 + 1024), af[i]);
-      unpack8(*reinterpret_cast<const uint4*>(lb + i * 2048),
-              *reinterpret_cast<const uint4*>(lb + i * 2048 + 1024), bf[i]);
-    }
+    if (more) stage_load<BM, BN, NT>(st, act, M, K, m0, wt, g0, KB, kb + 1);
+    const uint8_t* la = lds[cur] + (wm * MTM) * 2048 + lane * 16;
+    const uint8_t* lb = lds[cur] + A_BYTES + (wn * MTN) * 2048 + lane * 16;
     if (FP8) {
+      v8i af[MTM], bf[MTN];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MTM; ++i)
+        af[i] = as_v8i(*reinterpret_cast<const uint4*>(la + i * 2048),
+                       *reinterpret_cast<const uint4*>(la + i * 2048 + 1024));
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = mfma_fp8(as_v8i(make_uint4(af[i][0], af[i][1], af[i][2], af[i][3]),
-                                      make_uint4(af[i][4], af[i][5], af[i][6], af[i][7])),
-                               as_v8i(make_uint4(bf[j][0], bf[j][1], bf[j][2], bf[j][3]),
-                                      make_uint4(bf[j][4], bf[j][5], bf[j][6], bf[j][7])),
-                               acc[i][j]);
+      for (int j = 0; j < MTN; ++j)
+        bf[j] = as_v8i(*reinterpret_cast<const uint4*>(lb + j * 2048),
+                       *reinterpret_cast<const uint4*>(lb + j * 2048 + 1024));
+#pragma unroll
+      for (int i = 0; i < MTM; ++i)
+#pragma unroll
+        for (int j = 0; j < MTN; ++j) acc[i][j] = mfma_fp8(af[i], bf[j], acc[i][j]);
     } else {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        v8h ah[4], bh[4];
+      for (int h = 0; h < 2; ++h) {  // 16-byte half of each lane's 32 bytes
+        uint4 ar[MTM], br[MTN];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ah[i] = e4m3x8_to_f16(af[i][2 * t], af[i][2 * t + 1]);
-          bh[i] = e4m3x8_to_f16(bf[i][2 * t], bf[i][2 * t + 1]);
+        for (int i = 0; i < MTM; ++i) ar[i] = *reinterpret_cast<const uint4*>(la + i * 2048 + h * 1024);
+#pragma unroll
+        for (int j = 0; j < MTN; ++j) br[j] = *reinterpret_cast<const uint4*>(lb + j * 2048 + h * 1024);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {  // 8-value k-substeps
+          v8h ah[MTM], bh[MTN];
+#pragma unroll
+          for (int i = 0; i < MTM; ++i) ah[i] = t ? e4m3x8_to_f16(ar[i].z, ar[i].w) : e4m3x8_to_f16(ar[i].x, ar[i].y);
+#pragma unroll
+          for (int j = 0; j < MTN; ++j) bh[j] = t ? e4m3x8_to_f16(br[j].z, br[j].w) : e4m3x8_to_f16(br[j].x, br[j].y);
+#pragma unroll
+          for (int i = 0; i < MTM; ++i)
+#pragma unroll
+            for (int j = 0; j < MTN; ++j) acc[i][j] = mfma_f16(ah[i], bh[j], acc[i][j]);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f16(ah[i], bh[j], acc[i][j]);
       }
     }
-    if (more) stage_store(st, lds[cur ^ 1][0], lds[cur ^ 1][1]);
+    if (more) stage_store<BM, BN, NT>(st, lds[cur ^ 1], lds[cur ^ 1] + A_BYTES);
     __syncthreads();
     cur ^= 1;
   }
 
   const int q = lane >> 4, col = lane & 15;
+  const int gw = g0 + wn * MTN;  // first packed group of this wave
   if (!DOWN) {
-    // packed groups of this wave: g0 + wn*4 + j; pairs for the gated form
     uint8_t* hq = reinterpret_cast<uint8_t*>(out);
     const int I = GATED ? Npk / 2 : Npk;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MTM; ++i) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = m0 + (wm * 4 + i) * 16 + 4 * q + r;
+        const int m = m0 + (wm * MTM + i) * 16 + 4 * q + r;
         if (m >= M) continue;
         if (GATED) {
 #pragma unroll
-          for (int jp = 0; jp < 2; ++jp) {
-            const int pair = (g0 + wn * 4) / 2 + jp;
-            const float h = gated_h<MODE>(acc[i][2 * jp][r] * alpha_a, acc[i][2 * jp + 1][r] * alpha_b);
+          for (int jp = 0; jp < MTN / 2; ++jp) {
+            const int pair = gw / 2 + jp;
+            const float h = gated_h<EPI>(acc[i][2 * jp][r] * alpha_a, acc[i][2 * jp + 1][r] * alpha_b);
             hq[(size_t)m * I + pair * 16 + col] = (uint8_t)e4m3x1(h * inv_out);
           }
         } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int grp = g0 + wn * 4 + j;
-            const float h = gated_h<MODE>(0.0f, acc[i][j][r] * alpha_b);
-            hq[(size_t)m * I + grp * 16 + col] = (uint8_t)e4m3x1(h * inv_out);
+          for (int j = 0; j < MTN; ++j) {
+            const float h = gated_h<EPI>(0.0f, acc[i][j][r] * alpha_b);
+            hq[(size_t)m * I + (gw + j) * 16 + col] = (uint8_t)e4m3x1(h * inv_out);
           }
         }
       }
     }
     return;
   }
-
-  // down: optional split-K reduction, then bf16 output
-  uint16_t* y = reinterpret_cast<uint16_t*>(out);
+  // down: one split writes bf16 Y; several write fp32 partials for the consumer
   const int N = Npk;
-  if (S > 1) {
-    float* ps = part + (size_t)s * M * N;
+  uint16_t* y = reinterpret_cast<uint16_t*>(out);
+  float* ps = part + (size_t)s * M * N;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + (wm * 4 + i) * 16 + 4 * q + r;
-        if (m >= M) continue;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ps[(size_t)m * N + (g0 + wn * 4 + j) * 16 + col] = acc[i][j][r];
-      }
-    __threadfence();
-    __syncthreads();
-    const int tile = tm * gridDim.x + tn;
-    if (threadIdx.x == 0) *s_last = atomicAdd(&cnt[tile], 1u) == (unsigned)(S - 1);
-    __syncthreads();
-    if (!*s_last) return;
-    __threadfence();
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0, 0, 0, 0};
-    for (int t = 0; t < S; ++t) {
-      const float* pt = part + (size_t)t * M * N;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = m0 + (wm * 4 + i) * 16 + 4 * q + r;
-          if (m >= M) continue;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j][r] += pt[(size_t)m * N + (g0 + wn * 4 + j) * 16 + col];
-        }
-    }
-    if (threadIdx.x == 0) cnt[tile] = 0u;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MTM; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int m = m0 + (wm * 4 + i) * 16 + 4 * q + r;
+      const int m = m0 + (wm * MTM + i) * 16 + 4 * q + r;
       if (m >= M) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        y[(size_t)m * N + (g0 + wn * 4 + j) * 16 + col] = (uint16_t)f32_to_bf16(acc[i][j][r] * alpha_a);
+      for (int j = 0; j < MTN; ++j) {
+        const size_t o = (size_t)m * N + (gw + j) * 16 + col;
+        if (S == 1)
+          y[o] = (uint16_t)f32_to_bf16(acc[i][j][r] * alpha_a);
+        else
+          ps[o] = acc[i][j][r];
+      }
     }
 }
+
+// Workgroup tile configurations (index): {BM, BN, WGM, WGN}
+//   0: 128 x 128, 2 x 2 waves     1: 128 x 256, 2 x 2     2: 256 x 128, 2 x 2
+//   3: 128 x 256, 2 x 4           4: 128 x 256, 1 x 4     5:  64 x 256, 1 x 4
+//   6: 256 x 256, 2 x 2 (FP8 only: the f16 form runs out of registers)
+constexpr int kGemmConfigs = 7;
+__host__ __device__ constexpr int cfg_bm(int c) { return c == 2 || c == 6 ? 256 : (c == 5 ? 64 : 128); }
+__host__ __device__ constexpr int cfg_bn(int c) { return c == 0 || c == 2 ? 128 : 256; }
+__host__ __device__ constexpr int cfg_wgm(int c) { return c == 4 || c == 5 ? 1 : 2; }
+__host__ __device__ constexpr int cfg_wgn(int c) { return c >= 3 && c <= 5 ? 4 : 2; }
 
 // ---------------------------------------------------------------------------
 // host-side launchers
@@ -459,54 +678,171 @@ hipError_t launch_gemv_gateup(int act, const uint8_t* xq, const uint8_t* w, uint
   return hipGetLastError();
 }
 
-template <bool FP8>
+// Column groups per workgroup of the fused kernel: FRT_GEMV_FUSED_GROUPS
+// (1, 2 or 4; default 2).
+static int fused_groups() {
+  const char* e = getenv("FRT_GEMV_FUSED_GROUPS");
+  int g = (e && *e) ? atoi(e) : 2;
+  return (g == 1 || g == 2 || g == 4) ? g : 2;
+}
+
+template <int ACT, int W, int NCH>
+static hipError_t gateup_fused_nch(const uint16_t* r_prev, const uint16_t* y_prev, const uint16_t* w_norm,
+                                   uint16_t* r_out, uint8_t* xq_out, const uint8_t* w, uint8_t* hq,
+                                   int M, int K, int I, float eps, float inv_x, float a_g, float a_u,
+                                   float inv_h, hipStream_t s) {
+  const int G = fused_groups();
+  const int P = I / 16;
+  dim3 grid((P + G - 1) / G), block(W * 64);
+  if (G == 1)
+    hipLaunchKernelGGL((k_gemv_gateup_fused<ACT, W, NCH, 1>), grid, block, 0, s, r_prev, y_prev, w_norm,
+                       r_out, xq_out, w, hq, M, K, I, eps, inv_x, a_g, a_u, inv_h);
+  else if (G == 2)
+    hipLaunchKernelGGL((k_gemv_gateup_fused<ACT, W, NCH, 2>), grid, block, 0, s, r_prev, y_prev, w_norm,
+                       r_out, xq_out, w, hq, M, K, I, eps, inv_x, a_g, a_u, inv_h);
+  else
+    hipLaunchKernelGGL((k_gemv_gateup_fused<ACT, W, NCH, 4>), grid, block, 0, s, r_prev, y_prev, w_norm,
+                       r_out, xq_out, w, hq, M, K, I, eps, inv_x, a_g, a_u, inv_h);
+  return hipGetLastError();
+}
+
+template <int ACT, int W>
+static hipError_t gateup_fused_w(const uint16_t* r_prev, const uint16_t* y_prev, const uint16_t* w_norm,
+                                 uint16_t* r_out, uint8_t* xq_out, const uint8_t* w, uint8_t* hq,
+                                 int M, int K, int I, float eps, float inv_x, float a_g, float a_u,
+                                 float inv_h, hipStream_t s) {
+  const int nchunk = K / 8;
+  const int gt = (M == 1) ? W * 64 : 64;
+  const int nch = (nchunk + gt - 1) / gt;
+  if (nch <= 1)
+    return gateup_fused_nch<ACT, W, 1>(r_prev, y_prev, w_norm, r_out, xq_out, w, hq, M, K, I, eps, inv_x, a_g, a_u, inv_h, s);
+  if (nch <= 2)
+    return gateup_fused_nch<ACT, W, 2>(r_prev, y_prev, w_norm, r_out, xq_out, w, hq, M, K, I, eps, inv_x, a_g, a_u, inv_h, s);
+  if (nch <= 4)
+    return gateup_fused_nch<ACT, W, 4>(r_prev, y_prev, w_norm, r_out, xq_out, w, hq, M, K, I, eps, inv_x, a_g, a_u, inv_h, s);
+  if (nch <= 8)
+    return gateup_fused_nch<ACT, W, 8>(r_prev, y_prev, w_norm, r_out, xq_out, w, hq, M, K, I, eps, inv_x, a_g, a_u, inv_h, s);
+  return hipErrorInvalidValue;
+}
+
+template <int ACT>
+static hipError_t gateup_fused_act(int W, const uint16_t* r_prev, const uint16_t* y_prev,
+                                   const uint16_t* w_norm, uint16_t* r_out, uint8_t* xq_out,
+                                   const uint8_t* w, uint8_t* hq, int M, int K, int I, float eps,
+                                   float inv_x, float a_g, float a_u, float inv_h, hipStream_t s) {
+  switch (W) {
+    case 2: return gateup_fused_w<ACT, 2>(r_prev, y_prev, w_norm, r_out, xq_out, w, hq, M, K, I, eps, inv_x, a_g, a_u, inv_h, s);
+    case 4: return gateup_fused_w<ACT, 4>(r_prev, y_prev, w_norm, r_out, xq_out, w, hq, M, K, I, eps, inv_x, a_g, a_u, inv_h, s);
+    case 8: return gateup_fused_w<ACT, 8>(r_prev, y_prev, w_norm, r_out, xq_out, w, hq, M, K, I, eps, inv_x, a_g, a_u, inv_h, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Whether the fused decode kernel can take this shape (LDS for the rows,
+// register chunks of the prologue, at least two waves to share a row).
+bool gemv_fused_supported(int M, int K, int W) {
+  if (M < 1 || M > 16 || W < 2 || W > 8 || (long)M * K > kFusedXqBytes) return false;
+  const int gt = (M == 1) ? W * 64 : 64;
+  return (K / 8 + gt - 1) / gt <= 8;
+}
+
+hipError_t launch_gemv_gateup_fused(int act, const uint16_t* r_prev, const uint16_t* y_prev,
+                                    const uint16_t* w_norm, uint16_t* r_out, uint8_t* xq_out,
+                                    const uint8_t* w, uint8_t* hq, int M, int K, int I, int W,
+                                    float eps, float inv_x, float a_g, float a_u, float inv_h,
+                                    hipStream_t s) {
+  if (act == GU_GEGLU)
+    return gateup_fused_act<GU_GEGLU>(W, r_prev, y_prev, w_norm, r_out, xq_out, w, hq, M, K, I, eps, inv_x, a_g, a_u, inv_h, s);
+  if (act == GU_SWIGLU)
+    return gateup_fused_act<GU_SWIGLU>(W, r_prev, y_prev, w_norm, r_out, xq_out, w, hq, M, K, I, eps, inv_x, a_g, a_u, inv_h, s);
+  return gateup_fused_act<GU_GELU>(W, r_prev, y_prev, w_norm, r_out, xq_out, w, hq, M, K, I, eps, inv_x, a_g, a_u, inv_h, s);
+}
+
+template <bool FP8, int COLS>
 static hipError_t gemv_down_t(const uint8_t* hq, const uint8_t* w, uint16_t* y, int M, int K,
                               int N, int W, float alpha_d, hipStream_t s) {
-  dim3 grid(N / 16), block(W * 64);
+  dim3 grid((N / 16) * (16 / COLS)), block(W * 64);
   switch (W) {
-    case 1: hipLaunchKernelGGL((k_gemv_down<1, FP8>), grid, block, 0, s, hq, w, y, M, K, N, alpha_d); break;
-    case 2: hipLaunchKernelGGL((k_gemv_down<2, FP8>), grid, block, 0, s, hq, w, y, M, K, N, alpha_d); break;
-    case 4: hipLaunchKernelGGL((k_gemv_down<4, FP8>), grid, block, 0, s, hq, w, y, M, K, N, alpha_d); break;
-    case 8: hipLaunchKernelGGL((k_gemv_down<8, FP8>), grid, block, 0, s, hq, w, y, M, K, N, alpha_d); break;
-    case 16: hipLaunchKernelGGL((k_gemv_down<16, FP8>), grid, block, 0, s, hq, w, y, M, K, N, alpha_d); break;
+    case 1: hipLaunchKernelGGL((k_gemv_down<1, FP8, COLS>), grid, block, 0, s, hq, w, y, M, K, N, alpha_d); break;
+    case 2: hipLaunchKernelGGL((k_gemv_down<2, FP8, COLS>), grid, block, 0, s, hq, w, y, M, K, N, alpha_d); break;
+    case 4: hipLaunchKernelGGL((k_gemv_down<4, FP8, COLS>), grid, block, 0, s, hq, w, y, M, K, N, alpha_d); break;
+    case 8: hipLaunchKernelGGL((k_gemv_down<8, FP8, COLS>), grid, block, 0, s, hq, w, y, M, K, N, alpha_d); break;
+    case 16: hipLaunchKernelGGL((k_gemv_down<16, FP8, COLS>), grid, block, 0, s, hq, w, y, M, K, N, alpha_d); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+// Columns per down-GEMV workgroup (FRT_GEMV_DOWN_COLS = 8 or 16).
+static int down_cols(int N) {
+  (void)N;
+  const char* e = getenv("FRT_GEMV_DOWN_COLS");
+  if (e && *e) return atoi(e) == 8 ? 8 : 16;
+  return 16;  // measured: half-group workgroups stream slower at H = 5120
+}
+
 hipError_t launch_gemv_down(const uint8_t* hq, const uint8_t* w, uint16_t* y, int M, int K, int N,
                             int W, bool fp8, float alpha_d, hipStream_t s) {
-  return fp8 ? gemv_down_t<true>(hq, w, y, M, K, N, W, alpha_d, s)
-             : gemv_down_t<false>(hq, w, y, M, K, N, W, alpha_d, s);
-}
-
-hipError_t launch_gemm_gateup(int act, const uint8_t* xq, const uint8_t* w, uint8_t* hq, int M,
-                              int K, int Npk, float alpha_g, float alpha_u, float inv_h,
-                              hipStream_t s) {
-  dim3 grid(Npk / BN, (M + BM - 1) / BM, 1);
-  if (act == GU_GEGLU)
-    hipLaunchKernelGGL(k_gemm<GU_GEGLU>, grid, dim3(256), 0, s, xq, w, hq, nullptr, nullptr, M, K,
-                       Npk, 1, alpha_g, alpha_u, inv_h);
-  else if (act == GU_SWIGLU)
-    hipLaunchKernelGGL(k_gemm<GU_SWIGLU>, grid, dim3(256), 0, s, xq, w, hq, nullptr, nullptr, M,
-                       K, Npk, 1, alpha_g, alpha_u, inv_h);
-  else
-    hipLaunchKernelGGL(k_gemm<GU_GELU>, grid, dim3(256), 0, s, xq, w, hq, nullptr, nullptr, M, K,
-                       Npk, 1, alpha_g, alpha_u, inv_h);
-  return hipGetLastError();
-}
-
-hipError_t launch_gemm_down(const uint8_t* hq, const uint8_t* w, uint16_t* y, float* part,
-                            uint32_t* cnt, int M, int K, int N, int S, bool fp8, float alpha_d,
-                            hipStream_t s) {
-  dim3 grid(N / BN, (M + BM - 1) / BM, S);
+  const int cols = down_cols(N);
   if (fp8)
-    hipLaunchKernelGGL(k_gemm<4>, grid, dim3(256), 0, s, hq, w, y, part, cnt, M, K, N, S, alpha_d,
-                       0.0f, 0.0f);
-  else
-    hipLaunchKernelGGL(k_gemm<3>, grid, dim3(256), 0, s, hq, w, y, part, cnt, M, K, N, S, alpha_d,
-                       0.0f, 0.0f);
+    return cols == 8 ? gemv_down_t<true, 8>(hq, w, y, M, K, N, W, alpha_d, s)
+                     : gemv_down_t<true, 16>(hq, w, y, M, K, N, W, alpha_d, s);
+  return cols == 8 ? gemv_down_t<false, 8>(hq, w, y, M, K, N, W, alpha_d, s)
+                   : gemv_down_t<false, 16>(hq, w, y, M, K, N, W, alpha_d, s);
+}
+
+bool gemm_config_ok(int cfg, bool fp8) { return cfg >= 0 && cfg < kGemmConfigs && (fp8 || cfg != 6); }
+
+template <int EPI, bool FP8, int C>
+static void gemm_cfg(dim3 grid, hipStream_t s, const uint8_t* act, const uint8_t* w, void* out, float* part,
+                     int M, int K, int Npk, int S, float a, float b, float inv) {
+  constexpr int WGM = cfg_wgm(C), WGN = cfg_wgn(C);
+  hipLaunchKernelGGL((k_gemm<EPI, FP8, cfg_bm(C), cfg_bn(C), WGM, WGN>), grid, dim3(WGM * WGN * 64), 0, s,
+                     act, w, out, part, M, K, Npk, S, a, b, inv);
+}
+
+template <int EPI, bool FP8>
+static hipError_t gemm_mode(int cfg, const uint8_t* act, const uint8_t* w, void* out, float* part, int M,
+                            int K, int Npk, int S, float a, float b, float inv, hipStream_t s) {
+  if (!gemm_config_ok(cfg, FP8)) return hipErrorInvalidValue;
+  const int BM = cfg_bm(cfg), BN = cfg_bn(cfg);
+  if (Npk % BN) return hipErrorInvalidValue;
+  dim3 grid(Npk / BN, (M + BM - 1) / BM, S);
+  switch (cfg) {
+    case 0: gemm_cfg<EPI, FP8, 0>(grid, s, act, w, out, part, M, K, Npk, S, a, b, inv); break;
+    case 1: gemm_cfg<EPI, FP8, 1>(grid, s, act, w, out, part, M, K, Npk, S, a, b, inv); break;
+    case 2: gemm_cfg<EPI, FP8, 2>(grid, s, act, w, out, part, M, K, Npk, S, a, b, inv); break;
+    case 3: gemm_cfg<EPI, FP8, 3>(grid, s, act, w, out, part, M, K, Npk, S, a, b, inv); break;
+    case 4: gemm_cfg<EPI, FP8, 4>(grid, s, act, w, out, part, M, K, Npk, S, a, b, inv); break;
+    case 5: gemm_cfg<EPI, FP8, 5>(grid, s, act, w, out, part, M, K, Npk, S, a, b, inv); break;
+    default:
+      if constexpr (FP8) gemm_cfg<EPI, FP8, 6>(grid, s, act, w, out, part, M, K, Npk, S, a, b, inv);
+      break;
+  }
   return hipGetLastError();
+}
+
+int gemm_config_bm(int cfg) { return cfg_bm(cfg); }
+int gemm_config_bn(int cfg) { return cfg_bn(cfg); }
+
+hipError_t launch_gemm_gateup(int act, int cfg, bool fp8, const uint8_t* xq, const uint8_t* w, uint8_t* hq,
+                              int M, int K, int Npk, float alpha_g, float alpha_u, float inv_h, hipStream_t s) {
+  const float a = alpha_g, b = alpha_u;
+  if (fp8) {
+    if (act == GU_GEGLU) return gemm_mode<GU_GEGLU, true>(cfg, xq, w, hq, nullptr, M, K, Npk, 1, a, b, inv_h, s);
+    if (act == GU_SWIGLU) return gemm_mode<GU_SWIGLU, true>(cfg, xq, w, hq, nullptr, M, K, Npk, 1, a, b, inv_h, s);
+    return gemm_mode<GU_GELU, true>(cfg, xq, w, hq, nullptr, M, K, Npk, 1, a, b, inv_h, s);
+  }
+  if (act == GU_GEGLU) return gemm_mode<GU_GEGLU, false>(cfg, xq, w, hq, nullptr, M, K, Npk, 1, a, b, inv_h, s);
+  if (act == GU_SWIGLU) return gemm_mode<GU_SWIGLU, false>(cfg, xq, w, hq, nullptr, M, K, Npk, 1, a, b, inv_h, s);
+  return gemm_mode<GU_GELU, false>(cfg, xq, w, hq, nullptr, M, K, Npk, 1, a, b, inv_h, s);
+}
+
+// S > 1: fp32 partials [S][M][N] into part (summed by the consumer), else bf16 Y.
+hipError_t launch_gemm_down(int cfg, const uint8_t* hq, const uint8_t* w, uint16_t* y, float* part, int M,
+                            int K, int N, int S, bool fp8, float alpha_d, hipStream_t s) {
+  if (fp8) return gemm_mode<EPI_DOWN, true>(cfg, hq, w, y, part, M, K, N, S, alpha_d, 0.0f, 0.0f, s);
+  return gemm_mode<EPI_DOWN, false>(cfg, hq, w, y, part, M, K, N, S, alpha_d, 0.0f, 0.0f, s);
 }
 
 }  // namespace frt

@@ -14,7 +14,12 @@
 //   xq  = e4m3(f32(x * inv_x))              (measure mode: store x, amax|x|)
 //
 // Bound: HBM.  Algorithmic bytes per row: 2H (r) + 2H (y) + 2H (r') + H (xq),
-// plus 2H once for w.  Layout: TPR threads own one row; each thread holds
+// plus 2H once for w.
+//
+// When the previous down GEMM split K, its output arrives as S fp32 partial
+// tiles [S][M][H]; the kernel then forms y = bf16(f32(sum_s part[s]) * a_d),
+// adding the splits in split order, stores it to the Y slot and continues
+// with that y.  Layout: TPR threads own one row; each thread holds
 // NC chunks of 8 bf16 (16-byte loads) in registers between the two passes,
 // so r' is read from HBM once.  The fp64 sum of squares is reduced across
 // the wave with shuffles and across the row's waves through LDS.
@@ -22,12 +27,33 @@
 
 namespace frt {
 
+// y of 8 consecutive elements from S fp32 partial tiles (split order)
+__device__ __forceinline__ uint4 y_from_partials(const float* __restrict__ part, size_t split_stride,
+                                                 size_t off, int S, float alpha_d) {
+  float a[8];
+  {
+    const float4 p0 = *reinterpret_cast<const float4*>(part + off);
+    const float4 p1 = *reinterpret_cast<const float4*>(part + off + 4);
+    a[0] = p0.x; a[1] = p0.y; a[2] = p0.z; a[3] = p0.w;
+    a[4] = p1.x; a[5] = p1.y; a[6] = p1.z; a[7] = p1.w;
+  }
+  for (int sp = 1; sp < S; ++sp) {
+    const float4 p0 = *reinterpret_cast<const float4*>(part + sp * split_stride + off);
+    const float4 p1 = *reinterpret_cast<const float4*>(part + sp * split_stride + off + 4);
+    a[0] += p0.x; a[1] += p0.y; a[2] += p0.z; a[3] += p0.w;
+    a[4] += p1.x; a[5] += p1.y; a[6] += p1.z; a[7] += p1.w;
+  }
+  return make_uint4(pack_bf16x2(a[0] * alpha_d, a[1] * alpha_d), pack_bf16x2(a[2] * alpha_d, a[3] * alpha_d),
+                    pack_bf16x2(a[4] * alpha_d, a[5] * alpha_d), pack_bf16x2(a[6] * alpha_d, a[7] * alpha_d));
+}
+
 template <int TPR, int NC, bool MEASURE>
 __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
     const uint16_t* __restrict__ r_prev, const uint16_t* __restrict__ y_prev,
     const uint16_t* __restrict__ w_norm, uint16_t* __restrict__ r_out,
     uint8_t* __restrict__ xq_out, float* __restrict__ x_out, float* __restrict__ amax_out,
-    int M, int H, float eps, float inv_x) {
+    int M, int H, float eps, float inv_x, const float* __restrict__ y_part, int S, float alpha_d,
+    uint16_t* __restrict__ y_store) {
   constexpr int RPW = 256 / TPR;  // rows per workgroup
   constexpr int WPR = TPR / 64;   // waves per row
   __shared__ double red[256 / 64];
@@ -48,7 +74,12 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
     if (active && ch < nchunk) {
       const uint4 rv = *reinterpret_cast<const uint4*>(r_prev + base + (size_t)ch * 8);
       uint4 yv = make_uint4(0, 0, 0, 0);
-      if (y_prev) yv = *reinterpret_cast<const uint4*>(y_prev + base + (size_t)ch * 8);
+      if (y_part) {
+        yv = y_from_partials(y_part, (size_t)M * H, base + (size_t)ch * 8, S, alpha_d);
+        *reinterpret_cast<uint4*>(y_store + base + (size_t)ch * 8) = yv;
+      } else if (y_prev) {
+        yv = *reinterpret_cast<const uint4*>(y_prev + base + (size_t)ch * 8);
+      }
       uint32_t rr[4] = {rv.x, rv.y, rv.z, rv.w};
       uint32_t yy[4] = {yv.x, yv.y, yv.z, yv.w};
       uint32_t o[4];
@@ -110,14 +141,26 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
   }
 }
 
-// Z = bf16(R + Y), the residual add after the last block.
+// Z = bf16(R + Y), the residual add after the last block.  With partials
+// (S > 1 splits of the last down GEMM) Y is formed first and stored to its
+// slot; with z == nullptr only that Y is written (a forward range that ends
+// before the last layer).
 __global__ __launch_bounds__(256) void k_residual_add(const uint16_t* __restrict__ r,
-                                                      const uint16_t* __restrict__ y,
-                                                      uint16_t* __restrict__ z, size_t n8) {
+                                                      uint16_t* __restrict__ y,
+                                                      uint16_t* __restrict__ z, size_t n8,
+                                                      const float* __restrict__ y_part, int S,
+                                                      float alpha_d) {
   size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n8) return;
+  uint4 b;
+  if (y_part) {
+    b = y_from_partials(y_part, n8 * 8, i * 8, S, alpha_d);
+    reinterpret_cast<uint4*>(y)[i] = b;
+  } else {
+    b = reinterpret_cast<const uint4*>(y)[i];
+  }
+  if (!z) return;
   uint4 a = reinterpret_cast<const uint4*>(r)[i];
-  uint4 b = reinterpret_cast<const uint4*>(y)[i];
   uint32_t aa[4] = {a.x, a.y, a.z, a.w}, bb[4] = {b.x, b.y, b.z, b.w}, o[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -140,7 +183,8 @@ template <bool MEASURE>
 static hipError_t launch_norm_t(const uint16_t* r_prev, const uint16_t* y_prev,
                                 const uint16_t* w, uint16_t* r_out, uint8_t* xq, float* x_out,
                                 float* amax, int M, int H, float eps, float inv_x,
-                                hipStream_t s) {
+                                hipStream_t s, const float* y_part = nullptr, int S = 1,
+                                float alpha_d = 0.0f, uint16_t* y_store = nullptr) {
   const int nchunk = H / 8;
   // one wave per row when the row fits 8 chunks per lane, else a whole
   // workgroup per row
@@ -149,22 +193,27 @@ static hipError_t launch_norm_t(const uint16_t* r_prev, const uint16_t* y_prev,
     dim3 grid((M + 3) / 4);
     if (nc <= 2)
       hipLaunchKernelGGL((k_add_rmsnorm_quant<64, 2, MEASURE>), grid, dim3(256), 0, s, r_prev,
-                         y_prev, w, r_out, xq, x_out, amax, M, H, eps, inv_x);
+                         y_prev, w, r_out, xq, x_out, amax, M, H, eps, inv_x, y_part, S, alpha_d,
+                         y_store);
     else if (nc <= 4)
       hipLaunchKernelGGL((k_add_rmsnorm_quant<64, 4, MEASURE>), grid, dim3(256), 0, s, r_prev,
-                         y_prev, w, r_out, xq, x_out, amax, M, H, eps, inv_x);
+                         y_prev, w, r_out, xq, x_out, amax, M, H, eps, inv_x, y_part, S, alpha_d,
+                         y_store);
     else
       hipLaunchKernelGGL((k_add_rmsnorm_quant<64, 8, MEASURE>), grid, dim3(256), 0, s, r_prev,
-                         y_prev, w, r_out, xq, x_out, amax, M, H, eps, inv_x);
+                         y_prev, w, r_out, xq, x_out, amax, M, H, eps, inv_x, y_part, S, alpha_d,
+                         y_store);
   } else {
     const int nc = (nchunk + 255) / 256;
     dim3 grid(M);
     if (nc <= 4)
       hipLaunchKernelGGL((k_add_rmsnorm_quant<256, 4, MEASURE>), grid, dim3(256), 0, s, r_prev,
-                         y_prev, w, r_out, xq, x_out, amax, M, H, eps, inv_x);
+                         y_prev, w, r_out, xq, x_out, amax, M, H, eps, inv_x, y_part, S, alpha_d,
+                         y_store);
     else
       hipLaunchKernelGGL((k_add_rmsnorm_quant<256, 8, MEASURE>), grid, dim3(256), 0, s, r_prev,
-                         y_prev, w, r_out, xq, x_out, amax, M, H, eps, inv_x);
+                         y_prev, w, r_out, xq, x_out, amax, M, H, eps, inv_x, y_part, S, alpha_d,
+                         y_store);
   }
   return hipGetLastError();
 }
@@ -173,27 +222,28 @@ static hipError_t launch_norm_t(const uint16_t* r_prev, const uint16_t* y_prev,
 // issued by many waves at once (latency, not bandwidth, bounds M <= 64).
 hipError_t launch_add_rmsnorm_quant(const uint16_t* r_prev, const uint16_t* y_prev,
                                     const uint16_t* w, uint16_t* r_out, uint8_t* xq, int M,
-                                    int H, float eps, float inv_x, hipStream_t s) {
+                                    int H, float eps, float inv_x, hipStream_t s,
+                                    const float* y_part, int S, float alpha_d, uint16_t* y_store) {
   const int nchunk = H / 8;
   if (M <= 64 && nchunk > 64 && nchunk <= 256 * 8) {
     const int nc = (nchunk + 255) / 256;
     dim3 grid(M);
     if (nc <= 1)
       hipLaunchKernelGGL((k_add_rmsnorm_quant<256, 1, false>), grid, dim3(256), 0, s, r_prev,
-                         y_prev, w, r_out, xq, nullptr, nullptr, M, H, eps, inv_x);
+                         y_prev, w, r_out, xq, nullptr, nullptr, M, H, eps, inv_x, y_part, S, alpha_d, y_store);
     else if (nc <= 2)
       hipLaunchKernelGGL((k_add_rmsnorm_quant<256, 2, false>), grid, dim3(256), 0, s, r_prev,
-                         y_prev, w, r_out, xq, nullptr, nullptr, M, H, eps, inv_x);
+                         y_prev, w, r_out, xq, nullptr, nullptr, M, H, eps, inv_x, y_part, S, alpha_d, y_store);
     else if (nc <= 4)
       hipLaunchKernelGGL((k_add_rmsnorm_quant<256, 4, false>), grid, dim3(256), 0, s, r_prev,
-                         y_prev, w, r_out, xq, nullptr, nullptr, M, H, eps, inv_x);
+                         y_prev, w, r_out, xq, nullptr, nullptr, M, H, eps, inv_x, y_part, S, alpha_d, y_store);
     else
       hipLaunchKernelGGL((k_add_rmsnorm_quant<256, 8, false>), grid, dim3(256), 0, s, r_prev,
-                         y_prev, w, r_out, xq, nullptr, nullptr, M, H, eps, inv_x);
+                         y_prev, w, r_out, xq, nullptr, nullptr, M, H, eps, inv_x, y_part, S, alpha_d, y_store);
     return hipGetLastError();
   }
   return launch_norm_t<false>(r_prev, y_prev, w, r_out, xq, nullptr, nullptr, M, H, eps, inv_x,
-                              s);
+                              s, y_part, S, alpha_d, y_store);
 }
 
 hipError_t launch_add_rmsnorm_measure(const uint16_t* r_prev, const uint16_t* y_prev,
@@ -202,11 +252,11 @@ hipError_t launch_add_rmsnorm_measure(const uint16_t* r_prev, const uint16_t* y_
   return launch_norm_t<true>(r_prev, y_prev, w, r_out, nullptr, x_out, amax, M, H, eps, 1.0f, s);
 }
 
-hipError_t launch_residual_add(const uint16_t* r, const uint16_t* y, uint16_t* z, size_t n,
-                               hipStream_t s) {
+hipError_t launch_residual_add(const uint16_t* r, uint16_t* y, uint16_t* z, size_t n, hipStream_t s,
+                               const float* y_part, int S, float alpha_d) {
   size_t n8 = n / 8;
   hipLaunchKernelGGL(k_residual_add, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, r, y, z,
-                     n8);
+                     n8, y_part, S, alpha_d);
   return hipGetLastError();
 }
 
