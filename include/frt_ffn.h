@@ -79,7 +79,9 @@ typedef enum {
  *   RMSNorm + quantise step inside the gate/up GEMV kernel (two kernels per
  *   layer); every workgroup recomputes the rows' norm from the L2-resident
  *   inputs.  Results are identical to the separate kernel, which is the
- *   default because it measures faster.  Ignored for other shapes. */
+ *   default because it measures no slower.  Ignored for other shapes and
+ *   when the down GEMV splits K (its output then arrives as partial sums
+ *   that the separate norm kernel adds). */
 #define FRT_FLAG_FUSED_NORM 2u
 /* FRT_FLAG_FP8_MFMA_GATEUP: the gate/up GEMM for M > 16 runs on the FP8
  *   matrix cores (same accumulation behaviour as FRT_FLAG_FP8_MFMA_DOWN). */

@@ -39,8 +39,8 @@ hipError_t launch_amax_bf16(const uint16_t*, size_t, float*, hipStream_t);
 hipError_t launch_quant_pack(const uint16_t*, uint8_t*, int, int, float, int, hipStream_t);
 hipError_t launch_gemv_gateup(int, const uint8_t*, const uint8_t*, uint8_t*, int, int, int, int,
                               float, float, float, hipStream_t);
-hipError_t launch_gemv_down(const uint8_t*, const uint8_t*, uint16_t*, int, int, int, int, bool,
-                            float, hipStream_t);
+hipError_t launch_gemv_down(const uint8_t*, const uint8_t*, uint16_t*, float*, int, int, int, int, int,
+                            bool, float, hipStream_t);
 bool gemv_fused_supported(int, int, int);
 hipError_t launch_gemv_gateup_fused(int, const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*,
                                     uint8_t*, const uint8_t*, uint8_t*, int, int, int, int, float,
@@ -109,22 +109,41 @@ struct DeviceGuard {
 namespace {
 
 constexpr int kGemvMaxM = 16;
-constexpr int kTargetWaves = 6144;  // GEMV: ~6 waves per SIMD across the chip
+constexpr int kCUs = 256;  // MI355X compute units (workgroup rounds are counted against them)
+
+int env_int(const char* name, int dflt) {
+  const char* e = getenv(name);
+  return (e && *e) ? atoi(e) : dflt;
+}
 
 // Waves per GEMV workgroup: the smallest power of two (<= 16, <= K blocks)
-// that brings groups * W to kTargetWaves.  FRT_GEMV_WAVES_GATEUP /
-// FRT_GEMV_WAVES_DOWN override it (tuning sweeps).
-int gemv_waves(int groups, int kblocks, const char* env) {
+// that brings workgroups * W to `target` waves across the chip (measured best:
+// ~6 per SIMD for gate/up, ~4 for the K-split down GEMV).
+// FRT_GEMV_WAVES_GATEUP / FRT_GEMV_WAVES_DOWN override it (tuning sweeps).
+int gemv_waves(int groups, int kblocks, const char* env, int target) {
   const char* e = getenv(env);
   int w = 1;
   if (e && *e) {
     w = atoi(e);
   } else {
-    while (w < 16 && groups * w < kTargetWaves) w *= 2;
+    while (w < 16 && groups * w < target) w *= 2;
   }
   if (w != 1 && w != 2 && w != 4 && w != 8 && w != 16) w = 4;
   while (w > 1 && w > kblocks) w /= 2;
   return w;
+}
+
+// K splits of the decode down GEMV: at least two workgroups per CU (a grid of
+// a few hundred workgroups leaves CUs with one and others with two, and the
+// per-CU load rate then sets the time), each split at least 8 K blocks.
+// Measured at H = 5120, I = 17408: 2 splits x 8 waves stream 5.1 TB/s
+// against 3.9 TB/s unsplit; more splits cost more in the consumer than they
+// gain.  FRT_GEMV_DOWN_SPLIT overrides.
+int gemv_down_splits(int groups, int kblocks) {
+  int s = 1;
+  while (groups * s < 2 * kCUs && kblocks / (2 * s) >= 8) s *= 2;
+  s = env_int("FRT_GEMV_DOWN_SPLIT", s);
+  return std::max(1, std::min(s, kblocks));
 }
 
 struct Layout {
@@ -138,6 +157,8 @@ struct Layout {
   size_t cal_x, cal_h, cal_r, cal_y;
   size_t total;
   int s_gu, s_dn;  // GEMV: waves per workgroup; GEMM: K splits of the down GEMM
+  int k_dn;        // GEMV: K splits of the down GEMV (workgroups per 16 output columns)
+  int split_dn;    // K splits of the down projection, either path (> 1: fp32 partials)
   int cfg_gu, cfg_dn;  // GEMM tile configurations
 };
 
@@ -158,12 +179,7 @@ bool desc_ok(const frt_ffn_desc* d) {
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-int env_int(const char* name, int dflt) {
-  const char* e = getenv(name);
-  return (e && *e) ? atoi(e) : dflt;
-}
 
-constexpr int kCUs = 256;  // MI355X compute units (workgroup rounds are counted against them)
 
 // GEMM tile configurations for M > 16 (see k_gemm.hip): the gate/up GEMM
 // takes the largest tile whose workgroups fill the chip; the down GEMM (few
@@ -214,12 +230,16 @@ Layout make_layout(const frt_ffn_desc& d) {
 
   size_t part = 0, words = 1;
   if (d.M <= kGemvMaxM) {
-    lo.s_gu = gemv_waves((int)(I / 16), (int)(H / 128), "FRT_GEMV_WAVES_GATEUP");
-    lo.s_dn = gemv_waves((int)(H / 16), (int)(I / 128), "FRT_GEMV_WAVES_DOWN");
-    part = 4;
+    lo.s_gu = gemv_waves((int)(I / 16), (int)(H / 128), "FRT_GEMV_WAVES_GATEUP", 6144);
+    lo.k_dn = gemv_down_splits((int)(H / 16), (int)(I / 128));
+    lo.s_dn = gemv_waves((int)(H / 16) * lo.k_dn, (int)(I / 128) / lo.k_dn, "FRT_GEMV_WAVES_DOWN", 4096);
+    lo.split_dn = lo.k_dn;
+    part = lo.k_dn > 1 ? (size_t)lo.k_dn * M * H * 4 : 4;
     words = 1;
   } else {
     choose_gemm(d, lo);
+    lo.k_dn = 1;
+    lo.split_dn = lo.s_dn;
     part = lo.s_dn > 1 ? (size_t)lo.s_dn * M * H * 4 : 4;
     words = 1;
   }
@@ -268,7 +288,7 @@ struct frt_plan {
   bool fp8_gateup() const { return (d.flags & FRT_FLAG_FP8_MFMA_GATEUP) != 0u; }
   // optionally, decode shapes run the norm inside the gate/up GEMV
   bool fused_norm() const {
-    return d.M <= kGemvMaxM && (d.flags & FRT_FLAG_FUSED_NORM) != 0u &&
+    return d.M <= kGemvMaxM && (d.flags & FRT_FLAG_FUSED_NORM) != 0u && lo.split_dn == 1 &&
            gemv_fused_supported(d.M, d.H, lo.s_gu);
   }
   bool act_scales_set() const {
@@ -551,7 +571,7 @@ frt_status frt_ffn_io_get(const frt_plan* p, frt_ffn_io* out) {
 // GEMM) of layer l on stream s.  When the norm is fused into the gate/up
 // kernel, `which` 0 launches nothing and 1 runs both steps.
 // Down output of layer l-1 still in split-K partials (GEMM path, split > 1)?
-static bool down_split(const frt_plan* p) { return p->d.M > kGemvMaxM && p->lo.s_dn > 1; }
+static bool down_split(const frt_plan* p) { return p->lo.split_dn > 1; }
 
 static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t s,
                                       bool y_from_partials = false) {
@@ -570,7 +590,7 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
         a_prev = p->s_h[l - 1] * p->s_d[l - 1];
       }
       KERNEL_CHECK(launch_add_rmsnorm_quant(p->r(l), p->y(l), p->wn(l), p->r(l + 1), p->xq(l), M, H,
-                                            p->d.eps, inv_x, s, yp, p->lo.s_dn, a_prev, p->y(l)),
+                                            p->d.eps, inv_x, s, yp, p->lo.split_dn, a_prev, p->y(l)),
                    "add_rmsnorm_quant");
     }
   } else if (which == 1) {
@@ -586,7 +606,8 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
                                       p->hq(l), M, H, npk, a_g, a_u, inv_h, s), "gemm_gateup");
   } else {
     if (M <= kGemvMaxM)
-      KERNEL_CHECK(launch_gemv_down(p->hq(l), p->wd(l), p->y(l + 1), M, I, H, p->lo.s_dn, p->fp8_down(),
+      KERNEL_CHECK(launch_gemv_down(p->hq(l), p->wd(l), p->y(l + 1), p->part(), M, I, H, p->lo.s_dn,
+                                    p->lo.k_dn, p->fp8_down(),
                                     a_d, s), "gemv_down");
     else
       KERNEL_CHECK(launch_gemm_down(p->lo.cfg_dn, p->hq(l), p->wd(l), p->y(l + 1), p->part(), M, I, H,
@@ -614,9 +635,9 @@ static frt_status forward_range(frt_plan* p, int lb, int le, hipStream_t s,
   const float a_last = p->s_h[le - 1] * p->s_d[le - 1];
   if (le == L)
     KERNEL_CHECK(launch_residual_add(p->r(L), p->y(L), p->z(), p->mh(), s, split ? p->part() : nullptr,
-                                     p->lo.s_dn, a_last), "residual_add");
+                                     p->lo.split_dn, a_last), "residual_add");
   else if (split)
-    KERNEL_CHECK(launch_residual_add(p->r(le), p->y(le), nullptr, p->mh(), s, p->part(), p->lo.s_dn, a_last),
+    KERNEL_CHECK(launch_residual_add(p->r(le), p->y(le), nullptr, p->mh(), s, p->part(), p->lo.split_dn, a_last),
                  "finalize_y");
   return FRT_OK;
 }

@@ -380,14 +380,17 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup_fused(
 template <int W, bool FP8, int COLS>
 __global__ __launch_bounds__(W * 64) void k_gemv_down(const uint8_t* __restrict__ hq,
                                                       const uint8_t* __restrict__ w,
-                                                      uint16_t* __restrict__ y, int M, int K, int N,
-                                                      float alpha_d) {
+                                                      uint16_t* __restrict__ y, float* __restrict__ part,
+                                                      int M, int K, int N, float alpha_d) {
   __shared__ v4f red[W][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int p = (COLS == 16) ? blockIdx.x : (blockIdx.x >> 1);
   const int half = (COLS == 16) ? 0 : (blockIdx.x & 1);
   const int KB = K >> 7;
-  const int kb0 = wave * KB / W, kb1 = (wave + 1) * KB / W;
+  // K split blockIdx.y of gridDim.y, then this wave's share of it
+  const int S = gridDim.y, sp = blockIdx.y;
+  const int ks0 = sp * KB / S, ks1 = (sp + 1) * KB / S;
+  const int kb0 = ks0 + wave * (ks1 - ks0) / W, kb1 = ks0 + (wave + 1) * (ks1 - ks0) / W;
   const int row = lane & 15, q = lane >> 4;
   const bool has_row = row < M;
   const bool my_col = (COLS == 16) || ((row >> 3) == half);
@@ -437,10 +440,18 @@ __global__ __launch_bounds__(W * 64) void k_gemv_down(const uint8_t* __restrict_
     for (int v = 1; v < W; ++v) acc += red[v][lane];
   }
   if (!my_col) return;
+  // one split: bf16 Y; several: fp32 partial [split][M][N] (the consumer adds
+  // the splits in split order and dequantises)
+  float* ps = part + (size_t)sp * M * N;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = 4 * q + r;
-    if (m < M) y[(size_t)m * N + p * 16 + row] = (uint16_t)f32_to_bf16(acc[r] * alpha_d);
+    if (m < M) {
+      if (S == 1)
+        y[(size_t)m * N + p * 16 + row] = (uint16_t)f32_to_bf16(acc[r] * alpha_d);
+      else
+        ps[(size_t)m * N + p * 16 + row] = acc[r];
+    }
   }
 }
 
@@ -759,15 +770,15 @@ hipError_t launch_gemv_gateup_fused(int act, const uint16_t* r_prev, const uint1
 }
 
 template <bool FP8, int COLS>
-static hipError_t gemv_down_t(const uint8_t* hq, const uint8_t* w, uint16_t* y, int M, int K,
-                              int N, int W, float alpha_d, hipStream_t s) {
-  dim3 grid((N / 16) * (16 / COLS)), block(W * 64);
+static hipError_t gemv_down_t(const uint8_t* hq, const uint8_t* w, uint16_t* y, float* part, int M, int K,
+                              int N, int W, int S, float alpha_d, hipStream_t s) {
+  dim3 grid((N / 16) * (16 / COLS), S), block(W * 64);
   switch (W) {
-    case 1: hipLaunchKernelGGL((k_gemv_down<1, FP8, COLS>), grid, block, 0, s, hq, w, y, M, K, N, alpha_d); break;
-    case 2: hipLaunchKernelGGL((k_gemv_down<2, FP8, COLS>), grid, block, 0, s, hq, w, y, M, K, N, alpha_d); break;
-    case 4: hipLaunchKernelGGL((k_gemv_down<4, FP8, COLS>), grid, block, 0, s, hq, w, y, M, K, N, alpha_d); break;
-    case 8: hipLaunchKernelGGL((k_gemv_down<8, FP8, COLS>), grid, block, 0, s, hq, w, y, M, K, N, alpha_d); break;
-    case 16: hipLaunchKernelGGL((k_gemv_down<16, FP8, COLS>), grid, block, 0, s, hq, w, y, M, K, N, alpha_d); break;
+    case 1: hipLaunchKernelGGL((k_gemv_down<1, FP8, COLS>), grid, block, 0, s, hq, w, y, part, M, K, N, alpha_d); break;
+    case 2: hipLaunchKernelGGL((k_gemv_down<2, FP8, COLS>), grid, block, 0, s, hq, w, y, part, M, K, N, alpha_d); break;
+    case 4: hipLaunchKernelGGL((k_gemv_down<4, FP8, COLS>), grid, block, 0, s, hq, w, y, part, M, K, N, alpha_d); break;
+    case 8: hipLaunchKernelGGL((k_gemv_down<8, FP8, COLS>), grid, block, 0, s, hq, w, y, part, M, K, N, alpha_d); break;
+    case 16: hipLaunchKernelGGL((k_gemv_down<16, FP8, COLS>), grid, block, 0, s, hq, w, y, part, M, K, N, alpha_d); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -781,14 +792,17 @@ static int down_cols(int N) {
   return 16;  // measured: half-group workgroups stream slower at H = 5120
 }
 
-hipError_t launch_gemv_down(const uint8_t* hq, const uint8_t* w, uint16_t* y, int M, int K, int N,
-                            int W, bool fp8, float alpha_d, hipStream_t s) {
+// S > 1: K split over S workgroups per column group, fp32 partials [S][M][N]
+// into part (summed by the consumer), else bf16 Y.
+hipError_t launch_gemv_down(const uint8_t* hq, const uint8_t* w, uint16_t* y, float* part, int M, int K,
+                            int N, int W, int S, bool fp8, float alpha_d, hipStream_t s) {
   const int cols = down_cols(N);
+  if (S < 1 || S > (K >> 7)) return hipErrorInvalidValue;
   if (fp8)
-    return cols == 8 ? gemv_down_t<true, 8>(hq, w, y, M, K, N, W, alpha_d, s)
-                     : gemv_down_t<true, 16>(hq, w, y, M, K, N, W, alpha_d, s);
-  return cols == 8 ? gemv_down_t<false, 8>(hq, w, y, M, K, N, W, alpha_d, s)
-                   : gemv_down_t<false, 16>(hq, w, y, M, K, N, W, alpha_d, s);
+    return cols == 8 ? gemv_down_t<true, 8>(hq, w, y, part, M, K, N, W, S, alpha_d, s)
+                     : gemv_down_t<true, 16>(hq, w, y, part, M, K, N, W, S, alpha_d, s);
+  return cols == 8 ? gemv_down_t<false, 8>(hq, w, y, part, M, K, N, W, S, alpha_d, s)
+                   : gemv_down_t<false, 16>(hq, w, y, part, M, K, N, W, S, alpha_d, s);
 }
 
 bool gemm_config_ok(int cfg, bool fp8) { return cfg >= 0 && cfg < kGemmConfigs && (fp8 || cfg != 6); }

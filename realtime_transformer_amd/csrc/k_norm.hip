@@ -27,17 +27,27 @@
 
 namespace frt {
 
-// y of 8 consecutive elements from S fp32 partial tiles (split order)
+// y of 8 consecutive elements from S fp32 partial tiles (split order).  The
+// first four splits' loads are issued together before the adds.
 __device__ __forceinline__ uint4 y_from_partials(const float* __restrict__ part, size_t split_stride,
                                                  size_t off, int S, float alpha_d) {
-  float a[8];
-  {
-    const float4 p0 = *reinterpret_cast<const float4*>(part + off);
-    const float4 p1 = *reinterpret_cast<const float4*>(part + off + 4);
-    a[0] = p0.x; a[1] = p0.y; a[2] = p0.z; a[3] = p0.w;
-    a[4] = p1.x; a[5] = p1.y; a[6] = p1.z; a[7] = p1.w;
+  float4 lo[4], hi[4];
+#pragma unroll
+  for (int sp = 0; sp < 4; ++sp) {
+    if (sp < S) {
+      lo[sp] = *reinterpret_cast<const float4*>(part + sp * split_stride + off);
+      hi[sp] = *reinterpret_cast<const float4*>(part + sp * split_stride + off + 4);
+    }
   }
-  for (int sp = 1; sp < S; ++sp) {
+  float a[8] = {lo[0].x, lo[0].y, lo[0].z, lo[0].w, hi[0].x, hi[0].y, hi[0].z, hi[0].w};
+#pragma unroll
+  for (int sp = 1; sp < 4; ++sp) {
+    if (sp < S) {
+      a[0] += lo[sp].x; a[1] += lo[sp].y; a[2] += lo[sp].z; a[3] += lo[sp].w;
+      a[4] += hi[sp].x; a[5] += hi[sp].y; a[6] += hi[sp].z; a[7] += hi[sp].w;
+    }
+  }
+  for (int sp = 4; sp < S; ++sp) {
     const float4 p0 = *reinterpret_cast<const float4*>(part + sp * split_stride + off);
     const float4 p1 = *reinterpret_cast<const float4*>(part + sp * split_stride + off + 4);
     a[0] += p0.x; a[1] += p0.y; a[2] += p0.z; a[3] += p0.w;
@@ -65,13 +75,15 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
   const int nchunk = H >> 3;
   const size_t base = (size_t)(active ? row : 0) * (size_t)H;
 
-  uint4 rn[NC];
+  uint4 rn[NC], wn[NC];
   double sq = 0.0;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int ch = t + c * TPR;
     rn[c] = make_uint4(0, 0, 0, 0);
+    wn[c] = rn[c];
     if (active && ch < nchunk) {
+      wn[c] = *reinterpret_cast<const uint4*>(w_norm + (size_t)ch * 8);  // issued with r, y
       const uint4 rv = *reinterpret_cast<const uint4*>(r_prev + base + (size_t)ch * 8);
       uint4 yv = make_uint4(0, 0, 0, 0);
       if (y_part) {
@@ -112,7 +124,7 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
   for (int c = 0; c < NC; ++c) {
     const int ch = t + c * TPR;
     if (active && ch < nchunk) {
-      const uint4 wv = *reinterpret_cast<const uint4*>(w_norm + (size_t)ch * 8);
+      const uint4 wv = wn[c];
       uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
       uint32_t rr[4] = {rn[c].x, rn[c].y, rn[c].z, rn[c].w};
       float x[8];

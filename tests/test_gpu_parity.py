@@ -70,6 +70,17 @@ def test_small_shapes_fused_norm(spec):
     log(str(rep))
 
 
+@pytest.mark.parametrize("spec", [(107, 1, 256, 2048, 2, ACT_SWIGLU), (108, 5, 384, 2048, 3, ACT_GEGLU_TANH)],
+                         ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
+def test_small_shapes_gemv_down_split(spec):
+    # decode shapes whose down GEMV splits K over two workgroups per column
+    # group: the partial sums meet in the next layer's norm kernel
+    idx, M, H, I, L, act = spec
+    cfg = FFNConfig(idx, "small_split_%d" % idx, M, H, I, L, act)
+    rep = run_case(cfg)
+    log(str(rep))
+
+
 def test_ffn_block_m16():
     rep = run_case(CONFIGS[1])
     log(str(rep))
