@@ -11,7 +11,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfrt.so")
-SOURCES = ["frt_ffn.hip", "k_norm.hip", "k_quant.hip", "k_gemm.hip", "k_calib.hip"]
+SOURCES = ["frt_ffn.hip", "k_norm.hip", "k_quant.hip", "k_gemm.hip", "k_mm.hip", "k_calib.hip"]
 HEADERS = ["frt_device.h", os.path.join("..", "..", "include", "frt_ffn.h")]
 
 HIPCC_FLAGS = [

@@ -106,9 +106,21 @@ __host__ __device__ __forceinline__ uint32_t up_row_gated(uint32_t i) {
 //   tanh-GELU(z) = 0.5 z (1 + tanh(c (z + 0.044715 z^3))), c = sqrt(2/pi),
 //                = z * sigmoid(2 c (z + 0.044715 z^3))
 //   SiLU(z)      = z * sigmoid(z)
-// sigmoid(t) = 1 / (1 + exp(-t)) with the device library's expf; for
-// t < -88 exp overflows to +inf and the quotient is 0, the correct limit.
-__device__ __forceinline__ float sigmoid_f32(float t) { return 1.0f / (1.0f + expf(-t)); }
+// sigmoid(t) = 1 / (1 + exp(-t)), with exp(-t) = 2^(-t * log2 e) on the
+// hardware exp2 (v_exp_f32) and the hardware reciprocal (v_rcp_f32): two
+// transcendental instructions instead of the library expf and an IEEE
+// division (some twenty instructions per element in the GEMM epilogues).
+// Relative error: the product -t * log2 e is rounded once (2^-24 |t| log2 e
+// relative in exp), plus about one ulp from each instruction; for |t| < 16
+// that is under 1e-6, which moves a re-quantised E4M3 code only when the
+// value sits that close to a rounding boundary.  Limits: for t < -88 exp2
+// overflows to +inf and the reciprocal is 0; for t > 88 exp2 underflows to 0
+// and the result is 1; where the reciprocal would be an fp32 denormal it may
+// flush to 0, which every consumer quantises to E4M3 zero anyway.
+__device__ __forceinline__ float sigmoid_f32(float t) {
+  const float e = __builtin_amdgcn_exp2f(t * -1.4426950408889634f);
+  return __builtin_amdgcn_rcpf(1.0f + e);
+}
 __device__ __forceinline__ float gelu_tanh_f32(float z) {
   const float c2 = 1.5957691216057308f;  // 2 * sqrt(2/pi)
   float inner = z * (1.0f + 0.044715f * z * z);

@@ -50,6 +50,13 @@ hipError_t launch_gemm_gateup(int, int, bool, const uint8_t*, const uint8_t*, ui
 hipError_t launch_gemm_down(int, const uint8_t*, const uint8_t*, uint16_t*, float*, int, int, int, int,
                             bool, float, hipStream_t);
 bool gemm_config_ok(int, bool);
+hipError_t launch_mm_gateup(int, int, const uint8_t*, const uint8_t*, uint8_t*, int, int, int, float, float,
+                            float, hipStream_t);
+hipError_t launch_mm_down(int, const uint8_t*, const uint8_t*, uint16_t*, float*, int, int, int, int, float,
+                          hipStream_t);
+int mm_config_bm(int);
+int mm_config_bn(int);
+int mm_config_ks(int);
 int gemm_config_bm(int);
 int gemm_config_bn(int);
 hipError_t launch_calib_gateup(int, const float*, const uint8_t*, float*, float*, int, int, int,
@@ -109,6 +116,7 @@ struct DeviceGuard {
 namespace {
 
 constexpr int kGemvMaxM = 16;
+constexpr int kMMMinM = 128;  // from here on the LDS-DMA GEMM takes the f16 path
 constexpr int kCUs = 256;  // MI355X compute units (workgroup rounds are counted against them)
 
 int env_int(const char* name, int dflt) {
@@ -160,6 +168,7 @@ struct Layout {
   int k_dn;        // GEMV: K splits of the down GEMV (workgroups per 16 output columns)
   int split_dn;    // K splits of the down projection, either path (> 1: fp32 partials)
   int cfg_gu, cfg_dn;  // GEMM tile configurations
+  bool mm_gu, mm_dn;   // GEMM runs on the LDS-DMA f16 kernel (k_mm) rather than k_gemm
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -186,6 +195,35 @@ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 // output columns) takes 128 x 256 tiles and splits K until about two
 // workgroups per CU, its splits summed by the consumer.
 // FRT_GEMM_GATEUP_CFG / FRT_GEMM_DOWN_CFG / FRT_GEMM_DOWN_SPLIT override.
+// LDS-DMA GEMM (k_mm) configuration for an [M] x [N] output over K: the
+// tile that minimises workgroup rounds x tile work, and for the down GEMM the
+// K split that fills the chip against the cost of its fp32 partials (written
+// once, read once by the consumer).  Rates are rough per-CU figures; the
+// choice only has to rank the candidates.
+constexpr int kMMConfigCount = 6;
+void choose_mm(int M, int N, int K, bool allow_split, int& cfg, int& split) {
+  const double cu_flops = 1.5e15 / kCUs, hbm = 5.0e12;
+  double best = 1e30;
+  cfg = -1;
+  split = 1;
+  for (int c = 0; c < kMMConfigCount; ++c) {
+    const int bm = mm_config_bm(c), bn = mm_config_bn(c), ks = mm_config_ks(c);
+    if (N % bn || K % ks) continue;
+    const int tiles = (N / bn) * ceil_div(M, bm);
+    for (int sp = 1; sp <= (allow_split ? 8 : 1); sp *= 2) {
+      if (K / ks < 4 * sp) break;
+      const int rounds = ceil_div(tiles * sp, kCUs);
+      double t = rounds * (double)bm * bn * (K / sp) * 2.0 / cu_flops;
+      if (sp > 1) t += (double)sp * M * N * 8.0 / hbm;
+      if (t < best * 0.999) {
+        best = t;
+        cfg = c;
+        split = sp;
+      }
+    }
+  }
+}
+
 void choose_gemm(const frt_ffn_desc& d, Layout& lo) {
   const int npk = d.act != FRT_ACT_GELU_TANH ? 2 * d.I : d.I;
   const bool fp8_gu = (d.flags & FRT_FLAG_FP8_MFMA_GATEUP) != 0u;
@@ -204,6 +242,31 @@ void choose_gemm(const frt_ffn_desc& d, Layout& lo) {
   lo.cfg_dn = dn;
   lo.s_gu = 1;
   lo.s_dn = split;
+  // prefill-sized M: the LDS-DMA kernel unless the plan asks for the FP8
+  // matrix cores (FRT_MM_GATEUP_CFG / FRT_MM_DOWN_CFG / FRT_MM_DOWN_SPLIT override)
+  lo.mm_gu = lo.mm_dn = false;
+  if (d.M >= kMMMinM) {
+    int c, sp;
+    if (!fp8_gu) {
+      choose_mm(d.M, npk, d.H, false, c, sp);
+      c = env_int("FRT_MM_GATEUP_CFG", c);
+      if (c >= 0 && c < kMMConfigCount && npk % mm_config_bn(c) == 0 && d.H % mm_config_ks(c) == 0) {
+        lo.mm_gu = true;
+        lo.cfg_gu = c;
+      }
+    }
+    if (!fp8_dn) {
+      choose_mm(d.M, d.H, d.I, true, c, sp);
+      c = env_int("FRT_MM_DOWN_CFG", c);
+      sp = env_int("FRT_MM_DOWN_SPLIT", sp);
+      if (c >= 0 && c < kMMConfigCount && d.H % mm_config_bn(c) == 0 && d.I % mm_config_ks(c) == 0 && sp >= 1 &&
+          sp <= d.I / mm_config_ks(c)) {
+        lo.mm_dn = true;
+        lo.cfg_dn = c;
+        lo.s_dn = sp;
+      }
+    }
+  }
 }
 
 Layout make_layout(const frt_ffn_desc& d) {
@@ -601,6 +664,9 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
     else if (M <= kGemvMaxM)
       KERNEL_CHECK(launch_gemv_gateup(p->d.act, p->xq(l), p->wgu(l), p->hq(l), M, H, I, p->lo.s_gu,
                                       a_g, a_u, inv_h, s), "gemv_gateup");
+    else if (p->lo.mm_gu)
+      KERNEL_CHECK(launch_mm_gateup(p->d.act, p->lo.cfg_gu, p->xq(l), p->wgu(l), p->hq(l), M, H, npk, a_g, a_u,
+                                    inv_h, s), "mm_gateup");
     else
       KERNEL_CHECK(launch_gemm_gateup(p->d.act, p->lo.cfg_gu, p->fp8_gateup(), p->xq(l), p->wgu(l),
                                       p->hq(l), M, H, npk, a_g, a_u, inv_h, s), "gemm_gateup");
@@ -609,6 +675,9 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
       KERNEL_CHECK(launch_gemv_down(p->hq(l), p->wd(l), p->y(l + 1), p->part(), M, I, H, p->lo.s_dn,
                                     p->lo.k_dn, p->fp8_down(),
                                     a_d, s), "gemv_down");
+    else if (p->lo.mm_dn)
+      KERNEL_CHECK(launch_mm_down(p->lo.cfg_dn, p->hq(l), p->wd(l), p->y(l + 1), p->part(), M, I, H, p->lo.s_dn,
+                                  a_d, s), "mm_down");
     else
       KERNEL_CHECK(launch_gemm_down(p->lo.cfg_dn, p->hq(l), p->wd(l), p->y(l + 1), p->part(), M, I, H,
                                     p->lo.s_dn, p->fp8_down(), a_d, s), "gemm_down");
