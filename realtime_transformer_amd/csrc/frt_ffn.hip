@@ -50,9 +50,9 @@ hipError_t launch_gemm_gateup(int, int, bool, const uint8_t*, const uint8_t*, ui
 hipError_t launch_gemm_down(int, const uint8_t*, const uint8_t*, uint16_t*, float*, int, int, int, int,
                             bool, float, hipStream_t);
 bool gemm_config_ok(int, bool);
-hipError_t launch_mm_gateup(int, int, const uint8_t*, const uint8_t*, uint8_t*, int, int, int, float, float,
+hipError_t launch_mm_gateup(int, int, bool, const uint8_t*, const uint8_t*, uint8_t*, int, int, int, float, float,
                             float, hipStream_t);
-hipError_t launch_mm_down(int, const uint8_t*, const uint8_t*, uint16_t*, float*, int, int, int, int, float,
+hipError_t launch_mm_down(int, bool, const uint8_t*, const uint8_t*, uint16_t*, float*, int, int, int, int, float,
                           hipStream_t);
 int mm_config_bm(int);
 int mm_config_bn(int);
@@ -242,12 +242,12 @@ void choose_gemm(const frt_ffn_desc& d, Layout& lo) {
   lo.cfg_dn = dn;
   lo.s_gu = 1;
   lo.s_dn = split;
-  // prefill-sized M: the LDS-DMA kernel unless the plan asks for the FP8
+  // prefill-sized M: the LDS-DMA kernel, on the f16 or (plan flags) the FP8
   // matrix cores (FRT_MM_GATEUP_CFG / FRT_MM_DOWN_CFG / FRT_MM_DOWN_SPLIT override)
   lo.mm_gu = lo.mm_dn = false;
   if (d.M >= kMMMinM) {
     int c, sp;
-    if (!fp8_gu) {
+    {
       choose_mm(d.M, npk, d.H, false, c, sp);
       c = env_int("FRT_MM_GATEUP_CFG", c);
       if (c >= 0 && c < kMMConfigCount && npk % mm_config_bn(c) == 0 && d.H % mm_config_ks(c) == 0) {
@@ -255,7 +255,7 @@ void choose_gemm(const frt_ffn_desc& d, Layout& lo) {
         lo.cfg_gu = c;
       }
     }
-    if (!fp8_dn) {
+    {
       choose_mm(d.M, d.H, d.I, true, c, sp);
       c = env_int("FRT_MM_DOWN_CFG", c);
       sp = env_int("FRT_MM_DOWN_SPLIT", sp);
@@ -665,8 +665,8 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
       KERNEL_CHECK(launch_gemv_gateup(p->d.act, p->xq(l), p->wgu(l), p->hq(l), M, H, I, p->lo.s_gu,
                                       a_g, a_u, inv_h, s), "gemv_gateup");
     else if (p->lo.mm_gu)
-      KERNEL_CHECK(launch_mm_gateup(p->d.act, p->lo.cfg_gu, p->xq(l), p->wgu(l), p->hq(l), M, H, npk, a_g, a_u,
-                                    inv_h, s), "mm_gateup");
+      KERNEL_CHECK(launch_mm_gateup(p->d.act, p->lo.cfg_gu, p->fp8_gateup(), p->xq(l), p->wgu(l), p->hq(l), M, H,
+                                    npk, a_g, a_u, inv_h, s), "mm_gateup");
     else
       KERNEL_CHECK(launch_gemm_gateup(p->d.act, p->lo.cfg_gu, p->fp8_gateup(), p->xq(l), p->wgu(l),
                                       p->hq(l), M, H, npk, a_g, a_u, inv_h, s), "gemm_gateup");
@@ -676,8 +676,8 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
                                     p->lo.k_dn, p->fp8_down(),
                                     a_d, s), "gemv_down");
     else if (p->lo.mm_dn)
-      KERNEL_CHECK(launch_mm_down(p->lo.cfg_dn, p->hq(l), p->wd(l), p->y(l + 1), p->part(), M, I, H, p->lo.s_dn,
-                                  a_d, s), "mm_down");
+      KERNEL_CHECK(launch_mm_down(p->lo.cfg_dn, p->fp8_down(), p->hq(l), p->wd(l), p->y(l + 1), p->part(), M, I, H,
+                                  p->lo.s_dn, a_d, s), "mm_down");
     else
       KERNEL_CHECK(launch_gemm_down(p->lo.cfg_dn, p->hq(l), p->wd(l), p->y(l + 1), p->part(), M, I, H,
                                     p->lo.s_dn, p->fp8_down(), a_d, s), "gemm_down");

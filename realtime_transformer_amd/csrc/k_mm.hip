@@ -119,7 +119,7 @@ struct MMCfg {
 // swizzle only permutes which lane fetches which chunk); the fragment read
 // of lane l (row l % 32, chunk (l / 32) * 2 + q) then hits 16 distinct
 // 16-byte bank groups per 16 lanes, i.e. it is conflict-free.
-template <int EPI, class C>
+template <int EPI, class C, bool FP8>
 __global__ __launch_bounds__(C::NT) void k_mm(const uint8_t* __restrict__ act, const uint8_t* __restrict__ wt,
                                               void* __restrict__ out, float* __restrict__ part, int M, int K,
                                               int Npk, int tiles_n, int tiles_m, float alpha_a, float alpha_b,
@@ -216,20 +216,37 @@ __global__ __launch_bounds__(C::NT) void k_mm(const uint8_t* __restrict__ act, c
   const int w_rd = C::A_BYTES + (ww * TW) * 2048 + lane * 16;
 
   // a stage's fragments of this wave, both 16-byte K slices, in registers
+  typedef int v4i __attribute__((ext_vector_type(4)));
   struct Frag {
-    uint4 a[2][TA], w[2][TW];
+    v4i a[2][TA], w[2][TW];
   };
   auto read_stage = [&](const uint8_t* base, Frag& f) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
 #pragma unroll
       for (int i = 0; i < TA; ++i)
-        f.a[q][i] = *reinterpret_cast<const uint4*>(base + (q ? a_rd1 : a_rd0) + i * 32 * 64);
+        f.a[q][i] = *reinterpret_cast<const v4i*>(base + (q ? a_rd1 : a_rd0) + i * 32 * 64);
 #pragma unroll
-      for (int j = 0; j < TW; ++j) f.w[q][j] = *reinterpret_cast<const uint4*>(base + w_rd + j * 2048 + q * 1024);
+      for (int j = 0; j < TW; ++j) f.w[q][j] = *reinterpret_cast<const v4i*>(base + w_rd + j * 2048 + q * 1024);
     }
   };
   auto mma_stage = [&](const Frag& f) {
+    if (FP8) {
+      // one 32x32x64 FP8 step per tile pair: the lane's 32 bytes (both
+      // slices) are exactly the operand of v_mfma_scale_f32_32x32x64_f8f6f4
+      // (row l % 32, K bytes (l / 32) * 32 + [0, 32)); unit scales
+      v8i xa[TA], xw[TW];
+#pragma unroll
+      for (int i = 0; i < TA; ++i) xa[i] = __builtin_shufflevector(f.a[0][i], f.a[1][i], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int j = 0; j < TW; ++j) xw[j] = __builtin_shufflevector(f.w[0][j], f.w[1][j], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int j = 0; j < TW; ++j)
+#pragma unroll
+        for (int i = 0; i < TA; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xw[j], xa[i], acc[j][i], 0, 0, 0, 0, 0, 0);
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
 #pragma unroll
@@ -237,10 +254,10 @@ __global__ __launch_bounds__(C::NT) void k_mm(const uint8_t* __restrict__ act, c
         v8h xa[TA], xw[TW];
 #pragma unroll
         for (int i = 0; i < TA; ++i)
-          xa[i] = h ? cvt8_f16(f.a[q][i].z, f.a[q][i].w) : cvt8_f16(f.a[q][i].x, f.a[q][i].y);
+          xa[i] = h ? cvt8_f16(f.a[q][i][2], f.a[q][i][3]) : cvt8_f16(f.a[q][i][0], f.a[q][i][1]);
 #pragma unroll
         for (int j = 0; j < TW; ++j)
-          xw[j] = h ? cvt8_f16(f.w[q][j].z, f.w[q][j].w) : cvt8_f16(f.w[q][j].x, f.w[q][j].y);
+          xw[j] = h ? cvt8_f16(f.w[q][j][2], f.w[q][j][3]) : cvt8_f16(f.w[q][j][0], f.w[q][j][1]);
 #pragma unroll
         for (int j = 0; j < TW; ++j)
 #pragma unroll
@@ -265,7 +282,7 @@ __global__ __launch_bounds__(C::NT) void k_mm(const uint8_t* __restrict__ act, c
   if (nk > 1) issue(kb0 + 1, lds1);
   if (NS > 2 && nk > 2) issue(kb0 + 2, lds2);
   if (NS > 3 && nk > 3) issue(kb0 + 3, lds3);
-  Frag fcur, fnext;
+  Frag fa, fb;  // stage fragments, alternating between two register sets
   {
     // stage 0 complete: at most min(nk - 1, NS - 1) later stages outstanding
     const int after = (nk - 1) < (NS - 1) ? (nk - 1) : (NS - 1);
@@ -274,52 +291,68 @@ __global__ __launch_bounds__(C::NT) void k_mm(const uint8_t* __restrict__ act, c
     else if (after >= 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(CPW));
     else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     lds_barrier();
-    read_stage(lds0, fcur);
+    read_stage(lds0, fa);
   }
-  // step t: fcur holds stage t (reads issued); next = buffer of stage t + 1
-  auto step = [&](int t, uint8_t* cur, const uint8_t* next) {
-    if (t + 1 < nk) {
-      // loads of stage t + 1 done once at most min(nk - 2 - t, NS - 2)
-      // later stages of this wave are outstanding
-      const int after = (nk - 2 - t) < (NS - 2) ? (nk - 2 - t) : (NS - 2);
-      if (NS > 3 && after >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * CPW));
-      else if (NS > 2 && after >= 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(CPW));
-      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-      // this wave's reads of stage t must have returned before anyone refills it
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-      lds_barrier();
-      if (t + NS < nk) issue(kb0 + t + NS, cur);
-      read_stage(next, fnext);
-    }
-    mma_stage(fcur);
-    fcur = fnext;
+  // before step t: this wave's loads of stage t + 1 are complete once at most
+  // min(nk - 2 - t, NS - 2) later stages of its loads are outstanding, and
+  // its reads of stage t must have returned before anyone refills buffer t
+  auto sync_next = [&](int t) {
+    const int after = (nk - 2 - t) < (NS - 2) ? (nk - 2 - t) : (NS - 2);
+    if (NS > 3 && after >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * CPW));
+    else if (NS > 2 && after >= 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(CPW));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    lds_barrier();
   };
+  // step t: FC holds stage t (reads issued); NEXT is the buffer of stage
+  // t + 1, read into FN while FC is multiplied (the scheduling barrier keeps
+  // those reads ahead of the MFMAs, so their latency overlaps them).  A
+  // macro rather than a lambda: fragment sets passed by reference end up in
+  // scratch memory.
+#define FRT_MM_STEP(t, CUR, NEXT, FC, FN)            \
+  do {                                               \
+    if ((t) + 1 < nk) {                              \
+      sync_next(t);                                  \
+      if ((t) + NS < nk) issue(kb0 + (t) + NS, CUR); \
+      read_stage(NEXT, FN);                          \
+      __builtin_amdgcn_sched_barrier(0);             \
+    }                                                \
+    mma_stage(FC);                                   \
+  } while (0)
   int t = 0;
   if (NS == 2) {
     for (; t + 1 < nk; t += 2) {
-      step(t, lds0, lds1);
-      step(t + 1, lds1, lds0);
+      FRT_MM_STEP(t, lds0, lds1, fa, fb);
+      FRT_MM_STEP(t + 1, lds1, lds0, fb, fa);
     }
-    if (t < nk) step(t, lds0, lds1);
+    if (t < nk) FRT_MM_STEP(t, lds0, lds1, fa, fb);
   } else if (NS == 3) {
-    for (; t + 2 < nk; t += 3) {
-      step(t, lds0, lds1);
-      step(t + 1, lds1, lds2);
-      step(t + 2, lds2, lds0);
+    // period 6: three buffers x two register sets
+    for (; t + 5 < nk; t += 6) {
+      FRT_MM_STEP(t, lds0, lds1, fa, fb);
+      FRT_MM_STEP(t + 1, lds1, lds2, fb, fa);
+      FRT_MM_STEP(t + 2, lds2, lds0, fa, fb);
+      FRT_MM_STEP(t + 3, lds0, lds1, fb, fa);
+      FRT_MM_STEP(t + 4, lds1, lds2, fa, fb);
+      FRT_MM_STEP(t + 5, lds2, lds0, fb, fa);
     }
-    if (t < nk) step(t, lds0, lds1);
-    if (t + 1 < nk) step(t + 1, lds1, lds2);
+    if (t < nk) FRT_MM_STEP(t, lds0, lds1, fa, fb);
+    if (t + 1 < nk) FRT_MM_STEP(t + 1, lds1, lds2, fb, fa);
+    if (t + 2 < nk) FRT_MM_STEP(t + 2, lds2, lds0, fa, fb);
+    if (t + 3 < nk) FRT_MM_STEP(t + 3, lds0, lds1, fb, fa);
+    if (t + 4 < nk) FRT_MM_STEP(t + 4, lds1, lds2, fa, fb);
   } else {
     for (; t + 3 < nk; t += 4) {
-      step(t, lds0, lds1);
-      step(t + 1, lds1, lds2);
-      step(t + 2, lds2, lds3);
-      step(t + 3, lds3, lds0);
+      FRT_MM_STEP(t, lds0, lds1, fa, fb);
+      FRT_MM_STEP(t + 1, lds1, lds2, fb, fa);
+      FRT_MM_STEP(t + 2, lds2, lds3, fa, fb);
+      FRT_MM_STEP(t + 3, lds3, lds0, fb, fa);
     }
-    if (t < nk) step(t, lds0, lds1);
-    if (t + 1 < nk) step(t + 1, lds1, lds2);
-    if (t + 2 < nk) step(t + 2, lds2, lds3);
+    if (t < nk) FRT_MM_STEP(t, lds0, lds1, fa, fb);
+    if (t + 1 < nk) FRT_MM_STEP(t + 1, lds1, lds2, fb, fa);
+    if (t + 2 < nk) FRT_MM_STEP(t + 2, lds2, lds3, fa, fb);
   }
+#undef FRT_MM_STEP
 
   // ---- epilogue ----
   const int col = lane & 31, hi = lane >> 5;
@@ -400,43 +433,51 @@ int mm_config_bm(int c) { return (c >= 0 && c < kMMConfigs) ? kMM_BM[c] : 0; }
 int mm_config_bn(int c) { return (c >= 0 && c < kMMConfigs) ? kMM_BN[c] : 0; }
 int mm_config_ks(int c) { return (c >= 0 && c < kMMConfigs) ? kMM_KS[c] : 0; }
 
-template <int EPI, class C>
+template <int EPI, class C, bool FP8>
 static hipError_t mm_launch(const uint8_t* act, const uint8_t* w, void* out, float* part, int M, int K, int Npk,
                             int S, float a, float b, float inv, hipStream_t s) {
   if (Npk % C::BN || K % C::KS || S < 1 || S > K / C::KS) return hipErrorInvalidValue;
   const int tiles_n = Npk / C::BN, tiles_m = (M + C::BM - 1) / C::BM;
-  hipLaunchKernelGGL((k_mm<EPI, C>), dim3(tiles_n * tiles_m, S), dim3(C::NT), 0, s, act, w, out, part, M, K,
+  hipLaunchKernelGGL((k_mm<EPI, C, FP8>), dim3(tiles_n * tiles_m, S), dim3(C::NT), 0, s, act, w, out, part, M, K,
                      Npk, tiles_n, tiles_m, a, b, inv);
   return hipGetLastError();
 }
 
-template <int EPI>
+template <int EPI, bool FP8>
 static hipError_t mm_cfg(int cfg, const uint8_t* act, const uint8_t* w, void* out, float* part, int M, int K,
                          int Npk, int S, float a, float b, float inv, hipStream_t s) {
   switch (cfg) {
-    case 0: return mm_launch<EPI, MMC0>(act, w, out, part, M, K, Npk, S, a, b, inv, s);
-    case 1: return mm_launch<EPI, MMC1>(act, w, out, part, M, K, Npk, S, a, b, inv, s);
-    case 2: return mm_launch<EPI, MMC2>(act, w, out, part, M, K, Npk, S, a, b, inv, s);
-    case 3: return mm_launch<EPI, MMC3>(act, w, out, part, M, K, Npk, S, a, b, inv, s);
-    case 4: return mm_launch<EPI, MMC4>(act, w, out, part, M, K, Npk, S, a, b, inv, s);
-    case 5: return mm_launch<EPI, MMC5>(act, w, out, part, M, K, Npk, S, a, b, inv, s);
+    case 0: return mm_launch<EPI, MMC0, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s);
+    case 1: return mm_launch<EPI, MMC1, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s);
+    case 2: return mm_launch<EPI, MMC2, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s);
+    case 3: return mm_launch<EPI, MMC3, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s);
+    case 4: return mm_launch<EPI, MMC4, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s);
+    case 5: return mm_launch<EPI, MMC5, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 // Gate/up GEMM (act: 0 GeGLU, 1 SwiGLU, 2 non-gated GELU), E4M3 output.
-hipError_t launch_mm_gateup(int act, int cfg, const uint8_t* xq, const uint8_t* w, uint8_t* hq, int M, int K,
-                            int Npk, float alpha_g, float alpha_u, float inv_h, hipStream_t s) {
-  if (act == MM_GEGLU) return mm_cfg<MM_GEGLU>(cfg, xq, w, hq, nullptr, M, K, Npk, 1, alpha_g, alpha_u, inv_h, s);
-  if (act == MM_SWIGLU) return mm_cfg<MM_SWIGLU>(cfg, xq, w, hq, nullptr, M, K, Npk, 1, alpha_g, alpha_u, inv_h, s);
-  return mm_cfg<MM_GELU>(cfg, xq, w, hq, nullptr, M, K, Npk, 1, alpha_g, alpha_u, inv_h, s);
+// fp8: the products run on the FP8 matrix cores instead of the f16 ones.
+hipError_t launch_mm_gateup(int act, int cfg, bool fp8, const uint8_t* xq, const uint8_t* w, uint8_t* hq, int M,
+                            int K, int Npk, float alpha_g, float alpha_u, float inv_h, hipStream_t s) {
+  const float a = alpha_g, b = alpha_u;
+  if (fp8) {
+    if (act == MM_GEGLU) return mm_cfg<MM_GEGLU, true>(cfg, xq, w, hq, nullptr, M, K, Npk, 1, a, b, inv_h, s);
+    if (act == MM_SWIGLU) return mm_cfg<MM_SWIGLU, true>(cfg, xq, w, hq, nullptr, M, K, Npk, 1, a, b, inv_h, s);
+    return mm_cfg<MM_GELU, true>(cfg, xq, w, hq, nullptr, M, K, Npk, 1, a, b, inv_h, s);
+  }
+  if (act == MM_GEGLU) return mm_cfg<MM_GEGLU, false>(cfg, xq, w, hq, nullptr, M, K, Npk, 1, a, b, inv_h, s);
+  if (act == MM_SWIGLU) return mm_cfg<MM_SWIGLU, false>(cfg, xq, w, hq, nullptr, M, K, Npk, 1, a, b, inv_h, s);
+  return mm_cfg<MM_GELU, false>(cfg, xq, w, hq, nullptr, M, K, Npk, 1, a, b, inv_h, s);
 }
 
 // Down GEMM: S == 1 writes bf16 Y; S > 1 writes fp32 partials [S][M][N] to
 // part (summed in split order by the consumer).
-hipError_t launch_mm_down(int cfg, const uint8_t* hq, const uint8_t* w, uint16_t* y, float* part, int M, int K,
-                          int N, int S, float alpha_d, hipStream_t s) {
-  return mm_cfg<MM_DOWN>(cfg, hq, w, y, part, M, K, N, S, alpha_d, 0.0f, 0.0f, s);
+hipError_t launch_mm_down(int cfg, bool fp8, const uint8_t* hq, const uint8_t* w, uint16_t* y, float* part, int M,
+                          int K, int N, int S, float alpha_d, hipStream_t s) {
+  if (fp8) return mm_cfg<MM_DOWN, true>(cfg, hq, w, y, part, M, K, N, S, alpha_d, 0.0f, 0.0f, s);
+  return mm_cfg<MM_DOWN, false>(cfg, hq, w, y, part, M, K, N, S, alpha_d, 0.0f, 0.0f, s);
 }
 
 }  // namespace frt
