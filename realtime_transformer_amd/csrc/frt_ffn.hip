@@ -42,9 +42,9 @@ hipError_t launch_gemv_gateup(int, const uint8_t*, const uint8_t*, uint8_t*, int
 hipError_t launch_gemv_down(const uint8_t*, const uint8_t*, uint16_t*, float*, int, int, int, int, int,
                             bool, float, hipStream_t);
 bool gemv_fused_supported(int, int, int);
-hipError_t launch_gemv_gateup_fused(int, const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*,
-                                    uint8_t*, const uint8_t*, uint8_t*, int, int, int, int, float,
-                                    float, float, float, float, hipStream_t);
+hipError_t launch_gemv_gateup_fused(int, const uint16_t*, const uint16_t*, const float*, int, float, uint16_t*,
+                                    const uint16_t*, uint16_t*, uint8_t*, const uint8_t*, uint8_t*, int, int, int, int,
+                                    float, float, float, float, float, hipStream_t);
 hipError_t launch_gemm_gateup(int, int, bool, const uint8_t*, const uint8_t*, uint8_t*, int, int, int,
                               float, float, float, hipStream_t);
 hipError_t launch_gemm_down(int, const uint8_t*, const uint8_t*, uint16_t*, float*, int, int, int, int,
@@ -351,8 +351,7 @@ struct frt_plan {
   bool fp8_gateup() const { return (d.flags & FRT_FLAG_FP8_MFMA_GATEUP) != 0u; }
   // optionally, decode shapes run the norm inside the gate/up GEMV
   bool fused_norm() const {
-    return d.M <= kGemvMaxM && (d.flags & FRT_FLAG_FUSED_NORM) != 0u && lo.split_dn == 1 &&
-           gemv_fused_supported(d.M, d.H, lo.s_gu);
+    return d.M <= kGemvMaxM && (d.flags & FRT_FLAG_FUSED_NORM) != 0u && gemv_fused_supported(d.M, d.H, lo.s_gu);
   }
   bool act_scales_set() const {
     for (int l = 0; l < d.L; ++l)
@@ -637,7 +636,7 @@ frt_status frt_ffn_io_get(const frt_plan* p, frt_ffn_io* out) {
 static bool down_split(const frt_plan* p) { return p->lo.split_dn > 1; }
 
 static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t s,
-                                      bool y_from_partials = false) {
+                                      bool y_in_partials = false) {
   const int M = p->d.M, H = p->d.H, I = p->d.I;
   const int npk = p->gated ? 2 * I : I;
   const float s_x = p->s_x[l], s_h = p->s_h[l];
@@ -648,7 +647,7 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
     if (!fused) {
       const float* yp = nullptr;
       float a_prev = 0.0f;
-      if (y_from_partials && l > 0) {
+      if (y_in_partials && l > 0) {
         yp = p->part();
         a_prev = p->s_h[l - 1] * p->s_d[l - 1];
       }
@@ -657,10 +656,17 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
                    "add_rmsnorm_quant");
     }
   } else if (which == 1) {
-    if (fused)
-      KERNEL_CHECK(launch_gemv_gateup_fused(p->d.act, p->r(l), p->y(l), p->wn(l), p->r(l + 1), p->xq(l),
-                                            p->wgu(l), p->hq(l), M, H, I, p->lo.s_gu, p->d.eps, inv_x,
-                                            a_g, a_u, inv_h, s), "gemv_gateup_fused");
+    if (fused) {
+      const float* yp = nullptr;
+      float a_prev = 0.0f;
+      if (y_in_partials && l > 0) {
+        yp = p->part();
+        a_prev = p->s_h[l - 1] * p->s_d[l - 1];
+      }
+      KERNEL_CHECK(launch_gemv_gateup_fused(p->d.act, p->r(l), p->y(l), yp, p->lo.split_dn, a_prev, p->y(l), p->wn(l),
+                                            p->r(l + 1), p->xq(l), p->wgu(l), p->hq(l), M, H, I, p->lo.s_gu,
+                                            p->d.eps, inv_x, a_g, a_u, inv_h, s), "gemv_gateup_fused");
+    }
     else if (M <= kGemvMaxM)
       KERNEL_CHECK(launch_gemv_gateup(p->d.act, p->xq(l), p->wgu(l), p->hq(l), M, H, I, p->lo.s_gu,
                                       a_g, a_u, inv_h, s), "gemv_gateup");

@@ -182,30 +182,48 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup(const uint8_t* __restric
   }
 }
 
-// Decode form of gate/up with the norm fused in front (one kernel instead of
-// two per layer; batch-1 time goes to kernel boundaries).  Every workgroup
-// recomputes R' = bf16(R + Y), the fp64 mean square and the E4M3 row XQ of
-// its M <= 16 rows into LDS (the inputs are a few KiB, L2-resident after the
-// first workgroup), then streams its 16 columns of gate/up weights exactly as
-// k_gemv_gateup does with the activation fragments read from LDS.  Workgroup
-// 0 also stores R' and XQ to their slots.  The first two K blocks of weights
-// are requested before the prologue so the HBM stream starts at once.
-// Row layout of the prologue: for M == 1 the whole workgroup shares the row
-// (chunks of 8 elements, at most NCH per thread kept in registers); for
-// M > 1 each wave takes rows wave, wave + W, ...
+// Decode form of gate/up with the norm fused in front (two kernels per
+// layer instead of three; batch-1 time goes to kernel boundaries).  Every
+// workgroup forms y (from the previous down projection's split-K partials,
+// summed in split order and dequantised, or from the Y slot), R' = bf16(R +
+// y), the fp64 mean square and the E4M3 row XQ of its M <= 16 rows into LDS
+// (the inputs are a few KiB, L2-resident after the first workgroup), then
+// streams its 16 columns of gate/up weights exactly as k_gemv_gateup does
+// with the activation fragments read from LDS.  Workgroup 0 also stores y,
+// R' and XQ to their slots.  The first two K blocks of weights are requested
+// before the prologue so the HBM stream starts at once.  Row layout of the
+// prologue: for M == 1 the whole workgroup shares the row (chunks of 8
+// elements, at most NCH per thread kept in registers); for M > 1 each wave
+// takes rows wave, wave + W, ...
 constexpr int kFusedXqBytes = 32768;  // LDS for the quantised rows: M * H <= this
 
+struct FusedArgs {
+  const uint16_t* r_prev;  // R[l] bf16 [M][K]
+  const uint16_t* y_prev;  // Y[l] bf16 [M][K] (when y_part is null)
+  const float* y_part;     // previous down projection's fp32 partials [S][M][K], or null
+  int S;                   // their split count
+  float a_prev;            // their dequantisation scale
+  uint16_t* y_store;       // Y[l] slot, written from the partials by workgroup 0
+  const uint16_t* w_norm;  // RMSNorm weight [K]
+  uint16_t* r_out;         // R[l+1]
+  uint8_t* xq_out;         // XQ[l]
+  const uint8_t* w;        // packed gate/up weights
+  uint8_t* hq;             // HQ[l]
+  int M, K, I;
+  float eps, inv_x, alpha_g, alpha_u, inv_h;
+};
+
 template <int ACT, int W, int NCH, int G>
-__global__ __launch_bounds__(W * 64) void k_gemv_gateup_fused(
-    const uint16_t* __restrict__ r_prev, const uint16_t* __restrict__ y_prev,
-    const uint16_t* __restrict__ w_norm, uint16_t* __restrict__ r_out, uint8_t* __restrict__ xq_out,
-    const uint8_t* __restrict__ w, uint8_t* __restrict__ hq, int M, int K, int I, float eps,
-    float inv_x, float alpha_g, float alpha_u, float inv_h) {
+__global__ __launch_bounds__(W * 64, 4) void k_gemv_gateup_fused(const FusedArgs a) {
   constexpr bool GATED = ACT != GU_GELU;
   constexpr int NACC = GATED ? 2 : 1;
   __shared__ __attribute__((aligned(16))) uint8_t xs[kFusedXqBytes];
   __shared__ v4f red[W * NACC * 64];
   __shared__ double dred[W];
+  const int M = a.M, K = a.K, I = a.I;
+  const uint8_t* __restrict__ w = a.w;
+  uint8_t* __restrict__ hq = a.hq;
+  const float alpha_g = a.alpha_g, alpha_u = a.alpha_u, inv_h = a.inv_h, inv_x = a.inv_x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool writer = blockIdx.x == 0;
   const int KB = K >> 7;
@@ -241,9 +259,15 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup_fused(
       rn[c] = make_uint4(0, 0, 0, 0);
       wn[c] = rn[c];
       if (ch < nchunk) {
-        const uint4 rv = *reinterpret_cast<const uint4*>(r_prev + base + (size_t)ch * 8);
-        const uint4 yv = *reinterpret_cast<const uint4*>(y_prev + base + (size_t)ch * 8);
-        wn[c] = *reinterpret_cast<const uint4*>(w_norm + (size_t)ch * 8);
+        const uint4 rv = *reinterpret_cast<const uint4*>(a.r_prev + base + (size_t)ch * 8);
+        uint4 yv;
+        if (a.y_part) {
+          yv = y_from_partials(a.y_part, (size_t)M * K, base + (size_t)ch * 8, a.S, a.a_prev);
+          if (writer) *reinterpret_cast<uint4*>(a.y_store + base + (size_t)ch * 8) = yv;
+        } else {
+          yv = *reinterpret_cast<const uint4*>(a.y_prev + base + (size_t)ch * 8);
+        }
+        wn[c] = *reinterpret_cast<const uint4*>(a.w_norm + (size_t)ch * 8);
         const uint32_t rr[4] = {rv.x, rv.y, rv.z, rv.w}, yy[4] = {yv.x, yv.y, yv.z, yv.w};
         uint32_t o[4];
 #pragma unroll
@@ -254,7 +278,7 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup_fused(
           sq += dhi * dhi;
         }
         rn[c] = make_uint4(o[0], o[1], o[2], o[3]);
-        if (writer) *reinterpret_cast<uint4*>(r_out + base + (size_t)ch * 8) = rn[c];
+        if (writer) *reinterpret_cast<uint4*>(a.r_out + base + (size_t)ch * 8) = rn[c];
       }
     }
     sq = wave_sum_f64(sq);
@@ -265,7 +289,7 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup_fused(
 #pragma unroll
       for (int v = 0; v < W; ++v) sq += dred[v];
     }
-    const float inv_rms = (float)(1.0 / sqrt(sq / (double)K + (double)eps));
+    const float inv_rms = (float)(1.0 / sqrt(sq / (double)K + (double)a.eps));
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int ch = t_in + c * group_threads;
@@ -282,7 +306,7 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup_fused(
         q.x = e4m3x4(x[0] * inv_x, x[1] * inv_x, x[2] * inv_x, x[3] * inv_x);
         q.y = e4m3x4(x[4] * inv_x, x[5] * inv_x, x[6] * inv_x, x[7] * inv_x);
         *reinterpret_cast<uint2*>(xs + base + (size_t)ch * 8) = q;
-        if (writer) *reinterpret_cast<uint2*>(xq_out + base + (size_t)ch * 8) = q;
+        if (writer) *reinterpret_cast<uint2*>(a.xq_out + base + (size_t)ch * 8) = q;
       }
     }
   }
@@ -698,53 +722,37 @@ static int fused_groups() {
 }
 
 template <int ACT, int W, int NCH>
-static hipError_t gateup_fused_nch(const uint16_t* r_prev, const uint16_t* y_prev, const uint16_t* w_norm,
-                                   uint16_t* r_out, uint8_t* xq_out, const uint8_t* w, uint8_t* hq,
-                                   int M, int K, int I, float eps, float inv_x, float a_g, float a_u,
-                                   float inv_h, hipStream_t s) {
+static hipError_t gateup_fused_nch(const FusedArgs& a, hipStream_t s) {
   const int G = fused_groups();
-  const int P = I / 16;
+  const int P = a.I / 16;
   dim3 grid((P + G - 1) / G), block(W * 64);
   if (G == 1)
-    hipLaunchKernelGGL((k_gemv_gateup_fused<ACT, W, NCH, 1>), grid, block, 0, s, r_prev, y_prev, w_norm,
-                       r_out, xq_out, w, hq, M, K, I, eps, inv_x, a_g, a_u, inv_h);
+    hipLaunchKernelGGL((k_gemv_gateup_fused<ACT, W, NCH, 1>), grid, block, 0, s, a);
   else if (G == 2)
-    hipLaunchKernelGGL((k_gemv_gateup_fused<ACT, W, NCH, 2>), grid, block, 0, s, r_prev, y_prev, w_norm,
-                       r_out, xq_out, w, hq, M, K, I, eps, inv_x, a_g, a_u, inv_h);
+    hipLaunchKernelGGL((k_gemv_gateup_fused<ACT, W, NCH, 2>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((k_gemv_gateup_fused<ACT, W, NCH, 4>), grid, block, 0, s, r_prev, y_prev, w_norm,
-                       r_out, xq_out, w, hq, M, K, I, eps, inv_x, a_g, a_u, inv_h);
+    hipLaunchKernelGGL((k_gemv_gateup_fused<ACT, W, NCH, 4>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
 template <int ACT, int W>
-static hipError_t gateup_fused_w(const uint16_t* r_prev, const uint16_t* y_prev, const uint16_t* w_norm,
-                                 uint16_t* r_out, uint8_t* xq_out, const uint8_t* w, uint8_t* hq,
-                                 int M, int K, int I, float eps, float inv_x, float a_g, float a_u,
-                                 float inv_h, hipStream_t s) {
-  const int nchunk = K / 8;
-  const int gt = (M == 1) ? W * 64 : 64;
+static hipError_t gateup_fused_w(const FusedArgs& a, hipStream_t s) {
+  const int nchunk = a.K / 8;
+  const int gt = (a.M == 1) ? W * 64 : 64;
   const int nch = (nchunk + gt - 1) / gt;
-  if (nch <= 1)
-    return gateup_fused_nch<ACT, W, 1>(r_prev, y_prev, w_norm, r_out, xq_out, w, hq, M, K, I, eps, inv_x, a_g, a_u, inv_h, s);
-  if (nch <= 2)
-    return gateup_fused_nch<ACT, W, 2>(r_prev, y_prev, w_norm, r_out, xq_out, w, hq, M, K, I, eps, inv_x, a_g, a_u, inv_h, s);
-  if (nch <= 4)
-    return gateup_fused_nch<ACT, W, 4>(r_prev, y_prev, w_norm, r_out, xq_out, w, hq, M, K, I, eps, inv_x, a_g, a_u, inv_h, s);
-  if (nch <= 8)
-    return gateup_fused_nch<ACT, W, 8>(r_prev, y_prev, w_norm, r_out, xq_out, w, hq, M, K, I, eps, inv_x, a_g, a_u, inv_h, s);
+  if (nch <= 1) return gateup_fused_nch<ACT, W, 1>(a, s);
+  if (nch <= 2) return gateup_fused_nch<ACT, W, 2>(a, s);
+  if (nch <= 4) return gateup_fused_nch<ACT, W, 4>(a, s);
+  if (nch <= 8) return gateup_fused_nch<ACT, W, 8>(a, s);
   return hipErrorInvalidValue;
 }
 
 template <int ACT>
-static hipError_t gateup_fused_act(int W, const uint16_t* r_prev, const uint16_t* y_prev,
-                                   const uint16_t* w_norm, uint16_t* r_out, uint8_t* xq_out,
-                                   const uint8_t* w, uint8_t* hq, int M, int K, int I, float eps,
-                                   float inv_x, float a_g, float a_u, float inv_h, hipStream_t s) {
+static hipError_t gateup_fused_act(int W, const FusedArgs& a, hipStream_t s) {
   switch (W) {
-    case 2: return gateup_fused_w<ACT, 2>(r_prev, y_prev, w_norm, r_out, xq_out, w, hq, M, K, I, eps, inv_x, a_g, a_u, inv_h, s);
-    case 4: return gateup_fused_w<ACT, 4>(r_prev, y_prev, w_norm, r_out, xq_out, w, hq, M, K, I, eps, inv_x, a_g, a_u, inv_h, s);
-    case 8: return gateup_fused_w<ACT, 8>(r_prev, y_prev, w_norm, r_out, xq_out, w, hq, M, K, I, eps, inv_x, a_g, a_u, inv_h, s);
+    case 2: return gateup_fused_w<ACT, 2>(a, s);
+    case 4: return gateup_fused_w<ACT, 4>(a, s);
+    case 8: return gateup_fused_w<ACT, 8>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -757,16 +765,18 @@ bool gemv_fused_supported(int M, int K, int W) {
   return (K / 8 + gt - 1) / gt <= 8;
 }
 
-hipError_t launch_gemv_gateup_fused(int act, const uint16_t* r_prev, const uint16_t* y_prev,
-                                    const uint16_t* w_norm, uint16_t* r_out, uint8_t* xq_out,
-                                    const uint8_t* w, uint8_t* hq, int M, int K, int I, int W,
-                                    float eps, float inv_x, float a_g, float a_u, float inv_h,
+// y_part null: Y comes from y_prev; else from S fp32 partials (dequantised by
+// a_prev) and workgroup 0 stores it to y_store.
+hipError_t launch_gemv_gateup_fused(int act, const uint16_t* r_prev, const uint16_t* y_prev, const float* y_part,
+                                    int S, float a_prev, uint16_t* y_store, const uint16_t* w_norm,
+                                    uint16_t* r_out, uint8_t* xq_out, const uint8_t* w, uint8_t* hq, int M, int K,
+                                    int I, int W, float eps, float inv_x, float a_g, float a_u, float inv_h,
                                     hipStream_t s) {
-  if (act == GU_GEGLU)
-    return gateup_fused_act<GU_GEGLU>(W, r_prev, y_prev, w_norm, r_out, xq_out, w, hq, M, K, I, eps, inv_x, a_g, a_u, inv_h, s);
-  if (act == GU_SWIGLU)
-    return gateup_fused_act<GU_SWIGLU>(W, r_prev, y_prev, w_norm, r_out, xq_out, w, hq, M, K, I, eps, inv_x, a_g, a_u, inv_h, s);
-  return gateup_fused_act<GU_GELU>(W, r_prev, y_prev, w_norm, r_out, xq_out, w, hq, M, K, I, eps, inv_x, a_g, a_u, inv_h, s);
+  const FusedArgs a{r_prev, y_prev, y_part, S, a_prev, y_store, w_norm, r_out, xq_out, w, hq, M, K, I,
+                    eps, inv_x, a_g, a_u, inv_h};
+  if (act == GU_GEGLU) return gateup_fused_act<GU_GEGLU>(W, a, s);
+  if (act == GU_SWIGLU) return gateup_fused_act<GU_SWIGLU>(W, a, s);
+  return gateup_fused_act<GU_GELU>(W, a, s);
 }
 
 template <bool FP8, int COLS>

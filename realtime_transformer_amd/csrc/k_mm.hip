@@ -37,9 +37,10 @@
 // in the same lane, and four consecutive indices (r%4) form one 32-bit store.
 //
 // Workgroup order: consecutive workgroups go to different XCDs (round
-// robin over 8); tiles are numbered so that the workgroups of one XCD share
-// weight tiles (all row tiles of a column tile run on one XCD, whose L2 then
-// serves the weight tile to each of them).
+// robin over 8); work items are numbered so that the workgroups of one XCD
+// share operands (all row tiles of a column tile, and one K split, run on one
+// XCD, whose L2 then serves the weight tile and the activation rows to each
+// of them).
 #include "frt_device.h"
 
 namespace frt {
@@ -122,8 +123,8 @@ struct MMCfg {
 template <int EPI, class C, bool FP8>
 __global__ __launch_bounds__(C::NT) void k_mm(const uint8_t* __restrict__ act, const uint8_t* __restrict__ wt,
                                               void* __restrict__ out, float* __restrict__ part, int M, int K,
-                                              int Npk, int tiles_n, int tiles_m, float alpha_a, float alpha_b,
-                                              float inv_out) {
+                                              int Npk, int tiles_n, int tiles_m, int num_splits, float alpha_a,
+                                              float alpha_b, float inv_out) {
   constexpr int BM = C::BM, BN = C::BN, KS = C::KS, NS = C::NS, CPW = C::CPW;
   constexpr int TA = C::TA, TW = C::TW, NW = C::NW;
   constexpr bool GATED = EPI == MM_GEGLU || EPI == MM_SWIGLU;
@@ -139,22 +140,25 @@ __global__ __launch_bounds__(C::NT) void k_mm(const uint8_t* __restrict__ act, c
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wa = wave / C::WW, ww = wave % C::WW;
 
-  // tile of this workgroup (XCD-grouped when the column tiles split evenly)
-  int tn, tm;
+  // Work item of this workgroup: (split, column tile, row tile) numbered
+  // split-major, then column, then row.  Consecutive workgroups go to
+  // different XCDs (round robin over 8), so when the items divide evenly the
+  // numbering gives XCD x the contiguous range [x * T/8, (x+1) * T/8): one
+  // split, a few column tiles and all their row tiles share that XCD's L2
+  // (the weight tile once per column tile, the activation rows once per
+  // split).
+  const int S = num_splits, T = tiles_n * tiles_m * S;
+  int sp, tn, tm;
   {
     const int bid = blockIdx.x;
-    if ((tiles_n & 7) == 0) {
-      const int xcd = bid & 7, loc = bid >> 3;
-      tn = xcd * (tiles_n >> 3) + loc / tiles_m;
-      tm = loc % tiles_m;
-    } else {
-      tn = bid / tiles_m;
-      tm = bid % tiles_m;
-    }
+    const int idx = (T & 7) == 0 ? (bid & 7) * (T >> 3) + (bid >> 3) : bid;
+    sp = idx / (tiles_n * tiles_m);
+    const int rem = idx - sp * (tiles_n * tiles_m);
+    tn = rem / tiles_m;
+    tm = rem - tn * tiles_m;
   }
   const int m0 = tm * BM, n0 = tn * BN;
   const int nst = K / KS;
-  const int S = gridDim.y, sp = blockIdx.y;
   const int kb0 = sp * nst / S, kb1 = (sp + 1) * nst / S;
   const int KB = K >> 7;  // 128-byte K blocks of the packed weights
 
@@ -438,8 +442,8 @@ static hipError_t mm_launch(const uint8_t* act, const uint8_t* w, void* out, flo
                             int S, float a, float b, float inv, hipStream_t s) {
   if (Npk % C::BN || K % C::KS || S < 1 || S > K / C::KS) return hipErrorInvalidValue;
   const int tiles_n = Npk / C::BN, tiles_m = (M + C::BM - 1) / C::BM;
-  hipLaunchKernelGGL((k_mm<EPI, C, FP8>), dim3(tiles_n * tiles_m, S), dim3(C::NT), 0, s, act, w, out, part, M, K,
-                     Npk, tiles_n, tiles_m, a, b, inv);
+  hipLaunchKernelGGL((k_mm<EPI, C, FP8>), dim3(tiles_n * tiles_m * S), dim3(C::NT), 0, s, act, w, out, part, M, K,
+                     Npk, tiles_n, tiles_m, S, a, b, inv);
   return hipGetLastError();
 }
 

@@ -27,36 +27,6 @@
 
 namespace frt {
 
-// y of 8 consecutive elements from S fp32 partial tiles (split order).  The
-// first four splits' loads are issued together before the adds.
-__device__ __forceinline__ uint4 y_from_partials(const float* __restrict__ part, size_t split_stride,
-                                                 size_t off, int S, float alpha_d) {
-  float4 lo[4], hi[4];
-#pragma unroll
-  for (int sp = 0; sp < 4; ++sp) {
-    if (sp < S) {
-      lo[sp] = *reinterpret_cast<const float4*>(part + sp * split_stride + off);
-      hi[sp] = *reinterpret_cast<const float4*>(part + sp * split_stride + off + 4);
-    }
-  }
-  float a[8] = {lo[0].x, lo[0].y, lo[0].z, lo[0].w, hi[0].x, hi[0].y, hi[0].z, hi[0].w};
-#pragma unroll
-  for (int sp = 1; sp < 4; ++sp) {
-    if (sp < S) {
-      a[0] += lo[sp].x; a[1] += lo[sp].y; a[2] += lo[sp].z; a[3] += lo[sp].w;
-      a[4] += hi[sp].x; a[5] += hi[sp].y; a[6] += hi[sp].z; a[7] += hi[sp].w;
-    }
-  }
-  for (int sp = 4; sp < S; ++sp) {
-    const float4 p0 = *reinterpret_cast<const float4*>(part + sp * split_stride + off);
-    const float4 p1 = *reinterpret_cast<const float4*>(part + sp * split_stride + off + 4);
-    a[0] += p0.x; a[1] += p0.y; a[2] += p0.z; a[3] += p0.w;
-    a[4] += p1.x; a[5] += p1.y; a[6] += p1.z; a[7] += p1.w;
-  }
-  return make_uint4(pack_bf16x2(a[0] * alpha_d, a[1] * alpha_d), pack_bf16x2(a[2] * alpha_d, a[3] * alpha_d),
-                    pack_bf16x2(a[4] * alpha_d, a[5] * alpha_d), pack_bf16x2(a[6] * alpha_d, a[7] * alpha_d));
-}
-
 template <int TPR, int NC, bool MEASURE>
 __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
     const uint16_t* __restrict__ r_prev, const uint16_t* __restrict__ y_prev,

@@ -81,6 +81,17 @@ def test_small_shapes_gemv_down_split(spec):
     log(str(rep))
 
 
+@pytest.mark.parametrize("spec", [(109, 1, 256, 2048, 3, ACT_SWIGLU), (110, 4, 512, 2048, 2, ACT_GELU_TANH)],
+                         ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
+def test_small_shapes_fused_norm_split(spec):
+    # the norm fused into the gate/up GEMV, fed by the split down GEMV's
+    # partial sums (two kernels per layer)
+    idx, M, H, I, L, act = spec
+    cfg = FFNConfig(idx, "small_fusedsplit_%d" % idx, M, H, I, L, act)
+    rep = run_case(cfg, flags=2)
+    log(str(rep))
+
+
 def test_ffn_block_m16():
     rep = run_case(CONFIGS[1])
     log(str(rep))
