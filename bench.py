@@ -76,6 +76,8 @@ def setup(cfg, calibrate=True, keep_layers=(), flags=0):
 
 
 def time_replays(plan, steps, warmup):
+    """Mean ms per replay over `steps` back-to-back replays between two HIP
+    events on the plan's stream, and the wall time of that region."""
     import torch
     for _ in range(warmup):
         plan.replay()
@@ -92,6 +94,22 @@ def time_replays(plan, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     return e0.elapsed_time(e1) / steps, wall
+
+
+def replay_percentiles(plan, n):
+    """Each of n replays timed on its own (an event pair around it, a wait
+    after it): median, p10 and p90 in ms.  Isolated replays include the
+    graph launch latency that back-to-back replays overlap."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        a.record(plan.stream)
+        plan.replay()
+        b.record(plan.stream)
+        b.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    return {"median": round(float(np.median(t)), 4), "p10": round(float(np.percentile(t, 10)), 4),
+            "p90": round(float(np.percentile(t, 90)), 4), "n": n}
 
 
 def per_kernel_ms(plan, reps=3):
@@ -175,6 +193,7 @@ def main():
         plan.set_act_scales([0.01] * cfg.L, [0.01] * cfg.L)
         plan.capture()
     ms, wall = time_replays(plan, args.steps, args.warmup)
+    pct = replay_percentiles(plan, max(10, min(100, args.steps)))
     kms = [float(v) for v in per_kernel_ms(plan)]
     ms = float(ms)
     plan.close()
@@ -202,7 +221,8 @@ def main():
                    "tokens_per_s": round(cfg.M / (ms * 1e-3), 2),
                    "chain_hbm_gbs": round(chain_gbs, 1),
                    "chain_hbm_frac": round(chain_gbs / HBM_PEAK_GBS, 4),
-                   "wall_s_timed": round(wall, 4)},
+                   "wall_s_timed": round(wall, 4),
+                   "isolated_replay_ms": pct},
         "roofline": {"bound": "hbm", "kernel": "gemv_gateup", "achieved": round(gu_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic("traffic_gemv_gateup_llm_decode_m1.json")
@@ -224,6 +244,7 @@ def main():
                 p2.set_act_scales([0.01] * c2.L, [0.01] * c2.L)
                 p2.capture()
             ms2, _ = time_replays(p2, args.steps, args.warmup)
+            pct2 = replay_percentiles(p2, max(10, min(50, args.steps)))
             k2 = [float(v) for v in per_kernel_ms(p2)]
             p2.close()
             ms2 = float(ms2)
@@ -233,6 +254,7 @@ def main():
             return {"us_per_layer": round(ms2 * 1000.0 / c2.L, 3), "ms_per_step": round(ms2, 4),
                     "tokens_per_s": round(c2.M / (ms2 * 1e-3), 1), "chain_tflops": round(chain_tf, 1),
                     "fp8_mfma_frac": round(chain_tf / FP8_PEAK_TFLOPS, 4),
+                    "isolated_replay_ms": pct2,
                     "kernels_us": {"norm_quant": round(k2[0] * 1000, 3), "gateup": round(k2[1] * 1000, 3),
                                    "down": round(k2[2] * 1000, 3)},
                     "gateup_tflops": round(gu_tf, 1), "down_tflops": round(dn_tf, 1)}
