@@ -85,10 +85,13 @@ def lib():
         L.orc_quant_tensor.argtypes = [_c_u16p, ctypes.c_int64, _c_u8p]
         L.orc_quant_tensor_mt.restype = ctypes.c_float
         L.orc_quant_tensor_mt.argtypes = [_c_u16p, ctypes.c_int64, _c_u8p, ctypes.c_int]
+        L.orc_quant_tensor_fold.restype = ctypes.c_float
+        L.orc_quant_tensor_fold.argtypes = [_c_u16p, ctypes.c_int64, ctypes.c_int64, _c_u16p, _c_u8p,
+                                            ctypes.c_int]
         L.orc_add_rmsnorm_quant.restype = None
         L.orc_add_rmsnorm_quant.argtypes = [ctypes.c_int, ctypes.c_int, _c_u16p, _c_u16p, _c_u16p,
-                                            ctypes.c_float, ctypes.c_float, _c_u16p, _c_f32p,
-                                            _c_u8p, ctypes.c_int]
+                                            _c_u16p, _c_u16p, ctypes.c_float, ctypes.c_float, _c_u16p,
+                                            _c_f32p, _c_u8p, ctypes.c_int]
         L.orc_gateup.restype = ctypes.c_int
         L.orc_gateup.argtypes = [ctypes.c_int] * 4 + [_c_u8p, _c_u8p, _c_u8p, ctypes.c_float,
                                                       ctypes.c_float, ctypes.c_float, _c_f32p,
@@ -102,12 +105,13 @@ def lib():
         L.orc_down.argtypes = [ctypes.c_int] * 3 + [_c_u8p, _c_u8p, ctypes.c_float, _c_u16p,
                                                     ctypes.c_int]
         L.orc_block.restype = ctypes.c_int
-        L.orc_block.argtypes = ([ctypes.c_int] * 4 + [ctypes.c_float, _c_u16p, _c_u16p, _c_u16p,
-                                                     _c_u8p, _c_u8p, _c_u8p] + [ctypes.c_float] * 5
+        L.orc_block.argtypes = ([ctypes.c_int] * 4 + [ctypes.c_float, _c_u16p, _c_u16p, _c_u16p, _c_u16p,
+                                                     _c_u16p, _c_u8p, _c_u8p, _c_u8p] + [ctypes.c_float] * 5
                                 + [_c_u16p, _c_u8p, _c_u8p, _c_u16p, ctypes.c_int])
         L.orc_block_measure.restype = ctypes.c_int
         L.orc_block_measure.argtypes = ([ctypes.c_int] * 4 + [ctypes.c_float, _c_u16p, _c_u16p,
-                                                             _c_u16p, _c_u8p, _c_u8p, _c_u8p]
+                                                             _c_u16p, _c_u16p, _c_u16p, _c_u8p, _c_u8p,
+                                                             _c_u8p]
                                         + [ctypes.c_float] * 3
                                         + [_c_u16p, _c_u16p, _c_f32p, _c_f32p, ctypes.c_int])
         _lib = L
@@ -220,19 +224,35 @@ def quant_tensor(w_bf16, nthreads: Optional[int] = None) -> tuple:
     return codes, float(np.float32(s))
 
 
+def quant_tensor_fold(w_bf16, colw_bf16, nthreads: Optional[int] = None) -> tuple:
+    """Per-tensor E4M3 quantisation of f32(w[i][k] * colw[k]) for a bf16
+    [rows][cols] tensor and a bf16 [cols] column factor (norm fusion) ->
+    (codes, scale)."""
+    w = _u16(w_bf16)
+    c = _u16(colw_bf16)
+    rows, cols = w.shape
+    assert c.shape == (cols,)
+    codes = np.empty(w.shape, dtype=np.uint8)
+    s = lib().orc_quant_tensor_fold(_p(w, _c_u16p), rows, cols, _p(c, _c_u16p), _p(codes, _c_u8p),
+                                    nthreads or default_threads())
+    return codes, float(np.float32(s))
+
+
 def add_rmsnorm_quant(r_prev, y_prev, w_norm, eps: float, inv_x: float,
-                      nthreads: Optional[int] = None):
-    """-> (r_out bf16 [M,H], x fp32 [M,H], xq codes [M,H])."""
+                      nthreads: Optional[int] = None, mod=None):
+    """-> (r_out bf16 [M,H], x fp32 [M,H], xq codes [M,H]).  ``mod`` =
+    (scale, shift) bf16 [H] selects AdaRMSNorm modulation instead of w_norm."""
     r = _u16(r_prev)
     M, H = r.shape
     y = None if y_prev is None else _u16(y_prev)
     w = _u16(w_norm)
+    ms, mh = (None, None) if mod is None else (_u16(mod[0]), _u16(mod[1]))
     r_out = np.empty((M, H), np.uint16)
     x = np.empty((M, H), np.float32)
     xq = np.empty((M, H), np.uint8)
-    lib().orc_add_rmsnorm_quant(M, H, _p(r, _c_u16p), _p(y, _c_u16p), _p(w, _c_u16p),
-                                float(eps), float(inv_x), _p(r_out, _c_u16p), _p(x, _c_f32p),
-                                _p(xq, _c_u8p), nthreads or default_threads())
+    lib().orc_add_rmsnorm_quant(M, H, _p(r, _c_u16p), _p(y, _c_u16p), _p(w, _c_u16p), _p(ms, _c_u16p),
+                                _p(mh, _c_u16p), float(eps), float(inv_x), _p(r_out, _c_u16p),
+                                _p(x, _c_f32p), _p(xq, _c_u8p), nthreads or default_threads())
     return r_out, x, xq
 
 
@@ -286,9 +306,14 @@ def down(hq, qd, alpha_d: float, nthreads: Optional[int] = None) -> np.ndarray:
     return y
 
 
+ONES_BF16 = 0x3F80  # bf16 1.0
+
+
 @dataclass
 class LayerWeights:
-    """One layer's quantised weights as the oracle holds them."""
+    """One layer's quantised weights as the oracle holds them.  ``mod`` =
+    (scale, shift) bf16 [H] selects AdaRMSNorm modulation for the norm step
+    (then w_norm is unused)."""
     qg: Optional[np.ndarray]  # [I,H] codes (None when non-gated)
     qu: np.ndarray            # [I,H] codes
     qd: np.ndarray            # [H,I] codes
@@ -296,16 +321,26 @@ class LayerWeights:
     s_g: float
     s_u: float
     s_d: float
+    mod: Optional[tuple] = None
 
     @staticmethod
-    def quantize(w_gate, w_up, w_down, w_norm) -> "LayerWeights":
-        if w_gate is not None:
-            qg, s_g = quant_tensor(w_gate)
+    def quantize(w_gate, w_up, w_down, w_norm, norm_fuse: bool = False, mod=None) -> "LayerWeights":
+        """norm_fuse: fold w_norm into the gate/up matrices (per input
+        column) before quantising and normalise with a unit weight."""
+        w_norm = _u16(w_norm)
+        if norm_fuse:
+            qg, s_g = (None, 1.0) if w_gate is None else quant_tensor_fold(w_gate, w_norm)
+            qu, s_u = quant_tensor_fold(w_up, w_norm)
+            w_norm = np.full(w_norm.shape, ONES_BF16, np.uint16)
         else:
-            qg, s_g = None, 1.0
-        qu, s_u = quant_tensor(w_up)
+            qg, s_g = (None, 1.0) if w_gate is None else quant_tensor(w_gate)
+            qu, s_u = quant_tensor(w_up)
         qd, s_d = quant_tensor(w_down)
-        return LayerWeights(qg, qu, qd, _u16(w_norm), s_g, s_u, s_d)
+        mod = None if mod is None else (_u16(mod[0]), _u16(mod[1]))
+        return LayerWeights(qg, qu, qd, w_norm, s_g, s_u, s_d, mod)
+
+    def mod_ptrs(self):
+        return (None, None) if self.mod is None else self.mod
 
 
 def block(r_prev, y_prev, lw: LayerWeights, act: int, eps: float, s_x: float, s_h: float,
@@ -319,8 +354,10 @@ def block(r_prev, y_prev, lw: LayerWeights, act: int, eps: float, s_x: float, s_
     xq = np.empty((M, H), np.uint8)
     hq = np.empty((M, I), np.uint8)
     y_out = np.empty((M, H), np.uint16)
+    ms, mh = lw.mod_ptrs()
     rc = lib().orc_block(M, H, I, act, float(eps), _p(r, _c_u16p), _p(y, _c_u16p),
-                         _p(lw.w_norm, _c_u16p), _p(lw.qg, _c_u8p), _p(lw.qu, _c_u8p),
+                         _p(lw.w_norm, _c_u16p), _p(ms, _c_u16p), _p(mh, _c_u16p), _p(lw.qg, _c_u8p),
+                         _p(lw.qu, _c_u8p),
                          _p(lw.qd, _c_u8p), lw.s_g, lw.s_u, lw.s_d, float(s_x), float(s_h),
                          _p(r_out, _c_u16p), _p(xq, _c_u8p), _p(hq, _c_u8p), _p(y_out, _c_u16p),
                          nthreads or default_threads())
@@ -340,8 +377,10 @@ def block_measure(r_prev, y_prev, lw: LayerWeights, act: int, eps: float,
     y_out = np.empty((M, H), np.uint16)
     ax = ctypes.c_float(0.0)
     ah = ctypes.c_float(0.0)
+    ms, mh = lw.mod_ptrs()
     rc = lib().orc_block_measure(M, H, I, act, float(eps), _p(r, _c_u16p), _p(y, _c_u16p),
-                                 _p(lw.w_norm, _c_u16p), _p(lw.qg, _c_u8p), _p(lw.qu, _c_u8p),
+                                 _p(lw.w_norm, _c_u16p), _p(ms, _c_u16p), _p(mh, _c_u16p),
+                                 _p(lw.qg, _c_u8p), _p(lw.qu, _c_u8p),
                                  _p(lw.qd, _c_u8p), lw.s_g, lw.s_u, lw.s_d, _p(r_out, _c_u16p),
                                  _p(y_out, _c_u16p), ctypes.byref(ax), ctypes.byref(ah),
                                  nthreads or default_threads())

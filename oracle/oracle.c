@@ -254,7 +254,17 @@ typedef struct {
   float part_max[256];
   int64_t n;
   int nthreads;
+  const uint16_t *colw; /* optional per-column factor (norm fusion), NULL = none */
+  int64_t cols;
 } quant_ctx;
+
+/* element i of the tensor being quantised: bf16 w[i], or with norm fusion
+   f32(w[i] * colw[i % cols]) -- a product of two bf16 values, exact in fp32 */
+static float quant_value(const quant_ctx *q, int64_t i) {
+  float v = orc_bf16_to_f32(q->w[i]);
+  if (q->colw) v = v * orc_bf16_to_f32(q->colw[i % q->cols]);
+  return v;
+}
 
 static void amax_range(void *p, int64_t begin, int64_t end) {
   /* one range per thread: begin..end covers thread t's slice */
@@ -264,7 +274,7 @@ static void amax_range(void *p, int64_t begin, int64_t end) {
     int64_t lo = q->n * t / q->nthreads, hi = q->n * (t + 1) / q->nthreads;
     float m = 0.0f;
     for (int64_t i = lo; i < hi; ++i) {
-      float a = fabsf(orc_bf16_to_f32(q->w[i]));
+      float a = fabsf(quant_value(q, i));
       if (a > m) m = a;
     }
     q->part_max[t] = m;
@@ -273,15 +283,43 @@ static void amax_range(void *p, int64_t begin, int64_t end) {
 
 static void encode_range(void *p, int64_t begin, int64_t end) {
   quant_ctx *q = (quant_ctx *)p;
-  for (int64_t i = begin; i < end; ++i) q->codes[i] = orc_e4m3_encode(orc_bf16_to_f32(q->w[i]) * q->inv);
+  for (int64_t i = begin; i < end; ++i) q->codes[i] = orc_e4m3_encode(quant_value(q, i) * q->inv);
 }
 
 /* amax is an exact max (order does not matter); the threads only split the
    elements. */
+/* Pi0-style norm fusion (FlashRT itsolotime article, section 5.2: the
+   decoder spec folds the RMSNorm weight into the gate/up matrices before
+   Quant()): tensor [rows][cols] times colw[col] per input column, then the
+   same per-tensor quantisation. */
+float orc_quant_tensor_fold(const uint16_t *w, int64_t rows, int64_t cols, const uint16_t *colw,
+                            uint8_t *codes, int nthreads) {
+  quant_ctx q;
+  int64_t n = rows * cols;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  q.w = w;
+  q.codes = codes;
+  q.n = n;
+  q.nthreads = nthreads;
+  q.colw = colw;
+  q.cols = cols;
+  parallel_for(nthreads, nthreads, amax_range, &q);
+  float amax = 0.0f;
+  for (int t = 0; t < nthreads; ++t)
+    if (q.part_max[t] > amax) amax = q.part_max[t];
+  float s = orc_scale_from_amax(amax);
+  q.inv = 1.0f / s;
+  parallel_for(n, nthreads, encode_range, &q);
+  return s;
+}
+
 float orc_quant_tensor_mt(const uint16_t *w, int64_t n, uint8_t *codes, int nthreads) {
   quant_ctx q;
   if (nthreads < 1) nthreads = 1;
   if (nthreads > 256) nthreads = 256;
+  q.colw = NULL;
+  q.cols = 1;
   q.w = w;
   q.codes = codes;
   q.n = n;
@@ -304,13 +342,18 @@ float orc_quant_tensor(const uint16_t *w, int64_t n, uint8_t *codes) {
 /* Step 1: fused residual add + RMSNorm + E4M3 quantise, one row at a time. */
 /*   r'  = bf16( r + y )                          (new residual, stored)     */
 /*   S   = sum r'^2 in fp64;  inv_rms = f32( 1/sqrt(S/H + eps) ), fp64 math */
-/*   x   = f32( f32(r' * inv_rms) * w )                                     */
+/*   t   = f32( r' * inv_rms )                                              */
+/*   x   = f32( t * w )                       (RMSNorm weight w), or with   */
+/*         AdaRMSNorm modulation (itsolotime article, section 5.2: Pi0.5    */
+/*         modulates through AdaRMSNorm Dense layers instead of a folded    */
+/*         weight): x = f32( f32( t * f32(1 + scale) ) + shift )            */
 /*   xq  = e4m3( f32(x * inv_x) )                                           */
 /* ------------------------------------------------------------------------ */
 
 typedef struct {
   int H;
   const uint16_t *r_prev, *y_prev, *w_norm;
+  const uint16_t *mod_scale, *mod_shift; /* both NULL, or both [H] bf16 */
   float eps, inv_x;
   uint16_t *r_out;
   float *x_out; /* optional: the unquantised normalised row */
@@ -334,7 +377,14 @@ static void norm_range(void *p, int64_t begin, int64_t end) {
     float inv_rms = (float)(1.0 / sqrt(S / (double)H + (double)c->eps));
     for (int j = 0; j < H; ++j) {
       float t = orc_bf16_to_f32(ro[j]) * inv_rms;
-      float x = t * orc_bf16_to_f32(c->w_norm[j]);
+      float x;
+      if (c->mod_scale) {
+        float one_plus = 1.0f + orc_bf16_to_f32(c->mod_scale[j]);
+        float ts = t * one_plus;
+        x = ts + orc_bf16_to_f32(c->mod_shift[j]);
+      } else {
+        x = t * orc_bf16_to_f32(c->w_norm[j]);
+      }
       if (c->x_out) c->x_out[m * H + j] = x;
       if (c->xq_out) c->xq_out[m * H + j] = orc_e4m3_encode(x * c->inv_x);
     }
@@ -342,9 +392,10 @@ static void norm_range(void *p, int64_t begin, int64_t end) {
 }
 
 void orc_add_rmsnorm_quant(int M, int H, const uint16_t *r_prev, const uint16_t *y_prev,
-                           const uint16_t *w_norm, float eps, float inv_x, uint16_t *r_out,
+                           const uint16_t *w_norm, const uint16_t *mod_scale,
+                           const uint16_t *mod_shift, float eps, float inv_x, uint16_t *r_out,
                            float *x_out, uint8_t *xq_out, int nthreads) {
-  norm_ctx c = {H, r_prev, y_prev, w_norm, eps, inv_x, r_out, x_out, xq_out};
+  norm_ctx c = {H, r_prev, y_prev, w_norm, mod_scale, mod_shift, eps, inv_x, r_out, x_out, xq_out};
   parallel_for(M, nthreads, norm_range, &c);
 }
 
@@ -419,7 +470,8 @@ int orc_down(int M, int H, int I, const uint8_t *hq, const uint8_t *qd, float al
 /* ------------------------------------------------------------------------ */
 
 int orc_block(int M, int H, int I, int act, float eps, const uint16_t *r_prev,
-              const uint16_t *y_prev, const uint16_t *w_norm, const uint8_t *qg,
+              const uint16_t *y_prev, const uint16_t *w_norm, const uint16_t *mod_scale,
+              const uint16_t *mod_shift, const uint8_t *qg,
               const uint8_t *qu, const uint8_t *qd, float s_g, float s_u, float s_d, float s_x,
               float s_h, uint16_t *r_out, uint8_t *xq_out, uint8_t *hq_out, uint16_t *y_out,
               int nthreads) {
@@ -429,7 +481,9 @@ int orc_block(int M, int H, int I, int act, float eps, const uint16_t *r_prev,
   uint8_t *hq = hq_out ? hq_out : (uint8_t *)malloc((size_t)M * I);
   int rc = 0;
   if (!xq || !hq) rc = -2;
-  if (!rc) orc_add_rmsnorm_quant(M, H, r_prev, y_prev, w_norm, eps, inv_x, r_out, NULL, xq, nthreads);
+  if (!rc)
+    orc_add_rmsnorm_quant(M, H, r_prev, y_prev, w_norm, mod_scale, mod_shift, eps, inv_x, r_out, NULL, xq,
+                          nthreads);
   if (!rc) rc = orc_gateup(M, H, I, act, xq, qg, qu, alpha_g, alpha_u, inv_h, NULL, hq, nthreads);
   if (!rc) rc = orc_down(M, H, I, hq, qd, alpha_d, y_out, nthreads);
   if (!xq_out) free(xq);
@@ -482,7 +536,8 @@ static void measure_gemm(int M, int N, int K, const float *a, const uint8_t *b, 
 }
 
 int orc_block_measure(int M, int H, int I, int act, float eps, const uint16_t *r_prev,
-                      const uint16_t *y_prev, const uint16_t *w_norm, const uint8_t *qg,
+                      const uint16_t *y_prev, const uint16_t *w_norm, const uint16_t *mod_scale,
+                      const uint16_t *mod_shift, const uint8_t *qg,
                       const uint8_t *qu, const uint8_t *qd, float s_g, float s_u, float s_d,
                       uint16_t *r_out, uint16_t *y_out, float *amax_x, float *amax_h,
                       int nthreads) {
@@ -494,7 +549,8 @@ int orc_block_measure(int M, int H, int I, int act, float eps, const uint16_t *r
   int rc = 0;
   if (!x || !h || !su || !sd || (act != ORC_ACT_GELU_TANH && !sg)) rc = -2;
   if (!rc) {
-    orc_add_rmsnorm_quant(M, H, r_prev, y_prev, w_norm, eps, 1.0f, r_out, x, NULL, nthreads);
+    orc_add_rmsnorm_quant(M, H, r_prev, y_prev, w_norm, mod_scale, mod_shift, eps, 1.0f, r_out, x, NULL,
+                          nthreads);
     for (int64_t i = 0; i < (int64_t)M * H; ++i)
       if (fabsf(x[i]) > *amax_x) *amax_x = fabsf(x[i]);
     measure_gemm(M, I, H, x, qu, su, nthreads);

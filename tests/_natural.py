@@ -29,7 +29,7 @@ def block_fp32_sums(r, y, lw: oracle.LayerWeights, act: int, eps: float, s_x: fl
     L8 = lut()
     inv_x = np.float32(np.float32(1.0) / np.float32(s_x))
     inv_h = np.float32(np.float32(1.0) / np.float32(s_h))
-    r1, _, xq = oracle.add_rmsnorm_quant(r, y, lw.w_norm, eps, inv_x)
+    r1, _, xq = oracle.add_rmsnorm_quant(r, y, lw.w_norm, eps, inv_x, mod=lw.mod)
     X = L8[xq]
     Au = X @ L8[lw.qu].T
     Ag = None if lw.qg is None else X @ L8[lw.qg].T

@@ -127,7 +127,7 @@ def test_calibration_is_brute_force_max():
     for l, lw in enumerate(lws):
         ax = ah = 0.0
         for (r, y) in res.cal_states[l]:
-            _, x, _ = oracle.add_rmsnorm_quant(r, y, lw.w_norm, 1e-6, 1.0)
+            _, x, _ = oracle.add_rmsnorm_quant(r, y, lw.w_norm, 1e-6, 1.0, mod=lw.mod)
             ax = max(ax, float(np.abs(x).max()))
             # h recomputed from the definition with fp64 sums
             dec = lambda c: oracle.e4m3_decode(c)
