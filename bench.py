@@ -56,12 +56,15 @@ def setup(cfg, calibrate=True, keep_layers=(), flags=0):
     """Plan with every layer quantised, calibrated, inputs set, graph captured."""
     from realtime_transformer_amd import datagen
     from realtime_transformer_amd.plan import FFNPlan
+    from realtime_transformer_amd import _abi as abi
     t0 = time.time()
     plan = FFNPlan(cfg.M, cfg.H, cfg.I, cfg.L, cfg.act, cfg.eps, flags=flags)
     kept = {}
     for l in range(cfg.L):
         w = datagen.layer_weights(cfg, l)
         plan.load_layer(l, *w)
+        if flags & abi.FRT_FLAG_ADA_NORM:
+            plan.set_modulation(l, *datagen.modulation(cfg, l))
         if l in keep_layers:
             kept[l] = w
         if l % 8 == 7 or l == cfg.L - 1:
@@ -157,6 +160,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-fp8-modes", action="store_true",
                     help="skip timing the opt-in FP8 matrix-core modes of the second workload")
+    ap.add_argument("--no-norm-variants", action="store_true",
+                    help="skip timing the action-expert chain with the norm variants")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="first copy this many MiB device-to-device once (a plain copy kernel of known "
@@ -282,6 +287,26 @@ def main():
             modes["fp8_down"]["accuracy"] = "per-block bf16 Y within tolerance; chain drifts further than exact sums"
             modes["fp8_both"]["accuracy"] = "HQ code mismatch ~1.4e-3 (above the 1e-4 byte tolerance)"
             out["secondary"]["fp8_matrix_core_modes"] = modes
+
+    if not args.no_norm_variants:
+        # the action-expert chain (where the pages place AdaRMSNorm) with the
+        # plain norm, the norm weight folded into gate/up, and AdaRMSNorm
+        from realtime_transformer_amd import _abi as abi
+        c3 = BY_NAME["action_expert_m50"]
+        nv = {"workload": c3.name, "M": c3.M, "H": c3.H, "I": c3.I, "layers": c3.L}
+        for name, fl in (("plain", 0), ("norm_fuse", abi.FRT_FLAG_NORM_FUSE), ("ada_norm", abi.FRT_FLAG_ADA_NORM)):
+            p3, _, _ = setup(c3, calibrate=not args.no_calibrate, flags=fl)
+            if args.no_calibrate:
+                p3.set_act_scales([0.01] * c3.L, [0.01] * c3.L)
+                p3.capture()
+            ms3, _ = time_replays(p3, args.steps, args.warmup)
+            k3 = [float(v) for v in per_kernel_ms(p3)]
+            p3.close()
+            nv[name] = {"us_per_layer": round(float(ms3) * 1000.0 / c3.L, 3),
+                        "kernels_us": {"norm_quant": round(k3[0] * 1000, 3), "gateup": round(k3[1] * 1000, 3),
+                                       "down": round(k3[2] * 1000, 3)}}
+            log("[bench %s] %s: %.2f us/layer" % (c3.name, name, nv[name]["us_per_layer"]))
+        out["norm_variants"] = nv
 
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle for ~%.0fs" % args.cpu_seconds)

@@ -86,6 +86,20 @@ typedef enum {
 /* FRT_FLAG_FP8_MFMA_GATEUP: the gate/up GEMM for M > 16 runs on the FP8
  *   matrix cores (same accumulation behaviour as FRT_FLAG_FP8_MFMA_DOWN). */
 #define FRT_FLAG_FP8_MFMA_GATEUP 4u
+/* FRT_FLAG_NORM_FUSE (itsolotime article, section 5.2: the Pi0 decoder spec
+ *   folds each RMSNorm weight into the gate/up matrices): frt_quant_weights
+ *   quantises f32(W[i][k] * w_norm[k]) for the gate and up matrices (exact
+ *   products of two bf16 values) and the norm step multiplies by 1. */
+#define FRT_FLAG_NORM_FUSE 8u
+/* FRT_FLAG_ADA_NORM (same section: Pi0.5 modulates through AdaRMSNorm Dense
+ *   layers instead): the norm step computes
+ *   x = f32(f32(f32(r' * inv_rms) * f32(1 + scale[k])) + shift[k]) with the
+ *   per-layer bf16 vectors in the plan's modulation slots (frt_ffn_io
+ *   mod_slots; zeros after plan creation, i.e. unit scale and no shift); the
+ *   RMSNorm weight is not used.  The caller writes new modulation (from its
+ *   conditioning Dense layers) into the slots before a replay, like the
+ *   inputs.  Excludes FRT_FLAG_NORM_FUSE and FRT_FLAG_FUSED_NORM. */
+#define FRT_FLAG_ADA_NORM 16u
 
 /* Problem description.  Requirements: M >= 1, L >= 1, H and I multiples of
  * 128, H <= 16384, I <= 32768, act in frt_act, eps > 0.  `device` is the HIP
@@ -114,6 +128,9 @@ typedef struct {
   size_t stride_rh;  /* bytes between R (and Y) slots = M*H*2      */
   size_t stride_xq;  /* bytes between XQ slots = M*H              */
   size_t stride_hq;  /* bytes between HQ slots = M*I              */
+  void *mod_slots;   /* bf16 [L][2][H]: AdaRMSNorm scale, shift per layer
+                        (FRT_FLAG_ADA_NORM plans; NULL otherwise)   */
+  size_t stride_mod; /* bytes between layers' modulation = 2*H*2   */
 } frt_ffn_io;
 
 /* Workspace bytes a plan for `desc` needs (weights, slots, split-K partials,
@@ -140,7 +157,9 @@ frt_status frt_ffn_plan_destroy(frt_plan *plan);
  *   d_w_gate  device bf16 [I,H] (must be NULL for FRT_ACT_GELU_TANH)
  *   d_w_up    device bf16 [I,H]
  *   d_w_down  device bf16 [H,I]
- *   d_norm_w  device bf16 [H] RMSNorm weight (copied into the plan)
+ *   d_norm_w  device bf16 [H] RMSNorm weight (copied into the plan; with
+ *             FRT_FLAG_NORM_FUSE folded into the gate/up matrices and the
+ *             plan's norm weight set to 1; unused with FRT_FLAG_ADA_NORM)
  * Runs on `stream` and synchronises it (the scales are host scalars).  The
  * caller may free the bf16 inputs after return.  Marks a captured graph
  * stale. */

@@ -29,6 +29,8 @@ FRT_ACT_GELU_TANH = 2
 FRT_FLAG_FP8_MFMA_DOWN = 1
 FRT_FLAG_FUSED_NORM = 2
 FRT_FLAG_FP8_MFMA_GATEUP = 4
+FRT_FLAG_NORM_FUSE = 8
+FRT_FLAG_ADA_NORM = 16
 
 _STATUS_NAMES = {0: "FRT_OK", 1: "FRT_ERR_INVALID_ARG", 2: "FRT_ERR_HIP", 3: "FRT_ERR_STATE",
                  4: "FRT_ERR_UNSUPPORTED", 5: "FRT_ERR_WORKSPACE"}
@@ -58,7 +60,8 @@ class frt_ffn_io(ctypes.Structure):
     _fields_ = [("r_slots", ctypes.c_void_p), ("y_slots", ctypes.c_void_p),
                 ("xq_slots", ctypes.c_void_p), ("hq_slots", ctypes.c_void_p),
                 ("z_out", ctypes.c_void_p), ("stride_rh", ctypes.c_size_t),
-                ("stride_xq", ctypes.c_size_t), ("stride_hq", ctypes.c_size_t)]
+                ("stride_xq", ctypes.c_size_t), ("stride_hq", ctypes.c_size_t),
+                ("mod_slots", ctypes.c_void_p), ("stride_mod", ctypes.c_size_t)]
 
 
 _lib = None

@@ -27,16 +27,16 @@
 #include "frt_device.h"
 
 namespace frt {
-hipError_t launch_add_rmsnorm_quant(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*,
+hipError_t launch_add_rmsnorm_quant(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*,
                                     uint8_t*, int, int, float, float, hipStream_t, const float*, int,
                                     float, uint16_t*);
-hipError_t launch_add_rmsnorm_measure(const uint16_t*, const uint16_t*, const uint16_t*,
+hipError_t launch_add_rmsnorm_measure(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*,
                                       uint16_t*, float*, float*, int, int, float, hipStream_t);
 hipError_t launch_residual_add(const uint16_t*, uint16_t*, uint16_t*, size_t, hipStream_t, const float*,
                                int, float);
 hipError_t launch_e4m3_encode(const float*, uint8_t*, int64_t, hipStream_t);
-hipError_t launch_amax_bf16(const uint16_t*, size_t, float*, hipStream_t);
-hipError_t launch_quant_pack(const uint16_t*, uint8_t*, int, int, float, int, hipStream_t);
+hipError_t launch_amax_bf16(const uint16_t*, size_t, float*, hipStream_t, const uint16_t*, size_t);
+hipError_t launch_quant_pack(const uint16_t*, uint8_t*, int, int, float, int, hipStream_t, const uint16_t*);
 hipError_t launch_gemv_gateup(int, const uint8_t*, const uint8_t*, uint8_t*, int, int, int, int,
                               float, float, float, hipStream_t);
 hipError_t launch_gemv_down(const uint8_t*, const uint8_t*, uint16_t*, float*, int, int, int, int, int,
@@ -159,6 +159,7 @@ struct Layout {
   size_t wd, wd_layer;    // packed down weights
   size_t wn;              // norm weights [L][H] bf16
   size_t r, y, xq, hq, z; // activation slots
+  size_t mod;             // AdaRMSNorm modulation [L][2][H] bf16
   size_t part, part_bytes;
   size_t cnt, cnt_words;  // 2 regions of cnt_words uint32
   size_t amax;            // [2 + 2L] floats
@@ -180,8 +181,12 @@ bool desc_ok(const frt_ffn_desc* d) {
   if (d->H > 16384 || d->I > 32768) return false;
   if (d->act < FRT_ACT_GEGLU_TANH || d->act > FRT_ACT_GELU_TANH) return false;
   if (!(d->eps > 0.0f) || !std::isfinite(d->eps)) return false;
-  if ((d->flags & ~(uint32_t)(FRT_FLAG_FP8_MFMA_DOWN | FRT_FLAG_FUSED_NORM | FRT_FLAG_FP8_MFMA_GATEUP)) != 0u || d->device < 0)
+  if ((d->flags & ~(uint32_t)(FRT_FLAG_FP8_MFMA_DOWN | FRT_FLAG_FUSED_NORM | FRT_FLAG_FP8_MFMA_GATEUP |
+                              FRT_FLAG_NORM_FUSE | FRT_FLAG_ADA_NORM)) != 0u || d->device < 0)
     return false;
+  // AdaRMSNorm replaces the norm weight: no folding of it, and no fused
+  // decode prologue (which applies the weight)
+  if ((d->flags & FRT_FLAG_ADA_NORM) && (d->flags & (FRT_FLAG_NORM_FUSE | FRT_FLAG_FUSED_NORM))) return false;
   if ((int64_t)d->M * d->I > (int64_t)1 << 31) return false;
   return true;
 }
@@ -290,6 +295,7 @@ Layout make_layout(const frt_ffn_desc& d) {
   lo.xq = take(L * M * H);
   lo.hq = take(L * M * I);
   lo.z = take(M * H * 2);
+  lo.mod = take((d.flags & FRT_FLAG_ADA_NORM) ? L * 2 * H * 2 : 256);
 
   size_t part = 0, words = 1;
   if (d.M <= kGemvMaxM) {
@@ -342,6 +348,12 @@ struct frt_plan {
   uint8_t* xq(int l) const { return ws + lo.xq + (size_t)l * mh(); }
   uint8_t* hq(int l) const { return ws + lo.hq + (size_t)l * d.M * d.I; }
   uint16_t* z() const { return reinterpret_cast<uint16_t*>(ws + lo.z); }
+  bool ada() const { return (d.flags & FRT_FLAG_ADA_NORM) != 0u; }
+  bool norm_fuse() const { return (d.flags & FRT_FLAG_NORM_FUSE) != 0u; }
+  // layer l's modulation [2][H] (scale, shift), or null when the plan has none
+  const uint16_t* mod(int l) const {
+    return ada() ? reinterpret_cast<const uint16_t*>(ws + lo.mod) + (size_t)l * 2 * d.H : nullptr;
+  }
   float* part() const { return reinterpret_cast<float*>(ws + lo.part); }
   uint32_t* cnt(int region) const {
     return reinterpret_cast<uint32_t*>(ws + lo.cnt) + (size_t)region * lo.cnt_words;
@@ -438,6 +450,7 @@ frt_status frt_ffn_plan_create(const frt_ffn_desc* desc, void* d_workspace, size
   p->s_d.assign(desc->L, 1.0f);
   hipError_t e = hipMemset(p->ws + lo.cnt, 0, 2 * lo.cnt_words * 4);
   if (e == hipSuccess) e = hipMemset(p->y(0), 0, p->mh() * 2);
+  if (e == hipSuccess && p->ada()) e = hipMemset(p->ws + lo.mod, 0, (size_t)desc->L * 2 * desc->H * 2);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     delete p;
@@ -459,18 +472,19 @@ frt_status frt_ffn_plan_destroy(frt_plan* plan) {
 }
 
 static frt_status quant_one(frt_plan* p, const void* src, int N, int K, uint8_t* dst, int mode,
-                            float* scale_out, hipStream_t s) {
+                            float* scale_out, hipStream_t s, const void* colw = nullptr) {
+  const uint16_t* cw = static_cast<const uint16_t*>(colw);
   float* am = p->amax();
   float amax_h = 0.0f;
   HIP_CHECK(hipMemsetAsync(am, 0, sizeof(float), s));
-  KERNEL_CHECK(launch_amax_bf16(static_cast<const uint16_t*>(src), (size_t)N * K, am, s), "amax_bf16");
+  KERNEL_CHECK(launch_amax_bf16(static_cast<const uint16_t*>(src), (size_t)N * K, am, s, cw, (size_t)K), "amax_bf16");
   HIP_CHECK(hipMemcpyAsync(&amax_h, am, sizeof(float), hipMemcpyDeviceToHost, s));
   HIP_CHECK(hipStreamSynchronize(s));
   if (!std::isfinite(amax_h))
     return fail(FRT_ERR_INVALID_ARG, "frt_quant_weights: weight tensor holds a non-finite value");
   const float sc = amax_h > 0.0f ? amax_h / 448.0f : 1.0f;
   const float inv = 1.0f / sc;
-  KERNEL_CHECK(launch_quant_pack(static_cast<const uint16_t*>(src), dst, N, K, inv, mode, s),
+  KERNEL_CHECK(launch_quant_pack(static_cast<const uint16_t*>(src), dst, N, K, inv, mode, s, cw),
                "quant_pack");
   *scale_out = sc;
   return FRT_OK;
@@ -491,14 +505,20 @@ frt_status frt_quant_weights(frt_plan* p, int32_t layer, const void* d_w_gate, c
   const int H = p->d.H, I = p->d.I;
   float sg = 1.0f, su = 1.0f, sd = 1.0f;
   frt_status st;
+  // norm fusion folds the RMSNorm weight into the gate/up matrices per input
+  // column and normalises with a unit weight
+  const void* fold = p->norm_fuse() ? d_norm_w : nullptr;
   if (p->gated) {
-    if ((st = quant_one(p, d_w_gate, I, H, p->wgu(layer), 1, &sg, s)) != FRT_OK) return st;
-    if ((st = quant_one(p, d_w_up, I, H, p->wgu(layer), 2, &su, s)) != FRT_OK) return st;
+    if ((st = quant_one(p, d_w_gate, I, H, p->wgu(layer), 1, &sg, s, fold)) != FRT_OK) return st;
+    if ((st = quant_one(p, d_w_up, I, H, p->wgu(layer), 2, &su, s, fold)) != FRT_OK) return st;
   } else {
-    if ((st = quant_one(p, d_w_up, I, H, p->wgu(layer), 0, &su, s)) != FRT_OK) return st;
+    if ((st = quant_one(p, d_w_up, I, H, p->wgu(layer), 0, &su, s, fold)) != FRT_OK) return st;
   }
   if ((st = quant_one(p, d_w_down, H, I, p->wd(layer), 0, &sd, s)) != FRT_OK) return st;
-  HIP_CHECK(hipMemcpyAsync(p->wn(layer), d_norm_w, (size_t)H * 2, hipMemcpyDeviceToDevice, s));
+  if (p->norm_fuse())
+    HIP_CHECK(hipMemsetD16Async(reinterpret_cast<hipDeviceptr_t>(p->wn(layer)), 0x3F80u, (size_t)H, s));
+  else
+    HIP_CHECK(hipMemcpyAsync(p->wn(layer), d_norm_w, (size_t)H * 2, hipMemcpyDeviceToDevice, s));
   HIP_CHECK(hipStreamSynchronize(s));
   p->s_g[layer] = sg;
   p->s_u[layer] = su;
@@ -567,7 +587,7 @@ frt_status frt_calibrate(frt_plan* p, const void* const* d_r_batches, const void
     for (int l = layer_begin; l < layer_end; ++l) {
       uint16_t* r_next = cr + (size_t)(l & 1) * rh;
       uint16_t* y_next = cy + (size_t)(l & 1) * rh;
-      KERNEL_CHECK(launch_add_rmsnorm_measure(r_cur, y_cur, p->wn(l), r_next, x, am + l, rows, H,
+      KERNEL_CHECK(launch_add_rmsnorm_measure(r_cur, y_cur, p->wn(l), p->mod(l), r_next, x, am + l, rows, H,
                                               p->d.eps, s), "add_rmsnorm_measure");
       KERNEL_CHECK(launch_calib_gateup(p->d.act, x, p->wgu(l), h, am + L + l, rows, H, I,
                                        p->gated ? p->s_g[l] : p->s_u[l], p->s_u[l], s), "calib_gateup");
@@ -626,6 +646,8 @@ frt_status frt_ffn_io_get(const frt_plan* p, frt_ffn_io* out) {
   out->stride_rh = p->mh() * 2;
   out->stride_xq = p->mh();
   out->stride_hq = (size_t)p->d.M * p->d.I;
+  out->mod_slots = p->ada() ? p->ws + p->lo.mod : nullptr;
+  out->stride_mod = (size_t)2 * p->d.H * 2;
   return FRT_OK;
 }
 
@@ -651,7 +673,7 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
         yp = p->part();
         a_prev = p->s_h[l - 1] * p->s_d[l - 1];
       }
-      KERNEL_CHECK(launch_add_rmsnorm_quant(p->r(l), p->y(l), p->wn(l), p->r(l + 1), p->xq(l), M, H,
+      KERNEL_CHECK(launch_add_rmsnorm_quant(p->r(l), p->y(l), p->wn(l), p->mod(l), p->r(l + 1), p->xq(l), M, H,
                                             p->d.eps, inv_x, s, yp, p->lo.split_dn, a_prev, p->y(l)),
                    "add_rmsnorm_quant");
     }

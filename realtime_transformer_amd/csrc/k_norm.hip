@@ -10,7 +10,9 @@
 //   r'  = bf16(r + y)                       stored as the new residual
 //   S   = sum r'^2 in fp64 (each square is exact in fp64)
 //   inv = f32(1 / sqrt(S / H + eps)) in fp64, rounded once
-//   x   = f32(f32(r' * inv) * w)
+//   x   = f32(f32(r' * inv) * w), or with AdaRMSNorm modulation (per-channel
+//         scale and shift, itsolotime article section 5.2: Pi0.5)
+//         x = f32(f32(f32(r' * inv) * f32(1 + scale)) + shift)
 //   xq  = e4m3(f32(x * inv_x))              (measure mode: store x, amax|x|)
 //
 // Bound: HBM.  Algorithmic bytes per row: 2H (r) + 2H (y) + 2H (r') + H (xq),
@@ -30,7 +32,7 @@ namespace frt {
 template <int TPR, int NC, bool MEASURE>
 __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
     const uint16_t* __restrict__ r_prev, const uint16_t* __restrict__ y_prev,
-    const uint16_t* __restrict__ w_norm, uint16_t* __restrict__ r_out,
+    const uint16_t* __restrict__ w_norm, const uint16_t* __restrict__ mod, uint16_t* __restrict__ r_out,
     uint8_t* __restrict__ xq_out, float* __restrict__ x_out, float* __restrict__ amax_out,
     int M, int H, float eps, float inv_x, const float* __restrict__ y_part, int S, float alpha_d,
     uint16_t* __restrict__ y_store) {
@@ -45,15 +47,23 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
   const int nchunk = H >> 3;
   const size_t base = (size_t)(active ? row : 0) * (size_t)H;
 
-  uint4 rn[NC], wn[NC];
+  // wn: the norm weight, or with modulation the per-channel scale (mh: shift)
+  uint4 rn[NC], wn[NC], mh[NC];
   double sq = 0.0;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int ch = t + c * TPR;
     rn[c] = make_uint4(0, 0, 0, 0);
     wn[c] = rn[c];
+    mh[c] = rn[c];
     if (active && ch < nchunk) {
-      wn[c] = *reinterpret_cast<const uint4*>(w_norm + (size_t)ch * 8);  // issued with r, y
+      // issued with r, y
+      if (mod) {
+        wn[c] = *reinterpret_cast<const uint4*>(mod + (size_t)ch * 8);
+        mh[c] = *reinterpret_cast<const uint4*>(mod + H + (size_t)ch * 8);
+      } else {
+        wn[c] = *reinterpret_cast<const uint4*>(w_norm + (size_t)ch * 8);
+      }
       const uint4 rv = *reinterpret_cast<const uint4*>(r_prev + base + (size_t)ch * 8);
       uint4 yv = make_uint4(0, 0, 0, 0);
       if (y_part) {
@@ -97,11 +107,21 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
       const uint4 wv = wn[c];
       uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
       uint32_t rr[4] = {rn[c].x, rn[c].y, rn[c].z, rn[c].w};
+      uint32_t hh[4] = {mh[c].x, mh[c].y, mh[c].z, mh[c].w};
       float x[8];
+      if (mod) {
+        // AdaRMSNorm: f32(f32(t * f32(1 + scale)) + shift)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[2 * j] = (bf16_lo(rr[j]) * inv_rms) * bf16_lo(ww[j]);
-        x[2 * j + 1] = (bf16_hi(rr[j]) * inv_rms) * bf16_hi(ww[j]);
+        for (int j = 0; j < 4; ++j) {
+          x[2 * j] = ((bf16_lo(rr[j]) * inv_rms) * (1.0f + bf16_lo(ww[j]))) + bf16_lo(hh[j]);
+          x[2 * j + 1] = ((bf16_hi(rr[j]) * inv_rms) * (1.0f + bf16_hi(ww[j]))) + bf16_hi(hh[j]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[2 * j] = (bf16_lo(rr[j]) * inv_rms) * bf16_lo(ww[j]);
+          x[2 * j + 1] = (bf16_hi(rr[j]) * inv_rms) * bf16_hi(ww[j]);
+        }
       }
       if (MEASURE) {
         float4* dst = reinterpret_cast<float4*>(x_out + base + (size_t)ch * 8);
@@ -163,7 +183,7 @@ __global__ __launch_bounds__(256) void k_e4m3_encode(const float* __restrict__ i
 
 template <bool MEASURE>
 static hipError_t launch_norm_t(const uint16_t* r_prev, const uint16_t* y_prev,
-                                const uint16_t* w, uint16_t* r_out, uint8_t* xq, float* x_out,
+                                const uint16_t* w, const uint16_t* mod, uint16_t* r_out, uint8_t* xq, float* x_out,
                                 float* amax, int M, int H, float eps, float inv_x,
                                 hipStream_t s, const float* y_part = nullptr, int S = 1,
                                 float alpha_d = 0.0f, uint16_t* y_store = nullptr) {
@@ -175,26 +195,26 @@ static hipError_t launch_norm_t(const uint16_t* r_prev, const uint16_t* y_prev,
     dim3 grid((M + 3) / 4);
     if (nc <= 2)
       hipLaunchKernelGGL((k_add_rmsnorm_quant<64, 2, MEASURE>), grid, dim3(256), 0, s, r_prev,
-                         y_prev, w, r_out, xq, x_out, amax, M, H, eps, inv_x, y_part, S, alpha_d,
+                         y_prev, w, mod, r_out, xq, x_out, amax, M, H, eps, inv_x, y_part, S, alpha_d,
                          y_store);
     else if (nc <= 4)
       hipLaunchKernelGGL((k_add_rmsnorm_quant<64, 4, MEASURE>), grid, dim3(256), 0, s, r_prev,
-                         y_prev, w, r_out, xq, x_out, amax, M, H, eps, inv_x, y_part, S, alpha_d,
+                         y_prev, w, mod, r_out, xq, x_out, amax, M, H, eps, inv_x, y_part, S, alpha_d,
                          y_store);
     else
       hipLaunchKernelGGL((k_add_rmsnorm_quant<64, 8, MEASURE>), grid, dim3(256), 0, s, r_prev,
-                         y_prev, w, r_out, xq, x_out, amax, M, H, eps, inv_x, y_part, S, alpha_d,
+                         y_prev, w, mod, r_out, xq, x_out, amax, M, H, eps, inv_x, y_part, S, alpha_d,
                          y_store);
   } else {
     const int nc = (nchunk + 255) / 256;
     dim3 grid(M);
     if (nc <= 4)
       hipLaunchKernelGGL((k_add_rmsnorm_quant<256, 4, MEASURE>), grid, dim3(256), 0, s, r_prev,
-                         y_prev, w, r_out, xq, x_out, amax, M, H, eps, inv_x, y_part, S, alpha_d,
+                         y_prev, w, mod, r_out, xq, x_out, amax, M, H, eps, inv_x, y_part, S, alpha_d,
                          y_store);
     else
       hipLaunchKernelGGL((k_add_rmsnorm_quant<256, 8, MEASURE>), grid, dim3(256), 0, s, r_prev,
-                         y_prev, w, r_out, xq, x_out, amax, M, H, eps, inv_x, y_part, S, alpha_d,
+                         y_prev, w, mod, r_out, xq, x_out, amax, M, H, eps, inv_x, y_part, S, alpha_d,
                          y_store);
   }
   return hipGetLastError();
@@ -203,7 +223,7 @@ static hipError_t launch_norm_t(const uint16_t* r_prev, const uint16_t* y_prev,
 // Small M: spread one row over a whole workgroup so the row's loads are
 // issued by many waves at once (latency, not bandwidth, bounds M <= 64).
 hipError_t launch_add_rmsnorm_quant(const uint16_t* r_prev, const uint16_t* y_prev,
-                                    const uint16_t* w, uint16_t* r_out, uint8_t* xq, int M,
+                                    const uint16_t* w, const uint16_t* mod, uint16_t* r_out, uint8_t* xq, int M,
                                     int H, float eps, float inv_x, hipStream_t s,
                                     const float* y_part, int S, float alpha_d, uint16_t* y_store) {
   const int nchunk = H / 8;
@@ -212,26 +232,26 @@ hipError_t launch_add_rmsnorm_quant(const uint16_t* r_prev, const uint16_t* y_pr
     dim3 grid(M);
     if (nc <= 1)
       hipLaunchKernelGGL((k_add_rmsnorm_quant<256, 1, false>), grid, dim3(256), 0, s, r_prev,
-                         y_prev, w, r_out, xq, nullptr, nullptr, M, H, eps, inv_x, y_part, S, alpha_d, y_store);
+                         y_prev, w, mod, r_out, xq, nullptr, nullptr, M, H, eps, inv_x, y_part, S, alpha_d, y_store);
     else if (nc <= 2)
       hipLaunchKernelGGL((k_add_rmsnorm_quant<256, 2, false>), grid, dim3(256), 0, s, r_prev,
-                         y_prev, w, r_out, xq, nullptr, nullptr, M, H, eps, inv_x, y_part, S, alpha_d, y_store);
+                         y_prev, w, mod, r_out, xq, nullptr, nullptr, M, H, eps, inv_x, y_part, S, alpha_d, y_store);
     else if (nc <= 4)
       hipLaunchKernelGGL((k_add_rmsnorm_quant<256, 4, false>), grid, dim3(256), 0, s, r_prev,
-                         y_prev, w, r_out, xq, nullptr, nullptr, M, H, eps, inv_x, y_part, S, alpha_d, y_store);
+                         y_prev, w, mod, r_out, xq, nullptr, nullptr, M, H, eps, inv_x, y_part, S, alpha_d, y_store);
     else
       hipLaunchKernelGGL((k_add_rmsnorm_quant<256, 8, false>), grid, dim3(256), 0, s, r_prev,
-                         y_prev, w, r_out, xq, nullptr, nullptr, M, H, eps, inv_x, y_part, S, alpha_d, y_store);
+                         y_prev, w, mod, r_out, xq, nullptr, nullptr, M, H, eps, inv_x, y_part, S, alpha_d, y_store);
     return hipGetLastError();
   }
-  return launch_norm_t<false>(r_prev, y_prev, w, r_out, xq, nullptr, nullptr, M, H, eps, inv_x,
+  return launch_norm_t<false>(r_prev, y_prev, w, mod, r_out, xq, nullptr, nullptr, M, H, eps, inv_x,
                               s, y_part, S, alpha_d, y_store);
 }
 
 hipError_t launch_add_rmsnorm_measure(const uint16_t* r_prev, const uint16_t* y_prev,
-                                      const uint16_t* w, uint16_t* r_out, float* x_out,
+                                      const uint16_t* w, const uint16_t* mod, uint16_t* r_out, float* x_out,
                                       float* amax, int M, int H, float eps, hipStream_t s) {
-  return launch_norm_t<true>(r_prev, y_prev, w, r_out, nullptr, x_out, amax, M, H, eps, 1.0f, s);
+  return launch_norm_t<true>(r_prev, y_prev, w, mod, r_out, nullptr, x_out, amax, M, H, eps, 1.0f, s);
 }
 
 hipError_t launch_residual_add(const uint16_t* r, uint16_t* y, uint16_t* z, size_t n, hipStream_t s,

@@ -15,10 +15,13 @@ Distributions (one reading per workload, stated in the design doc of the repo):
                  distinct positions set to exactly +20 or -20 (fair coin)
   previous out   Y[0] ~ N(0,1) for the single block, zero for the chains
   calibration    4 batches drawn like the evaluation input, other seeds
+  modulation     AdaRMSNorm scale and shift per layer [H] ~ N(0, 0.1), bf16
+                 (stand-ins for a conditioning Dense layer's output)
 
 Seeds: evaluation residual 1000*c, its Y[0] 1000*c + 50; calibration batch b
 (1..4) 1000*c + b (and 1000*c + 50 + b for Y); layer l weights
-1000*c + 100 + 4*l + {0 gate, 1 up, 2 down, 3 norm}.
+1000*c + 100 + 4*l + {0 gate, 1 up, 2 down, 3 norm}; layer l modulation
+2^20 + 1000*c + 2*l + {0 scale, 1 shift}.
 """
 from __future__ import annotations
 
@@ -128,3 +131,9 @@ def layer_weights(cfg: FFNConfig, layer: int):
     wd = normal_bf16(layer_seed(cfg, layer, 2), (H, I), std=0.02)
     wn = normal_bf16(layer_seed(cfg, layer, 3), (H,), std=0.1, mean=1.0)
     return wg, wu, wd, wn
+
+
+def modulation(cfg: FFNConfig, layer: int, std: float = 0.1) -> Tuple[np.ndarray, np.ndarray]:
+    """(scale [H], shift [H]) bf16 bits for layer `layer`'s AdaRMSNorm."""
+    base = (1 << 20) + 1000 * cfg.index + 2 * layer
+    return normal_bf16(base, (cfg.H,), std=std), normal_bf16(base + 1, (cfg.H,), std=std)

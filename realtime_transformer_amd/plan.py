@@ -84,6 +84,19 @@ class FFNPlan:
     def hq_slot(self, l: int) -> torch.Tensor:
         return self._view(self.io.hq_slots + l * self.io.stride_hq, self.M * self.I).view(self.M, self.I)
 
+    def mod_slot(self, l: int) -> torch.Tensor:
+        """Layer l's AdaRMSNorm modulation [2][H] (scale, shift) as int16 bf16 bits."""
+        if not self.io.mod_slots:
+            raise RuntimeError("plan has no modulation slots (FRT_FLAG_ADA_NORM not set)")
+        return self._view(self.io.mod_slots + l * self.io.stride_mod, 2 * self.H * 2).view(torch.int16).view(2, self.H)
+
+    def set_modulation(self, l: int, scale: np.ndarray, shift: np.ndarray):
+        """Write layer l's scale and shift (numpy uint16 bf16 bits [H])."""
+        v = np.stack([np.asarray(scale, np.uint16), np.asarray(shift, np.uint16)])
+        with torch.cuda.stream(self.stream):
+            self.mod_slot(l).copy_(_to_dev_u16(v, self.device))
+        self.sync()
+
     def z(self) -> torch.Tensor:
         return self._view(self.io.z_out, self.M * self.H * 2).view(torch.int16).view(self.M, self.H)
 

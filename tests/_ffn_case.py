@@ -29,7 +29,7 @@ import numpy as np
 import torch
 
 import oracle
-from realtime_transformer_amd import datagen
+from realtime_transformer_amd import _abi, datagen
 from realtime_transformer_amd.configs import FFNConfig
 from realtime_transformer_amd.plan import FFNPlan, to_np_u16, to_np_u8
 
@@ -170,12 +170,18 @@ def run_case(cfg: FFNConfig, rows: Optional[Sequence[int]] = None, cal_rows: Opt
     try:
         weight_scales = []
         norm_w = {}
+        mods = {}
+        norm_fuse = bool(flags & _abi.FRT_FLAG_NORM_FUSE)
+        ada = bool(flags & _abi.FRT_FLAG_ADA_NORM)
 
         def provider(l):
             def get():
                 wg, wu, wd, wn = datagen.layer_weights(cfg, l)
                 plan.load_layer(l, wg, wu, wd, wn)
-                lw = oracle.LayerWeights.quantize(wg, wu, wd, wn)
+                mod = datagen.modulation(cfg, l) if ada else None
+                if ada:
+                    plan.set_modulation(l, *mod)
+                lw = oracle.LayerWeights.quantize(wg, wu, wd, wn, norm_fuse=norm_fuse, mod=mod)
                 names = ["up", "down"] if wg is None else ["gate", "up", "down"]
                 refs = [lw.qu, lw.qd] if wg is None else [lw.qg, lw.qu, lw.qd]
                 idx = [1, 2] if wg is None else [0, 1, 2]
@@ -184,7 +190,8 @@ def run_case(cfg: FFNConfig, rows: Optional[Sequence[int]] = None, cal_rows: Opt
                     nbad = int(np.count_nonzero(got != ref))
                     assert nbad == 0, "layer %d %s weight codes: %d mismatches" % (l, nm, nbad)
                 weight_scales.append((lw.s_g, lw.s_u, lw.s_d))
-                norm_w[l] = wn
+                norm_w[l] = lw.w_norm
+                mods[l] = lw.mod
                 if L > 4 and (l % 4 == 3 or l == L - 1):
                     log("[case %s] layers 0..%d quantised and compared (%.1fs)" % (cfg.name, l, time.time() - t0))
                 return lw
@@ -278,7 +285,7 @@ def run_case(cfg: FFNConfig, rows: Optional[Sequence[int]] = None, cal_rows: Opt
             nb = int(np.count_nonzero(r_g != orc.r[l + 1]))
             assert nb == 0, "layer %d residual: %d bf16 mismatches" % (l, nb)
             # oracle pre-rounding value of XQ for the boundary report
-            _, x_pre, _ = oracle.add_rmsnorm_quant(orc.r[l], orc.y[l], norm_w[l], cfg.eps, 1.0)
+            _, x_pre, _ = oracle.add_rmsnorm_quant(orc.r[l], orc.y[l], norm_w[l], cfg.eps, 1.0, mod=mods[l])
             inv_x = np.float32(np.float32(1.0) / np.float32(orc.s_x[l]))
             xs = code_stats(xq_g, orc.xq[l], (x_pre * inv_x).astype(np.float32))
             check_codes("layer %d XQ" % l, xs)

@@ -33,7 +33,8 @@ def test_library_is_in_tree():
 
 @pytest.mark.parametrize("bad", [
     dict(M=0), dict(L=0), dict(H=100), dict(I=200), dict(H=16384 + 128), dict(act=3),
-    dict(eps=0.0), dict(eps=float("nan")), dict(flags=8), dict(flags=13), dict(device=-1)])
+    dict(eps=0.0), dict(eps=float("nan")), dict(flags=32), dict(flags=45), dict(flags=16 | 8), dict(flags=16 | 2),
+    dict(device=-1)])
 def test_bad_descriptors_rejected(bad):
     kw = dict(M=16, H=256, I=1024, L=1, act=0, eps=1e-6, device=0, flags=0)
     kw.update(bad)

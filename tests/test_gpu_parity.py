@@ -9,6 +9,7 @@ large (rows are independent under static per-tensor scales).
 import numpy as np
 import pytest
 
+from realtime_transformer_amd import _abi
 from realtime_transformer_amd.configs import CONFIGS, FFNConfig, ACT_GEGLU_TANH, ACT_SWIGLU, ACT_GELU_TANH
 
 from _ffn_case import run_case, log
@@ -89,6 +90,47 @@ def test_small_shapes_fused_norm_split(spec):
     idx, M, H, I, L, act = spec
     cfg = FFNConfig(idx, "small_fusedsplit_%d" % idx, M, H, I, L, act)
     rep = run_case(cfg, flags=2)
+    log(str(rep))
+
+
+@pytest.mark.parametrize("spec", [SMALL[1], SMALL[3], (111, 200, 384, 640, 2, ACT_SWIGLU)],
+                         ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
+def test_small_shapes_norm_fuse(spec):
+    # RMSNorm weight folded into the gate/up codes, unit norm weight
+    idx, M, H, I, L, act = spec
+    cfg = FFNConfig(idx, "small_normfuse_%d" % idx, M, H, I, L, act)
+    rep = run_case(cfg, flags=_abi.FRT_FLAG_NORM_FUSE)
+    log(str(rep))
+
+
+@pytest.mark.parametrize("spec", [(109, 1, 256, 2048, 3, ACT_SWIGLU), (110, 4, 512, 2048, 2, ACT_GELU_TANH)],
+                         ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
+def test_small_shapes_norm_fuse_fused_decode(spec):
+    # the folded weights with the norm fused into the decode gate/up GEMV
+    idx, M, H, I, L, act = spec
+    cfg = FFNConfig(idx, "small_normfuse_fused_%d" % idx, M, H, I, L, act)
+    rep = run_case(cfg, flags=_abi.FRT_FLAG_NORM_FUSE | _abi.FRT_FLAG_FUSED_NORM)
+    log(str(rep))
+
+
+@pytest.mark.parametrize("spec", [SMALL[0], SMALL[2], SMALL[4], SMALL[6]],
+                         ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
+def test_small_shapes_ada_norm(spec):
+    # AdaRMSNorm: per-layer scale and shift written into the modulation slots
+    idx, M, H, I, L, act = spec
+    cfg = FFNConfig(idx, "small_ada_%d" % idx, M, H, I, L, act)
+    rep = run_case(cfg, flags=_abi.FRT_FLAG_ADA_NORM)
+    log(str(rep))
+
+
+def test_action_expert_m50_chain_ada_norm():
+    # the action expert's full 18-layer chain with AdaRMSNorm modulation
+    rep = run_case(CONFIGS[2], flags=_abi.FRT_FLAG_ADA_NORM)
+    log(str(rep))
+
+
+def test_action_expert_m50_chain_norm_fuse():
+    rep = run_case(CONFIGS[2], flags=_abi.FRT_FLAG_NORM_FUSE)
     log(str(rep))
 
 
