@@ -41,6 +41,10 @@ hipError_t launch_gemv_gateup(int, const uint8_t*, const uint8_t*, uint8_t*, int
                               float, float, float, hipStream_t);
 hipError_t launch_gemv_down(const uint8_t*, const uint8_t*, uint16_t*, float*, int, int, int, int, int,
                             bool, float, hipStream_t);
+hipError_t launch_gemv_gateup_mt(int, const uint8_t*, const uint8_t*, uint8_t*, int, int, int, int, float, float,
+                                 float, hipStream_t);
+hipError_t launch_gemv_down_mt(const uint8_t*, const uint8_t*, uint16_t*, float*, int, int, int, int, int, bool,
+                               float, hipStream_t);
 bool gemv_fused_supported(int, int, int);
 hipError_t launch_gemv_gateup_fused(int, const uint16_t*, const uint16_t*, const float*, int, float, uint16_t*,
                                     const uint16_t*, uint16_t*, uint8_t*, const uint8_t*, uint8_t*, int, int, int, int,
@@ -116,6 +120,7 @@ struct DeviceGuard {
 namespace {
 
 constexpr int kGemvMaxM = 16;
+constexpr int kGemvMtMaxM = 64;  // multi-tile GEMV up to here (FRT_GEMV_MT_MAX_M lowers it)
 constexpr int kMMMinM = 128;  // from here on the LDS-DMA GEMM takes the f16 path
 constexpr int kCUs = 256;  // MI355X compute units (workgroup rounds are counted against them)
 
@@ -168,6 +173,7 @@ struct Layout {
   int s_gu, s_dn;  // GEMV: waves per workgroup; GEMM: K splits of the down GEMM
   int k_dn;        // GEMV: K splits of the down GEMV (workgroups per 16 output columns)
   int split_dn;    // K splits of the down projection, either path (> 1: fp32 partials)
+  bool gemv_mt;    // 16 < M <= 64 on the multi-tile GEMVs
   int cfg_gu, cfg_dn;  // GEMM tile configurations
   bool mm_gu, mm_dn;   // GEMM runs on the LDS-DMA f16 kernel (k_mm) rather than k_gemm
 };
@@ -298,10 +304,16 @@ Layout make_layout(const frt_ffn_desc& d) {
   lo.mod = take((d.flags & FRT_FLAG_ADA_NORM) ? L * 2 * H * 2 : 256);
 
   size_t part = 0, words = 1;
-  if (d.M <= kGemvMaxM) {
+  lo.gemv_mt = d.M > kGemvMaxM && d.M <= std::min(kGemvMtMaxM, env_int("FRT_GEMV_MT_MAX_M", kGemvMtMaxM));
+  if (d.M <= kGemvMaxM || lo.gemv_mt) {
     lo.s_gu = gemv_waves((int)(I / 16), (int)(H / 128), "FRT_GEMV_WAVES_GATEUP", 6144);
     lo.k_dn = gemv_down_splits((int)(H / 16), (int)(I / 128));
     lo.s_dn = gemv_waves((int)(H / 16) * lo.k_dn, (int)(I / 128) / lo.k_dn, "FRT_GEMV_WAVES_DOWN", 4096);
+    if (lo.gemv_mt) {
+      // the multi-tile kernels take 4 or 8 waves (at least one per row tile)
+      lo.s_gu = lo.s_gu >= 8 ? 8 : 4;
+      lo.s_dn = lo.s_dn >= 8 ? 8 : 4;
+    }
     lo.split_dn = lo.k_dn;
     part = lo.k_dn > 1 ? (size_t)lo.k_dn * M * H * 4 : 4;
     words = 1;
@@ -692,6 +704,9 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
     else if (M <= kGemvMaxM)
       KERNEL_CHECK(launch_gemv_gateup(p->d.act, p->xq(l), p->wgu(l), p->hq(l), M, H, I, p->lo.s_gu,
                                       a_g, a_u, inv_h, s), "gemv_gateup");
+    else if (p->lo.gemv_mt)
+      KERNEL_CHECK(launch_gemv_gateup_mt(p->d.act, p->xq(l), p->wgu(l), p->hq(l), M, H, I, p->lo.s_gu,
+                                         a_g, a_u, inv_h, s), "gemv_gateup_mt");
     else if (p->lo.mm_gu)
       KERNEL_CHECK(launch_mm_gateup(p->d.act, p->lo.cfg_gu, p->fp8_gateup(), p->xq(l), p->wgu(l), p->hq(l), M, H,
                                     npk, a_g, a_u, inv_h, s), "mm_gateup");
@@ -703,6 +718,9 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
       KERNEL_CHECK(launch_gemv_down(p->hq(l), p->wd(l), p->y(l + 1), p->part(), M, I, H, p->lo.s_dn,
                                     p->lo.k_dn, p->fp8_down(),
                                     a_d, s), "gemv_down");
+    else if (p->lo.gemv_mt)
+      KERNEL_CHECK(launch_gemv_down_mt(p->hq(l), p->wd(l), p->y(l + 1), p->part(), M, I, H, p->lo.s_dn,
+                                       p->lo.k_dn, p->fp8_down(), a_d, s), "gemv_down_mt");
     else if (p->lo.mm_dn)
       KERNEL_CHECK(launch_mm_down(p->lo.cfg_dn, p->fp8_down(), p->hq(l), p->wd(l), p->y(l + 1), p->part(), M, I, H,
                                   p->lo.s_dn, a_d, s), "mm_down");

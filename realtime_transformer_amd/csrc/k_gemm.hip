@@ -698,6 +698,201 @@ static void gemv_gateup_w(int act, const uint8_t* xq, const uint8_t* w, uint8_t*
     hipLaunchKernelGGL((k_gemv_gateup<GU_GELU, W>), grid, block, 0, s, xq, w, hq, M, K, I, a_g, a_u, inv_h);
 }
 
+// ===========================================================================
+// Multi-tile GEMV (16 < M <= 64)
+// ===========================================================================
+//
+// The same weight stream as the GEMV above (one workgroup per 16 output
+// columns, waves splitting K, partials meeting in LDS in wave order), with
+// the M rows taken as MT = ceil(M / 16) activation tiles of 16: each weight
+// fragment is loaded and converted to f16 once and multiplied into all MT
+// tiles.  At these M the weights are still read exactly once per launch (a
+// 128-row GEMM tile would waste most of its rows and leave most CUs idle);
+// the activation rows (M x K bytes) come from L2.  After the reduction,
+// wave t finishes tile t (t < MT).
+
+// lane's 32 bytes of K block kb of weight rows as four f16 operands
+__device__ __forceinline__ void cvt_w32(const uint32_t w[8], v8h o[4]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) o[t] = e4m3x8_to_f16(w[2 * t], w[2 * t + 1]);
+}
+
+template <int ACT, int W, int MT>
+__global__ __launch_bounds__(W * 64) void k_gemv_gateup_mt(const uint8_t* __restrict__ xq,
+                                                           const uint8_t* __restrict__ w,
+                                                           uint8_t* __restrict__ hq, int M, int K,
+                                                           int I, float alpha_g, float alpha_u,
+                                                           float inv_h) {
+  constexpr bool GATED = ACT != GU_GELU;
+  constexpr int NACC = GATED ? 2 : 1;
+  static_assert(W >= MT, "one wave per tile finishes the epilogue");
+  __shared__ v4f red[W][MT][NACC][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int p = blockIdx.x;  // column group
+  const int KB = K >> 7;
+  const int kb0 = wave * KB / W, kb1 = (wave + 1) * KB / W;
+  const int row = lane & 15, q = lane >> 4;
+  const uint8_t* wg = w + (size_t)(GATED ? 2 * p : 0) * KB * 2048 + lane * 16;
+  const uint8_t* wu = w + (size_t)(GATED ? 2 * p + 1 : p) * KB * 2048 + lane * 16;
+  const uint8_t* xr[MT];
+  bool has[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    has[t] = 16 * t + row < M;
+    xr[t] = xq + (size_t)(has[t] ? 16 * t + row : 0) * K + q * 32;
+  }
+
+  v4f accg[MT], accu[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) accg[t] = accu[t] = v4f{0, 0, 0, 0};
+
+  for (int kb = kb0; kb < kb1; kb += 2) {
+    const bool two = kb + 1 < kb1;
+    uint32_t u0[8], u1[8], g0[8], g1[8], x0[MT][8], x1[MT][8];
+    load_w32(wu, kb, u0);
+    if (GATED) load_w32(wg, kb, g0);
+    if (two) {
+      load_w32(wu, kb + 1, u1);
+      if (GATED) load_w32(wg, kb + 1, g1);
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      load_x32(xr[t], has[t], kb, x0[t]);
+      load_x32(xr[t], has[t] && two, kb + (two ? 1 : 0), x1[t]);
+    }
+    v8h uh[4], gh[4];
+    cvt_w32(u0, uh);
+    if (GATED) cvt_w32(g0, gh);
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const v8h xh = e4m3x8_to_f16(x0[t][2 * s4], x0[t][2 * s4 + 1]);
+        accu[t] = mfma_f16(xh, uh[s4], accu[t]);
+        if (GATED) accg[t] = mfma_f16(xh, gh[s4], accg[t]);
+      }
+    if (two) {
+      cvt_w32(u1, uh);
+      if (GATED) cvt_w32(g1, gh);
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const v8h xh = e4m3x8_to_f16(x1[t][2 * s4], x1[t][2 * s4 + 1]);
+          accu[t] = mfma_f16(xh, uh[s4], accu[t]);
+          if (GATED) accg[t] = mfma_f16(xh, gh[s4], accg[t]);
+        }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    red[wave][t][0][lane] = accu[t];
+    if (GATED) red[wave][t][NACC - 1][lane] = accg[t];
+  }
+  __syncthreads();
+  if (wave >= MT) return;
+  const int t = wave;
+  v4f au = red[0][t][0][lane], ag = red[0][t][NACC - 1][lane];
+#pragma unroll
+  for (int v = 1; v < W; ++v) {
+    au += red[v][t][0][lane];
+    if (GATED) ag += red[v][t][NACC - 1][lane];
+  }
+  // lane holds rows m = 16t + 4q + r of column 16p + row
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = 16 * t + 4 * q + r;
+    if (m < M) {
+      const float h = gated_h<ACT>(ag[r] * alpha_g, au[r] * alpha_u);
+      hq[(size_t)m * I + p * 16 + row] = (uint8_t)e4m3x1(h * inv_h);
+    }
+  }
+}
+
+// Down projection, multi-tile form: K split over gridDim.y workgroups per 16
+// output columns (fp32 partials [split][M][N] when > 1, as k_gemv_down).
+template <int W, bool FP8, int MT>
+__global__ __launch_bounds__(W * 64) void k_gemv_down_mt(const uint8_t* __restrict__ hq,
+                                                         const uint8_t* __restrict__ w,
+                                                         uint16_t* __restrict__ y, float* __restrict__ part,
+                                                         int M, int K, int N, float alpha_d) {
+  static_assert(W >= MT, "one wave per tile finishes the epilogue");
+  __shared__ v4f red[W][MT][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int p = blockIdx.x;
+  const int KB = K >> 7;
+  const int S = gridDim.y, sp = blockIdx.y;
+  const int ks0 = sp * KB / S, ks1 = (sp + 1) * KB / S;
+  const int kb0 = ks0 + wave * (ks1 - ks0) / W, kb1 = ks0 + (wave + 1) * (ks1 - ks0) / W;
+  const int row = lane & 15, q = lane >> 4;
+  const uint8_t* wp = w + (size_t)p * KB * 2048 + lane * 16;
+  const uint8_t* xr[MT];
+  bool has[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    has[t] = 16 * t + row < M;
+    xr[t] = hq + (size_t)(has[t] ? 16 * t + row : 0) * K + q * 32;
+  }
+  v4f acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = v4f{0, 0, 0, 0};
+
+  for (int kb = kb0; kb < kb1; kb += 2) {
+    const bool two = kb + 1 < kb1;
+    uint32_t w0[8], w1[8], x0[MT][8], x1[MT][8];
+    load_w32(wp, kb, w0);
+    if (two) load_w32(wp, kb + 1, w1);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      load_x32(xr[t], has[t], kb, x0[t]);
+      load_x32(xr[t], has[t] && two, kb + (two ? 1 : 0), x1[t]);
+    }
+    if (FP8) {
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[t] = mfma_step<true>(x0[t], w0, acc[t]);
+      if (two) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[t] = mfma_step<true>(x1[t], w1, acc[t]);
+      }
+    } else {
+      v8h wh[4];
+      cvt_w32(w0, wh);
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+          acc[t] = mfma_f16(e4m3x8_to_f16(x0[t][2 * s4], x0[t][2 * s4 + 1]), wh[s4], acc[t]);
+      if (two) {
+        cvt_w32(w1, wh);
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4)
+            acc[t] = mfma_f16(e4m3x8_to_f16(x1[t][2 * s4], x1[t][2 * s4 + 1]), wh[s4], acc[t]);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < MT; ++t) red[wave][t][lane] = acc[t];
+  __syncthreads();
+  if (wave >= MT) return;
+  const int t = wave;
+  v4f a = red[0][t][lane];
+#pragma unroll
+  for (int v = 1; v < W; ++v) a += red[v][t][lane];
+  float* ps = part + (size_t)sp * M * N;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = 16 * t + 4 * q + r;
+    if (m < M) {
+      if (S == 1)
+        y[(size_t)m * N + p * 16 + row] = (uint16_t)f32_to_bf16(a[r] * alpha_d);
+      else
+        ps[(size_t)m * N + p * 16 + row] = a[r];
+    }
+  }
+}
+
 // waves per workgroup W: 1, 2, 4, 8 or 16 (at most the number of K blocks)
 hipError_t launch_gemv_gateup(int act, const uint8_t* xq, const uint8_t* w, uint8_t* hq, int M,
                               int K, int I, int W, float alpha_g, float alpha_u, float inv_h,
@@ -813,6 +1008,65 @@ hipError_t launch_gemv_down(const uint8_t* hq, const uint8_t* w, uint16_t* y, fl
                      : gemv_down_t<true, 16>(hq, w, y, part, M, K, N, W, S, alpha_d, s);
   return cols == 8 ? gemv_down_t<false, 8>(hq, w, y, part, M, K, N, W, S, alpha_d, s)
                    : gemv_down_t<false, 16>(hq, w, y, part, M, K, N, W, S, alpha_d, s);
+}
+
+// Multi-tile GEMV launchers (16 < M <= 64): W in {4, 8} waves (at least MT).
+template <int ACT, int W, int MT>
+static void gemv_gateup_mt_t(const uint8_t* xq, const uint8_t* w, uint8_t* hq, int M, int K, int I, float a_g,
+                             float a_u, float inv_h, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemv_gateup_mt<ACT, W, MT>), dim3(I / 16), dim3(W * 64), 0, s, xq, w, hq, M, K, I, a_g,
+                     a_u, inv_h);
+}
+
+template <int ACT, int W>
+static hipError_t gemv_gateup_mt_w(const uint8_t* xq, const uint8_t* w, uint8_t* hq, int M, int K, int I,
+                                   float a_g, float a_u, float inv_h, hipStream_t s) {
+  switch ((M + 15) / 16) {
+    case 2: gemv_gateup_mt_t<ACT, W, 2>(xq, w, hq, M, K, I, a_g, a_u, inv_h, s); break;
+    case 3: gemv_gateup_mt_t<ACT, W, 3>(xq, w, hq, M, K, I, a_g, a_u, inv_h, s); break;
+    case 4: gemv_gateup_mt_t<ACT, W, 4>(xq, w, hq, M, K, I, a_g, a_u, inv_h, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int ACT>
+static hipError_t gemv_gateup_mt_act(int W, const uint8_t* xq, const uint8_t* w, uint8_t* hq, int M, int K,
+                                     int I, float a_g, float a_u, float inv_h, hipStream_t s) {
+  if (W == 4) return gemv_gateup_mt_w<ACT, 4>(xq, w, hq, M, K, I, a_g, a_u, inv_h, s);
+  if (W == 8) return gemv_gateup_mt_w<ACT, 8>(xq, w, hq, M, K, I, a_g, a_u, inv_h, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemv_gateup_mt(int act, const uint8_t* xq, const uint8_t* w, uint8_t* hq, int M, int K, int I,
+                                 int W, float alpha_g, float alpha_u, float inv_h, hipStream_t s) {
+  if (M <= 16 || M > 64 || (K >> 7) < 1) return hipErrorInvalidValue;
+  if (act == GU_GEGLU) return gemv_gateup_mt_act<GU_GEGLU>(W, xq, w, hq, M, K, I, alpha_g, alpha_u, inv_h, s);
+  if (act == GU_SWIGLU) return gemv_gateup_mt_act<GU_SWIGLU>(W, xq, w, hq, M, K, I, alpha_g, alpha_u, inv_h, s);
+  return gemv_gateup_mt_act<GU_GELU>(W, xq, w, hq, M, K, I, alpha_g, alpha_u, inv_h, s);
+}
+
+template <int W, bool FP8>
+static hipError_t gemv_down_mt_w(const uint8_t* hq, const uint8_t* w, uint16_t* y, float* part, int M, int K,
+                                 int N, int S, float alpha_d, hipStream_t s) {
+  dim3 grid(N / 16, S), block(W * 64);
+  switch ((M + 15) / 16) {
+    case 2: hipLaunchKernelGGL((k_gemv_down_mt<W, FP8, 2>), grid, block, 0, s, hq, w, y, part, M, K, N, alpha_d); break;
+    case 3: hipLaunchKernelGGL((k_gemv_down_mt<W, FP8, 3>), grid, block, 0, s, hq, w, y, part, M, K, N, alpha_d); break;
+    case 4: hipLaunchKernelGGL((k_gemv_down_mt<W, FP8, 4>), grid, block, 0, s, hq, w, y, part, M, K, N, alpha_d); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_down_mt(const uint8_t* hq, const uint8_t* w, uint16_t* y, float* part, int M, int K,
+                               int N, int W, int S, bool fp8, float alpha_d, hipStream_t s) {
+  if (M <= 16 || M > 64 || S < 1 || S > (K >> 7)) return hipErrorInvalidValue;
+  if (W == 4) return fp8 ? gemv_down_mt_w<4, true>(hq, w, y, part, M, K, N, S, alpha_d, s)
+                         : gemv_down_mt_w<4, false>(hq, w, y, part, M, K, N, S, alpha_d, s);
+  if (W == 8) return fp8 ? gemv_down_mt_w<8, true>(hq, w, y, part, M, K, N, S, alpha_d, s)
+                         : gemv_down_mt_w<8, false>(hq, w, y, part, M, K, N, S, alpha_d, s);
+  return hipErrorInvalidValue;
 }
 
 bool gemm_config_ok(int cfg, bool fp8) { return cfg >= 0 && cfg < kGemmConfigs && (fp8 || cfg != 6); }

@@ -25,6 +25,12 @@ SMALL = [
     (105, 130, 384, 640, 2, ACT_SWIGLU),
     (106, 300, 256, 512, 3, ACT_GELU_TANH),
     (5, 40, 256, 512, 2, ACT_GELU_TANH),  # index 5: +-20 outliers exercise saturation
+    # multi-tile GEMVs (16 < M <= 64): 2, 3 and 4 row tiles, a split down GEMV
+    (113, 64, 256, 512, 2, ACT_SWIGLU),
+    (114, 33, 384, 640, 2, ACT_GELU_TANH),
+    (116, 48, 256, 2048, 2, ACT_GEGLU_TANH),
+    # the LDS-staged GEMM between the GEMVs and the prefill GEMM
+    (115, 100, 256, 384, 2, ACT_GEGLU_TANH),
 ]
 
 
