@@ -39,6 +39,7 @@ _c_u8p = ctypes.POINTER(ctypes.c_uint8)
 _c_u16p = ctypes.POINTER(ctypes.c_uint16)
 _c_f32p = ctypes.POINTER(ctypes.c_float)
 _c_f64p = ctypes.POINTER(ctypes.c_double)
+_c_i32p = ctypes.POINTER(ctypes.c_int32)
 
 
 def build(force: bool = False) -> str:
@@ -105,6 +106,11 @@ def lib():
         L.orc_down.argtypes = [ctypes.c_int] * 3 + [_c_u8p, _c_u8p, ctypes.c_float, _c_u16p,
                                                     ctypes.c_int]
         L.orc_block.restype = ctypes.c_int
+        L.orc_rope_table.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double, _c_f32p]
+        L.orc_rope_table.restype = None
+        L.orc_qkv_epilogue.argtypes = ([ctypes.c_int] * 4 + [_c_f32p, ctypes.c_float, _c_i32p, _c_f32p,
+                                        ctypes.c_int, _c_u16p, _c_u16p, _c_u16p])
+        L.orc_qkv_epilogue.restype = ctypes.c_int
         L.orc_block.argtypes = ([ctypes.c_int] * 4 + [ctypes.c_float, _c_u16p, _c_u16p, _c_u16p, _c_u16p,
                                                      _c_u16p, _c_u8p, _c_u8p, _c_u8p] + [ctypes.c_float] * 5
                                 + [_c_u16p, _c_u8p, _c_u8p, _c_u16p, ctypes.c_int])
@@ -457,3 +463,86 @@ def calibrate_and_run(layers: Iterable[Callable[[], LayerWeights]], act: int, ep
         if post_layer is not None:
             post_layer(li, lw, s_x, s_h)
     return res
+
+
+# ---------------------------------------------------------------------------
+# Attention input: fused QKV projection + split + rotary embedding
+# (FlashRT architecture doc, "Kernel library": the "qkv split + RoPE" fusion;
+# itsolotime article section 5.2: the FusedQKV weight of the Pi0/Pi0.5 specs)
+# ---------------------------------------------------------------------------
+
+def rope_table(P: int, hd: int, base: float) -> np.ndarray:
+    """[P, hd/2, 2] float32 (cos, sin) of p * base^(-2i/hd), fp64 then rounded."""
+    assert hd % 2 == 0 and P >= 1
+    out = np.empty((P, hd // 2, 2), np.float32)
+    lib().orc_rope_table(int(P), int(hd), float(base), _p(out, _c_f32p))
+    return out
+
+
+def qkv_epilogue(A, alpha: float, nq: int, nkv: int, hd: int, pos, table):
+    """fp32 GEMM result [M, (nq+2nkv)*hd] -> bf16 (Q [M,nq,hd], K [M,nkv,hd], V [M,nkv,hd])."""
+    A = np.ascontiguousarray(A, np.float32)
+    M = A.shape[0]
+    assert A.shape[1] == (nq + 2 * nkv) * hd
+    pos = np.ascontiguousarray(pos, np.int32)
+    table = np.ascontiguousarray(table, np.float32)
+    assert table.ndim == 3 and table.shape[1:] == (hd // 2, 2) and pos.shape == (M,)
+    q = np.empty((M, nq, hd), np.uint16)
+    k = np.empty((M, nkv, hd), np.uint16)
+    v = np.empty((M, nkv, hd), np.uint16)
+    rc = lib().orc_qkv_epilogue(M, nq, nkv, hd, _p(A, _c_f32p), float(alpha), _p(pos, _c_i32p),
+                                _p(table, _c_f32p), table.shape[0], _p(q, _c_u16p), _p(k, _c_u16p), _p(v, _c_u16p))
+    if rc:
+        raise ValueError("position outside the rotary table")
+    return q, k, v
+
+
+@dataclass
+class QkvWeights:
+    """One layer's fused QKV projection: codes [(nq+2nkv)*hd, H] over the rows
+    [Wq; Wk; Wv] with one per-tensor scale, the norm weight (unit when folded)
+    and optional AdaRMSNorm modulation."""
+    codes: np.ndarray
+    s_w: float
+    w_norm: np.ndarray
+    nq: int
+    nkv: int
+    hd: int
+    mod: Optional[tuple] = None
+
+    @staticmethod
+    def quantize(wq, wk, wv, w_norm, hd: int, norm_fuse: bool = False, mod=None) -> "QkvWeights":
+        wq, wk, wv = _u16(wq), _u16(wk), _u16(wv)
+        assert wq.shape[0] % hd == 0 and wk.shape == wv.shape and wk.shape[0] % hd == 0
+        fused = np.ascontiguousarray(np.concatenate([wq, wk, wv], axis=0))
+        w_norm = _u16(w_norm)
+        if norm_fuse:
+            codes, s = quant_tensor_fold(fused, w_norm)
+            w_norm = np.full(w_norm.shape, ONES_BF16, np.uint16)
+        else:
+            codes, s = quant_tensor(fused)
+        mod = None if mod is None else (_u16(mod[0]), _u16(mod[1]))
+        return QkvWeights(codes, s, w_norm, wq.shape[0] // hd, wk.shape[0] // hd, hd, mod)
+
+
+def qkv_block(r_prev, y_prev, qw: QkvWeights, eps: float, s_x: float, pos, table,
+              nthreads: Optional[int] = None):
+    """K1 then the fused QKV GEMM with the split + RoPE epilogue
+    -> (r_out, xq, q, k, v)."""
+    inv_x = np.float32(np.float32(1.0) / np.float32(s_x))
+    r_out, _, xq = add_rmsnorm_quant(r_prev, y_prev, qw.w_norm, eps, float(inv_x), nthreads, mod=qw.mod)
+    A = gemm_e4m3(xq, qw.codes, nthreads)
+    alpha = np.float32(np.float32(s_x) * np.float32(qw.s_w))
+    q, k, v = qkv_epilogue(A, float(alpha), qw.nq, qw.nkv, qw.hd, pos, table)
+    return r_out, xq, q, k, v
+
+
+def qkv_calibrate(batches, qw: QkvWeights, eps: float) -> float:
+    """Static activation scale of the QKV GEMM input: amax of the normalised
+    rows over the calibration batches (the measurement pass), then
+    f32(amax / 448)."""
+    amax = 0.0
+    for r, y in batches:
+        _, x, _ = add_rmsnorm_quant(r, y, qw.w_norm, eps, 1.0, mod=qw.mod)
+        amax = max(amax, float(np.max(np.abs(x))))
+    return scale_from_amax(amax)

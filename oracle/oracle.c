@@ -16,7 +16,9 @@
  *     input in a measurement pass, then alpha = act_scale * weight_scale
  *     baked as host scalars;
  *   - FlashRT architecture doc, component "Kernel library": the fused
- *     residual + norm + quant kernel.
+ *     residual + norm + quant kernel, and the "qkv split + RoPE" fusion that
+ *     follows the fused QKV projection on the attention side (the FusedQKV
+ *     weight of the Pi0/Pi0.5 specs, itsolotime article section 5.2).
  * Every rounding point the pages leave open is fixed here: OCP E4M3FN with
  * saturation at +-448, round-to-nearest-even everywhere, the RMSNorm mean
  * square summed in fp64 with 1/rms rounded once to fp32, FP8 products summed
@@ -571,4 +573,63 @@ int orc_block_measure(int M, int H, int I, int act, float eps, const uint16_t *r
   free(sg);
   free(sd);
   return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention input: fused QKV projection, split and rotary embedding.        */
+/* FlashRT architecture doc, "Kernel library" ("qkv split + RoPE" fusion);  */
+/* itsolotime article section 5.2 (FusedQKV: the q, k and v projections of  */
+/* a layer fused into one quantised weight, optionally with the norm weight */
+/* folded in).  The rotation is the half-split form: dimension i of a head  */
+/* is paired with dimension i + hd/2.                                        */
+/*                                                                          */
+/* Rotary table, entry (p, i) for i < hd/2:                                 */
+/*   theta_i = base^(-2i/hd),  cos/sin of p * theta_i in fp64, each rounded */
+/*   once to fp32; stored as [P][hd/2][2] = (cos, sin).                     */
+/* ------------------------------------------------------------------------ */
+
+void orc_rope_table(int P, int hd, double base, float *cos_sin) {
+  const int half = hd / 2;
+  for (int i = 0; i < half; ++i) {
+    const double theta = pow(base, -(2.0 * (double)i) / (double)hd);
+    for (int p = 0; p < P; ++p) {
+      const double a = (double)p * theta;
+      cos_sin[((int64_t)p * half + i) * 2] = (float)cos(a);
+      cos_sin[((int64_t)p * half + i) * 2 + 1] = (float)sin(a);
+    }
+  }
+}
+
+/* Split and rotate one row block.  A is the fp32 GEMM result [M][N] with  */
+/* N = (nq + 2*nkv) * hd over the fused rows [q heads; k heads; v heads].  */
+/*   v_n = f32(A[m][n] * alpha)                                            */
+/* Q and K heads, d < hd/2, (c, s) = table[pos[m]][d]:                     */
+/*   out[d]        = bf16( f32( f32(v_d * c) - f32(v_{d+hd/2} * s) ) )      */
+/*   out[d + hd/2] = bf16( f32( f32(v_{d+hd/2} * c) + f32(v_d * s) ) )      */
+/* V heads: out = bf16(v).  Outputs [M][heads][hd].  Returns -1 when a     */
+/* position lies outside the table.                                        */
+int orc_qkv_epilogue(int M, int nq, int nkv, int hd, const float *A, float alpha, const int32_t *pos,
+                     const float *table, int P, uint16_t *q, uint16_t *k, uint16_t *v) {
+  const int half = hd / 2;
+  const int64_t N = (int64_t)(nq + 2 * nkv) * hd;
+  for (int m = 0; m < M; ++m) {
+    const int p = pos[m];
+    if (p < 0 || p >= P) return -1;
+    for (int head = 0; head < nq + nkv; ++head) {
+      const float *a = A + (int64_t)m * N + (int64_t)head * hd;
+      uint16_t *o = head < nq ? q + ((int64_t)m * nq + head) * hd : k + ((int64_t)m * nkv + (head - nq)) * hd;
+      for (int d = 0; d < half; ++d) {
+        const float x1 = a[d] * alpha;
+        const float x2 = a[d + half] * alpha;
+        const float c = table[((int64_t)p * half + d) * 2];
+        const float sn = table[((int64_t)p * half + d) * 2 + 1];
+        const float x1c = x1 * c, x2s = x2 * sn, x2c = x2 * c, x1s = x1 * sn;
+        o[d] = orc_bf16_round(x1c - x2s);
+        o[d + half] = orc_bf16_round(x2c + x1s);
+      }
+    }
+    const float *av = A + (int64_t)m * N + (int64_t)(nq + nkv) * hd;
+    for (int64_t j = 0; j < (int64_t)nkv * hd; ++j) v[(int64_t)m * nkv * hd + j] = orc_bf16_round(av[j] * alpha);
+  }
+  return 0;
 }
