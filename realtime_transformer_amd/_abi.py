@@ -41,6 +41,11 @@ EXPORTED = [
     "frt_ffn_io_get", "frt_ffn_forward_range", "frt_ffn_forward", "frt_graph_capture",
     "frt_graph_replay", "frt_ffn_forward_profiled", "frt_ffn_time_kernel", "frt_e4m3_encode_f32",
     "frt_last_error",
+    # attention input (include/frt_qkv.h)
+    "frt_qkv_workspace_size", "frt_qkv_plan_create", "frt_qkv_plan_destroy", "frt_qkv_quant_weights",
+    "frt_qkv_export_weight_codes", "frt_qkv_calibrate", "frt_qkv_get_scales", "frt_qkv_set_act_scale",
+    "frt_qkv_set_positions", "frt_qkv_io_get", "frt_qkv_forward", "frt_qkv_time_kernel",
+    "frt_qkv_graph_capture", "frt_qkv_graph_replay",
 ]
 
 
@@ -62,6 +67,17 @@ class frt_ffn_io(ctypes.Structure):
                 ("z_out", ctypes.c_void_p), ("stride_rh", ctypes.c_size_t),
                 ("stride_xq", ctypes.c_size_t), ("stride_hq", ctypes.c_size_t),
                 ("mod_slots", ctypes.c_void_p), ("stride_mod", ctypes.c_size_t)]
+
+
+class frt_qkv_desc(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int32), ("H", ctypes.c_int32), ("nq", ctypes.c_int32),
+                ("nkv", ctypes.c_int32), ("hd", ctypes.c_int32), ("max_pos", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("rope_base", ctypes.c_float), ("device", ctypes.c_int32),
+                ("flags", ctypes.c_uint32)]
+
+
+class frt_qkv_io(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("r_in", "y_in", "pos", "mod", "r_out", "xq", "q", "k", "v", "rope")]
 
 
 _lib = None
@@ -99,6 +115,20 @@ def load(build_if_missing: bool = True):
         "frt_ffn_forward_profiled": [vp, vp, ctypes.POINTER(ctypes.c_float)],
         "frt_ffn_time_kernel": [vp, i32, i32, vp, ctypes.POINTER(ctypes.c_float)],
         "frt_e4m3_encode_f32": [vp, vp, ctypes.c_int64, vp],
+        "frt_qkv_workspace_size": [ctypes.POINTER(frt_qkv_desc), ctypes.POINTER(sz)],
+        "frt_qkv_plan_create": [ctypes.POINTER(frt_qkv_desc), vp, sz, ctypes.POINTER(vp)],
+        "frt_qkv_plan_destroy": [vp],
+        "frt_qkv_quant_weights": [vp, vp, vp, vp, vp, vp],
+        "frt_qkv_export_weight_codes": [vp, vp],
+        "frt_qkv_calibrate": [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i32, vp],
+        "frt_qkv_get_scales": [vp, ctypes.POINTER(ctypes.c_float)],
+        "frt_qkv_set_act_scale": [vp, ctypes.c_float],
+        "frt_qkv_set_positions": [vp, ctypes.POINTER(ctypes.c_int32), vp],
+        "frt_qkv_io_get": [vp, ctypes.POINTER(frt_qkv_io)],
+        "frt_qkv_forward": [vp, vp],
+        "frt_qkv_time_kernel": [vp, i32, i32, vp, ctypes.POINTER(ctypes.c_float)],
+        "frt_qkv_graph_capture": [vp, vp],
+        "frt_qkv_graph_replay": [vp, vp],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -207,3 +237,85 @@ def frt_e4m3_encode_f32(d_in: int, d_out: int, n: int, stream: int) -> None:
 
 def frt_last_error() -> str:
     return load().frt_last_error().decode(errors="replace")
+
+
+# ---------------------------------------------------------------------------
+# attention input (include/frt_qkv.h)
+# ---------------------------------------------------------------------------
+
+def make_qkv_desc(M: int, H: int, nq: int, nkv: int, hd: int, max_pos: int, eps: float = 1e-6,
+                  rope_base: float = 10000.0, device: int = 0, flags: int = 0) -> frt_qkv_desc:
+    return frt_qkv_desc(M, H, nq, nkv, hd, max_pos, eps, rope_base, device, flags)
+
+
+def frt_qkv_workspace_size(desc: frt_qkv_desc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().frt_qkv_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def frt_qkv_plan_create(desc: frt_qkv_desc, d_workspace: int, nbytes: int) -> int:
+    out = ctypes.c_void_p(None)
+    _check(load().frt_qkv_plan_create(ctypes.byref(desc), ctypes.c_void_p(d_workspace), nbytes, ctypes.byref(out)))
+    return out.value
+
+
+def frt_qkv_plan_destroy(plan: Optional[int]) -> None:
+    _check(load().frt_qkv_plan_destroy(ctypes.c_void_p(plan)))
+
+
+def frt_qkv_quant_weights(plan: int, d_wq: int, d_wk: int, d_wv: int, d_norm_w: int, stream: int) -> None:
+    _check(load().frt_qkv_quant_weights(plan, d_wq, d_wk, d_wv, d_norm_w, stream))
+
+
+def frt_qkv_export_weight_codes(plan: int, rows: int, cols: int) -> np.ndarray:
+    out = np.empty((rows, cols), dtype=np.uint8)
+    _check(load().frt_qkv_export_weight_codes(plan, out.ctypes.data_as(ctypes.c_void_p)))
+    return out
+
+
+def frt_qkv_calibrate(plan: int, d_r_batches: Sequence[int], d_y_batches: Optional[Sequence[int]], rows: int,
+                      stream: int) -> None:
+    n = len(d_r_batches)
+    rb = (ctypes.c_void_p * n)(*d_r_batches)
+    yb = None if d_y_batches is None else (ctypes.c_void_p * n)(*d_y_batches)
+    _check(load().frt_qkv_calibrate(plan, rb, yb, n, rows, stream))
+
+
+def frt_qkv_get_scales(plan: int) -> np.ndarray:
+    out = np.zeros(2, dtype=np.float32)
+    _check(load().frt_qkv_get_scales(plan, out.ctypes.data_as(ctypes.POINTER(ctypes.c_float))))
+    return out
+
+
+def frt_qkv_set_act_scale(plan: int, s_x: float) -> None:
+    _check(load().frt_qkv_set_act_scale(plan, float(s_x)))
+
+
+def frt_qkv_set_positions(plan: int, pos, stream: int) -> None:
+    a = np.ascontiguousarray(np.asarray(pos, dtype=np.int32))
+    _check(load().frt_qkv_set_positions(plan, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), stream))
+
+
+def frt_qkv_io_get(plan: int) -> frt_qkv_io:
+    io = frt_qkv_io()
+    _check(load().frt_qkv_io_get(plan, ctypes.byref(io)))
+    return io
+
+
+def frt_qkv_forward(plan: int, stream: int) -> None:
+    _check(load().frt_qkv_forward(plan, stream))
+
+
+def frt_qkv_time_kernel(plan: int, which: int, reps: int, stream: int) -> float:
+    us = ctypes.c_float(0.0)
+    _check(load().frt_qkv_time_kernel(plan, which, reps, stream, ctypes.byref(us)))
+    return us.value
+
+
+def frt_qkv_graph_capture(plan: int, stream: int) -> None:
+    _check(load().frt_qkv_graph_capture(plan, stream))
+
+
+def frt_qkv_graph_replay(plan: int, stream: int) -> None:
+    _check(load().frt_qkv_graph_replay(plan, stream))

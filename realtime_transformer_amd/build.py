@@ -1,21 +1,27 @@
 """Build libfrt.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
 Flags: -ffp-contract=off keeps every rounding point as written in the
-kernels; packed fp32 instructions are disabled for all device code.
+kernels; packed fp32 instructions are disabled for all device code.  Each
+source compiles to its own object (in parallel) under _build/, then one link
+makes the shared library.
 """
 from __future__ import annotations
 
 import os
 import subprocess
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfrt.so")
-SOURCES = ["frt_ffn.hip", "k_norm.hip", "k_quant.hip", "k_gemm.hip", "k_mm.hip", "k_calib.hip"]
-HEADERS = ["frt_device.h", os.path.join("..", "..", "include", "frt_ffn.h")]
+BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
+SOURCES = ["frt_ffn.hip", "frt_qkv.hip", "k_norm.hip", "k_quant.hip", "k_gemm.hip", "k_mm.hip", "k_calib.hip",
+           "k_qkv.hip"]
+HEADERS = ["frt_device.h", "frt_host.h", "frt_qkv_dev.h", os.path.join("..", "..", "include", "frt_ffn.h"),
+           os.path.join("..", "..", "include", "frt_qkv.h")]
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
@@ -35,17 +41,34 @@ def stale() -> bool:
     return any(os.path.getmtime(d) > t for d in deps if os.path.exists(d))
 
 
+def _compile(src: str) -> tuple:
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-c", "-o", obj, os.path.join(CSRC, src)]
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    return obj, res.returncode, res.stdout
+
+
 def build(force: bool = True, verbose: bool = False) -> str:
     """Compile every source into libfrt.so (always when force, else only if stale)."""
     if not force and not stale():
         return LIB
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    try:
+        workers = max(1, min(len(SOURCES), len(os.sched_getaffinity(0)), 8))
+    except AttributeError:  # pragma: no cover
+        workers = 4
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        results = list(ex.map(_compile, SOURCES))
+    bad = [(o, out) for o, rc, out in results if rc != 0]
+    if bad:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(out for _, out in bad))
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [o for o, _, _ in results]
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + res.stdout)
+        raise RuntimeError("hipcc link failed:\n" + res.stdout)
     if verbose:
-        print(res.stdout)
+        print("\n".join(out for _, _, out in results) + res.stdout)
     os.replace(tmp, LIB)
     return LIB
 

@@ -74,3 +74,51 @@ CONFIGS = {
 }
 
 BY_NAME = {c.name: c for c in CONFIGS.values()}
+
+
+# ---------------------------------------------------------------------------
+# Attention-input workloads (K1 + fused QKV projection + split + rotary
+# embedding), one layer each.  Head layouts: the Pi0 / Pi0.5 specs' FusedQKV
+# item interleaves 8 query heads and 1 key head (itsolotime article, section
+# 5.2), read here as 8 query heads and 1 key/value head of dimension 256 for
+# the action expert and the VLM prefix; the decode shape takes a grouped
+# layout of 64 query and 8 key/value heads of dimension 128 at the decode
+# chain's hidden size.  The residual inputs are those of the FFN workload of
+# the same model (same seed index).
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class QkvConfig:
+    index: int
+    name: str
+    M: int
+    H: int
+    nq: int
+    nkv: int
+    hd: int
+    pos0: int          # rotary position of row 0 (row m takes pos0 + m)
+    max_pos: int       # rotary table rows
+    rope_base: float
+    eps: float = 1e-6
+    L: int = 1         # one layer (the generator then also draws a nonzero Y)
+
+    @property
+    def N(self) -> int:
+        return (self.nq + 2 * self.nkv) * self.hd
+
+    def k1_bytes(self) -> int:
+        return 7 * self.M * self.H + 2 * self.H
+
+    def qkv_bytes(self) -> int:
+        # weights once, XQ, the positions, the table rows used, bf16 Q/K/V
+        return self.N * self.H + self.M * self.H + 4 * self.M + self.M * self.hd * 4 + 2 * self.M * self.N
+
+    def qkv_flops(self) -> int:
+        return 2 * self.M * self.N * self.H
+
+
+QKV_CONFIGS = {
+    "qkv_action_expert_m50": QkvConfig(2, "qkv_action_expert_m50", 50, 1024, 8, 1, 256, 788, 1024, 10000.0),
+    "qkv_vlm_prefix_m788": QkvConfig(3, "qkv_vlm_prefix_m788", 788, 2048, 8, 1, 256, 0, 1024, 10000.0),
+    "qkv_llm_decode_m1": QkvConfig(4, "qkv_llm_decode_m1", 1, 5120, 64, 8, 128, 4095, 4096, 1e6),
+}

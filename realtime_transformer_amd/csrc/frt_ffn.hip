@@ -25,6 +25,7 @@
 
 #include "../../include/frt_ffn.h"
 #include "frt_device.h"
+#include "frt_host.h"
 
 namespace frt {
 hipError_t launch_add_rmsnorm_quant(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*,
@@ -58,9 +59,6 @@ hipError_t launch_mm_gateup(int, int, bool, const uint8_t*, const uint8_t*, uint
                             float, hipStream_t);
 hipError_t launch_mm_down(int, bool, const uint8_t*, const uint8_t*, uint16_t*, float*, int, int, int, int, float,
                           hipStream_t);
-int mm_config_bm(int);
-int mm_config_bn(int);
-int mm_config_ks(int);
 int gemm_config_bm(int);
 int gemm_config_bn(int);
 hipError_t launch_calib_gateup(int, const float*, const uint8_t*, float*, float*, int, int, int,
@@ -70,48 +68,6 @@ hipError_t launch_calib_down(const float*, const uint8_t*, uint16_t*, int, int, 
 }  // namespace frt
 
 using namespace frt;
-
-// ---------------------------------------------------------------------------
-// errors
-// ---------------------------------------------------------------------------
-
-static thread_local std::string g_last_error;
-
-static frt_status fail(frt_status st, const char* fmt, ...) {
-  char buf[512];
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
-  va_end(ap);
-  g_last_error = buf;
-  return st;
-}
-
-#define HIP_CHECK(call)                                                                    \
-  do {                                                                                     \
-    hipError_t e_ = (call);                                                                \
-    if (e_ != hipSuccess) return fail(FRT_ERR_HIP, "%s failed: %s", #call, hipGetErrorString(e_)); \
-  } while (0)
-
-#define KERNEL_CHECK(call, name)                                                           \
-  do {                                                                                     \
-    hipError_t e_ = (call);                                                                \
-    if (e_ != hipSuccess) return fail(FRT_ERR_HIP, "launch of %s failed: %s", name, hipGetErrorString(e_)); \
-  } while (0)
-
-// Keep the plan's device current for the duration of a call, then restore.
-struct DeviceGuard {
-  int prev = -1;
-  hipError_t err = hipSuccess;
-  explicit DeviceGuard(int dev) {
-    err = hipGetDevice(&prev);
-    if (err == hipSuccess && prev != dev) err = hipSetDevice(dev);
-  }
-  ~DeviceGuard() {
-    int cur = -1;
-    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
-  }
-};
 
 // ---------------------------------------------------------------------------
 // plan and workspace layout
@@ -124,10 +80,14 @@ constexpr int kGemvMtMaxM = 64;  // multi-tile GEMV up to here (FRT_GEMV_MT_MAX_
 constexpr int kMMMinM = 128;  // from here on the LDS-DMA GEMM takes the f16 path
 constexpr int kCUs = 256;  // MI355X compute units (workgroup rounds are counted against them)
 
-int env_int(const char* name, int dflt) {
+}  // namespace
+
+int frt::env_int(const char* name, int dflt) {
   const char* e = getenv(name);
   return (e && *e) ? atoi(e) : dflt;
 }
+
+namespace {
 
 // Waves per GEMV workgroup: the smallest power of two (<= 16, <= K blocks)
 // that brings workgroups * W to `target` waves across the chip (measured best:
@@ -178,7 +138,6 @@ struct Layout {
   bool mm_gu, mm_dn;   // GEMM runs on the LDS-DMA f16 kernel (k_mm) rather than k_gemm
 };
 
-size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 bool desc_ok(const frt_ffn_desc* d) {
   if (!d) return false;
@@ -197,7 +156,6 @@ bool desc_ok(const frt_ffn_desc* d) {
   return true;
 }
 
-int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 
 
@@ -211,8 +169,9 @@ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 // K split that fills the chip against the cost of its fp32 partials (written
 // once, read once by the consumer).  Rates are rough per-CU figures; the
 // choice only has to rank the candidates.
-constexpr int kMMConfigCount = 6;
-void choose_mm(int M, int N, int K, bool allow_split, int& cfg, int& split) {
+}  // namespace
+
+void frt::choose_mm(int M, int N, int K, bool allow_split, int& cfg, int& split) {
   const double cu_flops = 1.5e15 / kCUs, hbm = 5.0e12;
   double best = 1e30;
   cfg = -1;
@@ -234,6 +193,8 @@ void choose_mm(int M, int N, int K, bool allow_split, int& cfg, int& split) {
     }
   }
 }
+
+namespace {
 
 void choose_gemm(const frt_ffn_desc& d, Layout& lo) {
   const int npk = d.act != FRT_ACT_GELU_TANH ? 2 * d.I : d.I;
@@ -410,7 +371,7 @@ struct frt_plan {
 
 extern "C" {
 
-const char* frt_last_error(void) { return g_last_error.c_str(); }
+const char* frt_last_error(void) { return frt::last_error_text().c_str(); }
 
 frt_status frt_ffn_workspace_size(const frt_ffn_desc* desc, size_t* bytes) {
   if (!bytes) return fail(FRT_ERR_INVALID_ARG, "frt_ffn_workspace_size: bytes is NULL");

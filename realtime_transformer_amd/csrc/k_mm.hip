@@ -42,10 +42,13 @@
 // XCD, whose L2 then serves the weight tile and the activation rows to each
 // of them).
 #include "frt_device.h"
+#include "frt_qkv_dev.h"
 
 namespace frt {
 
-enum { MM_GEGLU = 0, MM_SWIGLU = 1, MM_GELU = 2, MM_DOWN = 3 };
+// MM_QKV: the attention input's fused QKV projection with the split + rotary
+// epilogue (frt_qkv_dev.h); its packed pairs hold rotation partners.
+enum { MM_GEGLU = 0, MM_SWIGLU = 1, MM_GELU = 2, MM_DOWN = 3, MM_QKV = 4 };
 
 template <int EPI>
 __device__ __forceinline__ float mm_act(float g, float u) {
@@ -124,7 +127,7 @@ template <int EPI, class C, bool FP8>
 __global__ __launch_bounds__(C::NT) void k_mm(const uint8_t* __restrict__ act, const uint8_t* __restrict__ wt,
                                               void* __restrict__ out, float* __restrict__ part, int M, int K,
                                               int Npk, int tiles_n, int tiles_m, int num_splits, float alpha_a,
-                                              float alpha_b, float inv_out) {
+                                              float alpha_b, float inv_out, const QkvOut qo) {
   constexpr int BM = C::BM, BN = C::BN, KS = C::KS, NS = C::NS, CPW = C::CPW;
   constexpr int TA = C::TA, TW = C::TW, NW = C::NW;
   constexpr bool GATED = EPI == MM_GEGLU || EPI == MM_SWIGLU;
@@ -383,6 +386,18 @@ __global__ __launch_bounds__(C::NT) void k_mm(const uint8_t* __restrict__ act, c
             *reinterpret_cast<float4*>(ps + (size_t)m * N + n) = make_float4(a0, a1, a2, a3);
           }
         }
+      } else if (EPI == MM_QKV) {
+        // the tile is one pair: lane row rho = 8 g4 + 4 hi + r of both groups
+#pragma unroll
+        for (int g4 = 0; g4 < 2; ++g4) {
+          float f[4], g[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            f[r] = acc[j][i][4 * g4 + r];
+            g[r] = acc[j][i][8 + 4 * g4 + r];
+          }
+          qkv_store4(qo, m, nt / 32, 8 * g4 + 4 * hi, f, g);
+        }
       } else if (GATED) {
         const int I = Npk / 2;
         const int i0 = nt / 2;  // intermediate index of the tile's gate group
@@ -439,24 +454,24 @@ int mm_config_ks(int c) { return (c >= 0 && c < kMMConfigs) ? kMM_KS[c] : 0; }
 
 template <int EPI, class C, bool FP8>
 static hipError_t mm_launch(const uint8_t* act, const uint8_t* w, void* out, float* part, int M, int K, int Npk,
-                            int S, float a, float b, float inv, hipStream_t s) {
+                            int S, float a, float b, float inv, hipStream_t s, const QkvOut& qo) {
   if (Npk % C::BN || K % C::KS || S < 1 || S > K / C::KS) return hipErrorInvalidValue;
   const int tiles_n = Npk / C::BN, tiles_m = (M + C::BM - 1) / C::BM;
   hipLaunchKernelGGL((k_mm<EPI, C, FP8>), dim3(tiles_n * tiles_m * S), dim3(C::NT), 0, s, act, w, out, part, M, K,
-                     Npk, tiles_n, tiles_m, S, a, b, inv);
+                     Npk, tiles_n, tiles_m, S, a, b, inv, qo);
   return hipGetLastError();
 }
 
 template <int EPI, bool FP8>
 static hipError_t mm_cfg(int cfg, const uint8_t* act, const uint8_t* w, void* out, float* part, int M, int K,
-                         int Npk, int S, float a, float b, float inv, hipStream_t s) {
+                         int Npk, int S, float a, float b, float inv, hipStream_t s, const QkvOut& qo = QkvOut{}) {
   switch (cfg) {
-    case 0: return mm_launch<EPI, MMC0, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s);
-    case 1: return mm_launch<EPI, MMC1, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s);
-    case 2: return mm_launch<EPI, MMC2, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s);
-    case 3: return mm_launch<EPI, MMC3, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s);
-    case 4: return mm_launch<EPI, MMC4, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s);
-    case 5: return mm_launch<EPI, MMC5, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s);
+    case 0: return mm_launch<EPI, MMC0, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s, qo);
+    case 1: return mm_launch<EPI, MMC1, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s, qo);
+    case 2: return mm_launch<EPI, MMC2, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s, qo);
+    case 3: return mm_launch<EPI, MMC3, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s, qo);
+    case 4: return mm_launch<EPI, MMC4, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s, qo);
+    case 5: return mm_launch<EPI, MMC5, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s, qo);
     default: return hipErrorInvalidValue;
   }
 }
@@ -482,6 +497,13 @@ hipError_t launch_mm_down(int cfg, bool fp8, const uint8_t* hq, const uint8_t* w
                           int K, int N, int S, float alpha_d, hipStream_t s) {
   if (fp8) return mm_cfg<MM_DOWN, true>(cfg, hq, w, y, part, M, K, N, S, alpha_d, 0.0f, 0.0f, s);
   return mm_cfg<MM_DOWN, false>(cfg, hq, w, y, part, M, K, N, S, alpha_d, 0.0f, 0.0f, s);
+}
+
+// Fused QKV projection (attention input) with the split + rotary epilogue:
+// Npk = (nq + 2 nkv) hd packed rows, no K split (the rotation needs whole sums).
+hipError_t launch_mm_qkv(int cfg, const uint8_t* xq, const uint8_t* w, const QkvOut& o, int M, int K, int Npk,
+                         hipStream_t s) {
+  return mm_cfg<MM_QKV, false>(cfg, xq, w, nullptr, nullptr, M, K, Npk, 1, 0.0f, 0.0f, 0.0f, s, o);
 }
 
 }  // namespace frt

@@ -1,0 +1,224 @@
+// k_qkv.hip -- attention-input kernels: the rotary table, the packing of the
+// fused QKV weight, and the fused QKV GEMV (M <= 64) with the split + rotary
+// epilogue.
+//
+// FlashRT architecture doc, "Kernel library" (the "qkv split + RoPE" fusion
+// after the QKV projection); itsolotime article section 5.2 (the FusedQKV
+// weight: q, k, v rows fused, quantised with one scale, head interleave).
+//
+// The GEMV streams the packed weight exactly as the FFN's gate/up GEMV does
+// (one workgroup per pair of 16-row groups, waves splitting K, each weight
+// fragment converted to f16 once and multiplied into ceil(M/16) activation
+// tiles, partials meeting in LDS in wave order); only the epilogue differs.
+// Bound: HBM (N*H weight bytes per launch), latency at small N.
+#include "frt_qkv_dev.h"
+
+namespace frt {
+
+// Rotary table entry (p, i) = (f32(cos(p * theta_i)), f32(sin(p * theta_i))),
+// theta_i = base^(-2i/hd), all in fp64 and rounded once.
+__global__ __launch_bounds__(256) void k_rope_table(float2* __restrict__ out, int P, int half, int hd,
+                                                    double base) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)P * half) return;
+  const int i = (int)(idx % (size_t)half);
+  const int p = (int)(idx / (size_t)half);
+  const double theta = pow(base, -(2.0 * (double)i) / (double)hd);
+  const double a = (double)p * theta;
+  out[idx] = make_float2((float)cos(a), (float)sin(a));
+}
+
+hipError_t launch_rope_table(float2* out, int P, int hd, double base, hipStream_t s) {
+  const size_t n = (size_t)P * (hd / 2);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rope_table, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, out, P, hd / 2, hd, base);
+  return hipGetLastError();
+}
+
+// Quantise one of the three source matrices (rows [row_base, row_base +
+// nrows) of the fused weight, [nrows][K] bf16, times colw[k] when given) with
+// factor inv into the packed layout (frt_qkv_dev.h).  One thread per 16
+// consecutive K values of a row.
+__global__ __launch_bounds__(256) void k_quant_pack_qkv(const uint16_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                        int nrows, int K, float inv, int row_base, int hd, int n_rope,
+                                                        const uint16_t* __restrict__ colw) {
+  const size_t pieces_per_row = (size_t)K / 16;
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)nrows * pieces_per_row) return;
+  const int n = (int)(idx / pieces_per_row);
+  const int k0 = (int)(idx % pieces_per_row) * 16;
+  const uint4* sp = reinterpret_cast<const uint4*>(src + (size_t)n * K + k0);
+  const uint4 a = sp[0], b = sp[1];
+  const uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t c[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c[j] = 0x3F803F80u;  // bf16 1.0 pairs
+  if (colw) {
+    const uint4* cp = reinterpret_cast<const uint4*>(colw + k0);
+    const uint4 c0 = cp[0], c1 = cp[1];
+    c[0] = c0.x; c[1] = c0.y; c[2] = c0.z; c[3] = c0.w;
+    c[4] = c1.x; c[5] = c1.y; c[6] = c1.z; c[7] = c1.w;
+  }
+  uint32_t q[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    q[j] = e4m3x4((bf16_lo(v[2 * j]) * bf16_lo(c[2 * j])) * inv, (bf16_hi(v[2 * j]) * bf16_hi(c[2 * j])) * inv,
+                  (bf16_lo(v[2 * j + 1]) * bf16_lo(c[2 * j + 1])) * inv,
+                  (bf16_hi(v[2 * j + 1]) * bf16_hi(c[2 * j + 1])) * inv);
+  const uint32_t prow = qkv_packed_row((uint32_t)(row_base + n), (uint32_t)hd, (uint32_t)n_rope);
+  *reinterpret_cast<uint4*>(dst + packed_offset(prow, (uint32_t)k0, (uint32_t)K)) = make_uint4(q[0], q[1], q[2], q[3]);
+}
+
+hipError_t launch_quant_pack_qkv(const uint16_t* src, uint8_t* dst, int nrows, int K, float inv, int row_base,
+                                 int hd, int n_rope, const uint16_t* colw, hipStream_t s) {
+  const size_t pieces = (size_t)nrows * (K / 16);
+  if (pieces == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_quant_pack_qkv, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s, src, dst, nrows, K,
+                     inv, row_base, hd, n_rope, colw);
+  return hipGetLastError();
+}
+
+typedef unsigned v4u_q __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void qkv_load_w32(const uint8_t* wp, int kb, uint32_t o[8]) {
+  const v4u_q a = __builtin_nontemporal_load(reinterpret_cast<const v4u_q*>(wp + (size_t)kb * 2048));
+  const v4u_q b = __builtin_nontemporal_load(reinterpret_cast<const v4u_q*>(wp + (size_t)kb * 2048 + 1024));
+  o[0] = a[0]; o[1] = a[1]; o[2] = a[2]; o[3] = a[3];
+  o[4] = b[0]; o[5] = b[1]; o[6] = b[2]; o[7] = b[3];
+}
+__device__ __forceinline__ void qkv_load_x32(const uint8_t* xr, bool has_row, int kb, uint32_t o[8]) {
+  uint4 a = make_uint4(0, 0, 0, 0), b = a;
+  if (has_row) {
+    a = *reinterpret_cast<const uint4*>(xr + kb * 128);
+    b = *reinterpret_cast<const uint4*>(xr + kb * 128 + 16);
+  }
+  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+  o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+
+// One workgroup of W waves per pair p of 16-row groups; MT activation tiles.
+template <int W, int MT>
+__global__ __launch_bounds__(W * 64) void k_gemv_qkv(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ w,
+                                                     const QkvOut o, int M, int K) {
+  static_assert(W >= MT, "one wave per tile finishes the epilogue");
+  __shared__ v4f red[W][MT][2][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int p = blockIdx.x;
+  const int KB = K >> 7;
+  const int kb0 = wave * KB / W, kb1 = (wave + 1) * KB / W;
+  const int row = lane & 15, q = lane >> 4;
+  const uint8_t* w1 = w + (size_t)(2 * p) * KB * 2048 + lane * 16;
+  const uint8_t* w2 = w + (size_t)(2 * p + 1) * KB * 2048 + lane * 16;
+  const uint8_t* xr[MT];
+  bool has[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    has[t] = 16 * t + row < M;
+    xr[t] = xq + (size_t)(has[t] ? 16 * t + row : 0) * K + q * 32;
+  }
+  v4f acc1[MT], acc2[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc1[t] = acc2[t] = v4f{0, 0, 0, 0};
+
+  for (int kb = kb0; kb < kb1; kb += 2) {
+    const bool two = kb + 1 < kb1;
+    uint32_t a0[8], a1[8], b0[8], b1[8], x0[MT][8], x1[MT][8];
+    qkv_load_w32(w1, kb, a0);
+    qkv_load_w32(w2, kb, b0);
+    if (two) {
+      qkv_load_w32(w1, kb + 1, a1);
+      qkv_load_w32(w2, kb + 1, b1);
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      qkv_load_x32(xr[t], has[t], kb, x0[t]);
+      qkv_load_x32(xr[t], has[t] && two, kb + (two ? 1 : 0), x1[t]);
+    }
+    v8h ah[4], bh[4];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      ah[s4] = e4m3x8_to_f16(a0[2 * s4], a0[2 * s4 + 1]);
+      bh[s4] = e4m3x8_to_f16(b0[2 * s4], b0[2 * s4 + 1]);
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const v8h xh = e4m3x8_to_f16(x0[t][2 * s4], x0[t][2 * s4 + 1]);
+        acc1[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, ah[s4], acc1[t], 0, 0, 0);
+        acc2[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, bh[s4], acc2[t], 0, 0, 0);
+      }
+    if (two) {
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        ah[s4] = e4m3x8_to_f16(a1[2 * s4], a1[2 * s4 + 1]);
+        bh[s4] = e4m3x8_to_f16(b1[2 * s4], b1[2 * s4 + 1]);
+      }
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const v8h xh = e4m3x8_to_f16(x1[t][2 * s4], x1[t][2 * s4 + 1]);
+          acc1[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, ah[s4], acc1[t], 0, 0, 0);
+          acc2[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, bh[s4], acc2[t], 0, 0, 0);
+        }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    red[wave][t][0][lane] = acc1[t];
+    red[wave][t][1][lane] = acc2[t];
+  }
+  __syncthreads();
+  if (wave >= MT) return;
+  const int t = wave;
+  v4f f = red[0][t][0][lane], g = red[0][t][1][lane];
+#pragma unroll
+  for (int v = 1; v < W; ++v) {
+    f += red[v][t][0][lane];
+    g += red[v][t][1][lane];
+  }
+  // lane holds rows m = 16t + 4q + r of lane row `row` in both groups
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = 16 * t + 4 * q + r;
+    if (m < M) qkv_store(o, m, p, row, f[r], g[r]);
+  }
+}
+
+// (W = 16 only with MT <= 2: the reduction buffer is W * MT * 2 KiB of LDS)
+template <int W, int MT>
+static hipError_t gemv_qkv_t(const uint8_t* xq, const uint8_t* w, const QkvOut& o, int M, int K, int pairs,
+                             hipStream_t s) {
+  hipLaunchKernelGGL((k_gemv_qkv<W, MT>), dim3(pairs), dim3(W * 64), 0, s, xq, w, o, M, K);
+  return hipGetLastError();
+}
+
+// M <= 64; W in {4, 8, 16} (16 taken as 8 above M = 32); pairs = (nq + 2 nkv) * hd / 32.
+hipError_t launch_gemv_qkv(const uint8_t* xq, const uint8_t* w, const QkvOut& o, int M, int K, int W,
+                           hipStream_t s) {
+  if (M < 1 || M > 64 || K < 128 || (K & 127)) return hipErrorInvalidValue;
+  const int pairs = (o.nq + 2 * o.nkv) * o.hd / 32;
+  const int mt = (M + 15) / 16;
+  if (W == 16 && mt > 2) W = 8;
+  if (W == 16) return mt == 1 ? gemv_qkv_t<16, 1>(xq, w, o, M, K, pairs, s) : gemv_qkv_t<16, 2>(xq, w, o, M, K, pairs, s);
+  if (W == 8) {
+    switch (mt) {
+      case 1: return gemv_qkv_t<8, 1>(xq, w, o, M, K, pairs, s);
+      case 2: return gemv_qkv_t<8, 2>(xq, w, o, M, K, pairs, s);
+      case 3: return gemv_qkv_t<8, 3>(xq, w, o, M, K, pairs, s);
+      default: return gemv_qkv_t<8, 4>(xq, w, o, M, K, pairs, s);
+    }
+  }
+  if (W == 4) {
+    switch (mt) {
+      case 1: return gemv_qkv_t<4, 1>(xq, w, o, M, K, pairs, s);
+      case 2: return gemv_qkv_t<4, 2>(xq, w, o, M, K, pairs, s);
+      case 3: return gemv_qkv_t<4, 3>(xq, w, o, M, K, pairs, s);
+      default: return gemv_qkv_t<4, 4>(xq, w, o, M, K, pairs, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace frt

@@ -137,3 +137,20 @@ def modulation(cfg: FFNConfig, layer: int, std: float = 0.1) -> Tuple[np.ndarray
     """(scale [H], shift [H]) bf16 bits for layer `layer`'s AdaRMSNorm."""
     base = (1 << 20) + 1000 * cfg.index + 2 * layer
     return normal_bf16(base, (cfg.H,), std=std), normal_bf16(base + 1, (cfg.H,), std=std)
+
+
+def qkv_weights(cfg) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """(w_q [nq*hd, H], w_k [nkv*hd, H], w_v [nkv*hd, H], w_norm [H]) bf16 bits
+    for an attention-input workload: projections N(0, 0.02), norm 1 + N(0, 0.1).
+    Seeds 2^21 + 1000*c + {0 q, 1 k, 2 v, 3 norm}."""
+    base = (1 << 21) + 1000 * cfg.index
+    wq = normal_bf16(base, (cfg.nq * cfg.hd, cfg.H), std=0.02)
+    wk = normal_bf16(base + 1, (cfg.nkv * cfg.hd, cfg.H), std=0.02)
+    wv = normal_bf16(base + 2, (cfg.nkv * cfg.hd, cfg.H), std=0.02)
+    wn = normal_bf16(base + 3, (cfg.H,), std=0.1, mean=1.0)
+    return wq, wk, wv, wn
+
+
+def positions(cfg) -> np.ndarray:
+    """Rotary positions of the rows: pos0, pos0 + 1, ... (int32)."""
+    return (cfg.pos0 + np.arange(cfg.M)).astype(np.int32)

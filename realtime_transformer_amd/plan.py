@@ -175,3 +175,135 @@ def to_np_u16(t: torch.Tensor) -> np.ndarray:
 
 def to_np_u8(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy()
+
+
+class QkvPlan:
+    """Attention-input plan (include/frt_qkv.h) over a torch workspace tensor."""
+
+    def __init__(self, M: int, H: int, nq: int, nkv: int, hd: int, max_pos: int, eps: float = 1e-6,
+                 rope_base: float = 10000.0, device: int = 0, stream: Optional[torch.cuda.Stream] = None,
+                 flags: int = 0):
+        _require_gpu()
+        _abi.load()
+        self.M, self.H, self.nq, self.nkv, self.hd, self.max_pos = M, H, nq, nkv, hd, max_pos
+        self.N = (nq + 2 * nkv) * hd
+        self.device = torch.device("cuda", device)
+        self.desc = _abi.make_qkv_desc(M, H, nq, nkv, hd, max_pos, eps, rope_base, device, flags)
+        self.nbytes = _abi.frt_qkv_workspace_size(self.desc)
+        self.ws = torch.empty(self.nbytes + 256, dtype=torch.uint8, device=self.device)
+        base = self.ws.data_ptr()
+        self.ws_ptr = base + (-base) % 256
+        self.plan = _abi.frt_qkv_plan_create(self.desc, self.ws_ptr, self.nbytes)
+        self.io = _abi.frt_qkv_io_get(self.plan)
+        self.stream = stream if stream is not None else torch.cuda.Stream(self.device)
+
+    def close(self):
+        if getattr(self, "plan", None):
+            torch.cuda.synchronize(self.device)
+            _abi.frt_qkv_plan_destroy(self.plan)
+            self.plan = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def s(self) -> int:
+        return self.stream.cuda_stream
+
+    def sync(self):
+        self.stream.synchronize()
+
+    def _view(self, ptr: int, nbytes: int) -> torch.Tensor:
+        off = ptr - self.ws.data_ptr()
+        assert 0 <= off and off + nbytes <= self.ws.numel()
+        return self.ws[off:off + nbytes]
+
+    def _u16(self, ptr, *shape) -> torch.Tensor:
+        n = int(np.prod(shape))
+        return self._view(ptr, 2 * n).view(torch.int16).view(*shape)
+
+    def r_in(self):
+        return self._u16(self.io.r_in, self.M, self.H)
+
+    def y_in(self):
+        return self._u16(self.io.y_in, self.M, self.H)
+
+    def r_out(self):
+        return self._u16(self.io.r_out, self.M, self.H)
+
+    def xq(self):
+        return self._view(self.io.xq, self.M * self.H).view(self.M, self.H)
+
+    def q(self):
+        return self._u16(self.io.q, self.M, self.nq, self.hd)
+
+    def k(self):
+        return self._u16(self.io.k, self.M, self.nkv, self.hd)
+
+    def v(self):
+        return self._u16(self.io.v, self.M, self.nkv, self.hd)
+
+    def rope(self):
+        return self._view(self.io.rope, self.max_pos * self.hd * 4).view(torch.float32).view(
+            self.max_pos, self.hd // 2, 2)
+
+    def mod(self):
+        if not self.io.mod:
+            raise RuntimeError("plan has no modulation slot (FRT_FLAG_ADA_NORM not set)")
+        return self._u16(self.io.mod, 2, self.H)
+
+    def load(self, wq, wk, wv, w_norm):
+        tq, tk, tv, tn = (_to_dev_u16(a, self.device) for a in (wq, wk, wv, w_norm))
+        torch.cuda.synchronize(self.device)
+        _abi.frt_qkv_quant_weights(self.plan, tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), tn.data_ptr(), self.s)
+        del tq, tk, tv, tn
+
+    def export_codes(self) -> np.ndarray:
+        return _abi.frt_qkv_export_weight_codes(self.plan, self.N, self.H)
+
+    def scales(self) -> np.ndarray:
+        return _abi.frt_qkv_get_scales(self.plan)
+
+    def set_act_scale(self, s_x: float):
+        _abi.frt_qkv_set_act_scale(self.plan, s_x)
+
+    def set_modulation(self, scale: np.ndarray, shift: np.ndarray):
+        v = np.stack([np.asarray(scale, np.uint16), np.asarray(shift, np.uint16)])
+        with torch.cuda.stream(self.stream):
+            self.mod().copy_(_to_dev_u16(v, self.device))
+        self.sync()
+
+    def calibrate(self, batches, rows: Optional[int] = None):
+        rows = rows if rows is not None else batches[0][0].shape[0]
+        rs = [_to_dev_u16(r, self.device) for r, _ in batches]
+        ys = None if batches[0][1] is None else [_to_dev_u16(y, self.device) for _, y in batches]
+        torch.cuda.synchronize(self.device)
+        _abi.frt_qkv_calibrate(self.plan, [t.data_ptr() for t in rs], None if ys is None else [t.data_ptr() for t in ys],
+                               rows, self.s)
+        del rs, ys
+
+    def set_inputs(self, r0: np.ndarray, y0: Optional[np.ndarray], pos: np.ndarray):
+        with torch.cuda.stream(self.stream):
+            self.r_in().copy_(_to_dev_u16(r0, self.device))
+            if y0 is None:
+                self.y_in().zero_()
+            else:
+                self.y_in().copy_(_to_dev_u16(y0, self.device))
+        self.sync()
+        _abi.frt_qkv_set_positions(self.plan, pos, self.s)
+
+    def forward(self):
+        _abi.frt_qkv_forward(self.plan, self.s)
+
+    def time_kernel(self, which: int, reps: int = 10) -> float:
+        return _abi.frt_qkv_time_kernel(self.plan, which, reps, self.s)
+
+    def capture(self):
+        _abi.frt_qkv_graph_capture(self.plan, self.s)
+
+    def replay(self):
+        _abi.frt_qkv_graph_replay(self.plan, self.s)
+

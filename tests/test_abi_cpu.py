@@ -9,13 +9,16 @@ from realtime_transformer_amd import _abi
 from realtime_transformer_amd.configs import CONFIGS
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "frt_ffn.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 def _declared():
-    txt = open(HEADER).read()
-    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(frt_[a-z0-9_]+)\s*\(", txt)))
+    names = set()
+    for h in HEADERS:
+        txt = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(frt_[a-z0-9_]+)\s*\(", txt))
+    return sorted(names)
 
 
 def test_every_declared_symbol_is_exported():
@@ -59,3 +62,25 @@ def test_plan_create_rejects_null_workspace():
     with pytest.raises(_abi.FrtError) as e:
         _abi.frt_ffn_plan_create(d, 0, 1 << 20)
     assert e.value.status == _abi.FRT_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad", [
+    dict(M=0), dict(H=100), dict(H=16384 + 128), dict(nq=0), dict(nkv=0), dict(hd=48), dict(hd=16), dict(hd=544),
+    dict(max_pos=0), dict(eps=0.0), dict(rope_base=1.0), dict(rope_base=float("inf")), dict(flags=1), dict(flags=2),
+    dict(flags=8 | 16), dict(device=-1)])
+def test_bad_qkv_descriptors_rejected(bad):
+    kw = dict(M=4, H=256, nq=2, nkv=1, hd=64, max_pos=32, eps=1e-6, rope_base=1e4, device=0, flags=0)
+    kw.update(bad)
+    with pytest.raises(_abi.FrtError) as e:
+        _abi.frt_qkv_workspace_size(_abi.make_qkv_desc(**kw))
+    assert e.value.status == _abi.FRT_ERR_INVALID_ARG
+
+
+def test_qkv_workspace_covers_weights_table_and_slots():
+    from realtime_transformer_amd.configs import QKV_CONFIGS
+    for c in QKV_CONFIGS.values():
+        n = _abi.frt_qkv_workspace_size(_abi.make_qkv_desc(c.M, c.H, c.nq, c.nkv, c.hd, c.max_pos, c.eps, c.rope_base))
+        need = c.N * c.H + c.max_pos * c.hd * 4 + c.M * c.H * (2 + 2 + 2 + 1) + 2 * c.M * c.N
+        assert need <= n < 1.3 * need + (1 << 24)
+    for flags in (8, 16):
+        assert _abi.frt_qkv_workspace_size(_abi.make_qkv_desc(4, 256, 2, 1, 64, 32, flags=flags)) > 0
