@@ -122,6 +122,55 @@ def per_kernel_ms(plan, reps=3):
     return [plan.time_kernel(k, reps) / 1000.0 for k in range(3)]
 
 
+def measure_qkv(steps, warmup, calibrate=True):
+    """Attention-input workloads: graph replay of K1 + fused QKV GEMM with the
+    split + rotary epilogue, per-kernel times, and the GEMM's roofline (HBM
+    bytes for the GEMV shapes, matrix-core flops for the prefill shape)."""
+    import torch
+    from realtime_transformer_amd import datagen
+    from realtime_transformer_amd.configs import QKV_CONFIGS
+    from realtime_transformer_amd.plan import QkvPlan
+    res = {}
+    for name, c in QKV_CONFIGS.items():
+        p = QkvPlan(c.M, c.H, c.nq, c.nkv, c.hd, c.max_pos, c.eps, c.rope_base)
+        p.load(*datagen.qkv_weights(c))
+        if calibrate:
+            p.calibrate(datagen.calib_batches(c))
+        else:
+            p.set_act_scale(0.01)
+        r0, y0 = datagen.eval_inputs(c)
+        p.set_inputs(r0, y0, datagen.positions(c))
+        p.capture()
+        for _ in range(warmup):
+            p.replay()
+        p.sync()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(p.stream)
+        for _ in range(steps):
+            p.replay()
+        e1.record(p.stream)
+        e1.synchronize()
+        us = e0.elapsed_time(e1) * 1000.0 / steps
+        k = [p.time_kernel(i, 20) for i in range(2)]
+        p.close()
+        rec = {"M": c.M, "H": c.H, "heads": [c.nq, c.nkv, c.hd], "us_per_block": round(us, 3),
+               "kernels_us": {"norm_quant": round(k[0], 3), "qkv": round(k[1], 3)}}
+        if c.M <= 64:
+            gbs = c.qkv_bytes() / (k[1] * 1e-6) / 1e9
+            rec["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": c.qkv_bytes()}
+        else:
+            tf = c.qkv_flops() / (k[1] * 1e-6) / 1e12
+            rec["roofline"] = {"bound": "mfma", "achieved": round(tf, 1), "peak": F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                               "frac": round(tf / F16_PEAK_TFLOPS, 4), "flops_per_launch": c.qkv_flops(),
+                               "note": "f16 matrix cores on exactly converted E4M3 operands; of the FP8 peak: %.4f"
+                                       % (tf / FP8_PEAK_TFLOPS)}
+        res[name] = rec
+        log("[bench %s] %.2f us per block (norm %.2f, qkv %.2f)" % (name, us, k[0], k[1]))
+    return res
+
+
 def cpu_baseline(cfg, kept, inputs, budget_s):
     """Time the CPU oracle's block on the kept layers until budget_s has passed."""
     import oracle
@@ -162,6 +211,8 @@ def main():
                     help="skip timing the opt-in FP8 matrix-core modes of the second workload")
     ap.add_argument("--no-norm-variants", action="store_true",
                     help="skip timing the action-expert chain with the norm variants")
+    ap.add_argument("--no-qkv", action="store_true",
+                    help="skip timing the attention-input (K1 + fused QKV + rotary) workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="first copy this many MiB device-to-device once (a plain copy kernel of known "
@@ -307,6 +358,9 @@ def main():
                                        "down": round(k3[2] * 1000, 3)}}
             log("[bench %s] %s: %.2f us/layer" % (c3.name, name, nv[name]["us_per_layer"]))
         out["norm_variants"] = nv
+
+    if not args.no_qkv:
+        out["qkv"] = measure_qkv(args.steps, args.warmup, calibrate=not args.no_calibrate)
 
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle for ~%.0fs" % args.cpu_seconds)

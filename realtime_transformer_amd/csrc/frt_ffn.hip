@@ -171,12 +171,12 @@ bool desc_ok(const frt_ffn_desc* d) {
 // choice only has to rank the candidates.
 }  // namespace
 
-void frt::choose_mm(int M, int N, int K, bool allow_split, int& cfg, int& split) {
+void frt::choose_mm(int M, int N, int K, bool allow_split, int& cfg, int& split, int ncfg) {
   const double cu_flops = 1.5e15 / kCUs, hbm = 5.0e12;
   double best = 1e30;
   cfg = -1;
   split = 1;
-  for (int c = 0; c < kMMConfigCount; ++c) {
+  for (int c = 0; c < ncfg; ++c) {
     const int bm = mm_config_bm(c), bn = mm_config_bn(c), ks = mm_config_ks(c);
     if (N % bn || K % ks) continue;
     const int tiles = (N / bn) * ceil_div(M, bm);

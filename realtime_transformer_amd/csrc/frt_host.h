@@ -50,8 +50,11 @@ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 int env_int(const char* name, int dflt);
 // LDS-DMA GEMM (k_mm) tile configuration (and K split when allowed) for an
 // [M] x [N] output over K; cfg < 0 when no configuration fits.
-void choose_mm(int M, int N, int K, bool allow_split, int& cfg, int& split);
+// Configurations [0, ncfg) are considered: the FFN GEMMs use the first six,
+// the attention input all eight (6 and 7 are small tiles for short outputs).
 constexpr int kMMConfigCount = 6;
+constexpr int kMMConfigCountAll = 8;
+void choose_mm(int M, int N, int K, bool allow_split, int& cfg, int& split, int ncfg = kMMConfigCount);
 int mm_config_bm(int);
 int mm_config_bn(int);
 int mm_config_ks(int);

@@ -62,13 +62,15 @@ struct QkvLayout {
   int mm_cfg;  // LDS-DMA GEMM configuration (M > 64)
 };
 
-// GEMV waves: the smallest of 4, 8, 16 that gives ~6 waves per SIMD across
-// the pairs (as the FFN's gate/up GEMV), at most the K blocks, 8 above M = 32.
+// GEMV waves: the smallest of 4, 8, 16 that gives about 1280 waves across
+// the pairs (measured: 4 waves on the 320 pairs of the decode shape beat 16 by
+// 12%; 8 on the 80 pairs of the action-expert shape), at most the K blocks,
+// 8 above M = 32.
 int qkv_gemv_waves(int pairs, int kblocks, int M) {
   int w = env_int("FRT_QKV_GEMV_WAVES", 0);
   if (w != 4 && w != 8 && w != 16) {
     w = 4;
-    while (w < 16 && pairs * w < 6144) w *= 2;
+    while (w < 16 && pairs * w < 1280) w *= 2;
     while (w > 4 && w > kblocks) w /= 2;
   }
   if (w == 16 && M > 32) w = 8;
@@ -104,9 +106,13 @@ QkvLayout qkv_layout(const frt_qkv_desc& d) {
   lo.mm_cfg = -1;
   if (d.M > kQkvGemvMaxM) {
     int c = -1, sp = 1;
-    choose_mm(d.M, (int)N, d.H, false, c, sp);
+    choose_mm(d.M, (int)N, d.H, false, c, sp, kMMConfigCountAll);
+    // a short output leaves CUs idle under the chosen tiles: take 64 x 128
+    // tiles (measured at M=788, N=2560: 20.3 us against 23.3 us for 128 x 128)
+    if (c >= 0 && (int)(N / mm_config_bn(c)) * ceil_div(d.M, mm_config_bm(c)) < 256 && N % mm_config_bn(6) == 0)
+      c = 6;
     c = env_int("FRT_MM_QKV_CFG", c);
-    if (c >= 0 && c < kMMConfigCount && N % mm_config_bn(c) == 0 && d.H % mm_config_ks(c) == 0) lo.mm_cfg = c;
+    if (c >= 0 && c < kMMConfigCountAll && N % mm_config_bn(c) == 0 && d.H % mm_config_ks(c) == 0) lo.mm_cfg = c;
   }
   return lo;
 }

@@ -436,17 +436,23 @@ __global__ __launch_bounds__(C::NT) void k_mm(const uint8_t* __restrict__ act, c
 //   3: BM 128 x BN 256, waves 2 x 2 (wave tile  64 x 128), 4 stages  generic
 //   4: BM 256 x BN 256, waves 2 x 2 (wave tile 128 x 128), 4 stages  generic, large
 //   5: BM 128 x BN 128, waves 2 x 2 (wave tile  64 x 64), 4 stages   small grids
+//   6: BM  64 x BN 128, waves 2 x 2 (wave tile  32 x 64), 4 stages   QKV only
+//   7: BM 128 x BN  64, waves 2 x 2 (wave tile  64 x 32), 4 stages   QKV only
 using MMC0 = MMCfg<224, 256, 1, 4, 4>;
 using MMC1 = MMCfg<256, 224, 4, 1, 4>;
 using MMC2 = MMCfg<256, 192, 2, 2, 4>;
 using MMC3 = MMCfg<128, 256, 2, 2, 4>;
 using MMC4 = MMCfg<256, 256, 2, 2, 4>;
 using MMC5 = MMCfg<128, 128, 2, 2, 4>;
-constexpr int kMMConfigs = 6;
+// small tiles for short outputs (the attention input's fused QKV): more
+// workgroups than CUs where 128 x 128 tiles would leave part of the chip idle
+using MMC6 = MMCfg<64, 128, 2, 2, 4>;
+using MMC7 = MMCfg<128, 64, 2, 2, 4>;
+constexpr int kMMConfigs = 8;
 
-static const int kMM_BM[kMMConfigs] = {MMC0::BM, MMC1::BM, MMC2::BM, MMC3::BM, MMC4::BM, MMC5::BM};
-static const int kMM_BN[kMMConfigs] = {MMC0::BN, MMC1::BN, MMC2::BN, MMC3::BN, MMC4::BN, MMC5::BN};
-static const int kMM_KS[kMMConfigs] = {MMC0::KS, MMC1::KS, MMC2::KS, MMC3::KS, MMC4::KS, MMC5::KS};
+static const int kMM_BM[kMMConfigs] = {MMC0::BM, MMC1::BM, MMC2::BM, MMC3::BM, MMC4::BM, MMC5::BM, MMC6::BM, MMC7::BM};
+static const int kMM_BN[kMMConfigs] = {MMC0::BN, MMC1::BN, MMC2::BN, MMC3::BN, MMC4::BN, MMC5::BN, MMC6::BN, MMC7::BN};
+static const int kMM_KS[kMMConfigs] = {MMC0::KS, MMC1::KS, MMC2::KS, MMC3::KS, MMC4::KS, MMC5::KS, MMC6::KS, MMC7::KS};
 
 int mm_config_bm(int c) { return (c >= 0 && c < kMMConfigs) ? kMM_BM[c] : 0; }
 int mm_config_bn(int c) { return (c >= 0 && c < kMMConfigs) ? kMM_BN[c] : 0; }
@@ -472,6 +478,12 @@ static hipError_t mm_cfg(int cfg, const uint8_t* act, const uint8_t* w, void* ou
     case 3: return mm_launch<EPI, MMC3, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s, qo);
     case 4: return mm_launch<EPI, MMC4, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s, qo);
     case 5: return mm_launch<EPI, MMC5, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s, qo);
+    case 6:
+      if constexpr (EPI == MM_QKV) return mm_launch<EPI, MMC6, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s, qo);
+      return hipErrorInvalidValue;
+    case 7:
+      if constexpr (EPI == MM_QKV) return mm_launch<EPI, MMC7, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s, qo);
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
