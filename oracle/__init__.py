@@ -106,6 +106,21 @@ def lib():
         L.orc_down.argtypes = [ctypes.c_int] * 3 + [_c_u8p, _c_u8p, ctypes.c_float, _c_u16p,
                                                     ctypes.c_int]
         L.orc_block.restype = ctypes.c_int
+        L.orc_e2m1_decode.argtypes = [ctypes.c_uint8]
+        L.orc_e2m1_decode.restype = ctypes.c_double
+        L.orc_e2m1_encode.argtypes = [ctypes.c_double]
+        L.orc_e2m1_encode.restype = ctypes.c_uint8
+        L.orc_mx_scale_exp.argtypes = [ctypes.c_double]
+        L.orc_mx_scale_exp.restype = ctypes.c_int
+        L.orc_mxfp4_quant_rows.argtypes = [_c_f32p, ctypes.c_int64, ctypes.c_int64, _c_u8p, _c_u8p]
+        L.orc_mxfp4_quant_rows.restype = None
+        L.orc_mxfp4_quant_weight.argtypes = [_c_u16p, ctypes.c_int64, ctypes.c_int64, _c_u16p, _c_u8p, _c_u8p]
+        L.orc_mxfp4_quant_weight.restype = ctypes.c_int
+        L.orc_mxfp4_gemm.argtypes = [ctypes.c_int] * 3 + [_c_u8p] * 4 + [_c_f32p, ctypes.c_int]
+        L.orc_mxfp4_gemm.restype = ctypes.c_int
+        L.orc_block_mxfp4.argtypes = ([ctypes.c_int] * 4 + [ctypes.c_float] + [_c_u16p] * 5 + [_c_f32p] +
+                                      [_c_u8p] * 6 + [_c_u16p] + [_c_u8p] * 4 + [_c_u16p, ctypes.c_int])
+        L.orc_block_mxfp4.restype = ctypes.c_int
         L.orc_rope_table.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double, _c_f32p]
         L.orc_rope_table.restype = None
         L.orc_qkv_epilogue.argtypes = ([ctypes.c_int] * 4 + [_c_f32p, ctypes.c_float, _c_i32p, _c_f32p,
@@ -546,3 +561,138 @@ def qkv_calibrate(batches, qw: QkvWeights, eps: float) -> float:
         _, x, _ = add_rmsnorm_quant(r, y, qw.w_norm, eps, 1.0, mod=qw.mod)
         amax = max(amax, float(np.max(np.abs(x))))
     return scale_from_amax(amax)
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 FFN variant (itsolotime article section 7.2: the NVFP4 encoder FFN
+# with AWQ pre-scale and a 4-bit gated combine; here OCP MXFP4 blocks of 32
+# with E8M0 scales).  Codes: E2M1 nibbles, element 2i in the low nibble of
+# byte i; scales: E8M0 exponents e (X = 2^(e-127)), one per 32 elements.
+# ---------------------------------------------------------------------------
+
+def e2m1_decode(codes) -> np.ndarray:
+    c = np.asarray(codes, np.uint8)
+    return np.vectorize(lambda x: lib().orc_e2m1_decode(int(x)), otypes=[np.float64])(c) if c.size else c.astype(float)
+
+
+def e2m1_encode(v) -> np.ndarray:
+    a = np.asarray(v, np.float64)
+    return np.vectorize(lambda x: lib().orc_e2m1_encode(float(x)), otypes=[np.uint8])(a)
+
+
+def mx_scale_exp(amax: float) -> int:
+    return int(lib().orc_mx_scale_exp(float(amax)))
+
+
+def mxfp4_quant_rows(v):
+    """fp32 [rows, cols] (cols % 32 == 0) -> (codes [rows, cols/2], scales [rows, cols/32])."""
+    v = np.ascontiguousarray(v, np.float32)
+    rows, cols = v.shape
+    assert cols % 32 == 0
+    codes = np.empty((rows, cols // 2), np.uint8)
+    scales = np.empty((rows, cols // 32), np.uint8)
+    lib().orc_mxfp4_quant_rows(_p(v, _c_f32p), rows, cols, _p(codes, _c_u8p), _p(scales, _c_u8p))
+    return codes, scales
+
+
+def mxfp4_quant_weight(w_bf16, colw_bf16=None):
+    """bf16 [rows, cols] times the bf16 column factor (AWQ scale) -> MXFP4 along cols."""
+    w = _u16(w_bf16)
+    rows, cols = w.shape
+    cw = None if colw_bf16 is None else _u16(colw_bf16)
+    assert cw is None or cw.shape == (cols,)
+    codes = np.empty((rows, cols // 2), np.uint8)
+    scales = np.empty((rows, cols // 32), np.uint8)
+    rc = lib().orc_mxfp4_quant_weight(_p(w, _c_u16p), rows, cols, _p(cw, _c_u16p), _p(codes, _c_u8p),
+                                      _p(scales, _c_u8p))
+    if rc:
+        raise MemoryError("orc_mxfp4_quant_weight")
+    return codes, scales
+
+
+def mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, nthreads: Optional[int] = None) -> np.ndarray:
+    """f32(exact sum_k A[m][k] B[n][k]) for MXFP4 operands [M, K] and [N, K]."""
+    ac, as_, bc, bs = (_u8(x) for x in (a_codes, a_scales, b_codes, b_scales))
+    M, N, K = ac.shape[0], bc.shape[0], ac.shape[1] * 2
+    assert bc.shape[1] * 2 == K and as_.shape == (M, K // 32) and bs.shape == (N, K // 32)
+    out = np.empty((M, N), np.float32)
+    rc = lib().orc_mxfp4_gemm(M, N, K, _p(ac, _c_u8p), _p(as_, _c_u8p), _p(bc, _c_u8p), _p(bs, _c_u8p),
+                              _p(out, _c_f32p), nthreads or default_threads())
+    if rc:
+        raise ValueError("scale exponents spread beyond the exact accumulator")
+    return out
+
+
+@dataclass
+class MxLayerWeights:
+    """One layer in MXFP4: (codes, scales) of gate (None when non-gated), up and
+    down, the norm weight, the AWQ reciprocal f32(1/s) [H] (None: no AWQ) and
+    the optional AdaRMSNorm modulation."""
+    g: Optional[tuple]
+    u: tuple
+    d: tuple
+    w_norm: np.ndarray
+    inv_awq: Optional[np.ndarray] = None
+    mod: Optional[tuple] = None
+
+    @staticmethod
+    def quantize(w_gate, w_up, w_down, w_norm, awq=None, mod=None) -> "MxLayerWeights":
+        """awq: bf16 [H] per-input-channel scale s (> 0): gate/up weights are
+        quantised as f32(W[i][k] * s[k]) and the activations multiplied by
+        f32(1 / s[k]); the down matrix is not scaled."""
+        s = None if awq is None else _u16(awq)
+        g = None if w_gate is None else mxfp4_quant_weight(w_gate, s)
+        u = mxfp4_quant_weight(w_up, s)
+        d = mxfp4_quant_weight(w_down, None)
+        inv = None
+        if s is not None:
+            inv = (np.float32(1.0) / bf16_to_f32(s).astype(np.float32)).astype(np.float32)
+        m = None if mod is None else (_u16(mod[0]), _u16(mod[1]))
+        return MxLayerWeights(g, u, d, _u16(w_norm), inv, m)
+
+
+def block_mxfp4(r_prev, y_prev, lw: MxLayerWeights, act: int, eps: float, nthreads: Optional[int] = None):
+    """One MXFP4 block -> (r_out, (xq codes, scales), (hq codes, scales), y_out)."""
+    r = _u16(r_prev)
+    M, H = r.shape
+    I = lw.u[0].shape[0]
+    y = None if y_prev is None else _u16(y_prev)
+    r_out = np.empty((M, H), np.uint16)
+    xc = np.empty((M, H // 2), np.uint8)
+    xs = np.empty((M, H // 32), np.uint8)
+    hc = np.empty((M, I // 2), np.uint8)
+    hs = np.empty((M, I // 32), np.uint8)
+    y_out = np.empty((M, H), np.uint16)
+    ms, mh = (None, None) if lw.mod is None else lw.mod
+    gc, gs = (None, None) if lw.g is None else lw.g
+    inv = None if lw.inv_awq is None else np.ascontiguousarray(lw.inv_awq, np.float32)
+    rc = lib().orc_block_mxfp4(M, H, I, act, float(eps), _p(r, _c_u16p), _p(y, _c_u16p), _p(lw.w_norm, _c_u16p),
+                               _p(ms, _c_u16p), _p(mh, _c_u16p), _p(inv, _c_f32p), _p(gc, _c_u8p), _p(gs, _c_u8p),
+                               _p(lw.u[0], _c_u8p), _p(lw.u[1], _c_u8p), _p(lw.d[0], _c_u8p), _p(lw.d[1], _c_u8p),
+                               _p(r_out, _c_u16p), _p(xc, _c_u8p), _p(xs, _c_u8p), _p(hc, _c_u8p), _p(hs, _c_u8p),
+                               _p(y_out, _c_u16p), nthreads or default_threads())
+    if rc:
+        raise RuntimeError("orc_block_mxfp4 failed (%d)" % rc)
+    return r_out, (xc, xs), (hc, hs), y_out
+
+
+@dataclass
+class MxChainResult:
+    r: List[np.ndarray]
+    y: List[Optional[np.ndarray]]
+    xq: List[tuple]
+    hq: List[tuple]
+
+
+def run_chain_mxfp4(layers: Iterable[Callable[[], MxLayerWeights]], act: int, eps: float, r0, y0) -> MxChainResult:
+    """Layer after layer in the pages' order (no calibration: the block scales
+    are taken from the data as it flows)."""
+    res = MxChainResult([_u16(r0)], [None if y0 is None else _u16(y0)], [], [])
+    for get in layers:
+        lw = get()
+        r, xq, hq, y = block_mxfp4(res.r[-1], res.y[-1], lw, act, eps)
+        res.r.append(r)
+        res.y.append(y)
+        res.xq.append(xq)
+        res.hq.append(hq)
+    return res

@@ -15,6 +15,10 @@
  *   - FlashRT architecture doc, component "Calibration": amax per FP8 GEMM
  *     input in a measurement pass, then alpha = act_scale * weight_scale
  *     baked as host scalars;
+ *   - itsolotime article, section 7.2 (the NVFP4 encoder FFN: bf16/fp16
+ *     residual kept at high precision, AWQ pre-scale of the normalised
+ *     activations, 4-bit gate/up and down GEMMs, a gated combine that
+ *     re-quantises to 4 bits), here in the OCP microscaling FP4 format;
  *   - FlashRT architecture doc, component "Kernel library": the fused
  *     residual + norm + quant kernel, and the "qkv split + RoPE" fusion that
  *     follows the fused QKV projection on the attention side (the FusedQKV
@@ -632,4 +636,193 @@ int orc_qkv_epilogue(int M, int nq, int nkv, int hd, const float *A, float alpha
     for (int64_t j = 0; j < (int64_t)nkv * hd; ++j) v[(int64_t)m * nkv * hd + j] = orc_bf16_round(av[j] * alpha);
   }
   return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* MXFP4: the 4-bit FFN variant (itsolotime article section 7.2 describes   */
+/* the NVFP4 form: AWQ pre-scale, low-bit gate/up and down GEMMs, a gated   */
+/* combine that re-quantises to 4 bits, a high-precision residual).  The    */
+/* format is OCP Microscaling MXFP4: blocks of 32 consecutive values along  */
+/* the reduction dimension share one E8M0 scale X = 2^(e - 127); elements   */
+/* are FP4 E2M1 (sign bit 3; exponent bits 2..1, bias 1; mantissa bit 0):   */
+/* magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.                                    */
+/*   e = floor(log2(amax)) - 2 + 127, clamped to [0, 254]; amax = 0: e = 0   */
+/*   element = e2m1(v / X), round to nearest, ties to the even mantissa,     */
+/*   saturating at +-6; the sign bit follows v (so -0 is kept).              */
+/* Packing: element 2i in the low nibble of byte i, 2i+1 in the high one.   */
+/* ------------------------------------------------------------------------ */
+
+double orc_e2m1_decode(uint8_t c) {
+  const int e = (c >> 1) & 3, m = c & 1;
+  const double v = e ? ldexp(1.0 + 0.5 * m, e - 1) : 0.5 * m;
+  return (c & 8) ? -v : v;
+}
+
+/* nearest of the eight magnitudes, ties to the code with mantissa bit 0;
+   from 6 up (where distances to the grid would round together for huge
+   inputs) the largest magnitude */
+uint8_t orc_e2m1_encode(double v) {
+  const double a = fabs(v);
+  int best = 7;
+  double bd = INFINITY;
+  for (int c = 0; c < 8 && a < 6.0; ++c) {
+    const double d = fabs(orc_e2m1_decode((uint8_t)c) - a);
+    if (d < bd || (d == bd && (c & 1) == 0)) {
+      bd = d;
+      best = c;
+    }
+  }
+  return (uint8_t)(best | (signbit(v) ? 8 : 0));
+}
+
+int orc_mx_scale_exp(double amax) {
+  if (!(amax > 0.0)) return 0;
+  int ex;
+  (void)frexp(amax, &ex); /* amax = f * 2^ex, f in [0.5, 1): floor(log2(amax)) = ex - 1 */
+  int e = (ex - 1) - 2 + 127;
+  return e < 0 ? 0 : (e > 254 ? 254 : e);
+}
+
+/* v [rows][cols] (cols % 32 == 0) -> codes [rows][cols/2], scales [rows][cols/32] */
+void orc_mxfp4_quant_rows(const float *v, int64_t rows, int64_t cols, uint8_t *codes, uint8_t *scales) {
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < cols / 32; ++b) {
+      const float *blk = v + r * cols + b * 32;
+      double amax = 0.0;
+      for (int j = 0; j < 32; ++j) amax = fmax(amax, fabs((double)blk[j]));
+      const int e = orc_mx_scale_exp(amax);
+      scales[r * (cols / 32) + b] = (uint8_t)e;
+      for (int j = 0; j < 32; j += 2) {
+        const uint8_t lo = orc_e2m1_encode(ldexp((double)blk[j], 127 - e));
+        const uint8_t hi = orc_e2m1_encode(ldexp((double)blk[j + 1], 127 - e));
+        codes[r * (cols / 2) + b * 16 + j / 2] = (uint8_t)(lo | (hi << 4));
+      }
+    }
+  }
+}
+
+/* Weights: bf16 w [rows][cols] times the bf16 column factor colw[k] (the AWQ */
+/* scale; NULL = 1), an exact product, then MXFP4 along cols.                */
+int orc_mxfp4_quant_weight(const uint16_t *w, int64_t rows, int64_t cols, const uint16_t *colw, uint8_t *codes,
+                           uint8_t *scales) {
+  float *tmp = (float *)malloc(sizeof(float) * (size_t)cols);
+  if (!tmp) return -2;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t k = 0; k < cols; ++k)
+      tmp[k] = orc_bf16_to_f32(w[r * cols + k]) * (colw ? orc_bf16_to_f32(colw[k]) : 1.0f);
+    orc_mxfp4_quant_rows(tmp, 1, cols, codes + r * (cols / 2), scales + r * (cols / 32));
+  }
+  free(tmp);
+  return 0;
+}
+
+/* round v * 2^e (v a 128-bit integer) once to fp32, ties to even */
+static float i128_to_f32(__int128 v, int e) {
+  if (v == 0) return 0.0f;
+  const int neg = v < 0;
+  unsigned __int128 mag = neg ? (unsigned __int128)(-v) : (unsigned __int128)v;
+  int nbits = 0;
+  for (unsigned __int128 t = mag; t; t >>= 1) ++nbits;
+  if (nbits > 24) {
+    const int sh = nbits - 24;
+    unsigned __int128 q = mag >> sh;
+    const unsigned __int128 rem = mag & ((((unsigned __int128)1) << sh) - 1);
+    const unsigned __int128 half = ((unsigned __int128)1) << (sh - 1);
+    if (rem > half || (rem == half && (q & 1))) ++q;
+    mag = q;
+    e += sh;
+  }
+  const double r = ldexp((double)(uint64_t)mag, e); /* < 2^25 * 2^e: exact in double */
+  return (float)(neg ? -r : r);                      /* exact: at most 24 significant bits */
+}
+
+typedef struct {
+  int M, N, K;
+  const uint8_t *ac, *as, *bc, *bs;
+  float *out;
+  int err;
+} mxgemm_ctx;
+
+static int e2m1_twice(uint8_t c) { return (int)lrint(2.0 * orc_e2m1_decode(c)); } /* integer in [-12, 12] */
+
+static void mxgemm_range(void *p, int64_t begin, int64_t end) {
+  mxgemm_ctx *g = (mxgemm_ctx *)p;
+  const int nb = g->K / 32;
+  for (int64_t idx = begin; idx < end; ++idx) {
+    const int m = (int)(idx / g->N), n = (int)(idx % g->N);
+    int emin = 1 << 30, emax = -(1 << 30);
+    for (int b = 0; b < nb; ++b) {
+      const int e = (int)g->as[(int64_t)m * nb + b] + (int)g->bs[(int64_t)n * nb + b];
+      if (e < emin) emin = e;
+      if (e > emax) emax = e;
+    }
+    if (emax - emin > 100) {
+      g->err = 1;
+      g->out[idx] = NAN;
+      continue;
+    }
+    __int128 acc = 0;
+    for (int b = 0; b < nb; ++b) {
+      long S = 0;
+      for (int j = 0; j < 32; ++j) {
+        const int k = b * 32 + j;
+        const uint8_t ca = (g->ac[(int64_t)m * (g->K / 2) + k / 2] >> (4 * (k & 1))) & 15;
+        const uint8_t cb = (g->bc[(int64_t)n * (g->K / 2) + k / 2] >> (4 * (k & 1))) & 15;
+        S += (long)e2m1_twice(ca) * (long)e2m1_twice(cb);
+      }
+      const int e = (int)g->as[(int64_t)m * nb + b] + (int)g->bs[(int64_t)n * nb + b];
+      acc += ((__int128)S) << (e - emin);
+    }
+    /* each product is (2a)(2b)/4 * 2^(ea-127) * 2^(eb-127) */
+    g->out[idx] = i128_to_f32(acc, emin - 254 - 2);
+  }
+}
+
+/* out [M][N] = f32( exact sum_k A[m][k] B[n][k] ) for MXFP4 operands with   */
+/* K along the rows of both.  -1 when a row's scale exponents spread too far */
+/* for the 128-bit accumulator (never for the workloads here).               */
+int orc_mxfp4_gemm(int M, int N, int K, const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *b_codes,
+                   const uint8_t *b_scales, float *out, int nthreads) {
+  if (K % 32) return -1;
+  mxgemm_ctx g = {M, N, K, a_codes, a_scales, b_codes, b_scales, out, 0};
+  parallel_for((int64_t)M * N, nthreads, mxgemm_range, &g);
+  return g.err ? -1 : 0;
+}
+
+/* One MXFP4 block:                                                          */
+/*   r' = bf16(r + y); x = RMSNorm (or AdaRMSNorm) as in the FP8 block;     */
+/*   xs = f32(x * inv_awq[k]) (inv_awq NULL: xs = x);  XQ = MXFP4(xs)        */
+/*   g, u = f32(exact MXFP4 dot products);  h = f32(act(g) * u) (or         */
+/*   gelu_tanh(u));  HQ = MXFP4(h) along I;  y = bf16(f32(exact down sum))  */
+int orc_block_mxfp4(int M, int H, int I, int act, float eps, const uint16_t *r_prev, const uint16_t *y_prev,
+                    const uint16_t *w_norm, const uint16_t *mod_scale, const uint16_t *mod_shift,
+                    const float *inv_awq, const uint8_t *gc, const uint8_t *gs, const uint8_t *uc, const uint8_t *us,
+                    const uint8_t *dc, const uint8_t *ds, uint16_t *r_out, uint8_t *xq_codes, uint8_t *xq_scales,
+                    uint8_t *hq_codes, uint8_t *hq_scales, uint16_t *y_out, int nthreads) {
+  int rc = -2;
+  float *x = (float *)malloc(sizeof(float) * (size_t)M * H);
+  float *Ag = (float *)malloc(sizeof(float) * (size_t)M * I);
+  float *Au = (float *)malloc(sizeof(float) * (size_t)M * I);
+  float *h = (float *)malloc(sizeof(float) * (size_t)M * I);
+  float *Ad = (float *)malloc(sizeof(float) * (size_t)M * H);
+  if (!x || !Ag || !Au || !h || !Ad) goto done;
+  orc_add_rmsnorm_quant(M, H, r_prev, y_prev, w_norm, mod_scale, mod_shift, eps, 1.0f, r_out, x, NULL, nthreads);
+  if (inv_awq)
+    for (int64_t i = 0; i < (int64_t)M * H; ++i) x[i] = x[i] * inv_awq[i % H];
+  orc_mxfp4_quant_rows(x, M, H, xq_codes, xq_scales);
+  rc = -1;
+  if (act != ORC_ACT_GELU_TANH && orc_mxfp4_gemm(M, I, H, xq_codes, xq_scales, gc, gs, Ag, nthreads)) goto done;
+  if (orc_mxfp4_gemm(M, I, H, xq_codes, xq_scales, uc, us, Au, nthreads)) goto done;
+  orc_gateup_epilogue((int64_t)M * I, act, Ag, Au, 1.0f, 1.0f, 1.0f, h, NULL);
+  orc_mxfp4_quant_rows(h, M, I, hq_codes, hq_scales);
+  if (orc_mxfp4_gemm(M, H, I, hq_codes, hq_scales, dc, ds, Ad, nthreads)) goto done;
+  for (int64_t i = 0; i < (int64_t)M * H; ++i) y_out[i] = orc_bf16_round(Ad[i]);
+  rc = 0;
+done:
+  free(x);
+  free(Ag);
+  free(Au);
+  free(h);
+  free(Ad);
+  return rc;
 }
