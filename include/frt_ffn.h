@@ -100,6 +100,25 @@ typedef enum {
  *   conditioning Dense layers) into the slots before a replay, like the
  *   inputs.  Excludes FRT_FLAG_NORM_FUSE and FRT_FLAG_FUSED_NORM. */
 #define FRT_FLAG_ADA_NORM 16u
+/* FRT_FLAG_MXFP4 (itsolotime article, section 7.2: the NVFP4 encoder FFN --
+ *   AWQ pre-scale, 4-bit gate/up and down GEMMs, a gated combine that
+ *   re-quantises to 4 bits, a high-precision residual -- here in the OCP
+ *   MXFP4 format on gfx950's block-scaled FP4 matrix instructions):
+ *   weights, XQ and HQ are FP4 E2M1 codes with one E8M0 exponent e (scale
+ *   2^(e-127)) per 32 values along K; e = floor(log2(amax)) - 2 + 127 per
+ *   block, elements rounded to nearest (ties to the even mantissa) and
+ *   saturated at 6.  No activation scales: frt_calibrate returns
+ *   FRT_ERR_UNSUPPORTED and the forward needs none.  The residual stays bf16.
+ *     K1: x as without the flag, then xs = f32(x * f32(1/s[k])) with the
+ *         layer's AWQ scale s (frt_set_awq; 1 by default), XQ = MXFP4(xs)
+ *     gate/up: weights f32(W[i][k] * s[k]) in MXFP4; g, u fp32-accumulated
+ *         block-scaled products; h = act(g) * u; HQ = MXFP4(h) along I
+ *     down: Y = bf16(fp32-accumulated block-scaled products)
+ *   Requires M <= 64, H and I multiples of 512; excludes the FP8, fused-norm
+ *   and norm-fusion flags.  Slots: each XQ slot holds codes [M][H/2] (two per
+ *   byte, low nibble first) followed by exponents [M][H/32]; HQ likewise with
+ *   I. */
+#define FRT_FLAG_MXFP4 32u
 
 /* Problem description.  Requirements: M >= 1, L >= 1, H and I multiples of
  * 128, H <= 16384, I <= 32768, act in frt_act, eps > 0.  `device` is the HIP
@@ -172,6 +191,21 @@ frt_status frt_quant_weights(frt_plan *plan, int32_t layer, const void *d_w_gate
  * I*H bytes.  Synchronous. */
 frt_status frt_export_weight_codes(const frt_plan *plan, int32_t layer, int32_t which,
                                    void *host_dst);
+
+/* MXFP4 plans: copy layer `layer`'s weight `which` (0 gate, 1 up, 2 down) to
+ * host memory in plain row order: codes [rows][cols/2] (two per byte, low
+ * nibble first) and E8M0 exponents [rows][cols/32] (nn.Linear [out][in]
+ * orientation, K = in along the blocks).  FRT_ERR_STATE for other plans. */
+frt_status frt_export_mxfp4_weights(const frt_plan *plan, int32_t layer, int32_t which, void *host_codes,
+                                    void *host_exponents);
+
+/* MXFP4 plans: set layer `layer`'s AWQ pre-scale from device bf16 [H] (each
+ * finite and > 0; the pages' activation-aware pre-scale, computed by the
+ * caller from its calibration statistics).  The next frt_quant_weights of
+ * the layer multiplies the gate/up weights by it per input column, and K1
+ * multiplies the normalised activations by f32(1/s).  Marks the layer's
+ * weights unset (quantise again after it).  Synchronous. */
+frt_status frt_set_awq(frt_plan *plan, int32_t layer, const void *d_awq, void *stream);
 
 /* Calibration measurement pass (architecture doc, component "Calibration",
  * phase (a); the predict() flow's cache-miss path "run 1 fwd, record amax").

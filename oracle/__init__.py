@@ -114,7 +114,8 @@ def lib():
         L.orc_mx_scale_exp.restype = ctypes.c_int
         L.orc_mxfp4_quant_rows.argtypes = [_c_f32p, ctypes.c_int64, ctypes.c_int64, _c_u8p, _c_u8p]
         L.orc_mxfp4_quant_rows.restype = None
-        L.orc_mxfp4_quant_weight.argtypes = [_c_u16p, ctypes.c_int64, ctypes.c_int64, _c_u16p, _c_u8p, _c_u8p]
+        L.orc_mxfp4_quant_weight.argtypes = [_c_u16p, ctypes.c_int64, ctypes.c_int64, _c_u16p, _c_u8p, _c_u8p,
+                                             ctypes.c_int]
         L.orc_mxfp4_quant_weight.restype = ctypes.c_int
         L.orc_mxfp4_gemm.argtypes = [ctypes.c_int] * 3 + [_c_u8p] * 4 + [_c_f32p, ctypes.c_int]
         L.orc_mxfp4_gemm.restype = ctypes.c_int
@@ -604,7 +605,7 @@ def mxfp4_quant_weight(w_bf16, colw_bf16=None):
     codes = np.empty((rows, cols // 2), np.uint8)
     scales = np.empty((rows, cols // 32), np.uint8)
     rc = lib().orc_mxfp4_quant_weight(_p(w, _c_u16p), rows, cols, _p(cw, _c_u16p), _p(codes, _c_u8p),
-                                      _p(scales, _c_u8p))
+                                      _p(scales, _c_u8p), default_threads())
     if rc:
         raise MemoryError("orc_mxfp4_quant_weight")
     return codes, scales

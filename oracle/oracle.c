@@ -702,18 +702,35 @@ void orc_mxfp4_quant_rows(const float *v, int64_t rows, int64_t cols, uint8_t *c
 }
 
 /* Weights: bf16 w [rows][cols] times the bf16 column factor colw[k] (the AWQ */
-/* scale; NULL = 1), an exact product, then MXFP4 along cols.                */
-int orc_mxfp4_quant_weight(const uint16_t *w, int64_t rows, int64_t cols, const uint16_t *colw, uint8_t *codes,
-                           uint8_t *scales) {
-  float *tmp = (float *)malloc(sizeof(float) * (size_t)cols);
-  if (!tmp) return -2;
-  for (int64_t r = 0; r < rows; ++r) {
-    for (int64_t k = 0; k < cols; ++k)
-      tmp[k] = orc_bf16_to_f32(w[r * cols + k]) * (colw ? orc_bf16_to_f32(colw[k]) : 1.0f);
-    orc_mxfp4_quant_rows(tmp, 1, cols, codes + r * (cols / 2), scales + r * (cols / 32));
+/* scale; NULL = 1), an exact product, then MXFP4 along cols (rows in        */
+/* parallel: each is independent).                                           */
+typedef struct {
+  const uint16_t *w, *colw;
+  int64_t cols;
+  uint8_t *codes, *scales;
+  int err;
+} mxq_ctx;
+
+static void mxq_range(void *p, int64_t begin, int64_t end) {
+  mxq_ctx *c = (mxq_ctx *)p;
+  float *tmp = (float *)malloc(sizeof(float) * (size_t)c->cols);
+  if (!tmp) {
+    c->err = 1;
+    return;
+  }
+  for (int64_t r = begin; r < end; ++r) {
+    for (int64_t k = 0; k < c->cols; ++k)
+      tmp[k] = orc_bf16_to_f32(c->w[r * c->cols + k]) * (c->colw ? orc_bf16_to_f32(c->colw[k]) : 1.0f);
+    orc_mxfp4_quant_rows(tmp, 1, c->cols, c->codes + r * (c->cols / 2), c->scales + r * (c->cols / 32));
   }
   free(tmp);
-  return 0;
+}
+
+int orc_mxfp4_quant_weight(const uint16_t *w, int64_t rows, int64_t cols, const uint16_t *colw, uint8_t *codes,
+                           uint8_t *scales, int nthreads) {
+  mxq_ctx c = {w, colw, cols, codes, scales, 0};
+  parallel_for(rows, nthreads, mxq_range, &c);
+  return c.err ? -2 : 0;
 }
 
 /* round v * 2^e (v a 128-bit integer) once to fp32, ties to even */
@@ -741,9 +758,8 @@ typedef struct {
   const uint8_t *ac, *as, *bc, *bs;
   float *out;
   int err;
+  int twice[16]; /* 2 * decode(code): an integer in [-12, 12] */
 } mxgemm_ctx;
-
-static int e2m1_twice(uint8_t c) { return (int)lrint(2.0 * orc_e2m1_decode(c)); } /* integer in [-12, 12] */
 
 static void mxgemm_range(void *p, int64_t begin, int64_t end) {
   mxgemm_ctx *g = (mxgemm_ctx *)p;
@@ -768,7 +784,7 @@ static void mxgemm_range(void *p, int64_t begin, int64_t end) {
         const int k = b * 32 + j;
         const uint8_t ca = (g->ac[(int64_t)m * (g->K / 2) + k / 2] >> (4 * (k & 1))) & 15;
         const uint8_t cb = (g->bc[(int64_t)n * (g->K / 2) + k / 2] >> (4 * (k & 1))) & 15;
-        S += (long)e2m1_twice(ca) * (long)e2m1_twice(cb);
+        S += (long)g->twice[ca] * (long)g->twice[cb];
       }
       const int e = (int)g->as[(int64_t)m * nb + b] + (int)g->bs[(int64_t)n * nb + b];
       acc += ((__int128)S) << (e - emin);
@@ -784,7 +800,8 @@ static void mxgemm_range(void *p, int64_t begin, int64_t end) {
 int orc_mxfp4_gemm(int M, int N, int K, const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *b_codes,
                    const uint8_t *b_scales, float *out, int nthreads) {
   if (K % 32) return -1;
-  mxgemm_ctx g = {M, N, K, a_codes, a_scales, b_codes, b_scales, out, 0};
+  mxgemm_ctx g = {M, N, K, a_codes, a_scales, b_codes, b_scales, out, 0, {0}};
+  for (int c = 0; c < 16; ++c) g.twice[c] = (int)lrint(2.0 * orc_e2m1_decode((uint8_t)c));
   parallel_for((int64_t)M * N, nthreads, mxgemm_range, &g);
   return g.err ? -1 : 0;
 }

@@ -31,6 +31,7 @@ FRT_FLAG_FUSED_NORM = 2
 FRT_FLAG_FP8_MFMA_GATEUP = 4
 FRT_FLAG_NORM_FUSE = 8
 FRT_FLAG_ADA_NORM = 16
+FRT_FLAG_MXFP4 = 32
 
 _STATUS_NAMES = {0: "FRT_OK", 1: "FRT_ERR_INVALID_ARG", 2: "FRT_ERR_HIP", 3: "FRT_ERR_STATE",
                  4: "FRT_ERR_UNSUPPORTED", 5: "FRT_ERR_WORKSPACE"}
@@ -40,7 +41,7 @@ EXPORTED = [
     "frt_export_weight_codes", "frt_calibrate", "frt_get_scales", "frt_set_act_scales",
     "frt_ffn_io_get", "frt_ffn_forward_range", "frt_ffn_forward", "frt_graph_capture",
     "frt_graph_replay", "frt_ffn_forward_profiled", "frt_ffn_time_kernel", "frt_e4m3_encode_f32",
-    "frt_last_error",
+    "frt_last_error", "frt_export_mxfp4_weights", "frt_set_awq",
     # attention input (include/frt_qkv.h)
     "frt_qkv_workspace_size", "frt_qkv_plan_create", "frt_qkv_plan_destroy", "frt_qkv_quant_weights",
     "frt_qkv_export_weight_codes", "frt_qkv_calibrate", "frt_qkv_get_scales", "frt_qkv_set_act_scale",
@@ -115,6 +116,8 @@ def load(build_if_missing: bool = True):
         "frt_ffn_forward_profiled": [vp, vp, ctypes.POINTER(ctypes.c_float)],
         "frt_ffn_time_kernel": [vp, i32, i32, vp, ctypes.POINTER(ctypes.c_float)],
         "frt_e4m3_encode_f32": [vp, vp, ctypes.c_int64, vp],
+        "frt_export_mxfp4_weights": [vp, i32, i32, vp, vp],
+        "frt_set_awq": [vp, i32, vp, vp],
         "frt_qkv_workspace_size": [ctypes.POINTER(frt_qkv_desc), ctypes.POINTER(sz)],
         "frt_qkv_plan_create": [ctypes.POINTER(frt_qkv_desc), vp, sz, ctypes.POINTER(vp)],
         "frt_qkv_plan_destroy": [vp],
@@ -319,3 +322,15 @@ def frt_qkv_graph_capture(plan: int, stream: int) -> None:
 
 def frt_qkv_graph_replay(plan: int, stream: int) -> None:
     _check(load().frt_qkv_graph_replay(plan, stream))
+
+
+def frt_export_mxfp4_weights(plan: int, layer: int, which: int, rows: int, cols: int):
+    codes = np.empty((rows, cols // 2), dtype=np.uint8)
+    exps = np.empty((rows, cols // 32), dtype=np.uint8)
+    _check(load().frt_export_mxfp4_weights(plan, layer, which, codes.ctypes.data_as(ctypes.c_void_p),
+                                           exps.ctypes.data_as(ctypes.c_void_p)))
+    return codes, exps
+
+
+def frt_set_awq(plan: int, layer: int, d_awq: int, stream: int) -> None:
+    _check(load().frt_set_awq(plan, layer, d_awq, stream))

@@ -26,6 +26,7 @@
 #include "../../include/frt_ffn.h"
 #include "frt_device.h"
 #include "frt_host.h"
+#include "frt_mx.h"
 
 namespace frt {
 hipError_t launch_add_rmsnorm_quant(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*,
@@ -47,6 +48,15 @@ hipError_t launch_gemv_gateup_mt(int, const uint8_t*, const uint8_t*, uint8_t*, 
 hipError_t launch_gemv_down_mt(const uint8_t*, const uint8_t*, uint16_t*, float*, int, int, int, int, int, bool,
                                float, hipStream_t);
 bool gemv_fused_supported(int, int, int);
+hipError_t launch_add_rmsnorm_mx(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*, const float*,
+                                 uint16_t*, uint8_t*, uint8_t*, int, int, float, hipStream_t, const float*, int, float,
+                                 uint16_t*);
+hipError_t launch_quant_mx(const uint16_t*, uint8_t*, uint8_t*, int, int, int, const uint16_t*, hipStream_t);
+hipError_t launch_gemv_gateup_mx(int, const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, uint8_t*,
+                                 uint8_t*, int, int, int, int, hipStream_t);
+hipError_t launch_gemv_down_mx(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, uint16_t*, float*, int,
+                               int, int, int, int, hipStream_t);
+int gemv_mx_max_waves(int M);
 hipError_t launch_gemv_gateup_fused(int, const uint16_t*, const uint16_t*, const float*, int, float, uint16_t*,
                                     const uint16_t*, uint16_t*, uint8_t*, const uint8_t*, uint8_t*, int, int, int, int,
                                     float, float, float, float, float, hipStream_t);
@@ -134,6 +144,10 @@ struct Layout {
   int k_dn;        // GEMV: K splits of the down GEMV (workgroups per 16 output columns)
   int split_dn;    // K splits of the down projection, either path (> 1: fp32 partials)
   bool gemv_mt;    // 16 < M <= 64 on the multi-tile GEMVs
+  bool mx;         // MXFP4 plan
+  size_t wgu_sc, wd_sc;        // MXFP4: offset of the exponents inside a layer's weights
+  size_t xq_stride, hq_stride; // bytes per XQ / HQ slot
+  size_t awq, inv_awq;         // MXFP4: AWQ scale bf16 [L][H], its reciprocal fp32 [L][H]
   int cfg_gu, cfg_dn;  // GEMM tile configurations
   bool mm_gu, mm_dn;   // GEMM runs on the LDS-DMA f16 kernel (k_mm) rather than k_gemm
 };
@@ -147,7 +161,13 @@ bool desc_ok(const frt_ffn_desc* d) {
   if (d->act < FRT_ACT_GEGLU_TANH || d->act > FRT_ACT_GELU_TANH) return false;
   if (!(d->eps > 0.0f) || !std::isfinite(d->eps)) return false;
   if ((d->flags & ~(uint32_t)(FRT_FLAG_FP8_MFMA_DOWN | FRT_FLAG_FUSED_NORM | FRT_FLAG_FP8_MFMA_GATEUP |
-                              FRT_FLAG_NORM_FUSE | FRT_FLAG_ADA_NORM)) != 0u || d->device < 0)
+                              FRT_FLAG_NORM_FUSE | FRT_FLAG_ADA_NORM | FRT_FLAG_MXFP4)) != 0u || d->device < 0)
+    return false;
+  // MXFP4: the GEMV path (M <= 64), K dimensions in whole groups of four
+  // 128-blocks (one exponent dword per lane), no FP8 or fused-norm options
+  if ((d->flags & FRT_FLAG_MXFP4) &&
+      (d->M > 64 || d->H % 512 || d->I % 512 ||
+       (d->flags & (FRT_FLAG_FP8_MFMA_DOWN | FRT_FLAG_FP8_MFMA_GATEUP | FRT_FLAG_FUSED_NORM | FRT_FLAG_NORM_FUSE))))
     return false;
   // AdaRMSNorm replaces the norm weight: no folding of it, and no fused
   // decode prologue (which applies the weight)
@@ -252,25 +272,47 @@ Layout make_layout(const frt_ffn_desc& d) {
     off = align256(off + bytes);
     return at;
   };
-  lo.wgu_layer = align256(npk * H);
+  lo.mx = (d.flags & FRT_FLAG_MXFP4) != 0u;
+  if (lo.mx) {
+    // codes (half a byte per weight) then one exponent per 32 weights
+    lo.wgu_sc = align256(npk * H / 2);
+    lo.wgu_layer = lo.wgu_sc + align256(npk * H / 32);
+    lo.wd_sc = align256(H * I / 2);
+    lo.wd_layer = lo.wd_sc + align256(H * I / 32);
+    lo.xq_stride = align256(M * H / 2 + M * H / 32);
+    lo.hq_stride = align256(M * I / 2 + M * I / 32);
+  } else {
+    lo.wgu_layer = align256(npk * H);
+    lo.wd_layer = align256(H * I);
+    lo.xq_stride = M * H;
+    lo.hq_stride = M * I;
+  }
   lo.wgu = take(lo.wgu_layer * L);
-  lo.wd_layer = align256(H * I);
   lo.wd = take(lo.wd_layer * L);
   lo.wn = take(L * H * 2);
   lo.r = take((L + 1) * M * H * 2);
   lo.y = take((L + 1) * M * H * 2);
-  lo.xq = take(L * M * H);
-  lo.hq = take(L * M * I);
+  lo.xq = take(L * lo.xq_stride);
+  lo.hq = take(L * lo.hq_stride);
+  lo.awq = take(lo.mx ? L * H * 2 : 256);
+  lo.inv_awq = take(lo.mx ? L * H * 4 : 256);
   lo.z = take(M * H * 2);
   lo.mod = take((d.flags & FRT_FLAG_ADA_NORM) ? L * 2 * H * 2 : 256);
 
   size_t part = 0, words = 1;
   lo.gemv_mt = d.M > kGemvMaxM && d.M <= std::min(kGemvMtMaxM, env_int("FRT_GEMV_MT_MAX_M", kGemvMtMaxM));
-  if (d.M <= kGemvMaxM || lo.gemv_mt) {
+  if (d.M <= kGemvMaxM || lo.gemv_mt || lo.mx) {
     lo.s_gu = gemv_waves((int)(I / 16), (int)(H / 128), "FRT_GEMV_WAVES_GATEUP", 6144);
     lo.k_dn = gemv_down_splits((int)(H / 16), (int)(I / 128));
     lo.s_dn = gemv_waves((int)(H / 16) * lo.k_dn, (int)(I / 128) / lo.k_dn, "FRT_GEMV_WAVES_DOWN", 4096);
-    if (lo.gemv_mt) {
+    if (lo.mx) {
+      // MXFP4 GEMVs: 4, 8 or 16 waves, fewer for more row tiles (LDS)
+      const int wmax = gemv_mx_max_waves(d.M);
+      lo.s_gu = std::min(wmax, std::max(4, lo.s_gu));
+      lo.s_dn = std::min(wmax, std::max(4, lo.s_dn));
+      lo.s_gu = lo.s_gu >= 16 ? 16 : (lo.s_gu >= 8 ? 8 : 4);
+      lo.s_dn = lo.s_dn >= 16 ? 16 : (lo.s_dn >= 8 ? 8 : 4);
+    } else if (lo.gemv_mt) {
       // the multi-tile kernels take 4 or 8 waves (at least one per row tile)
       lo.s_gu = lo.s_gu >= 8 ? 8 : 4;
       lo.s_dn = lo.s_dn >= 8 ? 8 : 4;
@@ -318,8 +360,16 @@ struct frt_plan {
   size_t mh() const { return (size_t)d.M * d.H; }
   uint16_t* r(int l) const { return reinterpret_cast<uint16_t*>(ws + lo.r) + (size_t)l * mh(); }
   uint16_t* y(int l) const { return reinterpret_cast<uint16_t*>(ws + lo.y) + (size_t)l * mh(); }
-  uint8_t* xq(int l) const { return ws + lo.xq + (size_t)l * mh(); }
-  uint8_t* hq(int l) const { return ws + lo.hq + (size_t)l * d.M * d.I; }
+  uint8_t* xq(int l) const { return ws + lo.xq + (size_t)l * lo.xq_stride; }
+  uint8_t* hq(int l) const { return ws + lo.hq + (size_t)l * lo.hq_stride; }
+  // MXFP4: exponents after the codes of a slot / a layer's weights
+  uint8_t* xs(int l) const { return xq(l) + mh() / 2; }
+  uint8_t* hs(int l) const { return hq(l) + (size_t)d.M * d.I / 2; }
+  uint8_t* wgu_s(int l) const { return wgu(l) + lo.wgu_sc; }
+  uint8_t* wd_s(int l) const { return wd(l) + lo.wd_sc; }
+  uint16_t* awq(int l) const { return reinterpret_cast<uint16_t*>(ws + lo.awq) + (size_t)l * d.H; }
+  float* inv_awq(int l) const { return reinterpret_cast<float*>(ws + lo.inv_awq) + (size_t)l * d.H; }
+  bool mx() const { return lo.mx; }
   uint16_t* z() const { return reinterpret_cast<uint16_t*>(ws + lo.z); }
   bool ada() const { return (d.flags & FRT_FLAG_ADA_NORM) != 0u; }
   bool norm_fuse() const { return (d.flags & FRT_FLAG_NORM_FUSE) != 0u; }
@@ -339,6 +389,7 @@ struct frt_plan {
     return d.M <= kGemvMaxM && (d.flags & FRT_FLAG_FUSED_NORM) != 0u && gemv_fused_supported(d.M, d.H, lo.s_gu);
   }
   bool act_scales_set() const {
+    if (mx()) return true;  // MXFP4 takes its block scales from the data
     for (int l = 0; l < d.L; ++l)
       if (!(s_x[l] > 0.0f) || !(s_h[l] > 0.0f)) return false;
     return true;
@@ -424,6 +475,10 @@ frt_status frt_ffn_plan_create(const frt_ffn_desc* desc, void* d_workspace, size
   hipError_t e = hipMemset(p->ws + lo.cnt, 0, 2 * lo.cnt_words * 4);
   if (e == hipSuccess) e = hipMemset(p->y(0), 0, p->mh() * 2);
   if (e == hipSuccess && p->ada()) e = hipMemset(p->ws + lo.mod, 0, (size_t)desc->L * 2 * desc->H * 2);
+  if (e == hipSuccess && lo.mx)  // AWQ scale 1 and reciprocal 1 until set
+    e = hipMemsetD16(reinterpret_cast<hipDeviceptr_t>(p->ws + lo.awq), 0x3F80u, (size_t)desc->L * desc->H);
+  if (e == hipSuccess && lo.mx)
+    e = hipMemsetD32(reinterpret_cast<hipDeviceptr_t>(p->ws + lo.inv_awq), 0x3F800000, (size_t)desc->L * desc->H);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     delete p;
@@ -478,6 +533,27 @@ frt_status frt_quant_weights(frt_plan* p, int32_t layer, const void* d_w_gate, c
   const int H = p->d.H, I = p->d.I;
   float sg = 1.0f, su = 1.0f, sd = 1.0f;
   frt_status st;
+  if (p->mx()) {
+    // MXFP4: gate/up times the layer's AWQ scale per input column, then 32-blocks
+    const uint16_t* aw = p->awq(layer);
+    if (p->gated) {
+      KERNEL_CHECK(launch_quant_mx(static_cast<const uint16_t*>(d_w_gate), p->wgu(layer), p->wgu_s(layer), I, H, 1, aw, s),
+                   "quant_mx");
+      KERNEL_CHECK(launch_quant_mx(static_cast<const uint16_t*>(d_w_up), p->wgu(layer), p->wgu_s(layer), I, H, 2, aw, s),
+                   "quant_mx");
+    } else {
+      KERNEL_CHECK(launch_quant_mx(static_cast<const uint16_t*>(d_w_up), p->wgu(layer), p->wgu_s(layer), I, H, 0, aw, s),
+                   "quant_mx");
+    }
+    KERNEL_CHECK(launch_quant_mx(static_cast<const uint16_t*>(d_w_down), p->wd(layer), p->wd_s(layer), H, I, 0, nullptr,
+                                 s),
+                 "quant_mx");
+    HIP_CHECK(hipMemcpyAsync(p->wn(layer), d_norm_w, (size_t)H * 2, hipMemcpyDeviceToDevice, s));
+    HIP_CHECK(hipStreamSynchronize(s));
+    p->w_set[layer] = 1;
+    p->mark_stale();
+    return FRT_OK;
+  }
   // norm fusion folds the RMSNorm weight into the gate/up matrices per input
   // column and normalises with a unit weight
   const void* fold = p->norm_fuse() ? d_norm_w : nullptr;
@@ -507,6 +583,7 @@ frt_status frt_export_weight_codes(const frt_plan* p, int32_t layer, int32_t whi
   if (which < 0 || which > 2 || (which == 0 && !p->gated))
     return fail(FRT_ERR_INVALID_ARG, "frt_export_weight_codes: bad tensor index %d", which);
   if (!p->w_set[layer]) return fail(FRT_ERR_STATE, "frt_export_weight_codes: layer %d not quantised", layer);
+  if (p->mx()) return fail(FRT_ERR_STATE, "frt_export_weight_codes: MXFP4 plan (use frt_export_mxfp4_weights)");
   DeviceGuard g(p->d.device);
   HIP_CHECK(g.err);
   const uint32_t H = p->d.H, I = p->d.I;
@@ -531,10 +608,76 @@ frt_status frt_export_weight_codes(const frt_plan* p, int32_t layer, int32_t whi
   return FRT_OK;
 }
 
+frt_status frt_export_mxfp4_weights(const frt_plan* p, int32_t layer, int32_t which, void* host_codes,
+                                    void* host_exponents) {
+  if (!p || !host_codes || !host_exponents) return fail(FRT_ERR_INVALID_ARG, "frt_export_mxfp4_weights: NULL argument");
+  if (!p->mx()) return fail(FRT_ERR_STATE, "frt_export_mxfp4_weights: not an MXFP4 plan");
+  if (layer < 0 || layer >= p->d.L) return fail(FRT_ERR_INVALID_ARG, "frt_export_mxfp4_weights: layer out of range");
+  if (which < 0 || which > 2 || (which == 0 && !p->gated))
+    return fail(FRT_ERR_INVALID_ARG, "frt_export_mxfp4_weights: bad tensor index %d", which);
+  if (!p->w_set[layer]) return fail(FRT_ERR_STATE, "frt_export_mxfp4_weights: layer %d not quantised", layer);
+  DeviceGuard g(p->d.device);
+  HIP_CHECK(g.err);
+  const uint32_t H = p->d.H, I = p->d.I;
+  const bool down = which == 2;
+  const uint32_t N = down ? H : I, K = down ? I : H, KB = K / 128;
+  const uint32_t rows_packed = down ? H : (p->gated ? 2 * I : I);
+  const size_t code_bytes = (size_t)rows_packed * K / 2, sc_bytes = (size_t)rows_packed * K / 32;
+  std::vector<uint8_t> tc, ts;
+  try {
+    tc.resize(code_bytes);
+    ts.resize(sc_bytes);
+  } catch (...) {
+    return fail(FRT_ERR_INVALID_ARG, "frt_export_mxfp4_weights: out of host memory");
+  }
+  HIP_CHECK(hipMemcpy(tc.data(), down ? p->wd(layer) : p->wgu(layer), code_bytes, hipMemcpyDeviceToHost));
+  HIP_CHECK(hipMemcpy(ts.data(), down ? p->wd_s(layer) : p->wgu_s(layer), sc_bytes, hipMemcpyDeviceToHost));
+  uint8_t* dc = static_cast<uint8_t*>(host_codes);
+  uint8_t* dsc = static_cast<uint8_t*>(host_exponents);
+  for (uint32_t n = 0; n < N; ++n) {
+    const uint32_t pr = down || !p->gated ? n : (which == 0 ? gate_row(n) : up_row_gated(n));
+    for (uint32_t b = 0; b < K / 32; ++b) {
+      const uint32_t kb = b >> 2, lane = (pr & 15u) + 16u * (b & 3u);
+      memcpy(dc + (size_t)n * (K / 2) + (size_t)b * 16, tc.data() + mx_code_off(pr, kb, lane, KB), 16);
+      dsc[(size_t)n * (K / 32) + b] = ts[mx_scale_off(pr, kb, lane, KB)];
+    }
+  }
+  return FRT_OK;
+}
+
+frt_status frt_set_awq(frt_plan* p, int32_t layer, const void* d_awq, void* stream) {
+  if (!p || !d_awq) return fail(FRT_ERR_INVALID_ARG, "frt_set_awq: NULL argument");
+  if (!p->mx()) return fail(FRT_ERR_UNSUPPORTED, "frt_set_awq: AWQ pre-scale needs an MXFP4 plan");
+  if (layer < 0 || layer >= p->d.L) return fail(FRT_ERR_INVALID_ARG, "frt_set_awq: layer %d out of range", layer);
+  DeviceGuard g(p->d.device);
+  HIP_CHECK(g.err);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int H = p->d.H;
+  std::vector<uint16_t> sb(H);
+  std::vector<float> inv(H);
+  HIP_CHECK(hipMemcpyAsync(sb.data(), d_awq, (size_t)H * 2, hipMemcpyDeviceToHost, s));
+  HIP_CHECK(hipStreamSynchronize(s));
+  for (int k = 0; k < H; ++k) {
+    uint32_t u = (uint32_t)sb[k] << 16;
+    float v;
+    memcpy(&v, &u, 4);
+    if (!std::isfinite(v) || !(v > 0.0f))
+      return fail(FRT_ERR_INVALID_ARG, "frt_set_awq: scale %d is not finite and positive", k);
+    inv[k] = 1.0f / v;  // f32(1 / s), rounded once
+  }
+  HIP_CHECK(hipMemcpyAsync(p->awq(layer), sb.data(), (size_t)H * 2, hipMemcpyHostToDevice, s));
+  HIP_CHECK(hipMemcpyAsync(p->inv_awq(layer), inv.data(), (size_t)H * 4, hipMemcpyHostToDevice, s));
+  HIP_CHECK(hipStreamSynchronize(s));
+  p->w_set[layer] = 0;  // the layer's weights must be quantised (again) with this scale
+  p->mark_stale();
+  return FRT_OK;
+}
+
 frt_status frt_calibrate(frt_plan* p, const void* const* d_r_batches, const void* const* d_y_batches,
                          int32_t nbatch, int32_t rows, int32_t layer_begin, int32_t layer_end,
                          void* stream) {
   if (!p || !d_r_batches) return fail(FRT_ERR_INVALID_ARG, "frt_calibrate: NULL argument");
+  if (p->mx()) return fail(FRT_ERR_UNSUPPORTED, "frt_calibrate: an MXFP4 plan takes its block scales from the data");
   if (nbatch < 1 || rows < 1 || rows > p->d.M)
     return fail(FRT_ERR_INVALID_ARG, "frt_calibrate: nbatch %d rows %d (1..%d)", nbatch, rows, p->d.M);
   if (layer_begin < 0 || layer_end > p->d.L || layer_begin >= layer_end)
@@ -617,8 +760,8 @@ frt_status frt_ffn_io_get(const frt_plan* p, frt_ffn_io* out) {
   out->hq_slots = p->hq(0);
   out->z_out = p->z();
   out->stride_rh = p->mh() * 2;
-  out->stride_xq = p->mh();
-  out->stride_hq = (size_t)p->d.M * p->d.I;
+  out->stride_xq = p->lo.xq_stride;
+  out->stride_hq = p->lo.hq_stride;
   out->mod_slots = p->ada() ? p->ws + p->lo.mod : nullptr;
   out->stride_mod = (size_t)2 * p->d.H * 2;
   return FRT_OK;
@@ -638,6 +781,23 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
   const float inv_x = 1.0f / s_x, inv_h = 1.0f / s_h;
   const float a_g = s_x * p->s_g[l], a_u = s_x * p->s_u[l], a_d = s_h * p->s_d[l];
   const bool fused = p->fused_norm();
+  if (p->mx()) {
+    if (which == 0) {
+      const float* yp = (y_in_partials && l > 0) ? p->part() : nullptr;
+      KERNEL_CHECK(launch_add_rmsnorm_mx(p->r(l), p->y(l), p->wn(l), p->mod(l), p->inv_awq(l), p->r(l + 1), p->xq(l),
+                                         p->xs(l), M, H, p->d.eps, s, yp, p->lo.split_dn, 1.0f, p->y(l)),
+                   "add_rmsnorm_mx");
+    } else if (which == 1) {
+      KERNEL_CHECK(launch_gemv_gateup_mx(p->d.act, p->xq(l), p->xs(l), p->wgu(l), p->wgu_s(l), p->hq(l), p->hs(l), M,
+                                         H, I, p->lo.s_gu, s),
+                   "gemv_gateup_mx");
+    } else {
+      KERNEL_CHECK(launch_gemv_down_mx(p->hq(l), p->hs(l), p->wd(l), p->wd_s(l), p->y(l + 1), p->part(), M, I, H,
+                                       p->lo.s_dn, p->lo.k_dn, s),
+                   "gemv_down_mx");
+    }
+    return FRT_OK;
+  }
   if (which == 0) {
     if (!fused) {
       const float* yp = nullptr;
@@ -708,7 +868,7 @@ static frt_status forward_range(frt_plan* p, int lb, int le, hipStream_t s,
     }
     if (e) HIP_CHECK(hipEventRecord(e[3], s));
   }
-  const float a_last = p->s_h[le - 1] * p->s_d[le - 1];
+  const float a_last = p->mx() ? 1.0f : p->s_h[le - 1] * p->s_d[le - 1];
   if (le == L)
     KERNEL_CHECK(launch_residual_add(p->r(L), p->y(L), p->z(), p->mh(), s, split ? p->part() : nullptr,
                                      p->lo.split_dn, a_last), "residual_add");

@@ -1,0 +1,57 @@
+// frt_mx.h -- MXFP4 element and block-scale conversions on the device.
+//
+// OCP Microscaling MXFP4 (the 4-bit FFN variant modelled on the NVFP4 encoder
+// FFN of the itsolotime article, section 7.2): blocks of 32 values along the
+// reduction dimension share one E8M0 exponent e (scale 2^(e-127)); elements
+// are FP4 E2M1 codes (sign bit 3; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).
+//   e = floor(log2(amax)) - 2 + 127 clamped to [0, 254] (0 for amax == 0)
+//   code = E2M1(v * 2^(127-e)), round to nearest with ties to the even
+//   mantissa, saturating at 6; the sign bit follows v
+// Packing: element 2i in the low nibble of byte i.
+#pragma once
+#include "frt_device.h"
+
+namespace frt {
+
+// Packed MXFP4 weights (k_mx.hip): codes 1 KiB per (16-row group, 128-K
+// block), lane l's 16 bytes = row l%16, K sub-block l/16; exponents 64 lanes
+// x 4 bytes per (group, four K blocks), byte j = K block 4*kb4 + j.
+__host__ __device__ __forceinline__ size_t mx_code_off(uint32_t prow, uint32_t kb, uint32_t lane, uint32_t KB) {
+  return (((size_t)(prow >> 4) * KB + kb) * 64 + lane) * 16;
+}
+__host__ __device__ __forceinline__ size_t mx_scale_off(uint32_t prow, uint32_t kb, uint32_t lane, uint32_t KB) {
+  return (((size_t)(prow >> 4) * (KB >> 2) + (kb >> 2)) * 64 + lane) * 4 + (kb & 3);
+}
+
+__device__ __forceinline__ int mx_block_exp(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  const int e = ilogbf(amax) - 2 + 127;
+  return e < 0 ? 0 : (e > 254 ? 254 : e);
+}
+
+// E2M1 code of v (already divided by the block scale): the decision points
+// are the midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 between neighbouring
+// magnitudes; at a midpoint the neighbour with mantissa bit 0 wins (0.25 ->
+// 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4).
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = __builtin_fabsf(v);
+  const uint32_t c = a <= 0.25f ? 0u
+                     : a < 0.75f ? 1u
+                     : a <= 1.25f ? 2u
+                     : a < 1.75f ? 3u
+                     : a <= 2.5f ? 4u
+                     : a < 3.5f ? 5u
+                     : a <= 5.0f ? 6u
+                                 : 7u;
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// eight values of one 32-block (scale exponent e) -> one dword of codes
+__device__ __forceinline__ uint32_t mx_pack8(const float x[8], int e) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w |= e2m1_code(ldexpf(x[j], 127 - e)) << (4 * j);
+  return w;
+}
+
+}  // namespace frt

@@ -1,0 +1,351 @@
+// k_mx.hip -- the MXFP4 form of the FFN block's two GEMMs (M <= 64) and the
+// packing of its weights.
+//
+// itsolotime article, section 7.2 (the NVFP4 encoder FFN: AWQ pre-scaled
+// activations, 4-bit gate/up and down GEMMs, a gated combine that
+// re-quantises to 4 bits, a high-precision residual); the format here is OCP
+// MXFP4 (frt_mx.h) on gfx950's block-scaled FP4 matrix instructions.
+//
+// Packed weights.  Codes: 1 KiB per (16-row group, 128-K block), lane l's 16
+// bytes at l*16 hold row l%16, K values (l/16)*32 .. +32 (two per byte, low
+// nibble first) -- exactly the operand of v_mfma_scale_f32_16x16x128_f8f6f4
+// with FP4 inputs.  Scales: per (group, four K blocks) 64 lanes x 4 bytes,
+// byte j of lane l = exponent of row l%16, K block 4*kb4 + j, sub-block l/16
+// (mx_code_off / mx_scale_off in frt_mx.h).  Gate and up groups interleave as
+// in the FP8 layout (group 2i gate, 2i + 1 up).
+//
+// Products: one scaled MFMA multiplies 16 activation rows by 16 weight rows
+// over 128 K values with each lane's E8M0 scales applied per 32-block; within
+// an instruction the FP4 products are exact and the sum is accurate to an
+// fp32 rounding (measured), across instructions the accumulator is fp32.
+#include "frt_mx.h"
+
+namespace frt {
+
+enum { MX_GEGLU = 0, MX_SWIGLU = 1, MX_GELU = 2 };
+
+template <int ACT>
+__device__ __forceinline__ float mx_gated(float g, float u) {
+  if (ACT == MX_GELU) return gelu_tanh_f32(u);
+  const float a = (ACT == MX_SWIGLU) ? silu_f32(g) : gelu_tanh_f32(g);
+  return a * u;
+}
+
+// One thread per (row n, 32-block b) of src [N][K] bf16 (times colw[k] when
+// given, an exact product): block exponent, 32 codes into the packed layout.
+// mode 0: packed row n, 1: gate row, 2: up row (gated layout).
+__global__ __launch_bounds__(256) void k_quant_mx(const uint16_t* __restrict__ src, uint8_t* __restrict__ codes,
+                                                  uint8_t* __restrict__ scales, int N, int K, int mode,
+                                                  const uint16_t* __restrict__ colw) {
+  const size_t nb = (size_t)K / 32;
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)N * nb) return;
+  const int n = (int)(idx / nb), b = (int)(idx % nb);
+  const uint4* sp = reinterpret_cast<const uint4*>(src + (size_t)n * K + (size_t)b * 32);
+  float v[32];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 a = sp[q];
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * q + 2 * j] = bf16_lo(w[j]);
+      v[8 * q + 2 * j + 1] = bf16_hi(w[j]);
+    }
+  }
+  if (colw) {
+    const uint4* cp = reinterpret_cast<const uint4*>(colw + (size_t)b * 32);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 a = cp[q];
+      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * q + 2 * j] = v[8 * q + 2 * j] * bf16_lo(w[j]);
+        v[8 * q + 2 * j + 1] = v[8 * q + 2 * j + 1] * bf16_hi(w[j]);
+      }
+    }
+  }
+  float am = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) am = __builtin_fmaxf(am, __builtin_fabsf(v[j]));
+  const int e = mx_block_exp(am);
+  uint32_t out[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) out[q] = mx_pack8(v + 8 * q, e);
+  const uint32_t prow = mode == 0 ? (uint32_t)n : (mode == 1 ? gate_row((uint32_t)n) : up_row_gated((uint32_t)n));
+  const uint32_t KB = (uint32_t)K / 128, kb = (uint32_t)b >> 2, lane = (prow & 15u) + 16u * ((uint32_t)b & 3u);
+  *reinterpret_cast<uint4*>(codes + mx_code_off(prow, kb, lane, KB)) = make_uint4(out[0], out[1], out[2], out[3]);
+  scales[mx_scale_off(prow, kb, lane, KB)] = (uint8_t)e;
+}
+
+hipError_t launch_quant_mx(const uint16_t* src, uint8_t* codes, uint8_t* scales, int N, int K, int mode,
+                           const uint16_t* colw, hipStream_t s) {
+  if (K % 512) return hipErrorInvalidValue;
+  const size_t n = (size_t)N * (K / 32);
+  hipLaunchKernelGGL(k_quant_mx, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, codes, scales, N, K, mode,
+                     colw);
+  return hipGetLastError();
+}
+
+typedef unsigned v4u_mx __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v8i mx_w16(const uint8_t* p) {
+  const v4u_mx a = __builtin_nontemporal_load(reinterpret_cast<const v4u_mx*>(p));
+  v8i r;
+  r[0] = (int)a[0]; r[1] = (int)a[1]; r[2] = (int)a[2]; r[3] = (int)a[3];
+  r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
+  return r;
+}
+__device__ __forceinline__ v8i mx_x16(const uint8_t* p, bool has) {
+  uint4 a = make_uint4(0, 0, 0, 0);
+  if (has) a = *reinterpret_cast<const uint4*>(p);
+  v8i r;
+  r[0] = (int)a.x; r[1] = (int)a.y; r[2] = (int)a.z; r[3] = (int)a.w;
+  r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
+  return r;
+}
+__device__ __forceinline__ v4f mx_mfma(v8i a, int sa, v8i b, int sb, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
+}
+
+// Activation row pointers of tile t: codes [M][K/2], exponents [M][K/32].
+struct MxRows {
+  const uint8_t* c;
+  const uint8_t* s;
+  bool has;
+};
+
+// Gate/up: one workgroup per 32 intermediate columns (packed groups 4P..4P+3
+// = gate 2P, up 2P, gate 2P+1, up 2P+1), W waves splitting the K blocks, MT
+// activation tiles of 16 rows.  Epilogue (wave t < MT, tile t): h for 32
+// columns of each row, the block exponent from the 16 lanes of that row, two
+// codes per byte (the even lane writes), exponent from lane 0 of the row.
+template <int ACT, int W, int MT>
+__global__ __launch_bounds__(W * 64) void k_gemv_gateup_mx(const uint8_t* __restrict__ xc,
+                                                           const uint8_t* __restrict__ xs,
+                                                           const uint8_t* __restrict__ wc,
+                                                           const uint8_t* __restrict__ ws, uint8_t* __restrict__ hc,
+                                                           uint8_t* __restrict__ hs, int M, int K, int I) {
+  constexpr bool GATED = ACT != MX_GELU;
+  constexpr int NA = GATED ? 4 : 2;  // accumulators per tile
+  static_assert(W >= MT, "one wave per tile finishes the epilogue");
+  __shared__ v4f red[W][MT][NA][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int P = blockIdx.x;
+  const int KB = K >> 7;
+  const int kb0 = wave * KB / W, kb1 = (wave + 1) * KB / W;
+  const int row = lane & 15, q = lane >> 4;
+  // packed groups of this workgroup (gated: g0 u0 g1 u1; plain: u0 u1)
+  uint32_t grp[NA];
+#pragma unroll
+  for (int a = 0; a < NA; ++a) grp[a] = (uint32_t)(NA * P + a);
+  MxRows xr[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int m = 16 * t + row;
+    xr[t].has = m < M;
+    const int mm = xr[t].has ? m : 0;
+    xr[t].c = xc + (size_t)mm * (K / 2) + q * 16;
+    xr[t].s = xs + (size_t)mm * (K / 32) + q;
+  }
+  v4f acc[MT][NA];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int a = 0; a < NA; ++a) acc[t][a] = v4f{0, 0, 0, 0};
+
+  for (int kb = kb0; kb < kb1; ++kb) {
+    v8i wv[NA];
+    int wsc[NA];
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+      wv[a] = mx_w16(wc + mx_code_off(grp[a] * 16, kb, lane, KB));
+      const uint32_t d = *reinterpret_cast<const uint32_t*>(ws + mx_scale_off(grp[a] * 16, kb & ~3, lane, KB));
+      wsc[a] = (int)((d >> (8 * (kb & 3))) & 255u);
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const v8i xv = mx_x16(xr[t].c + (size_t)kb * 64, xr[t].has);
+      const int xsc = xr[t].has ? (int)xr[t].s[kb * 4] : 127;
+#pragma unroll
+      for (int a = 0; a < NA; ++a) acc[t][a] = mx_mfma(xv, xsc, wv[a], wsc[a], acc[t][a]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int a = 0; a < NA; ++a) red[wave][t][a][lane] = acc[t][a];
+  __syncthreads();
+  if (wave >= MT) return;
+  const int t = wave;
+  v4f f[NA];
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
+    f[a] = red[0][t][a][lane];
+#pragma unroll
+    for (int v = 1; v < W; ++v) f[a] += red[v][t][a][lane];
+  }
+  // lane holds rows m = 16t + 4q + r, columns 32P + row and 32P + 16 + row
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = 16 * t + 4 * q + r;
+    const float h0 = GATED ? mx_gated<ACT>(f[0][r], f[1][r]) : mx_gated<ACT>(0.0f, f[0][r]);
+    const float h1 = GATED ? mx_gated<ACT>(f[2][r], f[3][r]) : mx_gated<ACT>(0.0f, f[1][r]);
+    float am = __builtin_fmaxf(__builtin_fabsf(h0), __builtin_fabsf(h1));
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) am = __builtin_fmaxf(am, __shfl_xor(am, o, 64));
+    const int e = mx_block_exp(am);
+    const uint32_t c0 = e2m1_code(ldexpf(h0, 127 - e)), c1 = e2m1_code(ldexpf(h1, 127 - e));
+    const uint32_t p0 = (uint32_t)__shfl_xor((int)c0, 1, 64), p1 = (uint32_t)__shfl_xor((int)c1, 1, 64);
+    if (m < M && (row & 1) == 0) {
+      uint8_t* dst = hc + (size_t)m * (I / 2) + (size_t)P * 16 + (row >> 1);
+      dst[0] = (uint8_t)(c0 | (p0 << 4));
+      dst[8] = (uint8_t)(c1 | (p1 << 4));
+      if (row == 0) hs[(size_t)m * (I / 32) + P] = (uint8_t)e;
+    }
+  }
+}
+
+// Down: one workgroup per 16 output columns and K split (gridDim.y), W waves
+// splitting the split's K blocks, MT tiles.  One split: bf16 Y; several:
+// fp32 partials [split][M][N] for the consumer (as the FP8 form).
+template <int W, int MT>
+__global__ __launch_bounds__(W * 64) void k_gemv_down_mx(const uint8_t* __restrict__ hc,
+                                                         const uint8_t* __restrict__ hs,
+                                                         const uint8_t* __restrict__ wc,
+                                                         const uint8_t* __restrict__ ws, uint16_t* __restrict__ y,
+                                                         float* __restrict__ part, int M, int K, int N) {
+  static_assert(W >= MT, "one wave per tile finishes the epilogue");
+  __shared__ v4f red[W][MT][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int p = blockIdx.x;
+  const int KB = K >> 7;
+  const int S = gridDim.y, sp = blockIdx.y;
+  const int ks0 = sp * KB / S, ks1 = (sp + 1) * KB / S;
+  const int kb0 = ks0 + wave * (ks1 - ks0) / W, kb1 = ks0 + (wave + 1) * (ks1 - ks0) / W;
+  const int row = lane & 15, q = lane >> 4;
+  MxRows xr[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int m = 16 * t + row;
+    xr[t].has = m < M;
+    const int mm = xr[t].has ? m : 0;
+    xr[t].c = hc + (size_t)mm * (K / 2) + q * 16;
+    xr[t].s = hs + (size_t)mm * (K / 32) + q;
+  }
+  v4f acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = v4f{0, 0, 0, 0};
+  for (int kb = kb0; kb < kb1; ++kb) {
+    const v8i wv = mx_w16(wc + mx_code_off((uint32_t)p * 16, kb, lane, KB));
+    const uint32_t d = *reinterpret_cast<const uint32_t*>(ws + mx_scale_off((uint32_t)p * 16, kb & ~3, lane, KB));
+    const int wsc = (int)((d >> (8 * (kb & 3))) & 255u);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const v8i xv = mx_x16(xr[t].c + (size_t)kb * 64, xr[t].has);
+      const int xsc = xr[t].has ? (int)xr[t].s[kb * 4] : 127;
+      acc[t] = mx_mfma(xv, xsc, wv, wsc, acc[t]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < MT; ++t) red[wave][t][lane] = acc[t];
+  __syncthreads();
+  if (wave >= MT) return;
+  const int t = wave;
+  v4f a = red[0][t][lane];
+#pragma unroll
+  for (int v = 1; v < W; ++v) a += red[v][t][lane];
+  float* ps = part + (size_t)sp * M * N;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = 16 * t + 4 * q + r;
+    if (m < M) {
+      if (S == 1)
+        y[(size_t)m * N + p * 16 + row] = (uint16_t)f32_to_bf16(a[r]);
+      else
+        ps[(size_t)m * N + p * 16 + row] = a[r];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers: W in {4, 8, 16}, MT = ceil(M / 16) <= 4, W * MT <= 16 (the
+// reduction buffer: W * MT * NA KiB of LDS)
+// ---------------------------------------------------------------------------
+
+template <int ACT, int W, int MT>
+static hipError_t gateup_mx_t(const uint8_t* xc, const uint8_t* xs, const uint8_t* wc, const uint8_t* ws,
+                              uint8_t* hc, uint8_t* hs, int M, int K, int I, hipStream_t s) {
+  if constexpr (W >= MT && W * MT <= 16) {
+    hipLaunchKernelGGL((k_gemv_gateup_mx<ACT, W, MT>), dim3(I / 32), dim3(W * 64), 0, s, xc, xs, wc, ws, hc, hs, M,
+                       K, I);
+    return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int ACT, int W>
+static hipError_t gateup_mx_w(const uint8_t* xc, const uint8_t* xs, const uint8_t* wc, const uint8_t* ws,
+                              uint8_t* hc, uint8_t* hs, int M, int K, int I, hipStream_t s) {
+  switch ((M + 15) / 16) {
+    case 1: return gateup_mx_t<ACT, W, 1>(xc, xs, wc, ws, hc, hs, M, K, I, s);
+    case 2: return gateup_mx_t<ACT, W, 2>(xc, xs, wc, ws, hc, hs, M, K, I, s);
+    case 3: return gateup_mx_t<ACT, W, 3>(xc, xs, wc, ws, hc, hs, M, K, I, s);
+    case 4: return gateup_mx_t<ACT, W, 4>(xc, xs, wc, ws, hc, hs, M, K, I, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int ACT>
+static hipError_t gateup_mx_act(int W, const uint8_t* xc, const uint8_t* xs, const uint8_t* wc, const uint8_t* ws,
+                                uint8_t* hc, uint8_t* hs, int M, int K, int I, hipStream_t s) {
+  if (W == 4) return gateup_mx_w<ACT, 4>(xc, xs, wc, ws, hc, hs, M, K, I, s);
+  if (W == 8) return gateup_mx_w<ACT, 8>(xc, xs, wc, ws, hc, hs, M, K, I, s);
+  if (W == 16) return gateup_mx_w<ACT, 16>(xc, xs, wc, ws, hc, hs, M, K, I, s);
+  return hipErrorInvalidValue;
+}
+
+int gemv_mx_max_waves(int M) { return M <= 16 ? 16 : (M <= 32 ? 8 : 4); }
+
+hipError_t launch_gemv_gateup_mx(int act, const uint8_t* xc, const uint8_t* xs, const uint8_t* wc, const uint8_t* ws,
+                                 uint8_t* hc, uint8_t* hs, int M, int K, int I, int W, hipStream_t s) {
+  if (M < 1 || M > 64 || K % 512 || I % 32) return hipErrorInvalidValue;
+  if (act == MX_GEGLU) return gateup_mx_act<MX_GEGLU>(W, xc, xs, wc, ws, hc, hs, M, K, I, s);
+  if (act == MX_SWIGLU) return gateup_mx_act<MX_SWIGLU>(W, xc, xs, wc, ws, hc, hs, M, K, I, s);
+  return gateup_mx_act<MX_GELU>(W, xc, xs, wc, ws, hc, hs, M, K, I, s);
+}
+
+template <int W, int MT>
+static hipError_t down_mx_t(const uint8_t* hc, const uint8_t* hs, const uint8_t* wc, const uint8_t* ws, uint16_t* y,
+                            float* part, int M, int K, int N, int S, hipStream_t s) {
+  if constexpr (W >= MT && W * MT <= 32) {
+    hipLaunchKernelGGL((k_gemv_down_mx<W, MT>), dim3(N / 16, S), dim3(W * 64), 0, s, hc, hs, wc, ws, y, part, M, K,
+                       N);
+    return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int W>
+static hipError_t down_mx_w(const uint8_t* hc, const uint8_t* hs, const uint8_t* wc, const uint8_t* ws, uint16_t* y,
+                            float* part, int M, int K, int N, int S, hipStream_t s) {
+  switch ((M + 15) / 16) {
+    case 1: return down_mx_t<W, 1>(hc, hs, wc, ws, y, part, M, K, N, S, s);
+    case 2: return down_mx_t<W, 2>(hc, hs, wc, ws, y, part, M, K, N, S, s);
+    case 3: return down_mx_t<W, 3>(hc, hs, wc, ws, y, part, M, K, N, S, s);
+    case 4: return down_mx_t<W, 4>(hc, hs, wc, ws, y, part, M, K, N, S, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gemv_down_mx(const uint8_t* hc, const uint8_t* hs, const uint8_t* wc, const uint8_t* ws, uint16_t* y,
+                               float* part, int M, int K, int N, int W, int S, hipStream_t s) {
+  if (M < 1 || M > 64 || K % 512 || N % 16 || S < 1 || S > K / 128) return hipErrorInvalidValue;
+  if (W == 4) return down_mx_w<4>(hc, hs, wc, ws, y, part, M, K, N, S, s);
+  if (W == 8) return down_mx_w<8>(hc, hs, wc, ws, y, part, M, K, N, S, s);
+  if (W == 16) return down_mx_w<16>(hc, hs, wc, ws, y, part, M, K, N, S, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace frt

@@ -26,16 +26,22 @@
 // so r' is read from HBM once.  The fp64 sum of squares is reduced across
 // the wave with shuffles and across the row's waves through LDS.
 #include "frt_device.h"
+#include "frt_mx.h"
 
 namespace frt {
 
-template <int TPR, int NC, bool MEASURE>
+// MX: the MXFP4 form (frt_mx.h): x is multiplied by inv_awq[k] (the AWQ
+// pre-scale, itsolotime article section 7.2), each 32-block of a row (four
+// consecutive chunks, i.e. four neighbouring lanes) takes its E8M0 exponent
+// from the 4-lane maximum, and xq_out receives [M][H/2] E2M1 codes, xs_out
+// [M][H/32] exponents.
+template <int TPR, int NC, bool MEASURE, bool MX = false>
 __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
     const uint16_t* __restrict__ r_prev, const uint16_t* __restrict__ y_prev,
     const uint16_t* __restrict__ w_norm, const uint16_t* __restrict__ mod, uint16_t* __restrict__ r_out,
     uint8_t* __restrict__ xq_out, float* __restrict__ x_out, float* __restrict__ amax_out,
     int M, int H, float eps, float inv_x, const float* __restrict__ y_part, int S, float alpha_d,
-    uint16_t* __restrict__ y_store) {
+    uint16_t* __restrict__ y_store, const float* __restrict__ inv_awq = nullptr, uint8_t* __restrict__ xs_out = nullptr) {
   constexpr int RPW = 256 / TPR;  // rows per workgroup
   constexpr int WPR = TPR / 64;   // waves per row
   __shared__ double red[256 / 64];
@@ -103,6 +109,48 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int ch = t + c * TPR;
+    if (MX) {
+      // every lane takes part in the block maximum; rows and chunks outside
+      // the tensor contribute zeros and store nothing
+      const bool ok = active && ch < nchunk;
+      float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (ok) {
+        const uint4 wv = wn[c];
+        uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+        uint32_t rr[4] = {rn[c].x, rn[c].y, rn[c].z, rn[c].w};
+        uint32_t hh[4] = {mh[c].x, mh[c].y, mh[c].z, mh[c].w};
+        if (mod) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            x[2 * j] = ((bf16_lo(rr[j]) * inv_rms) * (1.0f + bf16_lo(ww[j]))) + bf16_lo(hh[j]);
+            x[2 * j + 1] = ((bf16_hi(rr[j]) * inv_rms) * (1.0f + bf16_hi(ww[j]))) + bf16_hi(hh[j]);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            x[2 * j] = (bf16_lo(rr[j]) * inv_rms) * bf16_lo(ww[j]);
+            x[2 * j + 1] = (bf16_hi(rr[j]) * inv_rms) * bf16_hi(ww[j]);
+          }
+        }
+        const float4* aw = reinterpret_cast<const float4*>(inv_awq + (size_t)ch * 8);
+        const float4 a0 = aw[0], a1 = aw[1];
+        const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = x[j] * av[j];
+      }
+      float am = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) am = __builtin_fmaxf(am, __builtin_fabsf(x[j]));
+      am = __builtin_fmaxf(am, __shfl_xor(am, 1, 64));
+      am = __builtin_fmaxf(am, __shfl_xor(am, 2, 64));
+      const int e = mx_block_exp(am);
+      const uint32_t codes = mx_pack8(x, e);
+      if (ok) {
+        *reinterpret_cast<uint32_t*>(xq_out + (size_t)row * (H / 2) + (size_t)ch * 4) = codes;
+        if ((ch & 3) == 0) xs_out[(size_t)row * (H / 32) + (ch >> 2)] = (uint8_t)e;
+      }
+      continue;
+    }
     if (active && ch < nchunk) {
       const uint4 wv = wn[c];
       uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
@@ -246,6 +294,31 @@ hipError_t launch_add_rmsnorm_quant(const uint16_t* r_prev, const uint16_t* y_pr
   }
   return launch_norm_t<false>(r_prev, y_prev, w, mod, r_out, xq, nullptr, nullptr, M, H, eps, inv_x,
                               s, y_part, S, alpha_d, y_store);
+}
+
+// MXFP4 form of K1: xq_codes [M][H/2], xq_scales [M][H/32]; inv_awq [H].
+// H % 32 == 0.
+hipError_t launch_add_rmsnorm_mx(const uint16_t* r_prev, const uint16_t* y_prev, const uint16_t* w,
+                                 const uint16_t* mod, const float* inv_awq, uint16_t* r_out, uint8_t* xq_codes,
+                                 uint8_t* xq_scales, int M, int H, float eps, hipStream_t s, const float* y_part,
+                                 int S, float alpha_d, uint16_t* y_store) {
+  if (H % 32 || !inv_awq) return hipErrorInvalidValue;
+  const int nchunk = H / 8;
+  const int nc = (nchunk + 255) / 256;
+#define FRT_MX_NORM(NCV)                                                                                          \
+  hipLaunchKernelGGL((k_add_rmsnorm_quant<256, NCV, false, true>), dim3(M), dim3(256), 0, s, r_prev, y_prev, w,   \
+                     mod, r_out, xq_codes, nullptr, nullptr, M, H, eps, 1.0f, y_part, S, alpha_d, y_store, inv_awq, \
+                     xq_scales)
+  if (nc <= 1)
+    FRT_MX_NORM(1);
+  else if (nc <= 2)
+    FRT_MX_NORM(2);
+  else if (nc <= 4)
+    FRT_MX_NORM(4);
+  else
+    FRT_MX_NORM(8);
+#undef FRT_MX_NORM
+  return hipGetLastError();
 }
 
 hipError_t launch_add_rmsnorm_measure(const uint16_t* r_prev, const uint16_t* y_prev,

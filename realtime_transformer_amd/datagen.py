@@ -154,3 +154,11 @@ def qkv_weights(cfg) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
 def positions(cfg) -> np.ndarray:
     """Rotary positions of the rows: pos0, pos0 + 1, ... (int32)."""
     return (cfg.pos0 + np.arange(cfg.M)).astype(np.int32)
+
+
+def awq_scales(cfg, layer: int) -> np.ndarray:
+    """AWQ pre-scale of layer `layer` for the MXFP4 variant: bf16 [H] of
+    2^N(0, 0.5) per input channel (a stand-in for the per-channel activation
+    statistics the pages' AWQ derives them from).  Seed 2^22 + 1000*c + l."""
+    z = normal_f32((1 << 22) + 1000 * cfg.index + layer, cfg.H) * np.float32(0.5)
+    return to_bf16_bits(np.exp2(z).astype(np.float32))

@@ -112,6 +112,29 @@ class FFNPlan:
                                tu.data_ptr(), td.data_ptr(), tn.data_ptr(), self.s)
         del tg, tu, td, tn
 
+    def set_awq(self, layer: int, s: np.ndarray):
+        """MXFP4 plans: the layer's AWQ pre-scale (bf16 bits [H]); quantise the layer after it."""
+        t = _to_dev_u16(s, self.device)
+        torch.cuda.synchronize(self.device)
+        _abi.frt_set_awq(self.plan, layer, t.data_ptr(), self.s)
+        del t
+
+    def export_mx(self, layer: int, which: int):
+        """MXFP4 plans: (codes [rows][cols/2], exponents [rows][cols/32]) of gate (0), up (1), down (2)."""
+        rows, cols = (self.H, self.I) if which == 2 else (self.I, self.H)
+        return _abi.frt_export_mxfp4_weights(self.plan, layer, which, rows, cols)
+
+    def xq_mx(self, l: int):
+        """MXFP4 plans: XQ slot l as (codes [M][H/2], exponents [M][H/32]) uint8 views."""
+        n = self.M * self.H // 2
+        v = self._view(self.io.xq_slots + l * self.io.stride_xq, n + n // 16)
+        return v[:n].view(self.M, self.H // 2), v[n:].view(self.M, self.H // 32)
+
+    def hq_mx(self, l: int):
+        n = self.M * self.I // 2
+        v = self._view(self.io.hq_slots + l * self.io.stride_hq, n + n // 16)
+        return v[:n].view(self.M, self.I // 2), v[n:].view(self.M, self.I // 32)
+
     def export_codes(self, layer: int, which: int) -> np.ndarray:
         rows, cols = (self.H, self.I) if which == 2 else (self.I, self.H)
         return _abi.frt_export_weight_codes(self.plan, layer, which, rows, cols)

@@ -36,8 +36,9 @@ def test_library_is_in_tree():
 
 @pytest.mark.parametrize("bad", [
     dict(M=0), dict(L=0), dict(H=100), dict(I=200), dict(H=16384 + 128), dict(act=3),
-    dict(eps=0.0), dict(eps=float("nan")), dict(flags=32), dict(flags=45), dict(flags=16 | 8), dict(flags=16 | 2),
-    dict(device=-1)])
+    dict(eps=0.0), dict(eps=float("nan")), dict(flags=64), dict(flags=77), dict(flags=16 | 8), dict(flags=16 | 2),
+    dict(flags=32, H=384), dict(flags=32, I=1536 + 128), dict(flags=32, M=65), dict(flags=32 | 1), dict(flags=32 | 4),
+    dict(flags=32 | 2), dict(flags=32 | 8), dict(device=-1)])
 def test_bad_descriptors_rejected(bad):
     kw = dict(M=16, H=256, I=1024, L=1, act=0, eps=1e-6, device=0, flags=0)
     kw.update(bad)
@@ -84,3 +85,11 @@ def test_qkv_workspace_covers_weights_table_and_slots():
         assert need <= n < 1.3 * need + (1 << 24)
     for flags in (8, 16):
         assert _abi.frt_qkv_workspace_size(_abi.make_qkv_desc(4, 256, 2, 1, 64, 32, flags=flags)) > 0
+
+
+def test_mxfp4_descriptors_accepted():
+    for kw in (dict(M=1, H=512, I=1024), dict(M=64, H=1024, I=4096, flags_extra=16)):
+        extra = kw.pop("flags_extra", 0)
+        n = _abi.frt_ffn_workspace_size(_abi.make_desc(kw["M"], kw["H"], kw["I"], 2, 0, flags=32 | extra))
+        fp8 = _abi.frt_ffn_workspace_size(_abi.make_desc(kw["M"], kw["H"], kw["I"], 2, 0))
+        assert 0 < n < fp8  # 4-bit weights take about half the bytes

@@ -1,0 +1,199 @@
+"""GPU parity of the MXFP4 FFN variant (FRT_FLAG_MXFP4) against the CPU
+oracle, through the C ABI.
+
+Checks: packed weight codes and E8M0 exponents equal the oracle's bit for bit
+(with and without the AWQ pre-scale); graph replay equals the eager forward;
+teacher-forced per block (the oracle's state entering layer l written into
+the slots): R' bit-exact, the XQ codes and exponents bit-exact (the same fp32
+arithmetic decides them on both sides), HQ codes/exponents at most 1e-4 of
+the blocks differing (the GPU sums the products in fp32 in its own order, so
+an h value sitting on a rounding or exponent boundary may fall the other
+way), Y within the block tolerance (max |d| / max |ref| <= 2e-2, cosine >=
+0.999); the free-running chain's Z at cosine >= 0.999 against the oracle's
+for chains of at most two layers (reported for deeper ones).
+"""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from realtime_transformer_amd import _abi, datagen
+from realtime_transformer_amd.configs import CONFIGS, FFNConfig, ACT_GEGLU_TANH, ACT_SWIGLU, ACT_GELU_TANH
+from realtime_transformer_amd.plan import FFNPlan, to_np_u16, to_np_u8
+
+from _ffn_case import check_y, log, y_metrics
+
+pytestmark = pytest.mark.gpu
+
+HQ_BLOCK_RATE = 1e-4
+MIN_COS = 0.999
+
+
+def _blocks_differ(codes_g, exps_g, codes_o, exps_o):
+    """Number of 32-blocks (per row) whose exponent or any code differs."""
+    M, nb = exps_o.shape
+    cd = (codes_g != codes_o).reshape(M, nb, 16).any(axis=2)
+    return int(np.count_nonzero(cd | (exps_g != exps_o))), M * nb
+
+
+def _teacher_forced_block(plan, l, r, y, lw, cfg, idx, rows):
+    """Write (r, y) into slot l, run layer l alone, compare with the oracle's block."""
+    with torch.cuda.stream(plan.stream):
+        plan.r_slot(l).index_copy_(0, idx, torch.from_numpy(r.view(np.int16)).to(plan.device))
+        if y is None:
+            plan.y_slot(l).index_fill_(0, idx, 0)
+        else:
+            plan.y_slot(l).index_copy_(0, idx, torch.from_numpy(y.view(np.int16)).to(plan.device))
+    plan.sync()
+    plan.forward_range(l, l + 1)
+    plan.sync()
+    r_o, xq_o, hq_o, y_o = oracle.block_mxfp4(r, y, lw, cfg.act, cfg.eps)
+    r_g = to_np_u16(plan.r_slot(l + 1)[idx])
+    assert np.array_equal(r_g, r_o), "layer %d residual differs" % l
+    xc, xe = (to_np_u8(t[idx]) for t in plan.xq_mx(l))
+    hc, he = (to_np_u8(t[idx]) for t in plan.hq_mx(l))
+    a, na = _blocks_differ(xc, xe, *xq_o)
+    assert a == 0, "layer %d XQ: %d of %d blocks differ" % (l, a, na)
+    b, nb = _blocks_differ(hc, he, *hq_o)
+    mr, cs = check_y("layer %d Y" % l, to_np_u16(plan.y_slot(l + 1)[idx]), y_o)
+    return a, na, b, nb, mr, cs
+
+
+def run_mx_case(cfg: FFNConfig, awq: bool = False, flags: int = 0, rows=None, check_layers=None,
+                chain: bool = True):
+    """chain: the oracle runs the whole chain, its Z is compared with the
+    graph's and every checked layer is teacher-forced with the oracle's own
+    state entering it (gated at cosine >= 0.999 only for chains of at most
+    two layers: deeper random-weight chains amplify summation-order
+    differences, reported then).  chain=False: only the checked layers are
+    quantised by the oracle and each is compared on fresh seeded (r, y)."""
+    t0 = time.time()
+    flags |= _abi.FRT_FLAG_MXFP4
+    M, H, I, L, act = cfg.M, cfg.H, cfg.I, cfg.L, cfg.act
+    rows = np.arange(M) if rows is None else np.asarray(sorted(rows))
+    layers = list(range(L)) if check_layers is None else list(check_layers)
+    ada = bool(flags & _abi.FRT_FLAG_ADA_NORM)
+    log("[mx %s] M=%d H=%d I=%d L=%d act=%d awq=%s flags=%d chain=%s" % (cfg.name, M, H, I, L, act, awq, flags, chain))
+    plan = FFNPlan(M, H, I, L, act, cfg.eps, flags=flags)
+    try:
+        lws = {}
+        for l in range(L):
+            wg, wu, wd, wn = datagen.layer_weights(cfg, l)
+            s = datagen.awq_scales(cfg, l) if awq else None
+            mod = datagen.modulation(cfg, l) if ada else None
+            if awq:
+                plan.set_awq(l, s)
+            plan.load_layer(l, wg, wu, wd, wn)
+            if ada:
+                plan.set_modulation(l, *mod)
+            if not chain and l not in layers:
+                continue
+            lw = oracle.MxLayerWeights.quantize(wg, wu, wd, wn, awq=s, mod=mod)
+            for which, ref in ((0, lw.g), (1, lw.u), (2, lw.d)):
+                if ref is None:
+                    continue
+                c, e = plan.export_mx(l, which)
+                assert np.array_equal(c, ref[0]), "layer %d tensor %d: %d code bytes differ" % (
+                    l, which, int(np.count_nonzero(c != ref[0])))
+                assert np.array_equal(e, ref[1]), "layer %d tensor %d: %d exponents differ" % (
+                    l, which, int(np.count_nonzero(e != ref[1])))
+            lws[l] = lw
+            if L > 8 and (l % 8 == 7 or l == L - 1):
+                log("[mx %s] layers 0..%d loaded (%.1fs)" % (cfg.name, l, time.time() - t0))
+        log("[mx %s] weights bit-exact (%.1fs)" % (cfg.name, time.time() - t0))
+
+        r0, y0 = datagen.eval_inputs(cfg)
+        plan.set_inputs(r0, y0)
+        plan.capture()
+        plan.replay()
+        plan.sync()
+        z_graph = to_np_u16(plan.z())
+        plan.forward()
+        plan.sync()
+        assert np.array_equal(to_np_u16(plan.z()), z_graph), "eager forward differs from graph replay"
+        orc = None
+        if chain:
+            orc = oracle.run_chain_mxfp4((lambda l=l: lws[l] for l in range(L)), act, cfg.eps, r0[rows],
+                                         None if y0 is None else y0[rows])
+            z_rel, z_cos = y_metrics(z_graph[rows], oracle.final_hidden(orc.r[L], orc.y[L]))
+            log("[mx %s] graph == eager; chain Z cos %.6f max rel %.3g" % (cfg.name, z_cos, z_rel))
+            if L <= 2:
+                assert z_cos >= MIN_COS, "chain Z cosine %.6f" % z_cos
+
+        idx = torch.as_tensor(rows, device=plan.device)
+        nx = nh = nxt = nht = 0
+        worst_rel, worst_cos = 0.0, 1.0
+        for l in layers:
+            if chain:
+                r, y = orc.r[l], orc.y[l]
+            else:
+                r = datagen.residual(cfg, 7000 + 10 * cfg.index + l)[rows]
+                y = datagen.normal_bf16(7500 + 10 * cfg.index + l, (cfg.M, cfg.H))[rows]
+            a, na, b, nb, mr, cs = _teacher_forced_block(plan, l, r, y, lws[l], cfg, idx, rows)
+            nx, nxt, nh, nht = nx + a, nxt + na, nh + b, nht + nb
+            worst_rel, worst_cos = max(worst_rel, mr), min(worst_cos, cs)
+        assert nh <= HQ_BLOCK_RATE * nht, "HQ: %d of %d blocks differ" % (nh, nht)
+        log("[mx %s] per-block: XQ %d/%d blocks, HQ %d/%d blocks differ; Y max rel %.3g min cos %.6f (%.1fs)" % (
+            cfg.name, nx, nxt, nh, nht, worst_rel, worst_cos, time.time() - t0))
+    finally:
+        plan.close()
+
+
+SMALL = [
+    # (index, M, H, I, L, act)
+    (131, 1, 512, 1024, 2, ACT_SWIGLU),
+    (132, 7, 512, 2048, 2, ACT_GEGLU_TANH),
+    (133, 16, 1024, 512, 2, ACT_GELU_TANH),
+    (134, 33, 512, 1536, 2, ACT_SWIGLU),
+    (135, 64, 1024, 1024, 2, ACT_GEGLU_TANH),
+]
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
+def test_mxfp4_small(spec):
+    idx, M, H, I, L, act = spec
+    run_mx_case(FFNConfig(idx, "mx_small_%d" % idx, M, H, I, L, act))
+
+
+@pytest.mark.parametrize("spec", [SMALL[0], SMALL[3]], ids=lambda s: "M%d" % s[1])
+def test_mxfp4_small_awq(spec):
+    idx, M, H, I, L, act = spec
+    run_mx_case(FFNConfig(idx, "mx_awq_%d" % idx, M, H, I, L, act), awq=True)
+
+
+def test_mxfp4_small_ada_norm():
+    idx, M, H, I, L, act = SMALL[1]
+    run_mx_case(FFNConfig(idx, "mx_ada_%d" % idx, M, H, I, L, act), flags=_abi.FRT_FLAG_ADA_NORM)
+
+
+def test_mxfp4_action_expert_m50_chain():
+    run_mx_case(CONFIGS[2], awq=True)
+
+
+@pytest.mark.timeout(900)
+def test_mxfp4_llm_decode_m1_full_size():
+    # all 64 layers on the GPU (graph == eager); the oracle checks a spread of
+    # layers on fresh seeded inputs
+    run_mx_case(CONFIGS[4], awq=True, check_layers=[0, 1, 21, 42, 63], chain=False)
+
+
+def test_mxfp4_rejects_calibration_and_fp8_exports():
+    cfg = FFNConfig(136, "mx_api", 2, 512, 512, 1, ACT_SWIGLU)
+    plan = FFNPlan(cfg.M, cfg.H, cfg.I, cfg.L, cfg.act, cfg.eps, flags=_abi.FRT_FLAG_MXFP4)
+    try:
+        wg, wu, wd, wn = datagen.layer_weights(cfg, 0)
+        plan.load_layer(0, wg, wu, wd, wn)
+        with pytest.raises(_abi.FrtError) as e:
+            plan.calibrate(datagen.calib_batches(cfg, 1))
+        assert e.value.status == _abi.FRT_ERR_UNSUPPORTED
+        with pytest.raises(_abi.FrtError) as e:
+            plan.export_codes(0, 1)
+        assert e.value.status == _abi.FRT_ERR_STATE
+        bad = np.zeros(cfg.H, np.uint16)  # scale 0 is rejected
+        with pytest.raises(_abi.FrtError) as e:
+            plan.set_awq(0, bad)
+        assert e.value.status == _abi.FRT_ERR_INVALID_ARG
+    finally:
+        plan.close()
