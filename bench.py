@@ -122,6 +122,53 @@ def per_kernel_ms(plan, reps=3):
     return [plan.time_kernel(k, reps) / 1000.0 for k in range(3)]
 
 
+def measure_mxfp4(steps, warmup):
+    """The MXFP4 variant (FRT_FLAG_MXFP4, AWQ pre-scale set) of the decode and
+    action-expert chains: graph replay per layer, per-kernel times, and the
+    HBM rate against the 4-bit algorithmic bytes (E2M1 codes + one E8M0 byte
+    per 32 values = 17/32 byte per value)."""
+    import torch
+    from realtime_transformer_amd import _abi, datagen
+    from realtime_transformer_amd.configs import BY_NAME
+    res = {"format": "OCP MXFP4 (E2M1, E8M0 per 32 along K), AWQ pre-scale, bf16 residual"}
+    for name in ("llm_decode_m1", "action_expert_m50"):
+        c = BY_NAME[name]
+        p, _, _ = setup_mx(c)
+        ms, _ = time_replays(p, steps, warmup)
+        k = [float(v) for v in per_kernel_ms(p)]
+        p.close()
+        f = 17.0 / 32
+        gu_b = 2 * c.I * c.H * f + c.M * c.H * f + c.M * c.I * f
+        dn_b = c.I * c.H * f + c.M * c.I * f + 2 * c.M * c.H
+        layer_b = gu_b + dn_b + 7 * c.M * c.H + 2 * c.H
+        us = float(ms) * 1000.0 / c.L
+        gbs = gu_b / (k[1] * 1e-3) / 1e9
+        res[name] = {"us_per_layer": round(us, 3), "layer_bytes": int(layer_b),
+                     "chain_hbm_gbs": round(layer_b / (us * 1e-6) / 1e9, 1),
+                     "kernels_us": {"norm_quant": round(k[0] * 1000, 3), "gateup": round(k[1] * 1000, 3),
+                                    "down": round(k[2] * 1000, 3)},
+                     "roofline": {"bound": "hbm", "kernel": "gemv_gateup_mx", "achieved": round(gbs, 1),
+                                  "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                  "bytes_per_launch": int(gu_b)}}
+        log("[bench %s mxfp4] %.2f us/layer (norm %.2f gate/up %.2f down %.2f us)" % (
+            name, us, k[0] * 1000, k[1] * 1000, k[2] * 1000))
+    return res
+
+
+def setup_mx(cfg):
+    """MXFP4 plan with the AWQ pre-scale and weights of every layer, inputs set, graph captured."""
+    from realtime_transformer_amd import _abi, datagen
+    from realtime_transformer_amd.plan import FFNPlan
+    plan = FFNPlan(cfg.M, cfg.H, cfg.I, cfg.L, cfg.act, cfg.eps, flags=_abi.FRT_FLAG_MXFP4)
+    for l in range(cfg.L):
+        plan.set_awq(l, datagen.awq_scales(cfg, l))
+        plan.load_layer(l, *datagen.layer_weights(cfg, l))
+    r0, y0 = datagen.eval_inputs(cfg)
+    plan.set_inputs(r0, y0)
+    plan.capture()
+    return plan, None, (r0, y0)
+
+
 def measure_qkv(steps, warmup, calibrate=True):
     """Attention-input workloads: graph replay of K1 + fused QKV GEMM with the
     split + rotary epilogue, per-kernel times, and the GEMM's roofline (HBM
@@ -211,6 +258,8 @@ def main():
                     help="skip timing the opt-in FP8 matrix-core modes of the second workload")
     ap.add_argument("--no-norm-variants", action="store_true",
                     help="skip timing the action-expert chain with the norm variants")
+    ap.add_argument("--no-mxfp4", action="store_true",
+                    help="skip timing the MXFP4 variant of the decode and action-expert chains")
     ap.add_argument("--no-qkv", action="store_true",
                     help="skip timing the attention-input (K1 + fused QKV + rotary) workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -358,6 +407,9 @@ def main():
                                        "down": round(k3[2] * 1000, 3)}}
             log("[bench %s] %s: %.2f us/layer" % (c3.name, name, nv[name]["us_per_layer"]))
         out["norm_variants"] = nv
+
+    if not args.no_mxfp4:
+        out["mxfp4"] = measure_mxfp4(args.steps, args.warmup)
 
     if not args.no_qkv:
         out["qkv"] = measure_qkv(args.steps, args.warmup, calibrate=not args.no_calibrate)

@@ -29,20 +29,17 @@ __device__ __forceinline__ int mx_block_exp(float amax) {
   return e < 0 ? 0 : (e > 254 ? 254 : e);
 }
 
-// E2M1 code of v (already divided by the block scale): the decision points
-// are the midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 between neighbouring
-// magnitudes; at a midpoint the neighbour with mantissa bit 0 wins (0.25 ->
-// 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4).
+// E2M1 code of v (already divided by the block scale): the magnitude code is
+// the number of decision points passed -- the midpoints 0.25, 0.75, 1.25,
+// 1.75, 2.5, 3.5, 5 between neighbouring magnitudes, each a strict or
+// non-strict comparison so that a value on a midpoint goes to the neighbour
+// with mantissa bit 0 (0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2,
+// 3.5 -> 4, 5 -> 4); NaN takes the largest magnitude.  No branches.
 __device__ __forceinline__ uint32_t e2m1_code(float v) {
   const float a = __builtin_fabsf(v);
-  const uint32_t c = a <= 0.25f ? 0u
-                     : a < 0.75f ? 1u
-                     : a <= 1.25f ? 2u
-                     : a < 1.75f ? 3u
-                     : a <= 2.5f ? 4u
-                     : a < 3.5f ? 5u
-                     : a <= 5.0f ? 6u
-                                 : 7u;
+  uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
+               (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+  c = (a == a) ? c : 7u;
   return c | ((__float_as_uint(v) >> 28) & 8u);
 }
 

@@ -155,21 +155,34 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup_mx(const uint8_t* __rest
 #pragma unroll
     for (int a = 0; a < NA; ++a) acc[t][a] = v4f{0, 0, 0, 0};
 
-  for (int kb = kb0; kb < kb1; ++kb) {
-    v8i wv[NA];
-    int wsc[NA];
+  // two K blocks per step: every load of the step is issued before its MFMAs
+  for (int kb = kb0; kb < kb1; kb += 2) {
+    const int nk = kb + 1 < kb1 ? 2 : 1;
+    v8i wv[2][NA], xv[2][MT];
+    int wsc[2][NA], xsc[2][MT];
 #pragma unroll
-    for (int a = 0; a < NA; ++a) {
-      wv[a] = mx_w16(wc + mx_code_off(grp[a] * 16, kb, lane, KB));
-      const uint32_t d = *reinterpret_cast<const uint32_t*>(ws + mx_scale_off(grp[a] * 16, kb & ~3, lane, KB));
-      wsc[a] = (int)((d >> (8 * (kb & 3))) & 255u);
+    for (int u = 0; u < 2; ++u) {
+      const int k = kb + (u < nk ? u : 0);
+#pragma unroll
+      for (int a = 0; a < NA; ++a) {
+        wv[u][a] = mx_w16(wc + mx_code_off(grp[a] * 16, k, lane, KB));
+        const uint32_t d = *reinterpret_cast<const uint32_t*>(ws + mx_scale_off(grp[a] * 16, k & ~3, lane, KB));
+        wsc[u][a] = (int)((d >> (8 * (k & 3))) & 255u);
+      }
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        xv[u][t] = mx_x16(xr[t].c + (size_t)k * 64, xr[t].has);
+        xsc[u][t] = xr[t].has ? (int)xr[t].s[k * 4] : 127;
+      }
     }
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const v8i xv = mx_x16(xr[t].c + (size_t)kb * 64, xr[t].has);
-      const int xsc = xr[t].has ? (int)xr[t].s[kb * 4] : 127;
+    for (int u = 0; u < 2; ++u) {
+      if (u < nk) {
 #pragma unroll
-      for (int a = 0; a < NA; ++a) acc[t][a] = mx_mfma(xv, xsc, wv[a], wsc[a], acc[t][a]);
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+          for (int a = 0; a < NA; ++a) acc[t][a] = mx_mfma(xv[u][t], xsc[u][t], wv[u][a], wsc[u][a], acc[t][a]);
+      }
     }
   }
 #pragma unroll
@@ -237,15 +250,29 @@ __global__ __launch_bounds__(W * 64) void k_gemv_down_mx(const uint8_t* __restri
   v4f acc[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = v4f{0, 0, 0, 0};
-  for (int kb = kb0; kb < kb1; ++kb) {
-    const v8i wv = mx_w16(wc + mx_code_off((uint32_t)p * 16, kb, lane, KB));
-    const uint32_t d = *reinterpret_cast<const uint32_t*>(ws + mx_scale_off((uint32_t)p * 16, kb & ~3, lane, KB));
-    const int wsc = (int)((d >> (8 * (kb & 3))) & 255u);
+  // four K blocks per step: every load of the step is issued before its MFMAs
+  for (int kb = kb0; kb < kb1; kb += 4) {
+    const int nk = kb1 - kb < 4 ? kb1 - kb : 4;
+    v8i wv[4], xv[4][MT];
+    int wsc[4], xsc[4][MT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const v8i xv = mx_x16(xr[t].c + (size_t)kb * 64, xr[t].has);
-      const int xsc = xr[t].has ? (int)xr[t].s[kb * 4] : 127;
-      acc[t] = mx_mfma(xv, xsc, wv, wsc, acc[t]);
+    for (int u = 0; u < 4; ++u) {
+      const int k = kb + (u < nk ? u : 0);
+      wv[u] = mx_w16(wc + mx_code_off((uint32_t)p * 16, k, lane, KB));
+      const uint32_t d = *reinterpret_cast<const uint32_t*>(ws + mx_scale_off((uint32_t)p * 16, k & ~3, lane, KB));
+      wsc[u] = (int)((d >> (8 * (k & 3))) & 255u);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        xv[u][t] = mx_x16(xr[t].c + (size_t)k * 64, xr[t].has);
+        xsc[u][t] = xr[t].has ? (int)xr[t].s[k * 4] : 127;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (u < nk) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[t] = mx_mfma(xv[u][t], xsc[u][t], wv[u], wsc[u], acc[t]);
+      }
     }
   }
 #pragma unroll

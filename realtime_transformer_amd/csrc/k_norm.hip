@@ -53,8 +53,10 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
   const int nchunk = H >> 3;
   const size_t base = (size_t)(active ? row : 0) * (size_t)H;
 
-  // wn: the norm weight, or with modulation the per-channel scale (mh: shift)
+  // wn: the norm weight, or with modulation the per-channel scale (mh: shift);
+  // aw: the MXFP4 form's AWQ reciprocals, requested with them
   uint4 rn[NC], wn[NC], mh[NC];
+  float4 aw[MX ? NC : 1][2];
   double sq = 0.0;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -62,8 +64,14 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
     rn[c] = make_uint4(0, 0, 0, 0);
     wn[c] = rn[c];
     mh[c] = rn[c];
+    if (MX) aw[MX ? c : 0][0] = aw[MX ? c : 0][1] = make_float4(0, 0, 0, 0);
     if (active && ch < nchunk) {
       // issued with r, y
+      if (MX) {
+        const float4* ap = reinterpret_cast<const float4*>(inv_awq + (size_t)ch * 8);
+        aw[MX ? c : 0][0] = ap[0];
+        aw[MX ? c : 0][1] = ap[1];
+      }
       if (mod) {
         wn[c] = *reinterpret_cast<const uint4*>(mod + (size_t)ch * 8);
         mh[c] = *reinterpret_cast<const uint4*>(mod + H + (size_t)ch * 8);
@@ -132,8 +140,7 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
             x[2 * j + 1] = (bf16_hi(rr[j]) * inv_rms) * bf16_hi(ww[j]);
           }
         }
-        const float4* aw = reinterpret_cast<const float4*>(inv_awq + (size_t)ch * 8);
-        const float4 a0 = aw[0], a1 = aw[1];
+        const float4 a0 = aw[MX ? c : 0][0], a1 = aw[MX ? c : 0][1];
         const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] = x[j] * av[j];
