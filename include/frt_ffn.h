@@ -114,8 +114,10 @@ typedef enum {
  *     gate/up: weights f32(W[i][k] * s[k]) in MXFP4; g, u fp32-accumulated
  *         block-scaled products; h = act(g) * u; HQ = MXFP4(h) along I
  *     down: Y = bf16(fp32-accumulated block-scaled products)
- *   Requires M <= 64, H and I multiples of 512; excludes the FP8, fused-norm
- *   and norm-fusion flags.  Slots: each XQ slot holds codes [M][H/2] (two per
+ *   M <= 64 runs GEMVs, larger M the block-scaled prefill GEMM (128 x 128
+ *   tiles, K split for the down projection into fp32 partials).  Requires H
+ *   and I multiples of 512; excludes the FP8, fused-norm and norm-fusion
+ *   flags.  Slots: each XQ slot holds codes [M][H/2] (two per
  *   byte, low nibble first) followed by exponents [M][H/32]; HQ likewise with
  *   I. */
 #define FRT_FLAG_MXFP4 32u

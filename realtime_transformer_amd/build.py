@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfrt.so")
 BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
 SOURCES = ["frt_ffn.hip", "frt_qkv.hip", "k_norm.hip", "k_quant.hip", "k_gemm.hip", "k_mm.hip", "k_calib.hip",
-           "k_qkv.hip", "k_mx.hip"]
+           "k_qkv.hip", "k_mx.hip", "k_mxmm.hip"]
 HEADERS = ["frt_device.h", "frt_host.h", "frt_qkv_dev.h", "frt_mx.h", os.path.join("..", "..", "include", "frt_ffn.h"),
            os.path.join("..", "..", "include", "frt_qkv.h")]
 

@@ -51,7 +51,11 @@ bool gemv_fused_supported(int, int, int);
 hipError_t launch_add_rmsnorm_mx(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*, const float*,
                                  uint16_t*, uint8_t*, uint8_t*, int, int, float, hipStream_t, const float*, int, float,
                                  uint16_t*);
-hipError_t launch_quant_mx(const uint16_t*, uint8_t*, uint8_t*, int, int, int, const uint16_t*, hipStream_t);
+hipError_t launch_quant_mx(const uint16_t*, uint8_t*, uint8_t*, int, int, int, const uint16_t*, hipStream_t, int);
+hipError_t launch_mxmm_gateup(int, const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, uint8_t*, uint8_t*,
+                              int, int, int, hipStream_t);
+hipError_t launch_mxmm_down(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, uint16_t*, float*, int, int,
+                            int, int, hipStream_t);
 hipError_t launch_gemv_gateup_mx(int, const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, uint8_t*,
                                  uint8_t*, int, int, int, int, hipStream_t);
 hipError_t launch_gemv_down_mx(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, uint16_t*, float*, int,
@@ -145,6 +149,7 @@ struct Layout {
   int split_dn;    // K splits of the down projection, either path (> 1: fp32 partials)
   bool gemv_mt;    // 16 < M <= 64 on the multi-tile GEMVs
   bool mx;         // MXFP4 plan
+  bool mx_mm;      // MXFP4 with M > 64: the prefill GEMMs (k_mxmm), their exponent layout
   size_t wgu_sc, wd_sc;        // MXFP4: offset of the exponents inside a layer's weights
   size_t xq_stride, hq_stride; // bytes per XQ / HQ slot
   size_t awq, inv_awq;         // MXFP4: AWQ scale bf16 [L][H], its reciprocal fp32 [L][H]
@@ -163,10 +168,10 @@ bool desc_ok(const frt_ffn_desc* d) {
   if ((d->flags & ~(uint32_t)(FRT_FLAG_FP8_MFMA_DOWN | FRT_FLAG_FUSED_NORM | FRT_FLAG_FP8_MFMA_GATEUP |
                               FRT_FLAG_NORM_FUSE | FRT_FLAG_ADA_NORM | FRT_FLAG_MXFP4)) != 0u || d->device < 0)
     return false;
-  // MXFP4: the GEMV path (M <= 64), K dimensions in whole groups of four
-  // 128-blocks (one exponent dword per lane), no FP8 or fused-norm options
+  // MXFP4: K dimensions in whole groups of four 128-blocks (one exponent
+  // dword per lane in the GEMV layout), no FP8 or fused-norm options
   if ((d->flags & FRT_FLAG_MXFP4) &&
-      (d->M > 64 || d->H % 512 || d->I % 512 ||
+      (d->H % 512 || d->I % 512 ||
        (d->flags & (FRT_FLAG_FP8_MFMA_DOWN | FRT_FLAG_FP8_MFMA_GATEUP | FRT_FLAG_FUSED_NORM | FRT_FLAG_NORM_FUSE))))
     return false;
   // AdaRMSNorm replaces the norm weight: no folding of it, and no fused
@@ -301,7 +306,19 @@ Layout make_layout(const frt_ffn_desc& d) {
 
   size_t part = 0, words = 1;
   lo.gemv_mt = d.M > kGemvMaxM && d.M <= std::min(kGemvMtMaxM, env_int("FRT_GEMV_MT_MAX_M", kGemvMtMaxM));
-  if (d.M <= kGemvMaxM || lo.gemv_mt || lo.mx) {
+  lo.mx_mm = lo.mx && d.M > kGemvMtMaxM;
+  if (lo.mx_mm) {
+    // K split of the MXFP4 down GEMM until the 128 x 128 tiles give at least
+    // one workgroup per CU (each split at least 8 stages)
+    const int tiles = (int)(H / 128) * ceil_div(d.M, 128);
+    int sp = 1;
+    while (tiles * sp < kCUs && (int)(I / 128) / (2 * sp) >= 8 && sp < 8) sp *= 2;
+    sp = std::max(1, std::min(env_int("FRT_MXMM_DOWN_SPLIT", sp), (int)(I / 128)));
+    lo.s_gu = lo.s_dn = 0;
+    lo.k_dn = lo.split_dn = sp;
+    part = sp > 1 ? (size_t)sp * M * H * 4 : 4;
+    words = 1;
+  } else if (d.M <= kGemvMaxM || lo.gemv_mt || lo.mx) {
     lo.s_gu = gemv_waves((int)(I / 16), (int)(H / 128), "FRT_GEMV_WAVES_GATEUP", 6144);
     lo.k_dn = gemv_down_splits((int)(H / 16), (int)(I / 128));
     lo.s_dn = gemv_waves((int)(H / 16) * lo.k_dn, (int)(I / 128) / lo.k_dn, "FRT_GEMV_WAVES_DOWN", 4096);
@@ -541,17 +558,21 @@ frt_status frt_quant_weights(frt_plan* p, int32_t layer, const void* d_w_gate, c
   if (p->mx()) {
     // MXFP4: gate/up times the layer's AWQ scale per input column, then 32-blocks
     const uint16_t* aw = p->awq(layer);
+    const int mml = p->lo.mx_mm ? 1 : 0;
     if (p->gated) {
-      KERNEL_CHECK(launch_quant_mx(static_cast<const uint16_t*>(d_w_gate), p->wgu(layer), p->wgu_s(layer), I, H, 1, aw, s),
+      KERNEL_CHECK(launch_quant_mx(static_cast<const uint16_t*>(d_w_gate), p->wgu(layer), p->wgu_s(layer), I, H, 1, aw, s,
+                                   mml),
                    "quant_mx");
-      KERNEL_CHECK(launch_quant_mx(static_cast<const uint16_t*>(d_w_up), p->wgu(layer), p->wgu_s(layer), I, H, 2, aw, s),
+      KERNEL_CHECK(launch_quant_mx(static_cast<const uint16_t*>(d_w_up), p->wgu(layer), p->wgu_s(layer), I, H, 2, aw, s,
+                                   mml),
                    "quant_mx");
     } else {
-      KERNEL_CHECK(launch_quant_mx(static_cast<const uint16_t*>(d_w_up), p->wgu(layer), p->wgu_s(layer), I, H, 0, aw, s),
+      KERNEL_CHECK(launch_quant_mx(static_cast<const uint16_t*>(d_w_up), p->wgu(layer), p->wgu_s(layer), I, H, 0, aw, s,
+                                   mml),
                    "quant_mx");
     }
     KERNEL_CHECK(launch_quant_mx(static_cast<const uint16_t*>(d_w_down), p->wd(layer), p->wd_s(layer), H, I, 0, nullptr,
-                                 s),
+                                 s, mml),
                  "quant_mx");
     HIP_CHECK(hipMemcpyAsync(p->wn(layer), d_norm_w, (size_t)H * 2, hipMemcpyDeviceToDevice, s));
     HIP_CHECK(hipStreamSynchronize(s));
@@ -644,7 +665,7 @@ frt_status frt_export_mxfp4_weights(const frt_plan* p, int32_t layer, int32_t wh
     for (uint32_t b = 0; b < K / 32; ++b) {
       const uint32_t kb = b >> 2, lane = (pr & 15u) + 16u * (b & 3u);
       memcpy(dc + (size_t)n * (K / 2) + (size_t)b * 16, tc.data() + mx_code_off(pr, kb, lane, KB), 16);
-      dsc[(size_t)n * (K / 32) + b] = ts[mx_scale_off(pr, kb, lane, KB)];
+      dsc[(size_t)n * (K / 32) + b] = ts[p->lo.mx_mm ? mx_scale_off_mm(pr, kb, lane, KB) : mx_scale_off(pr, kb, lane, KB)];
     }
   }
   return FRT_OK;
@@ -792,10 +813,18 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
       KERNEL_CHECK(launch_add_rmsnorm_mx(p->r(l), p->y(l), p->wn(l), p->mod(l), p->inv_awq(l), p->r(l + 1), p->xq(l),
                                          p->xs(l), M, H, p->d.eps, s, yp, p->lo.split_dn, 1.0f, p->y(l)),
                    "add_rmsnorm_mx");
+    } else if (which == 1 && p->lo.mx_mm) {
+      KERNEL_CHECK(launch_mxmm_gateup(p->d.act, p->xq(l), p->xs(l), p->wgu(l), p->wgu_s(l), p->hq(l), p->hs(l), M, H,
+                                      npk, s),
+                   "mxmm_gateup");
     } else if (which == 1) {
       KERNEL_CHECK(launch_gemv_gateup_mx(p->d.act, p->xq(l), p->xs(l), p->wgu(l), p->wgu_s(l), p->hq(l), p->hs(l), M,
                                          H, I, p->lo.s_gu, s),
                    "gemv_gateup_mx");
+    } else if (p->lo.mx_mm) {
+      KERNEL_CHECK(launch_mxmm_down(p->hq(l), p->hs(l), p->wd(l), p->wd_s(l), p->y(l + 1), p->part(), M, I, H,
+                                    p->lo.split_dn, s),
+                   "mxmm_down");
     } else {
       KERNEL_CHECK(launch_gemv_down_mx(p->hq(l), p->hs(l), p->wd(l), p->wd_s(l), p->y(l + 1), p->part(), M, I, H,
                                        p->lo.s_dn, p->lo.k_dn, s),

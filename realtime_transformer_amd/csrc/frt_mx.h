@@ -51,4 +51,44 @@ __device__ __forceinline__ uint32_t mx_pack8(const float x[8], int e) {
   return w;
 }
 
+// Gated combine of the MXFP4 FFN (act(g) * u, or gelu_tanh(u) without gate).
+enum { MX_GEGLU = 0, MX_SWIGLU = 1, MX_GELU = 2 };
+template <int ACT>
+__device__ __forceinline__ float mx_gated(float g, float u) {
+  if (ACT == MX_GELU) return gelu_tanh_f32(u);
+  const float a = (ACT == MX_SWIGLU) ? silu_f32(g) : gelu_tanh_f32(g);
+  return a * u;
+}
+
+// One 32-column block of h for one row, held by the 16 lanes of a lane row
+// group (lane row `row` = column row and 16 + row): block exponent from the
+// 16-lane maximum, E2M1 codes, two per byte written by the even lane, the
+// exponent by lane row 0.  Every lane of the wave must call it (shuffles);
+// `store` says whether this row exists.  codes points at the block's 16
+// bytes of the row, scale at its exponent byte.
+__device__ __forceinline__ void mx_store_h32(float h0, float h1, bool store, int row, uint8_t* codes,
+                                             uint8_t* scale) {
+  float am = __builtin_fmaxf(__builtin_fabsf(h0), __builtin_fabsf(h1));
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) am = __builtin_fmaxf(am, __shfl_xor(am, o, 64));
+  const int e = mx_block_exp(am);
+  const uint32_t c0 = e2m1_code(ldexpf(h0, 127 - e)), c1 = e2m1_code(ldexpf(h1, 127 - e));
+  const uint32_t p0 = (uint32_t)__shfl_xor((int)c0, 1, 64), p1 = (uint32_t)__shfl_xor((int)c1, 1, 64);
+  if (store && (row & 1) == 0) {
+    codes[row >> 1] = (uint8_t)(c0 | (p0 << 4));
+    codes[8 + (row >> 1)] = (uint8_t)(c1 | (p1 << 4));
+    if (row == 0) *scale = (uint8_t)e;
+  }
+}
+
+__device__ __forceinline__ v4f mx_mfma(v8i a, int sa, v8i b, int sb, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
+}
+
+// Prefill-layout weight exponents (k_mxmm): one byte per lane per (16-row
+// group, 128-K block): ((g * KB + kb) * 64 + lane).
+__host__ __device__ __forceinline__ size_t mx_scale_off_mm(uint32_t prow, uint32_t kb, uint32_t lane, uint32_t KB) {
+  return ((size_t)(prow >> 4) * KB + kb) * 64 + lane;
+}
+
 }  // namespace frt

@@ -22,21 +22,12 @@
 
 namespace frt {
 
-enum { MX_GEGLU = 0, MX_SWIGLU = 1, MX_GELU = 2 };
-
-template <int ACT>
-__device__ __forceinline__ float mx_gated(float g, float u) {
-  if (ACT == MX_GELU) return gelu_tanh_f32(u);
-  const float a = (ACT == MX_SWIGLU) ? silu_f32(g) : gelu_tanh_f32(g);
-  return a * u;
-}
-
 // One thread per (row n, 32-block b) of src [N][K] bf16 (times colw[k] when
 // given, an exact product): block exponent, 32 codes into the packed layout.
 // mode 0: packed row n, 1: gate row, 2: up row (gated layout).
 __global__ __launch_bounds__(256) void k_quant_mx(const uint16_t* __restrict__ src, uint8_t* __restrict__ codes,
                                                   uint8_t* __restrict__ scales, int N, int K, int mode,
-                                                  const uint16_t* __restrict__ colw) {
+                                                  const uint16_t* __restrict__ colw, int mm_layout) {
   const size_t nb = (size_t)K / 32;
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (size_t)N * nb) return;
@@ -76,15 +67,16 @@ __global__ __launch_bounds__(256) void k_quant_mx(const uint16_t* __restrict__ s
   const uint32_t prow = mode == 0 ? (uint32_t)n : (mode == 1 ? gate_row((uint32_t)n) : up_row_gated((uint32_t)n));
   const uint32_t KB = (uint32_t)K / 128, kb = (uint32_t)b >> 2, lane = (prow & 15u) + 16u * ((uint32_t)b & 3u);
   *reinterpret_cast<uint4*>(codes + mx_code_off(prow, kb, lane, KB)) = make_uint4(out[0], out[1], out[2], out[3]);
-  scales[mx_scale_off(prow, kb, lane, KB)] = (uint8_t)e;
+  scales[mm_layout ? mx_scale_off_mm(prow, kb, lane, KB) : mx_scale_off(prow, kb, lane, KB)] = (uint8_t)e;
 }
 
+// mm_layout: exponents in the prefill GEMM's layout (mx_scale_off_mm)
 hipError_t launch_quant_mx(const uint16_t* src, uint8_t* codes, uint8_t* scales, int N, int K, int mode,
-                           const uint16_t* colw, hipStream_t s) {
+                           const uint16_t* colw, hipStream_t s, int mm_layout) {
   if (K % 512) return hipErrorInvalidValue;
   const size_t n = (size_t)N * (K / 32);
   hipLaunchKernelGGL(k_quant_mx, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, codes, scales, N, K, mode,
-                     colw);
+                     colw, mm_layout);
   return hipGetLastError();
 }
 
@@ -104,9 +96,6 @@ __device__ __forceinline__ v8i mx_x16(const uint8_t* p, bool has) {
   r[0] = (int)a.x; r[1] = (int)a.y; r[2] = (int)a.z; r[3] = (int)a.w;
   r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
   return r;
-}
-__device__ __forceinline__ v4f mx_mfma(v8i a, int sa, v8i b, int sb, v4f c) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
 }
 
 // Activation row pointers of tile t: codes [M][K/2], exponents [M][K/32].
@@ -205,18 +194,8 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup_mx(const uint8_t* __rest
     const int m = 16 * t + 4 * q + r;
     const float h0 = GATED ? mx_gated<ACT>(f[0][r], f[1][r]) : mx_gated<ACT>(0.0f, f[0][r]);
     const float h1 = GATED ? mx_gated<ACT>(f[2][r], f[3][r]) : mx_gated<ACT>(0.0f, f[1][r]);
-    float am = __builtin_fmaxf(__builtin_fabsf(h0), __builtin_fabsf(h1));
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) am = __builtin_fmaxf(am, __shfl_xor(am, o, 64));
-    const int e = mx_block_exp(am);
-    const uint32_t c0 = e2m1_code(ldexpf(h0, 127 - e)), c1 = e2m1_code(ldexpf(h1, 127 - e));
-    const uint32_t p0 = (uint32_t)__shfl_xor((int)c0, 1, 64), p1 = (uint32_t)__shfl_xor((int)c1, 1, 64);
-    if (m < M && (row & 1) == 0) {
-      uint8_t* dst = hc + (size_t)m * (I / 2) + (size_t)P * 16 + (row >> 1);
-      dst[0] = (uint8_t)(c0 | (p0 << 4));
-      dst[8] = (uint8_t)(c1 | (p1 << 4));
-      if (row == 0) hs[(size_t)m * (I / 32) + P] = (uint8_t)e;
-    }
+    const int mm = m < M ? m : 0;
+    mx_store_h32(h0, h1, m < M, row, hc + (size_t)mm * (I / 2) + (size_t)P * 16, hs + (size_t)mm * (I / 32) + P);
   }
 }
 

@@ -37,7 +37,7 @@ def test_library_is_in_tree():
 @pytest.mark.parametrize("bad", [
     dict(M=0), dict(L=0), dict(H=100), dict(I=200), dict(H=16384 + 128), dict(act=3),
     dict(eps=0.0), dict(eps=float("nan")), dict(flags=64), dict(flags=77), dict(flags=16 | 8), dict(flags=16 | 2),
-    dict(flags=32, H=384), dict(flags=32, I=1536 + 128), dict(flags=32, M=65), dict(flags=32 | 1), dict(flags=32 | 4),
+    dict(flags=32, H=384), dict(flags=32, I=1536 + 128), dict(flags=32 | 1), dict(flags=32 | 4),
     dict(flags=32 | 2), dict(flags=32 | 8), dict(device=-1)])
 def test_bad_descriptors_rejected(bad):
     kw = dict(M=16, H=256, I=1024, L=1, act=0, eps=1e-6, device=0, flags=0)

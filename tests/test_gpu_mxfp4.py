@@ -168,6 +168,34 @@ def test_mxfp4_small_ada_norm():
     run_mx_case(FFNConfig(idx, "mx_ada_%d" % idx, M, H, I, L, act), flags=_abi.FRT_FLAG_ADA_NORM)
 
 
+# the block-scaled prefill GEMM (M > 64): one and several 128-row tiles,
+# ragged tails, all three activations, the K-split down GEMM
+MM = [
+    (137, 65, 512, 1024, 2, ACT_SWIGLU),
+    (138, 100, 1024, 512, 2, ACT_GELU_TANH),
+    (139, 300, 512, 2048, 2, ACT_GEGLU_TANH),
+]
+
+
+@pytest.mark.parametrize("spec", MM, ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
+def test_mxfp4_prefill_small(spec):
+    idx, M, H, I, L, act = spec
+    run_mx_case(FFNConfig(idx, "mx_mm_%d" % idx, M, H, I, L, act))
+
+
+def test_mxfp4_prefill_awq():
+    run_mx_case(FFNConfig(140, "mx_mm_awq", 129, 1024, 1536, 2, ACT_SWIGLU), awq=True)
+
+
+@pytest.mark.timeout(900)
+def test_mxfp4_vlm_prefix_m788_full_size():
+    # the pages' 4-bit encoder FFN shape: 18 layers, 768 image + 20 text rows
+    cfg = CONFIGS[3]
+    rng = np.random.default_rng(37)
+    rows = sorted(set(range(768, 788)) | set(rng.choice(768, 44, replace=False).tolist()))
+    run_mx_case(cfg, awq=True, rows=rows)
+
+
 def test_mxfp4_action_expert_m50_chain():
     run_mx_case(CONFIGS[2], awq=True)
 
