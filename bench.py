@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0   # dense FP8 MFMA
 F16_PEAK_TFLOPS = 2500.0   # dense fp16 MFMA
+FP4_PEAK_TFLOPS = 10100.0  # dense FP4 (MXFP4) MFMA
 
 
 def log(msg):
@@ -131,7 +132,7 @@ def measure_mxfp4(steps, warmup):
     from realtime_transformer_amd import _abi, datagen
     from realtime_transformer_amd.configs import BY_NAME
     res = {"format": "OCP MXFP4 (E2M1, E8M0 per 32 along K), AWQ pre-scale, bf16 residual"}
-    for name in ("llm_decode_m1", "action_expert_m50"):
+    for name in ("llm_decode_m1", "action_expert_m50", "vlm_prefix_m788"):
         c = BY_NAME[name]
         p, _, _ = setup_mx(c)
         ms, _ = time_replays(p, steps, warmup)
@@ -142,14 +143,23 @@ def measure_mxfp4(steps, warmup):
         dn_b = c.I * c.H * f + c.M * c.I * f + 2 * c.M * c.H
         layer_b = gu_b + dn_b + 7 * c.M * c.H + 2 * c.H
         us = float(ms) * 1000.0 / c.L
-        gbs = gu_b / (k[1] * 1e-3) / 1e9
-        res[name] = {"us_per_layer": round(us, 3), "layer_bytes": int(layer_b),
-                     "chain_hbm_gbs": round(layer_b / (us * 1e-6) / 1e9, 1),
-                     "kernels_us": {"norm_quant": round(k[0] * 1000, 3), "gateup": round(k[1] * 1000, 3),
-                                    "down": round(k[2] * 1000, 3)},
-                     "roofline": {"bound": "hbm", "kernel": "gemv_gateup_mx", "achieved": round(gbs, 1),
-                                  "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                                  "bytes_per_launch": int(gu_b)}}
+        rec = {"us_per_layer": round(us, 3), "layer_bytes": int(layer_b),
+               "chain_hbm_gbs": round(layer_b / (us * 1e-6) / 1e9, 1),
+               "kernels_us": {"norm_quant": round(k[0] * 1000, 3), "gateup": round(k[1] * 1000, 3),
+                              "down": round(k[2] * 1000, 3)}}
+        if c.M <= 64:
+            gbs = gu_b / (k[1] * 1e-3) / 1e9
+            rec["roofline"] = {"bound": "hbm", "kernel": "gemv_gateup_mx", "achieved": round(gbs, 1),
+                               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                               "bytes_per_launch": int(gu_b)}
+        else:
+            tf_gu = c.gateup_flops() / (k[1] * 1e-3) / 1e12
+            tf_chain = c.layer_flops() / (us * 1e-6) / 1e12
+            rec["chain_tflops"] = round(tf_chain, 1)
+            rec["roofline"] = {"bound": "mfma", "kernel": "mxmm_gateup", "achieved": round(tf_gu, 1),
+                               "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf_gu / FP4_PEAK_TFLOPS, 4),
+                               "flops_per_launch": c.gateup_flops()}
+        res[name] = rec
         log("[bench %s mxfp4] %.2f us/layer (norm %.2f gate/up %.2f down %.2f us)" % (
             name, us, k[0] * 1000, k[1] * 1000, k[2] * 1000))
     return res

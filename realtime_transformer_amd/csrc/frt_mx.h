@@ -23,31 +23,57 @@ __host__ __device__ __forceinline__ size_t mx_scale_off(uint32_t prow, uint32_t 
   return (((size_t)(prow >> 4) * (KB >> 2) + (kb >> 2)) * 64 + lane) * 4 + (kb & 3);
 }
 
+// floor(log2(amax)) from the exponent field (frexp: amax = f * 2^x, f in
+// [0.5, 1)); amax below 2^-126 (zero, subnormal) gives e = 0 either way.
 __device__ __forceinline__ int mx_block_exp(float amax) {
-  if (!(amax > 0.0f)) return 0;
-  const int e = ilogbf(amax) - 2 + 127;
+  if (!(amax >= 0x1p-126f)) return 0;
+  const int e = __builtin_amdgcn_frexp_expf(amax) - 1 - 2 + 127;
   return e < 0 ? 0 : (e > 254 ? 254 : e);
 }
 
-// E2M1 code of v (already divided by the block scale): the magnitude code is
-// the number of decision points passed -- the midpoints 0.25, 0.75, 1.25,
-// 1.75, 2.5, 3.5, 5 between neighbouring magnitudes, each a strict or
-// non-strict comparison so that a value on a midpoint goes to the neighbour
-// with mantissa bit 0 (0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2,
-// 3.5 -> 4, 5 -> 4); NaN takes the largest magnitude.  No branches.
-__device__ __forceinline__ uint32_t e2m1_code(float v) {
-  const float a = __builtin_fabsf(v);
-  uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
-               (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
-  c = (a == a) ? c : 7u;
-  return c | ((__float_as_uint(v) >> 28) & 8u);
+// Lane moves inside a 16-lane row (DPP, no LDS round trip): quad_perm
+// [1,0,3,2] and [2,3,0,1] exchange lane pairs and pairs of pairs,
+// row_half_mirror reverses each 8 lanes, row_mirror the 16.
+enum { DPP_QUAD_X1 = 0xB1, DPP_QUAD_X2 = 0x4E, DPP_ROW_HALF_MIRROR = 0x141, DPP_ROW_MIRROR = 0x140 };
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+// maximum over each aligned group of 4 lanes, and of 16 lanes
+__device__ __forceinline__ float quad_max(float v) {
+  v = __builtin_fmaxf(v, dpp_f32<DPP_QUAD_X1>(v));
+  return __builtin_fmaxf(v, dpp_f32<DPP_QUAD_X2>(v));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = quad_max(v);
+  v = __builtin_fmaxf(v, dpp_f32<DPP_ROW_HALF_MIRROR>(v));
+  return __builtin_fmaxf(v, dpp_f32<DPP_ROW_MIRROR>(v));
+}
+
+// E2M1 codes of two values already divided by the block scale, packed into
+// byte SEL of w (x0 low nibble, x1 high): gfx950's v_cvt_scalef32_pk_fp4_f32
+// with unit scale.  It rounds to nearest with ties to the even mantissa,
+// saturates at 6 and keeps the sign (including -0); NaN takes the largest
+// magnitude -- the encoding the format defines, checked value by value over
+// [-10, 10] in steps of 2^-8, each midpoint and its neighbouring floats,
+// zeros, subnormals, infinities and NaN.
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_pack2(uint32_t w, float x0, float x1) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x0, x1, 1.0f, SEL);
 }
 
 // eight values of one 32-block (scale exponent e) -> one dword of codes
 __device__ __forceinline__ uint32_t mx_pack8(const float x[8], int e) {
+  const int s = 127 - e;
   uint32_t w = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) w |= e2m1_code(ldexpf(x[j], 127 - e)) << (4 * j);
+  w = e2m1_pack2<0>(w, ldexpf(x[0], s), ldexpf(x[1], s));
+  w = e2m1_pack2<1>(w, ldexpf(x[2], s), ldexpf(x[3], s));
+  w = e2m1_pack2<2>(w, ldexpf(x[4], s), ldexpf(x[5], s));
+  w = e2m1_pack2<3>(w, ldexpf(x[6], s), ldexpf(x[7], s));
   return w;
 }
 
@@ -63,20 +89,19 @@ __device__ __forceinline__ float mx_gated(float g, float u) {
 // One 32-column block of h for one row, held by the 16 lanes of a lane row
 // group (lane row `row` = column row and 16 + row): block exponent from the
 // 16-lane maximum, E2M1 codes, two per byte written by the even lane, the
-// exponent by lane row 0.  Every lane of the wave must call it (shuffles);
+// exponent by lane row 0.  Every lane of the wave must call it (lane moves);
 // `store` says whether this row exists.  codes points at the block's 16
 // bytes of the row, scale at its exponent byte.
 __device__ __forceinline__ void mx_store_h32(float h0, float h1, bool store, int row, uint8_t* codes,
                                              uint8_t* scale) {
-  float am = __builtin_fmaxf(__builtin_fabsf(h0), __builtin_fabsf(h1));
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) am = __builtin_fmaxf(am, __shfl_xor(am, o, 64));
+  const float am = row16_max(__builtin_fmaxf(__builtin_fabsf(h0), __builtin_fabsf(h1)));
   const int e = mx_block_exp(am);
-  const uint32_t c0 = e2m1_code(ldexpf(h0, 127 - e)), c1 = e2m1_code(ldexpf(h1, 127 - e));
-  const uint32_t p0 = (uint32_t)__shfl_xor((int)c0, 1, 64), p1 = (uint32_t)__shfl_xor((int)c1, 1, 64);
+  const float x0 = ldexpf(h0, 127 - e), x1 = ldexpf(h1, 127 - e);
+  // the odd lane's values reach its even neighbour, which packs the byte
+  const uint32_t b = e2m1_pack2<1>(e2m1_pack2<0>(0u, x0, dpp_f32<DPP_QUAD_X1>(x0)), x1, dpp_f32<DPP_QUAD_X1>(x1));
   if (store && (row & 1) == 0) {
-    codes[row >> 1] = (uint8_t)(c0 | (p0 << 4));
-    codes[8 + (row >> 1)] = (uint8_t)(c1 | (p1 << 4));
+    codes[row >> 1] = (uint8_t)b;
+    codes[8 + (row >> 1)] = (uint8_t)(b >> 8);
     if (row == 0) *scale = (uint8_t)e;
   }
 }

@@ -70,10 +70,16 @@ __global__ __launch_bounds__(256) void k_mxmm(const uint8_t* __restrict__ xc, co
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wa = wave >> 1, wn = wave & 1;
 
-  // work item: split-major, then column tile, then row tile
+  // Work item: split-major, then column tile, then row tile.  Consecutive
+  // workgroups go to different XCDs (round robin over 8); workgroup b runs
+  // item (b % 8) * q + min(b % 8, r) + b / 8 (T = 8 q + r items), so XCD x
+  // holds one contiguous range of items: all row tiles of a column tile
+  // share that XCD's L2, which fetches the weight panel once.
   int sp, tn, tm;
   {
-    const int idx = blockIdx.x;
+    const int T = tiles_n * tiles_m * S, q = T >> 3, r = T & 7;
+    const int x = blockIdx.x & 7;
+    const int idx = x * q + (x < r ? x : r) + (blockIdx.x >> 3);
     sp = idx / (tiles_n * tiles_m);
     const int rem = idx - sp * tiles_n * tiles_m;
     tn = rem / tiles_m;

@@ -148,8 +148,7 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
       float am = 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) am = __builtin_fmaxf(am, __builtin_fabsf(x[j]));
-      am = __builtin_fmaxf(am, __shfl_xor(am, 1, 64));
-      am = __builtin_fmaxf(am, __shfl_xor(am, 2, 64));
+      am = quad_max(am);
       const int e = mx_block_exp(am);
       const uint32_t codes = mx_pack8(x, e);
       if (ok) {

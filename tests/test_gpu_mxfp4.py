@@ -207,6 +207,70 @@ def test_mxfp4_llm_decode_m1_full_size():
     run_mx_case(CONFIGS[4], awq=True, check_layers=[0, 1, 21, 42, 63], chain=False)
 
 
+# E2M1 decision points (between neighbouring magnitudes) and the grid itself,
+# in units of the block scale
+_E2M1_MIDPOINTS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+_E2M1_GRID = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def _edge_weights(rows, cols, seed):
+    """bf16 bits [rows, cols] built so that every 32-block tests the encoder at
+    its boundaries: one value of magnitude 6 * 2^k or 7.5 * 2^k fixes the
+    block exponent at 127 + k (clamped to 0 for the smallest k), the other 31
+    are drawn from the midpoints, one bf16 step below and above each, the grid,
+    values past 6 (saturating), zeros of both signs and bf16 subnormals, each
+    times 2^k with a random sign.  A few blocks are all +0 or all -0."""
+    rng = np.random.default_rng(seed)
+    mid = datagen.to_bf16_bits(np.array(_E2M1_MIDPOINTS, np.float32)).astype(np.int64)
+    pool_bits = np.concatenate([mid, mid - 1, mid + 1])
+    pool = np.concatenate([
+        pool_bits.astype(np.uint16).view(np.uint16).astype(np.uint32) << 16,
+        (datagen.to_bf16_bits(np.array(_E2M1_GRID + (6.5, 7.0, 7.5), np.float32)).astype(np.uint32) << 16),
+    ]).view(np.float32)
+    nb = cols // 32
+    out = np.empty((rows, cols), np.float32)
+    ks = rng.integers(-40, 12, size=(rows, nb))
+    low = rng.random((rows, nb)) < 0.05  # the exponent clamp region
+    ks[low] = rng.integers(-133, -122, size=int(low.sum()))
+    for r in range(rows):
+        for b in range(nb):
+            k = int(ks[r, b])
+            v = rng.choice(pool, 32) * rng.choice(np.array([-1.0, 1.0], np.float32), 32)
+            v[rng.integers(32)] = rng.choice(np.array([6.0, 7.5, -6.0, -7.5], np.float32))
+            out[r, b * 32:(b + 1) * 32] = np.ldexp(v.astype(np.float64), k).astype(np.float32)
+    bits = datagen.to_bf16_bits(out)
+    sub = rng.random((rows, cols)) < 0.02  # bf16 subnormals (both signs)
+    bits[sub] = (rng.integers(1, 128, size=int(sub.sum())) | (rng.integers(0, 2, size=int(sub.sum())) << 15)).astype(
+        np.uint16)
+    bits[0, :32] = 0x0000
+    bits[1, :32] = 0x8000
+    return bits
+
+
+def test_mxfp4_weight_codes_on_rounding_boundaries():
+    """The device encoder (codes and block exponents of the packed weights,
+    both exponent layouts) against the oracle's on values placed on and next to
+    every E2M1 rounding boundary, in blocks whose exponent spans the clamp."""
+    for M in (1, 100):  # GEMV and prefill exponent layouts
+        cfg = FFNConfig(141, "mx_edges", M, 512, 512, 1, ACT_SWIGLU)
+        wg, wu, wd = (_edge_weights(r, c, 90 + i) for i, (r, c) in enumerate(((512, 512), (512, 512), (512, 512))))
+        wn = datagen.layer_weights(cfg, 0)[3]
+        plan = FFNPlan(cfg.M, cfg.H, cfg.I, cfg.L, cfg.act, cfg.eps, flags=_abi.FRT_FLAG_MXFP4)
+        try:
+            plan.load_layer(0, wg, wu, wd, wn)
+            lw = oracle.MxLayerWeights.quantize(wg, wu, wd, wn)
+            for which, ref in ((0, lw.g), (1, lw.u), (2, lw.d)):
+                c, e = plan.export_mx(0, which)
+                assert np.array_equal(e, ref[1]), "M=%d tensor %d: %d exponents differ" % (
+                    M, which, int(np.count_nonzero(e != ref[1])))
+                assert np.array_equal(c, ref[0]), "M=%d tensor %d: %d code bytes differ" % (
+                    M, which, int(np.count_nonzero(c != ref[0])))
+            log("[mx edges M=%d] codes and exponents bit-exact; exponents span %d..%d" % (
+                M, int(lw.u[1].min()), int(lw.u[1].max())))
+        finally:
+            plan.close()
+
+
 def test_mxfp4_rejects_calibration_and_fp8_exports():
     cfg = FFNConfig(136, "mx_api", 2, 512, 512, 1, ACT_SWIGLU)
     plan = FFNPlan(cfg.M, cfg.H, cfg.I, cfg.L, cfg.act, cfg.eps, flags=_abi.FRT_FLAG_MXFP4)
