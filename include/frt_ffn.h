@@ -114,12 +114,15 @@ typedef enum {
  *     gate/up: weights f32(W[i][k] * s[k]) in MXFP4; g, u fp32-accumulated
  *         block-scaled products; h = act(g) * u; HQ = MXFP4(h) along I
  *     down: Y = bf16(fp32-accumulated block-scaled products)
- *   M <= 64 runs GEMVs, larger M the block-scaled prefill GEMM (128 x 128
- *   tiles, K split for the down projection into fp32 partials).  Requires H
- *   and I multiples of 512; excludes the FP8, fused-norm and norm-fusion
- *   flags.  Slots: each XQ slot holds codes [M][H/2] (two per
- *   byte, low nibble first) followed by exponents [M][H/32]; HQ likewise with
- *   I. */
+ *   M <= 64 runs GEMVs, larger M the block-scaled prefill GEMM (128 x 256
+ *   tiles for gate/up, 128 x 128 with K split into fp32 partials for down).
+ *   Requires H and I multiples of 512; excludes the FP8, fused-norm and
+ *   norm-fusion flags.  Slots: each XQ slot holds codes [M][H/2] (two per
+ *   byte, low nibble first) followed by the exponents: for M <= 64 row-major
+ *   [M][H/32]; for M > 64 in the prefill layout, rows padded to a multiple
+ *   of 128 -- the exponent of row m, 32-block b at byte
+ *   ((m/64) * (H/128) + b/4) * 256 + ((b%4) * 16 + m%16) * 4 + (m/16)%4.
+ *   HQ likewise with I. */
 #define FRT_FLAG_MXFP4 32u
 
 /* Problem description.  Requirements: M >= 1, L >= 1, H and I multiples of

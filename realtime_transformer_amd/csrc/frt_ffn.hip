@@ -50,12 +50,12 @@ hipError_t launch_gemv_down_mt(const uint8_t*, const uint8_t*, uint16_t*, float*
 bool gemv_fused_supported(int, int, int);
 hipError_t launch_add_rmsnorm_mx(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*, const float*,
                                  uint16_t*, uint8_t*, uint8_t*, int, int, float, hipStream_t, const float*, int, float,
-                                 uint16_t*);
+                                 uint16_t*, int);
 hipError_t launch_quant_mx(const uint16_t*, uint8_t*, uint8_t*, int, int, int, const uint16_t*, hipStream_t, int);
 hipError_t launch_mxmm_gateup(int, const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, uint8_t*, uint8_t*,
                               int, int, int, hipStream_t);
 hipError_t launch_mxmm_down(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, uint16_t*, float*, int, int,
-                            int, int, hipStream_t);
+                            int, int, int, hipStream_t);
 hipError_t launch_gemv_gateup_mx(int, const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, uint8_t*,
                                  uint8_t*, int, int, int, int, hipStream_t);
 hipError_t launch_gemv_down_mx(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, uint16_t*, float*, int,
@@ -149,7 +149,8 @@ struct Layout {
   int split_dn;    // K splits of the down projection, either path (> 1: fp32 partials)
   bool gemv_mt;    // 16 < M <= 64 on the multi-tile GEMVs
   bool mx;         // MXFP4 plan
-  bool mx_mm;      // MXFP4 with M > 64: the prefill GEMMs (k_mxmm), their exponent layout
+  bool mx_mm;      // MXFP4 with M > 64: the prefill GEMMs (k_mxmm), their exponent layouts
+  int mx_dn_nb;    // prefill down GEMM: weight blocks per wave (column tile 32 * nb)
   size_t wgu_sc, wd_sc;        // MXFP4: offset of the exponents inside a layer's weights
   size_t xq_stride, hq_stride; // bytes per XQ / HQ slot
   size_t awq, inv_awq;         // MXFP4: AWQ scale bf16 [L][H], its reciprocal fp32 [L][H]
@@ -278,14 +279,17 @@ Layout make_layout(const frt_ffn_desc& d) {
     return at;
   };
   lo.mx = (d.flags & FRT_FLAG_MXFP4) != 0u;
+  lo.mx_mm = lo.mx && d.M > kGemvMtMaxM;
   if (lo.mx) {
-    // codes (half a byte per weight) then one exponent per 32 weights
+    // codes (half a byte per weight) then one exponent per 32 weights; the
+    // prefill GEMM's activation exponents cover rows padded to 128
+    const size_t Mx = lo.mx_mm ? (size_t)ceil_div(d.M, 128) * 128 : M;
     lo.wgu_sc = align256(npk * H / 2);
     lo.wgu_layer = lo.wgu_sc + align256(npk * H / 32);
     lo.wd_sc = align256(H * I / 2);
     lo.wd_layer = lo.wd_sc + align256(H * I / 32);
-    lo.xq_stride = align256(M * H / 2 + M * H / 32);
-    lo.hq_stride = align256(M * I / 2 + M * I / 32);
+    lo.xq_stride = align256(M * H / 2 + Mx * H / 32);
+    lo.hq_stride = align256(M * I / 2 + Mx * I / 32);
   } else {
     lo.wgu_layer = align256(npk * H);
     lo.wd_layer = align256(H * I);
@@ -306,11 +310,11 @@ Layout make_layout(const frt_ffn_desc& d) {
 
   size_t part = 0, words = 1;
   lo.gemv_mt = d.M > kGemvMaxM && d.M <= std::min(kGemvMtMaxM, env_int("FRT_GEMV_MT_MAX_M", kGemvMtMaxM));
-  lo.mx_mm = lo.mx && d.M > kGemvMtMaxM;
   if (lo.mx_mm) {
-    // K split of the MXFP4 down GEMM until the 128 x 128 tiles give at least
-    // one workgroup per CU (each split at least 8 stages)
-    const int tiles = (int)(H / 128) * ceil_div(d.M, 128);
+    // K split of the MXFP4 down GEMM until its 128 x (32 nb) tiles give at
+    // least one workgroup per CU (each split at least 8 stages)
+    lo.mx_dn_nb = env_int("FRT_MXMM_DOWN_NB", 4) == 8 && H % 256 == 0 ? 8 : 4;
+    const int tiles = (int)(H / (32 * lo.mx_dn_nb)) * ceil_div(d.M, 128);
     int sp = 1;
     while (tiles * sp < kCUs && (int)(I / 128) / (2 * sp) >= 8 && sp < 8) sp *= 2;
     sp = std::max(1, std::min(env_int("FRT_MXMM_DOWN_SPLIT", sp), (int)(I / 128)));
@@ -811,7 +815,8 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
     if (which == 0) {
       const float* yp = (y_in_partials && l > 0) ? p->part() : nullptr;
       KERNEL_CHECK(launch_add_rmsnorm_mx(p->r(l), p->y(l), p->wn(l), p->mod(l), p->inv_awq(l), p->r(l + 1), p->xq(l),
-                                         p->xs(l), M, H, p->d.eps, s, yp, p->lo.split_dn, 1.0f, p->y(l)),
+                                         p->xs(l), M, H, p->d.eps, s, yp, p->lo.split_dn, 1.0f, p->y(l),
+                                         p->lo.mx_mm ? 1 : 0),
                    "add_rmsnorm_mx");
     } else if (which == 1 && p->lo.mx_mm) {
       KERNEL_CHECK(launch_mxmm_gateup(p->d.act, p->xq(l), p->xs(l), p->wgu(l), p->wgu_s(l), p->hq(l), p->hs(l), M, H,
@@ -823,7 +828,7 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
                    "gemv_gateup_mx");
     } else if (p->lo.mx_mm) {
       KERNEL_CHECK(launch_mxmm_down(p->hq(l), p->hs(l), p->wd(l), p->wd_s(l), p->y(l + 1), p->part(), M, I, H,
-                                    p->lo.split_dn, s),
+                                    p->lo.split_dn, p->lo.mx_dn_nb, s),
                    "mxmm_down");
     } else {
       KERNEL_CHECK(launch_gemv_down_mx(p->hq(l), p->hs(l), p->wd(l), p->wd_s(l), p->y(l + 1), p->part(), M, I, H,

@@ -110,10 +110,18 @@ __device__ __forceinline__ v4f mx_mfma(v8i a, int sa, v8i b, int sb, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
 }
 
-// Prefill-layout weight exponents (k_mxmm): one byte per lane per (16-row
-// group, 128-K block): ((g * KB + kb) * 64 + lane).
+// Prefill-layout exponents (k_mxmm), arranged so that one 32-bit LDS read
+// gives a lane the exponents of four MFMA operands and the instruction picks
+// the byte (op_sel).  Weights: per (quad of 16-row groups, 128-K block) 64
+// lanes x 4 bytes, byte j = group 4 * quad + j.
 __host__ __device__ __forceinline__ size_t mx_scale_off_mm(uint32_t prow, uint32_t kb, uint32_t lane, uint32_t KB) {
-  return ((size_t)(prow >> 4) * KB + kb) * 64 + lane;
+  return ((size_t)(prow >> 6) * KB + kb) * 256 + lane * 4 + ((prow >> 4) & 3u);
+}
+// Activations (rows padded to a multiple of 128): per (64-row group, 128-K
+// block) 64 lanes x 4 bytes; lane = 32-sub-block * 16 + row % 16 (the
+// operand's lane), byte i = 16-row block i of the group.  Row m, 32-block b.
+__host__ __device__ __forceinline__ size_t mx_act_scale_off_mm(uint32_t m, uint32_t b, uint32_t KB) {
+  return ((size_t)(m >> 6) * KB + (b >> 2)) * 256 + (((b & 3u) * 16u + (m & 15u)) * 4u) + ((m >> 4) & 3u);
 }
 
 }  // namespace frt

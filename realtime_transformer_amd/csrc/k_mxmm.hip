@@ -4,24 +4,33 @@
 // down GEMMs over a few hundred prefix tokens, a gated combine that
 // re-quantises to 4 bits); the format is OCP MXFP4 (frt_mx.h).
 //
-// Tile: 128 activation rows x 128 packed weight rows per workgroup, four
-// waves of 64 x 64 (4 x 4 blocks of 16 x 16).  K advances in stages of 128
-// values (64 bytes of codes per row).  Per stage each 16-row block of either
-// operand is one 1 KiB run in LDS in the operand order of the block-scaled
-// FP4 instruction (lane l: row l % 16, values (l / 16) * 32 .. + 32), so one
-// ds_read_b128 per block feeds one v_mfma_scale_f32_16x16x128_f8f6f4; the
-// exponents of the stage are staged beside the codes (activations: 4 bytes
-// per row; weights: 64 bytes per 16-row group in the prefill layout, one per
-// lane).  All staging is direct-to-LDS (global_load_lds_dwordx4 / _dword):
-// each wave issues exactly five such loads per stage (two activation runs,
-// two weight runs, one exponent run), into a ring of four stage buffers, so
-// its wait counts are static.
+// Tile: 128 activation rows x 32*NB packed weight rows per workgroup, four
+// waves of 64 x 16*NB (4 x NB blocks of 16 x 16).  K advances in stages of
+// 128 values (64 bytes of codes per row).  Per stage each 16-row block of
+// either operand is one 1 KiB run in LDS in the operand order of the
+// block-scaled FP4 instruction (lane l: row l % 16, values (l / 16) * 32 ..
+// + 32), so one ds_read_b128 per block feeds one
+// v_mfma_scale_f32_16x16x128_f8f6f4; the exponents of the stage are staged
+// beside the codes in the prefill layouts (frt_mx.h), where one 32-bit read
+// gives a lane the exponents of four blocks and op_sel picks the byte.  All
+// staging is direct-to-LDS (global_load_lds_dwordx4 / _dword) into a ring of
+// NS stage buffers; every wave issues the same number of loads per stage, so
+// its wait counts are static, and one barrier per stage both publishes the
+// stage and frees the buffer read one stage earlier.
 //
-// Epilogues: gate/up -- a wave's 64 packed rows are gate 2P, up 2P, gate
-// 2P + 1, up 2P + 1 of intermediate block P (32 columns), so the gated
-// combine and the 4-bit re-quantisation of that block run in registers as in
-// the GEMV (mx_store_h32).  Down -- bf16 Y, or fp32 partials [split][M][N]
-// when K is split over workgroups (summed by the consumer).
+// Why wide tiles: the staging path is the bound (measured with the MFMAs,
+// LDS reads and epilogue switched off: ~12 TB/s from L2 for 128 x 128 tiles
+// at M = 788, K = 2048), so the bytes staged per flop set the time; 128 x 256
+// tiles stage 27% fewer bytes than 128 x 128 for the gate/up GEMM.
+//
+// Epilogues: gate/up -- a wave's packed rows are, per intermediate block P
+// (32 columns), gate 2P, up 2P, gate 2P + 1, up 2P + 1, so the gated combine
+// and the 4-bit re-quantisation of that block run in registers as in the
+// GEMV (mx_store_h32); its exponents go out in the prefill layout for the
+// down GEMM.  Down -- bf16 Y, or fp32 partials [split][M][N] when K is split
+// over workgroups (summed by the consumer).
+#include <utility>
+
 #include "frt_mx.h"
 
 namespace frt {
@@ -46,25 +55,46 @@ __device__ __forceinline__ void mx_lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-constexpr int XBM = 128, XBN = 128, XNS = 4, XOPS = 5;
-constexpr int XA = XBM * 64;               // activation codes
-constexpr int XB = XBN * 64;               // weight codes
-constexpr int XAS = XBM * 4;               // activation exponents: [row][4]
-constexpr int XBS = (XBN / 16) * 64;       // weight exponents: [group][lane]
-constexpr int XSTAGE = XA + XB + XAS + XBS;
-
 typedef int v4i_mx __attribute__((ext_vector_type(4)));
 
-template <int EPI>
-__global__ __launch_bounds__(256) void k_mxmm(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs,
-                                              const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
-                                              uint8_t* __restrict__ hc, uint8_t* __restrict__ hs,
-                                              uint16_t* __restrict__ y, float* __restrict__ part, int M, int K,
-                                              int Npk, int tiles_n, int tiles_m, int S) {
-  __shared__ __attribute__((aligned(1024))) uint8_t l0[XSTAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t l1[XSTAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t l2[XSTAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t l3[XSTAGE];
+// Tile geometry for NB weight blocks per wave (4: 128 x 128 tiles, 4-stage
+// ring; 8: 128 x 256 tiles, 3-stage ring -- both leave room for two
+// workgroups per CU).
+template <int NB>
+struct MxTile {
+  static constexpr int BM = 128, BN = 32 * NB, NS = NB == 8 ? 3 : 4;
+  static constexpr int XA = BM * 64;          // activation codes: 8 runs of 1 KiB
+  static constexpr int XB = BN * 64;          // weight codes: 2 NB runs
+  static constexpr int XAS = 2 * 256;         // activation exponents: 2 row groups x 64 lanes x 4
+  static constexpr int XBS = (BN / 64) * 256; // weight exponents: NB / 2 group quads x 64 lanes x 4
+  static constexpr int STAGE = XA + XB + XAS + XBS;
+  static constexpr int CRUNS = 2 + NB / 2;       // code runs per wave per stage
+  static constexpr int ERUNS = NB == 8 ? 2 : 1;  // exponent runs per wave per stage
+  static constexpr int OPS = CRUNS + ERUNS;
+};
+
+template <int OA, int OB>
+__device__ __forceinline__ v4f mx_mfma_sel(v8i a, int sa, v8i b, int sb, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, OA, sa, OB, sb);
+}
+// all 4 x NB products of one stage; the exponent bytes are op_sel immediates
+template <int NB, int... IJ>
+__device__ __forceinline__ void mx_mma_all(v4f (&acc)[4][NB], const v8i (&a)[4], const v8i (&b)[NB], int sa,
+                                           const int (&sb)[NB / 4], std::integer_sequence<int, IJ...>) {
+  ((acc[IJ / NB][IJ % NB] = mx_mfma_sel<IJ / NB, (IJ % NB) & 3>(a[IJ / NB], sa, b[IJ % NB], sb[(IJ % NB) >> 2],
+                                                               acc[IJ / NB][IJ % NB])),
+   ...);
+}
+
+template <int EPI, int NB>
+__global__ __launch_bounds__(256, 2) void k_mxmm(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs,
+                                                 const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
+                                                 uint8_t* __restrict__ hc, uint8_t* __restrict__ hs,
+                                                 uint16_t* __restrict__ y, float* __restrict__ part, int M, int K,
+                                                 int Npk, int tiles_n, int tiles_m, int S) {
+  using T = MxTile<NB>;
+  constexpr int NS = T::NS;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * T::STAGE];
   constexpr bool DOWN = EPI == MXM_DOWN;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -77,7 +107,7 @@ __global__ __launch_bounds__(256) void k_mxmm(const uint8_t* __restrict__ xc, co
   // share that XCD's L2, which fetches the weight panel once.
   int sp, tn, tm;
   {
-    const int T = tiles_n * tiles_m * S, q = T >> 3, r = T & 7;
+    const int Ti = tiles_n * tiles_m * S, q = Ti >> 3, r = Ti & 7;
     const int x = blockIdx.x & 7;
     const int idx = x * q + (x < r ? x : r) + (blockIdx.x >> 3);
     sp = idx / (tiles_n * tiles_m);
@@ -85,17 +115,18 @@ __global__ __launch_bounds__(256) void k_mxmm(const uint8_t* __restrict__ xc, co
     tn = rem / tiles_m;
     tm = rem - tn * tiles_m;
   }
-  const int m0 = tm * XBM, n0 = tn * XBN;
+  const int m0 = tm * T::BM, n0 = tn * T::BN;
   const int KB = K >> 7;  // stages (128-value blocks)
   const int kb0 = sp * KB / S, kb1 = (sp + 1) * KB / S, nk = kb1 - kb0;
   const int g0 = n0 >> 4;  // first 16-row weight group of the tile
 
-  // This wave's five loads per stage: activation runs r = wave, wave + 4;
-  // weight runs g = wave, wave + 4; one exponent run (waves 0, 1: activation
-  // rows 64 t .. 64 t + 63; waves 2, 3: weight groups 4 t .. 4 t + 3).
-  // Source addresses at stage 0, the stage stride, LDS destinations.
-  const uint8_t* src[XOPS];
-  uint32_t step[XOPS], dst[XOPS];
+  // This wave's loads per stage: code runs (activation runs wave, wave + 4;
+  // weight runs wave + 4 i), then exponent runs e = wave (+ 4): e < 2 the
+  // activation row group e, else the weight group quad e - 2; a wave whose
+  // second exponent run index passes the end repeats its first (same bytes
+  // to the same place).  Source at stage 0, stage stride, LDS offset.
+  const uint8_t* src[T::OPS];
+  uint32_t step[T::OPS], dst[T::OPS];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int r = i * 4 + wave;
@@ -104,124 +135,118 @@ __global__ __launch_bounds__(256) void k_mxmm(const uint8_t* __restrict__ xc, co
     src[i] = xc + (size_t)m * (K / 2) + (lane >> 4) * 16;
     step[i] = 64;
     dst[i] = (uint32_t)(r * 1024);
-    const int g = g0 + i * 4 + wave;
-    src[2 + i] = wc + (size_t)g * KB * 1024 + lane * 16;
-    step[2 + i] = 1024;
-    dst[2 + i] = (uint32_t)(XA + (i * 4 + wave) * 1024);
   }
-  if (wave < 2) {
-    int m = m0 + wave * 64 + lane;
-    m = m < M ? m : M - 1;
-    src[4] = xs + (size_t)m * (K / 32);
-    step[4] = 4;
-    dst[4] = (uint32_t)(XA + XB + wave * 256);
-  } else {
-    const int t = wave - 2;
-    const int g = g0 + t * 4 + (lane >> 4);
-    src[4] = ws + (size_t)g * KB * 64 + (lane & 15) * 4;
-    step[4] = 64;
-    dst[4] = (uint32_t)(XA + XB + XAS + t * 256);
-  }
-  auto issue = [&](int kb, uint8_t* base) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) mx_dma16(src[i] + (size_t)kb * step[i], base + dst[i]);
-    mx_dma4(src[4] + (size_t)kb * step[4], base + dst[4]);
+  for (int i = 0; i < NB / 2; ++i) {
+    const int r = i * 4 + wave;
+    src[2 + i] = wc + (size_t)(g0 + r) * KB * 1024 + lane * 16;
+    step[2 + i] = 1024;
+    dst[2 + i] = (uint32_t)(T::XA + r * 1024);
+  }
+#pragma unroll
+  for (int j = 0; j < T::ERUNS; ++j) {
+    int e = wave + 4 * j;
+    if (e >= 2 + NB / 2) e = wave;
+    if (e < 2) {
+      src[T::CRUNS + j] = xs + ((size_t)((m0 >> 6) + e) * KB) * 256 + lane * 4;
+      dst[T::CRUNS + j] = (uint32_t)(T::XA + T::XB + e * 256);
+    } else {
+      src[T::CRUNS + j] = ws + ((size_t)((g0 >> 2) + e - 2) * KB) * 256 + lane * 4;
+      dst[T::CRUNS + j] = (uint32_t)(T::XA + T::XB + T::XAS + (e - 2) * 256);
+    }
+    step[T::CRUNS + j] = 256;
+  }
+  auto issue = [&](int kb, int buf) {
+    uint8_t* base = lds + buf * T::STAGE;
+#pragma unroll
+    for (int i = 0; i < T::CRUNS; ++i) mx_dma16(src[i] + (size_t)kb * step[i], base + dst[i]);
+#pragma unroll
+    for (int j = 0; j < T::ERUNS; ++j)
+      mx_dma4(src[T::CRUNS + j] + (size_t)kb * step[T::CRUNS + j], base + dst[T::CRUNS + j]);
   };
 
-  v4f acc[4][4];
+  v4f acc[4][NB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0, 0, 0, 0};
+    for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0, 0, 0, 0};
 
   // per-lane LDS read offsets inside a stage
   const int a_rd = (wa * 4) * 1024 + lane * 16;
-  const int b_rd = XA + (wn * 4) * 1024 + lane * 16;
-  const int as_rd = XA + XB + ((wa * 4) * 16 + (lane & 15)) * 4 + (lane >> 4);
-  const int bs_rd = XA + XB + XAS + (wn * 4) * 64 + lane;
+  const int b_rd = T::XA + (wn * NB) * 1024 + lane * 16;
+  const int as_rd = T::XA + T::XB + wa * 256 + lane * 4;
+  const int bs_rd = T::XA + T::XB + T::XAS + (wn * (NB / 4)) * 256 + lane * 4;
 
-  auto mma_stage = [&](const uint8_t* base) {
-    v8i a[4], b[4];
-    int sa[4], sb[4];
+  auto mma_stage = [&](int buf) {
+    const uint8_t* base = lds + buf * T::STAGE;
+    v8i a[4], b[NB];
+    int sb[NB / 4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const v4i_mx t = *reinterpret_cast<const v4i_mx*>(base + a_rd + i * 1024);
       a[i] = v8i{t[0], t[1], t[2], t[3], 0, 0, 0, 0};
-      sa[i] = base[as_rd + i * 16 * 4];
-      const v4i_mx u = *reinterpret_cast<const v4i_mx*>(base + b_rd + i * 1024);
-      b[i] = v8i{u[0], u[1], u[2], u[3], 0, 0, 0, 0};
-      sb[i] = base[bs_rd + i * 64];
     }
-    // the fragments are in registers: the buffer may be refilled after the
-    // next barrier
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const v4i_mx u = *reinterpret_cast<const v4i_mx*>(base + b_rd + j * 1024);
+      b[j] = v8i{u[0], u[1], u[2], u[3], 0, 0, 0, 0};
+    }
+    const int sa = *reinterpret_cast<const int*>(base + as_rd);
+#pragma unroll
+    for (int q = 0; q < NB / 4; ++q) sb[q] = *reinterpret_cast<const int*>(base + bs_rd + q * 256);
+    mx_mma_all<NB>(acc, a, b, sa, sb, std::make_integer_sequence<int, 4 * NB>{});
+  };
+
+  // Step t: wait until this wave's loads of stage t have landed (at most
+  // min(NS - 2, nk - 1 - t) later stages outstanding) and its reads of stage
+  // t - 1 are done; the barrier then publishes stage t and frees buffer
+  // (t - 1) % NS, which receives stage t + NS - 1; read stage t, multiply.
+  for (int t = 0; t < NS - 1 && t < nk; ++t) issue(kb0 + t, t);
+  int buf = 0;
+  for (int t = 0; t < nk; ++t) {
+    const int ahead = (nk - 1 - t) < (NS - 2) ? (nk - 1 - t) : (NS - 2);
+    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(mx_waitcnt_vm(2 * T::OPS));
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(mx_waitcnt_vm(T::OPS));
+    else __builtin_amdgcn_s_waitcnt(mx_waitcnt_vm(0));
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     mx_lds_barrier();
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mx_mfma(a[i], sa[i], b[j], sb[j], acc[i][j]);
-  };
-  // stage t complete for this wave once at most `after` later stages of its
-  // loads are outstanding
-  auto wait_stage = [&](int t) {
-    const int after = (nk - 1 - t) < (XNS - 1) ? (nk - 1 - t) : (XNS - 1);
-    if (after >= 3) __builtin_amdgcn_s_waitcnt(mx_waitcnt_vm(3 * XOPS));
-    else if (after == 2) __builtin_amdgcn_s_waitcnt(mx_waitcnt_vm(2 * XOPS));
-    else if (after == 1) __builtin_amdgcn_s_waitcnt(mx_waitcnt_vm(XOPS));
-    else __builtin_amdgcn_s_waitcnt(mx_waitcnt_vm(0));
-    mx_lds_barrier();
-  };
-  // step t: refill the buffer freed at step t - 1 with stage t + 3, wait for
-  // stage t, read its fragments, release its buffer, multiply
-#define FRT_MXMM_STEP(t, FILL, CUR)                     \
-  do {                                                  \
-    if ((t) + XNS - 1 < nk) issue(kb0 + (t) + XNS - 1, FILL); \
-    wait_stage(t);                                      \
-    mma_stage(CUR);                                     \
-  } while (0)
-  if (nk > 0) issue(kb0, l0);
-  if (nk > 1) issue(kb0 + 1, l1);
-  if (nk > 2) issue(kb0 + 2, l2);
-  int t = 0;
-  for (; t + 3 < nk; t += 4) {
-    FRT_MXMM_STEP(t, l3, l0);
-    FRT_MXMM_STEP(t + 1, l0, l1);
-    FRT_MXMM_STEP(t + 2, l1, l2);
-    FRT_MXMM_STEP(t + 3, l2, l3);
+    if (t + NS - 1 < nk) issue(kb0 + t + NS - 1, buf == 0 ? NS - 1 : buf - 1);
+    mma_stage(buf);
+    buf = buf == NS - 1 ? 0 : buf + 1;
   }
-  if (t < nk) FRT_MXMM_STEP(t, l3, l0);
-  if (t + 1 < nk) FRT_MXMM_STEP(t + 1, l0, l1);
-  if (t + 2 < nk) FRT_MXMM_STEP(t + 2, l1, l2);
-#undef FRT_MXMM_STEP
 
   // ---- epilogue ----
   const int row = lane & 15, q = lane >> 4;
   if (!DOWN) {
     const int I = (EPI == MXM_GELU) ? Npk : Npk / 2;
-    // packed groups g0 + 4 wn .. + 3 -> intermediate 32-column block P
-    const int P = (g0 + 4 * wn) >> 2;
+    const uint32_t KBh = (uint32_t)I / 128;
+    // this wave's packed groups g0 + NB wn .. + NB - 1: NB / 4 gated 32-column
+    // blocks starting at P, or NB / 2 plain ones starting at 2 P
+    const int P = (g0 + NB * wn) >> 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + (wa * 4 + i) * 16 + 4 * q + r;
-        float h0, h1;
-        if (EPI == MXM_GELU) {
-          // plain layout: groups 4P' .. 4P' + 3 are two 32-column blocks
-          h0 = mx_gated<MX_GELU>(0.0f, acc[i][0][r]);
-          h1 = mx_gated<MX_GELU>(0.0f, acc[i][1][r]);
-        } else {
-          h0 = mx_gated<EPI>(acc[i][0][r], acc[i][1][r]);
-          h1 = mx_gated<EPI>(acc[i][2][r], acc[i][3][r]);
-        }
         const int mm = m < M ? m : 0;
-        const int Pb = (EPI == MXM_GELU) ? 2 * P : P;
-        mx_store_h32(h0, h1, m < M, row, hc + (size_t)mm * (I / 2) + (size_t)Pb * 16, hs + (size_t)mm * (I / 32) + Pb);
-        if (EPI == MXM_GELU) {
-          const float h2 = mx_gated<MX_GELU>(0.0f, acc[i][2][r]);
-          const float h3 = mx_gated<MX_GELU>(0.0f, acc[i][3][r]);
-          mx_store_h32(h2, h3, m < M, row, hc + (size_t)mm * (I / 2) + (size_t)(Pb + 1) * 16,
-                       hs + (size_t)mm * (I / 32) + Pb + 1);
+        uint8_t* hrow = hc + (size_t)mm * (I / 2);
+#pragma unroll
+        for (int c = 0; c < NB / 4; ++c) {
+          // groups 4c .. 4c + 3 of the wave: one gated block, or two plain
+          if (EPI == MXM_GELU) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int Pb = 2 * P + 2 * c + h;
+              const float h0 = mx_gated<MX_GELU>(0.0f, acc[i][4 * c + 2 * h][r]);
+              const float h1 = mx_gated<MX_GELU>(0.0f, acc[i][4 * c + 2 * h + 1][r]);
+              mx_store_h32(h0, h1, m < M, row, hrow + (size_t)Pb * 16, hs + mx_act_scale_off_mm(mm, Pb, KBh));
+            }
+          } else {
+            const int Pb = P + c;
+            const float h0 = mx_gated<EPI>(acc[i][4 * c][r], acc[i][4 * c + 1][r]);
+            const float h1 = mx_gated<EPI>(acc[i][4 * c + 2][r], acc[i][4 * c + 3][r]);
+            mx_store_h32(h0, h1, m < M, row, hrow + (size_t)Pb * 16, hs + mx_act_scale_off_mm(mm, Pb, KBh));
+          }
         }
       }
     }
@@ -236,8 +261,8 @@ __global__ __launch_bounds__(256) void k_mxmm(const uint8_t* __restrict__ xc, co
       const int m = m0 + (wa * 4 + i) * 16 + 4 * q + r;
       if (m >= M) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const size_t o = (size_t)m * N + (size_t)(g0 + wn * 4 + j) * 16 + row;
+      for (int j = 0; j < NB; ++j) {
+        const size_t o = (size_t)m * N + (size_t)(g0 + wn * NB + j) * 16 + row;
         if (S == 1)
           y[o] = (uint16_t)f32_to_bf16(acc[i][j][r]);
         else
@@ -247,31 +272,37 @@ __global__ __launch_bounds__(256) void k_mxmm(const uint8_t* __restrict__ xc, co
   }
 }
 
-// Gate/up: Npk packed rows (2I gated, I plain), K = H; E4M3-free 4-bit out.
+template <int EPI, int NB>
+static void mxmm_launch(const uint8_t* xc, const uint8_t* xs, const uint8_t* wc, const uint8_t* ws, uint8_t* hc,
+                        uint8_t* hs, uint16_t* y, float* part, int M, int K, int Npk, int S, hipStream_t s) {
+  const int tn = Npk / MxTile<NB>::BN, tm = (M + 127) / 128;
+  hipLaunchKernelGGL((k_mxmm<EPI, NB>), dim3(tn * tm * S), dim3(256), 0, s, xc, xs, wc, ws, hc, hs, y, part, M, K,
+                     Npk, tn, tm, S);
+}
+
+// Gate/up: Npk packed rows (2I gated, I plain), K = H; 4-bit h out (codes
+// row-major [M][I/2], exponents in the prefill layout).  128 x 256 tiles.
 hipError_t launch_mxmm_gateup(int act, const uint8_t* xc, const uint8_t* xs, const uint8_t* wc, const uint8_t* ws,
                               uint8_t* hc, uint8_t* hs, int M, int K, int Npk, hipStream_t s) {
-  if (M < 1 || K % 512 || Npk % XBN) return hipErrorInvalidValue;
-  const int tn = Npk / XBN, tm = (M + XBM - 1) / XBM;
-  const dim3 grid(tn * tm), block(256);
+  if (M < 1 || K % 512 || Npk % 256) return hipErrorInvalidValue;
   if (act == MX_GEGLU)
-    hipLaunchKernelGGL((k_mxmm<MXM_GEGLU>), grid, block, 0, s, xc, xs, wc, ws, hc, hs, nullptr, nullptr, M, K, Npk, tn,
-                       tm, 1);
+    mxmm_launch<MXM_GEGLU, 8>(xc, xs, wc, ws, hc, hs, nullptr, nullptr, M, K, Npk, 1, s);
   else if (act == MX_SWIGLU)
-    hipLaunchKernelGGL((k_mxmm<MXM_SWIGLU>), grid, block, 0, s, xc, xs, wc, ws, hc, hs, nullptr, nullptr, M, K, Npk,
-                       tn, tm, 1);
+    mxmm_launch<MXM_SWIGLU, 8>(xc, xs, wc, ws, hc, hs, nullptr, nullptr, M, K, Npk, 1, s);
   else
-    hipLaunchKernelGGL((k_mxmm<MXM_GELU>), grid, block, 0, s, xc, xs, wc, ws, hc, hs, nullptr, nullptr, M, K, Npk, tn,
-                       tm, 1);
+    mxmm_launch<MXM_GELU, 8>(xc, xs, wc, ws, hc, hs, nullptr, nullptr, M, K, Npk, 1, s);
   return hipGetLastError();
 }
 
-// Down: N = H output columns, K = I; S splits (> 1: fp32 partials).
+// Down: N = H output columns, K = I; S splits (> 1: fp32 partials); column
+// tiles of 32 * nb (nb 4 or 8).
 hipError_t launch_mxmm_down(const uint8_t* hc, const uint8_t* hs, const uint8_t* wc, const uint8_t* ws, uint16_t* y,
-                            float* part, int M, int K, int N, int S, hipStream_t s) {
-  if (M < 1 || K % 512 || N % XBN || S < 1 || S > K / 128) return hipErrorInvalidValue;
-  const int tn = N / XBN, tm = (M + XBM - 1) / XBM;
-  hipLaunchKernelGGL((k_mxmm<MXM_DOWN>), dim3(tn * tm * S), dim3(256), 0, s, hc, hs, wc, ws, nullptr, nullptr, y, part,
-                     M, K, N, tn, tm, S);
+                            float* part, int M, int K, int N, int S, int nb, hipStream_t s) {
+  if (M < 1 || K % 512 || S < 1 || S > K / 128 || (nb != 4 && nb != 8) || N % (32 * nb)) return hipErrorInvalidValue;
+  if (nb == 8)
+    mxmm_launch<MXM_DOWN, 8>(hc, hs, wc, ws, nullptr, nullptr, y, part, M, K, N, S, s);
+  else
+    mxmm_launch<MXM_DOWN, 4>(hc, hs, wc, ws, nullptr, nullptr, y, part, M, K, N, S, s);
   return hipGetLastError();
 }
 

@@ -41,7 +41,8 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
     const uint16_t* __restrict__ w_norm, const uint16_t* __restrict__ mod, uint16_t* __restrict__ r_out,
     uint8_t* __restrict__ xq_out, float* __restrict__ x_out, float* __restrict__ amax_out,
     int M, int H, float eps, float inv_x, const float* __restrict__ y_part, int S, float alpha_d,
-    uint16_t* __restrict__ y_store, const float* __restrict__ inv_awq = nullptr, uint8_t* __restrict__ xs_out = nullptr) {
+    uint16_t* __restrict__ y_store, const float* __restrict__ inv_awq = nullptr, uint8_t* __restrict__ xs_out = nullptr,
+    int xs_mm = 0) {
   constexpr int RPW = 256 / TPR;  // rows per workgroup
   constexpr int WPR = TPR / 64;   // waves per row
   __shared__ double red[256 / 64];
@@ -153,7 +154,9 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
       const uint32_t codes = mx_pack8(x, e);
       if (ok) {
         *reinterpret_cast<uint32_t*>(xq_out + (size_t)row * (H / 2) + (size_t)ch * 4) = codes;
-        if ((ch & 3) == 0) xs_out[(size_t)row * (H / 32) + (ch >> 2)] = (uint8_t)e;
+        if ((ch & 3) == 0)
+          xs_out[xs_mm ? mx_act_scale_off_mm((uint32_t)row, (uint32_t)(ch >> 2), (uint32_t)H / 128)
+                       : (size_t)row * (H / 32) + (ch >> 2)] = (uint8_t)e;
       }
       continue;
     }
@@ -302,19 +305,20 @@ hipError_t launch_add_rmsnorm_quant(const uint16_t* r_prev, const uint16_t* y_pr
                               s, y_part, S, alpha_d, y_store);
 }
 
-// MXFP4 form of K1: xq_codes [M][H/2], xq_scales [M][H/32]; inv_awq [H].
-// H % 32 == 0.
+// MXFP4 form of K1: xq_codes [M][H/2], xq_scales [M][H/32] (xs_mm: the
+// prefill GEMM's exponent layout, rows padded to 128); inv_awq [H].
+// H % 32 == 0 (H % 128 == 0 with xs_mm).
 hipError_t launch_add_rmsnorm_mx(const uint16_t* r_prev, const uint16_t* y_prev, const uint16_t* w,
                                  const uint16_t* mod, const float* inv_awq, uint16_t* r_out, uint8_t* xq_codes,
                                  uint8_t* xq_scales, int M, int H, float eps, hipStream_t s, const float* y_part,
-                                 int S, float alpha_d, uint16_t* y_store) {
-  if (H % 32 || !inv_awq) return hipErrorInvalidValue;
+                                 int S, float alpha_d, uint16_t* y_store, int xs_mm) {
+  if (H % 32 || !inv_awq || (xs_mm && H % 128)) return hipErrorInvalidValue;
   const int nchunk = H / 8;
   const int nc = (nchunk + 255) / 256;
 #define FRT_MX_NORM(NCV)                                                                                          \
   hipLaunchKernelGGL((k_add_rmsnorm_quant<256, NCV, false, true>), dim3(M), dim3(256), 0, s, r_prev, y_prev, w,   \
                      mod, r_out, xq_codes, nullptr, nullptr, M, H, eps, 1.0f, y_part, S, alpha_d, y_store, inv_awq, \
-                     xq_scales)
+                     xq_scales, xs_mm)
   if (nc <= 1)
     FRT_MX_NORM(1);
   else if (nc <= 2)

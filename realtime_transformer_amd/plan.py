@@ -33,6 +33,9 @@ class FFNPlan:
         _abi.load()
         self.M, self.H, self.I, self.L, self.act = M, H, I, L, act
         self.gated = act != _abi.FRT_ACT_GELU_TANH
+        # MXFP4 plans above 64 rows run the prefill GEMMs, whose activation
+        # exponents sit in their own layout (rows padded to 128)
+        self.mx_mm = bool(flags & _abi.FRT_FLAG_MXFP4) and M > 64
         self.device = torch.device("cuda", device)
         self.desc = _abi.make_desc(M, H, I, L, act, eps, device, flags)
         self.nbytes = _abi.frt_ffn_workspace_size(self.desc)
@@ -124,16 +127,30 @@ class FFNPlan:
         rows, cols = (self.H, self.I) if which == 2 else (self.I, self.H)
         return _abi.frt_export_mxfp4_weights(self.plan, layer, which, rows, cols)
 
+    def _mx_slot(self, addr: int, K: int):
+        n = self.M * K // 2
+        if not self.mx_mm:
+            v = self._view(addr, n + n // 16)
+            return v[:n].view(self.M, K // 2), v[n:].view(self.M, K // 32)
+        # prefill layout: per (64-row group, 128-K block) 64 lanes x 4 bytes,
+        # lane = 32-sub-block * 16 + row % 16, byte = (row / 16) % 4; gathered
+        # here into row-major order (a copy)
+        mp = -(-self.M // 128) * 128
+        v = self._view(addr, n + mp * K // 32)
+        m = np.arange(self.M, dtype=np.int64)[:, None]
+        b = np.arange(K // 32, dtype=np.int64)[None, :]
+        off = ((m >> 6) * (K // 128) + (b >> 2)) * 256 + ((b & 3) * 16 + (m & 15)) * 4 + ((m >> 4) & 3)
+        idx = torch.as_tensor(off.reshape(-1), device=self.device)
+        return v[:n].view(self.M, K // 2), v[n:][idx].view(self.M, K // 32)
+
     def xq_mx(self, l: int):
-        """MXFP4 plans: XQ slot l as (codes [M][H/2], exponents [M][H/32]) uint8 views."""
-        n = self.M * self.H // 2
-        v = self._view(self.io.xq_slots + l * self.io.stride_xq, n + n // 16)
-        return v[:n].view(self.M, self.H // 2), v[n:].view(self.M, self.H // 32)
+        """MXFP4 plans: XQ slot l as (codes [M][H/2], exponents [M][H/32]) uint8
+        (views; for plans above 64 rows the exponents are a row-major copy)."""
+        return self._mx_slot(self.io.xq_slots + l * self.io.stride_xq, self.H)
 
     def hq_mx(self, l: int):
-        n = self.M * self.I // 2
-        v = self._view(self.io.hq_slots + l * self.io.stride_hq, n + n // 16)
-        return v[:n].view(self.M, self.I // 2), v[n:].view(self.M, self.I // 32)
+        """MXFP4 plans: HQ slot l as (codes [M][I/2], exponents [M][I/32]), as xq_mx."""
+        return self._mx_slot(self.io.hq_slots + l * self.io.stride_hq, self.I)
 
     def export_codes(self, layer: int, which: int) -> np.ndarray:
         rows, cols = (self.H, self.I) if which == 2 else (self.I, self.H)
