@@ -52,8 +52,10 @@ int env_int(const char* name, int dflt);
 // [M] x [N] output over K; cfg < 0 when no configuration fits.
 // Configurations [0, ncfg) are considered: the FFN GEMMs use the first six,
 // the attention input all eight (6 and 7 are small tiles for short outputs).
-constexpr int kMMConfigCount = 6;
-constexpr int kMMConfigCountAll = 8;
+constexpr int kMMConfigCount = 6;     // FFN candidates 0..5 of the cost model
+constexpr int kMMConfigCountAll = 8;  // 6, 7: the attention input's small tiles
+constexpr int kMMConfigTwoPerCU = 8;  // 128 x 256, two workgroups per CU (FFN)
+inline bool mm_config_ffn(int c) { return (c >= 0 && c < kMMConfigCount) || c == kMMConfigTwoPerCU; }
 void choose_mm(int M, int N, int K, bool allow_split, int& cfg, int& split, int ncfg = kMMConfigCount);
 int mm_config_bm(int);
 int mm_config_bn(int);

@@ -93,12 +93,13 @@ __device__ __forceinline__ v8h cvt8_f16(uint32_t w0, uint32_t w1) {
   return r;
 }
 
-template <int BM_, int BN_, int WA_, int WW_, int NS_>
+template <int BM_, int BN_, int WA_, int WW_, int NS_, int MINB_ = 1>
 struct MMCfg {
   static constexpr int BM = BM_, BN = BN_;   // activation rows, packed weight rows per workgroup
   static constexpr int WA = WA_, WW = WW_;   // waves along activations, along weights
   static constexpr int KS = 64;              // K bytes per stage
   static constexpr int NS = NS_;             // LDS stages (ring)
+  static constexpr int MINB = MINB_;         // workgroups per CU the registers and LDS are sized for
   static constexpr int NW = WA * WW, NT = 64 * NW;
   static constexpr int TA = BM / 32 / WA;    // 32-row activation tiles per wave
   static constexpr int TW = BN / 32 / WW;    // 32-row weight tiles per wave
@@ -109,7 +110,7 @@ struct MMCfg {
   static constexpr int CPW = ACPW + WCPW;
   static constexpr int A_BYTES = BM * KS, STAGE_BYTES = (BM + BN) * KS;
   static_assert(BM % (32 * WA) == 0 && BN % (32 * WW) == 0, "whole 32-row tiles per wave");
-  static_assert(NS >= 2 && NS <= 4 && NS * STAGE_BYTES <= 160 * 1024, "LDS");
+  static_assert(NS >= 2 && NS <= 4 && MINB * NS * STAGE_BYTES <= 160 * 1024, "LDS");
   static_assert((NS - 2) * CPW < 64, "vmcnt range");
 };
 
@@ -124,7 +125,7 @@ struct MMCfg {
 // of lane l (row l % 32, chunk (l / 32) * 2 + q) then hits 16 distinct
 // 16-byte bank groups per 16 lanes, i.e. it is conflict-free.
 template <int EPI, class C, bool FP8>
-__global__ __launch_bounds__(C::NT) void k_mm(const uint8_t* __restrict__ act, const uint8_t* __restrict__ wt,
+__global__ __launch_bounds__(C::NT, C::MINB) void k_mm(const uint8_t* __restrict__ act, const uint8_t* __restrict__ wt,
                                               void* __restrict__ out, float* __restrict__ part, int M, int K,
                                               int Npk, int tiles_n, int tiles_m, int num_splits, float alpha_a,
                                               float alpha_b, float inv_out, const QkvOut qo) {
@@ -438,6 +439,7 @@ __global__ __launch_bounds__(C::NT) void k_mm(const uint8_t* __restrict__ act, c
 //   5: BM 128 x BN 128, waves 2 x 2 (wave tile  64 x 64), 4 stages   small grids
 //   6: BM  64 x BN 128, waves 2 x 2 (wave tile  32 x 64), 4 stages   QKV only
 //   7: BM 128 x BN  64, waves 2 x 2 (wave tile  64 x 32), 4 stages   QKV only
+//   8: BM 128 x BN 256, waves 2 x 2 (wave tile  64 x 128), 3 stages, two workgroups per CU
 using MMC0 = MMCfg<224, 256, 1, 4, 4>;
 using MMC1 = MMCfg<256, 224, 4, 1, 4>;
 using MMC2 = MMCfg<256, 192, 2, 2, 4>;
@@ -448,11 +450,18 @@ using MMC5 = MMCfg<128, 128, 2, 2, 4>;
 // workgroups than CUs where 128 x 128 tiles would leave part of the chip idle
 using MMC6 = MMCfg<64, 128, 2, 2, 4>;
 using MMC7 = MMCfg<128, 64, 2, 2, 4>;
-constexpr int kMMConfigs = 8;
+// 128 x 256 on a 3-stage ring, registers and LDS sized for two workgroups
+// per CU (two waves per SIMD, so one wave's LDS reads, conversions and
+// barrier waits overlap the other's matrix instructions)
+using MMC8 = MMCfg<128, 256, 2, 2, 3, 2>;
+constexpr int kMMConfigs = 9;
 
-static const int kMM_BM[kMMConfigs] = {MMC0::BM, MMC1::BM, MMC2::BM, MMC3::BM, MMC4::BM, MMC5::BM, MMC6::BM, MMC7::BM};
-static const int kMM_BN[kMMConfigs] = {MMC0::BN, MMC1::BN, MMC2::BN, MMC3::BN, MMC4::BN, MMC5::BN, MMC6::BN, MMC7::BN};
-static const int kMM_KS[kMMConfigs] = {MMC0::KS, MMC1::KS, MMC2::KS, MMC3::KS, MMC4::KS, MMC5::KS, MMC6::KS, MMC7::KS};
+static const int kMM_BM[kMMConfigs] = {MMC0::BM, MMC1::BM, MMC2::BM, MMC3::BM, MMC4::BM,
+                                       MMC5::BM, MMC6::BM, MMC7::BM, MMC8::BM};
+static const int kMM_BN[kMMConfigs] = {MMC0::BN, MMC1::BN, MMC2::BN, MMC3::BN, MMC4::BN,
+                                       MMC5::BN, MMC6::BN, MMC7::BN, MMC8::BN};
+static const int kMM_KS[kMMConfigs] = {MMC0::KS, MMC1::KS, MMC2::KS, MMC3::KS, MMC4::KS,
+                                       MMC5::KS, MMC6::KS, MMC7::KS, MMC8::KS};
 
 int mm_config_bm(int c) { return (c >= 0 && c < kMMConfigs) ? kMM_BM[c] : 0; }
 int mm_config_bn(int c) { return (c >= 0 && c < kMMConfigs) ? kMM_BN[c] : 0; }
@@ -483,6 +492,9 @@ static hipError_t mm_cfg(int cfg, const uint8_t* act, const uint8_t* w, void* ou
       return hipErrorInvalidValue;
     case 7:
       if constexpr (EPI == MM_QKV) return mm_launch<EPI, MMC7, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s, qo);
+      return hipErrorInvalidValue;
+    case 8:
+      if constexpr (EPI != MM_QKV) return mm_launch<EPI, MMC8, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s, qo);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }

@@ -67,6 +67,18 @@ def test_small_shapes_fp8_gemms(spec):
     assert rep.hq_mismatch / rep.hq_n < 1e-2
 
 
+@pytest.mark.parametrize("spec", [SMALL[4], SMALL[5]], ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
+def test_small_shapes_two_per_cu_gateup_tile(spec, monkeypatch):
+    # the 128 x 256 three-stage gate/up tile sized for two workgroups per CU
+    # (the default on the FP8 matrix cores) on the f16 cores, with ragged row
+    # tiles; exact arithmetic, so the full byte tolerance applies
+    monkeypatch.setenv("FRT_MM_GATEUP_CFG", "8")
+    idx, M, H, I, L, act = spec
+    cfg = FFNConfig(idx, "small_cfg8_%d" % idx, M, H, I, L, act)
+    rep = run_case(cfg)
+    log(str(rep))
+
+
 @pytest.mark.parametrize("spec", [SMALL[0], SMALL[1], SMALL[2]],
                          ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
 def test_small_shapes_fused_norm(spec):
