@@ -118,9 +118,10 @@ typedef enum {
  *   tiles for gate/up, 128 x 128 with K split into fp32 partials for down).
  *   Requires H and I multiples of 512; excludes the FP8, fused-norm and
  *   norm-fusion flags.  Slots: each XQ slot holds codes [M][H/2] (two per
- *   byte, low nibble first) followed by the exponents: for M <= 64 row-major
- *   [M][H/32]; for M > 64 in the prefill layout, rows padded to a multiple
- *   of 128 -- the exponent of row m, 32-block b at byte
+ *   byte, low nibble first) followed by the exponents of row m, 32-block b:
+ *   for M <= 64 (rows padded to a multiple of 16) at byte
+ *   (((m/16) * (H/512) + b/16) * 64 + (b%4) * 16 + m%16) * 4 + (b/4)%4;
+ *   for M > 64 (rows padded to a multiple of 128) at byte
  *   ((m/64) * (H/128) + b/4) * 256 + ((b%4) * 16 + m%16) * 4 + (m/16)%4.
  *   HQ likewise with I. */
 #define FRT_FLAG_MXFP4 32u

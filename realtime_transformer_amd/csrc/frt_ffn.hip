@@ -288,8 +288,9 @@ Layout make_layout(const frt_ffn_desc& d) {
   lo.mx_mm = lo.mx && d.M > kGemvMtMaxM;
   if (lo.mx) {
     // codes (half a byte per weight) then one exponent per 32 weights; the
-    // prefill GEMM's activation exponents cover rows padded to 128
-    const size_t Mx = lo.mx_mm ? (size_t)ceil_div(d.M, 128) * 128 : M;
+    // activation exponents cover rows padded to 16 (GEMV layout) or to 128
+    // (the prefill GEMM's)
+    const size_t Mx = (size_t)ceil_div(d.M, lo.mx_mm ? 128 : 16) * (lo.mx_mm ? 128 : 16);
     lo.wgu_sc = align256(npk * H / 2);
     lo.wgu_layer = lo.wgu_sc + align256(npk * H / 32);
     lo.wd_sc = align256(H * I / 2);

@@ -110,6 +110,22 @@ __device__ __forceinline__ v4f mx_mfma(v8i a, int sa, v8i b, int sb, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
 }
 
+// GEMV-layout activation exponents (M <= 64, rows padded to 16): per (16-row
+// tile, four 128-K blocks) 64 lanes x 4 bytes; lane = 32-sub-block * 16 +
+// row % 16 (the MFMA operand's lane), byte = K block % 4 -- the weights'
+// layout with the row tile in place of the group, so one dword per lane
+// carries four K blocks of either operand.  Row m, 32-block b.
+__host__ __device__ __forceinline__ size_t mx_act_scale_off_gemv(uint32_t m, uint32_t b, uint32_t KB) {
+  return (((size_t)(m >> 4) * (KB >> 2) + (b >> 4)) * 64 + ((b & 3u) * 16u + (m & 15u))) * 4 + ((b >> 2) & 3u);
+}
+
+// Block-scaled FP4 product whose exponents are byte U of each operand's
+// exponent dword (op_sel)
+template <int U>
+__device__ __forceinline__ v4f mx_mfma_u(v8i a, int sa, v8i b, int sb, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, U, sa, U, sb);
+}
+
 // Prefill-layout exponents (k_mxmm), arranged so that one 32-bit LDS read
 // gives a lane the exponents of four MFMA operands and the instruction picks
 // the byte (op_sel).  Weights: per (quad of 16-row groups, 128-K block) 64

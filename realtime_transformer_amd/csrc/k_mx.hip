@@ -18,6 +18,8 @@
 // over 128 K values with each lane's E8M0 scales applied per 32-block; within
 // an instruction the FP4 products are exact and the sum is accurate to an
 // fp32 rounding (measured), across instructions the accumulator is fp32.
+#include <type_traits>
+
 #include "frt_mx.h"
 
 namespace frt {
@@ -98,7 +100,8 @@ __device__ __forceinline__ v8i mx_x16(const uint8_t* p, bool has) {
   return r;
 }
 
-// Activation row pointers of tile t: codes [M][K/2], exponents [M][K/32].
+// Activation row pointers of tile t: codes [M][K/2]; the lane's exponent
+// dword of quad 0 in the GEMV layout (mx_act_scale_off_gemv).
 struct MxRows {
   const uint8_t* c;
   const uint8_t* s;
@@ -122,8 +125,8 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup_mx(const uint8_t* __rest
   __shared__ v4f red[W][MT][NA][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int P = blockIdx.x;
-  const int KB = K >> 7;
-  const int kb0 = wave * KB / W, kb1 = (wave + 1) * KB / W;
+  const int KB = K >> 7, KQ = KB >> 2;  // K blocks, quads of four
+  const int kq0 = wave * KQ / W, kq1 = (wave + 1) * KQ / W;
   const int row = lane & 15, q = lane >> 4;
   // packed groups of this workgroup (gated: g0 u0 g1 u1; plain: u0 u1)
   uint32_t grp[NA];
@@ -136,7 +139,7 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup_mx(const uint8_t* __rest
     xr[t].has = m < M;
     const int mm = xr[t].has ? m : 0;
     xr[t].c = xc + (size_t)mm * (K / 2) + q * 16;
-    xr[t].s = xs + (size_t)mm * (K / 32) + q;
+    xr[t].s = xs + ((size_t)t * KQ * 64 + lane) * 4;  // this lane's exponent dword of quad 0
   }
   v4f acc[MT][NA];
 #pragma unroll
@@ -144,35 +147,35 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup_mx(const uint8_t* __rest
 #pragma unroll
     for (int a = 0; a < NA; ++a) acc[t][a] = v4f{0, 0, 0, 0};
 
-  // two K blocks per step: every load of the step is issued before its MFMAs
-  for (int kb = kb0; kb < kb1; kb += 2) {
-    const int nk = kb + 1 < kb1 ? 2 : 1;
-    v8i wv[2][NA], xv[2][MT];
-    int wsc[2][NA], xsc[2][MT];
+  // one quad of K blocks per step: every load of the step (four code runs
+  // per operand and one exponent dword per operand) is issued before its
+  // MFMAs, which take exponent byte u of each dword through op_sel
+  for (int kq = kq0; kq < kq1; ++kq) {
+    v8i wv[4][NA], xv[4][MT];
+    int wsd[NA], xsd[MT];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int k = kb + (u < nk ? u : 0);
+    for (int a = 0; a < NA; ++a)
+      wsd[a] = *reinterpret_cast<const int*>(ws + mx_scale_off(grp[a] * 16, 4 * kq, lane, KB));
 #pragma unroll
-      for (int a = 0; a < NA; ++a) {
-        wv[u][a] = mx_w16(wc + mx_code_off(grp[a] * 16, k, lane, KB));
-        const uint32_t d = *reinterpret_cast<const uint32_t*>(ws + mx_scale_off(grp[a] * 16, k & ~3, lane, KB));
-        wsc[u][a] = (int)((d >> (8 * (k & 3))) & 255u);
-      }
+    for (int t = 0; t < MT; ++t) xsd[t] = xr[t].has ? *reinterpret_cast<const int*>(xr[t].s + (size_t)kq * 256) : 0x7f7f7f7f;
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        xv[u][t] = mx_x16(xr[t].c + (size_t)k * 64, xr[t].has);
-        xsc[u][t] = xr[t].has ? (int)xr[t].s[k * 4] : 127;
-      }
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int a = 0; a < NA; ++a) wv[u][a] = mx_w16(wc + mx_code_off(grp[a] * 16, 4 * kq + u, lane, KB));
+#pragma unroll
+      for (int t = 0; t < MT; ++t) xv[u][t] = mx_x16(xr[t].c + (size_t)(4 * kq + u) * 64, xr[t].has);
     }
+    auto step = [&](auto U) {
+      constexpr int u = decltype(U)::value;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (u < nk) {
+      for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
-#pragma unroll
-          for (int a = 0; a < NA; ++a) acc[t][a] = mx_mfma(xv[u][t], xsc[u][t], wv[u][a], wsc[u][a], acc[t][a]);
-      }
-    }
+        for (int a = 0; a < NA; ++a) acc[t][a] = mx_mfma_u<u>(xv[u][t], xsd[t], wv[u][a], wsd[a], acc[t][a]);
+    };
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 2>{});
+    step(std::integral_constant<int, 3>{});
   }
 #pragma unroll
   for (int t = 0; t < MT; ++t)
@@ -195,7 +198,8 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup_mx(const uint8_t* __rest
     const float h0 = GATED ? mx_gated<ACT>(f[0][r], f[1][r]) : mx_gated<ACT>(0.0f, f[0][r]);
     const float h1 = GATED ? mx_gated<ACT>(f[2][r], f[3][r]) : mx_gated<ACT>(0.0f, f[1][r]);
     const int mm = m < M ? m : 0;
-    mx_store_h32(h0, h1, m < M, row, hc + (size_t)mm * (I / 2) + (size_t)P * 16, hs + (size_t)mm * (I / 32) + P);
+    mx_store_h32(h0, h1, m < M, row, hc + (size_t)mm * (I / 2) + (size_t)P * 16,
+                 hs + mx_act_scale_off_gemv((uint32_t)mm, (uint32_t)P, (uint32_t)I / 128));
   }
 }
 
@@ -212,10 +216,10 @@ __global__ __launch_bounds__(W * 64) void k_gemv_down_mx(const uint8_t* __restri
   __shared__ v4f red[W][MT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int p = blockIdx.x;
-  const int KB = K >> 7;
+  const int KB = K >> 7, KQ = KB >> 2;  // K blocks, quads of four
   const int S = gridDim.y, sp = blockIdx.y;
-  const int ks0 = sp * KB / S, ks1 = (sp + 1) * KB / S;
-  const int kb0 = ks0 + wave * (ks1 - ks0) / W, kb1 = ks0 + (wave + 1) * (ks1 - ks0) / W;
+  const int ks0 = sp * KQ / S, ks1 = (sp + 1) * KQ / S;
+  const int kq0 = ks0 + wave * (ks1 - ks0) / W, kq1 = ks0 + (wave + 1) * (ks1 - ks0) / W;
   const int row = lane & 15, q = lane >> 4;
   MxRows xr[MT];
 #pragma unroll
@@ -224,35 +228,33 @@ __global__ __launch_bounds__(W * 64) void k_gemv_down_mx(const uint8_t* __restri
     xr[t].has = m < M;
     const int mm = xr[t].has ? m : 0;
     xr[t].c = hc + (size_t)mm * (K / 2) + q * 16;
-    xr[t].s = hs + (size_t)mm * (K / 32) + q;
+    xr[t].s = hs + ((size_t)t * KQ * 64 + lane) * 4;  // this lane's exponent dword of quad 0
   }
   v4f acc[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = v4f{0, 0, 0, 0};
-  // four K blocks per step: every load of the step is issued before its MFMAs
-  for (int kb = kb0; kb < kb1; kb += 4) {
-    const int nk = kb1 - kb < 4 ? kb1 - kb : 4;
+  // one quad of K blocks per step, as in the gate/up GEMV
+  for (int kq = kq0; kq < kq1; ++kq) {
     v8i wv[4], xv[4][MT];
-    int wsc[4], xsc[4][MT];
+    const int wsd = *reinterpret_cast<const int*>(ws + mx_scale_off((uint32_t)p * 16, 4 * kq, lane, KB));
+    int xsd[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) xsd[t] = xr[t].has ? *reinterpret_cast<const int*>(xr[t].s + (size_t)kq * 256) : 0x7f7f7f7f;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int k = kb + (u < nk ? u : 0);
-      wv[u] = mx_w16(wc + mx_code_off((uint32_t)p * 16, k, lane, KB));
-      const uint32_t d = *reinterpret_cast<const uint32_t*>(ws + mx_scale_off((uint32_t)p * 16, k & ~3, lane, KB));
-      wsc[u] = (int)((d >> (8 * (k & 3))) & 255u);
+      wv[u] = mx_w16(wc + mx_code_off((uint32_t)p * 16, 4 * kq + u, lane, KB));
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        xv[u][t] = mx_x16(xr[t].c + (size_t)k * 64, xr[t].has);
-        xsc[u][t] = xr[t].has ? (int)xr[t].s[k * 4] : 127;
-      }
+      for (int t = 0; t < MT; ++t) xv[u][t] = mx_x16(xr[t].c + (size_t)(4 * kq + u) * 64, xr[t].has);
     }
+    auto step = [&](auto U) {
+      constexpr int u = decltype(U)::value;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (u < nk) {
-#pragma unroll
-        for (int t = 0; t < MT; ++t) acc[t] = mx_mfma(xv[u][t], xsc[u][t], wv[u], wsc[u], acc[t]);
-      }
-    }
+      for (int t = 0; t < MT; ++t) acc[t] = mx_mfma_u<u>(xv[u][t], xsd[t], wv[u], wsd, acc[t]);
+    };
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 2>{});
+    step(std::integral_constant<int, 3>{});
   }
 #pragma unroll
   for (int t = 0; t < MT; ++t) red[wave][t][lane] = acc[t];
@@ -347,7 +349,7 @@ static hipError_t down_mx_w(const uint8_t* hc, const uint8_t* hs, const uint8_t*
 
 hipError_t launch_gemv_down_mx(const uint8_t* hc, const uint8_t* hs, const uint8_t* wc, const uint8_t* ws, uint16_t* y,
                                float* part, int M, int K, int N, int W, int S, hipStream_t s) {
-  if (M < 1 || M > 64 || K % 512 || N % 16 || S < 1 || S > K / 128) return hipErrorInvalidValue;
+  if (M < 1 || M > 64 || K % 512 || N % 16 || S < 1 || S > K / 512) return hipErrorInvalidValue;
   if (W == 4) return down_mx_w<4>(hc, hs, wc, ws, y, part, M, K, N, S, s);
   if (W == 8) return down_mx_w<8>(hc, hs, wc, ws, y, part, M, K, N, S, s);
   if (W == 16) return down_mx_w<16>(hc, hs, wc, ws, y, part, M, K, N, S, s);

@@ -156,7 +156,7 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
         *reinterpret_cast<uint32_t*>(xq_out + (size_t)row * (H / 2) + (size_t)ch * 4) = codes;
         if ((ch & 3) == 0)
           xs_out[xs_mm ? mx_act_scale_off_mm((uint32_t)row, (uint32_t)(ch >> 2), (uint32_t)H / 128)
-                       : (size_t)row * (H / 32) + (ch >> 2)] = (uint8_t)e;
+                       : mx_act_scale_off_gemv((uint32_t)row, (uint32_t)(ch >> 2), (uint32_t)H / 128)] = (uint8_t)e;
       }
       continue;
     }
@@ -305,14 +305,14 @@ hipError_t launch_add_rmsnorm_quant(const uint16_t* r_prev, const uint16_t* y_pr
                               s, y_part, S, alpha_d, y_store);
 }
 
-// MXFP4 form of K1: xq_codes [M][H/2], xq_scales [M][H/32] (xs_mm: the
-// prefill GEMM's exponent layout, rows padded to 128); inv_awq [H].
-// H % 32 == 0 (H % 128 == 0 with xs_mm).
+// MXFP4 form of K1: xq_codes [M][H/2], the exponents in the GEMV layout
+// (rows padded to 16) or with xs_mm the prefill GEMM's (rows padded to 128);
+// inv_awq [H].  H % 512 == 0.
 hipError_t launch_add_rmsnorm_mx(const uint16_t* r_prev, const uint16_t* y_prev, const uint16_t* w,
                                  const uint16_t* mod, const float* inv_awq, uint16_t* r_out, uint8_t* xq_codes,
                                  uint8_t* xq_scales, int M, int H, float eps, hipStream_t s, const float* y_part,
                                  int S, float alpha_d, uint16_t* y_store, int xs_mm) {
-  if (H % 32 || !inv_awq || (xs_mm && H % 128)) return hipErrorInvalidValue;
+  if (H % 512 || !inv_awq) return hipErrorInvalidValue;
   const int nchunk = H / 8;
   const int nc = (nchunk + 255) / 256;
 #define FRT_MX_NORM(NCV)                                                                                          \

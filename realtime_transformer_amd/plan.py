@@ -128,24 +128,28 @@ class FFNPlan:
         return _abi.frt_export_mxfp4_weights(self.plan, layer, which, rows, cols)
 
     def _mx_slot(self, addr: int, K: int):
+        # exponents in the kernels' layouts, gathered here into row-major
+        # order (a copy).  GEMV (M <= 64, rows padded to 16): per (16-row
+        # tile, four 128-K blocks) 64 lanes x 4 bytes, lane = 32-sub-block *
+        # 16 + row % 16, byte = K block % 4.  Prefill (rows padded to 128):
+        # per (64-row group, 128-K block) 64 lanes x 4 bytes, same lane,
+        # byte = (row / 16) % 4.
         n = self.M * K // 2
-        if not self.mx_mm:
-            v = self._view(addr, n + n // 16)
-            return v[:n].view(self.M, K // 2), v[n:].view(self.M, K // 32)
-        # prefill layout: per (64-row group, 128-K block) 64 lanes x 4 bytes,
-        # lane = 32-sub-block * 16 + row % 16, byte = (row / 16) % 4; gathered
-        # here into row-major order (a copy)
-        mp = -(-self.M // 128) * 128
+        pad = 128 if self.mx_mm else 16
+        mp = -(-self.M // pad) * pad
         v = self._view(addr, n + mp * K // 32)
         m = np.arange(self.M, dtype=np.int64)[:, None]
         b = np.arange(K // 32, dtype=np.int64)[None, :]
-        off = ((m >> 6) * (K // 128) + (b >> 2)) * 256 + ((b & 3) * 16 + (m & 15)) * 4 + ((m >> 4) & 3)
+        if self.mx_mm:
+            off = ((m >> 6) * (K // 128) + (b >> 2)) * 256 + ((b & 3) * 16 + (m & 15)) * 4 + ((m >> 4) & 3)
+        else:
+            off = (((m >> 4) * (K // 512) + (b >> 4)) * 64 + (b & 3) * 16 + (m & 15)) * 4 + ((b >> 2) & 3)
         idx = torch.as_tensor(off.reshape(-1), device=self.device)
         return v[:n].view(self.M, K // 2), v[n:][idx].view(self.M, K // 32)
 
     def xq_mx(self, l: int):
-        """MXFP4 plans: XQ slot l as (codes [M][H/2], exponents [M][H/32]) uint8
-        (views; for plans above 64 rows the exponents are a row-major copy)."""
+        """MXFP4 plans: XQ slot l as (codes [M][H/2] view, exponents [M][H/32]
+        row-major copy) uint8."""
         return self._mx_slot(self.io.xq_slots + l * self.io.stride_xq, self.H)
 
     def hq_mx(self, l: int):
