@@ -54,54 +54,120 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
   const int nchunk = H >> 3;
   const size_t base = (size_t)(active ? row : 0) * (size_t)H;
 
-  // wn: the norm weight, or with modulation the per-channel scale (mh: shift);
-  // aw: the MXFP4 form's AWQ reciprocals, requested with them
-  uint4 rn[NC], wn[NC], mh[NC];
+  // Every load of the row is issued before any is used, so a row costs one
+  // memory round trip rather than one per chunk: chunk indices are clamped
+  // into the row (threads past the end re-read the last chunk and discard
+  // it) and the uniform choices select pointers, so no load waits behind a
+  // per-chunk branch.  wn: the norm weight, or with modulation the
+  // per-channel scale (mh: shift); aw: the MXFP4 form's AWQ reciprocals;
+  // p0, p1: the first two split-K partial tiles (further splits are read
+  // after these, in split order).  This is for the one-workgroup-per-row
+  // form (small M, where the row's latency is the kernel's time: the M = 1,
+  // H = 5120 decode chain gains 0.4 us per layer); the many-row form (one
+  // wave per row) reads chunk by chunk in the second loop instead, where
+  // occupancy hides the latency and the up-front registers would halve it.
+  constexpr bool UP = TPR == 256;
+  constexpr bool PF = UP && NC <= 4;
+  uint4 rn[NC], wn[NC], mh[NC], yv[NC];
   float4 aw[MX ? NC : 1][2];
+  float4 p0[PF ? NC : 1][2], p1[PF ? NC : 1][2];
+  const uint16_t* wsrc = mod ? mod : w_norm;
+  const uint16_t* hsrc = mod ? mod + H : w_norm;
+  const size_t pstride = (size_t)M * H;
+  const int s1 = S > 1 ? 1 : 0;
+  // loads of chunk c (clamped into the row)
+  auto load_chunk = [&](int c) {
+    const int chc = min(t + c * TPR, nchunk - 1);
+    const size_t o = base + (size_t)chc * 8;
+    rn[c] = *reinterpret_cast<const uint4*>(r_prev + o);
+    wn[c] = *reinterpret_cast<const uint4*>(wsrc + (size_t)chc * 8);
+    mh[c] = *reinterpret_cast<const uint4*>(hsrc + (size_t)chc * 8);
+    if (MX) {
+      const float4* ap = reinterpret_cast<const float4*>(inv_awq + (size_t)chc * 8);
+      aw[MX ? c : 0][0] = ap[0];
+      aw[MX ? c : 0][1] = ap[1];
+    }
+    if (!y_part && y_prev) yv[c] = *reinterpret_cast<const uint4*>(y_prev + o);
+  };
+  if (UP) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) load_chunk(c);
+  }
+  if (y_part) {
+    if (PF) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const size_t o = base + (size_t)min(t + c * TPR, nchunk - 1) * 8;
+        p0[PF ? c : 0][0] = *reinterpret_cast<const float4*>(y_part + o);
+        p0[PF ? c : 0][1] = *reinterpret_cast<const float4*>(y_part + o + 4);
+        p1[PF ? c : 0][0] = *reinterpret_cast<const float4*>(y_part + s1 * pstride + o);
+        p1[PF ? c : 0][1] = *reinterpret_cast<const float4*>(y_part + s1 * pstride + o + 4);
+      }
+    }
+  }
   double sq = 0.0;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int ch = t + c * TPR;
-    rn[c] = make_uint4(0, 0, 0, 0);
-    wn[c] = rn[c];
-    mh[c] = rn[c];
-    if (MX) aw[MX ? c : 0][0] = aw[MX ? c : 0][1] = make_float4(0, 0, 0, 0);
-    if (active && ch < nchunk) {
-      // issued with r, y
-      if (MX) {
-        const float4* ap = reinterpret_cast<const float4*>(inv_awq + (size_t)ch * 8);
-        aw[MX ? c : 0][0] = ap[0];
-        aw[MX ? c : 0][1] = ap[1];
+    const bool ok = active && ch < nchunk;
+    if (!UP) {
+      if (!ok) {
+        rn[c] = wn[c] = mh[c] = make_uint4(0, 0, 0, 0);
+        if (MX) aw[MX ? c : 0][0] = aw[MX ? c : 0][1] = make_float4(0, 0, 0, 0);
+        continue;
       }
-      if (mod) {
-        wn[c] = *reinterpret_cast<const uint4*>(mod + (size_t)ch * 8);
-        mh[c] = *reinterpret_cast<const uint4*>(mod + H + (size_t)ch * 8);
-      } else {
-        wn[c] = *reinterpret_cast<const uint4*>(w_norm + (size_t)ch * 8);
-      }
-      const uint4 rv = *reinterpret_cast<const uint4*>(r_prev + base + (size_t)ch * 8);
-      uint4 yv = make_uint4(0, 0, 0, 0);
-      if (y_part) {
-        yv = y_from_partials(y_part, (size_t)M * H, base + (size_t)ch * 8, S, alpha_d);
-        *reinterpret_cast<uint4*>(y_store + base + (size_t)ch * 8) = yv;
-      } else if (y_prev) {
-        yv = *reinterpret_cast<const uint4*>(y_prev + base + (size_t)ch * 8);
-      }
-      uint32_t rr[4] = {rv.x, rv.y, rv.z, rv.w};
-      uint32_t yy[4] = {yv.x, yv.y, yv.z, yv.w};
-      uint32_t o[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float lo = bf16_lo(rr[j]) + bf16_lo(yy[j]);
-        float hi = bf16_hi(rr[j]) + bf16_hi(yy[j]);
-        o[j] = pack_bf16x2(lo, hi);
-        double dlo = (double)bf16_lo(o[j]), dhi = (double)bf16_hi(o[j]);
-        sq += dlo * dlo;
-        sq += dhi * dhi;
-      }
-      rn[c] = make_uint4(o[0], o[1], o[2], o[3]);
-      *reinterpret_cast<uint4*>(r_out + base + (size_t)ch * 8) = rn[c];
+      load_chunk(c);
     }
+    if (!mod) mh[c] = make_uint4(0, 0, 0, 0);
+    if (y_part) {
+      // y = bf16(f32(sum of the splits in split order) * alpha_d)
+      const size_t o = base + (size_t)min(ch, nchunk - 1) * 8;
+      const int pc = PF ? c : 0;
+      if (!PF) {
+        p0[0][0] = *reinterpret_cast<const float4*>(y_part + o);
+        p0[0][1] = *reinterpret_cast<const float4*>(y_part + o + 4);
+        p1[0][0] = *reinterpret_cast<const float4*>(y_part + s1 * pstride + o);
+        p1[0][1] = *reinterpret_cast<const float4*>(y_part + s1 * pstride + o + 4);
+      }
+      float a[8] = {p0[pc][0].x, p0[pc][0].y, p0[pc][0].z, p0[pc][0].w,
+                    p0[pc][1].x, p0[pc][1].y, p0[pc][1].z, p0[pc][1].w};
+      if (S > 1) {
+        a[0] += p1[pc][0].x; a[1] += p1[pc][0].y; a[2] += p1[pc][0].z; a[3] += p1[pc][0].w;
+        a[4] += p1[pc][1].x; a[5] += p1[pc][1].y; a[6] += p1[pc][1].z; a[7] += p1[pc][1].w;
+      }
+      for (int sp = 2; sp < S; ++sp) {
+        const float4 q0 = *reinterpret_cast<const float4*>(y_part + sp * pstride + o);
+        const float4 q1 = *reinterpret_cast<const float4*>(y_part + sp * pstride + o + 4);
+        a[0] += q0.x; a[1] += q0.y; a[2] += q0.z; a[3] += q0.w;
+        a[4] += q1.x; a[5] += q1.y; a[6] += q1.z; a[7] += q1.w;
+      }
+      yv[c] = make_uint4(pack_bf16x2(a[0] * alpha_d, a[1] * alpha_d), pack_bf16x2(a[2] * alpha_d, a[3] * alpha_d),
+                         pack_bf16x2(a[4] * alpha_d, a[5] * alpha_d), pack_bf16x2(a[6] * alpha_d, a[7] * alpha_d));
+      if (ok) *reinterpret_cast<uint4*>(y_store + base + (size_t)ch * 8) = yv[c];
+    } else if (!y_prev) {
+      yv[c] = make_uint4(0, 0, 0, 0);
+    }
+    if (!ok) {
+      rn[c] = make_uint4(0, 0, 0, 0);
+      wn[c] = rn[c];
+      mh[c] = rn[c];
+      if (MX) aw[MX ? c : 0][0] = aw[MX ? c : 0][1] = make_float4(0, 0, 0, 0);
+      continue;
+    }
+    const uint32_t rr[4] = {rn[c].x, rn[c].y, rn[c].z, rn[c].w};
+    const uint32_t yy[4] = {yv[c].x, yv[c].y, yv[c].z, yv[c].w};
+    uint32_t o4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lo = bf16_lo(rr[j]) + bf16_lo(yy[j]);
+      const float hi = bf16_hi(rr[j]) + bf16_hi(yy[j]);
+      o4[j] = pack_bf16x2(lo, hi);
+      const double dlo = (double)bf16_lo(o4[j]), dhi = (double)bf16_hi(o4[j]);
+      sq += dlo * dlo;
+      sq += dhi * dhi;
+    }
+    rn[c] = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+    *reinterpret_cast<uint4*>(r_out + base + (size_t)ch * 8) = rn[c];
   }
   sq = wave_sum_f64(sq);
   if (WPR > 1) {
