@@ -31,18 +31,6 @@ __device__ __forceinline__ int mx_block_exp(float amax) {
   return e < 0 ? 0 : (e > 254 ? 254 : e);
 }
 
-// Lane moves inside a 16-lane row (DPP, no LDS round trip): quad_perm
-// [1,0,3,2] and [2,3,0,1] exchange lane pairs and pairs of pairs,
-// row_half_mirror reverses each 8 lanes, row_mirror the 16.
-enum { DPP_QUAD_X1 = 0xB1, DPP_QUAD_X2 = 0x4E, DPP_ROW_HALF_MIRROR = 0x141, DPP_ROW_MIRROR = 0x140 };
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
-}
 // maximum over each aligned group of 4 lanes, and of 16 lanes
 __device__ __forceinline__ float quad_max(float v) {
   v = __builtin_fmaxf(v, dpp_f32<DPP_QUAD_X1>(v));
