@@ -278,7 +278,7 @@ __global__ __launch_bounds__(W * 64) void k_gemv_down_mx(const uint8_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// launchers: W in {4, 8, 16}, MT = ceil(M / 16) <= 4, W * MT <= 16 (the
+// launchers: W in {4, 5, 8, 10, 16} (gate/up; {4, 8, 16} down), MT = ceil(M / 16) <= 4, W * MT <= 16 (the
 // reduction buffer: W * MT * NA KiB of LDS)
 // ---------------------------------------------------------------------------
 
@@ -309,7 +309,9 @@ template <int ACT>
 static hipError_t gateup_mx_act(int W, const uint8_t* xc, const uint8_t* xs, const uint8_t* wc, const uint8_t* ws,
                                 uint8_t* hc, uint8_t* hs, int M, int K, int I, hipStream_t s) {
   if (W == 4) return gateup_mx_w<ACT, 4>(xc, xs, wc, ws, hc, hs, M, K, I, s);
+  if (W == 5) return gateup_mx_w<ACT, 5>(xc, xs, wc, ws, hc, hs, M, K, I, s);
   if (W == 8) return gateup_mx_w<ACT, 8>(xc, xs, wc, ws, hc, hs, M, K, I, s);
+  if (W == 10) return gateup_mx_w<ACT, 10>(xc, xs, wc, ws, hc, hs, M, K, I, s);
   if (W == 16) return gateup_mx_w<ACT, 16>(xc, xs, wc, ws, hc, hs, M, K, I, s);
   return hipErrorInvalidValue;
 }
