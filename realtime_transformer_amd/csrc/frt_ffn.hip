@@ -48,6 +48,12 @@ hipError_t launch_gemv_gateup_mt(int, const uint8_t*, const uint8_t*, uint8_t*, 
 hipError_t launch_gemv_down_mt(const uint8_t*, const uint8_t*, uint16_t*, float*, int, int, int, int, int, bool,
                                float, hipStream_t);
 bool gemv_fused_supported(int, int, int);
+hipError_t launch_add_sumsq(const uint16_t*, const uint16_t*, const float*, int, float, uint16_t*, uint16_t*, double*,
+                            int, int, hipStream_t);
+int add_sumsq_slices(int);
+bool gemv_nq_supported(int, int, int);
+hipError_t launch_gemv_gateup_nq(int, const uint16_t*, const uint16_t*, const double*, int, float, float, uint8_t*,
+                                 const uint8_t*, uint8_t*, int, int, int, int, float, float, float, hipStream_t);
 hipError_t launch_add_rmsnorm_mx(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*, const float*,
                                  uint16_t*, uint8_t*, uint8_t*, int, int, float, hipStream_t, const float*, int, float,
                                  uint16_t*, int);
@@ -156,6 +162,8 @@ struct Layout {
   size_t awq, inv_awq;         // MXFP4: AWQ scale bf16 [L][H], its reciprocal fp32 [L][H]
   int cfg_gu, cfg_dn;  // GEMM tile configurations
   bool mm_gu, mm_dn;   // GEMM runs on the LDS-DMA f16 kernel (k_mm) rather than k_gemm
+  bool norm_split;     // decode GEMV path: k_add_sumsq, then the gate/up GEMV quantises (k_gemv_gateup_nq)
+  size_t sqp;          // its slice sums of squares, fp64 [M][G]
 };
 
 
@@ -366,6 +374,17 @@ Layout make_layout(const frt_ffn_desc& d) {
     part = lo.s_dn > 1 ? (size_t)lo.s_dn * M * H * 4 : 4;
     words = 1;
   }
+  // The decode GEMV path splits the norm: a short kernel forms r' and slice
+  // sums of squares, the gate/up GEMV quantises its own K range (measured
+  // at M = 1, H = 5120: the one-workgroup norm kernel's latency was its
+  // single CU's load queue).  FRT_NORM_SPLIT=0 keeps the one-kernel norm.
+  {
+    const int G = add_sumsq_slices((int)H);
+    lo.norm_split = !lo.mx && !lo.gemv_mt && d.M <= kGemvMaxM &&
+                    (d.flags & (FRT_FLAG_FUSED_NORM | FRT_FLAG_ADA_NORM)) == 0u &&
+                    gemv_nq_supported((int)M, (int)H, G) && env_int("FRT_NORM_SPLIT", 1) != 0;
+    lo.sqp = take(lo.norm_split ? M * G * 8 : 256);
+  }
   lo.part = take(part);
   lo.part_bytes = part;
   lo.cnt_words = words;
@@ -417,6 +436,7 @@ struct frt_plan {
     return ada() ? reinterpret_cast<const uint16_t*>(ws + lo.mod) + (size_t)l * 2 * d.H : nullptr;
   }
   float* part() const { return reinterpret_cast<float*>(ws + lo.part); }
+  double* sqp() const { return reinterpret_cast<double*>(ws + lo.sqp); }
   uint32_t* cnt(int region) const {
     return reinterpret_cast<uint32_t*>(ws + lo.cnt) + (size_t)region * lo.cnt_words;
   }
@@ -851,7 +871,17 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
     return FRT_OK;
   }
   if (which == 0) {
-    if (!fused) {
+    if (p->lo.norm_split) {
+      const float* yp = nullptr;
+      float a_prev = 0.0f;
+      if (y_in_partials && l > 0) {
+        yp = p->part();
+        a_prev = p->s_h[l - 1] * p->s_d[l - 1];
+      }
+      KERNEL_CHECK(launch_add_sumsq(p->r(l), p->y(l), yp, p->lo.split_dn, a_prev, p->y(l), p->r(l + 1), p->sqp(), M,
+                                    H, s),
+                   "add_sumsq");
+    } else if (!fused) {
       const float* yp = nullptr;
       float a_prev = 0.0f;
       if (y_in_partials && l > 0) {
@@ -874,6 +904,11 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
                                             p->r(l + 1), p->xq(l), p->wgu(l), p->hq(l), M, H, I, p->lo.s_gu,
                                             p->d.eps, inv_x, a_g, a_u, inv_h, s), "gemv_gateup_fused");
     }
+    else if (p->lo.norm_split)
+      KERNEL_CHECK(launch_gemv_gateup_nq(p->d.act, p->r(l + 1), p->wn(l), p->sqp(), add_sumsq_slices(H), p->d.eps,
+                                         inv_x, p->xq(l), p->wgu(l), p->hq(l), M, H, I, p->lo.s_gu, a_g, a_u, inv_h,
+                                         s),
+                   "gemv_gateup_nq");
     else if (M <= kGemvMaxM)
       KERNEL_CHECK(launch_gemv_gateup(p->d.act, p->xq(l), p->wgu(l), p->hq(l), M, H, I, p->lo.s_gu,
                                       a_g, a_u, inv_h, s), "gemv_gateup");

@@ -182,6 +182,202 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup(const uint8_t* __restric
   }
 }
 
+// Decode gate/up that finishes the norm itself (three kernels per layer
+// still, but the norm kernel before it is the short k_add_sumsq).  The
+// quantised row is needed by every workgroup, but each wave only needs its
+// own K range of it: wave w forms XQ[m][k] = e4m3(f32(f32(r'[m][k] * inv_m) *
+// w_norm[k]) * inv_x) for its K blocks [kb0, kb1) and all M rows, with
+// inv_m = f32(1 / sqrt(S_m / K + eps)) in fp64 and S_m the sum of the row's
+// slice sums in slice order (the arithmetic of k_add_rmsnorm_quant), writes
+// the codes to its own part of an LDS row buffer [M][K] and reads its
+// activation fragments from there.  Workgroup 0 also stores them to the XQ
+// slot.  Loads are issued in the order: slice sums and r' / w_norm chunks,
+// then the first step's weights, so the HBM stream starts before the
+// quantisation runs and only the activation loads (completed first) are
+// waited for.  LDS writes and reads stay inside one wave, which the LDS
+// serves in order.
+struct NormQ {
+  const uint16_t* r;       // r' = R[l+1], bf16 [M][K]
+  const uint16_t* w_norm;  // RMSNorm weight, bf16 [K]
+  const double* sq;        // slice sums of r'^2, fp64 [M][G]
+  int G;
+  float eps, inv_x;
+  uint8_t* xq_out;         // XQ[l], E4M3 [M][K] (workgroup 0 stores it)
+};
+constexpr int kNqChunks = 2;        // 8-element chunks per lane whose loads are issued together
+constexpr int kNqLdsBytes = 16384;  // row buffer M * K
+constexpr int kNqMaxSlices = 16;    // slice sums per row (H <= 8192)
+
+template <int ACT, int W>
+__global__ __launch_bounds__(W * 64) void k_gemv_gateup_nq(const NormQ nq, const uint8_t* __restrict__ w,
+                                                           uint8_t* __restrict__ hq, int M, int K, int I,
+                                                           float alpha_g, float alpha_u, float inv_h) {
+  constexpr bool GATED = ACT != GU_GELU;
+  constexpr int NACC = GATED ? 2 : 1;
+  extern __shared__ __attribute__((aligned(16))) uint8_t xrow[];  // [M][K] E4M3
+  __shared__ v4f red[W][NACC][64];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int p = blockIdx.x;
+  const int KB = K >> 7;
+  const int kb0 = wave * KB / W, kb1 = (wave + 1) * KB / W;
+  const int row = lane & 15, q = lane >> 4;
+  const bool has_row = row < M;
+  const uint8_t* wg = w + (size_t)(GATED ? 2 * p : 0) * KB * 2048 + lane * 16;
+  const uint8_t* wu = w + (size_t)(GATED ? 2 * p + 1 : p) * KB * 2048 + lane * 16;
+
+  // (1) activation-side loads: lane i < M*G holds slice sum i; chunk c of
+  // this wave's range is (row c / nkc, K chunk kb0 * 16 + c % nkc).  No
+  // load sits behind a branch (indices are clamped instead), so the
+  // compiler's wait before the quantisation counts only these loads and
+  // leaves the weight loads of (2) in flight.
+  const int G = nq.G;
+  const double part_v = nq.sq[lane < M * G ? lane : M * G - 1];
+  const int nkc = (kb1 - kb0) * 16, nch = M * nkc;  // kb1 > kb0: W <= K / 128
+  const float rcp_nkc = __builtin_amdgcn_rcpf((float)nkc);
+  int cm[kNqChunks], ck[kNqChunks];
+  uint4 rv[kNqChunks], wv[kNqChunks];
+  auto load_group = [&](int c0) {
+#pragma unroll
+    for (int j = 0; j < kNqChunks; ++j) {
+      int c = c0 + j * 64 + lane;
+      c = c < nch ? c : nch - 1;  // lanes past the end redo the last chunk (same bytes)
+      int m = (int)(((float)c + 0.5f) * rcp_nkc);
+      m -= (m * nkc > c) ? 1 : 0;
+      m += ((m + 1) * nkc <= c) ? 1 : 0;
+      cm[j] = m;
+      ck[j] = (kb0 * 16 + (c - m * nkc)) * 8;
+      rv[j] = *reinterpret_cast<const uint4*>(nq.r + (size_t)m * K + ck[j]);
+      wv[j] = *reinterpret_cast<const uint4*>(nq.w_norm + ck[j]);
+    }
+  };
+  load_group(0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // (2) the first step's weights (a one-block range loads its block twice)
+  uint32_t u0[8], u1[8], g0[8], g1[8];
+  {
+    const int kb_b = kb0 + 1 < kb1 ? kb0 + 1 : kb0;
+    load_w32(wu, kb0, u0);
+    load_w32(wu, kb_b, u1);
+    if (GATED) {
+      load_w32(wg, kb0, g0);
+      load_w32(wg, kb_b, g1);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // (3) 1/rms of row `lane` (lanes < M; the others compute row 0's), then
+  // the codes of this wave's range
+  const double part = lane < M * G ? part_v : 0.0;
+  double ssum = 0.0;
+  {
+    const int base = lane < M ? lane * G : 0;
+    const unsigned long long b = (unsigned long long)__double_as_longlong(part);
+#pragma unroll
+    for (int g = 0; g < kNqMaxSlices; ++g) {
+      const int src = base + (g < G ? g : 0);
+      const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)b, src, 64);
+      const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(b >> 32), src, 64);
+      const double v = __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+      ssum += g < G ? v : 0.0;
+    }
+  }
+  const float inv_rms = (float)(1.0 / sqrt(ssum / (double)K + (double)nq.eps));
+  const bool store_xq = blockIdx.x == 0;
+  auto quant_group = [&](int c0) {
+#pragma unroll
+    for (int j = 0; j < kNqChunks; ++j) {
+      const float inv = __shfl(inv_rms, cm[j], 64);
+      const uint32_t rr[4] = {rv[j].x, rv[j].y, rv[j].z, rv[j].w};
+      const uint32_t ww[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
+      float x[8];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        x[2 * t] = (bf16_lo(rr[t]) * inv) * bf16_lo(ww[t]);
+        x[2 * t + 1] = (bf16_hi(rr[t]) * inv) * bf16_hi(ww[t]);
+      }
+      const float ix = nq.inv_x;
+      uint2 code;
+      code.x = e4m3x4(x[0] * ix, x[1] * ix, x[2] * ix, x[3] * ix);
+      code.y = e4m3x4(x[4] * ix, x[5] * ix, x[6] * ix, x[7] * ix);
+      if (c0 + j * 64 + lane < nch) {
+        const size_t o = (size_t)cm[j] * K + ck[j];
+        *reinterpret_cast<uint2*>(xrow + o) = code;
+        if (store_xq) *reinterpret_cast<uint2*>(nq.xq_out + o) = code;
+      }
+    }
+  };
+  quant_group(0);
+  for (int c0 = kNqChunks * 64; c0 < nch; c0 += kNqChunks * 64) {
+    load_group(c0);
+    quant_group(c0);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // (4) the GEMV over this wave's K range, activations from LDS
+  auto lds_x32 = [&](int kb, uint32_t o[8]) {
+    uint4 a = make_uint4(0, 0, 0, 0), b = a;
+    if (has_row) {
+      const uint8_t* xp = xrow + (size_t)row * K + kb * 128 + q * 32;
+      a = *reinterpret_cast<const uint4*>(xp);
+      b = *reinterpret_cast<const uint4*>(xp + 16);
+    }
+    unpack8(a, b, o);
+  };
+  v4f accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
+  int kb = kb0;
+  for (; kb + 1 < kb1; kb += 2) {
+    uint32_t x0[8], x1[8];
+    if (kb != kb0) {
+      load_w32(wu, kb, u0);
+      load_w32(wu, kb + 1, u1);
+      if (GATED) {
+        load_w32(wg, kb, g0);
+        load_w32(wg, kb + 1, g1);
+      }
+    }
+    lds_x32(kb, x0);
+    lds_x32(kb + 1, x1);
+    accu = mfma_f16_x4(x0, u0, accu);
+    if (GATED) accg = mfma_f16_x4(x0, g0, accg);
+    accu = mfma_f16_x4(x1, u1, accu);
+    if (GATED) accg = mfma_f16_x4(x1, g1, accg);
+  }
+  if (kb < kb1) {
+    uint32_t x0[8];
+    if (kb != kb0) {
+      load_w32(wu, kb, u0);
+      if (GATED) load_w32(wg, kb, g0);
+    }
+    lds_x32(kb, x0);
+    accu = mfma_f16_x4(x0, u0, accu);
+    if (GATED) accg = mfma_f16_x4(x0, g0, accg);
+  }
+  if (W > 1) {
+    red[wave][0][lane] = accu;
+    if (GATED) red[wave][NACC - 1][lane] = accg;
+    __syncthreads();
+    if (wave != 0) return;
+    accu = red[0][0][lane];
+    if (GATED) accg = red[0][NACC - 1][lane];
+#pragma unroll
+    for (int v = 1; v < W; ++v) {
+      accu += red[v][0][lane];
+      if (GATED) accg += red[v][NACC - 1][lane];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = 4 * q + r;
+    if (m < M) {
+      const float h = gated_h<ACT>(accg[r] * alpha_g, accu[r] * alpha_u);
+      hq[(size_t)m * I + p * 16 + row] = (uint8_t)e4m3x1(h * inv_h);
+    }
+  }
+}
+
 // Decode form of gate/up with the norm fused in front (two kernels per
 // layer instead of three; batch-1 time goes to kernel boundaries).  Every
 // workgroup forms y (from the previous down projection's split-K partials,
@@ -891,6 +1087,43 @@ __global__ __launch_bounds__(W * 64) void k_gemv_down_mt(const uint8_t* __restri
         ps[(size_t)m * N + p * 16 + row] = a[r];
     }
   }
+}
+
+template <int W>
+static void gemv_gateup_nq_w(int act, const NormQ& nq, const uint8_t* w, uint8_t* hq, int M, int K, int I,
+                             float a_g, float a_u, float inv_h, hipStream_t s) {
+  dim3 grid(I / 16), block(W * 64);
+  const size_t lds = (size_t)M * K;
+  if (act == GU_GEGLU)
+    hipLaunchKernelGGL((k_gemv_gateup_nq<GU_GEGLU, W>), grid, block, lds, s, nq, w, hq, M, K, I, a_g, a_u, inv_h);
+  else if (act == GU_SWIGLU)
+    hipLaunchKernelGGL((k_gemv_gateup_nq<GU_SWIGLU, W>), grid, block, lds, s, nq, w, hq, M, K, I, a_g, a_u, inv_h);
+  else
+    hipLaunchKernelGGL((k_gemv_gateup_nq<GU_GELU, W>), grid, block, lds, s, nq, w, hq, M, K, I, a_g, a_u, inv_h);
+}
+
+// Whether k_gemv_gateup_nq takes the shape: the row buffer M*K fits its LDS
+// budget and every slice sum has a lane (M * G <= 64).
+bool gemv_nq_supported(int M, int K, int G) {
+  return M >= 1 && M <= 16 && K % 128 == 0 && (long)M * K <= kNqLdsBytes && G <= kNqMaxSlices && M * G <= 64;
+}
+
+// gate/up GEMV from r' and the slice sums (k_add_sumsq) instead of XQ; the
+// codes it forms are stored to xq_out.
+hipError_t launch_gemv_gateup_nq(int act, const uint16_t* r, const uint16_t* w_norm, const double* sq, int G,
+                                 float eps, float inv_x, uint8_t* xq_out, const uint8_t* w, uint8_t* hq, int M, int K,
+                                 int I, int W, float alpha_g, float alpha_u, float inv_h, hipStream_t s) {
+  if (!gemv_nq_supported(M, K, G) || G < 1 || I % 16 || W > K / 128) return hipErrorInvalidValue;
+  const NormQ nq{r, w_norm, sq, G, eps, inv_x, xq_out};
+  switch (W) {
+    case 1: gemv_gateup_nq_w<1>(act, nq, w, hq, M, K, I, alpha_g, alpha_u, inv_h, s); break;
+    case 2: gemv_gateup_nq_w<2>(act, nq, w, hq, M, K, I, alpha_g, alpha_u, inv_h, s); break;
+    case 4: gemv_gateup_nq_w<4>(act, nq, w, hq, M, K, I, alpha_g, alpha_u, inv_h, s); break;
+    case 8: gemv_gateup_nq_w<8>(act, nq, w, hq, M, K, I, alpha_g, alpha_u, inv_h, s); break;
+    case 16: gemv_gateup_nq_w<16>(act, nq, w, hq, M, K, I, alpha_g, alpha_u, inv_h, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // waves per workgroup W: 1, 2, 4, 8 or 16 (at most the number of K blocks)

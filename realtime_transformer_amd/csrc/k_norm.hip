@@ -266,6 +266,50 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
   }
 }
 
+// First half of the decode norm, for the gate/up GEMV that quantises its own
+// activations (k_gemv_gateup_nq): r' = bf16(r + y) as above (y from the Y
+// slot, or formed from the split-K partials and stored there) and the fp64
+// sum of r'^2 over each 512-element slice of a row.  Workgroup (g, m) owns
+// slice g of row m, one 8-element chunk per lane, and stores its sum to
+// sq_out[m * gridDim.x + g]; the consumer adds the slices in slice order.
+// Every square of a bf16 value is exact in fp64, so these slice sums and
+// the one-pass sum of the whole row differ only where the row's squares span
+// more than fp64's 53 bits.  Spread over H/512 workgroups, the row's loads
+// are issued by as many CUs (one CU's request queue was the latency of the
+// one-workgroup form).
+__global__ __launch_bounds__(64) void k_add_sumsq(const uint16_t* __restrict__ r_prev,
+                                                  const uint16_t* __restrict__ y_prev,
+                                                  const float* __restrict__ y_part, int S, float alpha_d,
+                                                  uint16_t* __restrict__ y_store, uint16_t* __restrict__ r_out,
+                                                  double* __restrict__ sq_out, int M, int H) {
+  const int m = blockIdx.y, g = blockIdx.x;
+  const int ch = g * 64 + (int)threadIdx.x;
+  double sq = 0.0;
+  if (ch < H / 8) {
+    const size_t o = (size_t)m * H + (size_t)ch * 8;
+    const uint4 rv = *reinterpret_cast<const uint4*>(r_prev + o);
+    uint4 yv = make_uint4(0, 0, 0, 0);
+    if (y_part) {
+      yv = y_from_partials(y_part, (size_t)M * H, o, S, alpha_d);
+      *reinterpret_cast<uint4*>(y_store + o) = yv;
+    } else if (y_prev) {
+      yv = *reinterpret_cast<const uint4*>(y_prev + o);
+    }
+    const uint32_t rr[4] = {rv.x, rv.y, rv.z, rv.w}, yy[4] = {yv.x, yv.y, yv.z, yv.w};
+    uint32_t o4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o4[j] = pack_bf16x2(bf16_lo(rr[j]) + bf16_lo(yy[j]), bf16_hi(rr[j]) + bf16_hi(yy[j]));
+      const double dlo = (double)bf16_lo(o4[j]), dhi = (double)bf16_hi(o4[j]);
+      sq += dlo * dlo;
+      sq += dhi * dhi;
+    }
+    *reinterpret_cast<uint4*>(r_out + o) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+  }
+  sq = wave_sum_f64(sq);
+  if (threadIdx.x == 0) sq_out[(size_t)m * gridDim.x + g] = sq;
+}
+
 // Z = bf16(R + Y), the residual add after the last block.  With partials
 // (S > 1 splits of the last down GEMM) Y is formed first and stored to its
 // slot; with z == nullptr only that Y is written (a forward range that ends
@@ -394,6 +438,18 @@ hipError_t launch_add_rmsnorm_mx(const uint16_t* r_prev, const uint16_t* y_prev,
   else
     FRT_MX_NORM(8);
 #undef FRT_MX_NORM
+  return hipGetLastError();
+}
+
+// Slices per row of k_add_sumsq (the consumer's G).
+int add_sumsq_slices(int H) { return (H / 8 + 63) / 64; }
+
+hipError_t launch_add_sumsq(const uint16_t* r_prev, const uint16_t* y_prev, const float* y_part, int S,
+                            float alpha_d, uint16_t* y_store, uint16_t* r_out, double* sq_out, int M, int H,
+                            hipStream_t s) {
+  if (M < 1 || H % 8 || (y_part && (S < 1 || !y_store))) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_add_sumsq, dim3(add_sumsq_slices(H), M), dim3(64), 0, s, r_prev, y_prev, y_part, S, alpha_d,
+                     y_store, r_out, sq_out, M, H);
   return hipGetLastError();
 }
 

@@ -100,6 +100,30 @@ def test_small_shapes_gemv_down_split(spec):
     log(str(rep))
 
 
+@pytest.mark.parametrize("spec", [SMALL[0], SMALL[1], SMALL[2], (107, 1, 256, 2048, 2, ACT_SWIGLU)],
+                         ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
+def test_small_shapes_one_kernel_norm(spec, monkeypatch):
+    # decode shapes with the whole norm in one kernel (by default M <= 16
+    # splits it: slice sums in k_add_sumsq, quantisation in the gate/up GEMV)
+    monkeypatch.setenv("FRT_NORM_SPLIT", "0")
+    idx, M, H, I, L, act = spec
+    cfg = FFNConfig(idx, "small_onenorm_%d" % idx, M, H, I, L, act)
+    rep = run_case(cfg)
+    log(str(rep))
+
+
+@pytest.mark.parametrize("spec", [(117, 16, 1024, 512, 2, ACT_GEGLU_TANH), (118, 2, 640, 512, 3, ACT_SWIGLU),
+                                  (119, 1, 8192, 1024, 2, ACT_GELU_TANH)],
+                         ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
+def test_small_shapes_split_norm_slices(spec):
+    # the split norm with several slice sums per row (up to 16), a partial
+    # last slice, and waves with more chunks than one load group
+    idx, M, H, I, L, act = spec
+    cfg = FFNConfig(idx, "small_splitnorm_%d" % idx, M, H, I, L, act)
+    rep = run_case(cfg)
+    log(str(rep))
+
+
 @pytest.mark.parametrize("spec", [(109, 1, 256, 2048, 3, ACT_SWIGLU), (110, 4, 512, 2048, 2, ACT_GELU_TANH)],
                          ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
 def test_small_shapes_fused_norm_split(spec):
