@@ -126,15 +126,17 @@ int gemv_waves(int groups, int kblocks, const char* env, int target) {
   return w;
 }
 
-// K splits of the decode down GEMV: at least two workgroups per CU (a grid of
-// a few hundred workgroups leaves CUs with one and others with two, and the
-// per-CU load rate then sets the time), each split at least 8 K blocks.
-// Measured at H = 5120, I = 17408: 2 splits x 8 waves stream 5.1 TB/s
-// against 3.9 TB/s unsplit; more splits cost more in the consumer than they
-// gain.  FRT_GEMV_DOWN_SPLIT overrides.
-int gemv_down_splits(int groups, int kblocks) {
+// K splits of the decode down GEMV: at least `per_cu` workgroups per CU (a
+// grid of a few hundred workgroups leaves CUs with one and others with two,
+// and the per-CU load rate then sets the time), each split at least 8 K
+// blocks.  Measured at H = 5120, I = 17408: 2 splits x 8 waves stream 5.1
+// TB/s against 3.9 TB/s unsplit; 4 splits x 4 waves gain another 0.6 us
+// when the consumer is the many-workgroup slice-sum kernel (per_cu 4), but
+// cost more than they gain in the one-workgroup norm kernel (per_cu 2).
+// FRT_GEMV_DOWN_SPLIT overrides.
+int gemv_down_splits(int groups, int kblocks, int per_cu) {
   int s = 1;
-  while (groups * s < 2 * kCUs && kblocks / (2 * s) >= 8) s *= 2;
+  while (groups * s < per_cu * kCUs && kblocks / (2 * s) >= 8) s *= 2;
   s = env_int("FRT_GEMV_DOWN_SPLIT", s);
   return std::max(1, std::min(s, kblocks));
 }
@@ -325,6 +327,13 @@ Layout make_layout(const frt_ffn_desc& d) {
 
   size_t part = 0, words = 1;
   lo.gemv_mt = d.M > kGemvMaxM && d.M <= std::min(kGemvMtMaxM, env_int("FRT_GEMV_MT_MAX_M", kGemvMtMaxM));
+  // The decode GEMV path splits the norm: a short kernel forms r' and slice
+  // sums of squares, the gate/up GEMV quantises its own K range (measured
+  // at M = 1, H = 5120: the one-workgroup norm kernel's latency was its
+  // single CU's load queue).  FRT_NORM_SPLIT=0 keeps the one-kernel norm.
+  lo.norm_split = !lo.mx && !lo.gemv_mt && d.M <= kGemvMaxM &&
+                  (d.flags & (FRT_FLAG_FUSED_NORM | FRT_FLAG_ADA_NORM)) == 0u &&
+                  gemv_nq_supported((int)M, (int)H, add_sumsq_slices((int)H)) && env_int("FRT_NORM_SPLIT", 1) != 0;
   if (lo.mx_mm) {
     // K split of the MXFP4 down GEMM until its 128 x (32 nb) tiles give at
     // least one workgroup per CU (each split at least 8 stages)
@@ -339,7 +348,7 @@ Layout make_layout(const frt_ffn_desc& d) {
     words = 1;
   } else if (d.M <= kGemvMaxM || lo.gemv_mt || lo.mx) {
     lo.s_gu = gemv_waves((int)(I / 16), (int)(H / 128), "FRT_GEMV_WAVES_GATEUP", 6144);
-    lo.k_dn = gemv_down_splits((int)(H / 16), (int)(I / 128));
+    lo.k_dn = gemv_down_splits((int)(H / 16), (int)(I / 128), lo.norm_split ? 4 : 2);
     lo.s_dn = gemv_waves((int)(H / 16) * lo.k_dn, (int)(I / 128) / lo.k_dn, "FRT_GEMV_WAVES_DOWN", 4096);
     if (lo.mx) {
       // MXFP4 GEMVs: 4, 8 or 16 waves, fewer for more row tiles (LDS); the
@@ -374,17 +383,7 @@ Layout make_layout(const frt_ffn_desc& d) {
     part = lo.s_dn > 1 ? (size_t)lo.s_dn * M * H * 4 : 4;
     words = 1;
   }
-  // The decode GEMV path splits the norm: a short kernel forms r' and slice
-  // sums of squares, the gate/up GEMV quantises its own K range (measured
-  // at M = 1, H = 5120: the one-workgroup norm kernel's latency was its
-  // single CU's load queue).  FRT_NORM_SPLIT=0 keeps the one-kernel norm.
-  {
-    const int G = add_sumsq_slices((int)H);
-    lo.norm_split = !lo.mx && !lo.gemv_mt && d.M <= kGemvMaxM &&
-                    (d.flags & (FRT_FLAG_FUSED_NORM | FRT_FLAG_ADA_NORM)) == 0u &&
-                    gemv_nq_supported((int)M, (int)H, G) && env_int("FRT_NORM_SPLIT", 1) != 0;
-    lo.sqp = take(lo.norm_split ? M * G * 8 : 256);
-  }
+  lo.sqp = take(lo.norm_split ? M * (size_t)add_sumsq_slices((int)H) * 8 : 256);
   lo.part = take(part);
   lo.part_bytes = part;
   lo.cnt_words = words;
