@@ -52,6 +52,10 @@ hipError_t launch_add_sumsq(const uint16_t*, const uint16_t*, const float*, int,
                             int, int, hipStream_t);
 int add_sumsq_slices(int);
 bool gemv_nq_supported(int, int, int);
+bool gemv_mx_nq_supported(int, int, int);
+hipError_t launch_gemv_gateup_mx_nq(int, const uint16_t*, const uint16_t*, const float*, const double*, int, float,
+                                    uint8_t*, uint8_t*, const uint8_t*, const uint8_t*, uint8_t*, uint8_t*, int, int,
+                                    int, int, hipStream_t);
 hipError_t launch_gemv_gateup_nq(int, const uint16_t*, const uint16_t*, const double*, int, float, float, uint8_t*,
                                  const uint8_t*, uint8_t*, int, int, int, int, float, float, float, hipStream_t);
 hipError_t launch_add_rmsnorm_mx(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*, const float*,
@@ -131,8 +135,9 @@ int gemv_waves(int groups, int kblocks, const char* env, int target) {
 // and the per-CU load rate then sets the time), each split at least 8 K
 // blocks.  Measured at H = 5120, I = 17408: 2 splits x 8 waves stream 5.1
 // TB/s against 3.9 TB/s unsplit; 4 splits x 4 waves gain another 0.6 us
-// when the consumer is the many-workgroup slice-sum kernel (per_cu 4), but
-// cost more than they gain in the one-workgroup norm kernel (per_cu 2).
+// (MXFP4: 0.4 us) when the consumer is the many-workgroup slice-sum kernel
+// (per_cu 4), but cost more than they gain in the one-workgroup norm kernel
+// (per_cu 2).
 // FRT_GEMV_DOWN_SPLIT overrides.
 int gemv_down_splits(int groups, int kblocks, int per_cu) {
   int s = 1;
@@ -331,9 +336,14 @@ Layout make_layout(const frt_ffn_desc& d) {
   // sums of squares, the gate/up GEMV quantises its own K range (measured
   // at M = 1, H = 5120: the one-workgroup norm kernel's latency was its
   // single CU's load queue).  FRT_NORM_SPLIT=0 keeps the one-kernel norm.
-  lo.norm_split = !lo.mx && !lo.gemv_mt && d.M <= kGemvMaxM &&
-                  (d.flags & (FRT_FLAG_FUSED_NORM | FRT_FLAG_ADA_NORM)) == 0u &&
-                  gemv_nq_supported((int)M, (int)H, add_sumsq_slices((int)H)) && env_int("FRT_NORM_SPLIT", 1) != 0;
+  // The MXFP4 decode GEMV path does the same (k_gemv_gateup_mx_nq).
+  {
+    const int G = add_sumsq_slices((int)H);
+    const bool shape_ok = lo.mx ? (!lo.mx_mm && gemv_mx_nq_supported((int)M, (int)H, G))
+                                : (!lo.gemv_mt && gemv_nq_supported((int)M, (int)H, G));
+    lo.norm_split = shape_ok && d.M <= kGemvMaxM && (d.flags & (FRT_FLAG_FUSED_NORM | FRT_FLAG_ADA_NORM)) == 0u &&
+                    env_int("FRT_NORM_SPLIT", 1) != 0;
+  }
   if (lo.mx_mm) {
     // K split of the MXFP4 down GEMM until its 128 x (32 nb) tiles give at
     // least one workgroup per CU (each split at least 8 stages)
@@ -844,7 +854,12 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
   const float a_g = s_x * p->s_g[l], a_u = s_x * p->s_u[l], a_d = s_h * p->s_d[l];
   const bool fused = p->fused_norm();
   if (p->mx()) {
-    if (which == 0) {
+    if (which == 0 && p->lo.norm_split) {
+      const float* yp = (y_in_partials && l > 0) ? p->part() : nullptr;
+      KERNEL_CHECK(launch_add_sumsq(p->r(l), p->y(l), yp, p->lo.split_dn, 1.0f, p->y(l), p->r(l + 1), p->sqp(), M, H,
+                                    s),
+                   "add_sumsq");
+    } else if (which == 0) {
       const float* yp = (y_in_partials && l > 0) ? p->part() : nullptr;
       KERNEL_CHECK(launch_add_rmsnorm_mx(p->r(l), p->y(l), p->wn(l), p->mod(l), p->inv_awq(l), p->r(l + 1), p->xq(l),
                                          p->xs(l), M, H, p->d.eps, s, yp, p->lo.split_dn, 1.0f, p->y(l),
@@ -854,6 +869,11 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
       KERNEL_CHECK(launch_mxmm_gateup(p->d.act, p->xq(l), p->xs(l), p->wgu(l), p->wgu_s(l), p->hq(l), p->hs(l), M, H,
                                       npk, s),
                    "mxmm_gateup");
+    } else if (which == 1 && p->lo.norm_split) {
+      KERNEL_CHECK(launch_gemv_gateup_mx_nq(p->d.act, p->r(l + 1), p->wn(l), p->inv_awq(l), p->sqp(),
+                                            add_sumsq_slices(H), p->d.eps, p->xq(l), p->xs(l), p->wgu(l), p->wgu_s(l),
+                                            p->hq(l), p->hs(l), M, H, I, p->lo.s_gu, s),
+                   "gemv_gateup_mx_nq");
     } else if (which == 1) {
       KERNEL_CHECK(launch_gemv_gateup_mx(p->d.act, p->xq(l), p->xs(l), p->wgu(l), p->wgu_s(l), p->hq(l), p->hs(l), M,
                                          H, I, p->lo.s_gu, s),

@@ -203,6 +203,208 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup_mx(const uint8_t* __rest
   }
 }
 
+// Decode gate/up (M <= 16) that finishes the norm itself, as the E4M3
+// k_gemv_gateup_nq: after k_add_sumsq has formed r' and the slice sums of
+// r'^2, each wave forms the MXFP4 activation of its own K quads,
+// x = f32(f32(f32(r' * inv_rms) * w_norm) * inv_awq) with inv_rms =
+// f32(1 / sqrt(S / K + eps)) in fp64 from the row's slice sums in slice
+// order (the arithmetic of the MXFP4 k_add_rmsnorm_quant), each 32-block's
+// exponent from the 4-lane maximum of its chunks, the codes and exponents
+// into a wave-private LDS copy of the activation slot (codes [M][K/2],
+// exponents in the GEMV layout), and multiplies from there.  Workgroup 0
+// also stores them to the slot.  Loads are issued as: slice sums, the
+// r' / w_norm / inv_awq chunks, then the first quad's weights.
+struct MxNormQ {
+  const uint16_t* r;       // r' bf16 [M][K]
+  const uint16_t* w_norm;  // RMSNorm weight bf16 [K]
+  const float* inv_awq;    // AWQ reciprocal fp32 [K]
+  const double* sq;        // slice sums fp64 [M][G]
+  int G;
+  float eps;
+  uint8_t* xc_out;         // codes [M][K/2]
+  uint8_t* xs_out;         // exponents, GEMV layout (rows padded to 16)
+};
+constexpr int kMxNqChunks = 2;      // 8-element chunks per lane whose loads are issued together
+constexpr int kMxNqLdsBytes = 16384;  // codes M*K/2 + exponents K/2
+constexpr int kMxNqMaxSlices = 16;
+
+template <int ACT, int W>
+__global__ __launch_bounds__(W * 64) void k_gemv_gateup_mx_nq(const MxNormQ nq, const uint8_t* __restrict__ wc,
+                                                              const uint8_t* __restrict__ ws,
+                                                              uint8_t* __restrict__ hc, uint8_t* __restrict__ hs,
+                                                              int M, int K, int I) {
+  constexpr bool GATED = ACT != MX_GELU;
+  constexpr int NA = GATED ? 4 : 2;
+  extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];  // codes [M][K/2], then exponents [K/2]
+  __shared__ v4f red[W][NA][64];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int P = blockIdx.x;
+  const int KB = K >> 7, KQ = KB >> 2;
+  const int kq0 = wave * KQ / W, kq1 = (wave + 1) * KQ / W;  // empty when W > KQ
+  const int row = lane & 15, q = lane >> 4;
+  const bool has = row < M;
+  // a wave without quads loads the last quad's activations and weights (in
+  // bounds, unused) so that no load sits behind a branch, and writes nothing
+  const bool work = kq1 > kq0;
+  const int kqa = work ? kq0 : KQ - 1, nqw = work ? kq1 - kq0 : 1;
+  uint8_t* lds_c = xlds;
+  uint8_t* lds_s = xlds + (size_t)M * (K / 2);
+  uint32_t grp[NA];
+#pragma unroll
+  for (int a = 0; a < NA; ++a) grp[a] = (uint32_t)(NA * P + a);
+
+  // (1) activation-side loads: 64-chunk groups (512 elements, one row each)
+  const int G = nq.G;
+  const double part_v = nq.sq[lane < M * G ? lane : M * G - 1];
+  const int ngrp = M * nqw;
+  int gm[kMxNqChunks], gk[kMxNqChunks];
+  uint4 rv[kMxNqChunks], wv[kMxNqChunks];
+  float4 av[kMxNqChunks][2];
+  auto load_group = [&](int g0) {
+#pragma unroll
+    for (int j = 0; j < kMxNqChunks; ++j) {
+      int g = g0 + j;
+      g = g < ngrp ? g : ngrp - 1;  // a missing group redoes the last (same bytes)
+      const int m = g / nqw;
+      gm[j] = m;
+      gk[j] = (kqa * 64 + (g - m * nqw) * 64 + lane) * 8;  // first element of the lane's chunk
+      rv[j] = *reinterpret_cast<const uint4*>(nq.r + (size_t)m * K + gk[j]);
+      wv[j] = *reinterpret_cast<const uint4*>(nq.w_norm + gk[j]);
+      av[j][0] = *reinterpret_cast<const float4*>(nq.inv_awq + gk[j]);
+      av[j][1] = *reinterpret_cast<const float4*>(nq.inv_awq + gk[j] + 4);
+    }
+  };
+  load_group(0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // (2) the first quad's weights
+  v8i wq[4][NA];
+  int wsd[NA];
+#pragma unroll
+  for (int a = 0; a < NA; ++a) wsd[a] = *reinterpret_cast<const int*>(ws + mx_scale_off(grp[a] * 16, 4 * kqa, lane, KB));
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int a = 0; a < NA; ++a) wq[u][a] = mx_w16(wc + mx_code_off(grp[a] * 16, 4 * kqa + u, lane, KB));
+  __builtin_amdgcn_sched_barrier(0);
+
+  // (3) 1/rms of row `lane` (lanes < M), then this wave's codes and exponents
+  const double part = lane < M * G ? part_v : 0.0;
+  double ssum = 0.0;
+  {
+    const int base = lane < M ? lane * G : 0;
+    const unsigned long long b = (unsigned long long)__double_as_longlong(part);
+#pragma unroll
+    for (int g = 0; g < kMxNqMaxSlices; ++g) {
+      const int src = base + (g < G ? g : 0);
+      const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)b, src, 64);
+      const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(b >> 32), src, 64);
+      const double v = __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+      ssum += g < G ? v : 0.0;
+    }
+  }
+  const float inv_rms = (float)(1.0 / sqrt(ssum / (double)K + (double)nq.eps));
+  const bool store_x = blockIdx.x == 0;
+  auto quant_group = [&](int g0) {
+#pragma unroll
+    for (int j = 0; j < kMxNqChunks; ++j) {
+      if (!work || g0 + j >= ngrp) continue;  // uniform
+      const float inv = __shfl(inv_rms, gm[j], 64);
+      const uint32_t rr[4] = {rv[j].x, rv[j].y, rv[j].z, rv[j].w};
+      const uint32_t ww[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
+      const float aw[8] = {av[j][0].x, av[j][0].y, av[j][0].z, av[j][0].w,
+                           av[j][1].x, av[j][1].y, av[j][1].z, av[j][1].w};
+      float x[8];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        x[2 * t] = (bf16_lo(rr[t]) * inv) * bf16_lo(ww[t]);
+        x[2 * t + 1] = (bf16_hi(rr[t]) * inv) * bf16_hi(ww[t]);
+      }
+      float am = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        x[t] = x[t] * aw[t];
+        am = __builtin_fmaxf(am, __builtin_fabsf(x[t]));
+      }
+      am = quad_max(am);
+      const int e = mx_block_exp(am);
+      const uint32_t codes = mx_pack8(x, e);
+      const uint32_t m = (uint32_t)gm[j], ch = (uint32_t)gk[j] >> 3;
+      const size_t co = (size_t)m * (K / 2) + (size_t)ch * 4;
+      const size_t so = mx_act_scale_off_gemv(m, ch >> 2, (uint32_t)KB);
+      *reinterpret_cast<uint32_t*>(lds_c + co) = codes;
+      if ((ch & 3) == 0) lds_s[so] = (uint8_t)e;
+      if (store_x) {
+        *reinterpret_cast<uint32_t*>(nq.xc_out + co) = codes;
+        if ((ch & 3) == 0) nq.xs_out[so] = (uint8_t)e;
+      }
+    }
+  };
+  quant_group(0);
+  for (int g0 = kMxNqChunks; g0 < ngrp; g0 += kMxNqChunks) {
+    load_group(g0);
+    quant_group(g0);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // (4) the GEMV over this wave's quads, activations from LDS
+  v4f acc[NA];
+#pragma unroll
+  for (int a = 0; a < NA; ++a) acc[a] = v4f{0, 0, 0, 0};
+  const uint8_t* xcl = lds_c + (size_t)(has ? row : 0) * (K / 2) + q * 16;
+  for (int kq = kq0; kq < kq1; ++kq) {
+    if (kq != kq0) {
+#pragma unroll
+      for (int a = 0; a < NA; ++a)
+        wsd[a] = *reinterpret_cast<const int*>(ws + mx_scale_off(grp[a] * 16, 4 * kq, lane, KB));
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int a = 0; a < NA; ++a) wq[u][a] = mx_w16(wc + mx_code_off(grp[a] * 16, 4 * kq + u, lane, KB));
+    }
+    const int xsd = has ? *reinterpret_cast<const int*>(lds_s + ((size_t)kq * 64 + lane) * 4) : 0x7f7f7f7f;
+    v8i xv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint4 c = make_uint4(0, 0, 0, 0);
+      if (has) c = *reinterpret_cast<const uint4*>(xcl + (size_t)(4 * kq + u) * 64);
+      xv[u][0] = (int)c.x; xv[u][1] = (int)c.y; xv[u][2] = (int)c.z; xv[u][3] = (int)c.w;
+      xv[u][4] = 0; xv[u][5] = 0; xv[u][6] = 0; xv[u][7] = 0;
+    }
+    auto step = [&](auto U) {
+      constexpr int u = decltype(U)::value;
+#pragma unroll
+      for (int a = 0; a < NA; ++a) acc[a] = mx_mfma_u<u>(xv[u], xsd, wq[u][a], wsd[a], acc[a]);
+    };
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 2>{});
+    step(std::integral_constant<int, 3>{});
+  }
+#pragma unroll
+  for (int a = 0; a < NA; ++a) red[wave][a][lane] = acc[a];
+  __syncthreads();
+  if (wave != 0) return;
+  v4f f[NA];
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
+    f[a] = red[0][a][lane];
+#pragma unroll
+    for (int v = 1; v < W; ++v) f[a] += red[v][a][lane];
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = 4 * q + r;
+    const float h0 = GATED ? mx_gated<ACT>(f[0][r], f[1][r]) : mx_gated<ACT>(0.0f, f[0][r]);
+    const float h1 = GATED ? mx_gated<ACT>(f[2][r], f[3][r]) : mx_gated<ACT>(0.0f, f[1][r]);
+    const int mm = m < M ? m : 0;
+    mx_store_h32(h0, h1, m < M, row, hc + (size_t)mm * (I / 2) + (size_t)P * 16,
+                 hs + mx_act_scale_off_gemv((uint32_t)mm, (uint32_t)P, (uint32_t)I / 128));
+  }
+}
+
 // Down: one workgroup per 16 output columns and K split (gridDim.y), W waves
 // splitting the split's K blocks, MT tiles.  One split: bf16 Y; several:
 // fp32 partials [split][M][N] for the consumer (as the FP8 form).
@@ -317,6 +519,45 @@ static hipError_t gateup_mx_act(int W, const uint8_t* xc, const uint8_t* xs, con
 }
 
 int gemv_mx_max_waves(int M) { return M <= 16 ? 16 : (M <= 32 ? 8 : 4); }
+
+template <int ACT, int W>
+static void gateup_mx_nq_t(const MxNormQ& nq, const uint8_t* wc, const uint8_t* ws, uint8_t* hc, uint8_t* hs, int M,
+                           int K, int I, hipStream_t s) {
+  const size_t lds = (size_t)M * (K / 2) + (size_t)K / 2;
+  hipLaunchKernelGGL((k_gemv_gateup_mx_nq<ACT, W>), dim3(I / 32), dim3(W * 64), lds, s, nq, wc, ws, hc, hs, M, K, I);
+}
+
+template <int ACT>
+static hipError_t gateup_mx_nq_act(int W, const MxNormQ& nq, const uint8_t* wc, const uint8_t* ws, uint8_t* hc,
+                                   uint8_t* hs, int M, int K, int I, hipStream_t s) {
+  switch (W) {
+    case 4: gateup_mx_nq_t<ACT, 4>(nq, wc, ws, hc, hs, M, K, I, s); break;
+    case 5: gateup_mx_nq_t<ACT, 5>(nq, wc, ws, hc, hs, M, K, I, s); break;
+    case 8: gateup_mx_nq_t<ACT, 8>(nq, wc, ws, hc, hs, M, K, I, s); break;
+    case 10: gateup_mx_nq_t<ACT, 10>(nq, wc, ws, hc, hs, M, K, I, s); break;
+    case 16: gateup_mx_nq_t<ACT, 16>(nq, wc, ws, hc, hs, M, K, I, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Whether k_gemv_gateup_mx_nq takes the shape (the LDS copy of the slot fits,
+// every slice sum has a lane).
+bool gemv_mx_nq_supported(int M, int K, int G) {
+  return M >= 1 && M <= 16 && K % 512 == 0 && (long)M * (K / 2) + K / 2 <= kMxNqLdsBytes && G >= 1 &&
+         G <= kMxNqMaxSlices && M * G <= 64;
+}
+
+hipError_t launch_gemv_gateup_mx_nq(int act, const uint16_t* r, const uint16_t* w_norm, const float* inv_awq,
+                                    const double* sq, int G, float eps, uint8_t* xc_out, uint8_t* xs_out,
+                                    const uint8_t* wc, const uint8_t* ws, uint8_t* hc, uint8_t* hs, int M, int K,
+                                    int I, int W, hipStream_t s) {
+  if (!gemv_mx_nq_supported(M, K, G) || I % 32 || !inv_awq) return hipErrorInvalidValue;
+  const MxNormQ nq{r, w_norm, inv_awq, sq, G, eps, xc_out, xs_out};
+  if (act == MX_GEGLU) return gateup_mx_nq_act<MX_GEGLU>(W, nq, wc, ws, hc, hs, M, K, I, s);
+  if (act == MX_SWIGLU) return gateup_mx_nq_act<MX_SWIGLU>(W, nq, wc, ws, hc, hs, M, K, I, s);
+  return gateup_mx_nq_act<MX_GELU>(W, nq, wc, ws, hc, hs, M, K, I, s);
+}
 
 hipError_t launch_gemv_gateup_mx(int act, const uint8_t* xc, const uint8_t* xs, const uint8_t* wc, const uint8_t* ws,
                                  uint8_t* hc, uint8_t* hs, int M, int K, int I, int W, hipStream_t s) {

@@ -163,6 +163,20 @@ def test_mxfp4_small_awq(spec):
     run_mx_case(FFNConfig(idx, "mx_awq_%d" % idx, M, H, I, L, act), awq=True)
 
 
+@pytest.mark.parametrize("spec", [SMALL[0], SMALL[2]], ids=lambda s: "M%d" % s[1])
+def test_mxfp4_small_one_kernel_norm(spec, monkeypatch):
+    # M <= 16 with the whole norm in one kernel (by default it is split: slice
+    # sums in k_add_sumsq, quantisation in the gate/up GEMV)
+    monkeypatch.setenv("FRT_NORM_SPLIT", "0")
+    idx, M, H, I, L, act = spec
+    run_mx_case(FFNConfig(idx, "mx_onenorm_%d" % idx, M, H, I, L, act), awq=True)
+
+
+def test_mxfp4_small_split_norm_slices():
+    # the split norm with 16 slice sums per row (H = 8192)
+    run_mx_case(FFNConfig(136, "mx_splitnorm_136", 1, 8192, 512, 2, ACT_GEGLU_TANH), awq=True)
+
+
 def test_mxfp4_small_ada_norm():
     idx, M, H, I, L, act = SMALL[1]
     run_mx_case(FFNConfig(idx, "mx_ada_%d" % idx, M, H, I, L, act), flags=_abi.FRT_FLAG_ADA_NORM)
