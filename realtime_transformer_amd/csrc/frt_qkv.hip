@@ -32,6 +32,12 @@ hipError_t launch_quant_pack_qkv(const uint16_t*, uint8_t*, int, int, float, int
                                  hipStream_t);
 hipError_t launch_gemv_qkv(const uint8_t*, const uint8_t*, const QkvOut&, int, int, int, hipStream_t);
 hipError_t launch_mm_qkv(int, const uint8_t*, const uint8_t*, const QkvOut&, int, int, int, hipStream_t);
+hipError_t launch_add_sumsq(const uint16_t*, const uint16_t*, const float*, int, float, uint16_t*, uint16_t*, double*,
+                            int, int, hipStream_t);
+int add_sumsq_slices(int);
+bool gemv_qkv_nq_supported(int, int, int);
+hipError_t launch_gemv_qkv_nq(const uint16_t*, const uint16_t*, const double*, int, float, float, uint8_t*,
+                              const uint8_t*, const QkvOut&, int, int, int, hipStream_t);
 }  // namespace frt
 
 using namespace frt;
@@ -57,7 +63,8 @@ bool qkv_desc_ok(const frt_qkv_desc* d) {
 }
 
 struct QkvLayout {
-  size_t w, wn, mod, rope, r_in, y_in, pos, r_out, xq, q, k, v, amax, cal_x, cal_r, total;
+  size_t w, wn, mod, rope, r_in, y_in, pos, r_out, xq, q, k, v, amax, cal_x, cal_r, sqp, total;
+  bool norm_split;  // M <= 16: k_add_sumsq, then the QKV GEMV quantises its own K blocks (k_gemv_qkv_nq)
   int gemv_w;  // GEMV waves per workgroup (M <= 64)
   int mm_cfg;  // LDS-DMA GEMM configuration (M > 64)
 };
@@ -101,8 +108,17 @@ QkvLayout qkv_layout(const frt_qkv_desc& d) {
   lo.amax = take(256);
   lo.cal_x = take(M * H * 4);
   lo.cal_r = take(M * H * 2);
+  lo.sqp = take(M * (size_t)add_sumsq_slices(d.H) * 8);
   lo.total = off;
   lo.gemv_w = qkv_gemv_waves((int)(N / 32), d.H / 128, d.M);
+  // Opt-in (FRT_QKV_NORM_SPLIT=1): the decode norm in two parts, as on the
+  // FFN plan.  The per-block graph replay that the benchmark times is bound
+  // by the host's graph launch (about 27 us against 14 us of kernels), so
+  // the gain the FFN chain shows (2 us per layer) could not be measured here
+  // and the one-kernel norm stays the default.
+  lo.norm_split = d.M <= 16 && (d.flags & FRT_FLAG_ADA_NORM) == 0u &&
+                  gemv_qkv_nq_supported(d.M, d.H, add_sumsq_slices(d.H)) && lo.gemv_w <= d.H / 128 &&
+                  env_int("FRT_QKV_NORM_SPLIT", 0) != 0;
   lo.mm_cfg = -1;
   if (d.M > kQkvGemvMaxM) {
     int c = -1, sp = 1;
@@ -163,13 +179,22 @@ struct frt_qkv_plan {
 
 static frt_status qkv_launch(frt_qkv_plan* p, int which, hipStream_t s) {
   const int M = p->d.M, H = p->d.H;
-  if (which == 0) {
+  if (which == 0 && p->lo.norm_split) {
+    KERNEL_CHECK(launch_add_sumsq(p->at<uint16_t>(p->lo.r_in), p->at<uint16_t>(p->lo.y_in), nullptr, 1, 0.0f, nullptr,
+                                  p->at<uint16_t>(p->lo.r_out), p->at<double>(p->lo.sqp), M, H, s),
+                 "add_sumsq");
+  } else if (which == 0) {
     const float inv_x = 1.0f / p->s_x;
     KERNEL_CHECK(launch_add_rmsnorm_quant(p->at<uint16_t>(p->lo.r_in), p->at<uint16_t>(p->lo.y_in),
                                           p->at<uint16_t>(p->lo.wn), p->ada() ? p->at<uint16_t>(p->lo.mod) : nullptr,
                                           p->at<uint16_t>(p->lo.r_out), p->at<uint8_t>(p->lo.xq), M, H, p->d.eps,
                                           inv_x, s, nullptr, 1, 0.0f, nullptr),
                  "add_rmsnorm_quant");
+  } else if (p->lo.norm_split) {
+    KERNEL_CHECK(launch_gemv_qkv_nq(p->at<uint16_t>(p->lo.r_out), p->at<uint16_t>(p->lo.wn), p->at<double>(p->lo.sqp),
+                                    add_sumsq_slices(H), p->d.eps, 1.0f / p->s_x, p->at<uint8_t>(p->lo.xq),
+                                    p->at<uint8_t>(p->lo.w), p->out(), M, H, p->lo.gemv_w, s),
+                 "gemv_qkv_nq");
   } else if (M <= kQkvGemvMaxM) {
     KERNEL_CHECK(launch_gemv_qkv(p->at<uint8_t>(p->lo.xq), p->at<uint8_t>(p->lo.w), p->out(), M, H, p->lo.gemv_w, s),
                  "gemv_qkv");

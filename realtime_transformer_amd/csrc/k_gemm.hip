@@ -30,6 +30,7 @@
 //     of 64x64.  The down GEMM may split K across workgroups with the same
 //     last-arrival fixed-order reduction.
 #include "frt_device.h"
+#include "frt_normq.h"
 
 namespace frt {
 
@@ -196,17 +197,7 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup(const uint8_t* __restric
 // quantisation runs and only the activation loads (completed first) are
 // waited for.  LDS writes and reads stay inside one wave, which the LDS
 // serves in order.
-struct NormQ {
-  const uint16_t* r;       // r' = R[l+1], bf16 [M][K]
-  const uint16_t* w_norm;  // RMSNorm weight, bf16 [K]
-  const double* sq;        // slice sums of r'^2, fp64 [M][G]
-  int G;
-  float eps, inv_x;
-  uint8_t* xq_out;         // XQ[l], E4M3 [M][K] (workgroup 0 stores it)
-};
-constexpr int kNqChunks = 2;        // 8-element chunks per lane whose loads are issued together
-constexpr int kNqLdsBytes = 16384;  // row buffer M * K
-constexpr int kNqMaxSlices = 16;    // slice sums per row (H <= 8192)
+constexpr int kNqChunks = 2;  // 8-element chunks per lane whose loads are issued together
 
 template <int ACT, int W>
 __global__ __launch_bounds__(W * 64) void k_gemv_gateup_nq(const NormQ nq, const uint8_t* __restrict__ w,
@@ -225,32 +216,11 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup_nq(const NormQ nq, const
   const uint8_t* wg = w + (size_t)(GATED ? 2 * p : 0) * KB * 2048 + lane * 16;
   const uint8_t* wu = w + (size_t)(GATED ? 2 * p + 1 : p) * KB * 2048 + lane * 16;
 
-  // (1) activation-side loads: lane i < M*G holds slice sum i; chunk c of
-  // this wave's range is (row c / nkc, K chunk kb0 * 16 + c % nkc).  No
-  // load sits behind a branch (indices are clamped instead), so the
-  // compiler's wait before the quantisation counts only these loads and
-  // leaves the weight loads of (2) in flight.
-  const int G = nq.G;
-  const double part_v = nq.sq[lane < M * G ? lane : M * G - 1];
-  const int nkc = (kb1 - kb0) * 16, nch = M * nkc;  // kb1 > kb0: W <= K / 128
-  const float rcp_nkc = __builtin_amdgcn_rcpf((float)nkc);
-  int cm[kNqChunks], ck[kNqChunks];
-  uint4 rv[kNqChunks], wv[kNqChunks];
-  auto load_group = [&](int c0) {
-#pragma unroll
-    for (int j = 0; j < kNqChunks; ++j) {
-      int c = c0 + j * 64 + lane;
-      c = c < nch ? c : nch - 1;  // lanes past the end redo the last chunk (same bytes)
-      int m = (int)(((float)c + 0.5f) * rcp_nkc);
-      m -= (m * nkc > c) ? 1 : 0;
-      m += ((m + 1) * nkc <= c) ? 1 : 0;
-      cm[j] = m;
-      ck[j] = (kb0 * 16 + (c - m * nkc)) * 8;
-      rv[j] = *reinterpret_cast<const uint4*>(nq.r + (size_t)m * K + ck[j]);
-      wv[j] = *reinterpret_cast<const uint4*>(nq.w_norm + ck[j]);
-    }
-  };
-  load_group(0);
+  // (1) activation-side loads: the row's slice sums (lane i < M*G holds
+  // sum i) and the r' / w_norm chunks of this wave's K blocks
+  NormQWave<kNqChunks> nqw;
+  nqw.init(nq, M, K, kb0, kb1, lane);  // kb1 > kb0: W <= K / 128
+  nqw.load(nq, 0, lane);
   __builtin_amdgcn_sched_barrier(0);
 
   // (2) the first step's weights (a one-block range loads its block twice)
@@ -266,55 +236,15 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup_nq(const NormQ nq, const
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // (3) 1/rms of row `lane` (lanes < M; the others compute row 0's), then
-  // the codes of this wave's range
-  const double part = lane < M * G ? part_v : 0.0;
-  double ssum = 0.0;
-  {
-    const int base = lane < M ? lane * G : 0;
-    const unsigned long long b = (unsigned long long)__double_as_longlong(part);
-#pragma unroll
-    for (int g = 0; g < kNqMaxSlices; ++g) {
-      const int src = base + (g < G ? g : 0);
-      const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)b, src, 64);
-      const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(b >> 32), src, 64);
-      const double v = __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
-      ssum += g < G ? v : 0.0;
-    }
-  }
-  const float inv_rms = (float)(1.0 / sqrt(ssum / (double)K + (double)nq.eps));
+  // (3) 1/rms of row `lane` (lanes < M), then the codes of this wave's range
+  const float inv_rms = nqw.inv_rms(nq, lane);
   const bool store_xq = blockIdx.x == 0;
-  auto quant_group = [&](int c0) {
-#pragma unroll
-    for (int j = 0; j < kNqChunks; ++j) {
-      const float inv = __shfl(inv_rms, cm[j], 64);
-      const uint32_t rr[4] = {rv[j].x, rv[j].y, rv[j].z, rv[j].w};
-      const uint32_t ww[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
-      float x[8];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        x[2 * t] = (bf16_lo(rr[t]) * inv) * bf16_lo(ww[t]);
-        x[2 * t + 1] = (bf16_hi(rr[t]) * inv) * bf16_hi(ww[t]);
-      }
-      const float ix = nq.inv_x;
-      uint2 code;
-      code.x = e4m3x4(x[0] * ix, x[1] * ix, x[2] * ix, x[3] * ix);
-      code.y = e4m3x4(x[4] * ix, x[5] * ix, x[6] * ix, x[7] * ix);
-      if (c0 + j * 64 + lane < nch) {
-        const size_t o = (size_t)cm[j] * K + ck[j];
-        *reinterpret_cast<uint2*>(xrow + o) = code;
-        if (store_xq) *reinterpret_cast<uint2*>(nq.xq_out + o) = code;
-      }
-    }
-  };
-  quant_group(0);
-  for (int c0 = kNqChunks * 64; c0 < nch; c0 += kNqChunks * 64) {
-    load_group(c0);
-    quant_group(c0);
+  nqw.quant(nq, 0, lane, inv_rms, xrow, store_xq);
+  for (int c0 = kNqChunks * 64; c0 < nqw.nch; c0 += kNqChunks * 64) {
+    nqw.load(nq, c0, lane);
+    nqw.quant(nq, c0, lane, inv_rms, xrow, store_xq);
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  wave_lds_sync();
 
   // (4) the GEMV over this wave's K range, activations from LDS
   auto lds_x32 = [&](int kb, uint32_t o[8]) {
@@ -1102,11 +1032,8 @@ static void gemv_gateup_nq_w(int act, const NormQ& nq, const uint8_t* w, uint8_t
     hipLaunchKernelGGL((k_gemv_gateup_nq<GU_GELU, W>), grid, block, lds, s, nq, w, hq, M, K, I, a_g, a_u, inv_h);
 }
 
-// Whether k_gemv_gateup_nq takes the shape: the row buffer M*K fits its LDS
-// budget and every slice sum has a lane (M * G <= 64).
-bool gemv_nq_supported(int M, int K, int G) {
-  return M >= 1 && M <= 16 && K % 128 == 0 && (long)M * K <= kNqLdsBytes && G <= kNqMaxSlices && M * G <= 64;
-}
+// Whether k_gemv_gateup_nq takes the shape (frt_normq.h).
+bool gemv_nq_supported(int M, int K, int G) { return normq_shape_ok(M, K, G); }
 
 // gate/up GEMV from r' and the slice sums (k_add_sumsq) instead of XQ; the
 // codes it forms are stored to xq_out.

@@ -12,6 +12,7 @@
 // tiles, partials meeting in LDS in wave order); only the epilogue differs.
 // Bound: HBM (N*H weight bytes per launch), latency at small N.
 #include "frt_qkv_dev.h"
+#include "frt_normq.h"
 
 namespace frt {
 
@@ -184,6 +185,122 @@ __global__ __launch_bounds__(W * 64) void k_gemv_qkv(const uint8_t* __restrict__
     const int m = 16 * t + 4 * q + r;
     if (m < M) qkv_store(o, m, p, row, f[r], g[r]);
   }
+}
+
+// Decode form (M <= 16) after the split norm's slice-sum kernel: each wave
+// quantises the activations of its own K blocks into a wave-private LDS row
+// buffer (frt_normq.h) between issuing its first weight loads and using
+// them, then multiplies as k_gemv_qkv with one activation tile; workgroup 0
+// stores XQ.
+constexpr int kQkvNqChunks = 3;  // 8-element chunks per lane loaded together (a 10-block range: 160 chunks)
+
+template <int W>
+__global__ __launch_bounds__(W * 64) void k_gemv_qkv_nq(const NormQ nq, const uint8_t* __restrict__ w, const QkvOut o,
+                                                        int M, int K) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t xrow[];  // [M][K] E4M3
+  __shared__ v4f red[W][2][64];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int p = blockIdx.x;
+  const int KB = K >> 7;
+  const int kb0 = wave * KB / W, kb1 = (wave + 1) * KB / W;  // kb1 > kb0: W <= K / 128
+  const int row = lane & 15, q = lane >> 4;
+  const bool has = row < M;
+  const uint8_t* w1 = w + (size_t)(2 * p) * KB * 2048 + lane * 16;
+  const uint8_t* w2 = w + (size_t)(2 * p + 1) * KB * 2048 + lane * 16;
+
+  NormQWave<kQkvNqChunks> nqw;
+  nqw.init(nq, M, K, kb0, kb1, lane);
+  nqw.load(nq, 0, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t a0[8], a1[8], b0[8], b1[8];
+  {
+    const int kb_b = kb0 + 1 < kb1 ? kb0 + 1 : kb0;  // a one-block range loads its block twice
+    qkv_load_w32(w1, kb0, a0);
+    qkv_load_w32(w2, kb0, b0);
+    qkv_load_w32(w1, kb_b, a1);
+    qkv_load_w32(w2, kb_b, b1);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const float inv_rms = nqw.inv_rms(nq, lane);
+  const bool store_xq = blockIdx.x == 0;
+  nqw.quant(nq, 0, lane, inv_rms, xrow, store_xq);
+  for (int c0 = kQkvNqChunks * 64; c0 < nqw.nch; c0 += kQkvNqChunks * 64) {
+    nqw.load(nq, c0, lane);
+    nqw.quant(nq, c0, lane, inv_rms, xrow, store_xq);
+  }
+  wave_lds_sync();
+
+  auto lds_x32 = [&](int kb, uint32_t x[8]) {
+    uint4 a = make_uint4(0, 0, 0, 0), b = a;
+    if (has) {
+      const uint8_t* xp = xrow + (size_t)row * K + kb * 128 + q * 32;
+      a = *reinterpret_cast<const uint4*>(xp);
+      b = *reinterpret_cast<const uint4*>(xp + 16);
+    }
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  };
+  v4f acc1 = {0, 0, 0, 0}, acc2 = {0, 0, 0, 0};
+  auto mma = [&](const uint32_t x[8], const uint32_t wa[8], const uint32_t wb[8]) {
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const v8h xh = e4m3x8_to_f16(x[2 * s4], x[2 * s4 + 1]);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, e4m3x8_to_f16(wa[2 * s4], wa[2 * s4 + 1]), acc1, 0, 0, 0);
+      acc2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, e4m3x8_to_f16(wb[2 * s4], wb[2 * s4 + 1]), acc2, 0, 0, 0);
+    }
+  };
+  for (int kb = kb0; kb < kb1; kb += 2) {
+    const bool two = kb + 1 < kb1;
+    if (kb != kb0) {
+      qkv_load_w32(w1, kb, a0);
+      qkv_load_w32(w2, kb, b0);
+      if (two) {
+        qkv_load_w32(w1, kb + 1, a1);
+        qkv_load_w32(w2, kb + 1, b1);
+      }
+    }
+    uint32_t x0[8], x1[8];
+    lds_x32(kb, x0);
+    mma(x0, a0, b0);
+    if (two) {
+      lds_x32(kb + 1, x1);
+      mma(x1, a1, b1);
+    }
+  }
+  red[wave][0][lane] = acc1;
+  red[wave][1][lane] = acc2;
+  __syncthreads();
+  if (wave != 0) return;
+  v4f f = red[0][0][lane], g = red[0][1][lane];
+#pragma unroll
+  for (int v = 1; v < W; ++v) {
+    f += red[v][0][lane];
+    g += red[v][1][lane];
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = 4 * q + r;
+    if (m < M) qkv_store(o, m, p, row, f[r], g[r]);
+  }
+}
+
+bool gemv_qkv_nq_supported(int M, int K, int G) { return normq_shape_ok(M, K, G); }
+
+// M <= 16 after k_add_sumsq; W in {4, 8, 16}, at most K / 128.
+hipError_t launch_gemv_qkv_nq(const uint16_t* r, const uint16_t* w_norm, const double* sq, int G, float eps,
+                              float inv_x, uint8_t* xq_out, const uint8_t* w, const QkvOut& o, int M, int K, int W,
+                              hipStream_t s) {
+  if (!normq_shape_ok(M, K, G) || W > K / 128) return hipErrorInvalidValue;
+  const NormQ nq{r, w_norm, sq, G, eps, inv_x, xq_out};
+  const int pairs = (o.nq + 2 * o.nkv) * o.hd / 32;
+  const size_t lds = (size_t)M * K;
+  switch (W) {
+    case 4: hipLaunchKernelGGL((k_gemv_qkv_nq<4>), dim3(pairs), dim3(256), lds, s, nq, w, o, M, K); break;
+    case 8: hipLaunchKernelGGL((k_gemv_qkv_nq<8>), dim3(pairs), dim3(512), lds, s, nq, w, o, M, K); break;
+    case 16: hipLaunchKernelGGL((k_gemv_qkv_nq<16>), dim3(pairs), dim3(1024), lds, s, nq, w, o, M, K); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // (W = 16 only with MT <= 2: the reduction buffer is W * MT * 2 KiB of LDS)

@@ -113,6 +113,7 @@ SMALL = [
     (125, 16, 1024, 8, 1, 256, 788, 1024, 10000.0),  # 16 waves
     (126, 100, 256, 4, 2, 64, 3, 128, 10000.0),       # LDS-DMA GEMM, one row tile
     (127, 300, 384, 2, 1, 256, 0, 300, 10000.0),      # LDS-DMA GEMM, ragged row tiles
+    (128, 1, 1024, 4, 2, 64, 9, 32, 10000.0),         # one K block per wave
 ]
 
 
@@ -134,6 +135,20 @@ def test_qkv_small_ada_norm(spec):
     idx, M, H, nq, nkv, hd, pos0, max_pos, base = spec
     run_qkv_case(QkvConfig(idx, "qkv_ada_%d" % idx, M, H, nq, nkv, hd, pos0, max_pos, base),
                  flags=_abi.FRT_FLAG_ADA_NORM)
+
+
+@pytest.mark.parametrize("spec", [SMALL[4], SMALL[7]], ids=lambda s: "M%d_H%d" % (s[1], s[2]))
+def test_qkv_small_split_norm(spec, monkeypatch):
+    # M <= 16 with the norm split (opt-in): slice sums in k_add_sumsq, the
+    # quantisation of each wave's K blocks in the QKV GEMV
+    monkeypatch.setenv("FRT_QKV_NORM_SPLIT", "1")
+    idx, M, H, nq, nkv, hd, pos0, max_pos, base = spec
+    run_qkv_case(QkvConfig(idx, "qkv_splitnorm_%d" % idx, M, H, nq, nkv, hd, pos0, max_pos, base))
+
+
+def test_qkv_llm_decode_m1_split_norm(monkeypatch):
+    monkeypatch.setenv("FRT_QKV_NORM_SPLIT", "1")
+    run_qkv_case(QKV_CONFIGS["qkv_llm_decode_m1"])
 
 
 def test_qkv_action_expert_m50():
