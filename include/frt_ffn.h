@@ -78,10 +78,12 @@ typedef enum {
 /* FRT_FLAG_FUSED_NORM: for M <= 16 (when M*H <= 32768) run the add +
  *   RMSNorm + quantise step inside the gate/up GEMV kernel (two kernels per
  *   layer); every workgroup recomputes the rows' norm from the L2-resident
- *   inputs.  Results are identical to the separate kernel, which is the
- *   default because it measures no slower.  Ignored for other shapes and
- *   when the down GEMV splits K (its output then arrives as partial sums
- *   that the separate norm kernel adds). */
+ *   inputs (the previous down GEMV's split-K partial sums included).
+ *   Results are identical to the separate kernels.  Not the default: it
+ *   measures slower than the default decode layer, whose norm is split
+ *   between a short slice-sum kernel and the gate/up GEMV's prologue (each
+ *   wave quantises the activations of its own K range).  Ignored for other
+ *   shapes. */
 #define FRT_FLAG_FUSED_NORM 2u
 /* FRT_FLAG_FP8_MFMA_GATEUP: the gate/up GEMM for M > 16 runs on the FP8
  *   matrix cores (same accumulation behaviour as FRT_FLAG_FP8_MFMA_DOWN). */
@@ -268,13 +270,17 @@ frt_status frt_graph_replay(frt_plan *plan, void *stream);
 /* Eager forward of the whole chain with a HIP event recorded on `stream`
  * before and after every kernel; writes each kernel's duration in
  * milliseconds to host_ms[L][3] = {norm+quantise, gate/up GEMM, down GEMM}
- * (with the norm fused into gate/up, the first entry times an empty slot).
+ * (with the norm fused into gate/up, the first entry times an empty slot;
+ * with the split decode norm (M <= 16, the default there) the first entry
+ * is the slice-sum kernel and the gate/up entry includes the quantisation).
  * Same kernels and launch configuration as frt_ffn_forward.  Synchronises
  * `stream`.  For measuring per-kernel time inside a running program. */
 frt_status frt_ffn_forward_profiled(frt_plan *plan, void *stream, float *host_ms);
 
 /* Average duration in microseconds of one kernel kind (which: 0 norm +
- * quantise, 1 gate/up GEMM (including the norm when fused), 2 down GEMM):
+ * quantise (the slice-sum kernel under the split decode norm), 1 gate/up
+ * GEMM (including the norm when fused, the quantisation when split), 2 down
+ * GEMM):
  * launches it for every layer, `reps` times, back to back on `stream`
  * between two HIP events (same kernels and launch configuration as the
  * forward).  The activation slots are left undefined (run the forward or
