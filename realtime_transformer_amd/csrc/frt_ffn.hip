@@ -276,6 +276,20 @@ void choose_gemm(const frt_ffn_desc& d, Layout& lo) {
     }
     {
       choose_mm(d.M, d.H, d.I, true, c, sp);
+      // On the f16 cores, when the down GEMM's tile grid is small enough to
+      // need a K split, the 128 x 256 two-per-CU tile splits K until its
+      // workgroups cover 7/8 of the CUs: per wave 64 x 128 (three
+      // conversions per MFMA against four for 64 x 64).  Measured on the
+      // M = 788 chain: 167.3-168.8 against 171.1-173.0 us/layer (128 x 128,
+      // 2 splits); on the FP8 matrix cores level, so unchanged there.
+      const int c8 = kMMConfigTwoPerCU;
+      if (!fp8_dn && sp > 1 && d.H % mm_config_bn(c8) == 0 && d.I % mm_config_ks(c8) == 0) {
+        const int tiles8 = (d.H / mm_config_bn(c8)) * ceil_div(d.M, mm_config_bm(c8));
+        int sp8 = 1;
+        while (tiles8 * sp8 < kCUs * 7 / 8 && d.I / (mm_config_ks(c8) * sp8 * 2) >= 4) sp8 *= 2;
+        c = c8;
+        sp = sp8;
+      }
       c = env_int("FRT_MM_DOWN_CFG", c);
       sp = env_int("FRT_MM_DOWN_SPLIT", sp);
       if (mm_config_ffn(c) && d.H % mm_config_bn(c) == 0 && d.I % mm_config_ks(c) == 0 && sp >= 1 &&
