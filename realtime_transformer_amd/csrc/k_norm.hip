@@ -277,6 +277,7 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
 // more than fp64's 53 bits.  Spread over H/512 workgroups, the row's loads
 // are issued by as many CUs (one CU's request queue was the latency of the
 // one-workgroup form).
+template <int SMAX>
 __global__ __launch_bounds__(64) void k_add_sumsq(const uint16_t* __restrict__ r_prev,
                                                   const uint16_t* __restrict__ y_prev,
                                                   const float* __restrict__ y_part, int S, float alpha_d,
@@ -289,7 +290,29 @@ __global__ __launch_bounds__(64) void k_add_sumsq(const uint16_t* __restrict__ r
     const size_t o = (size_t)m * H + (size_t)ch * 8;
     const uint4 rv = *reinterpret_cast<const uint4*>(r_prev + o);
     uint4 yv = make_uint4(0, 0, 0, 0);
-    if (y_part) {
+    if (y_part && SMAX > 0) {
+      // every split's loads first (split index clamped, extra ones unused),
+      // then the sum in split order: one memory round trip for any S <= SMAX
+      const size_t stride = (size_t)M * H;
+      float4 lo[SMAX > 0 ? SMAX : 1], hi[SMAX > 0 ? SMAX : 1];
+#pragma unroll
+      for (int sp = 0; sp < SMAX; ++sp) {
+        const size_t so = (size_t)(sp < S ? sp : S - 1) * stride + o;
+        lo[sp] = *reinterpret_cast<const float4*>(y_part + so);
+        hi[sp] = *reinterpret_cast<const float4*>(y_part + so + 4);
+      }
+      float a[8] = {lo[0].x, lo[0].y, lo[0].z, lo[0].w, hi[0].x, hi[0].y, hi[0].z, hi[0].w};
+#pragma unroll
+      for (int sp = 1; sp < SMAX; ++sp) {
+        if (sp < S) {
+          a[0] += lo[sp].x; a[1] += lo[sp].y; a[2] += lo[sp].z; a[3] += lo[sp].w;
+          a[4] += hi[sp].x; a[5] += hi[sp].y; a[6] += hi[sp].z; a[7] += hi[sp].w;
+        }
+      }
+      yv = make_uint4(pack_bf16x2(a[0] * alpha_d, a[1] * alpha_d), pack_bf16x2(a[2] * alpha_d, a[3] * alpha_d),
+                      pack_bf16x2(a[4] * alpha_d, a[5] * alpha_d), pack_bf16x2(a[6] * alpha_d, a[7] * alpha_d));
+      *reinterpret_cast<uint4*>(y_store + o) = yv;
+    } else if (y_part) {
       yv = y_from_partials(y_part, (size_t)M * H, o, S, alpha_d);
       *reinterpret_cast<uint4*>(y_store + o) = yv;
     } else if (y_prev) {
@@ -448,8 +471,21 @@ hipError_t launch_add_sumsq(const uint16_t* r_prev, const uint16_t* y_prev, cons
                             float alpha_d, uint16_t* y_store, uint16_t* r_out, double* sq_out, int M, int H,
                             hipStream_t s) {
   if (M < 1 || H % 8 || (y_part && (S < 1 || !y_store))) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_add_sumsq, dim3(add_sumsq_slices(H), M), dim3(64), 0, s, r_prev, y_prev, y_part, S, alpha_d,
-                     y_store, r_out, sq_out, M, H);
+  const dim3 grid(add_sumsq_slices(H), M);
+#define FRT_SUMSQ(SM)                                                                                        \
+  hipLaunchKernelGGL((k_add_sumsq<SM>), grid, dim3(64), 0, s, r_prev, y_prev, y_part, S, alpha_d, y_store, r_out, \
+                     sq_out, M, H)
+  if (!y_part || S <= 4)
+    FRT_SUMSQ(4);
+  else if (S <= 8)
+    FRT_SUMSQ(8);
+  else if (S <= 17)
+    FRT_SUMSQ(17);
+  else if (S <= 32)
+    FRT_SUMSQ(32);
+  else
+    FRT_SUMSQ(0);  // splits summed by the loop of y_from_partials
+#undef FRT_SUMSQ
   return hipGetLastError();
 }
 
