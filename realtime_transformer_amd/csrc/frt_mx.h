@@ -80,18 +80,58 @@ __device__ __forceinline__ float mx_gated(float g, float u) {
 // exponent by lane row 0.  Every lane of the wave must call it (lane moves);
 // `store` says whether this row exists.  codes points at the block's 16
 // bytes of the row, scale at its exponent byte.
-__device__ __forceinline__ void mx_store_h32(float h0, float h1, bool store, int row, uint8_t* codes,
-                                             uint8_t* scale) {
-  const float am = row16_max(__builtin_fmaxf(__builtin_fabsf(h0), __builtin_fabsf(h1)));
+// The two halves: mx_h32_codes returns the block exponent in bits 16..23
+// and the lane pair's two code bytes in bits 0..15 (valid in the even lane);
+// mx_h32_store writes them.  Callers with many blocks form every block's
+// codes first and store afterwards, so the lane moves and transcendentals of
+// independent blocks share one basic block (the stores' row guards would
+// otherwise split it and leave each lane move waiting on its own hazard).
+// 16-lane maximum of non-negative values through their bit patterns (for
+// finite values >= 0 the integer order is the float order), so no float
+// maximum needs its inputs canonicalised
+__device__ __forceinline__ uint32_t row16_max_u(uint32_t v) {
+  v = max(v, dpp_u32<DPP_QUAD_X1>(v));
+  v = max(v, dpp_u32<DPP_QUAD_X2>(v));
+  v = max(v, dpp_u32<DPP_ROW_HALF_MIRROR>(v));
+  return max(v, dpp_u32<DPP_ROW_MIRROR>(v));
+}
+__device__ __forceinline__ uint32_t mx_h32_pack(float h0, float h1, float am) {
   const int e = mx_block_exp(am);
   const float x0 = ldexpf(h0, 127 - e), x1 = ldexpf(h1, 127 - e);
   // the odd lane's values reach its even neighbour, which packs the byte
   const uint32_t b = e2m1_pack2<1>(e2m1_pack2<0>(0u, x0, dpp_f32<DPP_QUAD_X1>(x0)), x1, dpp_f32<DPP_QUAD_X1>(x1));
+  return (b & 0xffffu) | ((uint32_t)e << 16);
+}
+__device__ __forceinline__ uint32_t mx_h32_codes(float h0, float h1) {
+  const uint32_t am = row16_max_u(__float_as_uint(__builtin_fmaxf(__builtin_fabsf(h0), __builtin_fabsf(h1))));
+  return mx_h32_pack(h0, h1, __uint_as_float(am));
+}
+// two blocks at once, their lane-move chains interleaved (each lane move
+// waits on the previous step of its own chain only)
+__device__ __forceinline__ void mx_h32_codes2(float a0, float a1, float b0, float b1, uint32_t& ra, uint32_t& rb) {
+  uint32_t va = __float_as_uint(__builtin_fmaxf(__builtin_fabsf(a0), __builtin_fabsf(a1)));
+  uint32_t vb = __float_as_uint(__builtin_fmaxf(__builtin_fabsf(b0), __builtin_fabsf(b1)));
+  va = max(va, dpp_u32<DPP_QUAD_X1>(va));
+  vb = max(vb, dpp_u32<DPP_QUAD_X1>(vb));
+  va = max(va, dpp_u32<DPP_QUAD_X2>(va));
+  vb = max(vb, dpp_u32<DPP_QUAD_X2>(vb));
+  va = max(va, dpp_u32<DPP_ROW_HALF_MIRROR>(va));
+  vb = max(vb, dpp_u32<DPP_ROW_HALF_MIRROR>(vb));
+  va = max(va, dpp_u32<DPP_ROW_MIRROR>(va));
+  vb = max(vb, dpp_u32<DPP_ROW_MIRROR>(vb));
+  ra = mx_h32_pack(a0, a1, __uint_as_float(va));
+  rb = mx_h32_pack(b0, b1, __uint_as_float(vb));
+}
+__device__ __forceinline__ void mx_h32_store(uint32_t be, bool store, int row, uint8_t* codes, uint8_t* scale) {
   if (store && (row & 1) == 0) {
-    codes[row >> 1] = (uint8_t)b;
-    codes[8 + (row >> 1)] = (uint8_t)(b >> 8);
-    if (row == 0) *scale = (uint8_t)e;
+    codes[row >> 1] = (uint8_t)be;
+    codes[8 + (row >> 1)] = (uint8_t)(be >> 8);
+    if (row == 0) *scale = (uint8_t)(be >> 16);
   }
+}
+__device__ __forceinline__ void mx_store_h32(float h0, float h1, bool store, int row, uint8_t* codes,
+                                             uint8_t* scale) {
+  mx_h32_store(mx_h32_codes(h0, h1), store, row, codes, scale);
 }
 
 __device__ __forceinline__ v4f mx_mfma(v8i a, int sa, v8i b, int sb, v4f c) {

@@ -223,6 +223,33 @@ __global__ __launch_bounds__(256, 2) void k_mxmm(const uint8_t* __restrict__ xc,
     // this wave's packed groups g0 + NB wn .. + NB - 1: NB / 4 gated 32-column
     // blocks starting at P, or NB / 2 plain ones starting at 2 P
     const int P = (g0 + NB * wn) >> 2;
+    // every block's codes first (one basic block), then the stores
+    constexpr int NBLK = (EPI == MXM_GELU) ? NB / 2 : NB / 4;  // 32-column blocks per row
+    uint32_t be[4][4][NBLK];
+    // (two rows r, r + 1 at a time, their lane-move chains interleaved)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; r += 2)
+#pragma unroll
+        for (int c = 0; c < NB / 4; ++c) {
+          // groups 4c .. 4c + 3 of the wave: one gated block, or two plain
+          if (EPI == MXM_GELU) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              mx_h32_codes2(mx_gated<MX_GELU>(0.0f, acc[i][4 * c + 2 * h][r]),
+                            mx_gated<MX_GELU>(0.0f, acc[i][4 * c + 2 * h + 1][r]),
+                            mx_gated<MX_GELU>(0.0f, acc[i][4 * c + 2 * h][r + 1]),
+                            mx_gated<MX_GELU>(0.0f, acc[i][4 * c + 2 * h + 1][r + 1]), be[i][r][2 * c + h],
+                            be[i][r + 1][2 * c + h]);
+          } else {
+            mx_h32_codes2(mx_gated<EPI>(acc[i][4 * c][r], acc[i][4 * c + 1][r]),
+                          mx_gated<EPI>(acc[i][4 * c + 2][r], acc[i][4 * c + 3][r]),
+                          mx_gated<EPI>(acc[i][4 * c][r + 1], acc[i][4 * c + 1][r + 1]),
+                          mx_gated<EPI>(acc[i][4 * c + 2][r + 1], acc[i][4 * c + 3][r + 1]), be[i][r][c],
+                          be[i][r + 1][c]);
+          }
+        }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -231,22 +258,9 @@ __global__ __launch_bounds__(256, 2) void k_mxmm(const uint8_t* __restrict__ xc,
         const int mm = m < M ? m : 0;
         uint8_t* hrow = hc + (size_t)mm * (I / 2);
 #pragma unroll
-        for (int c = 0; c < NB / 4; ++c) {
-          // groups 4c .. 4c + 3 of the wave: one gated block, or two plain
-          if (EPI == MXM_GELU) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const int Pb = 2 * P + 2 * c + h;
-              const float h0 = mx_gated<MX_GELU>(0.0f, acc[i][4 * c + 2 * h][r]);
-              const float h1 = mx_gated<MX_GELU>(0.0f, acc[i][4 * c + 2 * h + 1][r]);
-              mx_store_h32(h0, h1, m < M, row, hrow + (size_t)Pb * 16, hs + mx_act_scale_off_mm(mm, Pb, KBh));
-            }
-          } else {
-            const int Pb = P + c;
-            const float h0 = mx_gated<EPI>(acc[i][4 * c][r], acc[i][4 * c + 1][r]);
-            const float h1 = mx_gated<EPI>(acc[i][4 * c + 2][r], acc[i][4 * c + 3][r]);
-            mx_store_h32(h0, h1, m < M, row, hrow + (size_t)Pb * 16, hs + mx_act_scale_off_mm(mm, Pb, KBh));
-          }
+        for (int b = 0; b < NBLK; ++b) {
+          const int Pb = (EPI == MXM_GELU) ? 2 * P + b : P + b;
+          mx_h32_store(be[i][r][b], m < M, row, hrow + (size_t)Pb * 16, hs + mx_act_scale_off_mm(mm, Pb, KBh));
         }
       }
     }
