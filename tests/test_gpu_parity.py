@@ -112,6 +112,19 @@ def test_small_shapes_one_kernel_norm(spec, monkeypatch):
     log(str(rep))
 
 
+@pytest.mark.parametrize("split,spec", [(8, (120, 1, 512, 2048, 2, ACT_SWIGLU)), (17, (129, 1, 512, 4352, 2, ACT_GEGLU_TANH)),
+                                        (32, (130, 3, 512, 4096, 2, ACT_GELU_TANH))],
+                         ids=lambda v: "S%d" % v if isinstance(v, int) else "M%d_H%d_I%d" % (v[1], v[2], v[3]))
+def test_small_shapes_many_down_splits(split, spec, monkeypatch):
+    # the decode down GEMV split into 8, 17 or 32 parts: the slice-sum kernel
+    # loads every split's partial rows before adding them in split order
+    monkeypatch.setenv("FRT_GEMV_DOWN_SPLIT", str(split))
+    idx, M, H, I, L, act = spec
+    cfg = FFNConfig(idx, "small_splits%d_%d" % (split, idx), M, H, I, L, act)
+    rep = run_case(cfg)
+    log(str(rep))
+
+
 @pytest.mark.parametrize("spec", [(117, 16, 1024, 512, 2, ACT_GEGLU_TANH), (118, 2, 640, 512, 3, ACT_SWIGLU),
                                   (119, 1, 8192, 1024, 2, ACT_GELU_TANH)],
                          ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
