@@ -280,8 +280,8 @@ def main():
                     help="skip the calibration pass (scales fixed to 1/448-ish); for profiling runs")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(rows shard with zero exchange; see the design notes). Use --gpus 1.", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
+              "(token rows would shard across GPUs with no exchange). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -7,7 +7,7 @@ count).  A bf16 input is the top 16 bits of its fp32 draw (truncation toward
 zero): a plain bit extraction, no rounding logic, which shifts each value by
 less than 2^-8 of itself.
 
-Distributions (one reading per workload, stated in the design doc of the repo):
+Distributions (one reading per workload):
   weights        W_gate, W_up [I,H], W_down [H,I] ~ N(0, 0.02) (std), bf16
   RMSNorm weight 1 + N(0, 0.1), bf16;  eps = 1e-6
   residual R[0]  N(0, 1) bf16; the M=788 prefix has rows 768..787 (20 text-like
