@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
   // it) and the uniform choices select pointers, so no load waits behind a
   // per-chunk branch.  wn: the norm weight, or with modulation the
   // per-channel scale (mh: shift); aw: the MXFP4 form's AWQ reciprocals;
-  // p0, p1: the first two split-K partial tiles (further splits are read
+  // pp: the first four split-K partial tiles (further splits are read
   // after these, in split order).  This is for the one-workgroup-per-row
   // form (small M, where the row's latency is the kernel's time: the M = 1,
   // H = 5120 decode chain gains 0.4 us per layer); the many-row form (one
@@ -70,11 +70,13 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
   constexpr bool PF = UP && NC <= 4;
   uint4 rn[NC], wn[NC], mh[NC], yv[NC];
   float4 aw[MX ? NC : 1][2];
-  float4 p0[PF ? NC : 1][2], p1[PF ? NC : 1][2];
+  // the first four split-K partial tiles (split index clamped to S - 1;
+  // splits past the fourth are read one at a time after these)
+  constexpr int SP = 4;
+  float4 pp[SP][PF ? NC : 1][2];
   const uint16_t* wsrc = mod ? mod : w_norm;
   const uint16_t* hsrc = mod ? mod + H : w_norm;
   const size_t pstride = (size_t)M * H;
-  const int s1 = S > 1 ? 1 : 0;
   // loads of chunk c (clamped into the row)
   auto load_chunk = [&](int c) {
     const int chc = min(t + c * TPR, nchunk - 1);
@@ -98,10 +100,12 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const size_t o = base + (size_t)min(t + c * TPR, nchunk - 1) * 8;
-        p0[PF ? c : 0][0] = *reinterpret_cast<const float4*>(y_part + o);
-        p0[PF ? c : 0][1] = *reinterpret_cast<const float4*>(y_part + o + 4);
-        p1[PF ? c : 0][0] = *reinterpret_cast<const float4*>(y_part + s1 * pstride + o);
-        p1[PF ? c : 0][1] = *reinterpret_cast<const float4*>(y_part + s1 * pstride + o + 4);
+#pragma unroll
+        for (int sp = 0; sp < SP; ++sp) {
+          const size_t so = (size_t)(sp < S ? sp : S - 1) * pstride + o;
+          pp[sp][PF ? c : 0][0] = *reinterpret_cast<const float4*>(y_part + so);
+          pp[sp][PF ? c : 0][1] = *reinterpret_cast<const float4*>(y_part + so + 4);
+        }
       }
     }
   }
@@ -124,18 +128,25 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
       const size_t o = base + (size_t)min(ch, nchunk - 1) * 8;
       const int pc = PF ? c : 0;
       if (!PF) {
-        p0[0][0] = *reinterpret_cast<const float4*>(y_part + o);
-        p0[0][1] = *reinterpret_cast<const float4*>(y_part + o + 4);
-        p1[0][0] = *reinterpret_cast<const float4*>(y_part + s1 * pstride + o);
-        p1[0][1] = *reinterpret_cast<const float4*>(y_part + s1 * pstride + o + 4);
+#pragma unroll
+        for (int sp = 0; sp < SP; ++sp) {
+          const size_t so = (size_t)(sp < S ? sp : S - 1) * pstride + o;
+          pp[sp][0][0] = *reinterpret_cast<const float4*>(y_part + so);
+          pp[sp][0][1] = *reinterpret_cast<const float4*>(y_part + so + 4);
+        }
       }
-      float a[8] = {p0[pc][0].x, p0[pc][0].y, p0[pc][0].z, p0[pc][0].w,
-                    p0[pc][1].x, p0[pc][1].y, p0[pc][1].z, p0[pc][1].w};
+      float a[8] = {pp[0][pc][0].x, pp[0][pc][0].y, pp[0][pc][0].z, pp[0][pc][0].w,
+                    pp[0][pc][1].x, pp[0][pc][1].y, pp[0][pc][1].z, pp[0][pc][1].w};
       if (S > 1) {
-        a[0] += p1[pc][0].x; a[1] += p1[pc][0].y; a[2] += p1[pc][0].z; a[3] += p1[pc][0].w;
-        a[4] += p1[pc][1].x; a[5] += p1[pc][1].y; a[6] += p1[pc][1].z; a[7] += p1[pc][1].w;
+#pragma unroll
+        for (int sp = 1; sp < SP; ++sp) {
+          if (sp < S) {
+            a[0] += pp[sp][pc][0].x; a[1] += pp[sp][pc][0].y; a[2] += pp[sp][pc][0].z; a[3] += pp[sp][pc][0].w;
+            a[4] += pp[sp][pc][1].x; a[5] += pp[sp][pc][1].y; a[6] += pp[sp][pc][1].z; a[7] += pp[sp][pc][1].w;
+          }
+        }
       }
-      for (int sp = 2; sp < S; ++sp) {
+      for (int sp = SP; sp < S; ++sp) {
         const float4 q0 = *reinterpret_cast<const float4*>(y_part + sp * pstride + o);
         const float4 q1 = *reinterpret_cast<const float4*>(y_part + sp * pstride + o + 4);
         a[0] += q0.x; a[1] += q0.y; a[2] += q0.z; a[3] += q0.w;
