@@ -171,6 +171,7 @@ struct Layout {
   bool mm_gu, mm_dn;   // GEMM runs on the LDS-DMA f16 kernel (k_mm) rather than k_gemm
   bool norm_split;     // decode GEMV path: k_add_sumsq, then the gate/up GEMV quantises (k_gemv_gateup_nq)
   size_t sqp;          // its slice sums of squares, fp64 [M][G]
+  size_t sqp_bytes;    // bytes of that region
 };
 
 
@@ -182,7 +183,8 @@ bool desc_ok(const frt_ffn_desc* d) {
   if (d->act < FRT_ACT_GEGLU_TANH || d->act > FRT_ACT_GELU_TANH) return false;
   if (!(d->eps > 0.0f) || !std::isfinite(d->eps)) return false;
   if ((d->flags & ~(uint32_t)(FRT_FLAG_FP8_MFMA_DOWN | FRT_FLAG_FUSED_NORM | FRT_FLAG_FP8_MFMA_GATEUP |
-                              FRT_FLAG_NORM_FUSE | FRT_FLAG_ADA_NORM | FRT_FLAG_MXFP4)) != 0u || d->device < 0)
+                              FRT_FLAG_NORM_FUSE | FRT_FLAG_ADA_NORM | FRT_FLAG_MXFP4)) != 0u ||
+      d->device < 0)
     return false;
   // MXFP4: K dimensions in whole groups of four 128-blocks (one exponent
   // dword per lane in the GEMV layout), no FP8 or fused-norm options
@@ -193,7 +195,10 @@ bool desc_ok(const frt_ffn_desc* d) {
   // AdaRMSNorm replaces the norm weight: no folding of it, and no fused
   // decode prologue (which applies the weight)
   if ((d->flags & FRT_FLAG_ADA_NORM) && (d->flags & (FRT_FLAG_NORM_FUSE | FRT_FLAG_FUSED_NORM))) return false;
+  // activation offsets inside the kernels are 32-bit: M*I and M*H bytes
+  // (and the fp32 split-K partials, 4*M*H per split, addressed per split)
   if ((int64_t)d->M * d->I > (int64_t)1 << 31) return false;
+  if ((int64_t)d->M * d->H > (int64_t)1 << 31) return false;
   return true;
 }
 
@@ -407,7 +412,8 @@ Layout make_layout(const frt_ffn_desc& d) {
     part = lo.s_dn > 1 ? (size_t)lo.s_dn * M * H * 4 : 4;
     words = 1;
   }
-  lo.sqp = take(lo.norm_split ? M * (size_t)add_sumsq_slices((int)H) * 8 : 256);
+  lo.sqp_bytes = lo.norm_split ? M * (size_t)add_sumsq_slices((int)H) * 8 : 256;
+  lo.sqp = take(lo.sqp_bytes);
   lo.part = take(part);
   lo.part_bytes = part;
   lo.cnt_words = words;

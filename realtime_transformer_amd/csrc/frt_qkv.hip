@@ -59,6 +59,8 @@ bool qkv_desc_ok(const frt_qkv_desc* d) {
   if ((d->flags & FRT_FLAG_NORM_FUSE) && (d->flags & FRT_FLAG_ADA_NORM)) return false;
   const int64_t N = (int64_t)(d->nq + 2 * d->nkv) * d->hd;
   if (N > 65536 || (int64_t)d->M * N > ((int64_t)1 << 31)) return false;
+  // activation offsets inside the kernels are 32-bit
+  if ((int64_t)d->M * d->H > ((int64_t)1 << 31)) return false;
   return true;
 }
 

@@ -11,16 +11,24 @@ Checks (tolerances from the workload statement; C-19 reading for HQ):
             sums fp32 in its own order, the oracle in fp64)
   per block (teacher-forced, every checked layer):
             R  bit-exact
-            XQ adjacent-code mismatches only, rate <= 1e-4
-            HQ adjacent-code mismatches only, rate <= 1e-4
+            XQ every mismatch adjacent and within 1 fp32 ulp of the E4M3
+               rounding boundary (its inputs are identical on both sides),
+               rate <= 1e-4
+            HQ adjacent-code mismatches only, rate <= 1e-4, and each one
+               reachable by an fp32 accumulation error of at most
+               T_MAX_EXPLAINED units (tests/_hq_explain.py)
             Y  max|d|/max|ref| <= 2e-2 and cosine >= 0.999
-  chain     free-running Z cosine >= 0.999 against the oracle's chain
+  chain     free-running: the GPU's distance from the oracle (1 - cosine of
+            Z) against the spread of several valid fp32 summation orders
+            (tests/_natural.py)
   graph     replay == eager forward, bit for bit; two replays agree
   saturation every XQ/HQ code finite (no 0x7f/0xff)
 """
 from __future__ import annotations
 
+import json
 import math
+import os
 import time
 from dataclasses import dataclass, field
 from typing import List, Optional, Sequence
@@ -33,6 +41,7 @@ from realtime_transformer_amd import _abi, datagen
 from realtime_transformer_amd.configs import FFNConfig
 from realtime_transformer_amd.plan import FFNPlan, to_np_u16, to_np_u8
 
+import _hq_explain
 import _natural
 
 CODE_RATE = 1e-4
@@ -47,12 +56,34 @@ MIN_COS = 0.999
 # then moves by up to a few of those steps: CAL_RTOL.
 CAL_RTOL_FIRST = 1e-4
 CAL_RTOL = 1e-2
-# Free-running chain: the GPU's distance from the oracle (1 - cosine of Z)
-# may be at most DRIFT_FACTOR times the distance between the oracle and a
-# second valid implementation (fp32 GEMM sums in BLAS order), plus a floor
-# for chains too short to drift at all.
-DRIFT_FACTOR = 4.0
+# Free-running chain (no teacher forcing): Z must reach cosine >= MIN_COS
+# against the oracle's chain, or, where valid implementations themselves
+# drift further than that (the 64-layer M=1 chain), the GPU's distance
+# (1 - cosine) may be at most DRIFT_FACTOR times the largest distance of the
+# valid fp32 summation orders in tests/_natural.py, plus a floor for chains
+# too short to drift.  DRIFT_FACTOR: across the five workloads the largest
+# of those distances is up to 2.1x the smallest (M=4096: 3.4e-4 to 7.1e-4),
+# so an implementation with yet another valid order can sit that far above
+# the largest; rounded up to 2.5.
+DRIFT_FACTOR = 2.5
 DRIFT_FLOOR = 1e-6
+NATURAL_DRIFT_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "natural_drift.json")
+
+
+def stored_natural_drift(cfg: FFNConfig, rows, cal_rows) -> Optional[dict]:
+    """Distances of the valid orders for a named workload, stored by
+    tests/golden/make_natural_drift.py (the oracle and tests/_natural.py
+    only), or None if there is no record for these rows."""
+    if not os.path.exists(NATURAL_DRIFT_FILE):
+        return None
+    rec = json.load(open(NATURAL_DRIFT_FILE)).get(cfg.name)
+    if rec is None:
+        return None
+    want_rows = None if rows is None else [int(r) for r in rows]
+    want_cal = None if cal_rows is None else [int(r) for r in cal_rows]
+    if rec["rows"] != want_rows or rec["cal_rows"] != want_cal or rec["shape"] != [cfg.M, cfg.H, cfg.I, cfg.L]:
+        return None
+    return rec["distances"]
 # Free-running whole-chain calibration: after tens of layers the measurement
 # chains of two valid implementations (fp32 vs fp64 sums) drift apart by a
 # few percent in amax; gated only as a sanity bound.  The per-layer check
@@ -99,10 +130,22 @@ def code_stats(gpu: np.ndarray, ref: np.ndarray, pre: Optional[np.ndarray] = Non
     return st
 
 
-def check_codes(name: str, st: CodeStats):
-    assert st.max_rank_diff <= 1, "%s: non-adjacent code mismatch (%d steps)" % (name, st.max_rank_diff)
-    assert st.rate <= CODE_RATE, "%s: code mismatch rate %.3g > %g (%d/%d)" % (
-        name, st.rate, CODE_RATE, st.mismatches, st.n)
+class CodeToleranceMiss(AssertionError):
+    """An FP8 byte tolerance (rate, adjacency or boundary rule) is missed."""
+
+
+def check_codes(name: str, st: CodeStats, boundary_rule: bool = False):
+    """Adjacency and rate; with boundary_rule (XQ, whose inputs are identical
+    on both sides) every mismatch must also lie within 1 fp32 ulp of the
+    rounding boundary between the two codes."""
+    if st.max_rank_diff > 1:
+        raise CodeToleranceMiss("%s: non-adjacent code mismatch (%d steps)" % (name, st.max_rank_diff))
+    if st.rate > CODE_RATE:
+        raise CodeToleranceMiss("%s: code mismatch rate %.3g > %g (%d/%d)" % (
+            name, st.rate, CODE_RATE, st.mismatches, st.n))
+    if boundary_rule and st.mismatches and st.near_boundary != st.mismatches:
+        raise CodeToleranceMiss("%s: %d of %d mismatches are not within 1 fp32 ulp of a rounding boundary" % (
+            name, st.mismatches - st.near_boundary, st.mismatches))
 
 
 def bf16_f64(bits: np.ndarray) -> np.ndarray:
@@ -135,12 +178,16 @@ class CaseReport:
     xq_near_boundary: int = 0
     hq_mismatch: int = 0
     hq_n: int = 0
+    hq_t_max: float = 0.0
     y_max_rel: float = 0.0
     y_min_cos: float = 1.0
     z_cos: float = 1.0
     z_dist: float = 0.0
     z_dist_natural: float = 0.0
+    natural: dict = field(default_factory=dict)
     z_max_rel: float = 0.0
+    p10_cos_gpu: float = 1.0
+    p10_cos_oracle: float = 1.0
     cal_max_rel: float = 0.0
     cal_tf_max_rel: float = 0.0
     saturated_codes: int = 0
@@ -157,6 +204,7 @@ def run_case(cfg: FFNConfig, rows: Optional[Sequence[int]] = None, cal_rows: Opt
     t0 = time.time()
     rep = CaseReport(cfg.name)
     M, H, I, L, act = cfg.M, cfg.H, cfg.I, cfg.L, cfg.act
+    rows_arg = rows
     rows = np.arange(M) if rows is None else np.asarray(sorted(rows))
     r0, y0 = datagen.eval_inputs(cfg)
     cal = datagen.calib_batches(cfg, nbatch)
@@ -173,6 +221,17 @@ def run_case(cfg: FFNConfig, rows: Optional[Sequence[int]] = None, cal_rows: Opt
         mods = {}
         norm_fuse = bool(flags & _abi.FRT_FLAG_NORM_FUSE)
         ada = bool(flags & _abi.FRT_FLAG_ADA_NORM)
+        # quantised weights kept for the HQ mismatch analysis when they are
+        # small; otherwise a layer is regenerated (seeded) if it has any
+        keep_weights = 3 * I * H * L <= (1 << 31)
+        kept_lw = {}
+
+        def layer_lw(l):
+            if l in kept_lw:
+                return kept_lw[l]
+            wg, wu, wd, wn = datagen.layer_weights(cfg, l)
+            mod = datagen.modulation(cfg, l) if ada else None
+            return oracle.LayerWeights.quantize(wg, wu, wd, wn, norm_fuse=norm_fuse, mod=mod)
 
         def provider(l):
             def get():
@@ -192,15 +251,26 @@ def run_case(cfg: FFNConfig, rows: Optional[Sequence[int]] = None, cal_rows: Opt
                 weight_scales.append((lw.s_g, lw.s_u, lw.s_d))
                 norm_w[l] = lw.w_norm
                 mods[l] = lw.mod
+                if keep_weights:
+                    kept_lw[l] = lw
                 if L > 4 and (l % 4 == 3 or l == L - 1):
                     log("[case %s] layers 0..%d quantised and compared (%.1fs)" % (cfg.name, l, time.time() - t0))
                 return lw
             return get
 
-        nat = {"r": r0[rows], "y": None if y0 is None else y0[rows]}
+        # the valid fp32 orders' chains: from the stored record for the
+        # large named workloads, else stepped here beside the oracle
+        stored = stored_natural_drift(cfg, None if rows_arg is None else rows, cal_rows)
+        nat = None if stored is not None else _natural.NaturalChains(r0[rows], None if y0 is None else y0[rows])
+
+        # P-10: the same chain with unquantised fp32 activations (the
+        # oracle's measurement-mode block) from the same input
+        unq = {"r": r0[rows], "y": None if y0 is None else y0[rows]}
 
         def natural_step(li, lw, s_x, s_h):
-            nat["r"], nat["y"] = _natural.block_fp32_sums(nat["r"], nat["y"], lw, act, cfg.eps, s_x, s_h)
+            if nat is not None:
+                nat.step(lw, act, cfg.eps, s_x, s_h)
+            unq["r"], unq["y"], _, _ = oracle.block_measure(unq["r"], unq["y"], lw, act, cfg.eps)
 
         orc = oracle.calibrate_and_run((provider(l) for l in range(L)), act, cfg.eps,
                                        r0[rows], None if y0 is None else y0[rows], cal,
@@ -255,15 +325,22 @@ def run_case(cfg: FFNConfig, rows: Optional[Sequence[int]] = None, cal_rows: Opt
                 assert not np.any((codes & 0x7F) == 0x7F), "NaN code in layer %d" % l
                 rep.saturated_codes += int(np.count_nonzero((codes & 0x7F) == 0x7E))
         z_ref = oracle.final_hidden(orc.r[L], orc.y[L])
-        z_nat = oracle.final_hidden(nat["r"], nat["y"])
         rep.z_max_rel, rep.z_cos = y_metrics(z_graph[rows], z_ref)
         rep.z_dist = _natural.cos_distance(z_graph[rows], z_ref)
-        rep.z_dist_natural = _natural.cos_distance(z_nat, z_ref)
-        log("[case %s] graph == eager; Z cos %.6f max rel %.3g; drift %.3g vs natural %.3g" % (
-            cfg.name, rep.z_cos, rep.z_max_rel, rep.z_dist, rep.z_dist_natural))
+        rep.natural = stored if stored is not None else nat.distances(z_ref)
+        rep.z_dist_natural = max(rep.natural.values())
+        z_unq = oracle.final_hidden(unq["r"], unq["y"])
+        _, rep.p10_cos_gpu = y_metrics(z_graph[rows], z_unq)
+        _, rep.p10_cos_oracle = y_metrics(z_ref, z_unq)
+        log("[case %s] P-10 (FP8 chain vs unquantised activations): Z cosine GPU %.6f, oracle %.6f" % (
+            cfg.name, rep.p10_cos_gpu, rep.p10_cos_oracle))
+        log("[case %s] graph == eager; Z cos %.6f max rel %.3g; drift %.3g, valid fp32 orders %s%s" % (
+            cfg.name, rep.z_cos, rep.z_max_rel, rep.z_dist,
+            " ".join("%s %.3g" % kv for kv in sorted(rep.natural.items())), " (stored)" if stored else ""))
         if gate_drift:
-            assert rep.z_dist <= DRIFT_FACTOR * rep.z_dist_natural + DRIFT_FLOOR, \
-                "free-running drift %.3g > %g x natural %.3g" % (rep.z_dist, DRIFT_FACTOR, rep.z_dist_natural)
+            assert rep.z_cos >= MIN_COS or rep.z_dist <= DRIFT_FACTOR * rep.z_dist_natural + DRIFT_FLOOR, \
+                "free-running Z cosine %.6f < %g and drift %.3g > %g x the valid orders' largest %.3g" % (
+                    rep.z_cos, MIN_COS, rep.z_dist, DRIFT_FACTOR, rep.z_dist_natural)
 
         # teacher-forced per-block checks
         idx = torch.as_tensor(rows, device=plan.device)
@@ -288,10 +365,20 @@ def run_case(cfg: FFNConfig, rows: Optional[Sequence[int]] = None, cal_rows: Opt
             _, x_pre, _ = oracle.add_rmsnorm_quant(orc.r[l], orc.y[l], norm_w[l], cfg.eps, 1.0, mod=mods[l])
             inv_x = np.float32(np.float32(1.0) / np.float32(orc.s_x[l]))
             xs = code_stats(xq_g, orc.xq[l], (x_pre * inv_x).astype(np.float32))
-            check_codes("layer %d XQ" % l, xs)
+            check_codes("layer %d XQ" % l, xs, boundary_rule=True)
             hs = code_stats(hq_g, orc.hq[l])
+            if hs.mismatches:
+                nh, tmax = _hq_explain.explain(orc.xq[l], hq_g, orc.hq[l], layer_lw(l), act,
+                                               orc.s_x[l], orc.s_h[l])
+                rep.hq_t_max = max(rep.hq_t_max, tmax)
+                log("[case %s] layer %d HQ: %d mismatches, largest accumulation error needed %.3g units"
+                    % (cfg.name, l, nh, tmax))
             if gate_hq:
                 check_codes("layer %d HQ" % l, hs)
+                if hs.mismatches and rep.hq_t_max > _hq_explain.T_MAX_EXPLAINED:
+                    raise CodeToleranceMiss(
+                        "layer %d HQ: a mismatch needs an accumulation error of %.3g units (> %g): "
+                        "not explained by fp32 accumulation" % (l, rep.hq_t_max, _hq_explain.T_MAX_EXPLAINED))
             mr, cs = check_y("layer %d Y" % l, y_g, orc.y[l + 1])
             rep.layers_checked.append(l)
             rep.xq_mismatch += xs.mismatches
@@ -301,10 +388,51 @@ def run_case(cfg: FFNConfig, rows: Optional[Sequence[int]] = None, cal_rows: Opt
             rep.hq_n += hs.n
             rep.y_max_rel = max(rep.y_max_rel, mr)
             rep.y_min_cos = min(rep.y_min_cos, cs)
-        log("[case %s] per-block: XQ %d/%d (near boundary %d), HQ %d/%d, Y max rel %.3g min cos %.6f"
+        log("[case %s] per-block: XQ %d/%d (near boundary %d), HQ %d/%d (largest error needed %.3g units), "
+            "Y max rel %.3g min cos %.6f"
             % (cfg.name, rep.xq_mismatch, rep.xq_n, rep.xq_near_boundary, rep.hq_mismatch, rep.hq_n,
-               rep.y_max_rel, rep.y_min_cos))
+               rep.hq_t_max, rep.y_max_rel, rep.y_min_cos))
     finally:
         plan.close()
     rep.seconds = time.time() - t0
     return rep
+
+
+def run_permutation(cfg: FFNConfig, flags: int = 0, seed: int = 7, layers: Optional[int] = None) -> int:
+    """Row independence on the GPU (one plan, one kernel path): the chain run
+    on the evaluation input with its rows permuted must give every slot
+    (R, XQ, HQ, Y per layer, and Z) permuted the same way, bit for bit.
+    Scales come from the GPU's own calibration pass (any fixed scales do).
+    Returns the number of layers compared."""
+    M, H, I = cfg.M, cfg.H, cfg.I
+    L = cfg.L if layers is None else min(cfg.L, layers)
+    r0, y0 = datagen.eval_inputs(cfg)
+    perm = np.random.default_rng(seed).permutation(M)
+    log("[perm %s] M=%d H=%d I=%d L=%d flags=%d" % (cfg.name, M, H, I, L, flags))
+    plan = FFNPlan(M, H, I, L, cfg.act, cfg.eps, flags=flags)
+    try:
+        for l in range(L):
+            plan.load_layer(l, *datagen.layer_weights(cfg, l))
+        plan.calibrate(datagen.calib_batches(cfg, 1))
+
+        def run(r, y):
+            plan.set_inputs(r, y)
+            plan.forward()
+            plan.sync()
+            out = []
+            for l in range(L):
+                out.append((to_np_u16(plan.r_slot(l + 1)), to_np_u8(plan.xq_slot(l)), to_np_u8(plan.hq_slot(l)),
+                            to_np_u16(plan.y_slot(l + 1))))
+            return out, to_np_u16(plan.z())
+
+        base, z = run(r0, y0)
+        prm, zp = run(np.ascontiguousarray(r0[perm]), None if y0 is None else np.ascontiguousarray(y0[perm]))
+        for l in range(L):
+            for name, a, b in zip(("R", "XQ", "HQ", "Y"), base[l], prm[l]):
+                nb = int(np.count_nonzero(a[perm] != b))
+                assert nb == 0, "layer %d %s: %d elements differ after the row permutation" % (l, name, nb)
+        assert np.array_equal(z[perm], zp), "Z differs after the row permutation"
+    finally:
+        plan.close()
+    log("[perm %s] %d layers: every slot permuted bit for bit" % (cfg.name, L))
+    return L

@@ -37,6 +37,7 @@ def test_library_is_in_tree():
 @pytest.mark.parametrize("bad", [
     dict(M=0), dict(L=0), dict(H=100), dict(I=200), dict(H=16384 + 128), dict(act=3),
     dict(eps=0.0), dict(eps=float("nan")), dict(flags=64), dict(flags=77), dict(flags=16 | 8), dict(flags=16 | 2),
+    dict(M=1 << 20, H=4096, I=1024),
     dict(flags=32, H=384), dict(flags=32, I=1536 + 128), dict(flags=32 | 1), dict(flags=32 | 4),
     dict(flags=32 | 2), dict(flags=32 | 8), dict(device=-1)])
 def test_bad_descriptors_rejected(bad):
@@ -68,7 +69,7 @@ def test_plan_create_rejects_null_workspace():
 @pytest.mark.parametrize("bad", [
     dict(M=0), dict(H=100), dict(H=16384 + 128), dict(nq=0), dict(nkv=0), dict(hd=48), dict(hd=16), dict(hd=544),
     dict(max_pos=0), dict(eps=0.0), dict(rope_base=1.0), dict(rope_base=float("inf")), dict(flags=1), dict(flags=2),
-    dict(flags=8 | 16), dict(device=-1)])
+    dict(flags=8 | 16), dict(device=-1), dict(M=1 << 20, H=4096)])
 def test_bad_qkv_descriptors_rejected(bad):
     kw = dict(M=4, H=256, nq=2, nkv=1, hd=64, max_pos=32, eps=1e-6, rope_base=1e4, device=0, flags=0)
     kw.update(bad)

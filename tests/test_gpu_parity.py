@@ -12,7 +12,8 @@ import pytest
 from realtime_transformer_amd import _abi
 from realtime_transformer_amd.configs import CONFIGS, FFNConfig, ACT_GEGLU_TANH, ACT_SWIGLU, ACT_GELU_TANH
 
-from _ffn_case import run_case, log
+from _ffn_case import run_case, run_permutation, log, CodeToleranceMiss
+from _samples import rows_for
 
 pytestmark = pytest.mark.gpu
 
@@ -53,18 +54,23 @@ def test_small_shapes_fp8_down(spec):
     log(str(rep))
 
 
-@pytest.mark.parametrize("spec", [SMALL[4], SMALL[5], SMALL[6]],
+@pytest.mark.xfail(strict=True, raises=CodeToleranceMiss,
+                   reason="FRT_FLAG_FP8_MFMA_GATEUP misses the HQ byte tolerance: gfx950's FP8 matrix "
+                          "instructions drop product bits below the largest product of each instruction, "
+                          "which flips 1.2-1.4e-3 of the re-quantised HQ codes (bound 1e-4) and, where h "
+                          "cancels toward the subnormal codes, can move a code by two steps")
+@pytest.mark.parametrize("spec", [SMALL[4], SMALL[5], SMALL[10]],
                          ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
 def test_small_shapes_fp8_gemms(spec):
-    # both GEMMs (M > 16) on the FP8 matrix cores.  Their products are
-    # aligned inside an instruction and lose low bits, so the re-quantised HQ
-    # codes flip near rounding boundaries about 1e-3 of the time (above the
-    # byte tolerance): HQ is reported, the per-block bf16 output is gated.
+    # both GEMMs on the FP8 matrix cores (the flag applies to the GEMMs of
+    # M > 64: the prefill GEMM and the LDS-staged GEMM below it; the GEMVs
+    # stay on the f16 cores), held to the full byte tolerance (rate,
+    # adjacency, fp32-explicable mismatches): expected to miss it, so the
+    # mode stays opt-in
     idx, M, H, I, L, act = spec
     cfg = FFNConfig(idx, "small_fp8_%d" % idx, M, H, I, L, act)
-    rep = run_case(cfg, flags=5, gate_drift=False, gate_hq=False)
+    rep = run_case(cfg, flags=5, gate_drift=False)
     log(str(rep))
-    assert rep.hq_mismatch / rep.hq_n < 1e-2
 
 
 @pytest.mark.parametrize("spec", [SMALL[4], SMALL[5]], ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
@@ -202,10 +208,19 @@ def test_action_expert_m50_chain():
 @pytest.mark.timeout(900)
 def test_vlm_prefix_m788_full_size():
     cfg = CONFIGS[3]
-    rng = np.random.default_rng(31)
-    rows = sorted(set(range(768, 788)) | set(rng.choice(768, 44, replace=False).tolist()))
-    cal_rows = sorted(set(range(772, 780)) | set(rng.choice(768, 8, replace=False).tolist()))
+    rows, cal_rows = rows_for(3)
     rep = run_case(cfg, rows=rows, cal_rows=cal_rows)
+    log(str(rep))
+
+
+@pytest.mark.timeout(900)
+def test_vlm_prefix_m788_full_size_fp8_down():
+    # the opt-in FP8-core down projection at full size: every per-block
+    # tolerance holds; the free-running drift is reported (it exceeds the
+    # chain rule, which is why the mode is not the default)
+    cfg = CONFIGS[3]
+    rows, cal_rows = rows_for(3)
+    rep = run_case(cfg, rows=rows, cal_rows=cal_rows, flags=_abi.FRT_FLAG_FP8_MFMA_DOWN, gate_drift=False)
     log(str(rep))
 
 
@@ -218,8 +233,22 @@ def test_llm_decode_m1_full_size():
 @pytest.mark.timeout(900)
 def test_dit_video_m4096_full_size():
     cfg = CONFIGS[5]
-    rng = np.random.default_rng(53)
-    rows = sorted(rng.choice(cfg.M, 48, replace=False).tolist())
-    cal_rows = sorted(rng.choice(cfg.M, 12, replace=False).tolist())
+    rows, cal_rows = rows_for(5)
     rep = run_case(cfg, rows=rows, cal_rows=cal_rows)
     log(str(rep))
+
+
+@pytest.mark.parametrize("spec", [SMALL[1], (112, 50, 1024, 4096, 2, ACT_GEGLU_TANH), SMALL[5], SMALL[4]],
+                         ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
+def test_row_permutation(spec):
+    # rows are independent under static per-tensor scales: permuting the
+    # input rows permutes every output bit for bit (GEMV, multi-tile GEMV,
+    # and prefill GEMM paths with ragged tiles)
+    idx, M, H, I, L, act = spec
+    run_permutation(FFNConfig(idx, "perm_%d" % idx, M, H, I, L, act))
+
+
+@pytest.mark.timeout(600)
+def test_row_permutation_vlm_prefix_m788():
+    # the M=788 workload in its benchmark launch configuration (4 layers)
+    run_permutation(CONFIGS[3], layers=4)
