@@ -260,6 +260,25 @@ frt_status frt_ffn_io_get(const frt_plan *plan, frt_ffn_io *out);
 frt_status frt_ffn_forward_range(frt_plan *plan, int32_t layer_begin, int32_t layer_end,
                                  void *stream);
 
+/* For callers that cannot allocate device memory at all (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid it), beyond the
+ * plan's workspace they already own: frt_ffn_forward_range with the
+ * forward's scratch -- the down projection's split-K fp32 partial sums and
+ * the decode norm's fp64 slice sums of squares -- in the library's static
+ * device array (16 MiB per GPU, held until the process ends) instead of the
+ * workspace's scratch region.  Same kernels, launch configuration and
+ * results as frt_ffn_forward_range, bit for bit.  Allocates nothing and calls
+ * no allocating routine; the first call on a device looks up the array's
+ * address there.  Nothing in the array needs to start at zero (every call
+ * writes what it reads).  FRT_ERR_UNSUPPORTED (with the sizes in
+ * frt_last_error) when the plan needs more scratch than the array holds:
+ * 4*M*H per split-K partial plus 8*M*ceil(H/512) of slice sums (the five
+ * FFN workloads of the benchmark fit).  All calls on one GPU share its
+ * array: calls that overlap in time on one GPU (other streams, other plans,
+ * other host threads) race; serialise them. */
+frt_status frt_ffn_forward_range_static_scratch(frt_plan *plan, int32_t layer_begin, int32_t layer_end,
+                                                void *stream);
+
 /* Eager forward of the whole chain: frt_ffn_forward_range(plan, 0, L). */
 frt_status frt_ffn_forward(frt_plan *plan, void *stream);
 

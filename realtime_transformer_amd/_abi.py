@@ -41,7 +41,7 @@ EXPORTED = [
     "frt_export_weight_codes", "frt_calibrate", "frt_get_scales", "frt_set_act_scales",
     "frt_ffn_io_get", "frt_ffn_forward_range", "frt_ffn_forward", "frt_graph_capture",
     "frt_graph_replay", "frt_ffn_forward_profiled", "frt_ffn_time_kernel", "frt_e4m3_encode_f32",
-    "frt_last_error", "frt_export_mxfp4_weights", "frt_set_awq",
+    "frt_last_error", "frt_export_mxfp4_weights", "frt_set_awq", "frt_ffn_forward_range_static_scratch",
     # attention input (include/frt_qkv.h)
     "frt_qkv_workspace_size", "frt_qkv_plan_create", "frt_qkv_plan_destroy", "frt_qkv_quant_weights",
     "frt_qkv_export_weight_codes", "frt_qkv_calibrate", "frt_qkv_get_scales", "frt_qkv_set_act_scale",
@@ -110,6 +110,7 @@ def load(build_if_missing: bool = True):
         "frt_set_act_scales": [vp, ctypes.POINTER(ctypes.c_float)],
         "frt_ffn_io_get": [vp, ctypes.POINTER(frt_ffn_io)],
         "frt_ffn_forward_range": [vp, i32, i32, vp],
+        "frt_ffn_forward_range_static_scratch": [vp, i32, i32, vp],
         "frt_ffn_forward": [vp, vp],
         "frt_graph_capture": [vp, vp],
         "frt_graph_replay": [vp, vp],
@@ -208,6 +209,10 @@ def frt_ffn_io_get(plan: int) -> frt_ffn_io:
 
 def frt_ffn_forward_range(plan: int, layer_begin: int, layer_end: int, stream: int) -> None:
     _check(load().frt_ffn_forward_range(plan, layer_begin, layer_end, stream))
+
+
+def frt_ffn_forward_range_static_scratch(plan: int, layer_begin: int, layer_end: int, stream: int) -> None:
+    _check(load().frt_ffn_forward_range_static_scratch(plan, layer_begin, layer_end, stream))
 
 
 def frt_ffn_forward(plan: int, stream: int) -> None:

@@ -19,6 +19,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -464,8 +465,16 @@ struct frt_plan {
   const uint16_t* mod(int l) const {
     return ada() ? reinterpret_cast<const uint16_t*>(ws + lo.mod) + (size_t)l * 2 * d.H : nullptr;
   }
-  float* part() const { return reinterpret_cast<float*>(ws + lo.part); }
-  double* sqp() const { return reinterpret_cast<double*>(ws + lo.sqp); }
+  // the forward's scratch (split-K partials, slice sums): in the workspace,
+  // or, during frt_ffn_forward_range_static_scratch, in the library's static
+  // device array (scratch_base set for the duration of that call)
+  uint8_t* scratch_base = nullptr;
+  size_t scratch_part_off() const { return align256(lo.sqp_bytes); }
+  size_t scratch_bytes() const { return scratch_part_off() + lo.part_bytes; }
+  float* part() const {
+    return reinterpret_cast<float*>(scratch_base ? scratch_base + scratch_part_off() : ws + lo.part);
+  }
+  double* sqp() const { return reinterpret_cast<double*>(scratch_base ? scratch_base : ws + lo.sqp); }
   uint32_t* cnt(int region) const {
     return reinterpret_cast<uint32_t*>(ws + lo.cnt) + (size_t)region * lo.cnt_words;
   }
@@ -1002,6 +1011,63 @@ static frt_status forward_range(frt_plan* p, int lb, int le, hipStream_t s,
     KERNEL_CHECK(launch_residual_add(p->r(le), p->y(le), nullptr, p->mh(), s, p->part(), p->lo.split_dn, a_last),
                  "finalize_y");
   return FRT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// The forward with its scratch in a static device array, for callers that
+// cannot allocate (the workspace's scratch region is not touched).
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+// One copy per GPU the library runs on, held until the process ends.  In
+// host code `scratch` names a host-side stand-in, never the device memory:
+// kernels get the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on device `dev` (which must be current),
+// looked up on the first call per device and kept.
+frt_status static_scratch(int dev, uint8_t** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(FRT_ERR_UNSUPPORTED, "static scratch: device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(FRT_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<uint8_t*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return FRT_OK;
+}
+
+}  // namespace
+
+frt_status frt_ffn_forward_range_static_scratch(frt_plan* p, int32_t layer_begin, int32_t layer_end, void* stream) {
+  if (!p) return fail(FRT_ERR_INVALID_ARG, "frt_ffn_forward_range_static_scratch: plan is NULL");
+  if (layer_begin < 0 || layer_end > p->d.L || layer_begin >= layer_end)
+    return fail(FRT_ERR_INVALID_ARG, "frt_ffn_forward_range_static_scratch: bad range [%d, %d)", layer_begin,
+                layer_end);
+  if (p->scratch_bytes() > kStaticScratchBytes)
+    return fail(FRT_ERR_UNSUPPORTED,
+                "frt_ffn_forward_range_static_scratch: the plan needs %zu bytes of scratch, the static array "
+                "holds %zu (use frt_ffn_forward_range)",
+                p->scratch_bytes(), kStaticScratchBytes);
+  for (int l = layer_begin; l < layer_end; ++l)
+    if (!p->w_set[l]) return fail(FRT_ERR_STATE, "frt_ffn_forward_range_static_scratch: weights of layer %d not set", l);
+  if (!p->act_scales_set()) return fail(FRT_ERR_STATE, "frt_ffn_forward_range_static_scratch: activation scales not set");
+  DeviceGuard g(p->d.device);
+  HIP_CHECK(g.err);
+  uint8_t* base = nullptr;
+  frt_status st = static_scratch(p->d.device, &base);
+  if (st != FRT_OK) return st;
+  p->scratch_base = base;
+  st = forward_range(p, layer_begin, layer_end, static_cast<hipStream_t>(stream));
+  p->scratch_base = nullptr;
+  return st;
 }
 
 frt_status frt_ffn_forward_range(frt_plan* p, int32_t layer_begin, int32_t layer_end, void* stream) {
