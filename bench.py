@@ -365,6 +365,41 @@ def measure_chain(cfg, steps, warmup, flags=0, calibrate=True, iso=50):
     return rec
 
 
+def graph_launch_floor(n=200):
+    """The cost of replaying a HIP graph of one trivial kernel (a one-element
+    add captured with torch's graph API, which calls hipGraphLaunch): host
+    time of the launch call and isolated replay time between two events.
+    The floor under any small chain's replay latency on this host."""
+    import torch
+    x = torch.zeros(1, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        x.add_(1)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        x.add_(1)
+    torch.cuda.synchronize()
+    for _ in range(20):
+        g.replay()
+    torch.cuda.synchronize()
+    host, dev = [], []
+    for _ in range(n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(torch.cuda.current_stream())
+        t0 = time.perf_counter()
+        g.replay()
+        host.append(time.perf_counter() - t0)
+        b.record(torch.cuda.current_stream())
+        b.synchronize()
+        dev.append(a.elapsed_time(b))
+    return {"kernels": 1, "host_launch_us_median": round(float(np.median(host)) * 1e6, 2),
+            "isolated_replay_us_median": round(float(np.median(dev)) * 1e3, 2),
+            "isolated_replay_us_p10": round(float(np.percentile(dev, 10)) * 1e3, 2),
+            "isolated_replay_us_p90": round(float(np.percentile(dev, 90)) * 1e3, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -480,6 +515,8 @@ def main():
                 modes[mname]["accuracy"] = acc
             per[name]["fp8_matrix_core_modes"] = modes
     out["configs"] = per
+    out["graph_launch_floor"] = graph_launch_floor()
+    log("[bench] one-kernel graph: %s" % out["graph_launch_floor"])
     tgt = {}
     if "llm_decode_m1" in per:
         f = per["llm_decode_m1"]["chain_hbm_frac"]
