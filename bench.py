@@ -409,6 +409,7 @@ def main():
     ap.add_argument("--configs", default="all",
                     help="comma-separated workloads timed beside it ('all' = the five, 'none')")
     ap.add_argument("--cpu-seconds", type=float, default=5.0, help="CPU-baseline budget per workload")
+    ap.add_argument("--flags", type=int, default=0, help="plan flags (FRT_FLAG_*) of the headline workload")
     ap.add_argument("--no-fp8-modes", action="store_true",
                     help="skip timing the opt-in FP8 matrix-core gate/up mode of the M=788 workload")
     ap.add_argument("--no-norm-variants", action="store_true",
@@ -449,7 +450,8 @@ def main():
 
     cal = not args.no_calibrate
     cfg = BY_NAME[args.workload]
-    head = measure_chain(cfg, args.steps, args.warmup, calibrate=cal, iso=max(10, min(100, args.steps)))
+    head = measure_chain(cfg, args.steps, args.warmup, flags=args.flags, calibrate=cal,
+                         iso=max(10, min(100, args.steps)))
     # dominant kernel of the headline workload: HIP events around every
     # layer's launch of it, back to back on the plan's stream
     gu_us = head["kernels_us"]["gateup"]
@@ -482,7 +484,7 @@ def main():
         "vs_baseline": None,
         "dtype": "e4m3 weights/activations, bf16 residual, fp32 accumulate",
         "data": "synthetic (seeded N(0,1) residual, N(0,0.02) weights, calibrated static scales)",
-        "config": dict({"workload": cfg.name}, **head),
+        "config": dict({"workload": cfg.name, "flags": args.flags}, **head),
         "roofline": roof,
     }
 

@@ -90,7 +90,8 @@ __device__ __forceinline__ v4f mfma_step(const uint32_t a[8], const uint32_t b[8
 // One workgroup of W waves owns 16 output columns (for the gated forms: 16
 // intermediate columns, i.e. the gate group and the up group of the packed
 // matrix).  Wave w streams K blocks [w*KB/W, (w+1)*KB/W) of those rows with
-// nontemporal 16-byte loads, two K blocks in flight per step; the W partial
+// nontemporal 16-byte loads (the decode gate/up and down kernels keep the
+// next K block's loads in flight while a block computes); the W partial
 // accumulators meet in LDS and wave 0 adds them in wave order (fixed order:
 // the result does not depend on timing) and runs the epilogue.  Keeping the
 // split inside the workgroup needs no cross-workgroup handshake, so no
@@ -199,7 +200,12 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup(const uint8_t* __restric
 // serves in order.
 constexpr int kNqChunks = 2;  // 8-element chunks per lane whose loads are issued together
 
-template <int ACT, int W>
+// The weight stream runs in steps of NB K blocks.  PIPE: two register sets
+// alternate, and the loads of step i + 1 are issued before the MFMAs of step
+// i, so every wave keeps a step in flight while it computes (the register
+// cost of 2 NB blocks); otherwise each step's loads are issued right before
+// its MFMAs.
+template <int ACT, int W, int NB, bool PIPE>
 __global__ __launch_bounds__(W * 64) void k_gemv_gateup_nq(const NormQ nq, const uint8_t* __restrict__ w,
                                                            uint8_t* __restrict__ hq, int M, int K, int I,
                                                            float alpha_g, float alpha_u, float inv_h) {
@@ -223,17 +229,21 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup_nq(const NormQ nq, const
   nqw.load(nq, 0, lane);
   __builtin_amdgcn_sched_barrier(0);
 
-  // (2) the first step's weights (a one-block range loads its block twice)
-  uint32_t u0[8], u1[8], g0[8], g1[8];
-  {
-    const int kb_b = kb0 + 1 < kb1 ? kb0 + 1 : kb0;
-    load_w32(wu, kb0, u0);
-    load_w32(wu, kb_b, u1);
-    if (GATED) {
-      load_w32(wg, kb0, g0);
-      load_w32(wg, kb_b, g1);
+  // (2) the first step's weights: blocks kb0 + i0 .. + NB - 1 (indices
+  // clamped to the range, so no load of a step sits behind a branch; a
+  // clamped block is loaded, not used)
+  const int nblk = kb1 - kb0;
+  typedef uint32_t Frag[NB][8];
+  Frag uA, gA, uB, gB;
+  auto load_step = [&](Frag& uu, Frag& gg, int i0) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int k = kb0 + (i0 + j < nblk ? i0 + j : nblk - 1);
+      load_w32(wu, k, uu[j]);
+      if (GATED) load_w32(wg, k, gg[j]);
     }
-  }
+  };
+  load_step(uA, gA, 0);
   __builtin_amdgcn_sched_barrier(0);
 
   // (3) 1/rms of row `lane` (lanes < M), then the codes of this wave's range
@@ -257,33 +267,56 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup_nq(const NormQ nq, const
     unpack8(a, b, o);
   };
   v4f accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
-  int kb = kb0;
-  for (; kb + 1 < kb1; kb += 2) {
-    uint32_t x0[8], x1[8];
-    if (kb != kb0) {
-      load_w32(wu, kb, u0);
-      load_w32(wu, kb + 1, u1);
-      if (GATED) {
-        load_w32(wg, kb, g0);
-        load_w32(wg, kb + 1, g1);
+  auto mma_step = [&](Frag& uu, Frag& gg, int i0) {
+    if (PIPE) {
+      // the step's weights count as written here: the compiler may not
+      // convert them earlier, which would wait for them (and for every load
+      // issued after them) before the previous step's MFMAs
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          asm volatile("" : "+v"(uu[j][t]));
+          if (GATED) asm volatile("" : "+v"(gg[j][t]));
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (i0 + j < nblk) {  // wave-uniform
+        uint32_t x0[8];
+        lds_x32(kb0 + i0 + j, x0);
+        accu = mfma_f16_x4(x0, uu[j], accu);
+        if (GATED) accg = mfma_f16_x4(x0, gg[j], accg);
       }
     }
-    lds_x32(kb, x0);
-    lds_x32(kb + 1, x1);
-    accu = mfma_f16_x4(x0, u0, accu);
-    if (GATED) accg = mfma_f16_x4(x0, g0, accg);
-    accu = mfma_f16_x4(x1, u1, accu);
-    if (GATED) accg = mfma_f16_x4(x1, g1, accg);
-  }
-  if (kb < kb1) {
-    uint32_t x0[8];
-    if (kb != kb0) {
-      load_w32(wu, kb, u0);
-      if (GATED) load_w32(wg, kb, g0);
+  };
+  if (PIPE) {
+    // Both loads of an iteration are unconditional (a load behind a branch
+    // makes the join wait for every load in flight); the last one or two
+    // steps are peeled.  The scheduling barriers keep the compiler from
+    // sinking the loads below the MFMAs of the step before them.
+    int i = 0;
+    for (; i + 2 * NB < nblk; i += 2 * NB) {
+      load_step(uB, gB, i + NB);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_step(uA, gA, i);
+      load_step(uA, gA, i + 2 * NB);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_step(uB, gB, i + NB);
     }
-    lds_x32(kb, x0);
-    accu = mfma_f16_x4(x0, u0, accu);
-    if (GATED) accg = mfma_f16_x4(x0, g0, accg);
+    if (i + NB < nblk) {
+      load_step(uB, gB, i + NB);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_step(uA, gA, i);
+      mma_step(uB, gB, i + NB);
+    } else {
+      mma_step(uA, gA, i);
+    }
+  } else {
+    for (int i = 0; i < nblk; i += NB) {
+      if (i != 0) load_step(uA, gA, i);
+      mma_step(uA, gA, i);
+    }
   }
   if (W > 1) {
     red[wave][0][lane] = accu;
@@ -527,7 +560,7 @@ __global__ __launch_bounds__(W * 64, 4) void k_gemv_gateup_fused(const FusedArgs
 // accumulator columns are discarded), doubling the workgroups so that every
 // CU gets the same share when the group count is small (H/16 = 320 for
 // H = 5120 on 256 CUs).  Half-group loads still read whole 128-byte lines.
-template <int W, bool FP8, int COLS>
+template <int W, bool FP8, int COLS, int NB, bool PIPE>
 __global__ __launch_bounds__(W * 64) void k_gemv_down(const uint8_t* __restrict__ hq,
                                                       const uint8_t* __restrict__ w,
                                                       uint16_t* __restrict__ y, float* __restrict__ part,
@@ -546,39 +579,80 @@ __global__ __launch_bounds__(W * 64) void k_gemv_down(const uint8_t* __restrict_
   const bool my_col = (COLS == 16) || ((row >> 3) == half);
   const uint8_t* wp = w + (size_t)p * KB * 2048 + lane * 16;
   const uint8_t* xr = hq + (size_t)(has_row ? row : 0) * K + q * 32;
-  const uint32_t zero8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 
+  // steps of NB K blocks, each step's weight and activation loads issued
+  // together (block indices clamped to the range: a clamped block is loaded,
+  // not used); PIPE as in k_gemv_gateup_nq (two register sets, the next
+  // step's loads in flight while the current one computes).  Blocks
+  // alternate between two accumulators by their index's parity.
+  const int nblk = kb1 - kb0;
+  typedef uint32_t Frag[NB][8];
+  Frag xA, wA, xB, wB;
+  auto load_step = [&](Frag& xs, Frag& ws, int i0) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int k = kb0 + (i0 + j < nblk ? i0 + j : nblk - 1);
+      if (my_col) {
+        load_w32(wp, k, ws[j]);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) ws[j][t] = 0u;
+      }
+    }
+    // every lane loads its activations (a load behind a lane branch would
+    // make the join wait for all loads in flight): lanes of rows past M read
+    // row 0's bytes, which reach only output rows past M, never stored
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int k = kb0 + (i0 + j < nblk ? i0 + j : nblk - 1);
+      unpack8(ld16(xr + k * 128), ld16(xr + k * 128 + 16), xs[j]);
+    }
+  };
   v4f acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-  int kb = kb0;
-  for (; kb + 3 < kb1; kb += 4) {
-    uint32_t x0[8], x1[8], w0[8], w1[8], x2[8], x3[8], w2[8], w3[8];
-    if (my_col) {
-      load_w32(wp, kb, w0);
-      load_w32(wp, kb + 1, w1);
-      load_w32(wp, kb + 2, w2);
-      load_w32(wp, kb + 3, w3);
+  auto mma_step = [&](Frag& xs, Frag& ws, int i0) {
+    if (PIPE) {
+      // the step's operands count as written here (as in k_gemv_gateup_nq)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          asm volatile("" : "+v"(xs[j][t]));
+          asm volatile("" : "+v"(ws[j][t]));
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (i0 + j < nblk) {  // wave-uniform
+        if ((i0 + j) & 1) acc1 = mfma_step<FP8>(xs[j], ws[j], acc1);
+        else acc0 = mfma_step<FP8>(xs[j], ws[j], acc0);
+      }
+    }
+  };
+  if (nblk > 0) load_step(xA, wA, 0);
+  if (PIPE && nblk > 0) {
+    // (loop shape as in k_gemv_gateup_nq)
+    int i = 0;
+    for (; i + 2 * NB < nblk; i += 2 * NB) {
+      load_step(xB, wB, i + NB);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_step(xA, wA, i);
+      load_step(xA, wA, i + 2 * NB);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_step(xB, wB, i + NB);
+    }
+    if (i + NB < nblk) {
+      load_step(xB, wB, i + NB);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_step(xA, wA, i);
+      mma_step(xB, wB, i + NB);
     } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w0[i] = w1[i] = w2[i] = w3[i] = zero8[i];
+      mma_step(xA, wA, i);
     }
-    load_x32(xr, has_row, kb, x0);
-    load_x32(xr, has_row, kb + 1, x1);
-    load_x32(xr, has_row, kb + 2, x2);
-    load_x32(xr, has_row, kb + 3, x3);
-    acc0 = mfma_step<FP8>(x0, w0, acc0);
-    acc1 = mfma_step<FP8>(x1, w1, acc1);
-    acc0 = mfma_step<FP8>(x2, w2, acc0);
-    acc1 = mfma_step<FP8>(x3, w3, acc1);
-  }
-  for (; kb < kb1; ++kb) {
-    uint32_t x0[8], w0[8];
-    if (my_col) load_w32(wp, kb, w0);
-    else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w0[i] = 0;
+  } else if (!PIPE) {
+    for (int i = 0; i < nblk; i += NB) {
+      if (i != 0) load_step(xA, wA, i);
+      mma_step(xA, wA, i);
     }
-    load_x32(xr, has_row, kb, x0);
-    acc0 = mfma_step<FP8>(x0, w0, acc0);
   }
   v4f acc = acc0 + acc1;
   if (W > 1) {
@@ -1019,17 +1093,46 @@ __global__ __launch_bounds__(W * 64) void k_gemv_down_mt(const uint8_t* __restri
   }
 }
 
-template <int W>
-static void gemv_gateup_nq_w(int act, const NormQ& nq, const uint8_t* w, uint8_t* hq, int M, int K, int I,
-                             float a_g, float a_u, float inv_h, hipStream_t s) {
+// K blocks per load step of the decode GEMVs and whether the steps are
+// pipelined (FRT_GEMV_NB_GATEUP / FRT_GEMV_NB_DOWN: 1 or 2;
+// FRT_GEMV_PIPE_GATEUP / FRT_GEMV_PIPE_DOWN: 0 or 1).
+static int gemv_nb(const char* env, int dflt) {
+  const char* e = getenv(env);
+  const int v = (e && *e) ? atoi(e) : dflt;
+  return v >= 2 ? 2 : 1;
+}
+static bool gemv_pipe(const char* env, bool dflt) {
+  const char* e = getenv(env);
+  return (e && *e) ? atoi(e) != 0 : dflt;
+}
+
+template <int W, int NB, bool PIPE>
+static void gemv_gateup_nq_wnp(int act, const NormQ& nq, const uint8_t* w, uint8_t* hq, int M, int K, int I,
+                               float a_g, float a_u, float inv_h, hipStream_t s) {
   dim3 grid(I / 16), block(W * 64);
   const size_t lds = (size_t)M * K;
   if (act == GU_GEGLU)
-    hipLaunchKernelGGL((k_gemv_gateup_nq<GU_GEGLU, W>), grid, block, lds, s, nq, w, hq, M, K, I, a_g, a_u, inv_h);
+    hipLaunchKernelGGL((k_gemv_gateup_nq<GU_GEGLU, W, NB, PIPE>), grid, block, lds, s, nq, w, hq, M, K, I, a_g, a_u,
+                       inv_h);
   else if (act == GU_SWIGLU)
-    hipLaunchKernelGGL((k_gemv_gateup_nq<GU_SWIGLU, W>), grid, block, lds, s, nq, w, hq, M, K, I, a_g, a_u, inv_h);
+    hipLaunchKernelGGL((k_gemv_gateup_nq<GU_SWIGLU, W, NB, PIPE>), grid, block, lds, s, nq, w, hq, M, K, I, a_g,
+                       a_u, inv_h);
   else
-    hipLaunchKernelGGL((k_gemv_gateup_nq<GU_GELU, W>), grid, block, lds, s, nq, w, hq, M, K, I, a_g, a_u, inv_h);
+    hipLaunchKernelGGL((k_gemv_gateup_nq<GU_GELU, W, NB, PIPE>), grid, block, lds, s, nq, w, hq, M, K, I, a_g, a_u,
+                       inv_h);
+}
+
+template <int W>
+static void gemv_gateup_nq_w(int act, const NormQ& nq, const uint8_t* w, uint8_t* hq, int M, int K, int I,
+                             float a_g, float a_u, float inv_h, hipStream_t s) {
+  const bool pipe = gemv_pipe("FRT_GEMV_PIPE_GATEUP", true);
+  if (gemv_nb("FRT_GEMV_NB_GATEUP", 1) == 2) {
+    if (pipe) gemv_gateup_nq_wnp<W, 2, true>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
+    else gemv_gateup_nq_wnp<W, 2, false>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
+  } else {
+    if (pipe) gemv_gateup_nq_wnp<W, 1, true>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
+    else gemv_gateup_nq_wnp<W, 1, false>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
+  }
 }
 
 // Whether k_gemv_gateup_nq takes the shape (frt_normq.h).
@@ -1134,19 +1237,33 @@ hipError_t launch_gemv_gateup_fused(int act, const uint16_t* r_prev, const uint1
   return gateup_fused_act<GU_GELU>(W, a, s);
 }
 
+template <bool FP8, int COLS, int NB, bool PIPE>
+static hipError_t gemv_down_tnp(const uint8_t* hq, const uint8_t* w, uint16_t* y, float* part, int M, int K,
+                                int N, int W, int S, float alpha_d, hipStream_t s) {
+  dim3 grid((N / 16) * (16 / COLS), S), block(W * 64);
+#define FRT_DOWN(WV) \
+  hipLaunchKernelGGL((k_gemv_down<WV, FP8, COLS, NB, PIPE>), grid, block, 0, s, hq, w, y, part, M, K, N, alpha_d)
+  switch (W) {
+    case 1: FRT_DOWN(1); break;
+    case 2: FRT_DOWN(2); break;
+    case 4: FRT_DOWN(4); break;
+    case 8: FRT_DOWN(8); break;
+    case 16: FRT_DOWN(16); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef FRT_DOWN
+  return hipGetLastError();
+}
+
 template <bool FP8, int COLS>
 static hipError_t gemv_down_t(const uint8_t* hq, const uint8_t* w, uint16_t* y, float* part, int M, int K,
                               int N, int W, int S, float alpha_d, hipStream_t s) {
-  dim3 grid((N / 16) * (16 / COLS), S), block(W * 64);
-  switch (W) {
-    case 1: hipLaunchKernelGGL((k_gemv_down<1, FP8, COLS>), grid, block, 0, s, hq, w, y, part, M, K, N, alpha_d); break;
-    case 2: hipLaunchKernelGGL((k_gemv_down<2, FP8, COLS>), grid, block, 0, s, hq, w, y, part, M, K, N, alpha_d); break;
-    case 4: hipLaunchKernelGGL((k_gemv_down<4, FP8, COLS>), grid, block, 0, s, hq, w, y, part, M, K, N, alpha_d); break;
-    case 8: hipLaunchKernelGGL((k_gemv_down<8, FP8, COLS>), grid, block, 0, s, hq, w, y, part, M, K, N, alpha_d); break;
-    case 16: hipLaunchKernelGGL((k_gemv_down<16, FP8, COLS>), grid, block, 0, s, hq, w, y, part, M, K, N, alpha_d); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  const bool pipe = gemv_pipe("FRT_GEMV_PIPE_DOWN", true);
+  if (gemv_nb("FRT_GEMV_NB_DOWN", 1) == 2)
+    return pipe ? gemv_down_tnp<FP8, COLS, 2, true>(hq, w, y, part, M, K, N, W, S, alpha_d, s)
+                : gemv_down_tnp<FP8, COLS, 2, false>(hq, w, y, part, M, K, N, W, S, alpha_d, s);
+  return pipe ? gemv_down_tnp<FP8, COLS, 1, true>(hq, w, y, part, M, K, N, W, S, alpha_d, s)
+              : gemv_down_tnp<FP8, COLS, 1, false>(hq, w, y, part, M, K, N, W, S, alpha_d, s);
 }
 
 // Columns per down-GEMV workgroup (FRT_GEMV_DOWN_COLS = 8 or 16).

@@ -131,6 +131,35 @@ def test_small_shapes_many_down_splits(split, spec, monkeypatch):
     log(str(rep))
 
 
+GEMV_VARIANTS = [
+    # decode GEMV launch shapes: K blocks per load step (1 or 2), and the
+    # pipelined stream (the next step's loads in flight during the MFMAs)
+    {"FRT_GEMV_PIPE_GATEUP": "1", "FRT_GEMV_PIPE_DOWN": "1"},
+    {"FRT_GEMV_PIPE_GATEUP": "1", "FRT_GEMV_PIPE_DOWN": "1", "FRT_GEMV_NB_GATEUP": "2", "FRT_GEMV_NB_DOWN": "2"},
+    {"FRT_GEMV_PIPE_GATEUP": "0", "FRT_GEMV_PIPE_DOWN": "0", "FRT_GEMV_NB_GATEUP": "2", "FRT_GEMV_NB_DOWN": "2"},
+    {"FRT_GEMV_PIPE_GATEUP": "0", "FRT_GEMV_PIPE_DOWN": "0"},
+    # few waves, so each streams several K blocks (odd counts peel a step)
+    {"FRT_GEMV_PIPE_GATEUP": "1", "FRT_GEMV_PIPE_DOWN": "1", "FRT_GEMV_WAVES_GATEUP": "2",
+     "FRT_GEMV_WAVES_DOWN": "1"},
+    {"FRT_GEMV_PIPE_GATEUP": "1", "FRT_GEMV_PIPE_DOWN": "1", "FRT_GEMV_NB_GATEUP": "2", "FRT_GEMV_NB_DOWN": "2",
+     "FRT_GEMV_WAVES_GATEUP": "1", "FRT_GEMV_WAVES_DOWN": "2"},
+]
+
+
+@pytest.mark.parametrize("env", GEMV_VARIANTS, ids=lambda e: "_".join("%s%s" % (k[9:], v) for k, v in e.items()))
+@pytest.mark.parametrize("spec", [SMALL[0], SMALL[2], (107, 1, 256, 2048, 2, ACT_SWIGLU),
+                                  (121, 5, 384, 2048, 3, ACT_GEGLU_TANH), (122, 2, 1664, 1152, 2, ACT_GELU_TANH),
+                                  (123, 1, 2048, 2304, 2, ACT_SWIGLU)],
+                         ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
+def test_small_shapes_gemv_launch_variants(spec, env, monkeypatch):
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    idx, M, H, I, L, act = spec
+    cfg = FFNConfig(idx, "small_gemvvar_%d" % idx, M, H, I, L, act)
+    rep = run_case(cfg)
+    log(str(rep))
+
+
 @pytest.mark.parametrize("spec", [(117, 16, 1024, 512, 2, ACT_GEGLU_TANH), (118, 2, 640, 512, 3, ACT_SWIGLU),
                                   (119, 1, 8192, 1024, 2, ACT_GELU_TANH)],
                          ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
