@@ -198,14 +198,16 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup(const uint8_t* __restric
 // quantisation runs and only the activation loads (completed first) are
 // waited for.  LDS writes and reads stay inside one wave, which the LDS
 // serves in order.
-constexpr int kNqChunks = 2;  // 8-element chunks per lane whose loads are issued together
+// NQC: 8-element chunks per lane whose loads are issued together (2, or 3
+// where a wave's range has up to 192 chunks, so that it is quantised after
+// one round trip)
 
 // The weight stream runs in steps of NB K blocks.  PIPE: two register sets
 // alternate, and the loads of step i + 1 are issued before the MFMAs of step
 // i, so every wave keeps a step in flight while it computes (the register
 // cost of 2 NB blocks); otherwise each step's loads are issued right before
 // its MFMAs.
-template <int ACT, int W, int NB, bool PIPE>
+template <int ACT, int W, int NB, bool PIPE, int NQC>
 __global__ __launch_bounds__(W * 64) void k_gemv_gateup_nq(const NormQ nq, const uint8_t* __restrict__ w,
                                                            uint8_t* __restrict__ hq, int M, int K, int I,
                                                            float alpha_g, float alpha_u, float inv_h) {
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup_nq(const NormQ nq, const
 
   // (1) activation-side loads: the row's slice sums (lane i < M*G holds
   // sum i) and the r' / w_norm chunks of this wave's K blocks
-  NormQWave<kNqChunks> nqw;
+  NormQWave<NQC> nqw;
   nqw.init(nq, M, K, kb0, kb1, lane);  // kb1 > kb0: W <= K / 128
   nqw.load(nq, 0, lane);
   __builtin_amdgcn_sched_barrier(0);
@@ -250,7 +252,7 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup_nq(const NormQ nq, const
   const float inv_rms = nqw.inv_rms(nq, lane);
   const bool store_xq = blockIdx.x == 0;
   nqw.quant(nq, 0, lane, inv_rms, xrow, store_xq);
-  for (int c0 = kNqChunks * 64; c0 < nqw.nch; c0 += kNqChunks * 64) {
+  for (int c0 = NQC * 64; c0 < nqw.nch; c0 += NQC * 64) {
     nqw.load(nq, c0, lane);
     nqw.quant(nq, c0, lane, inv_rms, xrow, store_xq);
   }
@@ -1106,20 +1108,29 @@ static bool gemv_pipe(const char* env, bool dflt) {
   return (e && *e) ? atoi(e) != 0 : dflt;
 }
 
-template <int W, int NB, bool PIPE>
-static void gemv_gateup_nq_wnp(int act, const NormQ& nq, const uint8_t* w, uint8_t* hq, int M, int K, int I,
-                               float a_g, float a_u, float inv_h, hipStream_t s) {
+template <int W, int NB, bool PIPE, int NQC>
+static void gemv_gateup_nq_wnpc(int act, const NormQ& nq, const uint8_t* w, uint8_t* hq, int M, int K, int I,
+                                float a_g, float a_u, float inv_h, hipStream_t s) {
   dim3 grid(I / 16), block(W * 64);
   const size_t lds = (size_t)M * K;
   if (act == GU_GEGLU)
-    hipLaunchKernelGGL((k_gemv_gateup_nq<GU_GEGLU, W, NB, PIPE>), grid, block, lds, s, nq, w, hq, M, K, I, a_g, a_u,
-                       inv_h);
-  else if (act == GU_SWIGLU)
-    hipLaunchKernelGGL((k_gemv_gateup_nq<GU_SWIGLU, W, NB, PIPE>), grid, block, lds, s, nq, w, hq, M, K, I, a_g,
+    hipLaunchKernelGGL((k_gemv_gateup_nq<GU_GEGLU, W, NB, PIPE, NQC>), grid, block, lds, s, nq, w, hq, M, K, I, a_g,
                        a_u, inv_h);
+  else if (act == GU_SWIGLU)
+    hipLaunchKernelGGL((k_gemv_gateup_nq<GU_SWIGLU, W, NB, PIPE, NQC>), grid, block, lds, s, nq, w, hq, M, K, I,
+                       a_g, a_u, inv_h);
   else
-    hipLaunchKernelGGL((k_gemv_gateup_nq<GU_GELU, W, NB, PIPE>), grid, block, lds, s, nq, w, hq, M, K, I, a_g, a_u,
-                       inv_h);
+    hipLaunchKernelGGL((k_gemv_gateup_nq<GU_GELU, W, NB, PIPE, NQC>), grid, block, lds, s, nq, w, hq, M, K, I, a_g,
+                       a_u, inv_h);
+}
+
+template <int W, int NB, bool PIPE>
+static void gemv_gateup_nq_wnp(int act, const NormQ& nq, const uint8_t* w, uint8_t* hq, int M, int K, int I,
+                               float a_g, float a_u, float inv_h, hipStream_t s) {
+  // chunks of the largest wave range: M x ceil(K blocks / W) x 16
+  const int chunks = M * (((K >> 7) + W - 1) / W) * 16;
+  if (chunks > 128 && chunks <= 192) gemv_gateup_nq_wnpc<W, NB, PIPE, 3>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
+  else gemv_gateup_nq_wnpc<W, NB, PIPE, 2>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
 }
 
 template <int W>

@@ -160,6 +160,20 @@ def test_small_shapes_gemv_launch_variants(spec, env, monkeypatch):
     log(str(rep))
 
 
+@pytest.mark.parametrize("waves,spec", [("1", (124, 1, 1280, 1024, 2, ACT_SWIGLU)),
+                                        ("2", (125, 3, 1024, 1024, 2, ACT_GEGLU_TANH)),
+                                        ("4", (126, 1, 5120, 512, 2, ACT_GELU_TANH))],
+                         ids=lambda v: "W%s" % v if isinstance(v, str) else "M%d_H%d_I%d" % (v[1], v[2], v[3]))
+def test_small_shapes_norm_quant_three_chunks(waves, spec, monkeypatch):
+    # decode gate/up waves whose K range holds 129-192 activation chunks:
+    # the norm-quantising prologue loads three per lane (one round trip)
+    monkeypatch.setenv("FRT_GEMV_WAVES_GATEUP", waves)
+    idx, M, H, I, L, act = spec
+    cfg = FFNConfig(idx, "small_nqc3_%d" % idx, M, H, I, L, act)
+    rep = run_case(cfg)
+    log(str(rep))
+
+
 @pytest.mark.parametrize("spec", [(117, 16, 1024, 512, 2, ACT_GEGLU_TANH), (118, 2, 640, 512, 3, ACT_SWIGLU),
                                   (119, 1, 8192, 1024, 2, ACT_GELU_TANH)],
                          ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
