@@ -296,6 +296,9 @@ void choose_gemm(const frt_ffn_desc& d, Layout& lo) {
         c = c8;
         sp = sp8;
       }
+      // the 256 x 192 tile with eight waves on the f16 cores (M = 4096 down
+      // GEMM: 271-273 against 280-283 us with four waves)
+      if (!fp8_dn && c == 2) c = kMMConfigEightWaves;
       c = env_int("FRT_MM_DOWN_CFG", c);
       sp = env_int("FRT_MM_DOWN_SPLIT", sp);
       if (mm_config_ffn(c) && d.H % mm_config_bn(c) == 0 && d.I % mm_config_ks(c) == 0 && sp >= 1 &&

@@ -55,7 +55,10 @@ int env_int(const char* name, int dflt);
 constexpr int kMMConfigCount = 6;     // FFN candidates 0..5 of the cost model
 constexpr int kMMConfigCountAll = 8;  // 6, 7: the attention input's small tiles
 constexpr int kMMConfigTwoPerCU = 8;  // 128 x 256, two workgroups per CU (FFN)
-inline bool mm_config_ffn(int c) { return (c >= 0 && c < kMMConfigCount) || c == kMMConfigTwoPerCU; }
+constexpr int kMMConfigEightWaves = 9;  // 256 x 192, eight waves: configuration 2 on the f16 cores (FFN)
+inline bool mm_config_ffn(int c) {
+  return (c >= 0 && c < kMMConfigCount) || c == kMMConfigTwoPerCU || c == kMMConfigEightWaves;
+}
 void choose_mm(int M, int N, int K, bool allow_split, int& cfg, int& split, int ncfg = kMMConfigCount);
 int mm_config_bm(int);
 int mm_config_bn(int);

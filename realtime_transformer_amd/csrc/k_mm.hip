@@ -440,6 +440,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_mm(const uint8_t* __restrict
 //   6: BM  64 x BN 128, waves 2 x 2 (wave tile  32 x 64), 4 stages   QKV only
 //   7: BM 128 x BN  64, waves 2 x 2 (wave tile  64 x 32), 4 stages   QKV only
 //   8: BM 128 x BN 256, waves 2 x 2 (wave tile  64 x 128), 3 stages, two workgroups per CU
+//   9: BM 256 x BN 192, waves 4 x 2 (wave tile  64 x  96), 4 stages, eight waves (f16 cores only)
 using MMC0 = MMCfg<224, 256, 1, 4, 4>;
 using MMC1 = MMCfg<256, 224, 4, 1, 4>;
 using MMC2 = MMCfg<256, 192, 2, 2, 4>;
@@ -454,14 +455,20 @@ using MMC7 = MMCfg<128, 64, 2, 2, 4>;
 // per CU (two waves per SIMD, so one wave's LDS reads, conversions and
 // barrier waits overlap the other's matrix instructions)
 using MMC8 = MMCfg<128, 256, 2, 2, 3, 2>;
-constexpr int kMMConfigs = 9;
+// 256 x 192 with eight waves (two per SIMD, so one wave's conversions and
+// LDS reads run while the other's matrix instructions do; wave tiles 64 x
+// 96): on the f16 cores it replaces configuration 2 (measured on the M=4096
+// down GEMM: 271-273 against 280-283 us; 256 x 256 eight-wave tiles were
+// level or slower where their grid leaves CUs idle)
+using MMC9 = MMCfg<256, 192, 4, 2, 4>;
+constexpr int kMMConfigs = 10;
 
 static const int kMM_BM[kMMConfigs] = {MMC0::BM, MMC1::BM, MMC2::BM, MMC3::BM, MMC4::BM,
-                                       MMC5::BM, MMC6::BM, MMC7::BM, MMC8::BM};
+                                       MMC5::BM, MMC6::BM, MMC7::BM, MMC8::BM, MMC9::BM};
 static const int kMM_BN[kMMConfigs] = {MMC0::BN, MMC1::BN, MMC2::BN, MMC3::BN, MMC4::BN,
-                                       MMC5::BN, MMC6::BN, MMC7::BN, MMC8::BN};
+                                       MMC5::BN, MMC6::BN, MMC7::BN, MMC8::BN, MMC9::BN};
 static const int kMM_KS[kMMConfigs] = {MMC0::KS, MMC1::KS, MMC2::KS, MMC3::KS, MMC4::KS,
-                                       MMC5::KS, MMC6::KS, MMC7::KS, MMC8::KS};
+                                       MMC5::KS, MMC6::KS, MMC7::KS, MMC8::KS, MMC9::KS};
 
 int mm_config_bm(int c) { return (c >= 0 && c < kMMConfigs) ? kMM_BM[c] : 0; }
 int mm_config_bn(int c) { return (c >= 0 && c < kMMConfigs) ? kMM_BN[c] : 0; }
@@ -495,6 +502,10 @@ static hipError_t mm_cfg(int cfg, const uint8_t* act, const uint8_t* w, void* ou
       return hipErrorInvalidValue;
     case 8:
       if constexpr (EPI != MM_QKV) return mm_launch<EPI, MMC8, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s, qo);
+      return hipErrorInvalidValue;
+    case 9:
+      if constexpr (EPI != MM_QKV && !FP8)
+        return mm_launch<EPI, MMC9, FP8>(act, w, out, part, M, K, Npk, S, a, b, inv, s, qo);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }

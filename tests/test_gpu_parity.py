@@ -85,6 +85,18 @@ def test_small_shapes_two_per_cu_gateup_tile(spec, monkeypatch):
     log(str(rep))
 
 
+@pytest.mark.parametrize("spec", [SMALL[4], (127, 300, 768, 512, 2, ACT_GELU_TANH)],
+                         ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
+def test_small_shapes_eight_wave_down_tile(spec, monkeypatch):
+    # the 256 x 192 eight-wave down tile (the default where the cost model
+    # picks 256 x 192 on the f16 cores), with ragged row tiles
+    monkeypatch.setenv("FRT_MM_DOWN_CFG", "9")
+    idx, M, H, I, L, act = spec
+    cfg = FFNConfig(idx, "small_cfg9_%d" % idx, M, H, I, L, act)
+    rep = run_case(cfg)
+    log(str(rep))
+
+
 @pytest.mark.parametrize("spec", [SMALL[0], SMALL[1], SMALL[2]],
                          ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
 def test_small_shapes_fused_norm(spec):
