@@ -191,22 +191,27 @@ class CaseReport:
     cal_max_rel: float = 0.0
     cal_tf_max_rel: float = 0.0
     saturated_codes: int = 0
+    subnormal_codes: int = 0    # E4M3 codes with a zero exponent field and a nonzero mantissa
+    zero_xq_rows: int = 0       # rows of XQ[0] that are all zero codes
     seconds: float = 0.0
 
 
 def run_case(cfg: FFNConfig, rows: Optional[Sequence[int]] = None, cal_rows: Optional[Sequence[int]] = None,
              check_layers: Optional[Sequence[int]] = None, nbatch: int = 4, flags: int = 0,
-             gate_drift: bool = True, gate_hq: bool = True) -> CaseReport:
+             gate_drift: bool = True, gate_hq: bool = True, edit_inputs=None) -> CaseReport:
     """Full parity procedure; rows / cal_rows select the evaluated / calibration
     rows (None = all); check_layers selects the teacher-forced layers (None = all);
     flags are plan flags; gate_drift gates the free-running chain and gate_hq the
-    re-quantised HQ bytes (else both are reported only)."""
+    re-quantised HQ bytes (else both are reported only); edit_inputs(r0, y0)
+    returns replaced evaluation inputs (bf16 bits), given to both sides."""
     t0 = time.time()
     rep = CaseReport(cfg.name)
     M, H, I, L, act = cfg.M, cfg.H, cfg.I, cfg.L, cfg.act
     rows_arg = rows
     rows = np.arange(M) if rows is None else np.asarray(sorted(rows))
     r0, y0 = datagen.eval_inputs(cfg)
+    if edit_inputs is not None:
+        r0, y0 = edit_inputs(r0, y0)
     cal = datagen.calib_batches(cfg, nbatch)
     if cal_rows is not None:
         cr = np.asarray(sorted(cal_rows))
@@ -324,6 +329,9 @@ def run_case(cfg: FFNConfig, rows: Optional[Sequence[int]] = None, cal_rows: Opt
                 codes = to_np_u8(t)
                 assert not np.any((codes & 0x7F) == 0x7F), "NaN code in layer %d" % l
                 rep.saturated_codes += int(np.count_nonzero((codes & 0x7F) == 0x7E))
+                rep.subnormal_codes += int(np.count_nonzero(((codes & 0x78) == 0) & ((codes & 0x07) != 0)))
+        xq0 = to_np_u8(plan.xq_slot(0)).reshape(M, H)
+        rep.zero_xq_rows = int(np.count_nonzero(~np.any(xq0 & 0x7F, axis=1)))
         z_ref = oracle.final_hidden(orc.r[L], orc.y[L])
         rep.z_max_rel, rep.z_cos = y_metrics(z_graph[rows], z_ref)
         rep.z_dist = _natural.cos_distance(z_graph[rows], z_ref)

@@ -239,6 +239,41 @@ def test_small_shapes_ada_norm(spec):
     log(str(rep))
 
 
+def _degenerate_rows(r0, y0):
+    """Row 0 all zeros (R and Y): the norm's mean square is eps alone and every
+    code is zero; row 1 scaled by 2^-24 (the bf16 exponent drops by 24; the
+    rare values too small for that become zero), so eps dominates its mean
+    square and its normalised values quantise to E4M3 subnormals or zero;
+    row 2 has +-300 in its first eight entries, which saturate at +-448 after
+    the norm."""
+    r = r0.copy()
+    r[0] = 0
+    b = r[1].astype(np.int32)
+    e = (b >> 7) & 0xFF
+    r[1] = np.where(e > 24, b - (24 << 7), b & 0x8000).astype(np.uint16)
+    r[2, :8] = np.array([0x4396, 0xC396] * 4, dtype=np.uint16)  # bf16 +300, -300
+    y = None
+    if y0 is not None:
+        y = y0.copy()
+        y[0] = 0
+    return r, y
+
+
+@pytest.mark.parametrize("spec", [(142, 3, 256, 512, 2, ACT_SWIGLU), (143, 40, 512, 1024, 2, ACT_GEGLU_TANH),
+                                  (144, 300, 256, 512, 2, ACT_GELU_TANH), (145, 4, 1024, 2048, 3, ACT_GEGLU_TANH)],
+                         ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
+def test_degenerate_rows(spec):
+    # a zero row, a row in the E4M3 subnormal range after the norm, and a row
+    # that saturates, through the decode GEMV (with the split norm), the
+    # multi-tile GEMV and the prefill GEMM paths
+    idx, M, H, I, L, act = spec
+    cfg = FFNConfig(idx, "degenerate_%d" % idx, M, H, I, L, act)
+    rep = run_case(cfg, edit_inputs=_degenerate_rows)
+    log(str(rep))
+    # the three rows did exercise what they are for
+    assert rep.zero_xq_rows >= 1 and rep.subnormal_codes > 0 and rep.saturated_codes > 0
+
+
 def test_action_expert_m50_chain_ada_norm():
     # the action expert's full 18-layer chain with AdaRMSNorm modulation
     rep = run_case(CONFIGS[2], flags=_abi.FRT_FLAG_ADA_NORM)
