@@ -100,15 +100,17 @@ def time_replays(plan, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall
 
 
-def replay_percentiles(plan, n):
-    """Each of n replays timed on its own (an event pair around it, a wait
-    after it): median, p10 and p90 in ms.  Isolated replays include the
-    graph launch latency that back-to-back replays overlap."""
+def replay_percentiles(plan, n, eager=False):
+    """Each of n replays (eager: eager forwards, the same kernels launched one
+    by one through frt_ffn_forward) timed on its own (an event pair around
+    it, a wait after it): median, p10 and p90 in ms.  Isolated replays
+    include the graph launch latency that back-to-back replays overlap."""
     import torch
+    run = plan.forward if eager else plan.replay
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
     for a, b in ev:
         a.record(plan.stream)
-        plan.replay()
+        run()
         b.record(plan.stream)
         b.synchronize()
     t = np.array([a.elapsed_time(b) for a, b in ev])
@@ -336,6 +338,9 @@ def measure_chain(cfg, steps, warmup, flags=0, calibrate=True, iso=50):
         plan.capture()
     ms, wall = time_replays(plan, steps, warmup)
     pct = replay_percentiles(plan, iso)
+    # the short chains are bound by launch latency: the eager forward's
+    # isolated latency beside the graph replay's
+    pct_eager = replay_percentiles(plan, iso, eager=True) if cfg.M * cfg.L <= 1024 else None
     host_us = host_enqueue_us(plan, min(iso, 50))
     k = [float(v) for v in per_kernel_ms(plan)]
     plan.close()
@@ -347,6 +352,7 @@ def measure_chain(cfg, steps, warmup, flags=0, calibrate=True, iso=50):
            "us_per_layer": round(us, 3), "ms_per_chain": round(ms, 4),
            "tokens_per_s": round(cfg.M / (ms * 1e-3), 1),
            "isolated_replay_ms": pct, "host_graph_launch_us": host_us, "wall_s_timed": round(wall, 4),
+           "isolated_eager_forward_ms": pct_eager,
            "kernels_us": {"norm_quant": round(k[0] * 1000, 3), "gateup": round(k[1] * 1000, 3),
                           "down": round(k[2] * 1000, 3)},
            "kernel_sum_us_per_layer": round(sum(k) * 1000, 3),
