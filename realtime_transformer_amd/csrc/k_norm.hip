@@ -35,7 +35,12 @@ namespace frt {
 // consecutive chunks, i.e. four neighbouring lanes) takes its E8M0 exponent
 // from the 4-lane maximum, and xq_out receives [M][H/2] E2M1 codes, xs_out
 // [M][H/32] exponents.
-template <int TPR, int NC, bool MEASURE, bool MX = false>
+// UPW: the one-wave-per-row form also issues every load of its row (and of
+// the first four split-K partials) before using any, as the one-workgroup
+// form does: one memory round trip per row instead of one per chunk, for
+// the workloads whose rows are too few for occupancy to hide the per-chunk
+// round trips.
+template <int TPR, int NC, bool MEASURE, bool MX = false, bool UPW = false>
 __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
     const uint16_t* __restrict__ r_prev, const uint16_t* __restrict__ y_prev,
     const uint16_t* __restrict__ w_norm, const uint16_t* __restrict__ mod, uint16_t* __restrict__ r_out,
@@ -66,7 +71,7 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
   // H = 5120 decode chain gains 0.4 us per layer); the many-row form (one
   // wave per row) reads chunk by chunk in the second loop instead, where
   // occupancy hides the latency and the up-front registers would halve it.
-  constexpr bool UP = TPR == 256;
+  constexpr bool UP = TPR == 256 || UPW;
   constexpr bool PF = UP && NC <= 4;
   uint4 rn[NC], wn[NC], mh[NC], yv[NC];
   float4 aw[MX ? NC : 1][2];
@@ -382,6 +387,18 @@ __global__ __launch_bounds__(256) void k_e4m3_encode(const float* __restrict__ i
 // host-side launchers
 // ---------------------------------------------------------------------------
 
+// Whether the one-wave-per-row form issues its row's loads up front (UPW):
+// where the rows are few enough (M <= 1024, at most four per CU) that the
+// per-chunk round trips are the kernel's time; with more rows the extra
+// registers cost the occupancy that hides them.  Measured: M=788 (H=2048,
+// four split-K partials) 9.05 -> 7.04 us; M=4096 (H=3072) 17.3 -> 19.8 us.
+// FRT_NORM_UPFRONT=0 / 1 forces it off / on.
+static bool norm_upfront(int M) {
+  const char* e = getenv("FRT_NORM_UPFRONT");
+  if (e && *e) return atoi(e) != 0;
+  return M <= 1024;
+}
+
 template <bool MEASURE>
 static hipError_t launch_norm_t(const uint16_t* r_prev, const uint16_t* y_prev,
                                 const uint16_t* w, const uint16_t* mod, uint16_t* r_out, uint8_t* xq, float* x_out,
@@ -394,18 +411,21 @@ static hipError_t launch_norm_t(const uint16_t* r_prev, const uint16_t* y_prev,
   if (nchunk <= 64 * 8) {
     const int nc = (nchunk + 63) / 64;
     dim3 grid((M + 3) / 4);
-    if (nc <= 2)
-      hipLaunchKernelGGL((k_add_rmsnorm_quant<64, 2, MEASURE>), grid, dim3(256), 0, s, r_prev,
-                         y_prev, w, mod, r_out, xq, x_out, amax, M, H, eps, inv_x, y_part, S, alpha_d,
-                         y_store);
-    else if (nc <= 4)
-      hipLaunchKernelGGL((k_add_rmsnorm_quant<64, 4, MEASURE>), grid, dim3(256), 0, s, r_prev,
-                         y_prev, w, mod, r_out, xq, x_out, amax, M, H, eps, inv_x, y_part, S, alpha_d,
-                         y_store);
-    else
-      hipLaunchKernelGGL((k_add_rmsnorm_quant<64, 8, MEASURE>), grid, dim3(256), 0, s, r_prev,
-                         y_prev, w, mod, r_out, xq, x_out, amax, M, H, eps, inv_x, y_part, S, alpha_d,
-                         y_store);
+    const bool upw = !MEASURE && norm_upfront(M);
+#define FRT_NORM64(NCV)                                                                                         \
+  do {                                                                                                          \
+    if (upw)                                                                                                    \
+      hipLaunchKernelGGL((k_add_rmsnorm_quant<64, NCV, MEASURE, false, true>), grid, dim3(256), 0, s, r_prev,  \
+                         y_prev, w, mod, r_out, xq, x_out, amax, M, H, eps, inv_x, y_part, S, alpha_d, y_store); \
+    else                                                                                                        \
+      hipLaunchKernelGGL((k_add_rmsnorm_quant<64, NCV, MEASURE>), grid, dim3(256), 0, s, r_prev, y_prev, w,    \
+                         mod, r_out, xq, x_out, amax, M, H, eps, inv_x, y_part, S, alpha_d, y_store);           \
+  } while (0)
+    if (nc <= 2) FRT_NORM64(2);
+    else if (nc <= 4) FRT_NORM64(4);
+    else if (nc <= 6) FRT_NORM64(6);
+    else FRT_NORM64(8);
+#undef FRT_NORM64
   } else {
     const int nc = (nchunk + 255) / 256;
     dim3 grid(M);
