@@ -150,6 +150,7 @@ GEMV_VARIANTS = [
     {"FRT_GEMV_PIPE_GATEUP": "1", "FRT_GEMV_PIPE_DOWN": "1", "FRT_GEMV_NB_GATEUP": "2", "FRT_GEMV_NB_DOWN": "2"},
     {"FRT_GEMV_PIPE_GATEUP": "0", "FRT_GEMV_PIPE_DOWN": "0", "FRT_GEMV_NB_GATEUP": "2", "FRT_GEMV_NB_DOWN": "2"},
     {"FRT_GEMV_PIPE_GATEUP": "0", "FRT_GEMV_PIPE_DOWN": "0"},
+    {"FRT_GEMV_DOWN_ORDER": "0"},
     # few waves, so each streams several K blocks (odd counts peel a step)
     {"FRT_GEMV_PIPE_GATEUP": "1", "FRT_GEMV_PIPE_DOWN": "1", "FRT_GEMV_WAVES_GATEUP": "2",
      "FRT_GEMV_WAVES_DOWN": "1"},
