@@ -214,9 +214,15 @@ def measure_qkv(steps, warmup, calibrate=True):
         e1.record(p.stream)
         e1.synchronize()
         us = e0.elapsed_time(e1) * 1000.0 / steps
+        # one block is two kernels: the launch is most of its latency, so the
+        # isolated replay and the isolated eager forward are reported beside
+        # the back-to-back rate
+        pct = replay_percentiles(p, 50)
+        pct_eager = replay_percentiles(p, 50, eager=True)
         k = [p.time_kernel(i, 20) for i in range(2)]
         p.close()
         rec = {"M": c.M, "H": c.H, "heads": [c.nq, c.nkv, c.hd], "us_per_block": round(us, 3),
+               "isolated_replay_ms": pct, "isolated_eager_forward_ms": pct_eager,
                "kernels_us": {"norm_quant": round(k[0], 3), "qkv": round(k[1], 3)}}
         if c.M <= 64:
             gbs = c.qkv_bytes() / (k[1] * 1e-6) / 1e9
