@@ -98,7 +98,11 @@ __device__ __forceinline__ void qkv_load_x32(const uint8_t* xr, bool has_row, in
 }
 
 // One workgroup of W waves per pair p of 16-row groups; MT activation tiles.
-template <int W, int MT>
+// PIPE: one K block per step over two register sets, the next block's
+// weight and activation loads issued before the current block's MFMAs (as
+// the FFN decode GEMVs do), every load unconditional (rows past M read row
+// 0, whose products reach only output rows past M, never stored).
+template <int W, int MT, bool PIPE>
 __global__ __launch_bounds__(W * 64) void k_gemv_qkv(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ w,
                                                      const QkvOut o, int M, int K) {
   static_assert(W >= MT, "one wave per tile finishes the epilogue");
@@ -121,7 +125,69 @@ __global__ __launch_bounds__(W * 64) void k_gemv_qkv(const uint8_t* __restrict__
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc1[t] = acc2[t] = v4f{0, 0, 0, 0};
 
-  for (int kb = kb0; kb < kb1; kb += 2) {
+  if (PIPE) {
+    const int nblk = kb1 - kb0;
+    typedef uint32_t Frag[8];
+    Frag aA, bA, aB, bB, xA[MT], xB[MT];
+    auto load_step = [&](Frag& a, Frag& b, Frag (&x)[MT], int i) {
+      const int kb = kb0 + (i < nblk ? i : nblk - 1);
+      qkv_load_w32(w1, kb, a);
+      qkv_load_w32(w2, kb, b);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(xr[t] + kb * 128);
+        const uint4 hi = *reinterpret_cast<const uint4*>(xr[t] + kb * 128 + 16);
+        x[t][0] = lo.x; x[t][1] = lo.y; x[t][2] = lo.z; x[t][3] = lo.w;
+        x[t][4] = hi.x; x[t][5] = hi.y; x[t][6] = hi.z; x[t][7] = hi.w;
+      }
+    };
+    auto mma_step = [&](Frag& a, Frag& b, Frag (&x)[MT]) {
+      // the step's operands count as written here, so the compiler cannot
+      // convert them early (which would wait for every later load as well)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        asm volatile("" : "+v"(a[j]));
+        asm volatile("" : "+v"(b[j]));
+#pragma unroll
+        for (int t = 0; t < MT; ++t) asm volatile("" : "+v"(x[t][j]));
+      }
+      v8h ah[4], bh[4];
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        ah[s4] = e4m3x8_to_f16(a[2 * s4], a[2 * s4 + 1]);
+        bh[s4] = e4m3x8_to_f16(b[2 * s4], b[2 * s4 + 1]);
+      }
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const v8h xh = e4m3x8_to_f16(x[t][2 * s4], x[t][2 * s4 + 1]);
+          acc1[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, ah[s4], acc1[t], 0, 0, 0);
+          acc2[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, bh[s4], acc2[t], 0, 0, 0);
+        }
+    };
+    if (nblk > 0) {
+      load_step(aA, bA, xA, 0);
+      int i = 0;
+      for (; i + 2 < nblk; i += 2) {
+        load_step(aB, bB, xB, i + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_step(aA, bA, xA);
+        load_step(aA, bA, xA, i + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_step(aB, bB, xB);
+      }
+      if (i + 1 < nblk) {
+        load_step(aB, bB, xB, i + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_step(aA, bA, xA);
+        mma_step(aB, bB, xB);
+      } else {
+        mma_step(aA, bA, xA);
+      }
+    }
+  }
+  for (int kb = kb0; !PIPE && kb < kb1; kb += 2) {
     const bool two = kb + 1 < kb1;
     uint32_t a0[8], a1[8], b0[8], b1[8], x0[MT][8], x1[MT][8];
     qkv_load_w32(w1, kb, a0);
@@ -304,10 +370,15 @@ hipError_t launch_gemv_qkv_nq(const uint16_t* r, const uint16_t* w_norm, const d
 }
 
 // (W = 16 only with MT <= 2: the reduction buffer is W * MT * 2 KiB of LDS)
+// FRT_QKV_GEMV_PIPE=0 keeps the unpipelined stream
 template <int W, int MT>
 static hipError_t gemv_qkv_t(const uint8_t* xq, const uint8_t* w, const QkvOut& o, int M, int K, int pairs,
                              hipStream_t s) {
-  hipLaunchKernelGGL((k_gemv_qkv<W, MT>), dim3(pairs), dim3(W * 64), 0, s, xq, w, o, M, K);
+  const char* e = getenv("FRT_QKV_GEMV_PIPE");
+  if (e && *e && atoi(e) == 0)
+    hipLaunchKernelGGL((k_gemv_qkv<W, MT, false>), dim3(pairs), dim3(W * 64), 0, s, xq, w, o, M, K);
+  else
+    hipLaunchKernelGGL((k_gemv_qkv<W, MT, true>), dim3(pairs), dim3(W * 64), 0, s, xq, w, o, M, K);
   return hipGetLastError();
 }
 

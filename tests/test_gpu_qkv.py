@@ -146,6 +146,26 @@ def test_qkv_small_split_norm(spec, monkeypatch):
     run_qkv_case(QkvConfig(idx, "qkv_splitnorm_%d" % idx, M, H, nq, nkv, hd, pos0, max_pos, base))
 
 
+GEMV_LAUNCH = [
+    # nine K blocks: 2 or 3 per wave at 4 waves, 1 or 2 at 8, none for some at 16
+    (129, 3, 1152, 4, 2, 64, 11, 64, 10000.0),
+    (130, 40, 1152, 2, 1, 128, 0, 64, 1e6),  # three row tiles (16 waves taken as 8)
+]
+
+
+@pytest.mark.parametrize("pipe", ["1", "0"], ids=["pipelined", "unpipelined"])
+@pytest.mark.parametrize("waves", ["4", "8", "16"])
+@pytest.mark.parametrize("spec", GEMV_LAUNCH, ids=lambda s: "M%d_H%d" % (s[1], s[2]))
+def test_qkv_gemv_launch_variants(spec, waves, pipe, monkeypatch):
+    # the decode GEMV under each wave count, with and without the two-stage
+    # K-block pipeline (FRT_QKV_GEMV_PIPE=0 keeps the unpipelined stream)
+    monkeypatch.setenv("FRT_QKV_GEMV_WAVES", waves)
+    monkeypatch.setenv("FRT_QKV_GEMV_PIPE", pipe)
+    idx, M, H, nq, nkv, hd, pos0, max_pos, base = spec
+    run_qkv_case(QkvConfig(idx, "qkv_gemv_%d_w%s_p%s" % (idx, waves, pipe), M, H, nq, nkv, hd, pos0, max_pos,
+                           base))
+
+
 def test_qkv_llm_decode_m1_split_norm(monkeypatch):
     monkeypatch.setenv("FRT_QKV_NORM_SPLIT", "1")
     run_qkv_case(QKV_CONFIGS["qkv_llm_decode_m1"])
