@@ -253,6 +253,23 @@ frt_status frt_set_act_scales(frt_plan *plan, const float *host_in);
 /* Fixed device addresses of the plan's activation slots. */
 frt_status frt_ffn_io_get(const frt_plan *plan, frt_ffn_io *out);
 
+/* Which kernels the plan's forward runs, as FRT_PATH_* bits (fixed at plan
+ * creation from M, H, I, the flags and the FRT_* environment overrides):
+ *   FRT_PATH_GEMV: M <= 16, the decode GEMVs (else multi-tile GEMVs or GEMMs)
+ *   FRT_PATH_NORM_SPLIT: the decode norm split into slice sums and the
+ *     gate/up GEMV's own quantisation
+ *   FRT_PATH_DOWN_WHOLE_COLUMN: the whole-column down GEMV (M <= 4), which
+ *     forms the next layer's R' and norm slice sums (no norm kernel between
+ *     layers; the down matrix is held in its column-quad layout)
+ *   FRT_PATH_DOWN_SPLIT_K: the down projection's K is split over
+ *     workgroups, the fp32 partials summed by the next kernel
+ * For tests and logs; FRT_ERR_INVALID_ARG on a NULL argument. */
+#define FRT_PATH_GEMV 1u
+#define FRT_PATH_NORM_SPLIT 2u
+#define FRT_PATH_DOWN_WHOLE_COLUMN 4u
+#define FRT_PATH_DOWN_SPLIT_K 8u
+frt_status frt_ffn_plan_path(const frt_plan *plan, uint32_t *path_bits);
+
 /* Eager forward of layers [layer_begin, layer_end) on `stream`: reads slots
  * R[layer_begin], Y[layer_begin], writes the later slots; when layer_end == L
  * also writes Z.  Asynchronous: no allocation, no host synchronisation.
@@ -297,15 +314,20 @@ frt_status frt_graph_replay(frt_plan *plan, void *stream);
  * milliseconds to host_ms[L][3] = {norm+quantise, gate/up GEMM, down GEMM}
  * (with the norm fused into gate/up, the first entry times an empty slot;
  * with the split decode norm (M <= 16, the default there) the first entry
- * is the slice-sum kernel and the gate/up entry includes the quantisation).
+ * is the slice-sum kernel and the gate/up entry includes the quantisation;
+ * with the whole-column down GEMV (M <= 4, the default there) the first
+ * entry runs only in layer 0, later layers' R' and slice sums coming from
+ * the previous down GEMV).
  * Same kernels and launch configuration as frt_ffn_forward.  Synchronises
  * `stream`.  For measuring per-kernel time inside a running program. */
 frt_status frt_ffn_forward_profiled(frt_plan *plan, void *stream, float *host_ms);
 
 /* Average duration in microseconds of one kernel kind (which: 0 norm +
- * quantise (the slice-sum kernel under the split decode norm), 1 gate/up
- * GEMM (including the norm when fused, the quantisation when split), 2 down
- * GEMM):
+ * quantise (the slice-sum kernel under the split decode norm; with the
+ * whole-column down GEMV it runs in layer 0 only and the average is over
+ * all layers), 1 gate/up GEMM (including the norm when fused, the
+ * quantisation when split), 2 down GEMM (with the whole-column down GEMV,
+ * also the next layer's residual add and slice sums)):
  * launches it for every layer, `reps` times, back to back on `stream`
  * between two HIP events (same kernels and launch configuration as the
  * forward).  The activation slots are left undefined (run the forward or

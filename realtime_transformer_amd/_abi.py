@@ -33,6 +33,11 @@ FRT_FLAG_NORM_FUSE = 8
 FRT_FLAG_ADA_NORM = 16
 FRT_FLAG_MXFP4 = 32
 
+FRT_PATH_GEMV = 1
+FRT_PATH_NORM_SPLIT = 2
+FRT_PATH_DOWN_WHOLE_COLUMN = 4
+FRT_PATH_DOWN_SPLIT_K = 8
+
 _STATUS_NAMES = {0: "FRT_OK", 1: "FRT_ERR_INVALID_ARG", 2: "FRT_ERR_HIP", 3: "FRT_ERR_STATE",
                  4: "FRT_ERR_UNSUPPORTED", 5: "FRT_ERR_WORKSPACE"}
 
@@ -42,6 +47,7 @@ EXPORTED = [
     "frt_ffn_io_get", "frt_ffn_forward_range", "frt_ffn_forward", "frt_graph_capture",
     "frt_graph_replay", "frt_ffn_forward_profiled", "frt_ffn_time_kernel", "frt_e4m3_encode_f32",
     "frt_last_error", "frt_export_mxfp4_weights", "frt_set_awq", "frt_ffn_forward_range_static_scratch",
+    "frt_ffn_plan_path",
     # attention input (include/frt_qkv.h)
     "frt_qkv_workspace_size", "frt_qkv_plan_create", "frt_qkv_plan_destroy", "frt_qkv_quant_weights",
     "frt_qkv_export_weight_codes", "frt_qkv_calibrate", "frt_qkv_get_scales", "frt_qkv_set_act_scale",
@@ -109,6 +115,7 @@ def load(build_if_missing: bool = True):
         "frt_get_scales": [vp, ctypes.POINTER(ctypes.c_float)],
         "frt_set_act_scales": [vp, ctypes.POINTER(ctypes.c_float)],
         "frt_ffn_io_get": [vp, ctypes.POINTER(frt_ffn_io)],
+        "frt_ffn_plan_path": [vp, ctypes.POINTER(ctypes.c_uint32)],
         "frt_ffn_forward_range": [vp, i32, i32, vp],
         "frt_ffn_forward_range_static_scratch": [vp, i32, i32, vp],
         "frt_ffn_forward": [vp, vp],
@@ -199,6 +206,12 @@ def frt_get_scales(plan: int, L: int) -> np.ndarray:
 def frt_set_act_scales(plan: int, scales) -> None:
     a = np.ascontiguousarray(np.asarray(scales, dtype=np.float32))
     _check(load().frt_set_act_scales(plan, a.ctypes.data_as(ctypes.POINTER(ctypes.c_float))))
+
+
+def frt_ffn_plan_path(plan: int) -> int:
+    bits = ctypes.c_uint32(0)
+    _check(load().frt_ffn_plan_path(plan, ctypes.byref(bits)))
+    return int(bits.value)
 
 
 def frt_ffn_io_get(plan: int) -> frt_ffn_io:

@@ -50,9 +50,13 @@ hipError_t launch_gemv_down_mt(const uint8_t*, const uint8_t*, uint16_t*, float*
                                float, hipStream_t);
 bool gemv_fused_supported(int, int, int);
 hipError_t launch_add_sumsq(const uint16_t*, const uint16_t*, const float*, int, float, uint16_t*, uint16_t*, double*,
-                            int, int, hipStream_t);
+                            int, int, hipStream_t, int = 0);
 int add_sumsq_slices(int);
 bool gemv_nq_supported(int, int, int);
+bool gemv_nq_wide_supported(int, int, int);
+bool gemv_down_quad_supported(int, int, int);
+hipError_t launch_gemv_down_quad(const uint8_t*, const uint8_t*, const uint16_t*, uint16_t*, uint16_t*, double*, int,
+                                 int, int, int, float, hipStream_t);
 bool gemv_mx_nq_supported(int, int, int);
 hipError_t launch_gemv_gateup_mx_nq(int, const uint16_t*, const uint16_t*, const float*, const double*, int, float,
                                     uint8_t*, uint8_t*, const uint8_t*, const uint8_t*, uint8_t*, uint8_t*, int, int,
@@ -89,7 +93,7 @@ int gemm_config_bn(int);
 hipError_t launch_calib_gateup(int, const float*, const uint8_t*, float*, float*, int, int, int,
                                float, float, hipStream_t);
 hipError_t launch_calib_down(const float*, const uint8_t*, uint16_t*, int, int, int, float,
-                             hipStream_t);
+                             hipStream_t, int);
 }  // namespace frt
 
 using namespace frt;
@@ -171,6 +175,8 @@ struct Layout {
   int cfg_gu, cfg_dn;  // GEMM tile configurations
   bool mm_gu, mm_dn;   // GEMM runs on the LDS-DMA f16 kernel (k_mm) rather than k_gemm
   bool norm_split;     // decode GEMV path: k_add_sumsq, then the gate/up GEMV quantises (k_gemv_gateup_nq)
+  bool dn_quad;        // ... with the whole-column down GEMV (k_gemv_down_quad), which forms the next
+                       // layer's R' and 4-column slice sums itself: no norm kernel between layers
   size_t sqp;          // its slice sums of squares, fp64 [M][G]
   size_t sqp_bytes;    // bytes of that region
 };
@@ -406,6 +412,23 @@ Layout make_layout(const frt_ffn_desc& d) {
       lo.s_gu = lo.s_gu >= 8 ? 8 : 4;
       lo.s_dn = lo.s_dn >= 8 ? 8 : 4;
     }
+    // M <= 4 on the split norm: the whole-column down GEMV (down matrix in
+    // the column-quad layout), FRT_DOWN_QUAD=0 keeps the split-K GEMV and
+    // the slice-sum kernel
+    lo.dn_quad = lo.norm_split && !lo.mx && !lo.gemv_mt && (d.flags & FRT_FLAG_FP8_MFMA_DOWN) == 0u &&
+                 gemv_down_quad_supported((int)M, (int)I, (int)H) && gemv_nq_wide_supported((int)M, (int)H, lo.s_gu) &&
+                 env_int("FRT_DOWN_QUAD", 1) != 0;
+    if (lo.dn_quad) {
+      // 1 KiB steps per workgroup: I / 256, over eight waves (at M=1,
+      // H=5120, I=17408: 16.0 us against 17.5 with sixteen and 18.2 with
+      // four), fewer where the steps do not reach one per wave
+      const int steps = (int)(I / 256);
+      int w = env_int("FRT_GEMV_WAVES_DOWN_QUAD", 8);
+      if (w != 1 && w != 2 && w != 4 && w != 8 && w != 16) w = 4;
+      while (w > 1 && w > steps) w /= 2;
+      lo.k_dn = 1;
+      lo.s_dn = w;
+    }
     lo.split_dn = lo.k_dn;
     part = lo.k_dn > 1 ? (size_t)lo.k_dn * M * H * 4 : 4;
     words = 1;
@@ -416,7 +439,7 @@ Layout make_layout(const frt_ffn_desc& d) {
     part = lo.s_dn > 1 ? (size_t)lo.s_dn * M * H * 4 : 4;
     words = 1;
   }
-  lo.sqp_bytes = lo.norm_split ? M * (size_t)add_sumsq_slices((int)H) * 8 : 256;
+  lo.sqp_bytes = lo.norm_split ? M * (size_t)(lo.dn_quad ? H / 4 : add_sumsq_slices((int)H)) * 8 : 256;
   lo.sqp = take(lo.sqp_bytes);
   lo.part = take(part);
   lo.part_bytes = part;
@@ -667,7 +690,7 @@ frt_status frt_quant_weights(frt_plan* p, int32_t layer, const void* d_w_gate, c
   } else {
     if ((st = quant_one(p, d_w_up, I, H, p->wgu(layer), 0, &su, s, fold)) != FRT_OK) return st;
   }
-  if ((st = quant_one(p, d_w_down, H, I, p->wd(layer), 0, &sd, s)) != FRT_OK) return st;
+  if ((st = quant_one(p, d_w_down, H, I, p->wd(layer), p->lo.dn_quad ? 3 : 0, &sd, s)) != FRT_OK) return st;
   if (p->norm_fuse())
     HIP_CHECK(hipMemsetD16Async(reinterpret_cast<hipDeviceptr_t>(p->wn(layer)), 0x3F80u, (size_t)H, s));
   else
@@ -707,7 +730,8 @@ frt_status frt_export_weight_codes(const frt_plan* p, int32_t layer, int32_t whi
     uint32_t prow = n;
     if (!down && p->gated) prow = which == 0 ? gate_row(n) : up_row_gated(n);
     for (uint32_t k = 0; k < K; k += 16)
-      memcpy(dst + (size_t)n * K + k, tmp.data() + packed_offset(prow, k, K), 16);
+      memcpy(dst + (size_t)n * K + k,
+             tmp.data() + (down && p->lo.dn_quad ? quad_offset(n, k, K) : packed_offset(prow, k, K)), 16);
   }
   return FRT_OK;
 }
@@ -811,7 +835,8 @@ frt_status frt_calibrate(frt_plan* p, const void* const* d_r_batches, const void
                                               p->d.eps, s), "add_rmsnorm_measure");
       KERNEL_CHECK(launch_calib_gateup(p->d.act, x, p->wgu(l), h, am + L + l, rows, H, I,
                                        p->gated ? p->s_g[l] : p->s_u[l], p->s_u[l], s), "calib_gateup");
-      KERNEL_CHECK(launch_calib_down(h, p->wd(l), y_next, rows, I, H, p->s_d[l], s), "calib_down");
+      KERNEL_CHECK(launch_calib_down(h, p->wd(l), y_next, rows, I, H, p->s_d[l], s, p->lo.dn_quad ? 1 : 0),
+                   "calib_down");
       r_cur = r_next;
       y_cur = y_next;
     }
@@ -856,6 +881,17 @@ frt_status frt_set_act_scales(frt_plan* p, const float* host_in) {
   return FRT_OK;
 }
 
+frt_status frt_ffn_plan_path(const frt_plan* p, uint32_t* path_bits) {
+  if (!p || !path_bits) return fail(FRT_ERR_INVALID_ARG, "frt_ffn_plan_path: NULL argument");
+  uint32_t b = 0;
+  if (p->d.M <= kGemvMaxM && !p->lo.mx_mm) b |= FRT_PATH_GEMV;
+  if (p->lo.norm_split) b |= FRT_PATH_NORM_SPLIT;
+  if (p->lo.dn_quad) b |= FRT_PATH_DOWN_WHOLE_COLUMN;
+  if (p->lo.split_dn > 1) b |= FRT_PATH_DOWN_SPLIT_K;
+  *path_bits = b;
+  return FRT_OK;
+}
+
 frt_status frt_ffn_io_get(const frt_plan* p, frt_ffn_io* out) {
   if (!p || !out) return fail(FRT_ERR_INVALID_ARG, "frt_ffn_io_get: NULL argument");
   out->r_slots = p->r(0);
@@ -877,8 +913,11 @@ frt_status frt_ffn_io_get(const frt_plan* p, frt_ffn_io* out) {
 // Down output of layer l-1 still in split-K partials (GEMM path, split > 1)?
 static bool down_split(const frt_plan* p) { return p->lo.split_dn > 1; }
 
+// after_down: layer l - 1's down GEMM ran before this launch in the same
+// sequence (with the whole-column down GEMV, layer l's norm step is then
+// already done and launches nothing).
 static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t s,
-                                      bool y_in_partials = false) {
+                                      bool y_in_partials = false, bool after_down = false) {
   const int M = p->d.M, H = p->d.H, I = p->d.I;
   const int npk = p->gated ? 2 * I : I;
   const float s_x = p->s_x[l], s_h = p->s_h[l];
@@ -922,7 +961,9 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
     return FRT_OK;
   }
   if (which == 0) {
-    if (p->lo.norm_split) {
+    if (p->lo.dn_quad && after_down) {
+      // R' and the slice sums came from layer l - 1's down GEMV
+    } else if (p->lo.norm_split) {
       const float* yp = nullptr;
       float a_prev = 0.0f;
       if (y_in_partials && l > 0) {
@@ -930,7 +971,7 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
         a_prev = p->s_h[l - 1] * p->s_d[l - 1];
       }
       KERNEL_CHECK(launch_add_sumsq(p->r(l), p->y(l), yp, p->lo.split_dn, a_prev, p->y(l), p->r(l + 1), p->sqp(), M,
-                                    H, s),
+                                    H, s, p->lo.dn_quad ? 1 : 0),
                    "add_sumsq");
     } else if (!fused) {
       const float* yp = nullptr;
@@ -956,7 +997,8 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
                                             p->d.eps, inv_x, a_g, a_u, inv_h, s), "gemv_gateup_fused");
     }
     else if (p->lo.norm_split)
-      KERNEL_CHECK(launch_gemv_gateup_nq(p->d.act, p->r(l + 1), p->wn(l), p->sqp(), add_sumsq_slices(H), p->d.eps,
+      KERNEL_CHECK(launch_gemv_gateup_nq(p->d.act, p->r(l + 1), p->wn(l), p->sqp(),
+                                         p->lo.dn_quad ? H / 4 : add_sumsq_slices(H), p->d.eps,
                                          inv_x, p->xq(l), p->wgu(l), p->hq(l), M, H, I, p->lo.s_gu, a_g, a_u, inv_h,
                                          s),
                    "gemv_gateup_nq");
@@ -973,7 +1015,12 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
       KERNEL_CHECK(launch_gemm_gateup(p->d.act, p->lo.cfg_gu, p->fp8_gateup(), p->xq(l), p->wgu(l),
                                       p->hq(l), M, H, npk, a_g, a_u, inv_h, s), "gemm_gateup");
   } else {
-    if (M <= kGemvMaxM)
+    if (p->lo.dn_quad)
+      KERNEL_CHECK(launch_gemv_down_quad(p->hq(l), p->wd(l), p->r(l + 1), p->y(l + 1),
+                                         l + 1 < p->d.L ? p->r(l + 2) : p->z(), p->sqp(), M, I, H, p->lo.s_dn, a_d,
+                                         s),
+                   "gemv_down_quad");
+    else if (M <= kGemvMaxM)
       KERNEL_CHECK(launch_gemv_down(p->hq(l), p->wd(l), p->y(l + 1), p->part(), M, I, H, p->lo.s_dn,
                                     p->lo.k_dn, p->fp8_down(),
                                     a_d, s), "gemv_down");
@@ -1001,13 +1048,15 @@ static frt_status forward_range(frt_plan* p, int lb, int le, hipStream_t s,
     const hipEvent_t* e = ev ? ev + 4 * (l - lb) : nullptr;
     for (int k = 0; k < 3; ++k) {
       if (e) HIP_CHECK(hipEventRecord(e[k], s));
-      frt_status st = launch_layer_kernel(p, l, k, s, split && l > lb);
+      frt_status st = launch_layer_kernel(p, l, k, s, split && l > lb, l > lb);
       if (st != FRT_OK) return st;
     }
     if (e) HIP_CHECK(hipEventRecord(e[3], s));
   }
   const float a_last = p->mx() ? 1.0f : p->s_h[le - 1] * p->s_d[le - 1];
-  if (le == L)
+  if (le == L && p->lo.dn_quad) {
+    // Z = bf16(R + Y) came from the last down GEMV
+  } else if (le == L)
     KERNEL_CHECK(launch_residual_add(p->r(L), p->y(L), p->z(), p->mh(), s, split ? p->part() : nullptr,
                                      p->lo.split_dn, a_last), "residual_add");
   else if (split)
@@ -1138,7 +1187,7 @@ frt_status frt_ffn_time_kernel(frt_plan* p, int32_t which, int32_t reps, void* s
   err = hipEventRecord(e0, s);
   for (int r = 0; r < reps && st == FRT_OK && err == hipSuccess; ++r)
     for (int l = 0; l < p->d.L && st == FRT_OK; ++l)
-      st = launch_layer_kernel(p, l, which, s, down_split(p) && l > 0);
+      st = launch_layer_kernel(p, l, which, s, down_split(p) && l > 0, l > 0);
   if (err == hipSuccess && st == FRT_OK) err = hipEventRecord(e1, s);
   if (err == hipSuccess && st == FRT_OK) err = hipEventSynchronize(e1);
   if (err == hipSuccess && st == FRT_OK) err = hipEventElapsedTime(&ms, e0, e1);

@@ -33,7 +33,7 @@ hipError_t launch_quant_pack_qkv(const uint16_t*, uint8_t*, int, int, float, int
 hipError_t launch_gemv_qkv(const uint8_t*, const uint8_t*, const QkvOut&, int, int, int, hipStream_t);
 hipError_t launch_mm_qkv(int, const uint8_t*, const uint8_t*, const QkvOut&, int, int, int, hipStream_t);
 hipError_t launch_add_sumsq(const uint16_t*, const uint16_t*, const float*, int, float, uint16_t*, uint16_t*, double*,
-                            int, int, hipStream_t);
+                            int, int, hipStream_t, int = 0);
 int add_sumsq_slices(int);
 bool gemv_qkv_nq_supported(int, int, int);
 hipError_t launch_gemv_qkv_nq(const uint16_t*, const uint16_t*, const double*, int, float, float, uint8_t*,

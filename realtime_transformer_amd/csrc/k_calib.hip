@@ -27,10 +27,11 @@ __device__ __forceinline__ float cal_h(float g, float u) {
   return a * u;
 }
 
-// Decode the 16 packed codes of row prow, columns [k0, k0+16) into dst[kk*LD + col].
+// Decode the 16 packed codes of row prow, columns [k0, k0+16) into dst[kk*LD + col]
+// (quad: the column-quad layout of the whole-column down GEMV).
 __device__ __forceinline__ void load_w16(const uint8_t* __restrict__ w, uint32_t prow, uint32_t k0,
-                                         uint32_t K, float* dst, int ld) {
-  const uint4 v = *reinterpret_cast<const uint4*>(w + packed_offset(prow, k0, K));
+                                         uint32_t K, float* dst, int ld, bool quad) {
+  const uint4 v = *reinterpret_cast<const uint4*>(w + (quad ? quad_offset(prow, k0, K) : packed_offset(prow, k0, K)));
   const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -48,7 +49,7 @@ template <int MODE>
 __global__ __launch_bounds__(256) void k_calib_gemm(const float* __restrict__ X,
                                                     const uint8_t* __restrict__ W, void* out,
                                                     float* __restrict__ amax, int rows, int K,
-                                                    int Nout, float s_a, float s_b) {
+                                                    int Nout, float s_a, float s_b, int quad) {
   constexpr bool TWO = MODE == CAL_GEGLU || MODE == CAL_SWIGLU;
   constexpr int LD = 64 + 1;
   __shared__ float xs[32][LD];
@@ -80,8 +81,8 @@ __global__ __launch_bounds__(256) void k_calib_gemm(const float* __restrict__ X,
       } else {
         prow_a = (uint32_t)n;
       }
-      load_w16(W, prow_a, (uint32_t)(k0 + kk), (uint32_t)K, &wa[kk][tid >> 1], LD);
-      if (TWO) load_w16(W, prow_b, (uint32_t)(k0 + kk), (uint32_t)K, &wb[kk][tid >> 1], LD);
+      load_w16(W, prow_a, (uint32_t)(k0 + kk), (uint32_t)K, &wa[kk][tid >> 1], LD, quad != 0);
+      if (TWO) load_w16(W, prow_b, (uint32_t)(k0 + kk), (uint32_t)K, &wb[kk][tid >> 1], LD, false);
     }
     __syncthreads();
 #pragma unroll 8
@@ -137,21 +138,21 @@ hipError_t launch_calib_gateup(int act, const float* x, const uint8_t* w, float*
   dim3 grid(I / 64, (rows + 63) / 64);
   if (act == CAL_GEGLU)
     hipLaunchKernelGGL(k_calib_gemm<CAL_GEGLU>, grid, dim3(256), 0, s, x, w, (void*)h, amax, rows,
-                       K, I, s_g, s_u);
+                       K, I, s_g, s_u, 0);
   else if (act == CAL_SWIGLU)
     hipLaunchKernelGGL(k_calib_gemm<CAL_SWIGLU>, grid, dim3(256), 0, s, x, w, (void*)h, amax,
-                       rows, K, I, s_g, s_u);
+                       rows, K, I, s_g, s_u, 0);
   else
     hipLaunchKernelGGL(k_calib_gemm<CAL_GELU>, grid, dim3(256), 0, s, x, w, (void*)h, amax, rows,
-                       K, I, s_u, 0.0f);
+                       K, I, s_u, 0.0f, 0);
   return hipGetLastError();
 }
 
 hipError_t launch_calib_down(const float* h, const uint8_t* w, uint16_t* y, int rows, int K, int H,
-                             float s_d, hipStream_t s) {
+                             float s_d, hipStream_t s, int quad) {
   dim3 grid(H / 64, (rows + 63) / 64);
   hipLaunchKernelGGL(k_calib_gemm<CAL_DOWN>, grid, dim3(256), 0, s, h, w, (void*)y, nullptr, rows,
-                     K, H, s_d, 0.0f);
+                     K, H, s_d, 0.0f, quad);
   return hipGetLastError();
 }
 

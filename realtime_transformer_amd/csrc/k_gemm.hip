@@ -207,7 +207,12 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup(const uint8_t* __restric
 // i, so every wave keeps a step in flight while it computes (the register
 // cost of 2 NB blocks); otherwise each step's loads are issued right before
 // its MFMAs.
-template <int ACT, int W, int NB, bool PIPE, int NQC>
+// WIDE: the slice sums are the whole-column down GEMV's, one per four
+// columns (G = K / 4, more than a lane each): the workgroup's threads load
+// them as 16-byte pairs, add their pairs per row in index order, the waves'
+// totals meet in LDS and are added in wave order (fp64 throughout).
+constexpr int kNqWidePairs = 4;  // 16-byte slice-sum loads per thread: M * G <= 8 * 64 * W
+template <int ACT, int W, int NB, bool PIPE, int NQC, bool WIDE = false, int NP = kNqWidePairs>
 __global__ __launch_bounds__(W * 64) void k_gemv_gateup_nq(const NormQ nq, const uint8_t* __restrict__ w,
                                                            uint8_t* __restrict__ hq, int M, int K, int I,
                                                            float alpha_g, float alpha_u, float inv_h) {
@@ -225,7 +230,17 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup_nq(const NormQ nq, const
   const uint8_t* wu = w + (size_t)(GATED ? 2 * p + 1 : p) * KB * 2048 + lane * 16;
 
   // (1) activation-side loads: the row's slice sums (lane i < M*G holds
-  // sum i) and the r' / w_norm chunks of this wave's K blocks
+  // sum i; WIDE: this thread's pairs) and the r' / w_norm chunks of this
+  // wave's K blocks
+  double2 sqp[WIDE ? NP : 1];
+  if (WIDE) {
+    const int npairs = (M * nq.G) >> 1;
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int i = (int)threadIdx.x + j * W * 64;
+      sqp[j] = reinterpret_cast<const double2*>(nq.sq)[i < npairs ? i : npairs - 1];
+    }
+  }
   NormQWave<NQC> nqw;
   nqw.init(nq, M, K, kb0, kb1, lane);  // kb1 > kb0: W <= K / 128
   nqw.load(nq, 0, lane);
@@ -249,7 +264,37 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup_nq(const NormQ nq, const
   __builtin_amdgcn_sched_barrier(0);
 
   // (3) 1/rms of row `lane` (lanes < M), then the codes of this wave's range
-  const float inv_rms = nqw.inv_rms(nq, lane);
+  float inv_rms;
+  if (WIDE) {
+    __shared__ double wsum[W][4];
+    const int npairs = (M * nq.G) >> 1;
+    double rs[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int i = (int)threadIdx.x + j * W * 64;
+      const int m = (2 * i) / nq.G;  // a pair never straddles rows (G even)
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm)
+        if (i < npairs && m == mm) {
+          rs[mm] += sqp[j].x;
+          rs[mm] += sqp[j].y;
+        }
+    }
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
+      if (mm >= M) break;  // uniform
+      const double t = wave_sum_f64(rs[mm]);
+      if (lane == 0) wsum[wave][mm] = t;
+    }
+    __syncthreads();
+    const int mrow = lane < M ? lane : 0;
+    double tot = 0.0;
+#pragma unroll
+    for (int v = 0; v < W; ++v) tot += wsum[v][mrow & 3];
+    inv_rms = (float)(1.0 / sqrt(tot / (double)K + (double)nq.eps));
+  } else {
+    inv_rms = nqw.inv_rms(nq, lane);
+  }
   const bool store_xq = blockIdx.x == 0;
   nqw.quant(nq, 0, lane, inv_rms, xrow, store_xq);
   for (int c0 = NQC * 64; c0 < nqw.nch; c0 += NQC * 64) {
@@ -685,6 +730,141 @@ __global__ __launch_bounds__(W * 64) void k_gemv_down(const uint8_t* __restrict_
   }
 }
 
+// Whole-column decode down GEMV (M <= 4), down matrix in the column-quad
+// layout (quad_offset): one workgroup per four output columns reads those
+// columns over all of K, so it owns their sums and no split-K partials or
+// norm kernel follow it.  Each MFMA takes the four K quarters side by side:
+// operand row 4 p' + m' is activation row m' over quarter p', operand column
+// 4 p + c is weight column c over quarter p, so the products with p' == p
+// are the quarters' partial dot products and the others are discarded
+// (lanes 20 p + c hold quarter p of column c, row m in element m).  The
+// epilogue forms, for its columns,
+//   Y = bf16(alpha_d * sum),  R' = bf16(R + Y)  (R' and Z alike: r_out),
+//   and the fp64 sum of R'^2 over the four columns, slice c4 of row m of
+//   sq [M][N / 4] (the next layer's split norm reads these slices);
+// r_out == nullptr stores Y only.  Steps of 64 K elements per quarter (1 KiB
+// of weights, 16 bytes per lane and 16 activation bytes), two MFMAs each,
+// NB steps per load stage, stages pipelined over two register sets as in
+// k_gemv_gateup_nq; rows m' >= M read row 0, whose products reach only
+// discarded rows.
+template <int W, int NB, bool PIPE>
+__global__ __launch_bounds__(W * 64) void k_gemv_down_quad(const uint8_t* __restrict__ hq,
+                                                           const uint8_t* __restrict__ w,
+                                                           const uint16_t* __restrict__ r_in,
+                                                           uint16_t* __restrict__ y, uint16_t* __restrict__ r_out,
+                                                           double* __restrict__ sq, int M, int K, int N,
+                                                           float alpha_d) {
+  __shared__ v4f red[W][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c4 = blockIdx.x;
+  const int T = K >> 8, Kq = K >> 2;
+  const int t0 = wave * T / W, t1 = (wave + 1) * T / W;
+  const int part = (lane & 15) >> 2, mr = lane & 3;
+  const uint8_t* wp = w + (size_t)c4 * T * 1024 + lane * 16;
+  const uint8_t* xr = hq + (size_t)(mr < M ? mr : 0) * K + part * Kq + (lane >> 4) * 16;
+  const int nstep = t1 - t0;
+  uint4 wA[NB], xA[NB], wB[NB], xB[NB];
+  // steps i0 .. i0 + NB - 1 (indices clamped to the range: a clamped step is
+  // loaded, not used)
+  auto load_step = [&](uint4 (&ww)[NB], uint4 (&xx)[NB], int i0) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int t = t0 + (i0 + j < nstep ? i0 + j : nstep - 1);
+      ww[j] = ld16_nt(wp + (size_t)t * 1024);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int t = t0 + (i0 + j < nstep ? i0 + j : nstep - 1);
+      xx[j] = ld16(xr + t * 64);
+    }
+  };
+  v4f acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+  auto mma_step = [&](uint4 (&ww)[NB], uint4 (&xx)[NB], int i0) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (PIPE) {
+        asm volatile("" : "+v"(ww[j].x), "+v"(ww[j].y), "+v"(ww[j].z), "+v"(ww[j].w));
+        asm volatile("" : "+v"(xx[j].x), "+v"(xx[j].y), "+v"(xx[j].z), "+v"(xx[j].w));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (i0 + j < nstep) {  // wave-uniform
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(e4m3x8_to_f16(xx[j].x, xx[j].y), e4m3x8_to_f16(ww[j].x, ww[j].y),
+                                                      acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(e4m3x8_to_f16(xx[j].z, xx[j].w), e4m3x8_to_f16(ww[j].z, ww[j].w),
+                                                      acc1, 0, 0, 0);
+      }
+    }
+  };
+  if (nstep > 0) {
+    load_step(wA, xA, 0);
+    if (PIPE) {
+      int i = 0;
+      for (; i + 2 * NB < nstep; i += 2 * NB) {
+        load_step(wB, xB, i + NB);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_step(wA, xA, i);
+        load_step(wA, xA, i + 2 * NB);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_step(wB, xB, i + NB);
+      }
+      if (i + NB < nstep) {
+        load_step(wB, xB, i + NB);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_step(wA, xA, i);
+        mma_step(wB, xB, i + NB);
+      } else {
+        mma_step(wA, xA, i);
+      }
+    } else {
+      for (int i = 0; i < nstep; i += NB) {
+        if (i != 0) load_step(wA, xA, i);
+        mma_step(wA, xA, i);
+      }
+    }
+  }
+  v4f acc = acc0 + acc1;
+  if (W > 1) {
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    acc = red[0][lane];
+#pragma unroll
+    for (int v = 1; v < W; ++v) acc += red[v][lane];
+  }
+  // column c = lane & 3 of lanes 0..3: its quarters in order, then the epilogue
+  const int c = lane & 3;
+  float tot[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const float q0 = __shfl(acc[m], c, 64), q1 = __shfl(acc[m], 20 + c, 64);
+    const float q2 = __shfl(acc[m], 40 + c, 64), q3 = __shfl(acc[m], 60 + c, 64);
+    tot[m] = ((q0 + q1) + q2) + q3;
+  }
+  const size_t col = (size_t)c4 * 4 + c;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    if (m >= M) break;  // uniform
+    const uint32_t yb = f32_to_bf16(tot[m] * alpha_d);
+    double d = 0.0;
+    if (lane < 4) {
+      y[(size_t)m * N + col] = (uint16_t)yb;
+      if (r_out) {
+        const float rf = __uint_as_float((uint32_t)r_in[(size_t)m * N + col] << 16);
+        const uint32_t rb = f32_to_bf16(rf + __uint_as_float(yb << 16));
+        r_out[(size_t)m * N + col] = (uint16_t)rb;
+        const double rd = (double)__uint_as_float(rb << 16);
+        d = rd * rd;
+      }
+    }
+    if (r_out) {
+      const double d1 = __shfl(d, 1, 64), d2 = __shfl(d, 2, 64), d3 = __shfl(d, 3, 64);
+      if (lane == 0) sq[(size_t)m * (N >> 2) + c4] = ((d + d1) + d2) + d3;
+    }
+  }
+}
+
 // ===========================================================================
 // GEMM path (M > 16)
 // ===========================================================================
@@ -1112,34 +1292,52 @@ static bool gemv_pipe(const char* env, bool dflt) {
   return (e && *e) ? atoi(e) != 0 : dflt;
 }
 
-template <int W, int NB, bool PIPE, int NQC>
+template <int W, int NB, bool PIPE, int NQC, bool WIDE, int NP = kNqWidePairs>
 static void gemv_gateup_nq_wnpc(int act, const NormQ& nq, const uint8_t* w, uint8_t* hq, int M, int K, int I,
                                 float a_g, float a_u, float inv_h, hipStream_t s) {
   dim3 grid(I / 16), block(W * 64);
   const size_t lds = (size_t)M * K;
   if (act == GU_GEGLU)
-    hipLaunchKernelGGL((k_gemv_gateup_nq<GU_GEGLU, W, NB, PIPE, NQC>), grid, block, lds, s, nq, w, hq, M, K, I, a_g,
-                       a_u, inv_h);
+    hipLaunchKernelGGL((k_gemv_gateup_nq<GU_GEGLU, W, NB, PIPE, NQC, WIDE, NP>), grid, block, lds, s, nq, w, hq, M,
+                       K, I, a_g, a_u, inv_h);
   else if (act == GU_SWIGLU)
-    hipLaunchKernelGGL((k_gemv_gateup_nq<GU_SWIGLU, W, NB, PIPE, NQC>), grid, block, lds, s, nq, w, hq, M, K, I,
-                       a_g, a_u, inv_h);
+    hipLaunchKernelGGL((k_gemv_gateup_nq<GU_SWIGLU, W, NB, PIPE, NQC, WIDE, NP>), grid, block, lds, s, nq, w, hq, M,
+                       K, I, a_g, a_u, inv_h);
   else
-    hipLaunchKernelGGL((k_gemv_gateup_nq<GU_GELU, W, NB, PIPE, NQC>), grid, block, lds, s, nq, w, hq, M, K, I, a_g,
-                       a_u, inv_h);
+    hipLaunchKernelGGL((k_gemv_gateup_nq<GU_GELU, W, NB, PIPE, NQC, WIDE, NP>), grid, block, lds, s, nq, w, hq, M,
+                       K, I, a_g, a_u, inv_h);
 }
 
-template <int W, int NB, bool PIPE>
+template <int W, int NB, bool PIPE, bool WIDE = false>
 static void gemv_gateup_nq_wnp(int act, const NormQ& nq, const uint8_t* w, uint8_t* hq, int M, int K, int I,
                                float a_g, float a_u, float inv_h, hipStream_t s) {
   // chunks of the largest wave range: M x ceil(K blocks / W) x 16
   const int chunks = M * (((K >> 7) + W - 1) / W) * 16;
-  if (chunks > 128 && chunks <= 192) gemv_gateup_nq_wnpc<W, NB, PIPE, 3>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
-  else gemv_gateup_nq_wnpc<W, NB, PIPE, 2>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
+  // WIDE: two slice-sum pairs per thread where they cover the rows, else four
+  if constexpr (WIDE) {
+    const bool np2 = (M * nq.G) / 2 <= 2 * W * 64;
+    if (chunks > 128 && chunks <= 192) {
+      if (np2) gemv_gateup_nq_wnpc<W, NB, PIPE, 3, true, 2>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
+      else gemv_gateup_nq_wnpc<W, NB, PIPE, 3, true>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
+    } else {
+      if (np2) gemv_gateup_nq_wnpc<W, NB, PIPE, 2, true, 2>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
+      else gemv_gateup_nq_wnpc<W, NB, PIPE, 2, true>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
+    }
+  } else {
+    if (chunks > 128 && chunks <= 192) gemv_gateup_nq_wnpc<W, NB, PIPE, 3, false>(act, nq, w, hq, M, K, I, a_g, a_u,
+                                                                                  inv_h, s);
+    else gemv_gateup_nq_wnpc<W, NB, PIPE, 2, false>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
+  }
 }
 
 template <int W>
 static void gemv_gateup_nq_w(int act, const NormQ& nq, const uint8_t* w, uint8_t* hq, int M, int K, int I,
                              float a_g, float a_u, float inv_h, hipStream_t s) {
+  if (nq.G > kNqMaxSlices) {
+    // the whole-column down GEMV's slice sums (one step per K block, pipelined)
+    gemv_gateup_nq_wnp<W, 1, true, true>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
+    return;
+  }
   const bool pipe = gemv_pipe("FRT_GEMV_PIPE_GATEUP", true);
   if (gemv_nb("FRT_GEMV_NB_GATEUP", 1) == 2) {
     if (pipe) gemv_gateup_nq_wnp<W, 2, true>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
@@ -1150,15 +1348,24 @@ static void gemv_gateup_nq_w(int act, const NormQ& nq, const uint8_t* w, uint8_t
   }
 }
 
-// Whether k_gemv_gateup_nq takes the shape (frt_normq.h).
+// Whether k_gemv_gateup_nq takes the shape (frt_normq.h), and with slice sums
+// per four columns (G = K / 4) at W waves.
 bool gemv_nq_supported(int M, int K, int G) { return normq_shape_ok(M, K, G); }
+bool gemv_nq_wide_supported(int M, int K, int W) {
+  const int G = K / 4;
+  return normq_shape_ok(M, K, 1) && M <= 4 && G > kNqMaxSlices && G % 2 == 0 &&
+         M * G <= 2 * kNqWidePairs * 64 * W;
+}
 
 // gate/up GEMV from r' and the slice sums (k_add_sumsq) instead of XQ; the
 // codes it forms are stored to xq_out.
 hipError_t launch_gemv_gateup_nq(int act, const uint16_t* r, const uint16_t* w_norm, const double* sq, int G,
                                  float eps, float inv_x, uint8_t* xq_out, const uint8_t* w, uint8_t* hq, int M, int K,
                                  int I, int W, float alpha_g, float alpha_u, float inv_h, hipStream_t s) {
-  if (!gemv_nq_supported(M, K, G) || G < 1 || I % 16 || W > K / 128) return hipErrorInvalidValue;
+  const bool wide = G > kNqMaxSlices;
+  if ((wide ? !(G == K / 4 && gemv_nq_wide_supported(M, K, W)) : !gemv_nq_supported(M, K, G)) || G < 1 || I % 16 ||
+      W > K / 128)
+    return hipErrorInvalidValue;
   const NormQ nq{r, w_norm, sq, G, eps, inv_x, xq_out};
   switch (W) {
     case 1: gemv_gateup_nq_w<1>(act, nq, w, hq, M, K, I, alpha_g, alpha_u, inv_h, s); break;
@@ -1305,6 +1512,46 @@ hipError_t launch_gemv_down(const uint8_t* hq, const uint8_t* w, uint16_t* y, fl
                      : gemv_down_t<true, 16>(hq, w, y, part, M, K, N, W, S, alpha_d, s);
   return cols == 8 ? gemv_down_t<false, 8>(hq, w, y, part, M, K, N, W, S, alpha_d, s)
                    : gemv_down_t<false, 16>(hq, w, y, part, M, K, N, W, S, alpha_d, s);
+}
+
+// Whole-column down GEMV (M <= 4, K % 256 == 0, N % 4 == 0, W at most
+// K / 256): Y, and with r_out R' = bf16(R + Y) and the quad slice sums.
+// FRT_GEMV_PIPE_DOWN=0 runs it unpipelined.
+bool gemv_down_quad_supported(int M, int K, int N) {
+  return M >= 1 && M <= 4 && K >= 256 && K % 256 == 0 && N >= 4 && N % 4 == 0;
+}
+
+hipError_t launch_gemv_down_quad(const uint8_t* hq, const uint8_t* w, const uint16_t* r_in, uint16_t* y,
+                                 uint16_t* r_out, double* sq, int M, int K, int N, int W, float alpha_d,
+                                 hipStream_t s) {
+  if (!gemv_down_quad_supported(M, K, N) || W < 1 || W > (K >> 8) || (r_out && (!r_in || !sq)))
+    return hipErrorInvalidValue;
+  const bool pipe = gemv_pipe("FRT_GEMV_PIPE_DOWN", true);
+  // one 1 KiB step per stage by default (measured at M=1, N=5120, K=17408 on
+  // eight waves: 16.0 us against 16.4 with two steps and 18.0 with four)
+  const int nb = gemv_nb("FRT_GEMV_NB_DOWN_QUAD", 1);
+  const dim3 grid(N / 4), block(W * 64);
+#define FRT_DQ(WV, B, P) \
+  hipLaunchKernelGGL((k_gemv_down_quad<WV, B, P>), grid, block, 0, s, hq, w, r_in, y, r_out, sq, M, K, N, alpha_d)
+#define FRT_DQW(WV)                   \
+  if (nb == 2) {                      \
+    if (pipe) FRT_DQ(WV, 2, true);    \
+    else FRT_DQ(WV, 2, false);        \
+  } else {                            \
+    if (pipe) FRT_DQ(WV, 1, true);    \
+    else FRT_DQ(WV, 1, false);        \
+  }
+  switch (W) {
+    case 1: FRT_DQW(1); break;
+    case 2: FRT_DQW(2); break;
+    case 4: FRT_DQW(4); break;
+    case 8: FRT_DQW(8); break;
+    case 16: FRT_DQW(16); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef FRT_DQW
+#undef FRT_DQ
+  return hipGetLastError();
 }
 
 // Multi-tile GEMV launchers (16 < M <= 64): W in {4, 8} waves (at least MT).

@@ -292,16 +292,17 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_quant(
 // the one-pass sum of the whole row differ only where the row's squares span
 // more than fp64's 53 bits.  Spread over H/512 workgroups, the row's loads
 // are issued by as many CUs (one CU's request queue was the latency of the
-// one-workgroup form).
+// one-workgroup form).  quad != 0: the sums are over 4-element slices
+// instead (sq_out[m * H/4 + k/4], the slices of the whole-column down GEMV).
 template <int SMAX>
 __global__ __launch_bounds__(64) void k_add_sumsq(const uint16_t* __restrict__ r_prev,
                                                   const uint16_t* __restrict__ y_prev,
                                                   const float* __restrict__ y_part, int S, float alpha_d,
                                                   uint16_t* __restrict__ y_store, uint16_t* __restrict__ r_out,
-                                                  double* __restrict__ sq_out, int M, int H) {
+                                                  double* __restrict__ sq_out, int M, int H, int quad) {
   const int m = blockIdx.y, g = blockIdx.x;
   const int ch = g * 64 + (int)threadIdx.x;
-  double sq = 0.0;
+  double sq = 0.0, sq4[2] = {0.0, 0.0};
   if (ch < H / 8) {
     const size_t o = (size_t)m * H + (size_t)ch * 8;
     const uint4 rv = *reinterpret_cast<const uint4*>(r_prev + o);
@@ -342,9 +343,18 @@ __global__ __launch_bounds__(64) void k_add_sumsq(const uint16_t* __restrict__ r
       const double dlo = (double)bf16_lo(o4[j]), dhi = (double)bf16_hi(o4[j]);
       sq += dlo * dlo;
       sq += dhi * dhi;
+      sq4[j >> 1] += dlo * dlo;
+      sq4[j >> 1] += dhi * dhi;
     }
     *reinterpret_cast<uint4*>(r_out + o) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+    if (quad) {
+      // slices of four elements (those of the whole-column down GEMV)
+      double* qo = sq_out + (size_t)m * (H / 4) + 2 * ch;
+      qo[0] = sq4[0];
+      qo[1] = sq4[1];
+    }
   }
+  if (quad) return;  // (uniform)
   sq = wave_sum_f64(sq);
   if (threadIdx.x == 0) sq_out[(size_t)m * gridDim.x + g] = sq;
 }
@@ -500,12 +510,12 @@ int add_sumsq_slices(int H) { return (H / 8 + 63) / 64; }
 
 hipError_t launch_add_sumsq(const uint16_t* r_prev, const uint16_t* y_prev, const float* y_part, int S,
                             float alpha_d, uint16_t* y_store, uint16_t* r_out, double* sq_out, int M, int H,
-                            hipStream_t s) {
+                            hipStream_t s, int quad) {
   if (M < 1 || H % 8 || (y_part && (S < 1 || !y_store))) return hipErrorInvalidValue;
   const dim3 grid(add_sumsq_slices(H), M);
 #define FRT_SUMSQ(SM)                                                                                        \
   hipLaunchKernelGGL((k_add_sumsq<SM>), grid, dim3(64), 0, s, r_prev, y_prev, y_part, S, alpha_d, y_store, r_out, \
-                     sq_out, M, H)
+                     sq_out, M, H, quad)
   if (!y_part || S <= 4)
     FRT_SUMSQ(4);
   else if (S <= 8)

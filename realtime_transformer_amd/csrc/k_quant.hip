@@ -73,9 +73,10 @@ __global__ __launch_bounds__(256) void k_quant_pack(const uint16_t* __restrict__
     q[j] = e4m3x4((bf16_lo(v[2 * j]) * bf16_lo(c[2 * j])) * inv, (bf16_hi(v[2 * j]) * bf16_hi(c[2 * j])) * inv,
                   (bf16_lo(v[2 * j + 1]) * bf16_lo(c[2 * j + 1])) * inv,
                   (bf16_hi(v[2 * j + 1]) * bf16_hi(c[2 * j + 1])) * inv);
-  const uint32_t prow = mode == 0 ? n : (mode == 1 ? gate_row(n) : up_row_gated(n));
-  *reinterpret_cast<uint4*>(dst + packed_offset(prow, k0, (uint32_t)K)) =
-      make_uint4(q[0], q[1], q[2], q[3]);
+  // mode 3: the column-quad layout of the whole-column down GEMV
+  const uint32_t prow = mode == 0 || mode == 3 ? n : (mode == 1 ? gate_row(n) : up_row_gated(n));
+  const size_t off = mode == 3 ? quad_offset(n, k0, (uint32_t)K) : packed_offset(prow, k0, (uint32_t)K);
+  *reinterpret_cast<uint4*>(dst + off) = make_uint4(q[0], q[1], q[2], q[3]);
 }
 
 hipError_t launch_amax_bf16(const uint16_t* w, size_t n, float* out, hipStream_t s, const uint16_t* colw,

@@ -156,6 +156,10 @@ class FFNPlan:
         """MXFP4 plans: HQ slot l as (codes [M][I/2], exponents [M][I/32]), as xq_mx."""
         return self._mx_slot(self.io.hq_slots + l * self.io.stride_hq, self.I)
 
+    def path(self) -> int:
+        """FRT_PATH_* bits of the kernels this plan's forward runs."""
+        return _abi.frt_ffn_plan_path(self.plan)
+
     def export_codes(self, layer: int, which: int) -> np.ndarray:
         rows, cols = (self.H, self.I) if which == 2 else (self.I, self.H)
         return _abi.frt_export_weight_codes(self.plan, layer, which, rows, cols)

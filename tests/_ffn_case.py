@@ -193,6 +193,7 @@ class CaseReport:
     saturated_codes: int = 0
     subnormal_codes: int = 0    # E4M3 codes with a zero exponent field and a nonzero mantissa
     zero_xq_rows: int = 0       # rows of XQ[0] that are all zero codes
+    path: int = 0               # FRT_PATH_* bits of the plan
     seconds: float = 0.0
 
 
@@ -220,6 +221,7 @@ def run_case(cfg: FFNConfig, rows: Optional[Sequence[int]] = None, cal_rows: Opt
         cfg.name, M, H, I, L, act, len(rows), cal[0][0].shape[0]))
 
     plan = FFNPlan(M, H, I, L, act, cfg.eps, flags=flags)
+    rep.path = plan.path()
     try:
         weight_scales = []
         norm_w = {}
@@ -323,6 +325,26 @@ def run_case(cfg: FFNConfig, rows: Optional[Sequence[int]] = None, cal_rows: Opt
         plan.sync()
         assert np.array_equal(to_np_u16(plan.z()), z_graph), "eager forward differs from graph replay"
         assert np.array_equal(to_np_u16(plan.y_slot(L)), yl_graph), "eager Y[L] differs from replay"
+        # chain consistency of the free-running forward: every layer's R' and
+        # XQ follow from the R and Y slots it started from (the oracle's
+        # residual add and norm applied to the GPU's own slots), R' bit for
+        # bit and XQ under the code rule, and Z from R[L] and Y[L].  This
+        # holds on every path, including where a down GEMV forms the next
+        # layer's R' and norm slice sums itself.
+        ridx = torch.as_tensor(rows, device=plan.device)
+        for l in range(L):
+            r_in = to_np_u16(plan.r_slot(l)[ridx])
+            y_in = to_np_u16(plan.y_slot(l)[ridx])
+            inv_x = np.float32(np.float32(1.0) / np.float32(orc.s_x[l]))
+            r_ref, x_pre, _ = oracle.add_rmsnorm_quant(r_in, y_in, norm_w[l], cfg.eps, 1.0, mod=mods[l])
+            nb = int(np.count_nonzero(to_np_u16(plan.r_slot(l + 1)[ridx]) != r_ref))
+            assert nb == 0, "free-running layer %d residual: %d bf16 mismatches against its own R and Y" % (l, nb)
+            _, _, xq_ref = oracle.add_rmsnorm_quant(r_in, y_in, norm_w[l], cfg.eps, float(inv_x), mod=mods[l])
+            xs = code_stats(to_np_u8(plan.xq_slot(l)[ridx]), xq_ref, (x_pre * inv_x).astype(np.float32))
+            check_codes("free-running layer %d XQ" % l, xs, boundary_rule=True)
+        z_own = oracle.final_hidden(to_np_u16(plan.r_slot(L)[ridx]), to_np_u16(plan.y_slot(L)[ridx]))
+        nb = int(np.count_nonzero(z_graph[rows] != z_own))
+        assert nb == 0, "Z: %d bf16 mismatches against the GPU's own R[L] + Y[L]" % nb
         # saturation invariant over every quantised slot
         for l in range(L):
             for t in (plan.xq_slot(l), plan.hq_slot(l)):

@@ -109,13 +109,16 @@ def test_small_shapes_fused_norm(spec):
 
 @pytest.mark.parametrize("spec", [(107, 1, 256, 2048, 2, ACT_SWIGLU), (108, 5, 384, 2048, 3, ACT_GEGLU_TANH)],
                          ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
-def test_small_shapes_gemv_down_split(spec):
+def test_small_shapes_gemv_down_split(spec, monkeypatch):
     # decode shapes whose down GEMV splits K over two workgroups per column
-    # group: the partial sums meet in the next layer's norm kernel
+    # group: the partial sums meet in the next layer's norm kernel (M <= 4
+    # takes the whole-column down GEMV by default: switched off here)
+    monkeypatch.setenv("FRT_DOWN_QUAD", "0")
     idx, M, H, I, L, act = spec
     cfg = FFNConfig(idx, "small_split_%d" % idx, M, H, I, L, act)
     rep = run_case(cfg)
     log(str(rep))
+    assert rep.path & _abi.FRT_PATH_DOWN_SPLIT_K
 
 
 @pytest.mark.parametrize("spec", [SMALL[0], SMALL[1], SMALL[2], (107, 1, 256, 2048, 2, ACT_SWIGLU)],
@@ -137,10 +140,45 @@ def test_small_shapes_many_down_splits(split, spec, monkeypatch):
     # the decode down GEMV split into 8, 17 or 32 parts: the slice-sum kernel
     # loads every split's partial rows before adding them in split order
     monkeypatch.setenv("FRT_GEMV_DOWN_SPLIT", str(split))
+    monkeypatch.setenv("FRT_DOWN_QUAD", "0")
     idx, M, H, I, L, act = spec
     cfg = FFNConfig(idx, "small_splits%d_%d" % (split, idx), M, H, I, L, act)
     rep = run_case(cfg)
     log(str(rep))
+    assert rep.path & _abi.FRT_PATH_DOWN_SPLIT_K
+
+
+DOWN_QUAD_VARIANTS = [
+    {},
+    {"FRT_GEMV_PIPE_DOWN": "0"},
+    {"FRT_GEMV_NB_DOWN_QUAD": "2"},
+    {"FRT_GEMV_NB_DOWN_QUAD": "2", "FRT_GEMV_PIPE_DOWN": "0"},
+    {"FRT_GEMV_WAVES_DOWN_QUAD": "1"},
+    {"FRT_GEMV_WAVES_DOWN_QUAD": "2"},
+    {"FRT_GEMV_WAVES_DOWN_QUAD": "4"},
+    {"FRT_GEMV_WAVES_DOWN_QUAD": "16"},
+]
+
+
+@pytest.mark.parametrize("env", DOWN_QUAD_VARIANTS, ids=lambda e: "_".join("%s%s" % (k[9:], v) for k, v in e.items())
+                         or "default")
+@pytest.mark.parametrize("spec", [(146, 2, 640, 768, 3, ACT_GEGLU_TANH), (147, 4, 512, 1280, 2, ACT_GELU_TANH),
+                                  (148, 3, 1024, 2304, 3, ACT_SWIGLU), (149, 1, 2048, 4352, 2, ACT_SWIGLU)],
+                         ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
+def test_small_shapes_down_quad(spec, env, monkeypatch):
+    # the whole-column decode down GEMV (M <= 4; the default there): 3, 5, 9
+    # and 17 K steps per column quad over 1-16 waves (uneven wave ranges),
+    # one or two steps per stage, pipelined or not; its epilogue forms the
+    # next layer's R' and
+    # four-column slice sums, which the free-running chain check and the
+    # next layer's XQ test
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    idx, M, H, I, L, act = spec
+    cfg = FFNConfig(idx, "small_quad_%d" % idx, M, H, I, L, act)
+    rep = run_case(cfg)
+    log(str(rep))
+    assert rep.path & _abi.FRT_PATH_DOWN_WHOLE_COLUMN
 
 
 GEMV_VARIANTS = [
@@ -165,6 +203,8 @@ GEMV_VARIANTS = [
                                   (123, 1, 2048, 2304, 2, ACT_SWIGLU)],
                          ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
 def test_small_shapes_gemv_launch_variants(spec, env, monkeypatch):
+    # (the split-K down GEMV at every M: the whole-column one is switched off)
+    monkeypatch.setenv("FRT_DOWN_QUAD", "0")
     for k, v in env.items():
         monkeypatch.setenv(k, v)
     idx, M, H, I, L, act = spec
@@ -177,22 +217,29 @@ def test_small_shapes_gemv_launch_variants(spec, env, monkeypatch):
                                         ("2", (125, 3, 1024, 1024, 2, ACT_GEGLU_TANH)),
                                         ("4", (126, 1, 5120, 512, 2, ACT_GELU_TANH))],
                          ids=lambda v: "W%s" % v if isinstance(v, str) else "M%d_H%d_I%d" % (v[1], v[2], v[3]))
-def test_small_shapes_norm_quant_three_chunks(waves, spec, monkeypatch):
+@pytest.mark.parametrize("quad", ["1", "0"], ids=["wide_slices", "slices"])
+def test_small_shapes_norm_quant_three_chunks(waves, spec, quad, monkeypatch):
     # decode gate/up waves whose K range holds 129-192 activation chunks:
-    # the norm-quantising prologue loads three per lane (one round trip)
+    # the norm-quantising prologue loads three per lane (one round trip);
+    # with the slice sums of the whole-column down GEMV (one per four
+    # columns) or of the slice-sum kernel
     monkeypatch.setenv("FRT_GEMV_WAVES_GATEUP", waves)
+    monkeypatch.setenv("FRT_DOWN_QUAD", quad)
     idx, M, H, I, L, act = spec
-    cfg = FFNConfig(idx, "small_nqc3_%d" % idx, M, H, I, L, act)
+    cfg = FFNConfig(idx, "small_nqc3_%d_%s" % (idx, quad), M, H, I, L, act)
     rep = run_case(cfg)
     log(str(rep))
+    assert bool(rep.path & _abi.FRT_PATH_DOWN_WHOLE_COLUMN) == (quad == "1")
 
 
 @pytest.mark.parametrize("spec", [(117, 16, 1024, 512, 2, ACT_GEGLU_TANH), (118, 2, 640, 512, 3, ACT_SWIGLU),
                                   (119, 1, 8192, 1024, 2, ACT_GELU_TANH)],
                          ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
-def test_small_shapes_split_norm_slices(spec):
+def test_small_shapes_split_norm_slices(spec, monkeypatch):
     # the split norm with several slice sums per row (up to 16), a partial
-    # last slice, and waves with more chunks than one load group
+    # last slice, and waves with more chunks than one load group (the slice
+    # sums of k_add_sumsq: the whole-column down GEMV is switched off)
+    monkeypatch.setenv("FRT_DOWN_QUAD", "0")
     idx, M, H, I, L, act = spec
     cfg = FFNConfig(idx, "small_splitnorm_%d" % idx, M, H, I, L, act)
     rep = run_case(cfg)
@@ -317,8 +364,19 @@ def test_vlm_prefix_m788_full_size_fp8_down():
 
 @pytest.mark.timeout(900)
 def test_llm_decode_m1_full_size():
+    # the benchmark's launch configuration: the whole-column down GEMV
     rep = run_case(CONFIGS[4])
     log(str(rep))
+    assert rep.path & _abi.FRT_PATH_DOWN_WHOLE_COLUMN
+
+
+@pytest.mark.timeout(900)
+def test_llm_decode_m1_full_size_split_down(monkeypatch):
+    # the same chain on the split-K down GEMV and the slice-sum kernel
+    monkeypatch.setenv("FRT_DOWN_QUAD", "0")
+    rep = run_case(CONFIGS[4], check_layers=[0, 1, 31, 62, 63])
+    log(str(rep))
+    assert rep.path & _abi.FRT_PATH_DOWN_SPLIT_K
 
 
 @pytest.mark.timeout(900)
@@ -329,7 +387,8 @@ def test_dit_video_m4096_full_size():
     log(str(rep))
 
 
-@pytest.mark.parametrize("spec", [SMALL[1], (112, 50, 1024, 4096, 2, ACT_GEGLU_TANH), SMALL[5], SMALL[4]],
+@pytest.mark.parametrize("spec", [SMALL[1], (150, 4, 512, 1024, 2, ACT_SWIGLU), (112, 50, 1024, 4096, 2, ACT_GEGLU_TANH),
+                                  SMALL[5], SMALL[4]],
                          ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
 def test_row_permutation(spec):
     # rows are independent under static per-tensor scales: permuting the
