@@ -338,6 +338,7 @@ def measure_chain(cfg, steps, warmup, flags=0, calibrate=True, iso=50):
     step time), isolated replays (median, p10, p90: launch latency included),
     the host's enqueue time, each kernel kind's average, and the chain's
     rate against its roofline (algorithmic bytes and flops per layer)."""
+    from realtime_transformer_amd import _abi
     plan, _, _ = setup(cfg, calibrate=calibrate, flags=flags)
     if not calibrate:
         plan.set_act_scales([0.01] * cfg.L, [0.01] * cfg.L)
@@ -349,7 +350,9 @@ def measure_chain(cfg, steps, warmup, flags=0, calibrate=True, iso=50):
     pct_eager = replay_percentiles(plan, iso, eager=True) if cfg.M * cfg.L <= 1024 else None
     host_us = host_enqueue_us(plan, min(iso, 50))
     k = [float(v) for v in per_kernel_ms(plan)]
+    path = plan.path()
     plan.close()
+    whole = bool(path & _abi.FRT_PATH_DOWN_WHOLE_COLUMN)
     ms = float(ms)
     us = ms * 1000.0 / cfg.L
     lb, lf = cfg.layer_bytes(), cfg.layer_flops()
@@ -371,7 +374,12 @@ def measure_chain(cfg, steps, warmup, flags=0, calibrate=True, iso=50):
            "down_tflops": round(cfg.down_flops() / (k[2] * 1e-3) / 1e12, 1),
            "gateup_gbs": round(cfg.gateup_bytes() / (k[1] * 1e-3) / 1e9, 1),
            "down_gbs": round(cfg.down_bytes() / (k[2] * 1e-3) / 1e9, 1),
-           "norm_gbs": round(cfg.k1_bytes() / (k[0] * 1e-3) / 1e9, 1)}
+           "norm_gbs": None if whole else round(cfg.k1_bytes() / (k[0] * 1e-3) / 1e9, 1),
+           "path": {"gemv": bool(path & _abi.FRT_PATH_GEMV), "norm_split": bool(path & _abi.FRT_PATH_NORM_SPLIT),
+                    "down_whole_column": whole, "down_split_k": bool(path & _abi.FRT_PATH_DOWN_SPLIT_K)}}
+    if whole:
+        rec["kernels_note"] = ("two kernels per layer: the down GEMV forms the next layer's R' and norm slice sums; "
+                               "norm_quant is the slice-sum kernel before layer 0 only, averaged over the layers")
     log("[bench %s flags=%d] %.3f us/layer (iso median %.4f ms), kernels %.2f / %.2f / %.2f us" % (
         cfg.name, flags, us, pct["median"], k[0] * 1000, k[1] * 1000, k[2] * 1000))
     return rec
