@@ -376,7 +376,8 @@ def measure_chain(cfg, steps, warmup, flags=0, calibrate=True, iso=50):
            "down_gbs": round(cfg.down_bytes() / (k[2] * 1e-3) / 1e9, 1),
            "norm_gbs": None if whole else round(cfg.k1_bytes() / (k[0] * 1e-3) / 1e9, 1),
            "path": {"gemv": bool(path & _abi.FRT_PATH_GEMV), "norm_split": bool(path & _abi.FRT_PATH_NORM_SPLIT),
-                    "down_whole_column": whole, "down_split_k": bool(path & _abi.FRT_PATH_DOWN_SPLIT_K)}}
+                    "down_whole_column": whole, "down_split_k": bool(path & _abi.FRT_PATH_DOWN_SPLIT_K),
+                    "gateup_octets": bool(path & _abi.FRT_PATH_GATEUP_OCTETS)}}
     if whole:
         rec["kernels_note"] = ("two kernels per layer: the down GEMV forms the next layer's R' and norm slice sums; "
                                "norm_quant is the slice-sum kernel before layer 0 only, averaged over the layers")

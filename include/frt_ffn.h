@@ -263,11 +263,15 @@ frt_status frt_ffn_io_get(const frt_plan *plan, frt_ffn_io *out);
  *     layers; the down matrix is held in its column-quad layout)
  *   FRT_PATH_DOWN_SPLIT_K: the down projection's K is split over
  *     workgroups, the fp32 partials summed by the next kernel
+ *   FRT_PATH_GATEUP_OCTETS: the decode gate/up GEMV's workgroups own eight
+ *     gate and eight up columns (the gated gate/up matrix held in octet
+ *     order) instead of sixteen of each
  * For tests and logs; FRT_ERR_INVALID_ARG on a NULL argument. */
 #define FRT_PATH_GEMV 1u
 #define FRT_PATH_NORM_SPLIT 2u
 #define FRT_PATH_DOWN_WHOLE_COLUMN 4u
 #define FRT_PATH_DOWN_SPLIT_K 8u
+#define FRT_PATH_GATEUP_OCTETS 16u
 frt_status frt_ffn_plan_path(const frt_plan *plan, uint32_t *path_bits);
 
 /* Eager forward of layers [layer_begin, layer_end) on `stream`: reads slots

@@ -37,6 +37,7 @@ FRT_PATH_GEMV = 1
 FRT_PATH_NORM_SPLIT = 2
 FRT_PATH_DOWN_WHOLE_COLUMN = 4
 FRT_PATH_DOWN_SPLIT_K = 8
+FRT_PATH_GATEUP_OCTETS = 16
 
 _STATUS_NAMES = {0: "FRT_OK", 1: "FRT_ERR_INVALID_ARG", 2: "FRT_ERR_HIP", 3: "FRT_ERR_STATE",
                  4: "FRT_ERR_UNSUPPORTED", 5: "FRT_ERR_WORKSPACE"}

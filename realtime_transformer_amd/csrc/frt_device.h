@@ -112,6 +112,11 @@ __host__ __device__ __forceinline__ uint32_t gate_row(uint32_t i) { return 32u *
 __host__ __device__ __forceinline__ uint32_t up_row_gated(uint32_t i) {
   return 32u * (i >> 4) + 16u + (i & 15u);
 }
+// ... in the octet order of the decode gate/up GEMV's eight-column
+// workgroups: one 16-row group holds gate rows 8j .. 8j+7, then up rows
+// 8j .. 8j+7, so a workgroup streams one group for both matrices.
+__host__ __device__ __forceinline__ uint32_t gate_row_oct(uint32_t i) { return 16u * (i >> 3) + (i & 7u); }
+__host__ __device__ __forceinline__ uint32_t up_row_oct(uint32_t i) { return 16u * (i >> 3) + 8u + (i & 7u); }
 
 // Activations in fp32, written from their definitions:
 //   tanh-GELU(z) = 0.5 z (1 + tanh(c (z + 0.044715 z^3))), c = sqrt(2/pi),

@@ -62,7 +62,7 @@ hipError_t launch_gemv_gateup_mx_nq(int, const uint16_t*, const uint16_t*, const
                                     uint8_t*, uint8_t*, const uint8_t*, const uint8_t*, uint8_t*, uint8_t*, int, int,
                                     int, int, hipStream_t);
 hipError_t launch_gemv_gateup_nq(int, const uint16_t*, const uint16_t*, const double*, int, float, float, uint8_t*,
-                                 const uint8_t*, uint8_t*, int, int, int, int, float, float, float, hipStream_t);
+                                 const uint8_t*, uint8_t*, int, int, int, int, float, float, float, hipStream_t, int);
 hipError_t launch_add_rmsnorm_mx(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*, const float*,
                                  uint16_t*, uint8_t*, uint8_t*, int, int, float, hipStream_t, const float*, int, float,
                                  uint16_t*, int);
@@ -91,7 +91,7 @@ hipError_t launch_mm_down(int, bool, const uint8_t*, const uint8_t*, uint16_t*, 
 int gemm_config_bm(int);
 int gemm_config_bn(int);
 hipError_t launch_calib_gateup(int, const float*, const uint8_t*, float*, float*, int, int, int,
-                               float, float, hipStream_t);
+                               float, float, hipStream_t, int);
 hipError_t launch_calib_down(const float*, const uint8_t*, uint16_t*, int, int, int, float,
                              hipStream_t, int);
 }  // namespace frt
@@ -175,6 +175,7 @@ struct Layout {
   int cfg_gu, cfg_dn;  // GEMM tile configurations
   bool mm_gu, mm_dn;   // GEMM runs on the LDS-DMA f16 kernel (k_mm) rather than k_gemm
   bool norm_split;     // decode GEMV path: k_add_sumsq, then the gate/up GEMV quantises (k_gemv_gateup_nq)
+  bool gu_oct;         // ... with the gated gate/up matrix in octet order (eight-column workgroups)
   bool dn_quad;        // ... with the whole-column down GEMV (k_gemv_down_quad), which forms the next
                        // layer's R' and 4-column slice sums itself: no norm kernel between layers
   size_t sqp;          // its slice sums of squares, fp64 [M][G]
@@ -412,6 +413,18 @@ Layout make_layout(const frt_ffn_desc& d) {
       lo.s_gu = lo.s_gu >= 8 ? 8 : 4;
       lo.s_dn = lo.s_dn >= 8 ? 8 : 4;
     }
+    // gated activations on the split norm: the gate/up matrix in octet order,
+    // one 16-row group per workgroup holding eight gate and eight up columns
+    // (twice the workgroups of half the bytes); FRT_GATEUP_OCT=0 keeps the
+    // 16 + 16 column workgroups
+    lo.gu_oct = lo.norm_split && !lo.mx && !lo.gemv_mt && d.act != FRT_ACT_GELU_TANH && I % 8 == 0 &&
+                env_int("FRT_GATEUP_OCT", 1) != 0;
+    if (lo.gu_oct) {
+      int w = env_int("FRT_GEMV_WAVES_GATEUP_OCT", 8);
+      if (w != 1 && w != 2 && w != 4 && w != 8 && w != 16) w = 8;
+      while (w > 1 && w > (int)(H / 128)) w /= 2;
+      lo.s_gu = w;
+    }
     // M <= 4 on the split norm: the whole-column down GEMV (down matrix in
     // the column-quad layout), FRT_DOWN_QUAD=0 keeps the split-K GEMV and
     // the slice-sum kernel
@@ -424,7 +437,7 @@ Layout make_layout(const frt_ffn_desc& d) {
       // four), fewer where the steps do not reach one per wave
       const int steps = (int)(I / 256);
       int w = env_int("FRT_GEMV_WAVES_DOWN_QUAD", 8);
-      if (w != 1 && w != 2 && w != 4 && w != 8 && w != 16) w = 4;
+      if (w != 1 && w != 2 && w != 4 && w != 8 && w != 16) w = 8;
       while (w > 1 && w > steps) w /= 2;
       lo.k_dn = 1;
       lo.s_dn = w;
@@ -685,8 +698,9 @@ frt_status frt_quant_weights(frt_plan* p, int32_t layer, const void* d_w_gate, c
   // column and normalises with a unit weight
   const void* fold = p->norm_fuse() ? d_norm_w : nullptr;
   if (p->gated) {
-    if ((st = quant_one(p, d_w_gate, I, H, p->wgu(layer), 1, &sg, s, fold)) != FRT_OK) return st;
-    if ((st = quant_one(p, d_w_up, I, H, p->wgu(layer), 2, &su, s, fold)) != FRT_OK) return st;
+    const bool oct = p->lo.gu_oct;
+    if ((st = quant_one(p, d_w_gate, I, H, p->wgu(layer), oct ? 4 : 1, &sg, s, fold)) != FRT_OK) return st;
+    if ((st = quant_one(p, d_w_up, I, H, p->wgu(layer), oct ? 5 : 2, &su, s, fold)) != FRT_OK) return st;
   } else {
     if ((st = quant_one(p, d_w_up, I, H, p->wgu(layer), 0, &su, s, fold)) != FRT_OK) return st;
   }
@@ -728,7 +742,8 @@ frt_status frt_export_weight_codes(const frt_plan* p, int32_t layer, int32_t whi
   uint8_t* dst = static_cast<uint8_t*>(host_dst);
   for (uint32_t n = 0; n < N; ++n) {
     uint32_t prow = n;
-    if (!down && p->gated) prow = which == 0 ? gate_row(n) : up_row_gated(n);
+    if (!down && p->gated && p->lo.gu_oct) prow = which == 0 ? gate_row_oct(n) : up_row_oct(n);
+    else if (!down && p->gated) prow = which == 0 ? gate_row(n) : up_row_gated(n);
     for (uint32_t k = 0; k < K; k += 16)
       memcpy(dst + (size_t)n * K + k,
              tmp.data() + (down && p->lo.dn_quad ? quad_offset(n, k, K) : packed_offset(prow, k, K)), 16);
@@ -834,7 +849,8 @@ frt_status frt_calibrate(frt_plan* p, const void* const* d_r_batches, const void
       KERNEL_CHECK(launch_add_rmsnorm_measure(r_cur, y_cur, p->wn(l), p->mod(l), r_next, x, am + l, rows, H,
                                               p->d.eps, s), "add_rmsnorm_measure");
       KERNEL_CHECK(launch_calib_gateup(p->d.act, x, p->wgu(l), h, am + L + l, rows, H, I,
-                                       p->gated ? p->s_g[l] : p->s_u[l], p->s_u[l], s), "calib_gateup");
+                                       p->gated ? p->s_g[l] : p->s_u[l], p->s_u[l], s, p->lo.gu_oct ? 1 : 0),
+                   "calib_gateup");
       KERNEL_CHECK(launch_calib_down(h, p->wd(l), y_next, rows, I, H, p->s_d[l], s, p->lo.dn_quad ? 1 : 0),
                    "calib_down");
       r_cur = r_next;
@@ -888,6 +904,7 @@ frt_status frt_ffn_plan_path(const frt_plan* p, uint32_t* path_bits) {
   if (p->lo.norm_split) b |= FRT_PATH_NORM_SPLIT;
   if (p->lo.dn_quad) b |= FRT_PATH_DOWN_WHOLE_COLUMN;
   if (p->lo.split_dn > 1) b |= FRT_PATH_DOWN_SPLIT_K;
+  if (p->lo.gu_oct) b |= FRT_PATH_GATEUP_OCTETS;
   *path_bits = b;
   return FRT_OK;
 }
@@ -1000,7 +1017,7 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
       KERNEL_CHECK(launch_gemv_gateup_nq(p->d.act, p->r(l + 1), p->wn(l), p->sqp(),
                                          p->lo.dn_quad ? H / 4 : add_sumsq_slices(H), p->d.eps,
                                          inv_x, p->xq(l), p->wgu(l), p->hq(l), M, H, I, p->lo.s_gu, a_g, a_u, inv_h,
-                                         s),
+                                         s, p->lo.gu_oct ? 1 : 0),
                    "gemv_gateup_nq");
     else if (M <= kGemvMaxM)
       KERNEL_CHECK(launch_gemv_gateup(p->d.act, p->xq(l), p->wgu(l), p->hq(l), M, H, I, p->lo.s_gu,

@@ -45,11 +45,13 @@ __device__ __forceinline__ void load_w16(const uint8_t* __restrict__ w, uint32_t
 
 // X [rows][K] fp32.  Gate/up modes write h [rows][Nout] fp32 and amax|h|;
 // CAL_DOWN writes y [rows][Nout] bf16.  Nout is I or H; Nout % 64 == 0.
+// layout != 0: the decode plans' orders (gated gate/up: octet rows; down:
+// column quads).
 template <int MODE>
 __global__ __launch_bounds__(256) void k_calib_gemm(const float* __restrict__ X,
                                                     const uint8_t* __restrict__ W, void* out,
                                                     float* __restrict__ amax, int rows, int K,
-                                                    int Nout, float s_a, float s_b, int quad) {
+                                                    int Nout, float s_a, float s_b, int layout) {
   constexpr bool TWO = MODE == CAL_GEGLU || MODE == CAL_SWIGLU;
   constexpr int LD = 64 + 1;
   __shared__ float xs[32][LD];
@@ -76,12 +78,12 @@ __global__ __launch_bounds__(256) void k_calib_gemm(const float* __restrict__ X,
       const int n = n0 + (tid >> 1), kk = (tid & 1) * 16;
       uint32_t prow_a, prow_b = 0;
       if (MODE == CAL_GEGLU || MODE == CAL_SWIGLU) {
-        prow_a = gate_row((uint32_t)n);
-        prow_b = up_row_gated((uint32_t)n);
+        prow_a = layout ? gate_row_oct((uint32_t)n) : gate_row((uint32_t)n);
+        prow_b = layout ? up_row_oct((uint32_t)n) : up_row_gated((uint32_t)n);
       } else {
         prow_a = (uint32_t)n;
       }
-      load_w16(W, prow_a, (uint32_t)(k0 + kk), (uint32_t)K, &wa[kk][tid >> 1], LD, quad != 0);
+      load_w16(W, prow_a, (uint32_t)(k0 + kk), (uint32_t)K, &wa[kk][tid >> 1], LD, MODE == CAL_DOWN && layout != 0);
       if (TWO) load_w16(W, prow_b, (uint32_t)(k0 + kk), (uint32_t)K, &wb[kk][tid >> 1], LD, false);
     }
     __syncthreads();
@@ -134,14 +136,14 @@ __global__ __launch_bounds__(256) void k_calib_gemm(const float* __restrict__ X,
 }
 
 hipError_t launch_calib_gateup(int act, const float* x, const uint8_t* w, float* h, float* amax,
-                               int rows, int K, int I, float s_g, float s_u, hipStream_t s) {
+                               int rows, int K, int I, float s_g, float s_u, hipStream_t s, int oct) {
   dim3 grid(I / 64, (rows + 63) / 64);
   if (act == CAL_GEGLU)
     hipLaunchKernelGGL(k_calib_gemm<CAL_GEGLU>, grid, dim3(256), 0, s, x, w, (void*)h, amax, rows,
-                       K, I, s_g, s_u, 0);
+                       K, I, s_g, s_u, oct);
   else if (act == CAL_SWIGLU)
     hipLaunchKernelGGL(k_calib_gemm<CAL_SWIGLU>, grid, dim3(256), 0, s, x, w, (void*)h, amax,
-                       rows, K, I, s_g, s_u, 0);
+                       rows, K, I, s_g, s_u, oct);
   else
     hipLaunchKernelGGL(k_calib_gemm<CAL_GELU>, grid, dim3(256), 0, s, x, w, (void*)h, amax, rows,
                        K, I, s_u, 0.0f, 0);

@@ -211,12 +211,18 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup(const uint8_t* __restric
 // columns (G = K / 4, more than a lane each): the workgroup's threads load
 // them as 16-byte pairs, add their pairs per row in index order, the waves'
 // totals meet in LDS and are added in wave order (fp64 throughout).
+// OCT (gated): the gate/up matrix in octet order (gate_row_oct / up_row_oct):
+// workgroup p streams the one 16-row group holding gate and up columns
+// 8p .. 8p+7, one weight fragment per K block; MFMA column j < 8 is gate
+// column 8p + j and j + 8 its up column, which the epilogue pairs by a lane
+// swap.  Twice the workgroups of half the bytes each.
 constexpr int kNqWidePairs = 4;  // 16-byte slice-sum loads per thread: M * G <= 8 * 64 * W
-template <int ACT, int W, int NB, bool PIPE, int NQC, bool WIDE = false, int NP = kNqWidePairs>
+template <int ACT, int W, int NB, bool PIPE, int NQC, bool WIDE = false, int NP = kNqWidePairs, bool OCT = false>
 __global__ __launch_bounds__(W * 64) void k_gemv_gateup_nq(const NormQ nq, const uint8_t* __restrict__ w,
                                                            uint8_t* __restrict__ hq, int M, int K, int I,
                                                            float alpha_g, float alpha_u, float inv_h) {
-  constexpr bool GATED = ACT != GU_GELU;
+  constexpr bool GATED = ACT != GU_GELU && !OCT;  // two weight streams
+  static_assert(!OCT || ACT != GU_GELU, "octet order is for the gated activations");
   constexpr int NACC = GATED ? 2 : 1;
   extern __shared__ __attribute__((aligned(16))) uint8_t xrow[];  // [M][K] E4M3
   __shared__ v4f red[W][NACC][64];
@@ -381,7 +387,14 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup_nq(const NormQ nq, const
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = 4 * q + r;
-    if (m < M) {
+    if (OCT) {
+      // lane row < 8 holds gate column 8p + row, lane row + 8 its up column
+      const float up = __shfl(accu[r], lane ^ 8, 64);
+      if (m < M && row < 8) {
+        const float h = gated_h<ACT>(accu[r] * alpha_g, up * alpha_u);
+        hq[(size_t)m * I + p * 8 + row] = (uint8_t)e4m3x1(h * inv_h);
+      }
+    } else if (m < M) {
       const float h = gated_h<ACT>(accg[r] * alpha_g, accu[r] * alpha_u);
       hq[(size_t)m * I + p * 16 + row] = (uint8_t)e4m3x1(h * inv_h);
     }
@@ -1292,23 +1305,25 @@ static bool gemv_pipe(const char* env, bool dflt) {
   return (e && *e) ? atoi(e) != 0 : dflt;
 }
 
-template <int W, int NB, bool PIPE, int NQC, bool WIDE, int NP = kNqWidePairs>
+template <int W, int NB, bool PIPE, int NQC, bool WIDE, int NP = kNqWidePairs, bool OCT = false>
 static void gemv_gateup_nq_wnpc(int act, const NormQ& nq, const uint8_t* w, uint8_t* hq, int M, int K, int I,
                                 float a_g, float a_u, float inv_h, hipStream_t s) {
-  dim3 grid(I / 16), block(W * 64);
+  dim3 grid(OCT ? I / 8 : I / 16), block(W * 64);
   const size_t lds = (size_t)M * K;
-  if (act == GU_GEGLU)
-    hipLaunchKernelGGL((k_gemv_gateup_nq<GU_GEGLU, W, NB, PIPE, NQC, WIDE, NP>), grid, block, lds, s, nq, w, hq, M,
-                       K, I, a_g, a_u, inv_h);
-  else if (act == GU_SWIGLU)
-    hipLaunchKernelGGL((k_gemv_gateup_nq<GU_SWIGLU, W, NB, PIPE, NQC, WIDE, NP>), grid, block, lds, s, nq, w, hq, M,
-                       K, I, a_g, a_u, inv_h);
-  else
-    hipLaunchKernelGGL((k_gemv_gateup_nq<GU_GELU, W, NB, PIPE, NQC, WIDE, NP>), grid, block, lds, s, nq, w, hq, M,
-                       K, I, a_g, a_u, inv_h);
+  if (act == GU_GEGLU) {
+    hipLaunchKernelGGL((k_gemv_gateup_nq<GU_GEGLU, W, NB, PIPE, NQC, WIDE, NP, OCT>), grid, block, lds, s, nq, w, hq,
+                       M, K, I, a_g, a_u, inv_h);
+  } else if (act == GU_SWIGLU) {
+    hipLaunchKernelGGL((k_gemv_gateup_nq<GU_SWIGLU, W, NB, PIPE, NQC, WIDE, NP, OCT>), grid, block, lds, s, nq, w,
+                       hq, M, K, I, a_g, a_u, inv_h);
+  } else {
+    if constexpr (!OCT)
+      hipLaunchKernelGGL((k_gemv_gateup_nq<GU_GELU, W, NB, PIPE, NQC, WIDE, NP>), grid, block, lds, s, nq, w, hq, M,
+                         K, I, a_g, a_u, inv_h);
+  }
 }
 
-template <int W, int NB, bool PIPE, bool WIDE = false>
+template <int W, int NB, bool PIPE, bool WIDE = false, bool OCT = false>
 static void gemv_gateup_nq_wnp(int act, const NormQ& nq, const uint8_t* w, uint8_t* hq, int M, int K, int I,
                                float a_g, float a_u, float inv_h, hipStream_t s) {
   // chunks of the largest wave range: M x ceil(K blocks / W) x 16
@@ -1317,22 +1332,29 @@ static void gemv_gateup_nq_wnp(int act, const NormQ& nq, const uint8_t* w, uint8
   if constexpr (WIDE) {
     const bool np2 = (M * nq.G) / 2 <= 2 * W * 64;
     if (chunks > 128 && chunks <= 192) {
-      if (np2) gemv_gateup_nq_wnpc<W, NB, PIPE, 3, true, 2>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
-      else gemv_gateup_nq_wnpc<W, NB, PIPE, 3, true>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
+      if (np2) gemv_gateup_nq_wnpc<W, NB, PIPE, 3, true, 2, OCT>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
+      else gemv_gateup_nq_wnpc<W, NB, PIPE, 3, true, kNqWidePairs, OCT>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
     } else {
-      if (np2) gemv_gateup_nq_wnpc<W, NB, PIPE, 2, true, 2>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
-      else gemv_gateup_nq_wnpc<W, NB, PIPE, 2, true>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
+      if (np2) gemv_gateup_nq_wnpc<W, NB, PIPE, 2, true, 2, OCT>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
+      else gemv_gateup_nq_wnpc<W, NB, PIPE, 2, true, kNqWidePairs, OCT>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
     }
   } else {
-    if (chunks > 128 && chunks <= 192) gemv_gateup_nq_wnpc<W, NB, PIPE, 3, false>(act, nq, w, hq, M, K, I, a_g, a_u,
-                                                                                  inv_h, s);
-    else gemv_gateup_nq_wnpc<W, NB, PIPE, 2, false>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
+    if (chunks > 128 && chunks <= 192)
+      gemv_gateup_nq_wnpc<W, NB, PIPE, 3, false, kNqWidePairs, OCT>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
+    else
+      gemv_gateup_nq_wnpc<W, NB, PIPE, 2, false, kNqWidePairs, OCT>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
   }
 }
 
 template <int W>
 static void gemv_gateup_nq_w(int act, const NormQ& nq, const uint8_t* w, uint8_t* hq, int M, int K, int I,
-                             float a_g, float a_u, float inv_h, hipStream_t s) {
+                             float a_g, float a_u, float inv_h, hipStream_t s, bool oct) {
+  if (oct) {
+    // octet order (gated): one step per K block, pipelined
+    if (nq.G > kNqMaxSlices) gemv_gateup_nq_wnp<W, 1, true, true, true>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
+    else gemv_gateup_nq_wnp<W, 1, true, false, true>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
+    return;
+  }
   if (nq.G > kNqMaxSlices) {
     // the whole-column down GEMV's slice sums (one step per K block, pipelined)
     gemv_gateup_nq_wnp<W, 1, true, true>(act, nq, w, hq, M, K, I, a_g, a_u, inv_h, s);
@@ -1359,20 +1381,22 @@ bool gemv_nq_wide_supported(int M, int K, int W) {
 
 // gate/up GEMV from r' and the slice sums (k_add_sumsq) instead of XQ; the
 // codes it forms are stored to xq_out.
+// oct: the gate/up matrix in octet order (gated activations only).
 hipError_t launch_gemv_gateup_nq(int act, const uint16_t* r, const uint16_t* w_norm, const double* sq, int G,
                                  float eps, float inv_x, uint8_t* xq_out, const uint8_t* w, uint8_t* hq, int M, int K,
-                                 int I, int W, float alpha_g, float alpha_u, float inv_h, hipStream_t s) {
+                                 int I, int W, float alpha_g, float alpha_u, float inv_h, hipStream_t s, int oct) {
   const bool wide = G > kNqMaxSlices;
   if ((wide ? !(G == K / 4 && gemv_nq_wide_supported(M, K, W)) : !gemv_nq_supported(M, K, G)) || G < 1 || I % 16 ||
-      W > K / 128)
+      W > K / 128 || (oct && act == GU_GELU))
     return hipErrorInvalidValue;
   const NormQ nq{r, w_norm, sq, G, eps, inv_x, xq_out};
+  const bool o = oct != 0;
   switch (W) {
-    case 1: gemv_gateup_nq_w<1>(act, nq, w, hq, M, K, I, alpha_g, alpha_u, inv_h, s); break;
-    case 2: gemv_gateup_nq_w<2>(act, nq, w, hq, M, K, I, alpha_g, alpha_u, inv_h, s); break;
-    case 4: gemv_gateup_nq_w<4>(act, nq, w, hq, M, K, I, alpha_g, alpha_u, inv_h, s); break;
-    case 8: gemv_gateup_nq_w<8>(act, nq, w, hq, M, K, I, alpha_g, alpha_u, inv_h, s); break;
-    case 16: gemv_gateup_nq_w<16>(act, nq, w, hq, M, K, I, alpha_g, alpha_u, inv_h, s); break;
+    case 1: gemv_gateup_nq_w<1>(act, nq, w, hq, M, K, I, alpha_g, alpha_u, inv_h, s, o); break;
+    case 2: gemv_gateup_nq_w<2>(act, nq, w, hq, M, K, I, alpha_g, alpha_u, inv_h, s, o); break;
+    case 4: gemv_gateup_nq_w<4>(act, nq, w, hq, M, K, I, alpha_g, alpha_u, inv_h, s, o); break;
+    case 8: gemv_gateup_nq_w<8>(act, nq, w, hq, M, K, I, alpha_g, alpha_u, inv_h, s, o); break;
+    case 16: gemv_gateup_nq_w<16>(act, nq, w, hq, M, K, I, alpha_g, alpha_u, inv_h, s, o); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -46,7 +46,8 @@ __global__ __launch_bounds__(256) void k_amax_bf16(const uint16_t* __restrict__ 
 // Quantise src [N][K] bf16 (times colw[k] when given) with factor inv and
 // scatter 16-column pieces into the packed matrix; source row n lands on
 // packed row
-//   mode 0: n (plain), 1: gate_row(n), 2: up_row_gated(n).
+//   mode 0: n (plain), 1: gate_row(n), 2: up_row_gated(n), 4: gate_row_oct(n),
+//   5: up_row_oct(n); mode 3 scatters row n into the column-quad layout.
 __global__ __launch_bounds__(256) void k_quant_pack(const uint16_t* __restrict__ src,
                                                     uint8_t* __restrict__ dst, int N, int K,
                                                     float inv, int mode, const uint16_t* __restrict__ colw) {
@@ -74,7 +75,11 @@ __global__ __launch_bounds__(256) void k_quant_pack(const uint16_t* __restrict__
                   (bf16_lo(v[2 * j + 1]) * bf16_lo(c[2 * j + 1])) * inv,
                   (bf16_hi(v[2 * j + 1]) * bf16_hi(c[2 * j + 1])) * inv);
   // mode 3: the column-quad layout of the whole-column down GEMV
-  const uint32_t prow = mode == 0 || mode == 3 ? n : (mode == 1 ? gate_row(n) : up_row_gated(n));
+  const uint32_t prow = mode == 0 || mode == 3 ? n
+                        : mode == 1            ? gate_row(n)
+                        : mode == 2            ? up_row_gated(n)
+                        : mode == 4            ? gate_row_oct(n)
+                                               : up_row_oct(n);
   const size_t off = mode == 3 ? quad_offset(n, k0, (uint32_t)K) : packed_offset(prow, k0, (uint32_t)K);
   *reinterpret_cast<uint4*>(dst + off) = make_uint4(q[0], q[1], q[2], q[3]);
 }

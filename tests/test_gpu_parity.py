@@ -181,6 +181,28 @@ def test_small_shapes_down_quad(spec, env, monkeypatch):
     assert rep.path & _abi.FRT_PATH_DOWN_WHOLE_COLUMN
 
 
+@pytest.mark.parametrize("env", [{}, {"FRT_GEMV_WAVES_GATEUP_OCT": "1"}, {"FRT_GEMV_WAVES_GATEUP_OCT": "2"},
+                                 {"FRT_GEMV_WAVES_GATEUP_OCT": "4"}, {"FRT_GEMV_WAVES_GATEUP_OCT": "16"},
+                                 {"FRT_DOWN_QUAD": "0"}],
+                         ids=lambda e: "_".join("%s%s" % (k[4:], v) for k, v in e.items()) or "default")
+@pytest.mark.parametrize("spec", [(151, 1, 640, 768, 2, ACT_SWIGLU), (152, 3, 1152, 1152, 2, ACT_GEGLU_TANH),
+                                  (153, 9, 256, 384, 2, ACT_SWIGLU)],
+                         ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
+def test_small_shapes_gateup_octets(spec, env, monkeypatch):
+    # the decode gate/up GEMV over eight gate + eight up columns per
+    # workgroup (the gated default on the split norm): 1-16 waves over 5, 9
+    # and 2 K blocks (uneven and, at 16 waves, clamped ranges), after the
+    # whole-column down GEMV (M = 1) or the slice-sum kernel (I = 1152 is no
+    # multiple of 256; M = 9)
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    idx, M, H, I, L, act = spec
+    cfg = FFNConfig(idx, "small_oct_%d" % idx, M, H, I, L, act)
+    rep = run_case(cfg)
+    log(str(rep))
+    assert rep.path & _abi.FRT_PATH_GATEUP_OCTETS
+
+
 GEMV_VARIANTS = [
     # decode GEMV launch shapes: K blocks per load step (1 or 2), and the
     # pipelined stream (the next step's loads in flight during the MFMAs)
@@ -203,8 +225,10 @@ GEMV_VARIANTS = [
                                   (123, 1, 2048, 2304, 2, ACT_SWIGLU)],
                          ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
 def test_small_shapes_gemv_launch_variants(spec, env, monkeypatch):
-    # (the split-K down GEMV at every M: the whole-column one is switched off)
+    # (the split-K down GEMV at every M and the 16 + 16 column gate/up
+    # workgroups: the whole-column down and octet gate/up forms are off)
     monkeypatch.setenv("FRT_DOWN_QUAD", "0")
+    monkeypatch.setenv("FRT_GATEUP_OCT", "0")
     for k, v in env.items():
         monkeypatch.setenv(k, v)
     idx, M, H, I, L, act = spec
@@ -224,6 +248,7 @@ def test_small_shapes_norm_quant_three_chunks(waves, spec, quad, monkeypatch):
     # with the slice sums of the whole-column down GEMV (one per four
     # columns) or of the slice-sum kernel
     monkeypatch.setenv("FRT_GEMV_WAVES_GATEUP", waves)
+    monkeypatch.setenv("FRT_GEMV_WAVES_GATEUP_OCT", waves)
     monkeypatch.setenv("FRT_DOWN_QUAD", quad)
     idx, M, H, I, L, act = spec
     cfg = FFNConfig(idx, "small_nqc3_%d_%s" % (idx, quad), M, H, I, L, act)
