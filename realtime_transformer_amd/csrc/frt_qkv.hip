@@ -29,8 +29,8 @@ hipError_t launch_add_rmsnorm_measure(const uint16_t*, const uint16_t*, const ui
 hipError_t launch_amax_bf16(const uint16_t*, size_t, float*, hipStream_t, const uint16_t*, size_t);
 hipError_t launch_rope_table(float2*, int, int, double, hipStream_t);
 hipError_t launch_quant_pack_qkv(const uint16_t*, uint8_t*, int, int, float, int, int, int, const uint16_t*,
-                                 hipStream_t);
-hipError_t launch_gemv_qkv(const uint8_t*, const uint8_t*, const QkvOut&, int, int, int, hipStream_t);
+                                 hipStream_t, int);
+hipError_t launch_gemv_qkv(const uint8_t*, const uint8_t*, const QkvOut&, int, int, int, hipStream_t, int);
 hipError_t launch_mm_qkv(int, const uint8_t*, const uint8_t*, const QkvOut&, int, int, int, hipStream_t);
 hipError_t launch_add_sumsq(const uint16_t*, const uint16_t*, const float*, int, float, uint16_t*, uint16_t*, double*,
                             int, int, hipStream_t, int = 0);
@@ -68,18 +68,21 @@ struct QkvLayout {
   size_t w, wn, mod, rope, r_in, y_in, pos, r_out, xq, q, k, v, amax, cal_x, cal_r, sqp, total;
   bool norm_split;  // M <= 16: k_add_sumsq, then the QKV GEMV quantises its own K blocks (k_gemv_qkv_nq)
   int gemv_w;  // GEMV waves per workgroup (M <= 64)
+  bool oct;    // the GEMV (M <= 64, no split norm) over the octet-ordered weight, one group per workgroup
   int mm_cfg;  // LDS-DMA GEMM configuration (M > 64)
 };
 
-// GEMV waves: the smallest of 4, 8, 16 that gives about 1280 waves across
-// the pairs (measured: 4 waves on the 320 pairs of the decode shape beat 16 by
-// 12%; 8 on the 80 pairs of the action-expert shape), at most the K blocks,
-// 8 above M = 32.
-int qkv_gemv_waves(int pairs, int kblocks, int M) {
+// GEMV waves: the smallest of 4, 8, 16 that gives about `target` waves
+// across the workgroups (pairs: 1280, measured: 4 waves on the 320 pairs of
+// the decode shape beat 16 by 12%, 8 on the 80 pairs of the action-expert
+// shape; octet groups: 4096, 8 waves on the 640 groups of the decode shape
+// 9.68-9.78 us against 9.89-9.91 with 4), at most the K blocks, 8 above
+// M = 32.
+int qkv_gemv_waves(int pairs, int kblocks, int M, int target = 1280) {
   int w = env_int("FRT_QKV_GEMV_WAVES", 0);
   if (w != 4 && w != 8 && w != 16) {
     w = 4;
-    while (w < 16 && pairs * w < 1280) w *= 2;
+    while (w < 16 && pairs * w < target) w *= 2;
     while (w > 4 && w > kblocks) w /= 2;
   }
   if (w == 16 && M > 32) w = 8;
@@ -121,6 +124,11 @@ QkvLayout qkv_layout(const frt_qkv_desc& d) {
   lo.norm_split = d.M <= 16 && (d.flags & FRT_FLAG_ADA_NORM) == 0u &&
                   gemv_qkv_nq_supported(d.M, d.H, add_sumsq_slices(d.H)) && lo.gemv_w <= d.H / 128 &&
                   env_int("FRT_QKV_NORM_SPLIT", 0) != 0;
+  // the plain decode GEMV over the octet-ordered weight: one 16-row group
+  // (eight rotation pairs, or sixteen v rows) per workgroup, twice the
+  // workgroups of the pair order; FRT_QKV_OCT=0 keeps pairs
+  lo.oct = d.M <= kQkvGemvMaxM && !lo.norm_split && env_int("FRT_QKV_OCT", 1) != 0;
+  if (lo.oct) lo.gemv_w = qkv_gemv_waves((int)(N / 16), d.H / 128, d.M, 4096);
   lo.mm_cfg = -1;
   if (d.M > kQkvGemvMaxM) {
     int c = -1, sp = 1;
@@ -198,7 +206,8 @@ static frt_status qkv_launch(frt_qkv_plan* p, int which, hipStream_t s) {
                                     p->at<uint8_t>(p->lo.w), p->out(), M, H, p->lo.gemv_w, s),
                  "gemv_qkv_nq");
   } else if (M <= kQkvGemvMaxM) {
-    KERNEL_CHECK(launch_gemv_qkv(p->at<uint8_t>(p->lo.xq), p->at<uint8_t>(p->lo.w), p->out(), M, H, p->lo.gemv_w, s),
+    KERNEL_CHECK(launch_gemv_qkv(p->at<uint8_t>(p->lo.xq), p->at<uint8_t>(p->lo.w), p->out(), M, H, p->lo.gemv_w, s,
+                                 p->lo.oct ? 1 : 0),
                  "gemv_qkv");
   } else {
     KERNEL_CHECK(launch_mm_qkv(p->lo.mm_cfg, p->at<uint8_t>(p->lo.xq), p->at<uint8_t>(p->lo.w), p->out(), M, H,
@@ -289,7 +298,8 @@ frt_status frt_qkv_quant_weights(frt_qkv_plan* p, const void* d_wq, const void* 
   const int n_rope = (p->d.nq + p->d.nkv) * hd;
   int base = 0;
   for (int t = 0; t < 3; ++t) {
-    KERNEL_CHECK(launch_quant_pack_qkv(src[t], p->at<uint8_t>(p->lo.w), rows[t], H, inv, base, hd, n_rope, fold, s),
+    KERNEL_CHECK(launch_quant_pack_qkv(src[t], p->at<uint8_t>(p->lo.w), rows[t], H, inv, base, hd, n_rope, fold, s,
+                                       p->lo.oct ? 1 : 0),
                  "quant_pack_qkv");
     base += rows[t];
   }
@@ -320,7 +330,7 @@ frt_status frt_qkv_export_weight_codes(const frt_qkv_plan* p, void* host_dst) {
   HIP_CHECK(hipMemcpy(tmp.data(), p->at<uint8_t>(p->lo.w), tmp.size(), hipMemcpyDeviceToHost));
   uint8_t* dst = static_cast<uint8_t*>(host_dst);
   for (uint32_t n = 0; n < N; ++n) {
-    const uint32_t pr = qkv_packed_row(n, hd, n_rope);
+    const uint32_t pr = p->lo.oct ? qkv_packed_row_oct(n, hd, n_rope) : qkv_packed_row(n, hd, n_rope);
     for (uint32_t k = 0; k < H; ++k) dst[(size_t)n * H + k] = tmp[packed_offset(pr, k, H)];
   }
   return FRT_OK;

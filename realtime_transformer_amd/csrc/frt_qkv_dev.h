@@ -39,6 +39,20 @@ __host__ __device__ __forceinline__ uint32_t qkv_packed_row(uint32_t n, uint32_t
   return (2u * pair + ((nv >> 4) & 1u)) * 16u + (nv & 15u);
 }
 
+// ... in the octet order of the decode GEMV's one-group workgroups: group g
+// of a q or k head holds dimensions 8j .. 8j+7 (j = g mod hd/16) in its first
+// eight rows and their partners hd/2 + 8j .. hd/2 + 8j+7 in the last eight;
+// v rows follow in plain order, 16 per group.
+__host__ __device__ __forceinline__ uint32_t qkv_packed_row_oct(uint32_t n, uint32_t hd, uint32_t n_rope) {
+  if (n < n_rope) {
+    const uint32_t head = n / hd, d = n - head * hd, half = hd >> 1;
+    const uint32_t hb = d >= half ? 1u : 0u, dd = d - hb * half;
+    const uint32_t g = head * (hd >> 4) + (dd >> 3);
+    return g * 16u + hb * 8u + (dd & 7u);
+  }
+  return n;  // (n_rope is a multiple of 16: v rows keep their places)
+}
+
 __device__ __forceinline__ int qkv_clamp_pos(const QkvOut& o, int m) {
   const int ps = o.pos[m];
   return ps < 0 ? 0 : (ps >= o.max_pos ? o.max_pos - 1 : ps);
@@ -67,6 +81,30 @@ __device__ __forceinline__ void qkv_store(const QkvOut& o, int m, int p, int rho
     uint16_t* dst = o.v + (size_t)m * o.nkv * o.hd;
     dst[nv] = (uint16_t)f32_to_bf16(x1);
     dst[nv + 16] = (uint16_t)f32_to_bf16(x2);
+  }
+}
+
+// Octet order: row m, group g, lane row rho of the group's accumulator,
+// with `partner` the accumulator of lane row rho ^ 8.  q/k groups: rows
+// rho < 8 store dimension 8j + rho and its partner (the rotation as in
+// qkv_store); v groups: every row stores its own value.
+__device__ __forceinline__ void qkv_store_oct(const QkvOut& o, int m, int g, int rho, float acc, float partner) {
+  const int gph = o.hd >> 4;
+  const int nrg = (o.nq + o.nkv) * gph;
+  if (g < nrg) {
+    if (rho >= 8) return;
+    const int head = g / gph, j = g - head * gph, half = o.hd >> 1;
+    const int d = 8 * j + rho;
+    const float x1 = acc * o.alpha, x2 = partner * o.alpha;
+    const float2 cs = o.rope[(size_t)qkv_clamp_pos(o, m) * half + d];
+    const float x1c = x1 * cs.x, x2s = x2 * cs.y, x2c = x2 * cs.x, x1s = x1 * cs.y;
+    uint16_t* dst = head < o.nq ? o.q + ((size_t)m * o.nq + head) * o.hd
+                                : o.k + ((size_t)m * o.nkv + (head - o.nq)) * o.hd;
+    dst[d] = (uint16_t)f32_to_bf16(x1c - x2s);
+    dst[d + half] = (uint16_t)f32_to_bf16(x2c + x1s);
+  } else {
+    const int nv = 16 * (g - nrg) + rho;
+    o.v[(size_t)m * o.nkv * o.hd + nv] = (uint16_t)f32_to_bf16(acc * o.alpha);
   }
 }
 

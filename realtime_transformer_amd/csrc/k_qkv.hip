@@ -42,7 +42,7 @@ hipError_t launch_rope_table(float2* out, int P, int hd, double base, hipStream_
 // consecutive K values of a row.
 __global__ __launch_bounds__(256) void k_quant_pack_qkv(const uint16_t* __restrict__ src, uint8_t* __restrict__ dst,
                                                         int nrows, int K, float inv, int row_base, int hd, int n_rope,
-                                                        const uint16_t* __restrict__ colw) {
+                                                        const uint16_t* __restrict__ colw, int oct) {
   const size_t pieces_per_row = (size_t)K / 16;
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (size_t)nrows * pieces_per_row) return;
@@ -66,16 +66,17 @@ __global__ __launch_bounds__(256) void k_quant_pack_qkv(const uint16_t* __restri
     q[j] = e4m3x4((bf16_lo(v[2 * j]) * bf16_lo(c[2 * j])) * inv, (bf16_hi(v[2 * j]) * bf16_hi(c[2 * j])) * inv,
                   (bf16_lo(v[2 * j + 1]) * bf16_lo(c[2 * j + 1])) * inv,
                   (bf16_hi(v[2 * j + 1]) * bf16_hi(c[2 * j + 1])) * inv);
-  const uint32_t prow = qkv_packed_row((uint32_t)(row_base + n), (uint32_t)hd, (uint32_t)n_rope);
+  const uint32_t prow = oct ? qkv_packed_row_oct((uint32_t)(row_base + n), (uint32_t)hd, (uint32_t)n_rope)
+                            : qkv_packed_row((uint32_t)(row_base + n), (uint32_t)hd, (uint32_t)n_rope);
   *reinterpret_cast<uint4*>(dst + packed_offset(prow, (uint32_t)k0, (uint32_t)K)) = make_uint4(q[0], q[1], q[2], q[3]);
 }
 
 hipError_t launch_quant_pack_qkv(const uint16_t* src, uint8_t* dst, int nrows, int K, float inv, int row_base,
-                                 int hd, int n_rope, const uint16_t* colw, hipStream_t s) {
+                                 int hd, int n_rope, const uint16_t* colw, hipStream_t s, int oct) {
   const size_t pieces = (size_t)nrows * (K / 16);
   if (pieces == 0) return hipSuccess;
   hipLaunchKernelGGL(k_quant_pack_qkv, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s, src, dst, nrows, K,
-                     inv, row_base, hd, n_rope, colw);
+                     inv, row_base, hd, n_rope, colw, oct);
   return hipGetLastError();
 }
 
@@ -102,7 +103,7 @@ __device__ __forceinline__ void qkv_load_x32(const uint8_t* xr, bool has_row, in
 // weight and activation loads issued before the current block's MFMAs (as
 // the FFN decode GEMVs do), every load unconditional (rows past M read row
 // 0, whose products reach only output rows past M, never stored).
-template <int W, int MT, bool PIPE>
+template <int W, int MT, bool PIPE, bool OCT = false>
 __global__ __launch_bounds__(W * 64) void k_gemv_qkv(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ w,
                                                      const QkvOut o, int M, int K) {
   static_assert(W >= MT, "one wave per tile finishes the epilogue");
@@ -112,8 +113,8 @@ __global__ __launch_bounds__(W * 64) void k_gemv_qkv(const uint8_t* __restrict__
   const int KB = K >> 7;
   const int kb0 = wave * KB / W, kb1 = (wave + 1) * KB / W;
   const int row = lane & 15, q = lane >> 4;
-  const uint8_t* w1 = w + (size_t)(2 * p) * KB * 2048 + lane * 16;
-  const uint8_t* w2 = w + (size_t)(2 * p + 1) * KB * 2048 + lane * 16;
+  const uint8_t* w1 = w + (size_t)(OCT ? p : 2 * p) * KB * 2048 + lane * 16;
+  const uint8_t* w2 = w + (size_t)(OCT ? p : 2 * p + 1) * KB * 2048 + lane * 16;
   const uint8_t* xr[MT];
   bool has[MT];
 #pragma unroll
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(W * 64) void k_gemv_qkv(const uint8_t* __restrict__
     auto load_step = [&](Frag& a, Frag& b, Frag (&x)[MT], int i) {
       const int kb = kb0 + (i < nblk ? i : nblk - 1);
       qkv_load_w32(w1, kb, a);
-      qkv_load_w32(w2, kb, b);
+      if (!OCT) qkv_load_w32(w2, kb, b);
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
         const uint4 lo = *reinterpret_cast<const uint4*>(xr[t] + kb * 128);
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(W * 64) void k_gemv_qkv(const uint8_t* __restrict__
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         asm volatile("" : "+v"(a[j]));
-        asm volatile("" : "+v"(b[j]));
+        if (!OCT) asm volatile("" : "+v"(b[j]));
 #pragma unroll
         for (int t = 0; t < MT; ++t) asm volatile("" : "+v"(x[t][j]));
       }
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(W * 64) void k_gemv_qkv(const uint8_t* __restrict__
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
         ah[s4] = e4m3x8_to_f16(a[2 * s4], a[2 * s4 + 1]);
-        bh[s4] = e4m3x8_to_f16(b[2 * s4], b[2 * s4 + 1]);
+        if (!OCT) bh[s4] = e4m3x8_to_f16(b[2 * s4], b[2 * s4 + 1]);
       }
 #pragma unroll
       for (int t = 0; t < MT; ++t)
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(W * 64) void k_gemv_qkv(const uint8_t* __restrict__
         for (int s4 = 0; s4 < 4; ++s4) {
           const v8h xh = e4m3x8_to_f16(x[t][2 * s4], x[t][2 * s4 + 1]);
           acc1[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, ah[s4], acc1[t], 0, 0, 0);
-          acc2[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, bh[s4], acc2[t], 0, 0, 0);
+          if (!OCT) acc2[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, bh[s4], acc2[t], 0, 0, 0);
         }
     };
     if (nblk > 0) {
@@ -245,11 +246,17 @@ __global__ __launch_bounds__(W * 64) void k_gemv_qkv(const uint8_t* __restrict__
     f += red[v][t][0][lane];
     g += red[v][t][1][lane];
   }
-  // lane holds rows m = 16t + 4q + r of lane row `row` in both groups
+  // lane holds rows m = 16t + 4q + r of lane row `row` in both groups (OCT:
+  // of the one group, its rotation partner in lane row `row` ^ 8)
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = 16 * t + 4 * q + r;
-    if (m < M) qkv_store(o, m, p, row, f[r], g[r]);
+    if (OCT) {
+      const float partner = __shfl(f[r], lane ^ 8, 64);
+      if (m < M) qkv_store_oct(o, m, p, row, f[r], partner);
+    } else if (m < M) {
+      qkv_store(o, m, p, row, f[r], g[r]);
+    }
   }
 }
 
@@ -373,37 +380,42 @@ hipError_t launch_gemv_qkv_nq(const uint16_t* r, const uint16_t* w_norm, const d
 // FRT_QKV_GEMV_PIPE=0 keeps the unpipelined stream
 template <int W, int MT>
 static hipError_t gemv_qkv_t(const uint8_t* xq, const uint8_t* w, const QkvOut& o, int M, int K, int pairs,
-                             hipStream_t s) {
+                             hipStream_t s, bool oct) {
   const char* e = getenv("FRT_QKV_GEMV_PIPE");
-  if (e && *e && atoi(e) == 0)
+  if (oct)
+    hipLaunchKernelGGL((k_gemv_qkv<W, MT, true, true>), dim3(2 * pairs), dim3(W * 64), 0, s, xq, w, o, M, K);
+  else if (e && *e && atoi(e) == 0)
     hipLaunchKernelGGL((k_gemv_qkv<W, MT, false>), dim3(pairs), dim3(W * 64), 0, s, xq, w, o, M, K);
   else
     hipLaunchKernelGGL((k_gemv_qkv<W, MT, true>), dim3(pairs), dim3(W * 64), 0, s, xq, w, o, M, K);
   return hipGetLastError();
 }
 
-// M <= 64; W in {4, 8, 16} (16 taken as 8 above M = 32); pairs = (nq + 2 nkv) * hd / 32.
+// M <= 64; W in {4, 8, 16} (16 taken as 8 above M = 32); pairs = (nq + 2 nkv) * hd / 32;
+// oct: the weight in octet order, one group (half a pair) per workgroup.
 hipError_t launch_gemv_qkv(const uint8_t* xq, const uint8_t* w, const QkvOut& o, int M, int K, int W,
-                           hipStream_t s) {
+                           hipStream_t s, int oct) {
   if (M < 1 || M > 64 || K < 128 || (K & 127)) return hipErrorInvalidValue;
   const int pairs = (o.nq + 2 * o.nkv) * o.hd / 32;
   const int mt = (M + 15) / 16;
   if (W == 16 && mt > 2) W = 8;
-  if (W == 16) return mt == 1 ? gemv_qkv_t<16, 1>(xq, w, o, M, K, pairs, s) : gemv_qkv_t<16, 2>(xq, w, o, M, K, pairs, s);
+  if (W == 16)
+    return mt == 1 ? gemv_qkv_t<16, 1>(xq, w, o, M, K, pairs, s, oct != 0)
+                   : gemv_qkv_t<16, 2>(xq, w, o, M, K, pairs, s, oct != 0);
   if (W == 8) {
     switch (mt) {
-      case 1: return gemv_qkv_t<8, 1>(xq, w, o, M, K, pairs, s);
-      case 2: return gemv_qkv_t<8, 2>(xq, w, o, M, K, pairs, s);
-      case 3: return gemv_qkv_t<8, 3>(xq, w, o, M, K, pairs, s);
-      default: return gemv_qkv_t<8, 4>(xq, w, o, M, K, pairs, s);
+      case 1: return gemv_qkv_t<8, 1>(xq, w, o, M, K, pairs, s, oct != 0);
+      case 2: return gemv_qkv_t<8, 2>(xq, w, o, M, K, pairs, s, oct != 0);
+      case 3: return gemv_qkv_t<8, 3>(xq, w, o, M, K, pairs, s, oct != 0);
+      default: return gemv_qkv_t<8, 4>(xq, w, o, M, K, pairs, s, oct != 0);
     }
   }
   if (W == 4) {
     switch (mt) {
-      case 1: return gemv_qkv_t<4, 1>(xq, w, o, M, K, pairs, s);
-      case 2: return gemv_qkv_t<4, 2>(xq, w, o, M, K, pairs, s);
-      case 3: return gemv_qkv_t<4, 3>(xq, w, o, M, K, pairs, s);
-      default: return gemv_qkv_t<4, 4>(xq, w, o, M, K, pairs, s);
+      case 1: return gemv_qkv_t<4, 1>(xq, w, o, M, K, pairs, s, oct != 0);
+      case 2: return gemv_qkv_t<4, 2>(xq, w, o, M, K, pairs, s, oct != 0);
+      case 3: return gemv_qkv_t<4, 3>(xq, w, o, M, K, pairs, s, oct != 0);
+      default: return gemv_qkv_t<4, 4>(xq, w, o, M, K, pairs, s, oct != 0);
     }
   }
   return hipErrorInvalidValue;

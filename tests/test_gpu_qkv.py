@@ -153,16 +153,23 @@ GEMV_LAUNCH = [
 ]
 
 
-@pytest.mark.parametrize("pipe", ["1", "0"], ids=["pipelined", "unpipelined"])
+QKV_GEMV_MODES = {"octets": {"FRT_QKV_OCT": "1"},
+                  "pairs": {"FRT_QKV_OCT": "0", "FRT_QKV_GEMV_PIPE": "1"},
+                  "pairs_unpipelined": {"FRT_QKV_OCT": "0", "FRT_QKV_GEMV_PIPE": "0"}}
+
+
+@pytest.mark.parametrize("mode", list(QKV_GEMV_MODES))
 @pytest.mark.parametrize("waves", ["4", "8", "16"])
 @pytest.mark.parametrize("spec", GEMV_LAUNCH, ids=lambda s: "M%d_H%d" % (s[1], s[2]))
-def test_qkv_gemv_launch_variants(spec, waves, pipe, monkeypatch):
-    # the decode GEMV under each wave count, with and without the two-stage
-    # K-block pipeline (FRT_QKV_GEMV_PIPE=0 keeps the unpipelined stream)
+def test_qkv_gemv_launch_variants(spec, waves, mode, monkeypatch):
+    # the decode GEMV under each wave count: over the octet-ordered weight
+    # (one 16-row group per workgroup, the default), or over pairs of groups
+    # with and without the two-stage K-block pipeline
     monkeypatch.setenv("FRT_QKV_GEMV_WAVES", waves)
-    monkeypatch.setenv("FRT_QKV_GEMV_PIPE", pipe)
+    for k, v in QKV_GEMV_MODES[mode].items():
+        monkeypatch.setenv(k, v)
     idx, M, H, nq, nkv, hd, pos0, max_pos, base = spec
-    run_qkv_case(QkvConfig(idx, "qkv_gemv_%d_w%s_p%s" % (idx, waves, pipe), M, H, nq, nkv, hd, pos0, max_pos,
+    run_qkv_case(QkvConfig(idx, "qkv_gemv_%d_w%s_%s" % (idx, waves, mode), M, H, nq, nkv, hd, pos0, max_pos,
                            base))
 
 
