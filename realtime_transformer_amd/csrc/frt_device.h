@@ -98,13 +98,14 @@ __host__ __device__ __forceinline__ size_t packed_offset(uint32_t n, uint32_t k,
 
 // Byte offset of element (n, k) of a [N][K] down matrix in the column-quad
 // layout of the whole-column decode down GEMV (K % 256 == 0, N % 4 == 0):
-// quad n / 4 owns K / 256 blocks of 1 KiB, and in block t lane l's 16 bytes
-// are column 4 (n / 4) + (l & 3), elements t * 64 + (l >> 4) * 16 .. + 15 of
-// the K quarter (l & 15) >> 2.
+// quad n / 4 owns K / 256 blocks of 1 KiB, block t covering elements
+// 256 t .. 256 t + 255 of its four columns as four 64-element parts; lane
+// l's 16 bytes are column 4 (n / 4) + (l & 3), elements 256 t + 64 p +
+// (l >> 4) * 16 .. + 15 with part p = (l & 15) >> 2.
 __host__ __device__ __forceinline__ size_t quad_offset(uint32_t n, uint32_t k, uint32_t K) {
-  const uint32_t kq = K >> 2, p = k / kq, r = k - p * kq;
-  const uint32_t lane = ((r & 63u) >> 4) * 16u + p * 4u + (n & 3u);
-  return (((size_t)(n >> 2) * (K >> 8) + (r >> 6)) * 64u + lane) * 16u + (k & 15u);
+  const uint32_t w = k & 255u, p = w >> 6;
+  const uint32_t lane = ((w & 63u) >> 4) * 16u + p * 4u + (n & 3u);
+  return (((size_t)(n >> 2) * (K >> 8) + (k >> 8)) * 64u + lane) * 16u + (k & 15u);
 }
 
 // Packed row of gate row i / up row i in the gated [2I][K] matrix.

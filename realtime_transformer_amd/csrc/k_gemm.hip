@@ -746,17 +746,19 @@ __global__ __launch_bounds__(W * 64) void k_gemv_down(const uint8_t* __restrict_
 // Whole-column decode down GEMV (M <= 4), down matrix in the column-quad
 // layout (quad_offset): one workgroup per four output columns reads those
 // columns over all of K, so it owns their sums and no split-K partials or
-// norm kernel follow it.  Each MFMA takes the four K quarters side by side:
-// operand row 4 p' + m' is activation row m' over quarter p', operand column
-// 4 p + c is weight column c over quarter p, so the products with p' == p
-// are the quarters' partial dot products and the others are discarded
-// (lanes 20 p + c hold quarter p of column c, row m in element m).  The
-// epilogue forms, for its columns,
+// norm kernel follow it.  K is cut into 64-element stripes dealt to four
+// parts in turn (part p: stripes 4t + p), and each MFMA takes the four
+// parts side by side: operand row 4 p' + m' is activation row m' over part
+// p', operand column 4 p + c is weight column c over part p, so the
+// products with p' == p are the parts' partial dot products and the others
+// are discarded (lanes 20 p + c hold part p of column c, row m in element
+// m).  The epilogue forms, for its columns,
 //   Y = bf16(alpha_d * sum),  R' = bf16(R + Y)  (R' and Z alike: r_out),
 //   and the fp64 sum of R'^2 over the four columns, slice c4 of row m of
 //   sq [M][N / 4] (the next layer's split norm reads these slices);
-// r_out == nullptr stores Y only.  Steps of 64 K elements per quarter (1 KiB
-// of weights, 16 bytes per lane and 16 activation bytes), two MFMAs each,
+// r_out == nullptr stores Y only.  Step t covers elements 256 t .. 256 t +
+// 255 (1 KiB of weights, 16 bytes per lane, and the 256 activation bytes
+// of each row read as one contiguous run), two MFMAs each,
 // NB steps per load stage, stages pipelined over two register sets as in
 // k_gemv_gateup_nq; rows m' >= M read row 0, whose products reach only
 // discarded rows.
@@ -770,11 +772,11 @@ __global__ __launch_bounds__(W * 64) void k_gemv_down_quad(const uint8_t* __rest
   __shared__ v4f red[W][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c4 = blockIdx.x;
-  const int T = K >> 8, Kq = K >> 2;
+  const int T = K >> 8;
   const int t0 = wave * T / W, t1 = (wave + 1) * T / W;
   const int part = (lane & 15) >> 2, mr = lane & 3;
   const uint8_t* wp = w + (size_t)c4 * T * 1024 + lane * 16;
-  const uint8_t* xr = hq + (size_t)(mr < M ? mr : 0) * K + part * Kq + (lane >> 4) * 16;
+  const uint8_t* xr = hq + (size_t)(mr < M ? mr : 0) * K + part * 64 + (lane >> 4) * 16;
   const int nstep = t1 - t0;
   uint4 wA[NB], xA[NB], wB[NB], xB[NB];
   // steps i0 .. i0 + NB - 1 (indices clamped to the range: a clamped step is
@@ -788,7 +790,7 @@ __global__ __launch_bounds__(W * 64) void k_gemv_down_quad(const uint8_t* __rest
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int t = t0 + (i0 + j < nstep ? i0 + j : nstep - 1);
-      xx[j] = ld16(xr + t * 64);
+      xx[j] = ld16(xr + t * 256);
     }
   };
   v4f acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
@@ -846,7 +848,7 @@ __global__ __launch_bounds__(W * 64) void k_gemv_down_quad(const uint8_t* __rest
 #pragma unroll
     for (int v = 1; v < W; ++v) acc += red[v][lane];
   }
-  // column c = lane & 3 of lanes 0..3: its quarters in order, then the epilogue
+  // column c = lane & 3 of lanes 0..3: its parts in order, then the epilogue
   const int c = lane & 3;
   float tot[4];
 #pragma unroll
