@@ -59,6 +59,14 @@ def test_workspace_sizes_cover_weights_and_slots():
         assert n < 1.2 * (c.L * nw + slots) + (1 << 30)
 
 
+def test_plan_path_rejects_null_arguments():
+    import ctypes
+    lib = _abi.load()
+    bits = ctypes.c_uint32(0)
+    assert lib.frt_ffn_plan_path(None, ctypes.byref(bits)) == _abi.FRT_ERR_INVALID_ARG
+    assert lib.frt_ffn_plan_path(None, None) == _abi.FRT_ERR_INVALID_ARG
+
+
 def test_plan_create_rejects_null_workspace():
     d = _abi.make_desc(16, 256, 1024, 1, 0)
     with pytest.raises(_abi.FrtError) as e:
