@@ -292,6 +292,18 @@ def test_small_shapes_norm_fuse(spec):
     log(str(rep))
 
 
+@pytest.mark.parametrize("spec", [SMALL[0], (158, 2, 768, 1280, 3, ACT_GEGLU_TANH)],
+                         ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
+def test_small_shapes_norm_fuse_decode_layouts(spec):
+    # the folded gate/up weights in octet order and the whole-column down GEMV
+    # (the decode defaults at M <= 4) with the unit norm weight
+    idx, M, H, I, L, act = spec
+    cfg = FFNConfig(idx, "small_normfuse_dec_%d" % idx, M, H, I, L, act)
+    rep = run_case(cfg, flags=_abi.FRT_FLAG_NORM_FUSE)
+    log(str(rep))
+    assert rep.path & _abi.FRT_PATH_DOWN_WHOLE_COLUMN and rep.path & _abi.FRT_PATH_GATEUP_OCTETS
+
+
 @pytest.mark.parametrize("spec", [(109, 1, 256, 2048, 3, ACT_SWIGLU), (110, 4, 512, 2048, 2, ACT_GELU_TANH)],
                          ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
 def test_small_shapes_norm_fuse_fused_decode(spec):
