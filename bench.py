@@ -142,6 +142,7 @@ def measure_mxfp4(steps, warmup):
         p, _, _ = setup_mx(c)
         ms, _ = time_replays(p, steps, warmup)
         k = [float(v) for v in per_kernel_ms(p)]
+        whole = bool(p.path() & _abi.FRT_PATH_DOWN_WHOLE_COLUMN)
         p.close()
         f = 17.0 / 32
         gu_b = 2 * c.I * c.H * f + c.M * c.H * f + c.M * c.I * f
@@ -151,7 +152,12 @@ def measure_mxfp4(steps, warmup):
         rec = {"us_per_layer": round(us, 3), "layer_bytes": int(layer_b),
                "chain_hbm_gbs": round(layer_b / (us * 1e-6) / 1e9, 1),
                "kernels_us": {"norm_quant": round(k[0] * 1000, 3), "gateup": round(k[1] * 1000, 3),
-                              "down": round(k[2] * 1000, 3)}}
+                              "down": round(k[2] * 1000, 3)},
+               "down_whole_column": whole}
+        if whole:
+            rec["kernels_note"] = ("two kernels per layer: the down GEMV forms the next layer's R' and norm slice "
+                                   "sums; norm_quant is the slice-sum kernel before layer 0 only, averaged over the "
+                                   "layers")
         if c.M <= 64:
             gbs = gu_b / (k[1] * 1e-3) / 1e9
             rec["roofline"] = {"bound": "hbm", "kernel": "gemv_gateup_mx", "achieved": round(gbs, 1),

@@ -76,6 +76,10 @@ hipError_t launch_gemv_gateup_mx(int, const uint8_t*, const uint8_t*, const uint
 hipError_t launch_gemv_down_mx(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, uint16_t*, float*, int,
                                int, int, int, int, hipStream_t);
 int gemv_mx_max_waves(int M);
+bool gemv_mx_nq_wide_supported(int M, int K, int W);
+bool gemv_down_mx_quad_supported(int M, int K, int N);
+hipError_t launch_gemv_down_mx_quad(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const uint16_t*,
+                                    uint16_t*, uint16_t*, double*, int, int, int, int, hipStream_t);
 hipError_t launch_gemv_gateup_fused(int, const uint16_t*, const uint16_t*, const float*, int, float, uint16_t*,
                                     const uint16_t*, uint16_t*, uint8_t*, const uint8_t*, uint8_t*, int, int, int, int,
                                     float, float, float, float, float, hipStream_t);
@@ -176,7 +180,7 @@ struct Layout {
   bool mm_gu, mm_dn;   // GEMM runs on the LDS-DMA f16 kernel (k_mm) rather than k_gemm
   bool norm_split;     // decode GEMV path: k_add_sumsq, then the gate/up GEMV quantises (k_gemv_gateup_nq)
   bool gu_oct;         // ... with the gated gate/up matrix in octet order (eight-column workgroups)
-  bool dn_quad;        // ... with the whole-column down GEMV (k_gemv_down_quad), which forms the next
+  bool dn_quad;        // ... with the whole-column down GEMV (k_gemv_down_quad, k_gemv_down_mx_quad), which forms the next
                        // layer's R' and 4-column slice sums itself: no norm kernel between layers
   size_t sqp;          // its slice sums of squares, fp64 [M][G]
   size_t sqp_bytes;    // bytes of that region
@@ -408,6 +412,22 @@ Layout make_layout(const frt_ffn_desc& d) {
       if (lo.s_gu == 4 && kq % 4 != 0 && kq % 5 == 0 && 5 * mt <= 16) lo.s_gu = 5;
       lo.s_gu = env_int("FRT_GEMV_WAVES_GATEUP_MX", lo.s_gu);
       lo.s_dn = lo.s_dn >= 16 ? 16 : (lo.s_dn >= 8 ? 8 : 4);
+      // M <= 4 on the split norm: the whole-column MXFP4 down GEMV (down
+      // matrix in the column-quad order), FRT_DOWN_QUAD=0 keeps the split-K
+      // GEMV and the slice-sum kernel
+      lo.dn_quad = lo.norm_split && gemv_down_mx_quad_supported((int)M, (int)I, (int)H) &&
+                   gemv_mx_nq_wide_supported((int)M, (int)H, lo.s_gu) && env_int("FRT_DOWN_QUAD", 1) != 0;
+      if (lo.dn_quad) {
+        // 512-value steps per workgroup: I / 512, over eight waves (at M=1,
+        // H=5120, I=17408: 30.7 us/layer against 30.9 with four), fewer
+        // where the steps do not reach one per wave
+        const int steps = (int)(I / 512);
+        int w = env_int("FRT_GEMV_WAVES_DOWN_QUAD_MX", 8);
+        if (w != 1 && w != 2 && w != 4 && w != 8 && w != 16) w = 8;
+        while (w > 1 && w > steps) w /= 2;
+        lo.k_dn = 1;
+        lo.s_dn = w;
+      }
     } else if (lo.gemv_mt) {
       // the multi-tile kernels take 4 or 8 waves (at least one per row tile)
       lo.s_gu = lo.s_gu >= 8 ? 8 : 4;
@@ -428,10 +448,11 @@ Layout make_layout(const frt_ffn_desc& d) {
     // M <= 4 on the split norm: the whole-column down GEMV (down matrix in
     // the column-quad layout), FRT_DOWN_QUAD=0 keeps the split-K GEMV and
     // the slice-sum kernel
-    lo.dn_quad = lo.norm_split && !lo.mx && !lo.gemv_mt && (d.flags & FRT_FLAG_FP8_MFMA_DOWN) == 0u &&
-                 gemv_down_quad_supported((int)M, (int)I, (int)H) && gemv_nq_wide_supported((int)M, (int)H, lo.s_gu) &&
-                 env_int("FRT_DOWN_QUAD", 1) != 0;
-    if (lo.dn_quad) {
+    if (!lo.mx)
+      lo.dn_quad = lo.norm_split && !lo.gemv_mt && (d.flags & FRT_FLAG_FP8_MFMA_DOWN) == 0u &&
+                   gemv_down_quad_supported((int)M, (int)I, (int)H) &&
+                   gemv_nq_wide_supported((int)M, (int)H, lo.s_gu) && env_int("FRT_DOWN_QUAD", 1) != 0;
+    if (lo.dn_quad && !lo.mx) {
       // 1 KiB steps per workgroup: I / 256, over eight waves (at M=1,
       // H=5120, I=17408: 16.0 us against 17.5 with sixteen and 18.2 with
       // four), fewer where the steps do not reach one per wave
@@ -686,7 +707,7 @@ frt_status frt_quant_weights(frt_plan* p, int32_t layer, const void* d_w_gate, c
                    "quant_mx");
     }
     KERNEL_CHECK(launch_quant_mx(static_cast<const uint16_t*>(d_w_down), p->wd(layer), p->wd_s(layer), H, I, 0, nullptr,
-                                 s, mml),
+                                 s, p->lo.dn_quad ? 2 : mml),
                  "quant_mx");
     HIP_CHECK(hipMemcpyAsync(p->wn(layer), d_norm_w, (size_t)H * 2, hipMemcpyDeviceToDevice, s));
     HIP_CHECK(hipStreamSynchronize(s));
@@ -780,6 +801,11 @@ frt_status frt_export_mxfp4_weights(const frt_plan* p, int32_t layer, int32_t wh
   for (uint32_t n = 0; n < N; ++n) {
     const uint32_t pr = down || !p->gated ? n : (which == 0 ? gate_row(n) : up_row_gated(n));
     for (uint32_t b = 0; b < K / 32; ++b) {
+      if (down && p->lo.dn_quad) {
+        memcpy(dc + (size_t)n * (K / 2) + (size_t)b * 16, tc.data() + mx_quad_code_off(n, b, K), 16);
+        dsc[(size_t)n * (K / 32) + b] = ts[mx_quad_scale_off(n, b, K)];
+        continue;
+      }
       const uint32_t kb = b >> 2, lane = (pr & 15u) + 16u * (b & 3u);
       memcpy(dc + (size_t)n * (K / 2) + (size_t)b * 16, tc.data() + mx_code_off(pr, kb, lane, KB), 16);
       dsc[(size_t)n * (K / 32) + b] = ts[p->lo.mx_mm ? mx_scale_off_mm(pr, kb, lane, KB) : mx_scale_off(pr, kb, lane, KB)];
@@ -942,10 +968,12 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
   const float a_g = s_x * p->s_g[l], a_u = s_x * p->s_u[l], a_d = s_h * p->s_d[l];
   const bool fused = p->fused_norm();
   if (p->mx()) {
-    if (which == 0 && p->lo.norm_split) {
+    if (which == 0 && p->lo.dn_quad && after_down) {
+      // R' and the slice sums came from layer l - 1's down GEMV
+    } else if (which == 0 && p->lo.norm_split) {
       const float* yp = (y_in_partials && l > 0) ? p->part() : nullptr;
       KERNEL_CHECK(launch_add_sumsq(p->r(l), p->y(l), yp, p->lo.split_dn, 1.0f, p->y(l), p->r(l + 1), p->sqp(), M, H,
-                                    s),
+                                    s, p->lo.dn_quad ? 1 : 0),
                    "add_sumsq");
     } else if (which == 0) {
       const float* yp = (y_in_partials && l > 0) ? p->part() : nullptr;
@@ -959,7 +987,7 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
                    "mxmm_gateup");
     } else if (which == 1 && p->lo.norm_split) {
       KERNEL_CHECK(launch_gemv_gateup_mx_nq(p->d.act, p->r(l + 1), p->wn(l), p->inv_awq(l), p->sqp(),
-                                            add_sumsq_slices(H), p->d.eps, p->xq(l), p->xs(l), p->wgu(l), p->wgu_s(l),
+                                            p->lo.dn_quad ? H / 4 : add_sumsq_slices(H), p->d.eps, p->xq(l), p->xs(l), p->wgu(l), p->wgu_s(l),
                                             p->hq(l), p->hs(l), M, H, I, p->lo.s_gu, s),
                    "gemv_gateup_mx_nq");
     } else if (which == 1) {
@@ -970,6 +998,10 @@ static frt_status launch_layer_kernel(frt_plan* p, int l, int which, hipStream_t
       KERNEL_CHECK(launch_mxmm_down(p->hq(l), p->hs(l), p->wd(l), p->wd_s(l), p->y(l + 1), p->part(), M, I, H,
                                     p->lo.split_dn, p->lo.mx_dn_nb, s),
                    "mxmm_down");
+    } else if (p->lo.dn_quad) {
+      KERNEL_CHECK(launch_gemv_down_mx_quad(p->hq(l), p->hs(l), p->wd(l), p->wd_s(l), p->r(l + 1), p->y(l + 1),
+                                            l + 1 < p->d.L ? p->r(l + 2) : p->z(), p->sqp(), M, I, H, p->lo.s_dn, s),
+                   "gemv_down_mx_quad");
     } else {
       KERNEL_CHECK(launch_gemv_down_mx(p->hq(l), p->hs(l), p->wd(l), p->wd_s(l), p->y(l + 1), p->part(), M, I, H,
                                        p->lo.s_dn, p->lo.k_dn, s),

@@ -23,6 +23,22 @@ __host__ __device__ __forceinline__ size_t mx_scale_off(uint32_t prow, uint32_t 
   return (((size_t)(prow >> 4) * (KB >> 2) + (kb >> 2)) * 64 + lane) * 4 + (kb & 3);
 }
 
+// MXFP4 down matrix in the column-quad order of the whole-column decode
+// down GEMV (K % 512 == 0): quad n / 4 owns K / 512 steps of 512 values;
+// in step t lane l holds column 4 (n / 4) + (l & 3), the 32 values at
+// 512 t + 128 p + 32 (l >> 4) with part p = (l & 15) >> 2 -- 16 code bytes
+// (1 KiB per step) and one exponent byte (64 per step).  b: 32-block index.
+__host__ __device__ __forceinline__ uint32_t mx_quad_lane(uint32_t n, uint32_t b) {
+  const uint32_t w = b & 15u;  // 32-block within the step: part w / 4, sub-block w % 4
+  return (w & 3u) * 16u + (w >> 2) * 4u + (n & 3u);
+}
+__host__ __device__ __forceinline__ size_t mx_quad_code_off(uint32_t n, uint32_t b, uint32_t K) {
+  return (((size_t)(n >> 2) * (K >> 9) + (b >> 4)) * 64 + mx_quad_lane(n, b)) * 16;
+}
+__host__ __device__ __forceinline__ size_t mx_quad_scale_off(uint32_t n, uint32_t b, uint32_t K) {
+  return ((size_t)(n >> 2) * (K >> 9) + (b >> 4)) * 64 + mx_quad_lane(n, b);
+}
+
 // floor(log2(amax)) from the exponent field (frexp: amax = f * 2^x, f in
 // [0.5, 1)); amax below 2^-126 (zero, subnormal) gives e = 0 either way.
 __device__ __forceinline__ int mx_block_exp(float amax) {

@@ -67,12 +67,19 @@ __global__ __launch_bounds__(256) void k_quant_mx(const uint16_t* __restrict__ s
 #pragma unroll
   for (int q = 0; q < 4; ++q) out[q] = mx_pack8(v + 8 * q, e);
   const uint32_t prow = mode == 0 ? (uint32_t)n : (mode == 1 ? gate_row((uint32_t)n) : up_row_gated((uint32_t)n));
+  if (mm_layout == 2) {  // the column-quad order (down matrix, mode 0)
+    *reinterpret_cast<uint4*>(codes + mx_quad_code_off(prow, (uint32_t)b, (uint32_t)K)) =
+        make_uint4(out[0], out[1], out[2], out[3]);
+    scales[mx_quad_scale_off(prow, (uint32_t)b, (uint32_t)K)] = (uint8_t)e;
+    return;
+  }
   const uint32_t KB = (uint32_t)K / 128, kb = (uint32_t)b >> 2, lane = (prow & 15u) + 16u * ((uint32_t)b & 3u);
   *reinterpret_cast<uint4*>(codes + mx_code_off(prow, kb, lane, KB)) = make_uint4(out[0], out[1], out[2], out[3]);
   scales[mm_layout ? mx_scale_off_mm(prow, kb, lane, KB) : mx_scale_off(prow, kb, lane, KB)] = (uint8_t)e;
 }
 
-// mm_layout: exponents in the prefill GEMM's layout (mx_scale_off_mm)
+// mm_layout: 1 exponents in the prefill GEMM's layout (mx_scale_off_mm); 2
+// codes and exponents in the column-quad order (mx_quad_code_off)
 hipError_t launch_quant_mx(const uint16_t* src, uint8_t* codes, uint8_t* scales, int N, int K, int mode,
                            const uint16_t* colw, hipStream_t s, int mm_layout) {
   if (K % 512) return hipErrorInvalidValue;
@@ -227,8 +234,14 @@ struct MxNormQ {
 constexpr int kMxNqChunks = 2;      // 8-element chunks per lane whose loads are issued together
 constexpr int kMxNqLdsBytes = 16384;  // codes M*K/2 + exponents K/2
 constexpr int kMxNqMaxSlices = 16;
+constexpr int kMxNqWidePairs = 4;  // WIDE: 16-byte slice-sum loads per thread, M * G <= 8 * 64 * W
 
-template <int ACT, int W>
+// WIDE (M <= 4): the slice sums are those of the whole-column down GEMV, one
+// per four columns (G = K / 4): the workgroup's threads load them as
+// 16-byte pairs, add their pairs per row in index order, and the waves'
+// totals meet in LDS, added in wave order (fp64 throughout; the terms are
+// squares of bf16 values, so the total does not depend on the order).
+template <int ACT, int W, bool WIDE = false, int NP = kMxNqWidePairs>
 __global__ __launch_bounds__(W * 64) void k_gemv_gateup_mx_nq(const MxNormQ nq, const uint8_t* __restrict__ wc,
                                                               const uint8_t* __restrict__ ws,
                                                               uint8_t* __restrict__ hc, uint8_t* __restrict__ hs,
@@ -255,7 +268,18 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup_mx_nq(const MxNormQ nq, 
 
   // (1) activation-side loads: 64-chunk groups (512 elements, one row each)
   const int G = nq.G;
-  const double part_v = nq.sq[lane < M * G ? lane : M * G - 1];
+  double part_v = 0.0;
+  double2 sqp[WIDE ? NP : 1];
+  if (WIDE) {
+    const int npairs = (M * G) >> 1;
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int i = (int)threadIdx.x + j * W * 64;
+      sqp[j] = reinterpret_cast<const double2*>(nq.sq)[i < npairs ? i : npairs - 1];
+    }
+  } else {
+    part_v = nq.sq[lane < M * G ? lane : M * G - 1];
+  }
   const int ngrp = M * nqw;
   int gm[kMxNqChunks], gk[kMxNqChunks];
   uint4 rv[kMxNqChunks], wv[kMxNqChunks];
@@ -289,9 +313,34 @@ __global__ __launch_bounds__(W * 64) void k_gemv_gateup_mx_nq(const MxNormQ nq, 
   __builtin_amdgcn_sched_barrier(0);
 
   // (3) 1/rms of row `lane` (lanes < M), then this wave's codes and exponents
-  const double part = lane < M * G ? part_v : 0.0;
   double ssum = 0.0;
-  {
+  if (WIDE) {
+    __shared__ double wsum[W][4];
+    const int npairs = (M * G) >> 1;
+    double rs[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int i = (int)threadIdx.x + j * W * 64;
+      const int m = (2 * i) / G;  // a pair never straddles rows (G even)
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm)
+        if (i < npairs && m == mm) {
+          rs[mm] += sqp[j].x;
+          rs[mm] += sqp[j].y;
+        }
+    }
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
+      if (mm >= M) break;  // uniform
+      const double t = wave_sum_f64(rs[mm]);
+      if (lane == 0) wsum[wave][mm] = t;
+    }
+    __syncthreads();
+    const int mrow = lane < M ? lane : 0;
+#pragma unroll
+    for (int v = 0; v < W; ++v) ssum += wsum[v][mrow & 3];
+  } else {
+    const double part = lane < M * G ? part_v : 0.0;
     const int base = lane < M ? lane * G : 0;
     const unsigned long long b = (unsigned long long)__double_as_longlong(part);
 #pragma unroll
@@ -479,6 +528,140 @@ __global__ __launch_bounds__(W * 64) void k_gemv_down_mx(const uint8_t* __restri
   }
 }
 
+// Whole-column down GEMV (M <= 4), MXFP4 down matrix in the column-quad
+// order (mx_quad_code_off): one workgroup per four output columns reads
+// them over all of K, so it owns their sums and neither split-K partials
+// nor a norm kernel follow it.  Step t covers K values 512 t .. 512 t + 511
+// dealt to four parts of 128 (part p: 512 t + 128 p ..), and one scaled
+// MFMA takes the four parts side by side: operand row 4 p' + m' is
+// activation row m' over part p', operand column 4 p + c weight column c
+// over part p, each lane's exponent byte scaling its own 32 values; the
+// products with p' == p are the parts' partial dot products, the others
+// are discarded (lanes 20 p + c hold part p of column c, row m in element
+// m).  Per step a lane loads 16 weight code bytes and one exponent byte
+// (1 KiB + 64 bytes per workgroup) and the 16 code bytes and exponent byte
+// of its activation row and part.  The epilogue forms, for its columns,
+//   Y = bf16(sum),  R' = bf16(R + Y)  (R' and Z alike: r_out),
+//   and the fp64 sum of R'^2 over the four columns, slice c4 of row m of
+//   sq [M][N / 4] (the next layer's split norm reads these slices);
+// r_out == nullptr stores Y only.  Steps are pipelined over two register
+// sets (the loads of step i + 1 issued before the MFMA of step i); rows
+// m' >= M read row 0, whose products reach only discarded rows.
+template <int W>
+__global__ __launch_bounds__(W * 64) void k_gemv_down_mx_quad(const uint8_t* __restrict__ hc,
+                                                              const uint8_t* __restrict__ hs,
+                                                              const uint8_t* __restrict__ wc,
+                                                              const uint8_t* __restrict__ ws,
+                                                              const uint16_t* __restrict__ r_in,
+                                                              uint16_t* __restrict__ y, uint16_t* __restrict__ r_out,
+                                                              double* __restrict__ sq, int M, int K, int N) {
+  __shared__ v4f red[W][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c4 = blockIdx.x;
+  const int T = K >> 9;
+  const int t0 = wave * T / W, t1 = (wave + 1) * T / W;
+  const int part = (lane & 15) >> 2, mr = lane & 3, sb = lane >> 4;
+  const int mx = mr < M ? mr : 0;
+  const uint8_t* wp = wc + ((size_t)c4 * T * 64 + lane) * 16;
+  const uint8_t* wsp = ws + (size_t)c4 * T * 64 + lane;
+  const uint8_t* xp = hc + (size_t)mx * (K / 2) + part * 64 + sb * 16;
+  const uint8_t* xsp = hs + (size_t)(sb * 16 + mx) * 4 + part;  // + 256 t: mx_act_scale_off_gemv, tile 0
+  const int nstep = t1 - t0;
+  struct Step {
+    v4u_mx w, x;
+    uint32_t we, xe;
+  };
+  // step i (clamped to the range: a clamped step is loaded, not used)
+  auto load_step = [&](Step& st, int i) {
+    const int t = t0 + (i < nstep ? i : nstep - 1);
+    st.w = __builtin_nontemporal_load(reinterpret_cast<const v4u_mx*>(wp + (size_t)t * 1024));
+    st.we = wsp[(size_t)t * 64];
+    st.x = *reinterpret_cast<const v4u_mx*>(xp + (size_t)t * 256);
+    st.xe = xsp[(size_t)t * 256];
+  };
+  v4f acc = {0, 0, 0, 0};
+  auto mma_step = [&](Step& st, int i) {
+    asm volatile("" : "+v"(st.w[0]), "+v"(st.w[1]), "+v"(st.w[2]), "+v"(st.w[3]));
+    asm volatile("" : "+v"(st.x[0]), "+v"(st.x[1]), "+v"(st.x[2]), "+v"(st.x[3]), "+v"(st.we), "+v"(st.xe));
+    if (i < nstep) {  // wave-uniform
+      v8i a, b;
+      a[0] = (int)st.x[0]; a[1] = (int)st.x[1]; a[2] = (int)st.x[2]; a[3] = (int)st.x[3];
+      a[4] = 0; a[5] = 0; a[6] = 0; a[7] = 0;
+      b[0] = (int)st.w[0]; b[1] = (int)st.w[1]; b[2] = (int)st.w[2]; b[3] = (int)st.w[3];
+      b[4] = 0; b[5] = 0; b[6] = 0; b[7] = 0;
+      acc = mx_mfma_u<0>(a, (int)st.xe, b, (int)st.we, acc);
+    }
+  };
+  // wave 0 (which runs the epilogue) requests its columns' R values right
+  // after its first weights, so that they arrive during the stream (rows
+  // clamped to M - 1; any valid address when R is not needed)
+  uint16_t rv[4] = {0, 0, 0, 0};
+  if (nstep > 0) {
+    Step A, B;
+    load_step(A, 0);
+    if (wave == 0) {
+      const uint16_t* rp = r_in ? r_in : y;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) rv[m] = rp[(size_t)(m < M ? m : M - 1) * N + (size_t)c4 * 4 + (lane & 3)];
+    }
+    int i = 0;
+    for (; i + 2 < nstep; i += 2) {
+      load_step(B, i + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_step(A, i);
+      load_step(A, i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_step(B, i + 1);
+    }
+    if (i + 1 < nstep) {
+      load_step(B, i + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_step(A, i);
+      mma_step(B, i + 1);
+    } else {
+      mma_step(A, i);
+    }
+  }
+  if (W > 1) {
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    acc = red[0][lane];
+#pragma unroll
+    for (int v = 1; v < W; ++v) acc += red[v][lane];
+  }
+  // column c = lane & 3 of lanes 0..3: its parts in order, then the epilogue
+  const int c = lane & 3;
+  float tot[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const float q0 = __shfl(acc[m], c, 64), q1 = __shfl(acc[m], 20 + c, 64);
+    const float q2 = __shfl(acc[m], 40 + c, 64), q3 = __shfl(acc[m], 60 + c, 64);
+    tot[m] = ((q0 + q1) + q2) + q3;
+  }
+  const size_t col = (size_t)c4 * 4 + c;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    if (m >= M) break;  // uniform
+    const uint32_t yb = f32_to_bf16(tot[m]);
+    double d = 0.0;
+    if (lane < 4) {
+      y[(size_t)m * N + col] = (uint16_t)yb;
+      if (r_out) {
+        const float rf = __uint_as_float((uint32_t)rv[m] << 16);
+        const uint32_t rb = f32_to_bf16(rf + __uint_as_float(yb << 16));
+        r_out[(size_t)m * N + col] = (uint16_t)rb;
+        const double rd = (double)__uint_as_float(rb << 16);
+        d = rd * rd;
+      }
+    }
+    if (r_out) {
+      const double d1 = __shfl(d, 1, 64), d2 = __shfl(d, 2, 64), d3 = __shfl(d, 3, 64);
+      if (lane == 0) sq[(size_t)m * (N >> 2) + c4] = ((d + d1) + d2) + d3;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // launchers: W in {4, 5, 8, 10, 16} (gate/up; {4, 8, 16} down), MT = ceil(M / 16) <= 4, W * MT <= 16 (the
 // reduction buffer: W * MT * NA KiB of LDS)
@@ -522,20 +705,29 @@ int gemv_mx_max_waves(int M) { return M <= 16 ? 16 : (M <= 32 ? 8 : 4); }
 
 template <int ACT, int W>
 static void gateup_mx_nq_t(const MxNormQ& nq, const uint8_t* wc, const uint8_t* ws, uint8_t* hc, uint8_t* hs, int M,
-                           int K, int I, hipStream_t s) {
+                           int K, int I, bool wide, hipStream_t s) {
   const size_t lds = (size_t)M * (K / 2) + (size_t)K / 2;
-  hipLaunchKernelGGL((k_gemv_gateup_mx_nq<ACT, W>), dim3(I / 32), dim3(W * 64), lds, s, nq, wc, ws, hc, hs, M, K, I);
+  // two slice-sum pairs per thread where they cover the rows, else four
+  if (wide && M * (K / 4) / 2 <= 2 * W * 64)
+    hipLaunchKernelGGL((k_gemv_gateup_mx_nq<ACT, W, true, 2>), dim3(I / 32), dim3(W * 64), lds, s, nq, wc, ws, hc, hs,
+                       M, K, I);
+  else if (wide)
+    hipLaunchKernelGGL((k_gemv_gateup_mx_nq<ACT, W, true, 4>), dim3(I / 32), dim3(W * 64), lds, s, nq, wc, ws, hc, hs,
+                       M, K, I);
+  else
+    hipLaunchKernelGGL((k_gemv_gateup_mx_nq<ACT, W, false>), dim3(I / 32), dim3(W * 64), lds, s, nq, wc, ws, hc, hs,
+                       M, K, I);
 }
 
 template <int ACT>
 static hipError_t gateup_mx_nq_act(int W, const MxNormQ& nq, const uint8_t* wc, const uint8_t* ws, uint8_t* hc,
-                                   uint8_t* hs, int M, int K, int I, hipStream_t s) {
+                                   uint8_t* hs, int M, int K, int I, bool wide, hipStream_t s) {
   switch (W) {
-    case 4: gateup_mx_nq_t<ACT, 4>(nq, wc, ws, hc, hs, M, K, I, s); break;
-    case 5: gateup_mx_nq_t<ACT, 5>(nq, wc, ws, hc, hs, M, K, I, s); break;
-    case 8: gateup_mx_nq_t<ACT, 8>(nq, wc, ws, hc, hs, M, K, I, s); break;
-    case 10: gateup_mx_nq_t<ACT, 10>(nq, wc, ws, hc, hs, M, K, I, s); break;
-    case 16: gateup_mx_nq_t<ACT, 16>(nq, wc, ws, hc, hs, M, K, I, s); break;
+    case 4: gateup_mx_nq_t<ACT, 4>(nq, wc, ws, hc, hs, M, K, I, wide, s); break;
+    case 5: gateup_mx_nq_t<ACT, 5>(nq, wc, ws, hc, hs, M, K, I, wide, s); break;
+    case 8: gateup_mx_nq_t<ACT, 8>(nq, wc, ws, hc, hs, M, K, I, wide, s); break;
+    case 10: gateup_mx_nq_t<ACT, 10>(nq, wc, ws, hc, hs, M, K, I, wide, s); break;
+    case 16: gateup_mx_nq_t<ACT, 16>(nq, wc, ws, hc, hs, M, K, I, wide, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -548,15 +740,25 @@ bool gemv_mx_nq_supported(int M, int K, int G) {
          G <= kMxNqMaxSlices && M * G <= 64;
 }
 
+// ... with the whole-column down GEMV's slice sums (G = K / 4) on W waves
+bool gemv_mx_nq_wide_supported(int M, int K, int W) {
+  const int G = K / 4;
+  return M >= 1 && M <= 4 && K % 512 == 0 && (long)M * (K / 2) + K / 2 <= kMxNqLdsBytes &&
+         M * G <= 2 * kMxNqWidePairs * 64 * W;
+}
+
+// G == K / 4 selects the whole-column down GEMV's slice sums (WIDE)
 hipError_t launch_gemv_gateup_mx_nq(int act, const uint16_t* r, const uint16_t* w_norm, const float* inv_awq,
                                     const double* sq, int G, float eps, uint8_t* xc_out, uint8_t* xs_out,
                                     const uint8_t* wc, const uint8_t* ws, uint8_t* hc, uint8_t* hs, int M, int K,
                                     int I, int W, hipStream_t s) {
-  if (!gemv_mx_nq_supported(M, K, G) || I % 32 || !inv_awq) return hipErrorInvalidValue;
+  const bool wide = K >= 64 && G == K / 4;
+  if (!(wide ? gemv_mx_nq_wide_supported(M, K, W) : gemv_mx_nq_supported(M, K, G)) || I % 32 || !inv_awq)
+    return hipErrorInvalidValue;
   const MxNormQ nq{r, w_norm, inv_awq, sq, G, eps, xc_out, xs_out};
-  if (act == MX_GEGLU) return gateup_mx_nq_act<MX_GEGLU>(W, nq, wc, ws, hc, hs, M, K, I, s);
-  if (act == MX_SWIGLU) return gateup_mx_nq_act<MX_SWIGLU>(W, nq, wc, ws, hc, hs, M, K, I, s);
-  return gateup_mx_nq_act<MX_GELU>(W, nq, wc, ws, hc, hs, M, K, I, s);
+  if (act == MX_GEGLU) return gateup_mx_nq_act<MX_GEGLU>(W, nq, wc, ws, hc, hs, M, K, I, wide, s);
+  if (act == MX_SWIGLU) return gateup_mx_nq_act<MX_SWIGLU>(W, nq, wc, ws, hc, hs, M, K, I, wide, s);
+  return gateup_mx_nq_act<MX_GELU>(W, nq, wc, ws, hc, hs, M, K, I, wide, s);
 }
 
 hipError_t launch_gemv_gateup_mx(int act, const uint8_t* xc, const uint8_t* xs, const uint8_t* wc, const uint8_t* ws,
@@ -597,6 +799,30 @@ hipError_t launch_gemv_down_mx(const uint8_t* hc, const uint8_t* hs, const uint8
   if (W == 8) return down_mx_w<8>(hc, hs, wc, ws, y, part, M, K, N, S, s);
   if (W == 16) return down_mx_w<16>(hc, hs, wc, ws, y, part, M, K, N, S, s);
   return hipErrorInvalidValue;
+}
+
+// Whether the whole-column MXFP4 down GEMV takes the shape
+bool gemv_down_mx_quad_supported(int M, int K, int N) { return M >= 1 && M <= 4 && K % 512 == 0 && N % 4 == 0; }
+
+// W waves per workgroup (1, 2, 4, 8, 16; at most one per 512-value step)
+hipError_t launch_gemv_down_mx_quad(const uint8_t* hc, const uint8_t* hs, const uint8_t* wc, const uint8_t* ws,
+                                    const uint16_t* r_in, uint16_t* y, uint16_t* r_out, double* sq, int M, int K,
+                                    int N, int W, hipStream_t s) {
+  if (!gemv_down_mx_quad_supported(M, K, N) || W < 1 || W > (K >> 9) || (r_out && (!r_in || !sq)))
+    return hipErrorInvalidValue;
+  const dim3 grid(N / 4), block(W * 64);
+#define FRT_DMQ(WV) \
+  hipLaunchKernelGGL((k_gemv_down_mx_quad<WV>), grid, block, 0, s, hc, hs, wc, ws, r_in, y, r_out, sq, M, K, N)
+  switch (W) {
+    case 1: FRT_DMQ(1); break;
+    case 2: FRT_DMQ(2); break;
+    case 4: FRT_DMQ(4); break;
+    case 8: FRT_DMQ(8); break;
+    case 16: FRT_DMQ(16); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef FRT_DMQ
+  return hipGetLastError();
 }
 
 }  // namespace frt

@@ -182,6 +182,47 @@ def test_mxfp4_small_ada_norm():
     run_mx_case(FFNConfig(idx, "mx_ada_%d" % idx, M, H, I, L, act), flags=_abi.FRT_FLAG_ADA_NORM)
 
 
+# the whole-column down GEMV (M <= 4 on the split norm: the down matrix in
+# the column-quad order, the next layer's R' and slice sums formed in its
+# epilogue, no norm kernel between layers): uneven step shares over the
+# waves, a single step on a single wave, every activation, rows 1..4, and
+# the gate/up prologue's slice-sum loads filled to their limit (M = 4,
+# H = 2048 on four waves)
+MX_QUAD = [
+    (160, 1, 512, 2560, 3, ACT_SWIGLU),
+    (161, 2, 1024, 1024, 2, ACT_GEGLU_TANH),
+    (162, 3, 512, 512, 2, ACT_GELU_TANH),
+    (163, 4, 2048, 1536, 2, ACT_SWIGLU),
+]
+
+
+def _mx_path(M, H, I, L, act):
+    plan = FFNPlan(M, H, I, L, act, 1e-6, flags=_abi.FRT_FLAG_MXFP4)
+    try:
+        return plan.path()
+    finally:
+        plan.close()
+
+
+@pytest.mark.parametrize("spec", MX_QUAD, ids=lambda s: "M%d_H%d_I%d_act%d" % (s[1], s[2], s[3], s[5]))
+def test_mxfp4_small_down_whole_column(spec):
+    idx, M, H, I, L, act = spec
+    assert _mx_path(M, H, I, L, act) & _abi.FRT_PATH_DOWN_WHOLE_COLUMN
+    run_mx_case(FFNConfig(idx, "mx_quad_%d" % idx, M, H, I, L, act), awq=True)
+
+
+@pytest.mark.parametrize("spec", [MX_QUAD[0], MX_QUAD[3]], ids=lambda s: "M%d" % s[1])
+def test_mxfp4_small_down_split_k(spec, monkeypatch):
+    # FRT_DOWN_QUAD=0: the down GEMV on 16-column workgroups (K split in two
+    # at I = 2560, whole at I = 1536) and the slice-sum kernel
+    monkeypatch.setenv("FRT_DOWN_QUAD", "0")
+    idx, M, H, I, L, act = spec
+    path = _mx_path(M, H, I, L, act)
+    assert not path & _abi.FRT_PATH_DOWN_WHOLE_COLUMN
+    assert bool(path & _abi.FRT_PATH_DOWN_SPLIT_K) == (I == 2560)
+    run_mx_case(FFNConfig(idx, "mx_splitk_%d" % idx, M, H, I, L, act), awq=True)
+
+
 # the block-scaled prefill GEMM (M > 64): one and several 128-row tiles,
 # ragged tails, all three activations, the K-split down GEMM
 MM = [
