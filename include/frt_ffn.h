@@ -258,9 +258,10 @@ frt_status frt_ffn_io_get(const frt_plan *plan, frt_ffn_io *out);
  *   FRT_PATH_GEMV: M <= 16, the decode GEMVs (else multi-tile GEMVs or GEMMs)
  *   FRT_PATH_NORM_SPLIT: the decode norm split into slice sums and the
  *     gate/up GEMV's own quantisation
- *   FRT_PATH_DOWN_WHOLE_COLUMN: the whole-column down GEMV (M <= 4), which
- *     forms the next layer's R' and norm slice sums (no norm kernel between
- *     layers; the down matrix is held in its column-quad layout)
+ *   FRT_PATH_DOWN_WHOLE_COLUMN: the whole-column down GEMV (M <= 4, E4M3 or
+ *     MXFP4), which forms the next layer's R' and norm slice sums (no norm
+ *     kernel between layers; the down matrix is held in its column-quad
+ *     layout)
  *   FRT_PATH_DOWN_SPLIT_K: the down projection's K is split over
  *     workgroups, the fp32 partials summed by the next kernel
  *   FRT_PATH_GATEUP_OCTETS: the decode gate/up GEMV's workgroups own eight
