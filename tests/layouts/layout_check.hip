@@ -1,9 +1,10 @@
 // Host-only checks of the packed weight orders the kernels and the export
-// paths share (csrc/frt_device.h, csrc/frt_qkv_dev.h): every order is a
+// paths share (csrc/frt_device.h, csrc/frt_qkv_dev.h, csrc/frt_mx.h): every order is a
 // bijection onto its packed range, and keeps together what its kernel needs
 // together.  Built with hipcc and run on the CPU by tests/test_layouts_cpu.py
 // (no GPU call is made).  Exit status 0 when every check holds.
 #include "frt_qkv_dev.h"
+#include "frt_mx.h"
 
 #include <cstdio>
 #include <vector>
@@ -83,10 +84,43 @@ static void check_qkv(uint32_t nq, uint32_t nkv, uint32_t hd) {
   }
 }
 
+// MXFP4 orders, per 32-value block b of row n.  GEMV order: 16-row groups,
+// 1 KiB per (group, 128-K block), exponents per (group, four K blocks).
+// Column-quad order (the whole-column down GEMV): quad q's codes in
+// [q K/2 * 4, (q + 1) K/2 * 4) and exponents in [q K/8, (q + 1) K/8); in step
+// t lane l holds column 4q + l % 4, part p = (l % 16) / 4, sub-block l / 16,
+// the block 16t + 4p + l / 16; the activation exponent the kernel reads for
+// row m < 4 and that block is byte p of dword 64t + 16 (l / 16) + m of the
+// HQ slot's GEMV layout.
+static void check_mx(uint32_t N, uint32_t K) {
+  const uint32_t nb = K / 32, KB = K / 128;
+  std::vector<int> c1(N * nb, 0), s1(N * nb, 0), c2(N * nb, 0), s2(N * nb, 0);
+  for (uint32_t n = 0; n < N; ++n)
+    for (uint32_t b = 0; b < nb; ++b) {
+      const uint32_t kb = b / 4, lane = (n % 16) + 16 * (b % 4);
+      const size_t co = mx_code_off(n, kb, lane, KB), so = mx_scale_off(n, kb, lane, KB);
+      CHECK(co % 16 == 0 && co / 16 < c1.size() && c1[co / 16]++ == 0, "mx_code_off(%u, %u, K %u) = %zu", n, b, K, co);
+      CHECK(so < s1.size() && s1[so]++ == 0, "mx_scale_off(%u, %u, K %u) = %zu", n, b, K, so);
+      const size_t qc = mx_quad_code_off(n, b, K), qs = mx_quad_scale_off(n, b, K);
+      CHECK(qc % 16 == 0 && qc / 16 < c2.size() && c2[qc / 16]++ == 0, "mx_quad_code_off(%u, %u, K %u) = %zu", n, b,
+            K, qc);
+      CHECK(qs < s2.size() && s2[qs]++ == 0, "mx_quad_scale_off(%u, %u, K %u) = %zu", n, b, K, qs);
+      const size_t q = n / 4;
+      CHECK(qc >= q * 2 * K && qc < (q + 1) * 2 * K, "mx_quad_code_off(%u, %u) outside its quad", n, b);
+      const uint32_t t = b / 16, p = (b % 16) / 4, sb = b % 4, l = sb * 16 + p * 4 + n % 4;
+      CHECK(qc == (((size_t)q * (K / 512) + t) * 64 + l) * 16 && qs == ((size_t)q * (K / 512) + t) * 64 + l,
+            "column-quad lane order at %u %u", n, b);
+      if (n < 4)
+        CHECK(mx_act_scale_off_gemv(n, b, KB) == ((size_t)t * 64 + sb * 16 + n) * 4 + p,
+              "activation exponent of row %u block %u", n, b);
+    }
+}
+
 int main() {
   for (uint32_t N : {16u, 48u}) for (uint32_t K : {128u, 384u}) check_packed(N, K);
   for (uint32_t N : {4u, 12u, 40u}) for (uint32_t K : {256u, 768u, 1280u}) check_quad(N, K);
   for (uint32_t I : {16u, 48u, 128u, 640u}) check_gated(I);
+  for (uint32_t N : {16u, 48u}) for (uint32_t K : {512u, 1536u, 2560u}) check_mx(N, K);
   check_qkv(2, 1, 64);
   check_qkv(4, 2, 32);
   check_qkv(8, 1, 256);

@@ -1,5 +1,6 @@
 """The packed weight orders (MFMA fragment order, the decode GEMVs' column
-quads and octets, the fused QKV pairs and octets) checked on the host: a
+quads and octets, the fused QKV pairs and octets, the MXFP4 GEMV and
+column-quad orders) checked on the host: a
 small program built with hipcc from the same headers the kernels and the
 export paths use (tests/layouts/layout_check.hip) verifies that every order
 is a bijection and keeps together what its kernel needs together.  No GPU is
