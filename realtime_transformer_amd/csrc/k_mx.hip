@@ -539,7 +539,7 @@ __global__ __launch_bounds__(W * 64) void k_gemv_down_mx(const uint8_t* __restri
 // products with p' == p are the parts' partial dot products, the others
 // are discarded (lanes 20 p + c hold part p of column c, row m in element
 // m).  Per step a lane loads 16 weight code bytes and one exponent byte
-// (1 KiB + 64 bytes per workgroup) and the 16 code bytes and exponent byte
+// (1 KiB + 64 bytes per step) and the 16 code bytes and exponent byte
 // of its activation row and part.  The epilogue forms, for its columns,
 //   Y = bf16(sum),  R' = bf16(R + Y)  (R' and Z alike: r_out),
 //   and the fp64 sum of R'^2 over the four columns, slice c4 of row m of
