@@ -83,6 +83,7 @@ __global__ __launch_bounds__(256) void k_quant_mx(const uint16_t* __restrict__ s
 hipError_t launch_quant_mx(const uint16_t* src, uint8_t* codes, uint8_t* scales, int N, int K, int mode,
                            const uint16_t* colw, hipStream_t s, int mm_layout) {
   if (K % 512) return hipErrorInvalidValue;
+  if (mm_layout == 2 && (mode != 0 || N % 4)) return hipErrorInvalidValue;  // column quads of a plain matrix
   const size_t n = (size_t)N * (K / 32);
   hipLaunchKernelGGL(k_quant_mx, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, codes, scales, N, K, mode,
                      colw, mm_layout);
