@@ -151,6 +151,7 @@ def measure_mxfp4(steps, warmup):
         us = float(ms) * 1000.0 / c.L
         rec = {"us_per_layer": round(us, 3), "layer_bytes": int(layer_b),
                "chain_hbm_gbs": round(layer_b / (us * 1e-6) / 1e9, 1),
+               "chain_hbm_frac": round(layer_b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                "kernels_us": {"norm_quant": round(k[0] * 1000, 3), "gateup": round(k[1] * 1000, 3),
                               "down": round(k[2] * 1000, 3)},
                "down_whole_column": whole}
