@@ -410,7 +410,12 @@ Layout make_layout(const frt_ffn_desc& d) {
       // take five (measured at the decode shape: 18.7 against 19.3 us)
       const int kq = (int)(H / 512), mt = ceil_div(d.M, 16);
       if (lo.s_gu == 4 && kq % 4 != 0 && kq % 5 == 0 && 5 * mt <= 16) lo.s_gu = 5;
-      lo.s_gu = env_int("FRT_GEMV_WAVES_GATEUP_MX", lo.s_gu);
+      {
+        // an override is taken only where the kernel has it: 4, 5, 8, 10 or
+        // 16 waves, at least one per row tile, W * row tiles <= 16
+        const int w = env_int("FRT_GEMV_WAVES_GATEUP_MX", lo.s_gu);
+        if ((w == 4 || w == 5 || w == 8 || w == 10 || w == 16) && w >= mt && w * mt <= 16) lo.s_gu = w;
+      }
       lo.s_dn = lo.s_dn >= 16 ? 16 : (lo.s_dn >= 8 ? 8 : 4);
       // M <= 4 on the split norm: the whole-column MXFP4 down GEMV (down
       // matrix in the column-quad order), FRT_DOWN_QUAD=0 keeps the split-K
