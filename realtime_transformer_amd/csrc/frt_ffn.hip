@@ -395,6 +395,9 @@ Layout make_layout(const frt_ffn_desc& d) {
     lo.k_dn = gemv_down_splits((int)(H / 16), (int)(I / 128), lo.norm_split ? 4 : 2);
     lo.s_dn = gemv_waves((int)(H / 16) * lo.k_dn, (int)(I / 128) / lo.k_dn, "FRT_GEMV_WAVES_DOWN", 4096);
     if (lo.mx) {
+      // the MXFP4 down GEMV splits K in whole 512-value quads (an override
+      // beyond them is clamped)
+      lo.k_dn = std::max(1, std::min(lo.k_dn, (int)(I / 512)));
       // MXFP4 GEMVs: 4, 8 or 16 waves, fewer for more row tiles (LDS); the
       // gate/up workgroups own 32 columns.  Target ~2 waves per SIMD
       // (measured at the decode shape: 4 waves per workgroup for both GEMVs,
