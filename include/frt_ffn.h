@@ -275,6 +275,12 @@ frt_status frt_ffn_io_get(const frt_plan *plan, frt_ffn_io *out);
 #define FRT_PATH_GATEUP_OCTETS 16u
 frt_status frt_ffn_plan_path(const frt_plan *plan, uint32_t *path_bits);
 
+/* The FRT_PATH_* bits a plan created from `desc` would have, under the
+ * current environment, without creating it: host only, no device call.
+ * FRT_ERR_INVALID_ARG on a NULL pointer or an invalid descriptor (as
+ * frt_ffn_workspace_size). */
+frt_status frt_ffn_desc_path(const frt_ffn_desc *desc, uint32_t *path_bits);
+
 /* Eager forward of layers [layer_begin, layer_end) on `stream`: reads slots
  * R[layer_begin], Y[layer_begin], writes the later slots; when layer_end == L
  * also writes Z.  Asynchronous: no allocation, no host synchronisation.

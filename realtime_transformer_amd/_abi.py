@@ -48,7 +48,7 @@ EXPORTED = [
     "frt_ffn_io_get", "frt_ffn_forward_range", "frt_ffn_forward", "frt_graph_capture",
     "frt_graph_replay", "frt_ffn_forward_profiled", "frt_ffn_time_kernel", "frt_e4m3_encode_f32",
     "frt_last_error", "frt_export_mxfp4_weights", "frt_set_awq", "frt_ffn_forward_range_static_scratch",
-    "frt_ffn_plan_path",
+    "frt_ffn_plan_path", "frt_ffn_desc_path",
     # attention input (include/frt_qkv.h)
     "frt_qkv_workspace_size", "frt_qkv_plan_create", "frt_qkv_plan_destroy", "frt_qkv_quant_weights",
     "frt_qkv_export_weight_codes", "frt_qkv_calibrate", "frt_qkv_get_scales", "frt_qkv_set_act_scale",
@@ -117,6 +117,7 @@ def load(build_if_missing: bool = True):
         "frt_set_act_scales": [vp, ctypes.POINTER(ctypes.c_float)],
         "frt_ffn_io_get": [vp, ctypes.POINTER(frt_ffn_io)],
         "frt_ffn_plan_path": [vp, ctypes.POINTER(ctypes.c_uint32)],
+        "frt_ffn_desc_path": [ctypes.POINTER(frt_ffn_desc), ctypes.POINTER(ctypes.c_uint32)],
         "frt_ffn_forward_range": [vp, i32, i32, vp],
         "frt_ffn_forward_range_static_scratch": [vp, i32, i32, vp],
         "frt_ffn_forward": [vp, vp],
@@ -212,6 +213,13 @@ def frt_set_act_scales(plan: int, scales) -> None:
 def frt_ffn_plan_path(plan: int) -> int:
     bits = ctypes.c_uint32(0)
     _check(load().frt_ffn_plan_path(plan, ctypes.byref(bits)))
+    return int(bits.value)
+
+
+def frt_ffn_desc_path(desc: frt_ffn_desc) -> int:
+    """FRT_PATH_* bits of a plan with this descriptor (host only)."""
+    bits = ctypes.c_uint32(0)
+    _check(load().frt_ffn_desc_path(ctypes.byref(desc), ctypes.byref(bits)))
     return int(bits.value)
 
 

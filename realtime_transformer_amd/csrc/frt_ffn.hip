@@ -931,15 +931,26 @@ frt_status frt_set_act_scales(frt_plan* p, const float* host_in) {
   return FRT_OK;
 }
 
+static uint32_t path_bits_of(const frt_ffn_desc& d, const Layout& lo) {
+  uint32_t b = 0;
+  if (d.M <= kGemvMaxM && !lo.mx_mm) b |= FRT_PATH_GEMV;
+  if (lo.norm_split) b |= FRT_PATH_NORM_SPLIT;
+  if (lo.dn_quad) b |= FRT_PATH_DOWN_WHOLE_COLUMN;
+  if (lo.split_dn > 1) b |= FRT_PATH_DOWN_SPLIT_K;
+  if (lo.gu_oct) b |= FRT_PATH_GATEUP_OCTETS;
+  return b;
+}
+
 frt_status frt_ffn_plan_path(const frt_plan* p, uint32_t* path_bits) {
   if (!p || !path_bits) return fail(FRT_ERR_INVALID_ARG, "frt_ffn_plan_path: NULL argument");
-  uint32_t b = 0;
-  if (p->d.M <= kGemvMaxM && !p->lo.mx_mm) b |= FRT_PATH_GEMV;
-  if (p->lo.norm_split) b |= FRT_PATH_NORM_SPLIT;
-  if (p->lo.dn_quad) b |= FRT_PATH_DOWN_WHOLE_COLUMN;
-  if (p->lo.split_dn > 1) b |= FRT_PATH_DOWN_SPLIT_K;
-  if (p->lo.gu_oct) b |= FRT_PATH_GATEUP_OCTETS;
-  *path_bits = b;
+  *path_bits = path_bits_of(p->d, p->lo);
+  return FRT_OK;
+}
+
+frt_status frt_ffn_desc_path(const frt_ffn_desc* desc, uint32_t* path_bits) {
+  if (!path_bits) return fail(FRT_ERR_INVALID_ARG, "frt_ffn_desc_path: path_bits is NULL");
+  if (!desc_ok(desc)) return fail(FRT_ERR_INVALID_ARG, "frt_ffn_desc_path: invalid descriptor");
+  *path_bits = path_bits_of(*desc, make_layout(*desc));
   return FRT_OK;
 }
 
